@@ -1,0 +1,182 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The operator (readings of the pages; the page title and section are cited
+ * at each call):
+ *   per sequence and head, with fp32 state S in R^{dk x dv} starting at h0
+ *   (or 0), for every token t
+ *       S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *       o_t = scale * S_t^T q_t
+ *   i.e. the delta-rule recurrence with a per-channel decay gate
+ *   ("Pure KDA 300M on Primus" guide, Overview; openkimi README, What is
+ *   implemented, and its FlashQLA paragraph: KDA's decay is channel-wise),
+ *   computed chunk by chunk (chunks of 64 tokens, in-chunk WY/UT form) with
+ *   optional document offsets that reset the state at every document start
+ *   (torchtitan PR #4347 "[kimi k3] Support sample packing in KDA",
+ *   Verification).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer, contiguous, 16-byte aligned,
+ *     row-major in the layout given at the call.  Token-major layouts
+ *     [B,T,H,d] follow the [B,T,D] activations of the Primus guide
+ *     (Troubleshooting: keep [B,T,D], call .contiguous()).
+ *   - The caller owns every buffer, including the workspace sized by the
+ *     *_workspace queries.  The library never allocates, frees or
+ *     synchronizes, and never reads device memory on the host.
+ *   - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream).
+ *   - Arguments are checked from the descriptor and the pointer values only.
+ *     On any error the call returns before launching anything and leaves all
+ *     outputs untouched; kda_last_error() then describes it (thread-local).
+ *   - Results are deterministic run to run (no floating-point atomics).
+ *   - No output may alias an input, except the in-place state of kda_step.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layout-compatible with hipStream_t, so this header needs no HIP include. */
+typedef struct ihipStream_t* kda_stream_t;
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID = 1,     /* bad shape, null/misaligned pointer, bad flag */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dk, dv pair) */
+    KDA_ERR_WORKSPACE = 3,   /* workspace null or too small */
+    KDA_ERR_HIP = 4          /* a HIP launch failed */
+} kda_status;
+
+typedef enum kda_dtype { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
+
+/* Optional fused preparation (openkimi README, What is implemented: fused
+ * Q/K norm, decay gate and beta; Primus guide, Overview: decay gate with
+ * learnable A_log and dt_bias through softplus).  With a flag set, the
+ * corresponding argument holds the RAW input and gradients are returned with
+ * respect to that raw input.
+ *   KDA_F_QK_L2NORM      q, k are normalised per token and head in-kernel:
+ *                        x^ = x * (sum x^2 + 1e-6)^(-1/2)
+ *   KDA_F_GATE_IN_KERNEL the `g` argument holds f; the log-decay is
+ *                        g = -exp(A_log[h]) * softplus(f + dt_bias[h][c]),
+ *                        softplus(x) = log1p(exp(x)) (x <= 20), x (x > 20)
+ *   KDA_F_BETA_LOGITS    the `beta` argument holds logits b; beta = sigmoid(b) */
+enum {
+    KDA_F_QK_L2NORM = 1u << 0,
+    KDA_F_GATE_IN_KERNEL = 1u << 1,
+    KDA_F_BETA_LOGITS = 1u << 2
+};
+
+/* Problem descriptor.
+ *   B      rows (B == 1 when packed)
+ *   T      tokens per row (dense) or total tokens of the packed row; T >= 0
+ *   H      heads (one head count for q, k and v: Primus guide, Overview)
+ *   dk,dv  head dims; supported pairs (32,64), (64,64), (128,128)
+ *   N      sequences: == B when dense, number of documents when packed
+ *   chunk  chunk length, must be 64
+ *   dtype      element type of q, k, v (and d_o in kda_bwd)
+ *   out_dtype  element type of o (kda_fwd) and dq, dk, dv (kda_bwd); bf16
+ *              outputs are the round-to-nearest-even of the fp32 result
+ *   scale  output scale (the caller passes dk^-0.5 for the usual choice)
+ *   flags  KDA_F_* above */
+typedef struct kda_desc {
+    int32_t B, T, H, dk, dv, N, chunk;
+    kda_dtype dtype;
+    kda_dtype out_dtype;
+    float scale;
+    uint32_t flags;
+} kda_desc;
+
+/* Host-only upper bound on the number of chunks that N documents totalling T
+ * tokens can have: floor((T + N*(chunk-1)) / chunk).  Returns -1 on bad
+ * arguments.  Size chunk_indices for kda_plan_varlen with it. */
+int32_t kda_max_chunks(int32_t T, int32_t N, int32_t chunk);
+
+/* Per-document chunk metadata for a packed row (torchtitan PR #4347: the
+ * offsets are turned into chunk tables once per batch and shared by every
+ * layer, forward and backward).  Device inputs/outputs:
+ *   cu_seqlens     int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T
+ *                  (a precondition, not checked on the device path; see
+ *                  kda_check_cu_seqlens)
+ *   chunk_indices  int32 [kda_max_chunks(T,N,chunk)][2], rows (doc n, chunk i)
+ *                  for n ascending and i = 0..ceil(L_n/chunk)-1; rows past the
+ *                  real count are filled with (-1,-1)
+ *   chunk_offsets  int32 [N+1], exclusive prefix sum of ceil(L_n/chunk)
+ * Chunk (n,i) covers tokens [cu[n] + i*chunk, min(cu[n] + (i+1)*chunk, cu[n+1])):
+ * chunks restart at each document, so a packed document is tiled exactly as
+ * it is when run alone.  No host synchronisation. */
+int kda_plan_varlen(const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t chunk,
+                    int32_t* chunk_indices, int32_t* chunk_offsets, kda_stream_t stream);
+
+/* Debug check of device cu_seqlens (cu[0] == 0, non-decreasing, cu[N] == T).
+ * SYNCHRONISES the stream and copies N+1 ints to the host.  Returns KDA_OK or
+ * KDA_ERR_INVALID. */
+int kda_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, kda_stream_t stream);
+
+/* Workspace bytes needed by kda_fwd / kda_bwd for this descriptor (0 if the
+ * descriptor is invalid; kda_last_error says why). */
+size_t kda_fwd_workspace(const kda_desc* desc);
+size_t kda_bwd_workspace(const kda_desc* desc);
+
+/* Forward.
+ *   q, k        [B,T,H,dk] dtype  (raw if KDA_F_QK_L2NORM)
+ *   v           [B,T,H,dv] dtype
+ *   g           [B,T,H,dk] fp32 log-decay (f if KDA_F_GATE_IN_KERNEL)
+ *   beta        [B,T,H]    fp32 (logits if KDA_F_BETA_LOGITS)
+ *   A_log       [H] fp32, dt_bias [H,dk] fp32: required iff KDA_F_GATE_IN_KERNEL
+ *   h0          [N,H,dk,dv] fp32 initial states, nullable (= 0)
+ *   cu_seqlens, chunk_indices, chunk_offsets: all null (dense) or all set
+ *               (packed; B == 1; tables from kda_plan_varlen)
+ *   o           [B,T,H,dv] out_dtype
+ *   hT          [N,H,dk,dv] fp32 final states, nullable
+ *   ws, ws_bytes  workspace of at least kda_fwd_workspace(desc) bytes */
+int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+            const int32_t* cu_seqlens, const int32_t* chunk_indices,
+            const int32_t* chunk_offsets, void* o, float* hT, void* ws, size_t ws_bytes,
+            kda_stream_t stream);
+
+/* Backward of kda_fwd with respect to every input it was given.
+ *   inputs as kda_fwd, plus
+ *   d_o         [B,T,H,dv] dtype upstream gradient of o
+ *   dhT         [N,H,dk,dv] fp32 upstream gradient of hT, nullable (= 0)
+ *   dq, dk      [B,T,H,dk] out_dtype   (w.r.t. raw q, k if KDA_F_QK_L2NORM)
+ *   dv          [B,T,H,dv] out_dtype
+ *   dg          [B,T,H,dk] fp32        (w.r.t. f if KDA_F_GATE_IN_KERNEL)
+ *   dbeta       [B,T,H]    fp32        (w.r.t. logits if KDA_F_BETA_LOGITS)
+ *   dh0         [N,H,dk,dv] fp32, nullable
+ *   dA_log [H], ddt_bias [H,dk] fp32: required iff KDA_F_GATE_IN_KERNEL;
+ *               sums over all tokens, reduced in a fixed order (deterministic)
+ *   ws, ws_bytes  workspace of at least kda_bwd_workspace(desc) bytes */
+int kda_bwd(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+            const int32_t* cu_seqlens, const int32_t* chunk_indices,
+            const int32_t* chunk_offsets, const void* d_o, const float* dhT, void* dq, void* dk,
+            void* dv, float* dg, float* dbeta, float* dh0, float* dA_log, float* ddt_bias,
+            void* ws, size_t ws_bytes, kda_stream_t stream);
+
+/* One-token recurrent decode for B sequences (one iteration of the token
+ * recurrence above; FlashKDA is the inference-only prior art named in the
+ * openkimi README's FlashQLA paragraph).
+ *   q, k   [B,H,dk] dtype (raw if KDA_F_QK_L2NORM); v [B,H,dv] dtype
+ *   g      [B,H,dk] fp32 (f if KDA_F_GATE_IN_KERNEL); beta [B,H] fp32
+ *   A_log, dt_bias as in kda_fwd
+ *   h      [B,H,dk,dv] fp32 state, updated IN PLACE
+ *   o      [B,H,dv] out_dtype, = scale * h_new^T q */
+int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_dtype out_dtype,
+             float scale, uint32_t flags, const void* q, const void* k, const void* v,
+             const float* g, const float* beta, const float* A_log, const float* dt_bias,
+             float* h, void* o, kda_stream_t stream);
+
+/* Static text for a status code, and the thread-local message of the last
+ * failing call on this thread ("" if none). */
+const char* kda_status_str(int status);
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

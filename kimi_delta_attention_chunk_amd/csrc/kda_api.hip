@@ -1,0 +1,261 @@
+// kda_api.hip -- the extern "C" entry points declared in include/kda.h.
+//
+// Every call validates its arguments from the descriptor and the pointer
+// values alone (no device reads, no synchronisation), then enqueues its
+// kernels on the caller's stream.  On an error nothing is launched and the
+// thread-local message returned by kda_last_error() says what was wrong.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name, bool required) {
+    if (p == nullptr) return required ? fail(KDA_ERR_INVALID, "%s must not be null", name) : KDA_OK;
+    if (!aligned16(p)) return fail(KDA_ERR_INVALID, "%s is not 16-byte aligned", name);
+    return KDA_OK;
+}
+
+bool dtype_ok(int d) { return d == KDA_BF16 || d == KDA_FP32; }
+
+const uint32_t kKnownFlags = KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS;
+
+int validate_desc(const kda_desc* d) {
+    if (d == nullptr) return fail(KDA_ERR_INVALID, "desc must not be null");
+    if (d->B < 1 || d->T < 0 || d->H < 1 || d->N < 1)
+        return fail(KDA_ERR_INVALID, "bad sizes B=%d T=%d H=%d N=%d", d->B, d->T, d->H, d->N);
+    if (d->dk < 1 || d->dv < 1) return fail(KDA_ERR_INVALID, "bad head dims dk=%d dv=%d", d->dk, d->dv);
+    if (!kda::dims_supported(d->dk, d->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "head dims (dk=%d, dv=%d) not supported; use (32,64), (64,64) or (128,128)",
+                    d->dk, d->dv);
+    if (d->chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk=%d not supported (64 only)", d->chunk);
+    if (!dtype_ok(d->dtype) || !dtype_ok(d->out_dtype)) return fail(KDA_ERR_INVALID, "bad dtype");
+    if (d->flags & ~kKnownFlags) return fail(KDA_ERR_INVALID, "unknown flag bits 0x%x", d->flags & ~kKnownFlags);
+    if ((int64_t)d->B * d->T > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "B*T exceeds 2^31-1 tokens");
+    if ((int64_t)d->B * d->T * d->H * (d->dk > d->dv ? d->dk : d->dv) > ((int64_t)1 << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
+    return KDA_OK;
+}
+
+// Fill the parts of ChunkArgs that come from the descriptor and the varlen tables.
+int make_args(const kda_desc* d, const int32_t* cu, const int32_t* cidx, const int32_t* coff,
+              kda::ChunkArgs& a) {
+    int rc = validate_desc(d);
+    if (rc) return rc;
+    const bool packed = cu != nullptr || cidx != nullptr || coff != nullptr;
+    if (packed) {
+        if (!cu || !cidx || !coff)
+            return fail(KDA_ERR_INVALID, "packed rows need cu_seqlens, chunk_indices and chunk_offsets together");
+        if (d->B != 1) return fail(KDA_ERR_INVALID, "packed rows require B == 1 (got B=%d)", d->B);
+        if ((rc = check_ptr(cu, "cu_seqlens", true)) || (rc = check_ptr(cidx, "chunk_indices", true)) ||
+            (rc = check_ptr(coff, "chunk_offsets", true)))
+            return rc;
+    } else if (d->N != d->B) {
+        return fail(KDA_ERR_INVALID, "dense rows require N == B (got N=%d, B=%d)", d->N, d->B);
+    }
+    memset(&a, 0, sizeof a);
+    a.B = d->B; a.T = d->T; a.H = d->H; a.dk = d->dk; a.dv = d->dv; a.N = d->N;
+    a.in_bf16 = d->dtype == KDA_BF16;
+    a.out_bf16 = d->out_dtype == KDA_BF16;
+    a.scale = d->scale;
+    a.flags = d->flags;
+    a.cu = cu; a.cidx = cidx; a.coff = coff;
+    if (packed) {
+        a.nc_dense = 0;
+        a.n_chunks_bound = kda_max_chunks(d->T, d->N, d->chunk);
+    } else {
+        a.nc_dense = (d->T + d->chunk - 1) / d->chunk;
+        a.n_chunks_bound = a.nc_dense * d->B;
+    }
+    return KDA_OK;
+}
+
+// Sizes for the workspace queries: N != B means packed rows (B must be 1);
+// a single packed document has the same chunk bound as one dense row.
+int ws_args(const kda_desc* d, kda::ChunkArgs& a) {
+    int rc = validate_desc(d);
+    if (rc) return rc;
+    const bool packed = d->N != d->B;
+    if (packed && d->B != 1) return fail(KDA_ERR_INVALID, "packed rows require B == 1 (got B=%d)", d->B);
+    memset(&a, 0, sizeof a);
+    a.B = d->B; a.T = d->T; a.H = d->H; a.dk = d->dk; a.dv = d->dv; a.N = d->N;
+    a.nc_dense = (d->T + d->chunk - 1) / d->chunk;
+    a.n_chunks_bound = packed ? kda_max_chunks(d->T, d->N, d->chunk) : a.nc_dense * d->B;
+    return KDA_OK;
+}
+
+int check_common_inputs(const kda_desc* d, const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* A_log, const float* dt_bias, const float* h0) {
+    int rc;
+    if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+        (rc = check_ptr(g, "g", true)) || (rc = check_ptr(beta, "beta", true)) || (rc = check_ptr(h0, "h0", false)))
+        return rc;
+    const bool gate = d->flags & KDA_F_GATE_IN_KERNEL;
+    if ((rc = check_ptr(A_log, "A_log", gate)) || (rc = check_ptr(dt_bias, "dt_bias", gate))) return rc;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_str(int s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+const char* kda_last_error(void) { return g_err; }
+
+int32_t kda_max_chunks(int32_t T, int32_t N, int32_t chunk) {
+    if (T < 0 || N < 0 || chunk < 1) return -1;
+    const int64_t m = ((int64_t)T + (int64_t)N * (chunk - 1)) / chunk;
+    return m > INT32_MAX ? -1 : (int32_t)m;
+}
+
+int kda_plan_varlen(const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t chunk,
+                    int32_t* chunk_indices, int32_t* chunk_offsets, kda_stream_t stream) {
+    g_err[0] = 0;
+    if (N < 1 || T < 0) return fail(KDA_ERR_INVALID, "bad sizes N=%d T=%d", N, T);
+    if (chunk < 1) return fail(KDA_ERR_INVALID, "bad chunk %d", chunk);
+    int rc;
+    if ((rc = check_ptr(cu_seqlens, "cu_seqlens", true)) || (rc = check_ptr(chunk_offsets, "chunk_offsets", true)))
+        return rc;
+    const int32_t mc = kda_max_chunks(T, N, chunk);
+    if (mc < 0) return fail(KDA_ERR_INVALID, "chunk bound overflows");
+    if (mc > 0 && (rc = check_ptr(chunk_indices, "chunk_indices", true))) return rc;
+    hipError_t e = kda::launch_plan(cu_seqlens, N, T, chunk, mc, chunk_indices, chunk_offsets, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, kda_stream_t stream) {
+    g_err[0] = 0;
+    if (N < 1 || cu_seqlens == nullptr) return fail(KDA_ERR_INVALID, "bad arguments");
+    int32_t* host = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N + 1));
+    if (!host) return fail(KDA_ERR_INVALID, "host allocation failed");
+    hipError_t e = hipMemcpyAsync(host, cu_seqlens, sizeof(int32_t) * (size_t)(N + 1), hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) { free(host); return fail(KDA_ERR_HIP, "copy: %s", hipGetErrorString(e)); }
+    int rc = KDA_OK;
+    if (host[0] != 0) rc = fail(KDA_ERR_INVALID, "cu_seqlens[0] = %d, expected 0", host[0]);
+    for (int i = 0; rc == KDA_OK && i < N; ++i)
+        if (host[i + 1] < host[i]) rc = fail(KDA_ERR_INVALID, "cu_seqlens decreases at %d", i);
+    if (rc == KDA_OK && host[N] != T) rc = fail(KDA_ERR_INVALID, "cu_seqlens[N] = %d, expected T = %d", host[N], T);
+    free(host);
+    return rc;
+}
+
+size_t kda_fwd_workspace(const kda_desc* desc) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    if (ws_args(desc, a)) return 0;
+    return kda::ws_layout(a, false).total;
+}
+
+size_t kda_bwd_workspace(const kda_desc* desc) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    if (ws_args(desc, a)) return 0;
+    return kda::ws_layout(a, true).total;
+}
+
+int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+            const int32_t* cu_seqlens, const int32_t* chunk_indices, const int32_t* chunk_offsets,
+            void* o, float* hT, void* ws, size_t ws_bytes, kda_stream_t stream) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
+    if (rc) return rc;
+    if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
+    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(hT, "hT", false))) return rc;
+    const size_t need = kda::ws_layout(a, false).total;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0;
+    a.o = o; a.hT = hT; a.ws = ws; a.ws_bytes = ws_bytes;
+    hipError_t e = kda::launch_fwd(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_bwd(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+            const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+            const int32_t* cu_seqlens, const int32_t* chunk_indices, const int32_t* chunk_offsets,
+            const void* d_o, const float* dhT, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+            float* dh0, float* dA_log, float* ddt_bias, void* ws, size_t ws_bytes, kda_stream_t stream) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
+    if (rc) return rc;
+    if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
+    const bool gate = desc->flags & KDA_F_GATE_IN_KERNEL;
+    if ((rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dhT, "dhT", false)) ||
+        (rc = check_ptr(dq, "dq", true)) || (rc = check_ptr(dk, "dk", true)) || (rc = check_ptr(dv, "dv", true)) ||
+        (rc = check_ptr(dg, "dg", true)) || (rc = check_ptr(dbeta, "dbeta", true)) ||
+        (rc = check_ptr(dh0, "dh0", false)) || (rc = check_ptr(dA_log, "dA_log", gate)) ||
+        (rc = check_ptr(ddt_bias, "ddt_bias", gate)))
+        return rc;
+    const size_t need = kda::ws_layout(a, true).total;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0;
+    a.d_o = d_o; a.dhT = dhT; a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.dA_log = dA_log; a.ddt_bias = ddt_bias; a.ws = ws; a.ws_bytes = ws_bytes;
+    hipError_t e = kda::launch_bwd(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_dtype out_dtype, float scale,
+             uint32_t flags, const void* q, const void* k, const void* v, const float* g, const float* beta,
+             const float* A_log, const float* dt_bias, float* h, void* o, kda_stream_t stream) {
+    g_err[0] = 0;
+    if (B < 1 || H < 1) return fail(KDA_ERR_INVALID, "bad sizes B=%d H=%d", B, H);
+    if ((int64_t)B * H > INT32_MAX / 2) return fail(KDA_ERR_UNSUPPORTED, "B*H too large");
+    if (!kda::dims_supported(dk, dv))
+        return fail(KDA_ERR_UNSUPPORTED, "head dims (dk=%d, dv=%d) not supported", dk, dv);
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return fail(KDA_ERR_INVALID, "bad dtype");
+    if (flags & ~kKnownFlags) return fail(KDA_ERR_INVALID, "unknown flag bits");
+    int rc;
+    const bool gate = flags & KDA_F_GATE_IN_KERNEL;
+    if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
+        (rc = check_ptr(g, "g", true)) || (rc = check_ptr(beta, "beta", true)) || (rc = check_ptr(h, "h", true)) ||
+        (rc = check_ptr(o, "o", true)) || (rc = check_ptr(A_log, "A_log", gate)) ||
+        (rc = check_ptr(dt_bias, "dt_bias", gate)))
+        return rc;
+    kda::StepArgs a;
+    a.B = B; a.H = H; a.dk = dk; a.dv = dv;
+    a.in_bf16 = dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.scale = scale; a.flags = flags;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias; a.h = h; a.o = o;
+    hipError_t e = kda::launch_step(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "step launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,203 @@
+// kda_chunk.cuh -- staging and in-chunk algebra shared by the forward and
+// backward chunk kernels.
+//
+// The chunked form is the exact algebraic rewrite of the token recurrence
+// over a chunk of L <= 64 tokens entering with state h (the pages name the
+// chunked FLA kernels -- Primus guide, the autotune paragraph of the training
+// step; openkimi README, What is implemented -- but print no formulas; these
+// are derived from the recurrence):
+//   G_t      = sum_{s<=t} g_s                          (in-chunk, per channel)
+//   Akk[t,s] = beta_t sum_c k_tc k_sc exp(G_tc - G_sc)     s <  t
+//   Aqk[t,s] =        sum_c q_tc k_sc exp(G_tc - G_sc)     s <= t
+//   T        = (I + Akk)^{-1}                          (unit lower triangular)
+//   w = T Diag(beta) (exp(G) . K),   u = T Diag(beta) V
+//   v_new    = u - w h
+//   o        = scale ((exp(G) . Q) h + Aqk v_new)
+//   h'       = Diag(exp(G_L)) h + (K . exp(G_L - G))^T v_new
+// Decay factors are only ever formed as exp of a non-positive difference
+// G_t - G_s (t >= s), so nothing overflows; the cumulative sum restarts at
+// every chunk.
+//
+// LDS layout: per-chunk token tiles are stored transposed, X^T[c][t] with a
+// padded row stride kLD, so a wave reading one channel for 64 tokens hits 64
+// consecutive words.
+#pragma once
+
+#include "kda_device.cuh"
+
+namespace kda {
+
+constexpr int kLD = kChunk + 4;  // padded stride of [channel][token] tiles
+
+// Kernel parameters (device view of one call).
+struct Prm {
+    int B, T, H, N;
+    float scale;
+    uint32_t flags;
+    SeqLayout seq;
+    const void *q, *k, *v;
+    const float *g, *beta, *A_log, *dt_bias, *h0;
+    void* o;
+    float* hT;
+    const void* d_o;
+    const float* dhT;
+    void *dq, *dk, *dv;
+    float *dg, *dbeta, *dh0;
+    // workspace arrays (fp32), indexed by slot = chunk * H + head
+    float *w, *u, *aqk, *hs, *vn, *dhs, *dvn, *part_a, *part_dt;
+};
+
+__device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
+    return ((size_t)t * H + h) * d;
+}
+
+// Stage q or k of one chunk into XT[c][t] (zero past the chunk end), and
+// L2-normalise every token if `l2`.  Ends with a barrier.
+template <int DK, typename TIn>
+__device__ void stage_qk(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, bool l2,
+                         float* XT, float* rnorm /* [64] scratch, nullable if !l2 */) {
+    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+        const int t = e / DK, c = e - t * DK;
+        float x = 0.f;
+        if (t < cr.len) x = Elem<TIn>::load(src, tok_index(cr.t0 + t, h, H, DK) + c);
+        XT[c * kLD + t] = x;
+    }
+    __syncthreads();
+    if (l2) {
+        if (threadIdx.x < kChunk) {
+            const int t = threadIdx.x;
+            float ss = 0.f;
+            for (int c = 0; c < DK; ++c) ss += XT[c * kLD + t] * XT[c * kLD + t];
+            rnorm[t] = 1.0f / sqrtf(ss + kL2Eps);
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+            const int c = e / kChunk, t = e - c * kChunk;
+            XT[c * kLD + t] *= rnorm[t];
+        }
+        __syncthreads();
+    }
+}
+
+// Stage the log-decay of one chunk (computing the gate from f if the gate
+// flag is set) and turn it into the in-chunk cumulative sum GT[c][t].  Past
+// the chunk end g = 0, so G stays at G_{L-1}.  Optionally also stages beta
+// (sigmoid of logits if flagged; 0 past the end).  Ends with a barrier.
+template <int DK>
+__device__ void stage_g(const Prm& p, const ChunkRef& cr, int h, float* GT, float* bet) {
+    const bool gate = p.flags & 2u;
+    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+        const int t = e / DK, c = e - t * DK;
+        float x = 0.f;
+        if (t < cr.len) {
+            x = p.g[tok_index(cr.t0 + t, h, p.H, DK) + c];
+            if (gate) x = -expf(p.A_log[h]) * softplus_f(x + p.dt_bias[h * DK + c]);
+        }
+        GT[c * kLD + t] = x;
+    }
+    if (bet != nullptr && threadIdx.x < kChunk) {
+        const int t = threadIdx.x;
+        float b = 0.f;
+        if (t < cr.len) {
+            b = p.beta[(size_t)(cr.t0 + t) * p.H + h];
+            if (p.flags & 4u) b = sigmoid_f(b);
+        }
+        bet[t] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x < DK) {
+        const int c = threadIdx.x;
+        float acc = 0.f;
+        for (int t = 0; t < kChunk; ++t) {
+            acc += GT[c * kLD + t];
+            GT[c * kLD + t] = acc;
+        }
+    }
+    __syncthreads();
+}
+
+// Pairwise decayed Gram matrices of one chunk (exact exp of each difference):
+//   A[t][s]  = beta_t sum_c K_tc K_sc e^{G_tc-G_sc}   (s < t, else 0)
+//   Aq(t,s)  =        sum_c Q_tc K_sc e^{G_tc-G_sc}   (s <= t, else 0), passed to `aq_out`
+// Each wave owns one row t at a time; its lanes run over s.
+template <int DK, class AqOut>
+__device__ void gram_pairwise(const float* KT, const float* QT, const float* GT, const float* bet,
+                              float* A, AqOut aq_out) {
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        const int t = e >> 6, s = e & 63;
+        float akk = 0.f, aqk = 0.f;
+        if (s <= t) {
+            for (int c = 0; c < DK; ++c) {
+                const float ex = __expf(GT[c * kLD + t] - GT[c * kLD + s]);
+                const float ks = KT[c * kLD + s] * ex;
+                akk += KT[c * kLD + t] * ks;
+                if (QT) aqk += QT[c * kLD + t] * ks;
+            }
+        }
+        A[t * kLD + s] = (s < t) ? bet[t] * akk : 0.f;
+        aq_out(t, s, (s <= t) ? aqk : 0.f);
+    }
+}
+
+// T = (I + A)^{-1} for strictly lower-triangular A (64x64, stride kLD), by
+// 16x16 blocks: diagonal blocks by forward substitution (one wave per block,
+// one lane per column), then the off-diagonal blocks level by level,
+//   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
+// X is scratch of 4*16*kLD16 floats.  Starts and ends with barriers.
+constexpr int kLD16 = 20;
+__device__ void solve_unit_lower(const float* A, float* Tm, float* X) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // zero the strict upper part and diagonal blocks are filled below
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        const int t = e >> 6, s = e & 63;
+        if ((s >> 4) > (t >> 4)) Tm[t * kLD + s] = 0.f;
+    }
+    {
+        const int I = wave;  // 4 waves <-> 4 diagonal blocks
+        if (lane < 16) {
+            const int j = lane;
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float acc = (t == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < t; ++m) acc -= A[(16 * I + t) * kLD + 16 * I + m] * x[m];
+                x[t] = acc;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) Tm[(16 * I + t) * kLD + 16 * I + j] = x[t];
+        }
+    }
+    __syncthreads();
+    for (int lvl = 1; lvl < 4; ++lvl) {
+        // blocks (I, J = I - lvl), I = lvl..3; one wave each
+        const int I = lvl + wave, J = wave;
+        const bool active = I < 4;
+        // X_w = sum_{K=J}^{I-1} A_IK T_KJ
+        if (active) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma16_f32(A + (16 * I) * kLD, kLD, 1, Tm + 16 * J, kLD, 1, 16 * J, 16 * I, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[wave * 16 * kLD16 + (4 * (lane >> 4) + i) * kLD16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+        if (active) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma16_f32(Tm + (16 * I) * kLD + 16 * I, kLD, 1, X + wave * 16 * kLD16, kLD16, 1, 0, 16, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tm[(16 * I + 4 * (lane >> 4) + i) * kLD + 16 * J + (lane & 15)] = -acc[i];
+        }
+        __syncthreads();
+    }
+}
+
+// Lower-triangular k-range for products T * X (T zero above the diagonal blocks).
+struct TriK {
+    __device__ __forceinline__ void operator()(int tm, int, int& k0, int& k1) const { k0 = 0; k1 = 16 * (tm + 1); }
+};
+// Upper-triangular k-range for products T^T * X (rows of T^T are zero left of the block).
+struct TriKUpper {
+    __device__ __forceinline__ void operator()(int tm, int, int& k0, int& k1) const { k0 = 16 * tm; k1 = kChunk; }
+};
+
+}  // namespace kda

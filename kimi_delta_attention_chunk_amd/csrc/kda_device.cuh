@@ -1,0 +1,144 @@
+// kda_device.cuh -- device helpers shared by the gfx950 KDA kernels.
+//
+// Wave64 everywhere.  Matrix products use the CDNA MFMA 16x16 tiles:
+//   v_mfma_f32_16x16x4_f32 : A 16x4, B 4x16, C/D 16x16, fp32 in and out.
+// Operand layout for one wave (lane l = 0..63):
+//   A fragment: element (row = l & 15, k = l >> 4)
+//   B fragment: element (k = l >> 4, col = l & 15)
+//   D fragment: four floats, rows 4*(l >> 4) + i (i = 0..3), col = l & 15.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;     // chunk length (tokens)
+constexpr int kThreads = 256;  // threads per workgroup of the chunk kernels
+constexpr int kWaves = kThreads / 64;
+constexpr float kL2Eps = 1e-6f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+    return __uint_as_float(((uint32_t)u) << 16);
+}
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+    __device__ __forceinline__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+// ----------------------------------------------------------------- prep math
+// softplus with the usual threshold: x for x > 20.
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float dsoftplus_f(float x) { return x > 20.f ? 1.f : 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// ----------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// ----------------------------------------------------------------- MFMA fp32 tiles
+// acc(16x16) += A(16 x K) * B(K x 16) over k in [k0, k1), k1 - k0 a multiple of 4.
+// A(m,k) = A[m*am + k*ak], B(k,n) = B[k*bk + n*bn]; pointers at the tile origin.
+__device__ __forceinline__ f32x4 mma16_f32(const float* A, int am, int ak, const float* B, int bk,
+                                           int bn, int k0, int k1, f32x4 acc) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    for (int k = k0; k < k1; k += 4) {
+        const float a = A[r * am + (k + kq) * ak];
+        const float b = B[(k + kq) * bk + r * bn];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Workgroup GEMM over 16x16 output tiles, tiles dealt round-robin to waves.
+//   out(m,n) = sum_k A(m,k) B(k,n), M x N x K, all multiples of 16 (K of 4).
+// `krange(tm, tn, &k0, &k1)` may narrow the k range of a tile (triangular
+// operands); `epi(m, n, value)` consumes each result element.
+template <int M, int N, class KRange, class Epi>
+__device__ __forceinline__ void wg_gemm(const float* A, int am, int ak, const float* B, int bk,
+                                        int bn, int K, KRange krange, Epi epi) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int TN = N / 16, TILES = (M / 16) * (N / 16);
+    for (int tile = wave; tile < TILES; tile += kWaves) {
+        const int tm = tile / TN, tn = tile % TN;
+        int k0 = 0, k1 = K;
+        krange(tm, tn, k0, k1);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (k1 > k0) acc = mma16_f32(A + tm * 16 * am, am, ak, B + tn * 16 * bn, bk, bn, k0, k1, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) epi(tm * 16 + 4 * (lane >> 4) + i, tn * 16 + (lane & 15), acc[i]);
+    }
+}
+
+struct FullK {
+    __device__ __forceinline__ void operator()(int, int, int&, int&) const {}
+};
+
+// ----------------------------------------------------------------- chunk addressing
+// A chunk is a run of at most kChunk tokens of one sequence.  Dense rows:
+// sequence n = row b, chunk i covers tokens [i*64, min(i*64+64, T)) of that
+// row.  Packed rows: chunk c is (doc n, i) = chunk_indices[c], covering
+// [cu[n] + i*64, min(cu[n] + i*64 + 64, cu[n+1])).  The global token index
+// (into the [B*T] token axis) is returned in t0.
+struct ChunkRef {
+    int n;      // sequence
+    int i;      // chunk index within the sequence
+    int64_t t0; // first token (global)
+    int len;    // tokens in the chunk, 1..64 (0 = no such chunk)
+};
+
+struct SeqLayout {
+    int B, T, N;
+    const int32_t* cu;       // null when dense
+    const int32_t* cidx;     // [max,2]
+    const int32_t* coff;     // [N+1]
+    int nc_dense;            // chunks per row when dense
+
+    __device__ __forceinline__ ChunkRef chunk(int c) const {
+        ChunkRef r;
+        if (cu == nullptr) {
+            r.n = c / nc_dense;
+            r.i = c - r.n * nc_dense;
+            if (r.n >= B) { r.len = 0; r.t0 = 0; return r; }
+            r.t0 = (int64_t)r.n * T + (int64_t)r.i * kChunk;
+            const int rem = T - r.i * kChunk;
+            r.len = rem < kChunk ? rem : kChunk;
+        } else {
+            if (c >= coff[N]) { r.n = 0; r.i = 0; r.len = 0; r.t0 = 0; return r; }
+            r.n = cidx[2 * c];
+            r.i = cidx[2 * c + 1];
+            const int s = cu[r.n] + r.i * kChunk;
+            const int rem = cu[r.n + 1] - s;
+            r.t0 = s;
+            r.len = rem < kChunk ? rem : kChunk;
+        }
+        return r;
+    }
+    // Range of global chunk ids belonging to sequence n.
+    __device__ __forceinline__ void seq_chunks(int n, int& c0, int& c1) const {
+        if (cu == nullptr) { c0 = n * nc_dense; c1 = c0 + nc_dense; }
+        else { c0 = coff[n]; c1 = coff[n + 1]; }
+    }
+};
+
+}  // namespace kda

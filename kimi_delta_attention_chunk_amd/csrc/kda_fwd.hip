@@ -1,0 +1,287 @@
+// kda_fwd.hip -- chunked forward: intra-chunk, inter-chunk state passing, output.
+//
+// Three launches per call (the in-chunk algebra is in kda_chunk.cuh):
+//   fwd_intra   one workgroup per (chunk, head): gate preparation, in-chunk
+//               cumulative decay, Gram matrices, UT inverse, w and u, Aqk;
+//   fwd_state   one workgroup per (sequence, head, 32-column block of dv):
+//               the only sequential part, chunk after chunk with the fp32
+//               state in LDS; stores the state entering every chunk and v_new;
+//   fwd_output  one workgroup per (chunk, head, column block): o.
+// All products are fp32 MFMA (v_mfma_f32_16x16x4_f32); decays are exact.
+#include "kda_chunk.cuh"
+#include "kda_internal.h"
+
+namespace kda {
+
+// Logical workgroup id such that consecutive logical ids run on the same XCD
+// (hardware deals workgroups round-robin over the 8 XCDs, each with its own
+// L2).  Identity when the grid is not a multiple of 8.
+__device__ __forceinline__ int xcd_local_id(int wg, int total) {
+    if ((total & 7) != 0) return wg;
+    return (wg & 7) * (total >> 3) + (wg >> 3);
+}
+
+// ============================================================== intra-chunk
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kThreads) fwd_intra_kernel(Prm p) {
+    constexpr int DX = DK > DV ? DK : DV;
+    __shared__ float KT[DK * kLD];
+    __shared__ float GT[DK * kLD];
+    __shared__ float QVT[DX * kLD];  // q during the Gram, then beta*v
+    __shared__ float A[kChunk * kLD];
+    __shared__ float Tm[kChunk * kLD];
+    __shared__ float X[4 * 16 * kLD16];
+    __shared__ float bet[kChunk];
+    __shared__ float rn[kChunk];
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const ChunkRef cr = p.seq.chunk(c);
+    if (cr.len == 0) return;
+    const size_t slot = (size_t)c * p.H + h;
+    const bool l2 = p.flags & 1u;
+
+    stage_qk<DK, TIn>((const TIn*)p.k, cr, h, p.H, l2, KT, rn);
+    stage_qk<DK, TIn>((const TIn*)p.q, cr, h, p.H, l2, QVT, rn);
+    stage_g<DK>(p, cr, h, GT, bet);
+
+    float* aq = p.aqk + slot * kChunk * kChunk;
+    gram_pairwise<DK>(KT, QVT, GT, bet, A, [&](int t, int s, float x) { aq[t * kChunk + s] = x; });
+    __syncthreads();
+
+    // beta * v (into the q buffer) and beta * exp(G) * k (in place)
+    for (int e = threadIdx.x; e < kChunk * DV; e += kThreads) {
+        const int t = e / DV, j = e - t * DV;
+        float x = 0.f;
+        if (t < cr.len) x = Elem<TIn>::load((const TIn*)p.v, tok_index(cr.t0 + t, h, p.H, DV) + j);
+        QVT[j * kLD + t] = bet[t] * x;
+    }
+    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+        const int cc = e / kChunk, t = e - cc * kChunk;
+        KT[cc * kLD + t] *= bet[t] * __expf(GT[cc * kLD + t]);
+    }
+    solve_unit_lower(A, Tm, X);  // begins/ends with barriers
+
+    float* wo = p.w + slot * kChunk * DK;
+    float* uo = p.u + slot * kChunk * DV;
+    wg_gemm<kChunk, DK>(Tm, kLD, 1, KT, 1, kLD, kChunk, TriK(),
+                        [&](int t, int cc, float x) { wo[t * DK + cc] = x; });
+    wg_gemm<kChunk, DV>(Tm, kLD, 1, QVT, 1, kLD, kChunk, TriK(),
+                        [&](int t, int j, float x) { uo[t * DV + j] = x; });
+}
+
+// ============================================================== state passing
+constexpr int kBV = 32;  // state columns per workgroup
+
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kThreads) fwd_state_kernel(Prm p, int total_wg) {
+    constexpr int LS = kBV + 4;
+    __shared__ float S[DK * LS];        // state block, [c][j]
+    __shared__ float KhT[DK * kLD];     // k . exp(G_L - G), transposed
+    __shared__ float GT[DK * kLD];
+    __shared__ float WL[kChunk * (DK + 4)];
+    __shared__ float VN[kChunk * LS];
+    __shared__ float gL[DK];
+    __shared__ float rn[kChunk];
+
+    constexpr int NV = DV / kBV;
+    const int lid = xcd_local_id(blockIdx.x, total_wg);
+    const int vb = lid % NV;
+    const int nh = lid / NV;
+    const int n = nh / p.H, h = nh % p.H;
+    if (n >= p.N) return;
+    const int jb = vb * kBV;
+    const bool l2 = p.flags & 1u;
+
+    for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+        const int cc = e / kBV, j = e - cc * kBV;
+        S[cc * LS + j] = p.h0 ? p.h0[((size_t)nh * DK + cc) * DV + jb + j] : 0.f;
+    }
+    int c0, c1;
+    p.seq.seq_chunks(n, c0, c1);
+    for (int c = c0; c < c1; ++c) {
+        const ChunkRef cr = p.seq.chunk(c);
+        const size_t slot = (size_t)c * p.H + h;
+        __syncthreads();  // S of the previous chunk complete
+        stage_qk<DK, TIn>((const TIn*)p.k, cr, h, p.H, l2, KhT, rn);
+        stage_g<DK>(p, cr, h, GT, nullptr);
+        float* hs = p.hs + slot * DK * DV;
+        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+            const int cc = e / kBV, j = e - cc * kBV;
+            hs[cc * DV + jb + j] = S[cc * LS + j];
+        }
+        const int last = cr.len - 1;
+        for (int e = threadIdx.x; e < DK * kChunk; e += kThreads) {
+            const int cc = e / kChunk, t = e - cc * kChunk;
+            KhT[cc * kLD + t] *= __expf(GT[cc * kLD + last] - GT[cc * kLD + t]);
+        }
+        if (threadIdx.x < DK) gL[threadIdx.x] = __expf(GT[threadIdx.x * kLD + last]);
+        const float* wi = p.w + slot * kChunk * DK;
+        for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+            const int t = e / DK, cc = e - t * DK;
+            WL[t * (DK + 4) + cc] = wi[t * DK + cc];
+        }
+        __syncthreads();
+        // v_new = u - w S
+        const float* ui = p.u + slot * kChunk * DV;
+        float* vo = p.vn + slot * kChunk * DV;
+        wg_gemm<kChunk, kBV>(WL, DK + 4, 1, S, LS, 1, DK, FullK(), [&](int t, int j, float x) {
+            const float val = ui[t * DV + jb + j] - x;
+            VN[t * LS + j] = val;
+            vo[t * DV + jb + j] = val;
+        });
+        __syncthreads();
+        // S = Diag(exp G_L) S + Kh^T v_new
+        wg_gemm<DK, kBV>(KhT, kLD, 1, VN, LS, 1, kChunk, FullK(), [&](int cc, int j, float x) {
+            S[cc * LS + j] = gL[cc] * S[cc * LS + j] + x;
+        });
+    }
+    __syncthreads();
+    if (p.hT) {
+        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+            const int cc = e / kBV, j = e - cc * kBV;
+            p.hT[((size_t)nh * DK + cc) * DV + jb + j] = S[cc * LS + j];
+        }
+    }
+}
+
+// ============================================================== output
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads) fwd_output_kernel(Prm p) {
+    constexpr int OB = DV < 64 ? DV : 64;  // output columns per workgroup
+    constexpr int LO = OB + 4;
+    __shared__ float QT[DK * kLD];
+    __shared__ float GT[DK * kLD];
+    __shared__ float Hs[DK * LO];
+    __shared__ float VN[kChunk * LO];
+    __shared__ float AQ[kChunk * kLD];
+    __shared__ float rn[kChunk];
+
+    const int c = blockIdx.x, h = blockIdx.y, jb = blockIdx.z * OB;
+    const ChunkRef cr = p.seq.chunk(c);
+    if (cr.len == 0) return;
+    const size_t slot = (size_t)c * p.H + h;
+
+    stage_qk<DK, TIn>((const TIn*)p.q, cr, h, p.H, p.flags & 1u, QT, rn);
+    stage_g<DK>(p, cr, h, GT, nullptr);
+    const float* hs = p.hs + slot * DK * DV;
+    const float* vn = p.vn + slot * kChunk * DV;
+    const float* aq = p.aqk + slot * kChunk * kChunk;
+    for (int e = threadIdx.x; e < DK * OB; e += kThreads) {
+        const int cc = e / OB, j = e - cc * OB;
+        Hs[cc * LO + j] = hs[cc * DV + jb + j];
+    }
+    for (int e = threadIdx.x; e < kChunk * OB; e += kThreads) {
+        const int t = e / OB, j = e - t * OB;
+        VN[t * LO + j] = vn[t * DV + jb + j];
+    }
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        const int t = e >> 6, s = e & 63;
+        AQ[t * kLD + s] = aq[e];
+    }
+    for (int e = threadIdx.x; e < DK * kChunk; e += kThreads) {
+        const int cc = e / kChunk, t = e - cc * kChunk;
+        QT[cc * kLD + t] *= __expf(GT[cc * kLD + t]);
+    }
+    __syncthreads();
+    TOut* o = (TOut*)p.o;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int TN = OB / 16, TILES = (kChunk / 16) * TN;
+    for (int tile = wave; tile < TILES; tile += kWaves) {
+        const int tm = tile / TN, tn = tile % TN;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma16_f32(QT + tm * 16, 1, kLD, Hs + tn * 16, LO, 1, 0, DK, acc);
+        acc = mma16_f32(AQ + tm * 16 * kLD, kLD, 1, VN + tn * 16, LO, 1, 0, 16 * (tm + 1), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
+            if (t < cr.len) Elem<TOut>::store(o, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, p.scale * acc[i]);
+        }
+    }
+}
+
+// ============================================================== host side
+Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
+    Prm p{};
+    p.B = a.B; p.T = a.T; p.H = a.H; p.N = a.N;
+    p.scale = a.scale; p.flags = a.flags;
+    p.seq.B = a.B; p.seq.T = a.T; p.seq.N = a.N;
+    p.seq.cu = a.cu; p.seq.cidx = a.cidx; p.seq.coff = a.coff; p.seq.nc_dense = a.nc_dense;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
+    p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.h0 = a.h0;
+    p.o = a.o; p.hT = a.hT; p.d_o = a.d_o; p.dhT = a.dhT;
+    p.dq = a.dq; p.dk = a.dk_; p.dv = a.dv_; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
+    char* base = (char*)a.ws;
+    auto at = [&](size_t off) { return (float*)(base + off); };
+    p.w = at(L.w); p.u = at(L.u); p.aqk = at(L.aqk); p.hs = at(L.hs); p.vn = at(L.vn);
+    p.dhs = at(L.dhs); p.dvn = at(L.dvn); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
+    return p;
+}
+
+WsLayout ws_layout(const ChunkArgs& a, bool backward) {
+    WsLayout L{};
+    const size_t slots = (size_t)a.n_chunks_bound * a.H;
+    auto bytes = [](size_t n) { return (n * sizeof(float) + 255) & ~(size_t)255; };
+    size_t off = 0;
+    L.w = off; off += bytes(slots * kChunk * a.dk);
+    L.u = off; off += bytes(slots * kChunk * a.dv);
+    L.aqk = off; off += bytes(slots * kChunk * kChunk);
+    L.hs = off; off += bytes(slots * (size_t)a.dk * a.dv);
+    L.vn = off; off += bytes(slots * kChunk * a.dv);
+    if (backward) {
+        L.dhs = off; off += bytes(slots * (size_t)a.dk * a.dv);
+        L.dvn = off; off += bytes(slots * kChunk * a.dv);
+        L.part_a = off; off += bytes(slots);
+        L.part_dt = off; off += bytes(slots * a.dk);
+    } else {
+        L.dhs = L.dvn = L.part_a = L.part_dt = 0;
+    }
+    L.total = off;
+    return L;
+}
+
+bool dims_supported(int dk, int dv) {
+    return (dk == 32 && dv == 64) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128);
+}
+
+template <int DK, int DV, typename TIn>
+hipError_t launch_fwd_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
+    if (a.n_chunks_bound > 0) {
+        hipLaunchKernelGGL((fwd_intra_kernel<DK, DV, TIn>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int total = a.N * a.H * (DV / kBV);
+    hipLaunchKernelGGL((fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), 0, s, p, total);
+    return hipGetLastError();
+}
+template hipError_t launch_fwd_recompute<32, 64, float>(const Prm&, const ChunkArgs&, hipStream_t);
+
+template <int DK, int DV, typename TIn, typename TOut>
+static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
+    const WsLayout L = ws_layout(a, false);
+    const Prm p = make_prm(a, L);
+    hipError_t e = launch_fwd_recompute<DK, DV, TIn>(p, a, s);
+    if (e != hipSuccess || a.n_chunks_bound == 0) return e;
+    constexpr int OB = DV < 64 ? DV : 64;
+    hipLaunchKernelGGL((fwd_output_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H, DV / OB),
+                       dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_fwd_dims(const ChunkArgs& a, hipStream_t s) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_fwd_t<DK, DV, uint16_t, uint16_t>(a, s)
+                          : launch_fwd_t<DK, DV, uint16_t, float>(a, s);
+    return a.out_bf16 ? launch_fwd_t<DK, DV, float, uint16_t>(a, s)
+                      : launch_fwd_t<DK, DV, float, float>(a, s);
+}
+
+hipError_t launch_fwd(const ChunkArgs& a, hipStream_t s) {
+    if (a.dk == 32 && a.dv == 64) return launch_fwd_dims<32, 64>(a, s);
+    if (a.dk == 64 && a.dv == 64) return launch_fwd_dims<64, 64>(a, s);
+    if (a.dk == 128 && a.dv == 128) return launch_fwd_dims<128, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,60 @@
+// kda_internal.h -- host-side launch interface between the C ABI (kda_api.hip)
+// and the kernel files.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct StepArgs {
+    int B, H, dk, dv;
+    bool in_bf16, out_bf16;
+    float scale;
+    uint32_t flags;
+    const void *q, *k, *v;
+    const float *g, *beta, *A_log, *dt_bias;
+    float* h;
+    void* o;
+};
+hipError_t launch_step(const StepArgs& a, hipStream_t s);
+
+hipError_t launch_plan(const int32_t* cu, int N, int T, int chunk, int max_chunks,
+                       int32_t* chunk_indices, int32_t* chunk_offsets, hipStream_t s);
+
+// Everything a chunked forward/backward launch needs.
+struct ChunkArgs {
+    int B, T, H, dk, dv, N;
+    bool in_bf16, out_bf16;
+    float scale;
+    uint32_t flags;
+    int n_chunks_bound;  // grid size over chunks (exact when dense)
+    int nc_dense;        // chunks per row when dense
+    const int32_t *cu, *cidx, *coff;
+    const void *q, *k, *v;
+    const float *g, *beta, *A_log, *dt_bias, *h0;
+    // forward outputs
+    void* o;
+    float* hT;
+    // backward inputs / outputs
+    const void* d_o;
+    const float* dhT;
+    void *dq, *dk_, *dv_;
+    float *dg, *dbeta, *dh0, *dA_log, *ddt_bias;
+    // workspace
+    void* ws;
+    size_t ws_bytes;
+};
+
+// Workspace layout shared by the forward and backward launches.
+struct WsLayout {
+    size_t w, u, aqk, hs, vn, dhs, dvn, part_a, part_dt, total;
+};
+WsLayout ws_layout(const ChunkArgs& a, bool backward);
+
+bool dims_supported(int dk, int dv);
+hipError_t launch_fwd(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_bwd(const ChunkArgs& a, hipStream_t s);
+
+}  // namespace kda

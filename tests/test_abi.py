@@ -1,0 +1,128 @@
+"""Host-side checks of libkda.so: it loads, exports every function declared in
+include/kda.h, and rejects bad arguments before launching anything (no GPU
+needed: every call here returns from argument validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_chunk_amd as kda
+from kimi_delta_attention_chunk_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_max_chunks_formula():
+    lib = kda.load_library()
+    assert lib.kda_max_chunks(256, 2, 64) == (256 + 2 * 63) // 64
+    assert lib.kda_max_chunks(0, 1, 64) == 0
+    assert lib.kda_max_chunks(-1, 1, 64) == -1
+    assert lib.kda_max_chunks(10, 1, 0) == -1
+
+
+def _desc(**kw):
+    d = dict(B=1, T=128, H=1, dk=32, dv=64, N=1, chunk=64, dtype=B.KDA_FP32, out_dtype=B.KDA_FP32,
+             scale=0.1767767, flags=0)
+    d.update(kw)
+    return B.KdaDesc(**d)
+
+
+def _ws(desc, backward=False):
+    lib = kda.load_library()
+    return (lib.kda_bwd_workspace if backward else lib.kda_fwd_workspace)(ctypes.byref(desc))
+
+
+def test_workspace_sizes():
+    assert _ws(_desc()) > 0
+    assert _ws(_desc(), True) > _ws(_desc())
+    # packed row of 3 documents
+    assert _ws(_desc(N=3)) >= _ws(_desc())
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(dk=48), B.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=32), B.KDA_ERR_UNSUPPORTED),
+    (dict(T=-1), B.KDA_ERR_INVALID),
+    (dict(H=0), B.KDA_ERR_INVALID),
+    (dict(dtype=7), B.KDA_ERR_INVALID),
+    (dict(flags=1 << 9), B.KDA_ERR_INVALID),
+    (dict(B=2, N=3), B.KDA_ERR_INVALID),
+])
+def test_invalid_descriptor_rejected(bad, code):
+    lib = kda.load_library()
+    d = _desc(**bad)
+    assert _ws(d) == 0
+    fake = ctypes.c_void_p(0x10000)
+    rc = lib.kda_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, None, None, None,
+                     None, fake, None, fake, 1 << 40, None)
+    assert rc == code, lib.kda_last_error()
+    assert lib.kda_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = kda.load_library()
+    d = _desc()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
+    ws = _ws(d)
+    args = [fake] * 5 + [None, None, None, None, None, None, fake, None, fake, ws, None]
+    bad_null = list(args)
+    bad_null[0] = None
+    assert lib.kda_fwd(ctypes.byref(d), *bad_null) == B.KDA_ERR_INVALID
+    assert b"q must not be null" in lib.kda_last_error()
+    bad_al = list(args)
+    bad_al[2] = odd
+    assert lib.kda_fwd(ctypes.byref(d), *bad_al) == B.KDA_ERR_INVALID
+    assert b"aligned" in lib.kda_last_error()
+    small = list(args)
+    small[-2] = ws - 1
+    assert lib.kda_fwd(ctypes.byref(d), *small) == B.KDA_ERR_WORKSPACE
+    # gate in kernel needs A_log and dt_bias
+    dg = _desc(flags=B.F_GATE_IN_KERNEL)
+    assert lib.kda_fwd(ctypes.byref(dg), *args) == B.KDA_ERR_INVALID
+    assert b"A_log" in lib.kda_last_error()
+    # packed needs all three tables and B == 1
+    part = list(args)
+    part[8] = fake  # cu_seqlens only
+    assert lib.kda_fwd(ctypes.byref(d), *part) == B.KDA_ERR_INVALID
+    d2 = _desc(B=2, N=2)
+    full = list(args)
+    full[8] = full[9] = full[10] = fake
+    assert lib.kda_fwd(ctypes.byref(d2), *full) == B.KDA_ERR_INVALID
+    assert b"B == 1" in lib.kda_last_error()
+
+
+def test_step_and_plan_validation():
+    lib = kda.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    rc = lib.kda_step(4, 2, 32, 48, 0, 0, 1.0, 0, *([fake] * 5), None, None, fake, fake, None)
+    assert rc == B.KDA_ERR_UNSUPPORTED
+    rc = lib.kda_step(4, 2, 32, 64, 0, 0, 1.0, 0, *([fake] * 5), None, None, None, fake, None)
+    assert rc == B.KDA_ERR_INVALID and b"h must not be null" in lib.kda_last_error()
+    assert lib.kda_plan_varlen(None, 2, 10, 64, fake, fake, None) == B.KDA_ERR_INVALID
+    assert lib.kda_plan_varlen(fake, 0, 10, 64, fake, fake, None) == B.KDA_ERR_INVALID
+    assert lib.kda_status_str(B.KDA_ERR_WORKSPACE) == b"workspace missing or too small"
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        kda.fwd(x, x, torch.zeros(1, 4, 1, 64), x, torch.zeros(1, 4, 1), 1.0)

@@ -1,0 +1,93 @@
+"""Decode step (kda_step) against the oracle's token step."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import kimi_delta_attention_chunk_amd as kda
+import oracle
+from cases import check_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_inputs(seed, steps, B, H, dk, dv, dtype, weak=False):
+    raw = kda_inputs.draw_decode(seed, steps, B, H, dk, dv,
+                                 a_log_range=kda_inputs.A_LOG_RANGE_WEAK if weak else kda_inputs.A_LOG_RANGE)
+    qh, kh, g, beta = oracle.prep_forward(raw["q_raw"], raw["k_raw"], raw["f"], raw["A_log"],
+                                          raw["dt_bias"], raw["b"])
+    inp = dict(q=torch.tensor(qh, dtype=torch.float32).to(dtype),
+               k=torch.tensor(kh, dtype=torch.float32).to(dtype), v=raw["v"].to(dtype),
+               g=torch.tensor(g, dtype=torch.float32), beta=torch.tensor(beta, dtype=torch.float32))
+    return inp, raw
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 32, 64), (torch.bfloat16, 32, 64),
+                                         (torch.bfloat16, 128, 128), (torch.float32, 64, 64)])
+def test_step_matches_oracle(dtype, dk, dv):
+    B, H, steps = 64, 4, 24
+    inp, raw = _decode_inputs(3, steps, B, H, dk, dv, dtype, weak=True)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    h = raw["h"].clone().cuda()
+    href = to_np(raw["h"])
+    scale = dk ** -0.5
+    for t in range(steps):
+        o = kda.step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], h, scale,
+                     out_dtype=torch.float32)
+        oref, href = oracle.step(to_np(inp["q"][t]), to_np(inp["k"][t]), to_np(inp["v"][t]),
+                                 to_np(inp["g"][t]), to_np(inp["beta"][t]), scale, href)
+        check_close("o[%d]" % t, o, oref, dtype)
+    check_close("h", h, href, dtype)
+
+
+def test_step_decode_config_shape_with_prep():
+    """B=256, H=8, dk=32, dv=64 (the decode configuration), fused preparation, bf16."""
+    B, H, dk, dv, steps = 256, 8, 32, 64, 16
+    raw = kda_inputs.draw_decode(2, steps, B, H, dk, dv)
+    dt = torch.bfloat16
+    q, k, v = (raw[x].to(dt).cuda() for x in ("q_raw", "k_raw", "v"))
+    f, b = raw["f"].cuda(), raw["b"].cuda()
+    A_log, dtb = raw["A_log"].cuda(), raw["dt_bias"].cuda()
+    h = raw["h"].clone().cuda()
+    href = to_np(raw["h"])
+    scale = dk ** -0.5
+    for t in range(steps):
+        o = kda.step(q[t], k[t], v[t], f[t], b[t], h, scale, A_log=A_log, dt_bias=dtb, l2norm_qk=True,
+                     gate_in_kernel=True, beta_logits=True, out_dtype=torch.float32)
+        qh, kh, g, beta = oracle.prep_forward(to_np(q[t]), to_np(k[t]), to_np(f[t]), to_np(A_log),
+                                              to_np(dtb), to_np(b[t]))
+        oref, href = oracle.step(qh, kh, to_np(v[t]), g, beta, scale, href)
+        check_close("o[%d]" % t, o, oref, dt)
+    check_close("h", h, href, dt)
+
+
+def test_step_continuation_is_bitwise():
+    """500 + 500 steps with the state copied out in between equal 1000 straight steps."""
+    B, H, dk, dv, steps = 32, 8, 32, 64, 1000
+    inp, raw = _decode_inputs(4, steps, B, H, dk, dv, torch.bfloat16)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    scale = dk ** -0.5
+    h1 = raw["h"].clone().cuda()
+    for t in range(steps):
+        o1 = kda.step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], h1, scale)
+    h2 = raw["h"].clone().cuda()
+    for t in range(500):
+        kda.step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], h2, scale)
+    saved = h2.cpu().clone()
+    h3 = saved.cuda()
+    for t in range(500, steps):
+        o3 = kda.step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], h3, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h3)
+    assert torch.equal(o1, o3)
+
+
+def test_step_bf16_output_is_rounded_fp32_output():
+    B, H, dk, dv = 16, 8, 32, 64
+    inp, raw = _decode_inputs(5, 1, B, H, dk, dv, torch.bfloat16)
+    dev = {k: v[0].cuda() for k, v in inp.items()}
+    ha, hb = raw["h"].clone().cuda(), raw["h"].clone().cuda()
+    oa = kda.step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], ha, 0.17, out_dtype=torch.float32)
+    ob = kda.step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], hb, 0.17, out_dtype=torch.bfloat16)
+    assert torch.equal(oa.to(torch.bfloat16), ob)
+    assert torch.equal(ha, hb)
