@@ -1,7 +1,668 @@
-// kda_bwd.hip -- chunked backward (placeholder until the kernels land).
+// kda_bwd.hip -- chunked backward.
+//
+// Reverse-mode of the chunk form in kda_chunk.cuh (derived by hand from the
+// recurrence; the pages only name the FLA backward kernels and their
+// "diagonal phases": openkimi README, the paragraph on the guarded midpoint
+// change, and the Primus guide's autotune paragraph on
+// chunk_kda_bwd_kernel_intra).  Launch sequence:
+//   1. forward recompute: intra (w, u, Aqk, T) and state pass (h_n, v_new);
+//   2. bwd_dh   one workgroup per (sequence, head, 32 state columns), chunks
+//               in reverse: D = dL/dS at each chunk end, and
+//               dv_new = scale Aqk^T dO + Kh D,
+//               D     <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new;
+//   3. bwd_dv   one workgroup per (chunk, head): the products that contract
+//               over dv (register accumulators over 32-column blocks):
+//               dQg = scale dO h^T, dAqk = scale dO vn^T, dKh = vn D^T,
+//               dw = -dvn h^T, dT_v = dvn (beta V)^T, dGamma_L = rowsum(h . D),
+//               and through u = T beta V: dV = beta . (T^T dvn), dbeta_v;
+//   4. bwd_dk   one workgroup per (chunk, head): dT += dw (beta Kg)^T,
+//               dKg = beta . (T^T dw), dA = -T^T dT T^T (strictly lower), the
+//               decayed pair terms of Akk and Aqk (exact exp of each
+//               non-positive difference), the explicit factors exp(G) Q,
+//               exp(G) K, K exp(G_L - G), exp(G_L), the reverse in-chunk
+//               cumulative sum dg, and the preparation chain;
+//   5. (gate in kernel) a fixed-order reduction of dA_log and dt_bias.
+// Every reduction has a fixed order: no floating-point atomics anywhere.
 #include "kda_chunk.cuh"
 #include "kda_internal.h"
 
 namespace kda {
-hipError_t launch_bwd(const ChunkArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+// ============================================================== reverse state pass
+template <int DK, int DV, typename TIn>
+__global__ void __launch_bounds__(kThreads) bwd_dh_kernel(Prm p, int total_wg) {
+    constexpr int LS = kBV + 4;
+    __shared__ float D[DK * LS];
+    __shared__ float QT[DK * kLD];   // scale * q * exp(G), transposed
+    __shared__ float KhT[DK * kLD];  // k * exp(G_L - G), transposed
+    constexpr int GW = DK * kLD > kChunk * (DK + 4) ? DK * kLD : kChunk * (DK + 4);
+    __shared__ float GT[GW];         // cumulative decay, then w (row-major, stride DK+4)
+    __shared__ float AQ[kChunk * kLD];
+    __shared__ float DOs[kChunk * LS];
+    __shared__ float DVN[kChunk * LS];
+    __shared__ float gL[DK];
+    __shared__ float rn[kChunk];
+
+    constexpr int NV = DV / kBV;
+    const int lid = xcd_local_id(blockIdx.x, total_wg);
+    const int vb = lid % NV, nh = lid / NV;
+    const int n = nh / p.H, h = nh % p.H;
+    if (n >= p.N) return;
+    const int jb = vb * kBV;
+    const bool l2 = p.flags & 1u;
+    const float scale = p.scale;
+    const TIn* dO = (const TIn*)p.d_o;
+
+    for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+        const int cc = e / kBV, j = e - cc * kBV;
+        D[cc * LS + j] = p.dhT ? p.dhT[((size_t)nh * DK + cc) * DV + jb + j] : 0.f;
+    }
+    int c0, c1;
+    p.seq.seq_chunks(n, c0, c1);
+    for (int c = c1 - 1; c >= c0; --c) {
+        const ChunkRef cr = p.seq.chunk(c);
+        const size_t slot = (size_t)c * p.H + h;
+        __syncthreads();
+        float* dhs = p.dhs + slot * DK * DV;
+        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+            const int cc = e / kBV, j = e - cc * kBV;
+            dhs[cc * DV + jb + j] = D[cc * LS + j];
+        }
+        stage_qk<DK, TIn>((const TIn*)p.k, cr, h, p.H, l2, KhT, rn);
+        stage_qk<DK, TIn>((const TIn*)p.q, cr, h, p.H, l2, QT, rn);
+        stage_g<DK>(p, cr, h, GT, nullptr);
+        const int last = cr.len - 1;
+        for (int e = threadIdx.x; e < DK * kChunk; e += kThreads) {
+            const int cc = e / kChunk, t = e - cc * kChunk;
+            const float gt = GT[cc * kLD + t];
+            KhT[cc * kLD + t] *= __expf(GT[cc * kLD + last] - gt);
+            QT[cc * kLD + t] *= scale * __expf(gt);
+        }
+        if (threadIdx.x < DK) gL[threadIdx.x] = __expf(GT[threadIdx.x * kLD + last]);
+        const float* aq = p.aqk + slot * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) AQ[(e >> 6) * kLD + (e & 63)] = aq[e];
+        for (int e = threadIdx.x; e < kChunk * kBV; e += kThreads) {
+            const int t = e / kBV, j = e - t * kBV;
+            DOs[t * LS + j] = t < cr.len ? Elem<TIn>::load(dO, tok_index(cr.t0 + t, h, p.H, DV) + jb + j) : 0.f;
+        }
+        __syncthreads();  // GT fully consumed: reuse it for w
+        float* WL = GT;
+        const float* wi = p.w + slot * kChunk * DK;
+        for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
+            const int t = e / DK, cc = e - t * DK;
+            WL[t * (DK + 4) + cc] = wi[e];
+        }
+        __syncthreads();
+        // dv_new = scale Aqk^T dO + Kh D
+        float* dvo = p.dvn + slot * kChunk * DV;
+        {
+            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            constexpr int TN = kBV / 16, TILES = (kChunk / 16) * TN;
+            for (int tile = wave; tile < TILES; tile += kWaves) {
+                const int tm = tile / TN, tn = tile % TN;
+                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+                a1 = mma16_f32(AQ + tm * 16, 1, kLD, DOs + tn * 16, LS, 1, 16 * tm, kChunk, a1);
+                a2 = mma16_f32(KhT + tm * 16, 1, kLD, D + tn * 16, LS, 1, 0, DK, a2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
+                    const float val = scale * a1[i] + a2[i];
+                    DVN[t * LS + j] = val;
+                    dvo[t * DV + jb + j] = val;
+                }
+            }
+        }
+        __syncthreads();
+        // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
+        {
+            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            constexpr int TN = kBV / 16, TILES = (DK / 16) * TN;
+            for (int tile = wave; tile < TILES; tile += kWaves) {
+                const int tm = tile / TN, tn = tile % TN;
+                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+                a1 = mma16_f32(QT + tm * 16 * kLD, kLD, 1, DOs + tn * 16, LS, 1, 0, kChunk, a1);
+                a2 = mma16_f32(WL + tm * 16, 1, DK + 4, DVN + tn * 16, LS, 1, 0, kChunk, a2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int cc = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
+                    D[cc * LS + j] = gL[cc] * D[cc * LS + j] + a1[i] - a2[i];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (p.dh0) {
+        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
+            const int cc = e / kBV, j = e - cc * kBV;
+            p.dh0[((size_t)nh * DK + cc) * DV + jb + j] = D[cc * LS + j];
+        }
+    }
+}
+
+// ============================================================== dv-side contractions
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
+    constexpr int VB = 32, LB = VB + 4, NG = DV / 16;
+    __shared__ float Tm[kChunk * kLD];
+    __shared__ float Hb[DK * LB];
+    __shared__ float Db[DK * LB];
+    __shared__ float DOb[kChunk * LB];
+    __shared__ float VNb[kChunk * LB];
+    __shared__ float DVNb[kChunk * LB];
+    __shared__ float Vb[kChunk * LB];
+    __shared__ float bet[kChunk];
+    __shared__ float dbv_part[kChunk * NG];
+    __shared__ float dgl[DK];
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const ChunkRef cr = p.seq.chunk(c);
+    if (cr.len == 0) return;
+    const size_t slot = (size_t)c * p.H + h;
+    const TIn* dO = (const TIn*)p.d_o;
+    const TIn* vin = (const TIn*)p.v;
+    TOut* dvout = (TOut*)p.dv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+    const float* tmi = p.tm + slot * kChunk * kChunk;
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
+    if (threadIdx.x < kChunk) {
+        const int t = threadIdx.x;
+        float b = 0.f;
+        if (t < cr.len) {
+            b = p.beta[(size_t)(cr.t0 + t) * p.H + h];
+            if (p.flags & 4u) b = sigmoid_f(b);
+        }
+        bet[t] = b;
+    }
+    if (threadIdx.x < DK) dgl[threadIdx.x] = 0.f;
+
+    TileSet<kChunk, DK> aQ, aKh, aW;
+    TileSet<kChunk, kChunk> aAq, aT;
+    aQ.zero(); aKh.zero(); aW.zero(); aAq.zero(); aT.zero();
+
+    const float* hs = p.hs + slot * DK * DV;
+    const float* dhs = p.dhs + slot * DK * DV;
+    const float* vn = p.vn + slot * kChunk * DV;
+    const float* dvn = p.dvn + slot * kChunk * DV;
+    for (int jb = 0; jb < DV; jb += VB) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < DK * VB; e += kThreads) {
+            const int cc = e / VB, j = e - cc * VB;
+            Hb[cc * LB + j] = hs[cc * DV + jb + j];
+            Db[cc * LB + j] = dhs[cc * DV + jb + j];
+        }
+        for (int e = threadIdx.x; e < kChunk * VB; e += kThreads) {
+            const int t = e / VB, j = e - t * VB;
+            const bool in = t < cr.len;
+            const size_t gi = tok_index(cr.t0 + t, h, p.H, DV) + jb + j;
+            DOb[t * LB + j] = in ? Elem<TIn>::load(dO, gi) : 0.f;
+            Vb[t * LB + j] = in ? Elem<TIn>::load(vin, gi) : 0.f;
+            VNb[t * LB + j] = vn[t * DV + jb + j];
+            DVNb[t * LB + j] = dvn[t * DV + jb + j];
+        }
+        __syncthreads();
+        aQ.mma(DOb, LB, 1, Hb, 1, LB, VB);
+        aKh.mma(VNb, LB, 1, Db, 1, LB, VB);
+        aW.mma(DVNb, LB, 1, Hb, 1, LB, VB);
+        aAq.mma(DOb, LB, 1, VNb, 1, LB, VB);
+        aT.mma(DVNb, LB, 1, Vb, 1, LB, VB);
+        // X_u = T^T dvn  ->  dV = beta . X_u,  dbeta_v = rowsum(X_u . V)
+        {
+            constexpr int TN = VB / 16, TILES = (kChunk / 16) * TN;
+            for (int tile = wave; tile < TILES; tile += kWaves) {
+                const int tm = tile / TN, tn = tile % TN;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma16_f32(Tm + tm * 16, 1, kLD, DVNb + tn * 16, LB, 1, 16 * tm, kChunk, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
+                    if (t < cr.len)
+                        Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, bet[t] * acc[i]);
+                    const float part = row16_sum(acc[i] * Vb[t * LB + j]);
+                    if ((lane & 15) == 0) dbv_part[t * NG + (jb >> 4) + tn] = part;
+                }
+            }
+        }
+        if (threadIdx.x < DK) {
+            const int cc = threadIdx.x;
+            float acc = 0.f;
+            for (int j = 0; j < VB; ++j) acc += Hb[cc * LB + j] * Db[cc * LB + j];
+            dgl[cc] += acc;
+        }
+    }
+    const float scale = p.scale;
+    float* o_q = p.dqt + slot * kChunk * DK;
+    float* o_kh = p.dkh + slot * kChunk * DK;
+    float* o_w = p.dwv + slot * kChunk * DK;
+    float* o_aq = p.daq + slot * kChunk * kChunk;
+    float* o_t = p.dtv + slot * kChunk * kChunk;
+    aQ.store([&](int t, int cc, float x) { o_q[t * DK + cc] = scale * x; });
+    aKh.store([&](int t, int cc, float x) { o_kh[t * DK + cc] = x; });
+    aW.store([&](int t, int cc, float x) { o_w[t * DK + cc] = -x; });
+    aAq.store([&](int t, int s, float x) { o_aq[t * kChunk + s] = s <= t ? scale * x : 0.f; });
+    aT.store([&](int t, int s, float x) { o_t[t * kChunk + s] = bet[s] * x; });
+    __syncthreads();
+    if (threadIdx.x < kChunk) {
+        const int t = threadIdx.x;
+        float acc = 0.f;
+        for (int gidx = 0; gidx < NG; ++gidx) acc += dbv_part[t * NG + gidx];
+        p.dbv[slot * kChunk + t] = acc;
+    }
+    if (threadIdx.x < DK) p.dgl[slot * DK + threadIdx.x] = dgl[threadIdx.x];
+}
+
+// ============================================================== dk-side
+constexpr int kCB = 32;  // channels per block in the dk-side kernel
+
+// Stage channels [cb, cb+kCB) of q or k into XT[c][t] (times the row's
+// inverse norm if `rn` is given); zero past the chunk end.
+template <int DK, typename TIn>
+__device__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
+                               const float* rn, float* XT) {
+    for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+        const int t = e / kCB, cc = e - t * kCB;
+        float x = 0.f;
+        if (t < cr.len) {
+            x = Elem<TIn>::load(src, tok_index(cr.t0 + t, h, H, DK) + cb + cc);
+            if (rn) x *= rn[t];
+        }
+        XT[cc * kLD + t] = x;
+    }
+}
+
+// Stage channels [cb, cb+kCB) of the log-decay (gate from f if flagged) and
+// form their in-chunk cumulative sums.  Also returns, in graw (nullable), the
+// per-token log-decay itself.  Ends with a barrier.
+template <int DK>
+__device__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw) {
+    const bool gate = p.flags & 2u;
+    for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+        const int t = e / kCB, cc = e - t * kCB;
+        float x = 0.f;
+        if (t < cr.len) {
+            x = p.g[tok_index(cr.t0 + t, h, p.H, DK) + cb + cc];
+            if (gate) x = -expf(p.A_log[h]) * softplus_f(x + p.dt_bias[h * DK + cb + cc]);
+        }
+        GT[cc * kLD + t] = x;
+        if (graw) graw[cc * kLD + t] = x;
+    }
+    __syncthreads();
+    if (threadIdx.x < kCB) {
+        const int cc = threadIdx.x;
+        float acc = 0.f;
+        for (int t = 0; t < kChunk; ++t) {
+            acc += GT[cc * kLD + t];
+            GT[cc * kLD + t] = acc;
+        }
+    }
+    __syncthreads();
+}
+
+// Inverse L2 norms of the raw rows of q or k (4 threads per token).
+template <int DK, typename TIn>
+__device__ void row_rnorm(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, float* rn) {
+    const int t = threadIdx.x >> 2, part = threadIdx.x & 3;
+    float ss = 0.f;
+    if (t < cr.len) {
+        const size_t base = tok_index(cr.t0 + t, h, H, DK);
+        for (int c = part; c < DK; c += 4) {
+            const float x = Elem<TIn>::load(src, base + c);
+            ss += x * x;
+        }
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (part == 0) rn[t] = 1.0f / sqrtf(ss + kL2Eps);
+}
+
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
+    constexpr int LC = kCB + 4, NB = DK / kCB, NG = DK / 16;
+    __shared__ float Tm[kChunk * kLD];   // T, later dAqk^T
+    __shared__ float dT[kChunk * kLD];
+    __shared__ float dAq[kChunk * kLD];  // scale * dAqk (lower incl. diagonal)
+    __shared__ float dA[kChunk * kLD];   // dAkk (strictly lower)
+    __shared__ float Y[kChunk * kLD];    // dT T^T, later dAkk^T
+    __shared__ float QTb[kCB * kLD];
+    __shared__ float KTb[kCB * kLD];
+    __shared__ float GTb[kCB * kLD];
+    __shared__ float GRb[kCB * kLD];     // per-token log-decay (gate chain)
+    __shared__ float X1[kChunk * LC];
+    __shared__ float X2[kChunk * LC];
+    __shared__ float X3[kChunk * LC];
+    __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
+    __shared__ float dbw_part[kChunk * NG];
+    __shared__ float wpart[kWaves * kChunk];   // per-wave row partials
+    __shared__ float dbA[kChunk], dotq[kChunk], dotk[kChunk];
+    __shared__ float pa_part[kWaves * NB];
+    __shared__ float dgl[DK];
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const ChunkRef cr = p.seq.chunk(c);
+    if (cr.len == 0) return;
+    const size_t slot = (size_t)c * p.H + h;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool l2 = p.flags & 1u, gate = p.flags & 2u;
+    const TIn* qin = (const TIn*)p.q;
+    const TIn* kin = (const TIn*)p.k;
+    const int last = cr.len - 1;
+
+    // ---- load the chunk matrices and row scalars
+    {
+        const float* tmi = p.tm + slot * kChunk * kChunk;
+        const float* dti = p.dtv + slot * kChunk * kChunk;
+        const float* dai = p.daq + slot * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+            const int idx = (e >> 6) * kLD + (e & 63);
+            Tm[idx] = tmi[e];
+            dT[idx] = dti[e];
+            dAq[idx] = dai[e];
+        }
+    }
+    if (threadIdx.x < kChunk) {
+        const int t = threadIdx.x;
+        float b = 0.f;
+        if (t < cr.len) {
+            b = p.beta[(size_t)(cr.t0 + t) * p.H + h];
+            if (p.flags & 4u) b = sigmoid_f(b);
+        }
+        bet[t] = b;
+        dbA[t] = 0.f; dotq[t] = 0.f; dotk[t] = 0.f;
+        rnq[t] = 1.f; rnk[t] = 1.f;
+    }
+    if (threadIdx.x < DK) dgl[threadIdx.x] = p.dgl[slot * DK + threadIdx.x];
+    __syncthreads();
+    if (l2) {
+        row_rnorm<DK, TIn>(qin, cr, h, p.H, rnq);
+        row_rnorm<DK, TIn>(kin, cr, h, p.H, rnk);
+    }
+    __syncthreads();
+
+    // ---- phase 3: dT += dw (beta Kg)^T ; dKg = beta . (T^T dw) ; dbeta_w
+    for (int b = 0; b < NB; ++b) {
+        const int cb = b * kCB;
+        stage_qk_block<DK, TIn>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        stage_g_block<DK>(p, cr, h, cb, GTb, nullptr);  // barrier inside covers KTb
+        const float* dwi = p.dwv + slot * kChunk * DK;
+        for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+            const int t = e / kCB, cc = e - t * kCB;
+            X1[t * LC + cc] = dwi[t * DK + cb + cc];
+            const float kg = KTb[cc * kLD + t] * __expf(GTb[cc * kLD + t]);
+            X2[t * LC + cc] = kg;                 // Kg[t][c]
+            QTb[cc * kLD + t] = bet[t] * kg;      // (beta Kg)^T, reusing the q tile
+        }
+        __syncthreads();
+        {
+            constexpr int TILES = 16;  // 64 x 64 tiles of dT
+            for (int tile = wave; tile < TILES; tile += kWaves) {
+                const int tm = tile >> 2, tn = tile & 3;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma16_f32(X1 + tm * 16 * LC, LC, 1, QTb + tn * 16, kLD, 1, 0, kCB, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tm * 16 + 4 * (lane >> 4) + i, s = tn * 16 + (lane & 15);
+                    dT[t * kLD + s] += acc[i];
+                }
+            }
+            constexpr int TN = kCB / 16, T2 = (kChunk / 16) * TN;
+            float* dkt = p.dkt + slot * kChunk * DK;
+            for (int tile = wave; tile < T2; tile += kWaves) {
+                const int tm = tile / TN, tn = tile % TN;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma16_f32(Tm + tm * 16, 1, kLD, X1 + tn * 16, LC, 1, 16 * tm, kChunk, acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = tm * 16 + 4 * (lane >> 4) + i, cc = tn * 16 + (lane & 15);
+                    dkt[t * DK + cb + cc] = bet[t] * acc[i];
+                    const float part = row16_sum(acc[i] * X2[t * LC + cc]);
+                    if ((lane & 15) == 0) dbw_part[t * NG + (cb >> 4) + tn] = part;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: Y = dT T^T ; dA = -T^T Y (strictly lower)
+    {
+        for (int tile = wave; tile < 16; tile += kWaves) {
+            const int tm = tile >> 2, tn = tile & 3;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma16_f32(dT + tm * 16 * kLD, kLD, 1, Tm + tn * 16 * kLD, 1, kLD, 0, 16 * (tn + 1), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Y[(tm * 16 + 4 * (lane >> 4) + i) * kLD + tn * 16 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+        for (int tile = wave; tile < 16; tile += kWaves) {
+            const int tm = tile >> 2, tn = tile & 3;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (tn <= tm) acc = mma16_f32(Tm + tm * 16, 1, kLD, Y + tn * 16, kLD, 1, 16 * tm, kChunk, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int a = tm * 16 + 4 * (lane >> 4) + i, bb = tn * 16 + (lane & 15);
+                dA[a * kLD + bb] = bb < a ? -acc[i] : 0.f;
+            }
+        }
+        __syncthreads();
+        // transposed copies for the row-side pair sums (lanes run over t)
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+            const int t = e >> 6, s = e & 63;
+            Y[s * kLD + t] = dA[t * kLD + s];
+            Tm[s * kLD + t] = dAq[t * kLD + s];
+        }
+        __syncthreads();
+    }
+
+    // ---- phases 5-6: pair terms, explicit factors, dg, preparation chain
+    const float eA = gate ? expf(p.A_log[h]) : 0.f;
+    const int t = lane;
+    float pa_acc = 0.f;               // sum of dg * g over this wave's (t, c)
+    float r_dbA = 0.f, r_dq = 0.f, r_dk = 0.f;  // per-row partials of this wave
+    for (int b = 0; b < NB; ++b) {
+        const int cb = b * kCB;
+        stage_qk_block<DK, TIn>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
+        stage_qk_block<DK, TIn>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        {
+            const float* a1 = p.dqt + slot * kChunk * DK;
+            const float* a2 = p.dkh + slot * kChunk * DK;
+            const float* a3 = p.dkt + slot * kChunk * DK;
+            for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+                const int tt = e / kCB, cc = e - tt * kCB;
+                X1[tt * LC + cc] = a1[tt * DK + cb + cc];
+                X2[tt * LC + cc] = a2[tt * DK + cb + cc];
+                X3[tt * LC + cc] = a3[tt * DK + cb + cc];
+            }
+        }
+        stage_g_block<DK>(p, cr, h, cb, GTb, GRb);  // ends with a barrier
+        for (int cc = wave; cc < kCB; cc += kWaves) {
+            const float gt = GTb[cc * kLD + t];
+            const float kt = KTb[cc * kLD + t];
+            const float qt = QTb[cc * kLD + t];
+            // pair sums: rows (partner s <= t) and columns (partner s >= t)
+            float rk = 0.f, rq = 0.f, ck = 0.f, cq = 0.f;
+            for (int s = 0; s < kChunk; ++s) {
+                const float gs = GTb[cc * kLD + s];
+                const float ks = KTb[cc * kLD + s];
+                if (s <= t) {
+                    const float e = __expf(gt - gs) * ks;
+                    rk += Y[s * kLD + t] * e;   // dA[t][s]
+                    rq += Tm[s * kLD + t] * e;  // scale dAqk[t][s]
+                }
+                if (s >= t) {
+                    const float e = __expf(gs - gt);
+                    ck += bet[s] * dA[s * kLD + t] * ks * e;
+                    cq += dAq[s * kLD + t] * QTb[cc * kLD + s] * e;
+                }
+            }
+            const float gam = __expf(gt);
+            const float gl_c = GTb[cc * kLD + last];
+            const float eL = __expf(gl_c - gt);
+            const float dqt = X1[t * LC + cc], dkh = X2[t * LC + cc], dkg = X3[t * LC + cc];
+            const float bt = bet[t];
+            const float kh = kt * eL;
+            float dQ = rq + gam * dqt;
+            float dK = bt * rk + ck + cq + gam * dkg + eL * dkh;
+            float dG = bt * kt * rk + qt * rq - kt * (ck + cq) + qt * gam * dqt + kt * gam * dkg - kh * dkh;
+            // dG_L collects sum_t Kh . dKh and exp(G_L) dGamma_L
+            const float sl = wave_sum(t < cr.len ? kh * dkh : 0.f);
+            if (t == last) dG += sl + __expf(gl_c) * dgl[cb + cc];
+            if (t >= cr.len) { dQ = 0.f; dK = 0.f; dG = 0.f; }
+            r_dbA += kt * rk;
+            r_dq += qt * dQ;
+            r_dk += kt * dK;
+            // reverse in-chunk cumulative sum: dg_t = sum_{u >= t} dG_u
+            float sfx = dG;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_down(sfx, off, 64);
+                if (t + off < 64) sfx += o;
+            }
+            float dgo = sfx;
+            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + cb + cc;
+            if (gate) {
+                float dfv = 0.f;
+                if (t < cr.len) {
+                    const float x = p.g[gi] + p.dt_bias[h * DK + cb + cc];
+                    dfv = sfx * (-eA) * dsoftplus_f(x);
+                    pa_acc += sfx * GRb[cc * kLD + t];
+                }
+                dgo = dfv;
+                const float colsum = wave_sum(dfv);
+                if (lane == 0) p.part_dt[slot * DK + cb + cc] = colsum;
+            }
+            if (t < cr.len) {
+                p.dg[gi] = dgo;
+                if (l2) {
+                    p.dxq[slot * kChunk * DK + t * DK + cb + cc] = dQ;
+                    p.dxk[slot * kChunk * DK + t * DK + cb + cc] = dK;
+                } else {
+                    Elem<TOut>::store((TOut*)p.dq, gi, dQ);
+                    Elem<TOut>::store((TOut*)p.dk, gi, dK);
+                }
+            }
+        }
+        __syncthreads();  // tiles of this block are reused by the next
+    }
+
+    // ---- row results: dbeta, and the second pass of the L2-norm chain
+    wpart[wave * kChunk + t] = r_dbA;
+    const float pa_w = wave_sum(pa_acc);
+    if (lane == 0) pa_part[wave] = pa_w;
+    __syncthreads();
+    if (threadIdx.x < kChunk) {
+        float acc = 0.f;
+        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        dbA[t] = acc;
+    }
+    __syncthreads();
+    wpart[wave * kChunk + t] = r_dq;
+    __syncthreads();
+    if (threadIdx.x < kChunk) {
+        float acc = 0.f;
+        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        dotq[t] = acc;
+    }
+    __syncthreads();
+    wpart[wave * kChunk + t] = r_dk;
+    __syncthreads();
+    if (threadIdx.x < kChunk) {
+        float acc = 0.f;
+        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        dotk[t] = acc;
+        if (t < cr.len) {
+            float db = p.dbv[slot * kChunk + t] + dbA[t];
+            for (int gidx = 0; gidx < NG; ++gidx) db += dbw_part[t * NG + gidx];
+            if (p.flags & 4u) db *= bet[t] * (1.f - bet[t]);
+            p.dbeta[(size_t)(cr.t0 + t) * p.H + h] = db;
+        }
+    }
+    if (gate && threadIdx.x == 0) {
+        float acc = 0.f;
+        for (int w = 0; w < kWaves; ++w) acc += pa_part[w];
+        p.part_a[slot] = acc;
+    }
+    if (l2) {
+        __syncthreads();
+        // dx = r (dx^ - (x^ . dx^) x^), x^ the normalised row
+        for (int e = threadIdx.x; e < cr.len * DK; e += kThreads) {
+            const int tt = e / DK, cc = e - tt * DK;
+            const size_t gi = tok_index(cr.t0 + tt, h, p.H, DK) + cc;
+            const float qh = Elem<TIn>::load(qin, gi) * rnq[tt];
+            const float kh = Elem<TIn>::load(kin, gi) * rnk[tt];
+            const float dxq = p.dxq[slot * kChunk * DK + tt * DK + cc];
+            const float dxk = p.dxk[slot * kChunk * DK + tt * DK + cc];
+            Elem<TOut>::store((TOut*)p.dq, gi, rnq[tt] * (dxq - dotq[tt] * qh));
+            Elem<TOut>::store((TOut*)p.dk, gi, rnk[tt] * (dxk - dotk[tt] * kh));
+        }
+    }
+}
+
+// ============================================================== gate parameter sums
+// dA_log[h] = sum over chunks of part_a, ddt_bias[h][c] = sum of part_dt, each
+// in a fixed order: thread i takes chunks i, i + 256, ... and the partial sums
+// are then added in thread order.
+template <int DK>
+__global__ void __launch_bounds__(kThreads) bwd_gate_sum_kernel(Prm p, int n_chunks) {
+    __shared__ float red[kThreads];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    for (int col = -1; col < DK; ++col) {
+        float acc = 0.f;
+        for (int c = tid; c < n_chunks; c += kThreads) {
+            if (p.seq.chunk(c).len == 0) continue;
+            const size_t slot = (size_t)c * p.H + h;
+            acc += col < 0 ? p.part_a[slot] : p.part_dt[slot * DK + col];
+        }
+        red[tid] = acc;
+        __syncthreads();
+        for (int off = kThreads / 2; off > 0; off >>= 1) {
+            if (tid < off) red[tid] += red[tid + off];
+            __syncthreads();
+        }
+        if (tid == 0) {
+            if (col < 0) p.dA_log[h] = red[0];
+            else p.ddt_bias[h * DK + col] = red[0];
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================== host side
+template <int DK, int DV, typename TIn, typename TOut>
+static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
+    const WsLayout L = ws_layout(a, true);
+    Prm p = make_prm(a, L);
+    p.hT = nullptr;
+    p.o = nullptr;
+    hipError_t e = launch_recompute(p, a, s);
+    if (e != hipSuccess) return e;
+    const int total = a.N * a.H * (DV / kBV);
+    hipLaunchKernelGGL((bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), 0, s, p, total);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.n_chunks_bound > 0) {
+        hipLaunchKernelGGL((bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.flags & 2u) {
+        hipLaunchKernelGGL((bwd_gate_sum_kernel<DK>), dim3(a.H), dim3(kThreads), 0, s, p, a.n_chunks_bound);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int DK, int DV>
+static hipError_t launch_bwd_dims(const ChunkArgs& a, hipStream_t s) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_bwd_t<DK, DV, uint16_t, uint16_t>(a, s)
+                          : launch_bwd_t<DK, DV, uint16_t, float>(a, s);
+    return a.out_bf16 ? launch_bwd_t<DK, DV, float, uint16_t>(a, s) : launch_bwd_t<DK, DV, float, float>(a, s);
+}
+
+hipError_t launch_bwd(const ChunkArgs& a, hipStream_t s) {
+    if (a.dk == 32 && a.dv == 64) return launch_bwd_dims<32, 64>(a, s);
+    if (a.dk == 64 && a.dv == 64) return launch_bwd_dims<64, 64>(a, s);
+    if (a.dk == 128 && a.dv == 128) return launch_bwd_dims<128, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace kda

@@ -24,10 +24,20 @@
 #pragma once
 
 #include "kda_device.cuh"
+#include "kda_internal.h"
 
 namespace kda {
 
 constexpr int kLD = kChunk + 4;  // padded stride of [channel][token] tiles
+constexpr int kBV = 32;          // state columns per workgroup of the sequential passes
+
+// Logical workgroup id such that consecutive logical ids run on the same XCD
+// (hardware deals workgroups round-robin over the 8 XCDs, each with its own
+// L2).  Identity when the grid is not a multiple of 8.
+__device__ __forceinline__ int xcd_local_id(int wg, int total) {
+    if ((total & 7) != 0) return wg;
+    return (wg & 7) * (total >> 3) + (wg >> 3);
+}
 
 // Kernel parameters (device view of one call).
 struct Prm {
@@ -43,8 +53,12 @@ struct Prm {
     const float* dhT;
     void *dq, *dk, *dv;
     float *dg, *dbeta, *dh0;
+    float *dA_log, *ddt_bias;
     // workspace arrays (fp32), indexed by slot = chunk * H + head
-    float *w, *u, *aqk, *hs, *vn, *dhs, *dvn, *part_a, *part_dt;
+    float *w, *u, *aqk, *tm, *hs, *vn;   // forward recompute (tm only for the backward)
+    float *dhs, *dvn;                    // backward state pass
+    float *dqt, *dkh, *dwv, *daq, *dtv, *dgl, *dbv;
+    float *dkt, *dxq, *dxk, *part_a, *part_dt;
 };
 
 __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
@@ -200,4 +214,61 @@ struct TriKUpper {
     __device__ __forceinline__ void operator()(int tm, int, int& k0, int& k1) const { k0 = 16 * tm; k1 = kChunk; }
 };
 
+// ----------------------------------------------------------------- host helpers
+// (kda_fwd.hip) Kernel parameters of a call, and the forward recompute used
+// by the backward: intra-chunk (w, u, Aqk and, if p.tm is set, T) then the
+// state pass (states entering each chunk, v_new; hT if p.hT is set).
+Prm make_prm(const ChunkArgs& a, const WsLayout& L);
+hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s);
+
+// Register-resident accumulators for the 16x16 tiles of an M x N result that
+// this wave owns (tile = wave + i * kWaves), so several products can be
+// accumulated over blocks of their contraction index without LDS traffic.
+template <int M, int N>
+struct TileSet {
+    static constexpr int TN = N / 16, TILES = (M / 16) * TN;
+    static constexpr int PER = (TILES + kWaves - 1) / kWaves;
+    f32x4 acc[PER];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // acc += A(M x K) * B(K x N) with element strides as in mma16_f32
+    __device__ __forceinline__ void mma(const float* A, int am, int ak, const float* B, int bk, int bn, int K) {
+        const int wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int tile = wave + i * kWaves;
+            if (tile < TILES) {
+                const int tm = tile / TN, tn = tile % TN;
+                acc[i] = mma16_f32(A + tm * 16 * am, am, ak, B + tn * 16 * bn, bk, bn, 0, K, acc[i]);
+            }
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void store(F f) const {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int tile = wave + i * kWaves;
+            if (tile < TILES) {
+                const int tm = tile / TN, tn = tile % TN;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f(tm * 16 + 4 * (lane >> 4) + r, tn * 16 + (lane & 15), acc[i][r]);
+            }
+        }
+    }
+};
+
+// Sum over the 16 lanes that share the rows of an MFMA D fragment (lanes
+// 16g .. 16g+15), in a fixed order; every lane of the group gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
 }  // namespace kda
+

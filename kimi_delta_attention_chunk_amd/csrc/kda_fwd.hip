@@ -13,14 +13,6 @@
 
 namespace kda {
 
-// Logical workgroup id such that consecutive logical ids run on the same XCD
-// (hardware deals workgroups round-robin over the 8 XCDs, each with its own
-// L2).  Identity when the grid is not a multiple of 8.
-__device__ __forceinline__ int xcd_local_id(int wg, int total) {
-    if ((total & 7) != 0) return wg;
-    return (wg & 7) * (total >> 3) + (wg >> 3);
-}
-
 // ============================================================== intra-chunk
 template <int DK, int DV, typename TIn>
 __global__ void __launch_bounds__(kThreads) fwd_intra_kernel(Prm p) {
@@ -61,6 +53,10 @@ __global__ void __launch_bounds__(kThreads) fwd_intra_kernel(Prm p) {
     }
     solve_unit_lower(A, Tm, X);  // begins/ends with barriers
 
+    if (p.tm) {
+        float* to = p.tm + slot * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) to[e] = Tm[(e >> 6) * kLD + (e & 63)];
+    }
     float* wo = p.w + slot * kChunk * DK;
     float* uo = p.u + slot * kChunk * DV;
     wg_gemm<kChunk, DK>(Tm, kLD, 1, KT, 1, kLD, kChunk, TriK(),
@@ -70,8 +66,6 @@ __global__ void __launch_bounds__(kThreads) fwd_intra_kernel(Prm p) {
 }
 
 // ============================================================== state passing
-constexpr int kBV = 32;  // state columns per workgroup
-
 template <int DK, int DV, typename TIn>
 __global__ void __launch_bounds__(kThreads) fwd_state_kernel(Prm p, int total_wg) {
     constexpr int LS = kBV + 4;
@@ -210,30 +204,46 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.A_log = a.A_log; p.dt_bias = a.dt_bias; p.h0 = a.h0;
     p.o = a.o; p.hT = a.hT; p.d_o = a.d_o; p.dhT = a.dhT;
     p.dq = a.dq; p.dk = a.dk_; p.dv = a.dv_; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
+    p.dA_log = a.dA_log; p.ddt_bias = a.ddt_bias;
     char* base = (char*)a.ws;
-    auto at = [&](size_t off) { return (float*)(base + off); };
-    p.w = at(L.w); p.u = at(L.u); p.aqk = at(L.aqk); p.hs = at(L.hs); p.vn = at(L.vn);
-    p.dhs = at(L.dhs); p.dvn = at(L.dvn); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
+    auto at = [&](size_t off) { return off ? (float*)(base + off) : (float*)nullptr; };
+    p.w = (float*)(base + L.w);  // offset 0
+    p.u = at(L.u); p.aqk = at(L.aqk); p.tm = at(L.tm); p.hs = at(L.hs); p.vn = at(L.vn);
+    p.dhs = at(L.dhs); p.dvn = at(L.dvn);
+    p.dqt = at(L.dqt); p.dkh = at(L.dkh); p.dwv = at(L.dwv); p.daq = at(L.daq); p.dtv = at(L.dtv);
+    p.dgl = at(L.dgl); p.dbv = at(L.dbv);
+    p.dkt = at(L.dkt); p.dxq = at(L.dxq); p.dxk = at(L.dxk); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
     return p;
 }
 
 WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     WsLayout L{};
     const size_t slots = (size_t)a.n_chunks_bound * a.H;
+    const size_t C = kChunk, dk = a.dk, dv = a.dv;
     auto bytes = [](size_t n) { return (n * sizeof(float) + 255) & ~(size_t)255; };
     size_t off = 0;
-    L.w = off; off += bytes(slots * kChunk * a.dk);
-    L.u = off; off += bytes(slots * kChunk * a.dv);
-    L.aqk = off; off += bytes(slots * kChunk * kChunk);
-    L.hs = off; off += bytes(slots * (size_t)a.dk * a.dv);
-    L.vn = off; off += bytes(slots * kChunk * a.dv);
+    auto take = [&](size_t& field, size_t n) { field = off; off += bytes(n ? n : 1); };
+    take(L.w, slots * C * dk);
+    take(L.u, slots * C * dv);
+    take(L.aqk, slots * C * C);
+    take(L.hs, slots * dk * dv);
+    take(L.vn, slots * C * dv);
     if (backward) {
-        L.dhs = off; off += bytes(slots * (size_t)a.dk * a.dv);
-        L.dvn = off; off += bytes(slots * kChunk * a.dv);
-        L.part_a = off; off += bytes(slots);
-        L.part_dt = off; off += bytes(slots * a.dk);
-    } else {
-        L.dhs = L.dvn = L.part_a = L.part_dt = 0;
+        take(L.tm, slots * C * C);
+        take(L.dhs, slots * dk * dv);
+        take(L.dvn, slots * C * dv);
+        take(L.dqt, slots * C * dk);
+        take(L.dkh, slots * C * dk);
+        take(L.dwv, slots * C * dk);
+        take(L.daq, slots * C * C);
+        take(L.dtv, slots * C * C);
+        take(L.dgl, slots * dk);
+        take(L.dbv, slots * C);
+        take(L.dkt, slots * C * dk);
+        take(L.dxq, slots * C * dk);
+        take(L.dxk, slots * C * dk);
+        take(L.part_a, slots);
+        take(L.part_dt, slots * dk);
     }
     L.total = off;
     return L;
@@ -254,7 +264,17 @@ hipError_t launch_fwd_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s)
     hipLaunchKernelGGL((fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), 0, s, p, total);
     return hipGetLastError();
 }
-template hipError_t launch_fwd_recompute<32, 64, float>(const Prm&, const ChunkArgs&, hipStream_t);
+
+hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
+    if (a.dk == 32 && a.dv == 64)
+        return a.in_bf16 ? launch_fwd_recompute<32, 64, uint16_t>(p, a, s) : launch_fwd_recompute<32, 64, float>(p, a, s);
+    if (a.dk == 64 && a.dv == 64)
+        return a.in_bf16 ? launch_fwd_recompute<64, 64, uint16_t>(p, a, s) : launch_fwd_recompute<64, 64, float>(p, a, s);
+    if (a.dk == 128 && a.dv == 128)
+        return a.in_bf16 ? launch_fwd_recompute<128, 128, uint16_t>(p, a, s)
+                         : launch_fwd_recompute<128, 128, float>(p, a, s);
+    return hipErrorInvalidValue;
+}
 
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {

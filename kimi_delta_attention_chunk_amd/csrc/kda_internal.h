@@ -48,8 +48,15 @@ struct ChunkArgs {
 };
 
 // Workspace layout shared by the forward and backward launches.
+// Byte offsets of the per-chunk fp32 arrays inside the caller's workspace;
+// every array is indexed by slot = chunk * H + head.  The backward-only
+// arrays are 0 (absent) in a forward layout.
 struct WsLayout {
-    size_t w, u, aqk, hs, vn, dhs, dvn, part_a, part_dt, total;
+    size_t w, u, aqk, tm, hs, vn;                    // forward recompute
+    size_t dhs, dvn;                                 // backward state pass
+    size_t dqt, dkh, dwv, daq, dtv, dgl, dbv;        // dv-side intermediates
+    size_t dkt, dxq, dxk, part_a, part_dt;           // dk-side intermediates
+    size_t total;
 };
 WsLayout ws_layout(const ChunkArgs& a, bool backward);
 
