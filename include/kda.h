@@ -171,6 +171,19 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
              const float* g, const float* beta, const float* A_log, const float* dt_bias,
              float* h, void* o, kda_stream_t stream);
 
+/* Opt-in per-kernel timing for benchmarks.  kda_timing_enable(1) clears the
+ * record and brackets every later kernel launch of this library with a pair
+ * of hipEvents on the launch stream (enable(0) stops; pending events are
+ * dropped).  kda_timing_collect() waits for the recorded events (it
+ * SYNCHRONISES on them) and adds their durations to per-kernel totals, read
+ * with kda_timing_count() / kda_timing_get(i, &name, &launches, &total_ms);
+ * `name` stays valid until the next enable call.  Kernel names: plan, step,
+ * fwd_intra, fwd_state, fwd_output, bwd_dh, bwd_dv, bwd_dk, bwd_gate_sum. */
+int kda_timing_enable(int on);
+int kda_timing_collect(void);
+int kda_timing_count(void);
+int kda_timing_get(int i, const char** name, int64_t* launches, double* total_ms);
+
 /* Static text for a status code, and the thread-local message of the last
  * failing call on this thread ("" if none). */
 const char* kda_status_str(int status);

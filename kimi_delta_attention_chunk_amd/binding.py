@@ -24,7 +24,8 @@ CHUNK = 64
 
 EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd_workspace",
            "kda_bwd_workspace", "kda_fwd", "kda_bwd", "kda_step", "kda_status_str",
-           "kda_last_error"]
+           "kda_last_error", "kda_timing_enable", "kda_timing_collect", "kda_timing_count",
+           "kda_timing_get"]
 
 
 class KdaDesc(ctypes.Structure):
@@ -75,6 +76,15 @@ def load_library():
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_timing_enable.argtypes = [ctypes.c_int]
+    lib.kda_timing_enable.restype = ctypes.c_int
+    lib.kda_timing_collect.argtypes = []
+    lib.kda_timing_collect.restype = ctypes.c_int
+    lib.kda_timing_count.argtypes = []
+    lib.kda_timing_count.restype = ctypes.c_int
+    lib.kda_timing_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                   ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    lib.kda_timing_get.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -278,3 +288,22 @@ def step(q, k, v, g, beta, h, scale, *, A_log=None, dt_bias=None, l2norm_qk=Fals
                         _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(h),
                         _ptr(o), _stream(dev)))
     return o
+
+
+def timing_enable(on: bool = True):
+    """Start (and clear) or stop the library's per-kernel event timing."""
+    _check(load_library().kda_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> dict:
+    """Wait for the recorded events; returns {kernel: (launches, total_ms)} so far."""
+    lib = load_library()
+    _check(lib.kda_timing_collect())
+    out = {}
+    for i in range(lib.kda_timing_count()):
+        name = ctypes.c_char_p()
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib.kda_timing_get(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)))
+        out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out

@@ -635,17 +635,13 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     hipError_t e = launch_recompute(p, a, s);
     if (e != hipSuccess) return e;
     const int total = a.N * a.H * (DV / kBV);
-    hipLaunchKernelGGL((bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), 0, s, p, total);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
     if (a.n_chunks_bound > 0) {
-        hipLaunchKernelGGL((bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+        KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     }
     if (a.flags & 2u) {
-        hipLaunchKernelGGL((bwd_gate_sum_kernel<DK>), dim3(a.H), dim3(kThreads), 0, s, p, a.n_chunks_bound);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        KDA_LAUNCH("bwd_gate_sum", (bwd_gate_sum_kernel<DK>), dim3(a.H), dim3(kThreads), s, p, a.n_chunks_bound);
     }
     return hipSuccess;
 }

@@ -256,13 +256,11 @@ bool dims_supported(int dk, int dv) {
 template <int DK, int DV, typename TIn>
 hipError_t launch_fwd_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
     if (a.n_chunks_bound > 0) {
-        hipLaunchKernelGGL((fwd_intra_kernel<DK, DV, TIn>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), 0, s, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        KDA_LAUNCH("fwd_intra", (fwd_intra_kernel<DK, DV, TIn>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     }
     const int total = a.N * a.H * (DV / kBV);
-    hipLaunchKernelGGL((fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), 0, s, p, total);
-    return hipGetLastError();
+    KDA_LAUNCH("fwd_state", (fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
+    return hipSuccess;
 }
 
 hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
@@ -283,9 +281,9 @@ static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
     hipError_t e = launch_fwd_recompute<DK, DV, TIn>(p, a, s);
     if (e != hipSuccess || a.n_chunks_bound == 0) return e;
     constexpr int OB = DV < 64 ? DV : 64;
-    hipLaunchKernelGGL((fwd_output_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H, DV / OB),
-                       dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    KDA_LAUNCH("fwd_output", (fwd_output_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H, DV / OB),
+               dim3(kThreads), s, p);
+    return hipSuccess;
 }
 
 template <int DK, int DV>

@@ -62,6 +62,21 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward);
 
 bool dims_supported(int dk, int dv);
 hipError_t launch_fwd(const ChunkArgs& a, hipStream_t s);
+
+// Opt-in per-kernel timing (kda_timing.hip): a pair of hipEvents around a launch.
+void prof_begin(hipStream_t s);
+void prof_end(hipStream_t s, const char* name);
+// Launches `kernel` and returns its launch error from the enclosing function
+// (which must return hipError_t); the error is read before the timing event
+// is recorded so that event calls cannot mask it.
+#define KDA_LAUNCH(name, kernel, grid, block, stream, ...)                     \
+    do {                                                                       \
+        ::kda::prof_begin(stream);                                             \
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);       \
+        const hipError_t kda_launch_err_ = hipGetLastError();                  \
+        ::kda::prof_end(stream, name);                                         \
+        if (kda_launch_err_ != hipSuccess) return kda_launch_err_;             \
+    } while (0)
 hipError_t launch_bwd(const ChunkArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -68,9 +68,9 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
 hipError_t launch_plan(const int32_t* cu, int N, int T, int chunk, int max_chunks,
                        int32_t* chunk_indices, int32_t* chunk_offsets, hipStream_t s) {
     (void)T;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, cu, N, chunk, max_chunks,
-                       chunk_indices, chunk_offsets);
-    return hipGetLastError();
+    KDA_LAUNCH("plan", plan_kernel, dim3(1), dim3(kPlanThreads), s, cu, N, chunk, max_chunks,
+               chunk_indices, chunk_offsets);
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -98,10 +98,10 @@ __global__ void __launch_bounds__(kThreads) step_kernel(
 
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_step_t(const StepArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((step_kernel<DK, DV, TIn, TOut>), dim3(a.B * a.H), dim3(kThreads), 0, s,
-                       a.B * a.H, a.H, a.scale, a.flags, (const TIn*)a.q, (const TIn*)a.k,
+    KDA_LAUNCH("step", (step_kernel<DK, DV, TIn, TOut>), dim3(a.B * a.H), dim3(kThreads), s,
+               a.B * a.H, a.H, a.scale, a.flags, (const TIn*)a.q, (const TIn*)a.k,
                        (const TIn*)a.v, a.g, a.beta, a.A_log, a.dt_bias, a.h, (TOut*)a.o);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <int DK, int DV>
