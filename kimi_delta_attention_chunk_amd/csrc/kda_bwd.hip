@@ -23,7 +23,10 @@
 //               cumulative sum dg, and the preparation chain;
 //   5. (gate in kernel) a fixed-order reduction of dA_log and dt_bias.
 // Every reduction has a fixed order: no floating-point atomics anywhere.
+#include <type_traits>
+
 #include "kda_chunk.cuh"
+#include "kda_dhscan.cuh"
 #include "kda_internal.h"
 
 namespace kda {
@@ -634,8 +637,13 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     p.o = nullptr;
     hipError_t e = launch_recompute(p, a, s);
     if (e != hipSuccess) return e;
+    constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     const int total = a.N * a.H * (DV / kBV);
-    KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
+    if constexpr (DK <= 64) {
+        KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, TIn, P>), dim3(total), dim3(kThreads), s, p, total);
+    } else {
+        KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
+    }
     if (a.n_chunks_bound > 0) {
         KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
         KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);

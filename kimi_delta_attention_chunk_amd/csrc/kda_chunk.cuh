@@ -56,6 +56,7 @@ struct Prm {
     float *dA_log, *ddt_bias;
     // workspace arrays (fp32), indexed by slot = chunk * H + head
     float *w, *u, *aqk, *tm, *hs, *vn;   // forward recompute (tm only for the backward)
+    float *qg, *khT, *gl;                // exp(G) q, (k exp(G_L - G))^T, exp(G_L)
     float *dhs, *dvn;                    // backward state pass
     float *dqt, *dkh, *dwv, *daq, *dtv, *dgl, *dbv;
     float *dkt, *dxq, *dxk, *part_a, *part_dt;

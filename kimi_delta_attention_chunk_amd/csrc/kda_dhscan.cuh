@@ -1,0 +1,203 @@
+// kda_dhscan.cuh -- the sequential part of the backward: the state gradient.
+//
+// One workgroup per (sequence, head, 32 columns of the state), chunks in
+// reverse.  With D = dL/dS at the end of the chunk (dhT, or 0, at the end of
+// the sequence), per chunk:
+//   dv_new = scale Aqk^T dO + Kh D                       (64 x 32)
+//   D     <- scale (exp(G) q)^T dO + Diag(exp G_L) D - w^T dv_new
+// (the reverse of v_new = u - w h, o = scale (Qg h + Aqk v_new),
+// h' = Diag(exp G_L) h + Kh^T v_new).  D at every chunk end and dv_new are
+// stored for the per-chunk gradient kernel; D after the first chunk is dh0.
+// Operands come from the intra-chunk kernel (aqk, khT, qg, w, gl) and from dO,
+// loaded one chunk ahead into registers, then transposed into MFMA tiles.
+// The fp32 D stays in the registers of the lanes that own its tiles.
+#pragma once
+
+#include "kda_chunk.cuh"
+#include "kda_mma.cuh"
+
+namespace kda {
+
+template <int DK, typename TIn>
+struct DhRegs {
+    static constexpr int NW = kChunk * DK / 4 / kThreads;      // float4 of w, qg, khT
+    static constexpr int NA = kChunk * kChunk / 4 / kThreads;  // float4 of aqk
+    f32x4 w[NW], q[NW], k[NW], a[NA];
+    float d[8];   // dO[t][jb + 8 part + i] for t = tid >> 2
+    float g[4 * ((DK / 16) * 2 + kWaves - 1) / kWaves];
+};
+
+template <int DK, int DV, typename TIn>
+__device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb,
+                                        DhRegs<DK, TIn>& R) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const f32x4* w = (const f32x4*)(p.w + slot * kChunk * DK);
+    const f32x4* q = (const f32x4*)(p.qg + slot * kChunk * DK);
+    const f32x4* k = (const f32x4*)(p.khT + slot * DK * kChunk);
+    const f32x4* a = (const f32x4*)(p.aqk + slot * kChunk * kChunk);
+#pragma unroll
+    for (int i = 0; i < DhRegs<DK, TIn>::NW; ++i) {
+        R.w[i] = w[tid + kThreads * i];
+        R.q[i] = q[tid + kThreads * i];
+        R.k[i] = k[tid + kThreads * i];
+    }
+#pragma unroll
+    for (int i = 0; i < DhRegs<DK, TIn>::NA; ++i) R.a[i] = a[tid + kThreads * i];
+    const int t = tid >> 2, part = tid & 3;
+    if (t < cr.len) {
+        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 8 * part;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R.d[i] = Elem<TIn>::load(src, i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R.d[i] = 0.f;
+    }
+    constexpr int TH = (DK / 16) * 2;
+#pragma unroll
+    for (int i = 0; i < (TH + kWaves - 1) / kWaves; ++i) {
+        const int tile = wave + kWaves * i;
+        if (tile < TH) {
+            const int tm = tile >> 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + tm * 16 + frag_row(r)];
+        }
+    }
+}
+
+template <int DK, int DV, typename TIn, Prec P>
+__global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_wg) {
+    constexpr int BV = 32, LK = DK + 8, LA = kChunk + 8, NV = DV / BV;
+    constexpr int TH = (DK / 16) * 2;
+    constexpr int HPW = (TH + kWaves - 1) / kWaves;
+    __shared__ __attribute__((aligned(16))) float sAq[kChunk * LA];   // Aqk^T [t][s]
+    __shared__ __attribute__((aligned(16))) float sKh[kChunk * LK];   // Kh [t][c]
+    __shared__ __attribute__((aligned(16))) float sQ[DK * LA];        // Qg^T [c][t]
+    __shared__ __attribute__((aligned(16))) float sW[DK * LA];        // w^T [c][t]
+    __shared__ __attribute__((aligned(16))) float sO[BV * LA];        // dO^T [j][t]
+    __shared__ __attribute__((aligned(16))) float sD[2][BV * LK];     // D^T [j][c]
+    __shared__ __attribute__((aligned(16))) float sV[BV * LA];        // dv_new^T [j][t]
+    const Tile<P> AqT(sAq, kChunk, LA), Kh(sKh, kChunk, LK), QgT(sQ, DK, LA), WT(sW, DK, LA), dOT(sO, BV, LA),
+        dvnT(sV, BV, LA);
+    const Tile<P> DT0(sD[0], BV, LK), DT1(sD[1], BV, LK);
+
+    const int lid = xcd_local_id(blockIdx.x, total_wg);
+    const int vb = lid % NV, nh = lid / NV;
+    const int n = nh / p.H, h = nh % p.H;
+    if (n >= p.N) return;
+    const int jb = vb * BV;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const float scale = p.scale;
+
+    f32x4 D[HPW];
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int tile = wave + kWaves * i;
+        D[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tile < TH) {
+            const int tm = tile >> 1, tn = tile & 1, j = tn * 16 + frag_col();
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                D[i][r] = p.dhT ? p.dhT[((size_t)nh * DK + tm * 16 + frag_row(r)) * DV + jb + j] : 0.f;
+            DT0.put4(j, tm * 16 + frag_row(0), D[i]);
+        }
+    }
+    int c0, c1;
+    p.seq.seq_chunks(n, c0, c1);
+    DhRegs<DK, TIn> R;
+    if (c0 < c1) dh_load<DK, DV, TIn>(p, (size_t)(c1 - 1) * p.H + h, p.seq.chunk(c1 - 1), h, jb, R);
+    for (int c = c1 - 1; c >= c0; --c) {
+        const size_t slot = (size_t)c * p.H + h;
+        __syncthreads();  // the previous chunk is done with the operand tiles
+#pragma unroll
+        for (int i = 0; i < DhRegs<DK, TIn>::NW; ++i) {
+            const int e4 = 4 * (tid + kThreads * i);
+            const int t = e4 / DK, cc = e4 - t * DK;       // w, qg: [t][c]
+            const int kc = e4 / kChunk, kt = e4 - kc * kChunk;  // khT: [c][t]
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                WT.put(cc + m, t, R.w[i][m]);
+                QgT.put(cc + m, t, R.q[i][m]);
+                Kh.put(kt + m, kc, R.k[i][m]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < DhRegs<DK, TIn>::NA; ++i) {
+            const int e4 = 4 * (tid + kThreads * i);
+            const int s = e4 >> 6, t = e4 & 63;  // aqk[s][t]
+#pragma unroll
+            for (int m = 0; m < 4; ++m) AqT.put(t + m, s, R.a[i][m]);
+        }
+        {
+            const int t = tid >> 2, part = tid & 3;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dOT.put(8 * part + i, t, R.d[i]);
+        }
+        float gl[4 * HPW];
+#pragma unroll
+        for (int i = 0; i < 4 * HPW; ++i) gl[i] = R.g[i];
+        __syncthreads();
+        if (c - 1 >= c0) dh_load<DK, DV, TIn>(p, slot - p.H, p.seq.chunk(c - 1), h, jb, R);
+        const bool odd = (c1 - 1 - c) & 1;
+        const Tile<P> Db = odd ? DT1 : DT0;
+        const Tile<P> Dn = odd ? DT0 : DT1;
+        // D at the end of this chunk
+        float* dhs = p.dhs + slot * DK * DV;
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int tile = wave + kWaves * i;
+            if (tile < TH) {
+                const int tm = tile >> 1, tn = tile & 1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dhs[(size_t)(tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[i][r];
+            }
+        }
+        // dv_new = scale Aqk^T dO + Kh D
+        float* dvo = p.dvn + slot * kChunk * DV;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
+            int k0 = 16 * tm, k1 = kChunk;
+            widen<P>(k0, k1);
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+            a1 = mma_tile(AqT.sub(tm * 16), dOT.sub(tn * 16), k0, k1, a1);
+            a2 = mma_tile(Kh.sub(tm * 16), Db.sub(tn * 16), 0, DK, a2);
+            f32x4 val;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) val[r] = scale * a1[r] + a2[r];
+            const int j = tn * 16 + frag_col();
+            dvnT.put4(j, tm * 16 + frag_row(0), val);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dvo[(size_t)(tm * 16 + frag_row(r)) * DV + jb + j] = val[r];
+        }
+        __syncthreads();
+        // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int tile = wave + kWaves * i;
+            if (tile < TH) {
+                const int tm = tile >> 1, tn = tile & 1;
+                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+                a1 = mma_tile(QgT.sub(tm * 16), dOT.sub(tn * 16), 0, kChunk, a1);
+                a2 = mma_tile(WT.sub(tm * 16), dvnT.sub(tn * 16), 0, kChunk, a2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) D[i][r] = gl[4 * i + r] * D[i][r] + scale * a1[r] - a2[r];
+                Dn.put4(tn * 16 + frag_col(), tm * 16 + frag_row(0), D[i]);
+            }
+        }
+    }
+    if (p.dh0) {
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int tile = wave + kWaves * i;
+            if (tile < TH) {
+                const int tm = tile >> 1, tn = tile & 1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p.dh0[((size_t)nh * DK + tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[i][r];
+            }
+        }
+    }
+}
+
+}  // namespace kda

@@ -8,62 +8,14 @@
 //               state in LDS; stores the state entering every chunk and v_new;
 //   fwd_output  one workgroup per (chunk, head, column block): o.
 // All products are fp32 MFMA (v_mfma_f32_16x16x4_f32); decays are exact.
+#include <type_traits>
+
 #include "kda_chunk.cuh"
 #include "kda_internal.h"
+#include "kda_intra.cuh"
+#include "kda_scan.cuh"
 
 namespace kda {
-
-// ============================================================== intra-chunk
-template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kThreads) fwd_intra_kernel(Prm p) {
-    constexpr int DX = DK > DV ? DK : DV;
-    __shared__ float KT[DK * kLD];
-    __shared__ float GT[DK * kLD];
-    __shared__ float QVT[DX * kLD];  // q during the Gram, then beta*v
-    __shared__ float A[kChunk * kLD];
-    __shared__ float Tm[kChunk * kLD];
-    __shared__ float X[4 * 16 * kLD16];
-    __shared__ float bet[kChunk];
-    __shared__ float rn[kChunk];
-
-    const int c = blockIdx.x, h = blockIdx.y;
-    const ChunkRef cr = p.seq.chunk(c);
-    if (cr.len == 0) return;
-    const size_t slot = (size_t)c * p.H + h;
-    const bool l2 = p.flags & 1u;
-
-    stage_qk<DK, TIn>((const TIn*)p.k, cr, h, p.H, l2, KT, rn);
-    stage_qk<DK, TIn>((const TIn*)p.q, cr, h, p.H, l2, QVT, rn);
-    stage_g<DK>(p, cr, h, GT, bet);
-
-    float* aq = p.aqk + slot * kChunk * kChunk;
-    gram_pairwise<DK>(KT, QVT, GT, bet, A, [&](int t, int s, float x) { aq[t * kChunk + s] = x; });
-    __syncthreads();
-
-    // beta * v (into the q buffer) and beta * exp(G) * k (in place)
-    for (int e = threadIdx.x; e < kChunk * DV; e += kThreads) {
-        const int t = e / DV, j = e - t * DV;
-        float x = 0.f;
-        if (t < cr.len) x = Elem<TIn>::load((const TIn*)p.v, tok_index(cr.t0 + t, h, p.H, DV) + j);
-        QVT[j * kLD + t] = bet[t] * x;
-    }
-    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
-        const int cc = e / kChunk, t = e - cc * kChunk;
-        KT[cc * kLD + t] *= bet[t] * __expf(GT[cc * kLD + t]);
-    }
-    solve_unit_lower(A, Tm, X);  // begins/ends with barriers
-
-    if (p.tm) {
-        float* to = p.tm + slot * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) to[e] = Tm[(e >> 6) * kLD + (e & 63)];
-    }
-    float* wo = p.w + slot * kChunk * DK;
-    float* uo = p.u + slot * kChunk * DV;
-    wg_gemm<kChunk, DK>(Tm, kLD, 1, KT, 1, kLD, kChunk, TriK(),
-                        [&](int t, int cc, float x) { wo[t * DK + cc] = x; });
-    wg_gemm<kChunk, DV>(Tm, kLD, 1, QVT, 1, kLD, kChunk, TriK(),
-                        [&](int t, int j, float x) { uo[t * DV + j] = x; });
-}
 
 // ============================================================== state passing
 template <int DK, int DV, typename TIn>
@@ -209,6 +161,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     auto at = [&](size_t off) { return off ? (float*)(base + off) : (float*)nullptr; };
     p.w = (float*)(base + L.w);  // offset 0
     p.u = at(L.u); p.aqk = at(L.aqk); p.tm = at(L.tm); p.hs = at(L.hs); p.vn = at(L.vn);
+    p.qg = at(L.qg); p.khT = at(L.khT); p.gl = at(L.gl);
     p.dhs = at(L.dhs); p.dvn = at(L.dvn);
     p.dqt = at(L.dqt); p.dkh = at(L.dkh); p.dwv = at(L.dwv); p.daq = at(L.daq); p.dtv = at(L.dtv);
     p.dgl = at(L.dgl); p.dbv = at(L.dbv);
@@ -228,6 +181,9 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     take(L.aqk, slots * C * C);
     take(L.hs, slots * dk * dv);
     take(L.vn, slots * C * dv);
+    take(L.qg, slots * C * dk);
+    take(L.khT, slots * C * dk);
+    take(L.gl, slots * dk);
     if (backward) {
         take(L.tm, slots * C * C);
         take(L.dhs, slots * dk * dv);
@@ -253,24 +209,43 @@ bool dims_supported(int dk, int dv) {
     return (dk == 32 && dv == 64) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128);
 }
 
-template <int DK, int DV, typename TIn>
-hipError_t launch_fwd_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
-    if (a.n_chunks_bound > 0) {
-        KDA_LAUNCH("fwd_intra", (fwd_intra_kernel<DK, DV, TIn>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+// Intra-chunk kernel, then the sequential pass.  `write_o`: produce o (the
+// forward); `store` : keep the state entering each chunk and v_new (the
+// backward's recompute).  dk <= 64 uses the precomputed-operand scan; dk = 128
+// keeps the staging state and output kernels above (the scan's tiles would
+// exceed the 160 KB of LDS).
+template <int DK, int DV, typename TIn, typename TOut>
+hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, bool write_o, bool store) {
+    constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
+    if (a.n_chunks_bound > 0)
+        KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+    if constexpr (DK <= 64) {
+        const int total = a.N * a.H * (DV / 32);
+        KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, TOut, P>), dim3(total), dim3(kThreads), s, p, total,
+                   write_o ? 1 : 0, store ? 1 : 0);
+    } else {
+        const int total = a.N * a.H * (DV / kBV);
+        KDA_LAUNCH("fwd_state", (fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
+        if (write_o && a.n_chunks_bound > 0) {
+            constexpr int OB = DV < 64 ? DV : 64;
+            KDA_LAUNCH("fwd_output", (fwd_output_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H, DV / OB),
+                       dim3(kThreads), s, p);
+        }
     }
-    const int total = a.N * a.H * (DV / kBV);
-    KDA_LAUNCH("fwd_state", (fwd_state_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
     return hipSuccess;
 }
 
 hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
+    // the output dtype is irrelevant without o
     if (a.dk == 32 && a.dv == 64)
-        return a.in_bf16 ? launch_fwd_recompute<32, 64, uint16_t>(p, a, s) : launch_fwd_recompute<32, 64, float>(p, a, s);
+        return a.in_bf16 ? launch_fwd_pipeline<32, 64, uint16_t, float>(p, a, s, false, true)
+                         : launch_fwd_pipeline<32, 64, float, float>(p, a, s, false, true);
     if (a.dk == 64 && a.dv == 64)
-        return a.in_bf16 ? launch_fwd_recompute<64, 64, uint16_t>(p, a, s) : launch_fwd_recompute<64, 64, float>(p, a, s);
+        return a.in_bf16 ? launch_fwd_pipeline<64, 64, uint16_t, float>(p, a, s, false, true)
+                         : launch_fwd_pipeline<64, 64, float, float>(p, a, s, false, true);
     if (a.dk == 128 && a.dv == 128)
-        return a.in_bf16 ? launch_fwd_recompute<128, 128, uint16_t>(p, a, s)
-                         : launch_fwd_recompute<128, 128, float>(p, a, s);
+        return a.in_bf16 ? launch_fwd_pipeline<128, 128, uint16_t, float>(p, a, s, false, true)
+                         : launch_fwd_pipeline<128, 128, float, float>(p, a, s, false, true);
     return hipErrorInvalidValue;
 }
 
@@ -278,12 +253,7 @@ template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
     const WsLayout L = ws_layout(a, false);
     const Prm p = make_prm(a, L);
-    hipError_t e = launch_fwd_recompute<DK, DV, TIn>(p, a, s);
-    if (e != hipSuccess || a.n_chunks_bound == 0) return e;
-    constexpr int OB = DV < 64 ? DV : 64;
-    KDA_LAUNCH("fwd_output", (fwd_output_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H, DV / OB),
-               dim3(kThreads), s, p);
-    return hipSuccess;
+    return launch_fwd_pipeline<DK, DV, TIn, TOut>(p, a, s, true, DK > 64);
 }
 
 template <int DK, int DV>

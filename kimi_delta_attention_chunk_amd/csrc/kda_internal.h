@@ -53,6 +53,7 @@ struct ChunkArgs {
 // arrays are 0 (absent) in a forward layout.
 struct WsLayout {
     size_t w, u, aqk, tm, hs, vn;                    // forward recompute
+    size_t qg, khT, gl;                              // per-chunk operands of the scan
     size_t dhs, dvn;                                 // backward state pass
     size_t dqt, dkh, dwv, daq, dtv, dgl, dbv;        // dv-side intermediates
     size_t dkt, dxq, dxk, part_a, part_dt;           // dk-side intermediates

@@ -1,0 +1,380 @@
+// kda_intra.cuh -- the intra-chunk kernel: everything of a chunk that does not
+// depend on the state entering it.
+//
+// Per (chunk, head), 256 threads, channels processed in blocks of 32:
+//   pass 1 (per channel block): stage k, q (L2-normalised if flagged; the row
+//     norms are taken first over all channels), the per-token log-decay g
+//     (from f, A_log, dt_bias if flagged) and its in-chunk cumulative sum G
+//     (a scan over the 64 tokens in registers and cross-lane shuffles); write
+//     exp(G) q and (k exp(G_L - G))^T and exp(G_L); accumulate the Gram
+//     matrices Akk and Aqk.
+//   Gram matrices by 16x16 blocks: for a row block I and an earlier column
+//     block J, the decay is factored through r = 16 I (the first row of I):
+//       exp(G_t - G_s) = exp(G_t - G_r) * exp(G_r - G_s),   s < r <= t,
+//     both factors at most 1, so the block is an MFMA product of two scaled
+//     operands.  Diagonal blocks take the exact exp of each (t, s) difference.
+//   solve: T = (I + Akk)^{-1} (kda_chunk.cuh, fp32).
+//   pass 2: w = T beta exp(G) k  (per channel block) and u = T beta v (per
+//     32-column block of v), as MFMA products.
+// Outputs (fp32 workspace, slot = chunk * H + head): w [64][DK], u [64][DV],
+// qg = exp(G) q^ [64][DK], khT = (k^ exp(G_L - G))^T [DK][64], gl = exp(G_L)
+// [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested.
+#pragma once
+
+#include "kda_chunk.cuh"
+#include "kda_mma.cuh"
+
+namespace kda {
+
+constexpr int kCB32 = 32;        // channels per block
+constexpr int kLB = kCB32 + 4;   // row stride of [token][channel-block] tiles
+
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ float wave_scan(float x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Load 8 consecutive elements of one token row (16-byte aligned) as fp32.
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(v[i] << 16);
+        x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+
+// In-chunk inclusive cumulative sum over t of one channel block held in
+// registers (thread = 4 t + part, 8 channels), across the four waves (wave w
+// holds rows 16 w .. 16 w + 15).  wsum: LDS scratch [4][32].  Contains
+// barriers.
+__device__ __forceinline__ void cumsum_rows(float (&G)[8], float* wsum) {
+    const int part = threadIdx.x & 3;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // scan over the 16 rows of this wave (lanes 4 apart hold consecutive rows)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float x = G[i];
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        G[i] = x;
+    }
+    __syncthreads();  // wsum free
+    if (lane >= 60) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wsum[wave * 32 + 8 * part + i] = G[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float pre = 0.f;
+        for (int w = 0; w < wave; ++w) pre += wsum[w * 32 + 8 * part + i];
+        G[i] += pre;
+    }
+}
+
+// The p-th pair (t, s), s <= t, of the four 16x16 diagonal blocks (136 each).
+__device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
+    const int I = p / 136, q = p - 136 * I;
+    int tl = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+    if ((tl + 1) * (tl + 2) / 2 <= q) ++tl;
+    if (tl * (tl + 1) / 2 > q) --tl;
+    t = 16 * I + tl;
+    s = 16 * I + q - tl * (tl + 1) / 2;
+}
+
+// Gram tile list: pairs (I, J), J < I, of 16x16 blocks below the diagonal.
+__device__ __forceinline__ void gram_pair(int p, int& I, int& J) {
+    // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    I = p < 1 ? 1 : (p < 3 ? 2 : 3);
+    J = p - (I * (I - 1)) / 2;
+}
+// row offset of the column-factor rows for row block I inside Kc
+__device__ __forceinline__ int kc_off(int I) { return (I - 1) * I * 8; }  // 0, 16, 48
+
+template <int DK, int DV, typename TIn, Prec P>
+__global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
+    constexpr int NB = DK / kCB32, NVB = DV / 32;
+    // LDS (about 77 KB, two workgroups per CU):
+    //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: BT tile and solve scratch
+    //   S1   Kr | Qr | Kc   MFMA tiles of the off-diagonal Gram blocks; then Akk (fp32); then T (tile)
+    //   Tm   T, fp32 (the solve)
+    constexpr int LB8 = kCB32 + 8, LA = kChunk + 8;
+    constexpr int S1F = (48 + 48 + 96) * LB8;
+    __shared__ __attribute__((aligned(16))) float KQG[3 * kChunk * kLB];
+    __shared__ __attribute__((aligned(16))) float S1[S1F];
+    __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
+    __shared__ float bet[kChunk];
+    __shared__ float wsum[4 * 32];
+    __shared__ float Gref[4 * 32];       // G at rows 16, 32, 48 and at the last row
+    static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
+    static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
+
+    float* Kb = KQG;
+    float* Qb = KQG + kChunk * kLB;
+    float* Gb = KQG + 2 * kChunk * kLB;
+    float* X = KQG + kCB32 * LA;         // solve scratch (after pass 1)
+    const Tile<P> Kr(S1, 48, LB8);
+    const Tile<P> Qr(S1 + 48 * LB8, 48, LB8);
+    const Tile<P> Kc(S1 + 96 * LB8, 96, LB8);
+    float* A = S1;                        // fp32 Akk, after pass 1
+    const Tile<P> Tt(S1, kChunk, LA);     // T as an MFMA operand, after the solve
+    const Tile<P> BT(KQG, kCB32, LA);     // (beta exp(G) k)^T or (beta v)^T of one block
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const ChunkRef cr = p.seq.chunk(c);
+    if (cr.len == 0) return;
+    const size_t slot = (size_t)c * p.H + h;
+    const int wave = threadIdx.x >> 6;
+    const int tr = threadIdx.x >> 2, part = threadIdx.x & 3;  // staging row / channel group
+    const bool l2 = p.flags & 1u;
+    const TIn* qin = (const TIn*)p.q;
+    const TIn* kin = (const TIn*)p.k;
+    const TIn* vin = (const TIn*)p.v;
+    const int last = cr.len - 1;
+    const bool in = tr < cr.len;
+
+    // ---- every global load of the chunk, issued up front
+    float kx[NB][8], qx[NB][8], G[NB][8], vx[NVB][8];
+    float braw = 0.f;
+    (void)Gb;
+    if (threadIdx.x < kChunk && threadIdx.x < cr.len) braw = p.beta[(size_t)(cr.t0 + threadIdx.x) * p.H + h];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if (in) {
+            const size_t base = tok_index(cr.t0 + tr, h, p.H, DK) + b * kCB32 + 8 * part;
+            load8<TIn>(kin + base, kx[b]);
+            load8<TIn>(qin + base, qx[b]);
+            load8<float>(p.g + base, G[b]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kx[b][i] = qx[b][i] = G[b][i] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+        if (in) load8<TIn>(vin + tok_index(cr.t0 + tr, h, p.H, DV) + 32 * vb + 8 * part, vx[vb]);
+        else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vx[vb][i] = 0.f;
+        }
+    }
+    // ---- preparation in registers: beta, L2 norms, gate, in-chunk cumulative decay
+    if (threadIdx.x < kChunk) bet[threadIdx.x] = (p.flags & 4u) ? (threadIdx.x < cr.len ? sigmoid_f(braw) : 0.f) : braw;
+    if (l2) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { sk += kx[b][i] * kx[b][i]; sq += qx[b][i] * qx[b][i]; }
+        sk += __shfl_xor(sk, 1, 64); sk += __shfl_xor(sk, 2, 64);
+        sq += __shfl_xor(sq, 1, 64); sq += __shfl_xor(sq, 2, 64);
+        const float rk = 1.0f / sqrtf(sk + kL2Eps), rq = 1.0f / sqrtf(sq + kL2Eps);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { kx[b][i] *= rk; qx[b][i] *= rq; }
+    }
+    if ((p.flags & 2u) && in) {
+        const float eA = expf(p.A_log[h]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) G[b][i] = -eA * softplus_f(G[b][i] + p.dt_bias[h * DK + b * kCB32 + 8 * part + i]);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cumsum_rows(G[b], wsum);
+
+    // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,
+    // and this thread's 4 diagonal-block entries of each.
+    f32x4 gacc[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dkk[3] = {0.f, 0.f, 0.f}, dqk[3] = {0.f, 0.f, 0.f};
+
+    float* qg = p.qg + slot * kChunk * DK;
+    float* khT = p.khT + slot * DK * kChunk;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int cb = b * kCB32;
+        if (tr == 16 || tr == 32 || tr == 48 || tr == last) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (tr == last) Gref[3 * 32 + 8 * part + i] = G[b][i];
+                if (tr == 16 || tr == 32 || tr == 48) Gref[(tr / 16 - 1) * 32 + 8 * part + i] = G[b][i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            Kb[tr * kLB + 8 * part + i] = kx[b][i];
+            Qb[tr * kLB + 8 * part + i] = qx[b][i];
+            Gb[tr * kLB + 8 * part + i] = G[b][i];
+        }
+        __syncthreads();
+        // scaled operands for the off-diagonal Gram blocks, exp(G) q, k exp(G_L - G)
+        {
+            const int I = tr >> 4;
+            float qgv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int cc = 8 * part + i;
+                const float gt = G[b][i];
+                qgv[i] = __expf(gt) * qx[b][i];
+                khT[(size_t)(cb + cc) * kChunk + tr] = kx[b][i] * __expf(Gref[3 * 32 + cc] - gt);
+                if (I >= 1) {
+                    const float e = __expf(gt - Gref[(I - 1) * 32 + cc]);
+                    Kr.put(tr - 16, cc, kx[b][i] * e);
+                    Qr.put(tr - 16, cc, qx[b][i] * e);
+                }
+#pragma unroll
+                for (int J = 1; J <= 3; ++J)
+                    if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gref[(J - 1) * 32 + cc] - gt));
+            }
+            float* dst = qg + (size_t)tr * DK + cb + 8 * part;
+            *(f32x4*)dst = f32x4{qgv[0], qgv[1], qgv[2], qgv[3]};
+            *(f32x4*)(dst + 4) = f32x4{qgv[4], qgv[5], qgv[6], qgv[7]};
+        }
+        if (tr == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gref[3 * 32 + 8 * part + i]);
+        }
+        __syncthreads();
+        // off-diagonal Gram tiles
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int tau = wave + 4 * i;         // 0..11
+            const int pr = tau % 6, kind = tau / 6;  // kind 0: Akk, 1: Aqk
+            int I, J;
+            gram_pair(pr, I, J);
+            const Tile<P> Aop = (kind == 0 ? Kr : Qr).sub((I - 1) * 16);
+            gacc[i] = mma_tile(Aop, Kc.sub(kc_off(I) + 16 * J), 0, kCB32, gacc[i]);
+        }
+        // diagonal blocks, exact pairwise decays: the 4 x 136 pairs s <= t of the
+        // 16x16 diagonal blocks, packed over the threads
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int pidx = threadIdx.x + kThreads * i;
+            if (pidx < 4 * 136) {
+                int t, s;
+                diag_pair(pidx, t, s);
+                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aqv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c4 = 0; c4 < kCB32; c4 += 4) {
+                    const f32x4 gt = *(const f32x4*)&Gb[t * kLB + c4];
+                    const f32x4 gs = *(const f32x4*)&Gb[s * kLB + c4];
+                    const f32x4 ks = *(const f32x4*)&Kb[s * kLB + c4];
+                    const f32x4 kt = *(const f32x4*)&Kb[t * kLB + c4];
+                    const f32x4 qt = *(const f32x4*)&Qb[t * kLB + c4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float e = ks[m] * __expf(gt[m] - gs[m]);
+                        ak[m] += kt[m] * e;
+                        aqv[m] += qt[m] * e;
+                    }
+                }
+                dkk[i] += (ak[0] + ak[1]) + (ak[2] + ak[3]);
+                dqk[i] += (aqv[0] + aqv[1]) + (aqv[2] + aqv[3]);
+            }
+        }
+        __syncthreads();  // channel-block tiles are rewritten next
+    }
+
+    // ---- assemble Akk (LDS, rows times beta, over S1) and Aqk (workspace)
+    float* aq = p.aqk + slot * kChunk * kChunk;
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        const int t = e >> 6, s = e & 63;
+        if ((s >> 4) > (t >> 4)) {  // above the diagonal blocks
+            A[t * kLD + s] = 0.f;
+            aq[e] = 0.f;
+        }
+    }
+    // diagonal blocks: zero first, then the packed pairs s <= t
+    for (int e = threadIdx.x; e < 4 * 256; e += kThreads) {
+        const int I = e >> 8, t = 16 * I + ((e >> 4) & 15), s = 16 * I + (e & 15);
+        if (s >= t) {
+            A[t * kLD + s] = 0.f;
+            if (s > t) aq[t * kChunk + s] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int pidx = threadIdx.x + kThreads * i;
+        if (pidx < 4 * 136) {
+            int t, s;
+            diag_pair(pidx, t, s);
+            if (s < t) A[t * kLD + s] = bet[t] * dkk[i];
+            aq[t * kChunk + s] = dqk[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int tau = wave + 4 * i;
+        const int pr = tau % 6, kind = tau / 6;
+        int I, J;
+        gram_pair(pr, I, J);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * I + frag_row(r), s = 16 * J + frag_col();
+            if (kind == 0) A[t * kLD + s] = bet[t] * gacc[i][r];
+            else aq[t * kChunk + s] = gacc[i][r];
+        }
+    }
+    __syncthreads();
+    solve_unit_lower(A, Tm, X);  // ends with a barrier
+    if (p.tm) {
+        float* to = p.tm + slot * kChunk * kChunk;
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) to[e] = Tm[(e >> 6) * kLD + (e & 63)];
+    }
+
+    // ---- pass 2: w = T (beta exp(G) k) per channel block, u = T (beta v) per column block
+    for (int e = threadIdx.x; e < kChunk * kChunk / 4; e += kThreads) {
+        const int t = e >> 4, s4 = (e & 15) * 4;
+        Tt.put4(t, s4, *(const f32x4*)&Tm[t * kLD + s4]);
+    }
+    const float bt = bet[tr];
+    float* wo = p.w + slot * kChunk * DK;
+    float* uo = p.u + slot * kChunk * DV;
+#pragma unroll
+    for (int b = 0; b < NB + NVB; ++b) {
+        if (b < NB) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) BT.put(8 * part + i, tr, bt * __expf(G[b][i]) * kx[b][i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) BT.put(8 * part + i, tr, bt * vx[b - NB][i]);
+        }
+        __syncthreads();
+        float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
+        const int ld = b < NB ? DK : DV;
+        for (int tile = wave; tile < 8; tile += kWaves) {  // 4 x 2 tiles of [64 x 32]
+            const int tm = tile >> 1, tn = tile & 1;
+            int k0 = 0, k1 = 16 * (tm + 1);
+            widen<P>(k0, k1);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_tile(Tt.sub(tm * 16), BT.sub(tn * 16), k0, k1, acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * ld + tn * 16 + frag_col()] = acc[r];
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace kda
