@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "kda_chunk.cuh"
+#include "kda_bwdchunk.cuh"
 #include "kda_dhscan.cuh"
 #include "kda_internal.h"
 
@@ -645,8 +646,15 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
         KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
     }
     if (a.n_chunks_bound > 0) {
-        KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
-        KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+        if constexpr (DK == 32 && DV == 64) {
+            KDA_LAUNCH("bwd_chunk", (bwd_chunk_kernel<DV, TIn, TOut, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads),
+                       s, p);
+        } else {
+            KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+                       p);
+            KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+                       p);
+        }
     }
     if (a.flags & 2u) {
         KDA_LAUNCH("bwd_gate_sum", (bwd_gate_sum_kernel<DK>), dim3(a.H), dim3(kThreads), s, p, a.n_chunks_bound);
