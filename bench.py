@@ -135,12 +135,12 @@ def main():
     scale = dk ** -0.5
     flags = dict(A_log=A_log, dt_bias=dtb, l2norm_qk=True, gate_in_kernel=True, beta_logits=True,
                  out_dtype=out_dtype)
-    ws_f = torch.empty(kda.workspace_bytes((B, T, H, dk), dv, B, False), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(kda.workspace_bytes((B, T, H, dk), dv, B, True), dtype=torch.uint8, device=dev)
+    # one workspace: the forward keeps what the backward needs (save-for-backward)
+    ws = torch.empty(kda.workspace_bytes((B, T, H, dk), dv, B, True), dtype=torch.uint8, device=dev)
 
     def step():
-        o, hT = kda.fwd(q, k, v, f, b, scale, workspace=ws_f, **flags)
-        g = kda.bwd(q, k, v, f, b, scale, do, workspace=ws_b, need_dh0=False, **flags)
+        o, hT = kda.fwd(q, k, v, f, b, scale, workspace=ws, save_for_bwd=True, **flags)
+        g = kda.bwd(q, k, v, f, b, scale, do, workspace=ws, fwd_saved=True, need_dh0=False, **flags)
         return o, g
 
     for _ in range(args.warmup):

@@ -67,8 +67,21 @@ typedef enum kda_dtype { KDA_BF16 = 0, KDA_FP32 = 1 } kda_dtype;
 enum {
     KDA_F_QK_L2NORM = 1u << 0,
     KDA_F_GATE_IN_KERNEL = 1u << 1,
-    KDA_F_BETA_LOGITS = 1u << 2
+    KDA_F_BETA_LOGITS = 1u << 2,
+    KDA_F_SAVE_FOR_BWD = 1u << 3,
+    KDA_F_FWD_SAVED = 1u << 4
 };
+/* Saving the forward for the backward (the usual training pattern):
+ *   KDA_F_SAVE_FOR_BWD  (kda_fwd) also keep, in the workspace, the per-chunk
+ *                       quantities the backward needs (the UT inverse, the
+ *                       state entering every chunk, v_new); the workspace must
+ *                       then hold kda_bwd_workspace(desc) bytes.
+ *   KDA_F_FWD_SAVED     (kda_bwd) read them from `ws` instead of recomputing
+ *                       the forward.  `ws` must be the workspace of a kda_fwd
+ *                       call with KDA_F_SAVE_FOR_BWD on the same descriptor
+ *                       (other flags equal), inputs and varlen tables, with
+ *                       nothing written to it in between.  The results are
+ *                       identical to a backward that recomputes. */
 
 /* Problem descriptor.
  *   B      rows (B == 1 when packed)

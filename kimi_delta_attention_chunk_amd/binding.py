@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_BF16, KDA_FP32 = 0, 1
-F_QK_L2NORM, F_GATE_IN_KERNEL, F_BETA_LOGITS = 1, 2, 4
+F_QK_L2NORM, F_GATE_IN_KERNEL, F_BETA_LOGITS, F_SAVE_FOR_BWD, F_FWD_SAVED = 1, 2, 4, 8, 16
 CHUNK = 64
 
 EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd_workspace",
@@ -194,18 +194,22 @@ def _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias, gate_i
 
 def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=None,
         dt_bias=None, l2norm_qk=False, gate_in_kernel=False, beta_logits=False, out_dtype=None,
-        output_final_state=True, workspace=None):
-    """kda_fwd.  Returns (o [B,T,H,dv], hT [N,H,dk,dv] or None)."""
+        output_final_state=True, workspace=None, save_for_bwd=False):
+    """kda_fwd.  Returns (o [B,T,H,dv], hT [N,H,dk,dv] or None).
+
+    With save_for_bwd the workspace (which must then be sized for the backward)
+    keeps what kda_bwd(..., fwd_saved=True, workspace=same) needs.
+    """
     lib = load_library()
     B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias,
                                        gate_in_kernel)
     out_dtype = out_dtype or q.dtype
-    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits)
+    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_SAVE_FOR_BWD if save_for_bwd else 0)
     desc = _desc(q, v, N, scale, flags, out_dtype)
     dev = q.device
     o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
-    need = lib.kda_fwd_workspace(ctypes.byref(desc))
+    need = (lib.kda_bwd_workspace if save_for_bwd else lib.kda_fwd_workspace)(ctypes.byref(desc))
     if need == 0:
         _check(KDA_ERR_INVALID)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
@@ -218,8 +222,12 @@ def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=N
 
 def bwd(q, k, v, g, beta, scale, d_o, h0=None, dhT=None, cu_seqlens=None, plan=None, *,
         A_log=None, dt_bias=None, l2norm_qk=False, gate_in_kernel=False, beta_logits=False,
-        out_dtype=None, need_dh0=True, workspace=None):
-    """kda_bwd.  Returns dict dq, dk, dv, dg, dbeta, dh0 (and dA_log, ddt_bias with the gate)."""
+        out_dtype=None, need_dh0=True, workspace=None, fwd_saved=False):
+    """kda_bwd.  Returns dict dq, dk, dv, dg, dbeta, dh0 (and dA_log, ddt_bias with the gate).
+
+    fwd_saved: `workspace` holds a kda_fwd(..., save_for_bwd=True) of the same
+    inputs, so the forward is not recomputed.
+    """
     lib = load_library()
     B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias,
                                        gate_in_kernel)
@@ -227,7 +235,9 @@ def bwd(q, k, v, g, beta, scale, d_o, h0=None, dhT=None, cu_seqlens=None, plan=N
     _req(d_o, "d_o", q.dtype, (B, T, H, dv), dev)
     _req(dhT, "dhT", torch.float32, (N, H, dk, dv), dev, optional=True)
     out_dtype = out_dtype or q.dtype
-    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits)
+    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_FWD_SAVED if fwd_saved else 0)
+    if fwd_saved and workspace is None:
+        raise ValueError("fwd_saved needs the forward's workspace")
     desc = _desc(q, v, N, scale, flags, out_dtype)
     out = dict(
         dq=torch.empty((B, T, H, dk), dtype=out_dtype, device=dev),

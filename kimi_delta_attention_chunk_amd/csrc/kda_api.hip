@@ -33,7 +33,9 @@ int check_ptr(const void* p, const char* name, bool required) {
 
 bool dtype_ok(int d) { return d == KDA_BF16 || d == KDA_FP32; }
 
-const uint32_t kKnownFlags = KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS;
+const uint32_t kKnownFlags =
+    KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS | KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED;
+const uint32_t kStepFlags = KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS;
 
 int validate_desc(const kda_desc* d) {
     if (d == nullptr) return fail(KDA_ERR_INVALID, "desc must not be null");
@@ -191,7 +193,8 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     if (rc) return rc;
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
     if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(hT, "hT", false))) return rc;
-    const size_t need = kda::ws_layout(a, false).total;
+    if (desc->flags & KDA_F_FWD_SAVED) return fail(KDA_ERR_INVALID, "KDA_F_FWD_SAVED is a backward flag");
+    const size_t need = kda::ws_layout(a, (desc->flags & KDA_F_SAVE_FOR_BWD) != 0).total;
     if (ws == nullptr || ws_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
@@ -212,6 +215,7 @@ int kda_bwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
     if (rc) return rc;
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
+    if (desc->flags & KDA_F_SAVE_FOR_BWD) return fail(KDA_ERR_INVALID, "KDA_F_SAVE_FOR_BWD is a forward flag");
     const bool gate = desc->flags & KDA_F_GATE_IN_KERNEL;
     if ((rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dhT, "dhT", false)) ||
         (rc = check_ptr(dq, "dq", true)) || (rc = check_ptr(dk, "dk", true)) || (rc = check_ptr(dv, "dv", true)) ||
@@ -240,7 +244,7 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
     if (!kda::dims_supported(dk, dv))
         return fail(KDA_ERR_UNSUPPORTED, "head dims (dk=%d, dv=%d) not supported", dk, dv);
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return fail(KDA_ERR_INVALID, "bad dtype");
-    if (flags & ~kKnownFlags) return fail(KDA_ERR_INVALID, "unknown flag bits");
+    if (flags & ~kStepFlags) return fail(KDA_ERR_INVALID, "unknown flag bits");
     int rc;
     const bool gate = flags & KDA_F_GATE_IN_KERNEL;
     if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||

@@ -601,31 +601,29 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
 }
 
 // ============================================================== gate parameter sums
-// dA_log[h] = sum over chunks of part_a, ddt_bias[h][c] = sum of part_dt, each
-// in a fixed order: thread i takes chunks i, i + 256, ... and the partial sums
-// are then added in thread order.
+// dA_log[h] = sum over chunks of part_a, ddt_bias[h][c] = sum of part_dt.  One
+// workgroup per (head, column; column -1 = A_log): thread i takes chunks
+// i, i + 256, ... and the 256 partial sums are added by a fixed tree, so the
+// result does not depend on scheduling.
 template <int DK>
 __global__ void __launch_bounds__(kThreads) bwd_gate_sum_kernel(Prm p, int n_chunks) {
     __shared__ float red[kThreads];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    for (int col = -1; col < DK; ++col) {
-        float acc = 0.f;
-        for (int c = tid; c < n_chunks; c += kThreads) {
-            if (p.seq.chunk(c).len == 0) continue;
-            const size_t slot = (size_t)c * p.H + h;
-            acc += col < 0 ? p.part_a[slot] : p.part_dt[slot * DK + col];
-        }
-        red[tid] = acc;
+    const int h = blockIdx.x, col = (int)blockIdx.y - 1, tid = threadIdx.x;
+    float acc = 0.f;
+    for (int c = tid; c < n_chunks; c += kThreads) {
+        if (p.seq.chunk(c).len == 0) continue;
+        const size_t slot = (size_t)c * p.H + h;
+        acc += col < 0 ? p.part_a[slot] : p.part_dt[slot * DK + col];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) red[tid] += red[tid + off];
         __syncthreads();
-        for (int off = kThreads / 2; off > 0; off >>= 1) {
-            if (tid < off) red[tid] += red[tid + off];
-            __syncthreads();
-        }
-        if (tid == 0) {
-            if (col < 0) p.dA_log[h] = red[0];
-            else p.ddt_bias[h * DK + col] = red[0];
-        }
-        __syncthreads();
+    }
+    if (tid == 0) {
+        if (col < 0) p.dA_log[h] = red[0];
+        else p.ddt_bias[h * DK + col] = red[0];
     }
 }
 
@@ -636,8 +634,10 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     Prm p = make_prm(a, L);
     p.hT = nullptr;
     p.o = nullptr;
-    hipError_t e = launch_recompute(p, a, s);
-    if (e != hipSuccess) return e;
+    if (!(a.flags & (1u << 4))) {  // no forward saved in ws: recompute it
+        hipError_t e = launch_recompute(p, a, s);
+        if (e != hipSuccess) return e;
+    }
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     const int total = a.N * a.H * (DV / kBV);
     if constexpr (DK <= 64) {
@@ -657,7 +657,8 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
         }
     }
     if (a.flags & 2u) {
-        KDA_LAUNCH("bwd_gate_sum", (bwd_gate_sum_kernel<DK>), dim3(a.H), dim3(kThreads), s, p, a.n_chunks_bound);
+        KDA_LAUNCH("bwd_gate_sum", (bwd_gate_sum_kernel<DK>), dim3(a.H, DK + 1), dim3(kThreads), s, p,
+                   a.n_chunks_bound);
     }
     return hipSuccess;
 }

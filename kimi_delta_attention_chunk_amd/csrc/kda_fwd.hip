@@ -251,9 +251,10 @@ hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
 
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
-    const WsLayout L = ws_layout(a, false);
+    const bool save = a.flags & (1u << 3);
+    const WsLayout L = ws_layout(a, save);
     const Prm p = make_prm(a, L);
-    return launch_fwd_pipeline<DK, DV, TIn, TOut>(p, a, s, true, DK > 64);
+    return launch_fwd_pipeline<DK, DV, TIn, TOut>(p, a, s, true, save || DK > 64);
 }
 
 template <int DK, int DV>

@@ -154,3 +154,32 @@ def test_bwd_packed_config_row():
     got = run_bwd(d, 32 ** -0.5)
     ref = oracle_bwd(inp, 32 ** -0.5, cu=cu)
     compare(got, ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype,dims", [(torch.bfloat16, (32, 64)), (torch.float32, (32, 64)),
+                                        (torch.bfloat16, (128, 128))])
+def test_bwd_from_saved_forward_equals_recompute(dtype, dims):
+    """kda_fwd(save_for_bwd) + kda_bwd(fwd_saved) gives bitwise the same gradients as a
+    backward that recomputes the forward, and the same forward outputs."""
+    dk, dv = dims
+    raw = kda_inputs.draw(31, 2, 200, 4, dk, dv, h0_std=0.1, upstream=True, dhT=True,
+                          a_log_range=kda_inputs.A_LOG_RANGE_WEAK)
+    rin = raw_inputs(raw, dtype)
+    d = to_dev(rin)
+    kw = dict(A_log=d["A_log"], dt_bias=d["dt_bias"], l2norm_qk=True, gate_in_kernel=True,
+              beta_logits=True, out_dtype=torch.float32)
+    scale = dk ** -0.5
+    o1, h1 = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, h0=d["h0"], **kw)
+    ws = torch.empty(kda.workspace_bytes(tuple(d["q"].shape), dv, 2, True), dtype=torch.uint8,
+                     device="cuda")
+    o2, h2 = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, h0=d["h0"], workspace=ws,
+                     save_for_bwd=True, **kw)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    g_saved = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, d["do"], h0=d["h0"],
+                      dhT=d["dhT"], workspace=ws, fwd_saved=True, **kw)
+    g_rec = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, d["do"], h0=d["h0"],
+                    dhT=d["dhT"], **kw)
+    for nm in GRADS + ("dA_log", "ddt_bias"):
+        assert torch.equal(g_saved[nm], g_rec[nm]), nm
+    ref = oracle_bwd_raw(rin, scale)
+    compare(g_saved, ref, dtype, GRADS + ("dA_log", "ddt_bias"))
