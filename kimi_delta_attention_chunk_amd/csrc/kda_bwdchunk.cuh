@@ -34,7 +34,7 @@ namespace kda {
 
 template <int DV, typename TIn, typename TOut, Prec P>
 __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
-    constexpr int DK = 32, NVB = DV / 32, LR = DK + 4;
+    constexpr int DK = 32, NVB = DV / 32, LR = DK + 1;  // odd stride: lanes over tokens hit distinct banks
     constexpr int L40 = 40, L72 = 72, GV = DV / 16;
     constexpr int NT4 = kChunk * kChunk / 4 / kThreads;  // float4 of T per thread
     constexpr int NH4 = DK * DV / 4 / kThreads;          // float4 of h (and D)
@@ -126,6 +126,9 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         for (int i = 0; i < 8; ++i) { kx[i] *= rk; qx[i] *= rq; }
         if (part == 0) { rnk[tr] = rk; rnq[tr] = rq; }
     }
+    float graw_f[8];  // the raw gate input f (with the gate flag)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) graw_f[i] = graw[i];
     if (gate && in) {
         const float eA = expf(p.A_log[h]);
 #pragma unroll
@@ -522,9 +525,7 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     __syncthreads();
 
     // ------------------------------------------------ P5: dg, gate chain, outputs
-    float dotq = 0.f, dotk = 0.f;  // per lane (t = lane), this wave's channels
-    float pa_acc = 0.f;
-    const float eA = gate ? expf(p.A_log[h]) : 0.f;
+    // (a) lane = token: add dG_L to the last row, reverse in-chunk cumsum -> DG holds dg
     {
         const int t = lane;
         for (int cc = wave; cc < DK; cc += kWaves) {
@@ -536,39 +537,73 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
                 dG += sl + __expf(GL[cc]) * dgl[cc];
             }
             if (t >= cr.len) dG = 0.f;
-            // reverse in-chunk cumulative sum
             float sfx = dG;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float o = __shfl_down(sfx, off, 64);
                 if (t + off < 64) sfx += o;
             }
-            const float dQ = DQ[t * LR + cc], dK = DKa[t * LR + cc];
-            dotq += Qs[t * LR + cc] * dQ;
-            dotk += Ks[t * LR + cc] * dK;
-            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + cc;
-            float dgo = sfx;
-            if (gate) {
-                float dfv = 0.f;
-                if (t < cr.len) {
-                    const float x = p.g[gi] + p.dt_bias[h * DK + cc];
-                    dfv = sfx * (-eA) * dsoftplus_f(x);
-                    pa_acc += sfx * (-eA * softplus_f(x));
-                }
-                dgo = dfv;
-                const float colsum = wave_sum(dfv);
-                if (lane == 0) p.part_dt[slot * DK + cc] = colsum;
-            }
-            if (t < cr.len) {
-                p.dg[gi] = dgo;
-                if (!l2) {
-                    Elem<TOut>::store((TOut*)p.dq, gi, dQ);
-                    Elem<TOut>::store((TOut*)p.dk, gi, dK);
-                }
-            }
+            DG[t * LR + cc] = sfx;
         }
     }
-    __syncthreads();  // rowp (dbeta_A) read below, then reused
+    __syncthreads();
+    // (b) coalesced pass, thread = (row tr, 8 channels): gate, sigmoid and L2 chains, stores
+    {
+        const int t = tr;
+        float dgv[8], dqv[8], dkv[8], qh[8], kh[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int cc = 8 * part + i;
+            dgv[i] = DG[t * LR + cc];
+            dqv[i] = DQ[t * LR + cc];
+            dkv[i] = DKa[t * LR + cc];
+            qh[i] = Qs[t * LR + cc];
+            kh[i] = Ks[t * LR + cc];
+        }
+        float pa = 0.f;
+        if (gate) {
+            const float eA = expf(p.A_log[h]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // graw still holds this row's raw f (the staging layout is the same)
+                const float x = in ? graw_f[i] + p.dt_bias[h * DK + 8 * part + i] : 0.f;
+                const float df = in ? dgv[i] * (-eA) * dsoftplus_f(x) : 0.f;
+                pa += in ? dgv[i] * (-eA * softplus_f(x)) : 0.f;
+                dgv[i] = df;
+            }
+            // column sums of df over the chunk: 16 rows per wave (lanes 4 apart), then waves
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float cs = dgv[i];
+#pragma unroll
+                for (int off = 4; off < 64; off <<= 1) cs += __shfl_xor(cs, off, 64);
+                if (lane < 4) colp[wave * DK + 8 * part + i] = cs;
+            }
+        }
+        float dotq = 0.f, dotk = 0.f;
+        if (l2) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { dotq += qh[i] * dqv[i]; dotk += kh[i] * dkv[i]; }
+            dotq += __shfl_xor(dotq, 1, 64); dotq += __shfl_xor(dotq, 2, 64);
+            dotk += __shfl_xor(dotk, 1, 64); dotk += __shfl_xor(dotk, 2, 64);
+            const float r_q = rnq[t], r_k = rnk[t];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                dqv[i] = r_q * (dqv[i] - dotq * qh[i]);
+                dkv[i] = r_k * (dkv[i] - dotk * kh[i]);
+            }
+        }
+        if (in) {
+            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + 8 * part;
+            store8<TOut>((TOut*)p.dq + gi, dqv);
+            store8<TOut>((TOut*)p.dk + gi, dkv);
+            store8<float>(p.dg + gi, dgv);
+        }
+        if (gate) {
+            const float pw = wave_sum(pa);
+            if (lane == 0) wsum[wave] = pw;
+        }
+    }
     if (tid < kChunk) {
         const int t = tid;
         float db = 0.f;
@@ -581,35 +616,8 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         }
     }
     if (gate) {
-        const float pa = wave_sum(pa_acc);
-        if (lane == 0) wsum[wave] = pa;
-    }
-    if (l2) {
         __syncthreads();
-        rowp[wave * kChunk + lane] = dotq;
-        __syncthreads();
-        float dq_dot = 0.f;
-        if (tid < kChunk)
-            for (int w = 0; w < kWaves; ++w) dq_dot += rowp[w * kChunk + tid];
-        __syncthreads();
-        rowp[wave * kChunk + lane] = dotk;
-        __syncthreads();
-        float dk_dot = 0.f;
-        if (tid < kChunk)
-            for (int w = 0; w < kWaves; ++w) dk_dot += rowp[w * kChunk + tid];
-        __syncthreads();
-        if (tid < kChunk) { rowp[tid] = dq_dot; rowp[kChunk + tid] = dk_dot; }
-        __syncthreads();
-        // dx = r (dx^ - (x^ . dx^) x^)
-        for (int e = tid; e < cr.len * DK; e += kThreads) {
-            const int t = e / DK, cc = e - t * DK;
-            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + cc;
-            Elem<TOut>::store((TOut*)p.dq, gi, rnq[t] * (DQ[t * LR + cc] - rowp[t] * Qs[t * LR + cc]));
-            Elem<TOut>::store((TOut*)p.dk, gi, rnk[t] * (DKa[t * LR + cc] - rowp[kChunk + t] * Ks[t * LR + cc]));
-        }
-    }
-    if (gate) {
-        __syncthreads();
+        if (tid < DK) p.part_dt[slot * DK + tid] = (colp[tid] + colp[DK + tid]) + (colp[2 * DK + tid] + colp[3 * DK + tid]);
         if (tid == 0) p.part_a[slot] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     }
 }
