@@ -647,7 +647,7 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     }
     if (a.n_chunks_bound > 0) {
         if constexpr (DK == 32 && DV == 64) {
-            KDA_LAUNCH("bwd_chunk", (bwd_chunk_kernel<DV, TIn, TOut, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads),
+            KDA_LAUNCH("bwd_chunk", (bwd_chunk_kernel<DV, TIn, TOut, P>), dim3(a.n_chunks_bound, a.H), dim3(kBcThreads),
                        s, p);
         } else {
             KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,

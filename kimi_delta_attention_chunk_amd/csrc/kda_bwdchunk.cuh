@@ -1,11 +1,11 @@
 // kda_bwdchunk.cuh -- the per-chunk backward (everything but the state
-// gradient recurrence), one workgroup per (chunk, head), dk = 32.
+// gradient recurrence), one workgroup of 8 waves per (chunk, head), dk = 32.
 //
 // Given, for the chunk, the state h entering it and D = dL/dS at its end (from
-// the forward recompute and the reverse scan), v_new and dv_new, it forms the
-// gradients of the chunk form (kda_chunk.cuh) with respect to q, k, v, beta
-// and the log-decay, then the preparation chain.  With Qg = exp(G) q,
-// Kg = exp(G) k, Kh = k exp(G_L - G), u = T beta V, w = T beta Kg:
+// the forward and the reverse scan), v_new and dv_new, it forms the gradients
+// of the chunk form (kda_chunk.cuh) with respect to q, k, v, beta and the
+// log-decay, then the preparation chain.  With Qg = exp(G) q, Kg = exp(G) k,
+// Kh = k exp(G_L - G), u = T beta V, w = T beta Kg:
 //   P1  dQg = scale dO h^T, dAqk = scale dO vn^T (s <= t), dKh = vn D^T,
 //       dw = -dvn h^T, dT_v = dvn (beta V)^T, and through u:
 //       dV = beta (T^T dvn), dbeta += rowsum((T^T dvn) V); dGamma_L = rowsum(h D)
@@ -24,6 +24,11 @@
 //       gate, sigmoid and L2-norm chains.
 // Gradient accumulators DQ, DK, DG live in LDS (fp32); every element is owned
 // by one lane in each phase, so no atomics are used.
+//
+// Latency: the workgroup holds ~156 KB of LDS, so one runs per CU; 8 waves
+// give two per SIMD to cover LDS and MFMA latency.  Epilogues read their LDS
+// operands unconditionally (selects, not branches) so the reads issue
+// together, and cross-lane sums use DPP / permlane swaps.
 #pragma once
 
 #include "kda_chunk.cuh"
@@ -32,13 +37,74 @@
 
 namespace kda {
 
+constexpr int kBcThreads = 512, kBcWaves = 8;
+
+template <typename TIn>
+__device__ __forceinline__ void load4(const TIn* p, float (&x)[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float (&x)[4]) {
+    const f32x4 a = *(const f32x4*)p;
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float (&x)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = *(const u32x2*)p;
+    x[0] = __uint_as_float(v[0] << 16);
+    x[1] = __uint_as_float(v[0] & 0xffff0000u);
+    x[2] = __uint_as_float(v[1] << 16);
+    x[3] = __uint_as_float(v[1] & 0xffff0000u);
+}
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* p, const float (&x)[4]);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float (&x)[4]) {
+    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v;
+    v[0] = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    v[1] = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    *(u32x2*)p = v;
+}
+
+// Inclusive cumulative sum over the 64 rows of the 32 columns of A (row
+// stride ld), forward or in reverse, in place, by 512 threads: thread (s, c)
+// scans rows 4s .. 4s+3 of column c, then adds the totals of the segments
+// before (after) it.  seg: LDS [16][32].  Ends with a barrier.
+template <bool REV>
+__device__ __forceinline__ void col_scan64x32(float* A, int ld, float* seg, float (&x)[4]) {
+    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    if (!REV) {
+        x[1] += x[0]; x[2] += x[1]; x[3] += x[2];
+        seg[sg * 32 + c] = x[3];
+    } else {
+        x[2] += x[3]; x[1] += x[2]; x[0] += x[1];
+        seg[sg * 32 + c] = x[0];
+    }
+    __syncthreads();
+    float off = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float v = seg[j * 32 + c];
+        off += (REV ? j > sg : j < sg) ? v : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[(4 * sg + i) * ld + c] = x[i] + off;
+    __syncthreads();
+}
+
 template <int DV, typename TIn, typename TOut, Prec P>
-__global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
+__global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
+    constexpr int NTH = kBcThreads, NW = kBcWaves;
     constexpr int DK = 32, NVB = DV / 32, LR = DK + 1;  // odd stride: lanes over tokens hit distinct banks
     constexpr int L40 = 40, L72 = 72, GV = DV / 16;
-    constexpr int NT4 = kChunk * kChunk / 4 / kThreads;  // float4 of T per thread
-    constexpr int NH4 = DK * DV / 4 / kThreads;          // float4 of h (and D)
-    constexpr int NV4 = kChunk * DV / 4 / kThreads;      // float4 of vn (and dvn)
+    constexpr int NT4 = kChunk * kChunk / 4 / NTH;  // float4 of T per thread
+    constexpr int NH4 = DK * DV / 4 / NTH;          // float4 of h (and D)
+    constexpr int NV4 = kChunk * DV / 4 / NTH;      // float4 of vn (and dvn)
+    static_assert(NT4 >= 1 && NH4 >= 1 && NV4 >= 1, "shapes");
     __shared__ __attribute__((aligned(16))) float Ks[kChunk * LR];
     __shared__ __attribute__((aligned(16))) float Qs[kChunk * LR];
     __shared__ __attribute__((aligned(16))) float Gs[kChunk * LR];
@@ -47,9 +113,9 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     __shared__ __attribute__((aligned(16))) float DG[kChunk * LR];
     __shared__ float dAd[4 * 16 * 17], dAqd[4 * 16 * 17];  // diagonal blocks of dA, dAq
     __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
-    __shared__ float wsum[4 * 32];
-    __shared__ float GL[DK], dgl[DK], colp[4 * DK];
-    __shared__ float dbv[kChunk * GV], dbw[kChunk * 2], dba[kChunk * 2], rowp[kWaves * kChunk];
+    __shared__ float seg[16 * 32], wsum[NW];
+    __shared__ float GL[DK], dgl[DK], colp[NW * DK];
+    __shared__ float dbv[kChunk * GV], dbw[kChunk * 2], dba[kChunk * 2], rowp[NW * kChunk];
     constexpr int PH = 23040;
     __shared__ __attribute__((aligned(16))) float ph[PH];
 
@@ -58,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     if (cr.len == 0) return;
     const size_t slot = (size_t)c * p.H + h;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tr = tid >> 2, part = tid & 3;
+    const int tr = tid >> 3, part = tid & 7;  // row-wise work: token tr, channels 4 part .. 4 part + 3
     const bool l2 = p.flags & 1u, gate = p.flags & 2u;
     const TIn* qin = (const TIn*)p.q;
     const TIn* kin = (const TIn*)p.k;
@@ -71,21 +137,21 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ every global load, up front
     float braw = 0.f;
     if (tid < kChunk && tid < cr.len) braw = p.beta[(size_t)(cr.t0 + tid) * p.H + h];
-    float kx[8], qx[8], G[8], graw[8], vx[NVB][8], dox[NVB][8];
+    float kx[4], qx[4], G[4], graw[4], vx[NVB][4], dox[NVB][4];
     if (in) {
-        const size_t base = tok_index(cr.t0 + tr, h, p.H, DK) + 8 * part;
-        load8<TIn>(kin + base, kx);
-        load8<TIn>(qin + base, qx);
-        load8<float>(p.g + base, graw);
+        const size_t base = tok_index(cr.t0 + tr, h, p.H, DK) + 4 * part;
+        load4<TIn>(kin + base, kx);
+        load4<TIn>(qin + base, qx);
+        load4<float>(p.g + base, graw);
 #pragma unroll
         for (int b = 0; b < NVB; ++b) {
-            const size_t vb = tok_index(cr.t0 + tr, h, p.H, DV) + 32 * b + 8 * part;
-            load8<TIn>(vin + vb, vx[b]);
-            load8<TIn>(doin + vb, dox[b]);
+            const size_t vb = tok_index(cr.t0 + tr, h, p.H, DV) + 32 * b + 4 * part;
+            load4<TIn>(vin + vb, vx[b]);
+            load4<TIn>(doin + vb, dox[b]);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             kx[i] = qx[i] = graw[i] = 0.f;
 #pragma unroll
             for (int b = 0; b < NVB; ++b) vx[b][i] = dox[b][i] = 0.f;
@@ -99,11 +165,11 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         const f32x4* v4 = (const f32x4*)(p.vn + slot * kChunk * DV);
         const f32x4* w4 = (const f32x4*)(p.dvn + slot * kChunk * DV);
 #pragma unroll
-        for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + kThreads * i];
+        for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + NTH * i];
 #pragma unroll
-        for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + kThreads * i]; Dr[i] = d4[tid + kThreads * i]; }
+        for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
 #pragma unroll
-        for (int i = 0; i < NV4; ++i) { Vn[i] = v4[tid + kThreads * i]; dVn[i] = w4[tid + kThreads * i]; }
+        for (int i = 0; i < NV4; ++i) { Vn[i] = v4[tid + NTH * i]; dVn[i] = w4[tid + NTH * i]; }
     }
 
     // ------------------------------------------------ preparation (registers), resident tiles
@@ -113,70 +179,69 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         dba[2 * tid] = 0.f;
         dba[2 * tid + 1] = 0.f;
     }
-    float rk = 1.f, rq = 1.f;
     if (l2) {
         float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { sk += kx[i] * kx[i]; sq += qx[i] * qx[i]; }
-        sk += __shfl_xor(sk, 1, 64); sk += __shfl_xor(sk, 2, 64);
-        sq += __shfl_xor(sq, 1, 64); sq += __shfl_xor(sq, 2, 64);
-        rk = 1.0f / sqrtf(sk + kL2Eps);
-        rq = 1.0f / sqrtf(sq + kL2Eps);
+        for (int i = 0; i < 4; ++i) { sk += kx[i] * kx[i]; sq += qx[i] * qx[i]; }
+        sk = sum8(sk);
+        sq = sum8(sq);
+        const float rk = 1.0f / sqrtf(sk + kL2Eps), rq = 1.0f / sqrtf(sq + kL2Eps);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { kx[i] *= rk; qx[i] *= rq; }
+        for (int i = 0; i < 4; ++i) { kx[i] *= rk; qx[i] *= rq; }
         if (part == 0) { rnk[tr] = rk; rnq[tr] = rq; }
     }
-    float graw_f[8];  // the raw gate input f (with the gate flag)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) graw_f[i] = graw[i];
+    const float graw_f[4] = {graw[0], graw[1], graw[2], graw[3]};  // the raw gate input f (gate flag)
     if (gate && in) {
         const float eA = expf(p.A_log[h]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) graw[i] = -eA * softplus_f(graw[i] + p.dt_bias[h * DK + 8 * part + i]);
+        for (int i = 0; i < 4; ++i) graw[i] = -eA * softplus_f(graw[i] + p.dt_bias[h * DK + 4 * part + i]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) G[i] = graw[i];
-    cumsum_rows(G, wsum);  // barriers inside
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int cc = 8 * part + i;
+    for (int i = 0; i < 4; ++i) {
+        const int cc = 4 * part + i;
         Ks[tr * LR + cc] = kx[i];
         Qs[tr * LR + cc] = qx[i];
-        Gs[tr * LR + cc] = G[i];
-        DQ[tr * LR + cc] = 0.f;
-        DKa[tr * LR + cc] = 0.f;
-        DG[tr * LR + cc] = 0.f;
-        if (tr == last) GL[cc] = G[i];
+        Gs[tr * LR + cc] = graw[i];
     }
     // dGamma_L = rowsum(h . D): 16 consecutive lanes share one row c per float4 slot
-    {
 #pragma unroll
-        for (int i = 0; i < NH4; ++i) {
-            const int e4 = 4 * (tid + kThreads * i);
-            const int cc = e4 / DV;
-            float s = Hr[i][0] * Dr[i][0] + Hr[i][1] * Dr[i][1] + Hr[i][2] * Dr[i][2] + Hr[i][3] * Dr[i][3];
-            constexpr int LPR = DV / 4;  // lanes per row of h
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off, 64);
-            if ((tid % LPR) == 0) dgl[cc] = s;
-        }
+    for (int i = 0; i < NH4; ++i) {
+        const int e4 = 4 * (tid + NTH * i);
+        const int cc = e4 / DV;
+        const float s = sum16(Hr[i][0] * Dr[i][0] + Hr[i][1] * Dr[i][1] + Hr[i][2] * Dr[i][2] + Hr[i][3] * Dr[i][3]);
+        static_assert(DV == 64, "one row of h per 16 lanes");
+        if ((lane & 15) == 0) dgl[cc] = s;
     }
     __syncthreads();
+    {
+        // in-chunk cumulative log-decay G, in place in Gs
+        float x[4];
+        const int cs = tid & 31, sg = tid >> 5;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = Gs[(4 * sg + i) * LR + cs];
+        col_scan64x32<false>(Gs, LR, seg, x);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) G[i] = Gs[tr * LR + 4 * part + i];
+    if (tr == last) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) GL[4 * part + i] = G[i];
+    }
 
     // ------------------------------------------------ P1: contractions over dv
     const Tile<P> TT(ph, kChunk, L72);  // T^T [t][s], phases 1-3
 #pragma unroll
     for (int i = 0; i < NT4; ++i) {
-        const int e4 = 4 * (tid + kThreads * i);
+        const int e4 = 4 * (tid + NTH * i);
         const int s = e4 >> 6, t = e4 & 63;  // T[s][t .. t+3]
 #pragma unroll
         for (int m = 0; m < 4; ++m) TT.put(t + m, s, Tr[i][m]);
     }
-    f32x4 aQ[2], aKh[2], aW[2], aAq[4], aT[4];
+    // [64 x 32] results: wave w owns tile (w >> 1, w & 1); [64 x 64]: tiles w, w + 8 -> (tile >> 2, tile & 3)
+    const int am = wave >> 1, an = wave & 1;
+    f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aKh = aQ, aW = aQ, aAq[2], aT[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) aQ[i] = aKh[i] = aW[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aAq[i] = aT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) aAq[i] = aT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
         const Tile<P> dOb(ph + 4608, kChunk, L40), vnb(ph + 7168, kChunk, L40), dvnb(ph + 9728, kChunk, L40),
             bVb(ph + 12288, kChunk, L40), hb(ph + 14848, DK, L40), Db(ph + 16128, DK, L40),
@@ -187,18 +252,15 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         for (int vbk = 0; vbk < NVB; ++vbk) {
             const int jb = 32 * vbk;
             __syncthreads();  // previous block's tiles consumed
-            dOb.put4(tr, 8 * part, f32x4{dox[vbk][0], dox[vbk][1], dox[vbk][2], dox[vbk][3]});
-            dOb.put4(tr, 8 * part + 4, f32x4{dox[vbk][4], dox[vbk][5], dox[vbk][6], dox[vbk][7]});
             {
                 const float b = bet[tr];
-                bVb.put4(tr, 8 * part, f32x4{b * vx[vbk][0], b * vx[vbk][1], b * vx[vbk][2], b * vx[vbk][3]});
-                bVb.put4(tr, 8 * part + 4, f32x4{b * vx[vbk][4], b * vx[vbk][5], b * vx[vbk][6], b * vx[vbk][7]});
-                *(f32x4*)&Vf[tr * 36 + 8 * part] = f32x4{vx[vbk][0], vx[vbk][1], vx[vbk][2], vx[vbk][3]};
-                *(f32x4*)&Vf[tr * 36 + 8 * part + 4] = f32x4{vx[vbk][4], vx[vbk][5], vx[vbk][6], vx[vbk][7]};
+                dOb.put4(tr, 4 * part, f32x4{dox[vbk][0], dox[vbk][1], dox[vbk][2], dox[vbk][3]});
+                bVb.put4(tr, 4 * part, f32x4{b * vx[vbk][0], b * vx[vbk][1], b * vx[vbk][2], b * vx[vbk][3]});
+                *(f32x4*)&Vf[tr * 36 + 4 * part] = f32x4{vx[vbk][0], vx[vbk][1], vx[vbk][2], vx[vbk][3]};
             }
 #pragma unroll
             for (int i = 0; i < NV4; ++i) {
-                const int e4 = 4 * (tid + kThreads * i);
+                const int e4 = 4 * (tid + NTH * i);
                 const int t = e4 / DV, j = e4 - t * DV;
                 if (j >= jb && j < jb + 32) {
                     vnb.put4(t, j - jb, Vn[i]);
@@ -209,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
             }
 #pragma unroll
             for (int i = 0; i < NH4; ++i) {
-                const int e4 = 4 * (tid + kThreads * i);
+                const int e4 = 4 * (tid + NTH * i);
                 const int cc = e4 / DV, j = e4 - cc * DV;
                 if (j >= jb && j < jb + 32) {
                     hb.put4(cc, j - jb, Hr[i]);
@@ -217,59 +279,64 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
                 }
             }
             __syncthreads();
+            aQ = mma_tile(dOb.sub(16 * am), hb.sub(16 * an), 0, 32, aQ);
+            aKh = mma_tile(vnb.sub(16 * am), Db.sub(16 * an), 0, 32, aKh);
+            aW = mma_tile(dvnb.sub(16 * am), hb.sub(16 * an), 0, 32, aW);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {  // [64 x 32] tiles
-                const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
-                aQ[i] = mma_tile(dOb.sub(16 * tm), hb.sub(16 * tn), 0, 32, aQ[i]);
-                aKh[i] = mma_tile(vnb.sub(16 * tm), Db.sub(16 * tn), 0, 32, aKh[i]);
-                aW[i] = mma_tile(dvnb.sub(16 * tm), hb.sub(16 * tn), 0, 32, aW[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {  // [64 x 64] tiles
-                const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+            for (int i = 0; i < 2; ++i) {
+                const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
                 aAq[i] = mma_tile(dOb.sub(16 * tm), vnb.sub(16 * tn), 0, 32, aAq[i]);
                 aT[i] = mma_tile(dvnb.sub(16 * tm), bVb.sub(16 * tn), 0, 32, aT[i]);
             }
             // X_u = T^T dvn: dV = beta X_u, dbeta_v = rowsum(X_u V)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
-                int k0 = 16 * tm, k1 = kChunk;
+            {
+                int k0 = 16 * am, k1 = kChunk;
                 widen<P>(k0, k1);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_tile(TT.sub(16 * tm), dvnT.sub(16 * tn), k0, k1, acc);
+                acc = mma_tile(TT.sub(16 * am), dvnT.sub(16 * an), k0, k1, acc);
+                float bt[4], vv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tm + frag_row(r), j = 16 * tn + frag_col();
-                    const float bt = bet[t];
-                    if (t < cr.len) Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, bt * acc[r]);
-                    const float part_v = row16_sum(acc[r] * Vf[t * 36 + j]);
-                    if (frag_col() == 0) dbv[t * GV + 2 * vbk + tn] = part_v;
+                    const int t = 16 * am + frag_row(r), j = 16 * an + frag_col();
+                    bt[r] = bet[t];
+                    vv[r] = Vf[t * 36 + j];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * am + frag_row(r), j = 16 * an + frag_col();
+                    const float part_v = row16_sum(acc[r] * vv[r]);
+                    if (frag_col() == 0) dbv[t * GV + 2 * vbk + an] = part_v;
+                    if (t < cr.len) Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, bt[r] * acc[r]);
                 }
             }
         }
     }
     // explicit factors of Qg and Kh, as the dQg and dKh tiles come out
+    {
+        const int cc = 16 * an + frag_col();
+        const float glc = GL[cc];
+        float gt[4], kt[4], qt[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
-        const int cc = 16 * tn + frag_col();
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * am + frag_row(r);
+            gt[r] = Gs[t * LR + cc];
+            kt[r] = Ks[t * LR + cc];
+            qt[r] = Qs[t * LR + cc];
+        }
         float colsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tm + frag_row(r);
-            const float gt = Gs[t * LR + cc], kt = Ks[t * LR + cc], qt = Qs[t * LR + cc];
-            const float gam = __expf(gt), eL = __expf(GL[cc] - gt);
-            const float dqg = scale * aQ[i][r], dkh = aKh[i][r];
-            const float kh = kt * eL;
+            const int t = 16 * am + frag_row(r);
+            const float gam = __expf(gt[r]), eL = __expf(glc - gt[r]);
+            const float dqg = scale * aQ[r], dkh = aKh[r];
+            const float kh = kt[r] * eL;
             DQ[t * LR + cc] = gam * dqg;
             DKa[t * LR + cc] = eL * dkh;
-            DG[t * LR + cc] = qt * gam * dqg - kh * dkh;
+            DG[t * LR + cc] = qt[r] * gam * dqg - kh * dkh;
             colsum += t < cr.len ? kh * dkh : 0.f;
         }
-        colsum += __shfl_xor(colsum, 16, 64);
-        colsum += __shfl_xor(colsum, 32, 64);
-        if (lane < 16) colp[tm * DK + cc] = colsum;
+        colsum = sum_rows(colsum);
+        if (lane < 16) colp[am * DK + cc] = colsum;
     }
 
     // ------------------------------------------------ P2: through w
@@ -278,77 +345,79 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         __syncthreads();  // P1 tiles consumed
         {
             const float b = bet[tr];
-            f32x4 v0, v1;
+            f32x4 v0;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                v0[m] = b * __expf(G[m]) * kx[m];
-                v1[m] = b * __expf(G[4 + m]) * kx[4 + m];
-            }
-            bKg.put4(tr, 8 * part, v0);
-            bKg.put4(tr, 8 * part + 4, v1);
+            for (int m = 0; m < 4; ++m) v0[m] = b * __expf(G[m]) * kx[m];
+            bKg.put4(tr, 4 * part, v0);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
-            const int cc = 16 * tn + frag_col();
+        {
+            const int cc = 16 * an + frag_col();
             f32x4 dw;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                dw[r] = -aW[i][r];
-                dwt.put(16 * tm + frag_row(r), cc, dw[r]);
+                dw[r] = -aW[r];
+                dwt.put(16 * am + frag_row(r), cc, dw[r]);
             }
-            dwT.put4(cc, 16 * tm + frag_row(0), dw);
+            dwT.put4(cc, 16 * am + frag_row(0), dw);
         }
         __syncthreads();
         // dT = dT_v + dw (beta Kg)^T   (dT_v already carries beta_s: it was formed with beta V)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
             aT[i] = mma_tile(dwt.sub(16 * tm), bKg.sub(16 * tn), 0, DK, aT[i]);
         }
         // X_w = T^T dw: dKg = beta X_w, dbeta_w = rowsum(X_w Kg)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
-            int k0 = 16 * tm, k1 = kChunk;
+        {
+            int k0 = 16 * am, k1 = kChunk;
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_tile(TT.sub(16 * tm), dwT.sub(16 * tn), k0, k1, acc);
-            const int cc = 16 * tn + frag_col();
+            acc = mma_tile(TT.sub(16 * am), dwT.sub(16 * an), k0, k1, acc);
+            const int cc = 16 * an + frag_col();
+            float gt[4], kt[4], bt[4], dk0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tm + frag_row(r);
-                const float gam = __expf(Gs[t * LR + cc]), kt = Ks[t * LR + cc];
-                const float kg = gam * kt, dkg = bet[t] * acc[r];
-                DKa[t * LR + cc] += gam * dkg;
-                DG[t * LR + cc] += kt * gam * dkg;
+                const int t = 16 * am + frag_row(r);
+                gt[r] = Gs[t * LR + cc];
+                kt[r] = Ks[t * LR + cc];
+                bt[r] = bet[t];
+                dk0[r] = DKa[t * LR + cc];
+                dg0[r] = DG[t * LR + cc];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * am + frag_row(r);
+                const float gam = __expf(gt[r]);
+                const float kg = gam * kt[r], dkg = bt[r] * acc[r];
+                DKa[t * LR + cc] = dk0[r] + gam * dkg;
+                DG[t * LR + cc] = dg0[r] + kt[r] * gam * dkg;
                 const float pb = row16_sum(acc[r] * kg);
-                if (frag_col() == 0) dbw[t * 2 + tn] = pb;
+                if (frag_col() == 0) dbw[t * 2 + an] = pb;
             }
         }
     }
 
     // ------------------------------------------------ P3: dA = -T^T dT T^T
-    f32x4 dAr[4];
+    f32x4 dAr[2];
     {
         const Tile<P> Trow(ph + 4608, kChunk, L72), dTt(ph + 9216, kChunk, L72), YT(ph + 13824, kChunk, L72);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
-            const int e4 = 4 * (tid + kThreads * i);
+            const int e4 = 4 * (tid + NTH * i);
             Trow.put4(e4 >> 6, e4 & 63, Tr[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
 #pragma unroll
             for (int r = 0; r < 4; ++r) dTt.put(16 * tm + frag_row(r), 16 * tn + frag_col(), aT[i][r]);
         }
         __syncthreads();
         // Y = dT T^T, stored transposed: YT[b][t]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
             int k0 = 0, k1 = 16 * (tn + 1);
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -357,8 +426,8 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (tn <= tm) {
                 int k0 = 16 * tm, k1 = kChunk;
@@ -374,8 +443,8 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     }
     // scale and mask dAqk (s <= t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+    for (int i = 0; i < 2; ++i) {
+        const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * tm + frag_row(r), s = 16 * tn + frag_col();
@@ -384,15 +453,19 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     }
 
     // ------------------------------------------------ P4: decayed pair sums
-    float r_dbA = 0.f;  // this lane's share of dbeta from Akk (rows t = lane, this wave's channels)
     {
         // row sums: R'k[t] = sum_{s<t} dA[t][s] k_s e^{G_t-G_s},  Rq[t] = sum_{s<=t} dAq[t][s] k_s e^{..}
         const Tile<P> dAt(ph, kChunk, L72), dAqt(ph + 4608, kChunk, L72);
         auto KcT = [&](int i) { return Tile<P>(ph + 9216 + 2304 * i, DK, L72); };
+        float gref[3][4];
+#pragma unroll
+        for (int I = 1; I <= 3; ++I)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gref[I - 1][i] = Gs[(16 * I) * LR + 4 * part + i];
         __syncthreads();  // P3 tiles consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tm + frag_row(r), s = 16 * tn + frag_col();
@@ -408,16 +481,15 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int I = 1; I <= 3; ++I) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int cc = 8 * part + i;
-                const float v = tr < 16 * I ? kx[i] * __expf(Gs[(16 * I) * LR + cc] - G[i]) : 0.f;
-                KcT(I - 1).put(cc, tr, v);
+            for (int i = 0; i < 4; ++i) {
+                const float e = __expf(gref[I - 1][i] - G[i]);
+                KcT(I - 1).put(4 * part + i, tr, tr < 16 * I ? kx[i] * e : 0.f);
             }
         }
         __syncthreads();
-        // 6 tasks: (I, column tile of c)
-        for (int task = wave; task < 6; task += kWaves) {
-            const int I = 1 + task / 2, tn = task & 1;
+        // 6 tasks: (I, column tile of c), on waves 0..5
+        if (wave < 6) {
+            const int I = 1 + (wave >> 1), tn = wave & 1;
             int k0 = 0, k1 = 16 * I;
             widen<P>(k0, k1);
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
@@ -426,16 +498,27 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
             aq = mma_tile(dAqt.sub(16 * I), kc.sub(16 * tn), k0, k1, aq);
             const int cc = 16 * tn + frag_col();
             const float gr = Gs[(16 * I) * LR + cc];
+            float gt[4], kt[4], qt[4], bt[4], dk0[4], dq0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * I + frag_row(r);
-                const float e = __expf(Gs[t * LR + cc] - gr);
+                gt[r] = Gs[t * LR + cc];
+                kt[r] = Ks[t * LR + cc];
+                qt[r] = Qs[t * LR + cc];
+                bt[r] = bet[t];
+                dk0[r] = DKa[t * LR + cc];
+                dq0[r] = DQ[t * LR + cc];
+                dg0[r] = DG[t * LR + cc];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * I + frag_row(r);
+                const float e = __expf(gt[r] - gr);
                 const float rkv = e * ak[r], rqv = e * aq[r];
-                const float kt = Ks[t * LR + cc], qt = Qs[t * LR + cc], bt = bet[t];
-                DKa[t * LR + cc] += bt * rkv;
-                DQ[t * LR + cc] += rqv;
-                DG[t * LR + cc] += bt * kt * rkv + qt * rqv;
-                const float pb = row16_sum(kt * rkv);
+                DKa[t * LR + cc] = dk0[r] + bt[r] * rkv;
+                DQ[t * LR + cc] = dq0[r] + rqv;
+                DG[t * LR + cc] = dg0[r] + bt[r] * kt[r] * rkv + qt[r] * rqv;
+                const float pb = row16_sum(kt[r] * rkv);
                 if (frag_col() == 0) dba[t * 2 + tn] = pb;
             }
         }
@@ -445,10 +528,15 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
         const Tile<P> bdAT(ph, kChunk, L72), dAqT(ph + 4608, kChunk, L72);
         auto KxT = [&](int j) { return Tile<P>(ph + 9216 + 2304 * j, DK, L72); };
         auto QxT = [&](int j) { return Tile<P>(ph + 16128 + 2304 * j, DK, L72); };
+        float gref[3][4];
+#pragma unroll
+        for (int J = 0; J < 3; ++J)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gref[J][i] = Gs[(16 * J + 15) * LR + 4 * part + i];
         __syncthreads();  // row-sum tiles consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 2, tn = tile & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
             const int s = 16 * tn + frag_col();
             f32x4 bd;
 #pragma unroll
@@ -460,17 +548,17 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int J = 0; J < 3; ++J) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int cc = 8 * part + i;
+            for (int i = 0; i < 4; ++i) {
+                const int cc = 4 * part + i;
                 const bool after = tr > 16 * J + 15;
-                const float e = after ? __expf(G[i] - Gs[(16 * J + 15) * LR + cc]) : 0.f;
+                const float e = after ? __expf(G[i] - gref[J][i]) : 0.f;
                 KxT(J).put(cc, tr, kx[i] * e);
                 QxT(J).put(cc, tr, qx[i] * e);
             }
         }
         __syncthreads();
-        for (int task = wave; task < 6; task += kWaves) {
-            const int J = task / 2, tn = task & 1;
+        if (wave < 6) {
+            const int J = wave >> 1, tn = wave & 1;
             int k0 = 16 * J + 16, k1 = kChunk;
             widen<P>(k0, k1);
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
@@ -478,13 +566,22 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
             aq = mma_tile(dAqT.sub(16 * J), QxT(J).sub(16 * tn), k0, k1, aq);
             const int cc = 16 * tn + frag_col();
             const float gr = Gs[(16 * J + 15) * LR + cc];
+            float gs[4], ks[4], dk0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * J + frag_row(r);
-                const float e = __expf(gr - Gs[s * LR + cc]);
+                gs[r] = Gs[s * LR + cc];
+                ks[r] = Ks[s * LR + cc];
+                dk0[r] = DKa[s * LR + cc];
+                dg0[r] = DG[s * LR + cc];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 16 * J + frag_row(r);
+                const float e = __expf(gr - gs[r]);
                 const float cs = e * (ak[r] + aq[r]);
-                DKa[s * LR + cc] += cs;
-                DG[s * LR + cc] -= Ks[s * LR + cc] * cs;
+                DKa[s * LR + cc] = dk0[r] + cs;
+                DG[s * LR + cc] = dg0[r] - ks[r] * cs;
             }
         }
         __syncthreads();
@@ -492,7 +589,10 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     // diagonal blocks, exact pairwise decays; lane = token t, waves take channels
     {
         const int t = lane, blk = t >> 4, t0b = blk * 16;
-        for (int cc = wave; cc < DK; cc += kWaves) {
+        float r_dbA = 0.f;  // this lane's share of dbeta from Akk
+#pragma unroll
+        for (int jc = 0; jc < DK / NW; ++jc) {
+            const int cc = wave + NW * jc;
             const float gt = Gs[t * LR + cc], kt = Ks[t * LR + cc], qt = Qs[t * LR + cc];
             float rkv = 0.f, rqv = 0.f, ck = 0.f, cq = 0.f;
 #pragma unroll
@@ -503,101 +603,87 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
                 const float aq_ts = dAqd[blk * 272 + (t & 15) * 17 + u];  // dAq[t][s]
                 const float ad_st = dAd[blk * 272 + u * 17 + (t & 15)];   // dA[s][t]
                 const float aq_st = dAqd[blk * 272 + u * 17 + (t & 15)];  // dAq[s][t]
-                if (s <= t) {
-                    const float e = __expf(gt - gs) * ks;
-                    rkv += ad_ts * e;
-                    rqv += aq_ts * e;
-                }
-                if (s >= t) {
-                    const float e = __expf(gs - gt);
-                    ck += bet[s] * ad_st * ks * e;
-                    cq += aq_st * qs * e;
-                }
+                const bool lo = u <= (t & 15), hi = u >= (t & 15);
+                const float el = __expf(lo ? gt - gs : 0.f) * ks;   // s <= t: e^{G_t - G_s} k_s
+                const float eh = __expf(hi ? gs - gt : 0.f);        // s >= t: e^{G_s - G_t}
+                rkv += lo ? ad_ts * el : 0.f;
+                rqv += lo ? aq_ts * el : 0.f;
+                ck += hi ? bet[s] * ad_st * ks * eh : 0.f;
+                cq += hi ? aq_st * qs * eh : 0.f;
             }
             const float bt = bet[t];
-            DKa[t * LR + cc] += bt * rkv + ck + cq;
-            DQ[t * LR + cc] += rqv;
-            DG[t * LR + cc] += bt * kt * rkv + qt * rqv - kt * (ck + cq);
+            const float dk0 = DKa[t * LR + cc], dq0 = DQ[t * LR + cc], dg0 = DG[t * LR + cc];
+            DKa[t * LR + cc] = dk0 + (bt * rkv + ck + cq);
+            DQ[t * LR + cc] = dq0 + rqv;
+            DG[t * LR + cc] = dg0 + (bt * kt * rkv + qt * rqv - kt * (ck + cq));
             r_dbA += kt * rkv;
         }
+        rowp[wave * kChunk + lane] = r_dbA;
     }
-    rowp[wave * kChunk + lane] = r_dbA;
     __syncthreads();
 
     // ------------------------------------------------ P5: dg, gate chain, outputs
-    // (a) lane = token: add dG_L to the last row, reverse in-chunk cumsum -> DG holds dg
+    // (a) dG_L into the last row, rows past the end zeroed, reverse cumulative sum -> DG holds dg
     {
-        const int t = lane;
-        for (int cc = wave; cc < DK; cc += kWaves) {
-            float dG = DG[t * LR + cc];
-            if (t == last) {
-                float sl = 0.f;
+        const int cs = tid & 31, sg = tid >> 5;
+        const float extra = ((colp[cs] + colp[DK + cs]) + (colp[2 * DK + cs] + colp[3 * DK + cs])) +
+                            __expf(GL[cs]) * dgl[cs];
+        float x[4];
 #pragma unroll
-                for (int tm = 0; tm < 4; ++tm) sl += colp[tm * DK + cc];
-                dG += sl + __expf(GL[cc]) * dgl[cc];
-            }
-            if (t >= cr.len) dG = 0.f;
-            float sfx = dG;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_down(sfx, off, 64);
-                if (t + off < 64) sfx += o;
-            }
-            DG[t * LR + cc] = sfx;
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * sg + i;
+            const float v = DG[t * LR + cs];
+            x[i] = t < cr.len ? v + (t == last ? extra : 0.f) : 0.f;
         }
+        __syncthreads();  // colp is reused below
+        col_scan64x32<true>(DG, LR, seg, x);
     }
-    __syncthreads();
-    // (b) coalesced pass, thread = (row tr, 8 channels): gate, sigmoid and L2 chains, stores
+    // (b) row-wise pass, thread = (token tr, 4 channels): gate, sigmoid and L2 chains, stores
     {
         const int t = tr;
-        float dgv[8], dqv[8], dkv[8], qh[8], kh[8];
+        float dgv[4], dqv[4], dkv[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int cc = 8 * part + i;
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 4 * part + i;
             dgv[i] = DG[t * LR + cc];
             dqv[i] = DQ[t * LR + cc];
             dkv[i] = DKa[t * LR + cc];
-            qh[i] = Qs[t * LR + cc];
-            kh[i] = Ks[t * LR + cc];
         }
         float pa = 0.f;
         if (gate) {
             const float eA = expf(p.A_log[h]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // graw still holds this row's raw f (the staging layout is the same)
-                const float x = in ? graw_f[i] + p.dt_bias[h * DK + 8 * part + i] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const float x = in ? graw_f[i] + p.dt_bias[h * DK + 4 * part + i] : 0.f;
                 const float df = in ? dgv[i] * (-eA) * dsoftplus_f(x) : 0.f;
                 pa += in ? dgv[i] * (-eA * softplus_f(x)) : 0.f;
                 dgv[i] = df;
             }
-            // column sums of df over the chunk: 16 rows per wave (lanes 4 apart), then waves
+            // column sums of df over this wave's 8 rows (lanes 8 apart), per wave
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float cs = dgv[i];
-#pragma unroll
-                for (int off = 4; off < 64; off <<= 1) cs += __shfl_xor(cs, off, 64);
-                if (lane < 4) colp[wave * DK + 8 * part + i] = cs;
+            for (int i = 0; i < 4; ++i) {
+                const float cs = sum_rows(sum_x8(dgv[i]));
+                if (lane < 8) colp[wave * DK + 4 * part + i] = cs;
             }
         }
-        float dotq = 0.f, dotk = 0.f;
         if (l2) {
+            float dotq = 0.f, dotk = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { dotq += qh[i] * dqv[i]; dotk += kh[i] * dkv[i]; }
-            dotq += __shfl_xor(dotq, 1, 64); dotq += __shfl_xor(dotq, 2, 64);
-            dotk += __shfl_xor(dotk, 1, 64); dotk += __shfl_xor(dotk, 2, 64);
+            for (int i = 0; i < 4; ++i) { dotq += qx[i] * dqv[i]; dotk += kx[i] * dkv[i]; }
+            dotq = sum8(dotq);
+            dotk = sum8(dotk);
             const float r_q = rnq[t], r_k = rnk[t];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                dqv[i] = r_q * (dqv[i] - dotq * qh[i]);
-                dkv[i] = r_k * (dkv[i] - dotk * kh[i]);
+            for (int i = 0; i < 4; ++i) {
+                dqv[i] = r_q * (dqv[i] - dotq * qx[i]);
+                dkv[i] = r_k * (dkv[i] - dotk * kx[i]);
             }
         }
         if (in) {
-            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + 8 * part;
-            store8<TOut>((TOut*)p.dq + gi, dqv);
-            store8<TOut>((TOut*)p.dk + gi, dkv);
-            store8<float>(p.dg + gi, dgv);
+            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + 4 * part;
+            store4<TOut>((TOut*)p.dq + gi, dqv);
+            store4<TOut>((TOut*)p.dk + gi, dkv);
+            store4<float>(p.dg + gi, dgv);
         }
         if (gate) {
             const float pw = wave_sum(pa);
@@ -607,8 +693,10 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     if (tid < kChunk) {
         const int t = tid;
         float db = 0.f;
-        for (int w = 0; w < kWaves; ++w) db += rowp[w * kChunk + t];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += rowp[w * kChunk + t];
         db += dba[t * 2] + dba[t * 2 + 1] + dbw[t * 2] + dbw[t * 2 + 1];
+#pragma unroll
         for (int g = 0; g < GV; ++g) db += dbv[t * GV + g];
         if (t < cr.len) {
             if (p.flags & 4u) db *= bet[t] * (1.f - bet[t]);
@@ -617,8 +705,18 @@ __global__ void __launch_bounds__(kThreads) bwd_chunk_kernel(Prm p) {
     }
     if (gate) {
         __syncthreads();
-        if (tid < DK) p.part_dt[slot * DK + tid] = (colp[tid] + colp[DK + tid]) + (colp[2 * DK + tid] + colp[3 * DK + tid]);
-        if (tid == 0) p.part_a[slot] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        if (tid < DK) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) s += colp[w * DK + tid];
+            p.part_dt[slot * DK + tid] = s;
+        }
+        if (tid == 0) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) s += wsum[w];
+            p.part_a[slot] = s;
+        }
     }
 }
 

@@ -262,14 +262,8 @@ struct TileSet {
 };
 
 // Sum over the 16 lanes that share the rows of an MFMA D fragment (lanes
-// 16g .. 16g+15), in a fixed order; every lane of the group gets the sum.
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    return x;
-}
+// 16g .. 16g+15); every lane of the group gets the sum.
+__device__ __forceinline__ float row16_sum(float x) { return sum16(x); }
 
 }  // namespace kda
 

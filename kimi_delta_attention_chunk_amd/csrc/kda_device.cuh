@@ -48,12 +48,34 @@ __device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log
 __device__ __forceinline__ float dsoftplus_f(float x) { return x > 20.f ? 1.f : 1.f / (1.f + expf(-x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
-// ----------------------------------------------------------------- wave reductions
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+// ----------------------------------------------------------------- cross-lane sums
+// All of these run on the VALU (DPP lane permutes and the gfx950 permlane
+// swaps), with no LDS round trip.  They must be called with every lane of the
+// wave active.  Each lane of a group receives the same sum: pair sums are
+// formed as x_a + x_b on both sides, which is exact commutation.
+template <int CTL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTL, 0xF, 0xF, false));
 }
+// lanes l, l^1, l^2, l^3 (a quad)
+__device__ __forceinline__ float sum4(float x) {
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+    return x + dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
+}
+// the 8 lanes 8m .. 8m+7
+__device__ __forceinline__ float sum8(float x) { x = sum4(x); return x + dpp_f<0x141>(x); }   // row_half_mirror
+// the 16 lanes 16m .. 16m+15 (one DPP row)
+__device__ __forceinline__ float sum16(float x) { x = sum8(x); return x + dpp_f<0x140>(x); }  // row_mirror
+// lanes l and l^8
+__device__ __forceinline__ float sum_x8(float x) { return x + dpp_f<0x128>(x); }  // row_ror:8
+// lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float sum_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(a[0]) + __int_as_float(a[1]);   // even row + odd row
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);  // lower half + upper half
+}
+__device__ __forceinline__ float wave_sum(float x) { return sum_rows(sum16(x)); }
 
 // ----------------------------------------------------------------- MFMA fp32 tiles
 // acc(16x16) += A(16 x K) * B(K x 16) over k in [k0, k1), k1 - k0 a multiple of 4.
