@@ -27,38 +27,81 @@ METRIC = "KDA fwd+bwd tokens/s at H=8,dk=32,dv=64,T=2048; % of MI355X roofline"
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "bwd_chunk_layer300M_B16_hbm_traffic.txt")
 
 
 def kda_work(B, T, H, dk, dv, C=64):
-    """Algorithmic work per kernel launch of one step, from the chunk algebra.
+    """Algorithmic work per launch of each kernel of one step.
 
-    Bytes: what the operator must read and write at least once
-      forward   q,k (bf16) + v (bf16) + f (fp32) + b (fp32) -> o (bf16)
-      backward  the forward inputs + do -> dq, dk, dv (bf16), df (fp32), db (fp32)
-    FLOPs (2 per multiply-add) of the products each kernel performs per
-    chunk-head, Gram/pair terms counted on their triangles:
+    Per token-head (dk=32, dv=64, bf16 q/k/v/o/do/dq/dk/dv, fp32 f/b/df/db):
+      bytes  forward  read q, k, v, f, b; write o         -> fwd_intra reads the inputs,
+                                                             fwd_scan writes o and the final state
+             backward read q, k, v, f, b, do; write dq, dk, dv, df, db
+                                                          -> all of it in bwd_chunk
+      FLOPs  (2 per multiply-add, triangles counted as halves)
+             fwd_intra  Akk, Aqk, w (3 C dk), u (C dv), the unit-triangular inverse (C^2/3)
+             fwd_scan   w h, Kh^T v_new, Qg h (6 dk dv), Aqk v_new (C dv)
+             bwd_dh     Aqk^T dO (C dv), Kh D, Qg^T dO, w^T dv_new (6 dk dv)
+             bwd_chunk  dO h^T, vn D^T, dvn h^T (6 dk dv); dAqk, dT_v, T^T dvn (3 C dv);
+                        dw (bKg)^T, T^T dw (2 C dk); dA = -T^T dT T^T (2 C^2/3);
+                        four decayed pair sums (4 C dk)
+    Intermediates the kernels pass to each other (T, w, u, states, v_new, ...) are
+    not algorithmic bytes; the measured traffic shows them.
     """
-    th = B * T * H                      # token-heads
-    ch = B * ((T + C - 1) // C) * H     # chunk-heads
-    tri = C * (C + 1) // 2              # lower triangle incl. diagonal
-    f = {}
-    # fwd_intra: Akk and Aqk pairwise (tri*dk each), UT inverse (~C^3/6), w (tri*dk), u (tri*dv)
-    f["fwd_intra"] = 2 * ch * (2 * tri * dk + C ** 3 // 6 + tri * dk + tri * dv)
-    # fwd_state: v_new = u - w h (C*dk*dv), h' = Kh^T v_new (C*dk*dv)
-    f["fwd_state"] = 2 * ch * (2 * C * dk * dv)
-    # fwd_output: Qg h (C*dk*dv) + Aqk v_new (tri*dv)
-    f["fwd_output"] = 2 * ch * (C * dk * dv + tri * dv)
-    # bwd_dh: Aqk^T dO (tri*dv), Kh D (C*dk*dv), Qg^T dO (C*dk*dv), w^T dvn (C*dk*dv)
-    f["bwd_dh"] = 2 * ch * (tri * dv + 3 * C * dk * dv)
-    # bwd_dv: dQg, dKh, dw (3*C*dk*dv), dAqk, dT_v (2*C*C*dv), T^T dvn (tri*dv)
-    f["bwd_dv"] = 2 * ch * (3 * C * dk * dv + 2 * C * C * dv + tri * dv)
-    # bwd_dk: dT += dw Kg^T (C*C*dk), T^T dw (tri*dk), dT T^T and T^T Y (2*C^3/2),
-    #         four decayed pair sums (4*tri*dk)
-    f["bwd_dk"] = 2 * ch * (C * C * dk + tri * dk + C ** 3 + 4 * tri * dk)
-    fwd_bytes = th * (2 * 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv)
-    bwd_bytes = th * (2 * 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv + 2 * 2 * dk + 2 * dv + 4 * dk + 4)
-    return f, fwd_bytes, bwd_bytes
+    th = B * T * H  # token-heads
+    per = {
+        "fwd_intra": (2 * 2 * dk + 2 * dv + 4 * dk + 4, 3 * C * dk + C * dv + C * C / 3),
+        "fwd_scan": (2 * dv + 4 * dk * dv / T, C * dv + 6 * dk * dv),
+        "bwd_dh": (0.0, C * dv + 6 * dk * dv),
+        "bwd_chunk": (2 * 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv + 2 * 2 * dk + 2 * dv + 4 * dk + 4,
+                      6 * dk * dv + 3 * C * dv + 2 * C * dk + 2 * C * C / 3 + 4 * C * dk),
+        "bwd_gate_sum": (0.0, 0.0),
+    }
+    return {k: (th * b, th * f) for k, (b, f) in per.items()}
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources, so measured counters are used only for the code they measured."""
+    import hashlib
+
+    d = os.path.join(HERE, "kimi_delta_attention_chunk_amd", "csrc")
+    hsh = hashlib.sha256()
+    for nm in sorted(os.listdir(d)):
+        with open(os.path.join(d, nm), "rb") as fh:
+            hsh.update(nm.encode() + b"\0" + fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter on a copy of known size), or None when
+    there is none for this kernel or the sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = [json.loads(l) for l in fh if l.startswith("{")][-1]
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("csrc_sha") != kernel_source_hash():
+        return None
+    return rec["fetch_bytes"] / rec["fetch_factor"] + rec["write_bytes"] / rec["write_factor"]
+
+
+def copy_calibration(mb):
+    """A plain device copy of `mb` MiB (torch copy_), 5 times: the reference reading for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = mb * (1 << 20) // 4
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
 def cpu_baseline(B, T, H, dk, dv, seconds):
@@ -106,12 +149,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", choices=["bf16", "fp32"], default="bf16")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the operator shards by sequence and head with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
+        return
 
     import torch
 
@@ -163,17 +212,29 @@ def main():
 
     tokens = B * T
     value = tokens / (ms * 1e-3)
-    flops, fwd_bytes, bwd_bytes = kda_work(B, T, H, dk, dv)
+    work = kda_work(B, T, H, dk, dv)
     kernels = {name: {"launches_per_step": n / args.steps, "avg_us": 1e3 * tot / n,
                       "share": tot / (ms * args.steps)} for name, (n, tot) in per_kernel.items()}
     dom = max(per_kernel, key=lambda nm: per_kernel[nm][1])
     n_dom, tot_dom = per_kernel[dom]
     avg_s = tot_dom / n_dom * 1e-3
-    achieved = flops.get(dom, 0) / avg_s / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
-            "avg_us": avg_s * 1e6, "work_per_launch": flops.get(dom, 0), "precision": "fp32"}
-    step_bytes = fwd_bytes + bwd_bytes
+    bytes_dom, flops_dom = work.get(dom, (0.0, 0.0))
+    # the binding roofline of the dominant kernel: its bytes at HBM peak against its
+    # products, issued as bf16 MFMA three times each (hi/lo split), at the bf16 peak
+    t_hbm = bytes_dom / (PEAK_HBM_GBS * 1e9)
+    t_mfma = 3 * flops_dom / (PEAK_BF16_TFLOPS * 1e12)
+    traffic = measured_traffic(dom)
+    if t_hbm >= t_mfma:
+        achieved = bytes_dom / avg_s / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        achieved = 3 * flops_dom / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+    roof.update({"avg_us": avg_s * 1e6, "algorithmic_bytes": bytes_dom, "flops": flops_dom,
+                 "fp32_equiv_tflops": flops_dom / avg_s / 1e12})
+    step_bytes = sum(b for b, _ in work.values())
     line = {
         "metric": METRIC,
         "value": value,
