@@ -590,7 +590,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     {
         const int t = lane, blk = t >> 4, t0b = blk * 16;
         float r_dbA = 0.f;  // this lane's share of dbeta from Akk
-#pragma unroll
+#pragma unroll 1
         for (int jc = 0; jc < DK / NW; ++jc) {
             const int cc = wave + NW * jc;
             const float gt = Gs[t * LR + cc], kt = Ks[t * LR + cc], qt = Qs[t * LR + cc];
@@ -603,13 +603,16 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 const float aq_ts = dAqd[blk * 272 + (t & 15) * 17 + u];  // dAq[t][s]
                 const float ad_st = dAd[blk * 272 + u * 17 + (t & 15)];   // dA[s][t]
                 const float aq_st = dAqd[blk * 272 + u * 17 + (t & 15)];  // dAq[s][t]
-                const bool lo = u <= (t & 15), hi = u >= (t & 15);
-                const float el = __expf(lo ? gt - gs : 0.f) * ks;   // s <= t: e^{G_t - G_s} k_s
-                const float eh = __expf(hi ? gs - gt : 0.f);        // s >= t: e^{G_s - G_t}
-                rkv += lo ? ad_ts * el : 0.f;
-                rqv += lo ? aq_ts * el : 0.f;
-                ck += hi ? bet[s] * ad_st * ks * eh : 0.f;
-                cq += hi ? aq_st * qs * eh : 0.f;
+                // One exp per pair: e^{G_t - G_s} for s <= t, e^{G_s - G_t} for s >= t.  The
+                // stored diagonal blocks are zero outside their triangles (dA strictly lower,
+                // dAq lower), so each product below only counts on its own side.
+                const float x = gt - gs;
+                const float e = exp_hw(u <= (t & 15) ? x : -x);
+                const float ek = e * ks;
+                rkv = fmaf(ad_ts, ek, rkv);
+                rqv = fmaf(aq_ts, ek, rqv);
+                ck = fmaf(bet[s] * ad_st * ks, e, ck);
+                cq = fmaf(aq_st * qs, e, cq);
             }
             const float bt = bet[t];
             const float dk0 = DKa[t * LR + cc], dq0 = DQ[t * LR + cc], dg0 = DG[t * LR + cc];

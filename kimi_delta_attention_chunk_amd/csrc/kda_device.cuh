@@ -43,10 +43,24 @@ template <> struct Elem<uint16_t> {
 };
 
 // ----------------------------------------------------------------- prep math
-// softplus with the usual threshold: x for x > 20.
-__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
-__device__ __forceinline__ float dsoftplus_f(float x) { return x > 20.f ? 1.f : 1.f / (1.f + expf(-x)); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+// Hardware transcendentals (v_exp_f32, v_log_f32, v_rcp_f32: about 1 ulp),
+// instead of the library's range-reduced versions: the preparation runs
+// them per element in every chunk kernel.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+// log(1 + y) for y >= 0 to full relative precision: log(z) * y / (z - 1) with
+// z = 1 + y rounded, which cancels the rounding of z (y when z rounds to 1).
+__device__ __forceinline__ float log1p_hw(float y) {
+    const float z = 1.f + y;
+    const float l = __builtin_amdgcn_logf(z) * 0.6931471805599453f;
+    return z == 1.f ? y : l * (y / (z - 1.f));
+}
+// softplus with the usual threshold: x for x > 20; else max(x, 0) + log1p(e^-|x|).
+__device__ __forceinline__ float softplus_f(float x) {
+    return x > 20.f ? x : fmaxf(x, 0.f) + log1p_hw(exp_hw(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.f + exp_hw(-x)); }
+__device__ __forceinline__ float dsoftplus_f(float x) { return x > 20.f ? 1.f : sigmoid_f(x); }
 
 // ----------------------------------------------------------------- cross-lane sums
 // All of these run on the VALU (DPP lane permutes and the gfx950 permlane
