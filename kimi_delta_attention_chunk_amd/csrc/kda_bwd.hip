@@ -261,7 +261,7 @@ constexpr int kCB = 32;  // channels per block in the dk-side kernel
 // Stage channels [cb, cb+kCB) of q or k into XT[c][t] (times the row's
 // inverse norm if `rn` is given); zero past the chunk end.
 template <int DK, typename TIn>
-__device__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
+__device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
                                const float* rn, float* XT) {
     for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
         const int t = e / kCB, cc = e - t * kCB;
@@ -278,7 +278,7 @@ __device__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, 
 // form their in-chunk cumulative sums.  Also returns, in graw (nullable), the
 // per-token log-decay itself.  Ends with a barrier.
 template <int DK>
-__device__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw) {
+__device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw) {
     const bool gate = p.flags & 2u;
     for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
         const int t = e / kCB, cc = e - t * kCB;
@@ -304,7 +304,7 @@ __device__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, f
 
 // Inverse L2 norms of the raw rows of q or k (4 threads per token).
 template <int DK, typename TIn>
-__device__ void row_rnorm(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, float* rn) {
+__device__ __forceinline__ void row_rnorm(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, float* rn) {
     const int t = threadIdx.x >> 2, part = threadIdx.x & 3;
     float ss = 0.f;
     if (t < cr.len) {

@@ -70,32 +70,6 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4
     *(u32x2*)p = v;
 }
 
-// Inclusive cumulative sum over the 64 rows of the 32 columns of A (row
-// stride ld), forward or in reverse, in place, by 512 threads: thread (s, c)
-// scans rows 4s .. 4s+3 of column c, then adds the totals of the segments
-// before (after) it.  seg: LDS [16][32].  Ends with a barrier.
-template <bool REV>
-__device__ __forceinline__ void col_scan64x32(float* A, int ld, float* seg, float (&x)[4]) {
-    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
-    if (!REV) {
-        x[1] += x[0]; x[2] += x[1]; x[3] += x[2];
-        seg[sg * 32 + c] = x[3];
-    } else {
-        x[2] += x[3]; x[1] += x[2]; x[0] += x[1];
-        seg[sg * 32 + c] = x[0];
-    }
-    __syncthreads();
-    float off = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float v = seg[j * 32 + c];
-        off += (REV ? j > sg : j < sg) ? v : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A[(4 * sg + i) * ld + c] = x[i] + off;
-    __syncthreads();
-}
-
 template <int DV, typename TIn, typename TOut, Prec P>
 __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     constexpr int NTH = kBcThreads, NW = kBcWaves;
@@ -219,7 +193,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         const int cs = tid & 31, sg = tid >> 5;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = Gs[(4 * sg + i) * LR + cs];
-        col_scan64x32<false>(Gs, LR, seg, x);
+        col_scan_regs<false>(x, Gs, LR, seg);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[i] = Gs[tr * LR + 4 * part + i];
@@ -639,7 +613,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             x[i] = t < cr.len ? v + (t == last ? extra : 0.f) : 0.f;
         }
         __syncthreads();  // colp is reused below
-        col_scan64x32<true>(DG, LR, seg, x);
+        col_scan_regs<true>(x, DG, LR, seg);
     }
     // (b) row-wise pass, thread = (token tr, 4 channels): gate, sigmoid and L2 chains, stores
     {

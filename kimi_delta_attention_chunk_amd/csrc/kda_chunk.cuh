@@ -69,7 +69,7 @@ __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
 // Stage q or k of one chunk into XT[c][t] (zero past the chunk end), and
 // L2-normalise every token if `l2`.  Ends with a barrier.
 template <int DK, typename TIn>
-__device__ void stage_qk(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, bool l2,
+__device__ __forceinline__ void stage_qk(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, bool l2,
                          float* XT, float* rnorm /* [64] scratch, nullable if !l2 */) {
     for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
         const int t = e / DK, c = e - t * DK;
@@ -99,7 +99,7 @@ __device__ void stage_qk(const TIn* __restrict__ src, const ChunkRef& cr, int h,
 // the chunk end g = 0, so G stays at G_{L-1}.  Optionally also stages beta
 // (sigmoid of logits if flagged; 0 past the end).  Ends with a barrier.
 template <int DK>
-__device__ void stage_g(const Prm& p, const ChunkRef& cr, int h, float* GT, float* bet) {
+__device__ __forceinline__ void stage_g(const Prm& p, const ChunkRef& cr, int h, float* GT, float* bet) {
     const bool gate = p.flags & 2u;
     for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
         const int t = e / DK, c = e - t * DK;
@@ -136,7 +136,7 @@ __device__ void stage_g(const Prm& p, const ChunkRef& cr, int h, float* GT, floa
 //   Aq(t,s)  =        sum_c Q_tc K_sc e^{G_tc-G_sc}   (s <= t, else 0), passed to `aq_out`
 // Each wave owns one row t at a time; its lanes run over s.
 template <int DK, class AqOut>
-__device__ void gram_pairwise(const float* KT, const float* QT, const float* GT, const float* bet,
+__device__ __forceinline__ void gram_pairwise(const float* KT, const float* QT, const float* GT, const float* bet,
                               float* A, AqOut aq_out) {
     for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
         const int t = e >> 6, s = e & 63;
@@ -160,7 +160,7 @@ __device__ void gram_pairwise(const float* KT, const float* QT, const float* GT,
 //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
 // X is scratch of 4*16*kLD16 floats.  Starts and ends with barriers.
 constexpr int kLD16 = 20;
-__device__ void solve_unit_lower(const float* A, float* Tm, float* X) {
+__device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, float* X) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     // zero the strict upper part and diagonal blocks are filled below
     for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
@@ -204,6 +204,38 @@ __device__ void solve_unit_lower(const float* A, float* Tm, float* X) {
         }
         __syncthreads();
     }
+}
+
+// Inclusive cumulative sum over the 64 rows of a 64 x 32 LDS array A (row
+// stride ld), forward or in reverse, by every thread of the workgroup:
+// thread (sg, c) = (tid >> 5, tid & 31) brings in x, the R = 64 * 32
+// / blockDim values of rows R sg .. R sg + R - 1 of column c, scans them, and
+// adds the totals of the segments before (after) its own.  The results go
+// back to A.  seg: LDS [64 / R][32].  Starts with the segment exchange and
+// ends with a barrier.
+template <bool REV, int R>
+__device__ __forceinline__ void col_scan_regs(float (&x)[R], float* A, int ld, float* seg) {
+    constexpr int NS = 64 / R;
+    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    if (!REV) {
+#pragma unroll
+        for (int i = 1; i < R; ++i) x[i] += x[i - 1];
+        seg[sg * 32 + c] = x[R - 1];
+    } else {
+#pragma unroll
+        for (int i = R - 2; i >= 0; --i) x[i] += x[i + 1];
+        seg[sg * 32 + c] = x[0];
+    }
+    __syncthreads();
+    float off = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const float v = seg[j * 32 + c];
+        off += (REV ? j > sg : j < sg) ? v : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) A[(R * sg + i) * ld + c] = x[i] + off;
+    __syncthreads();
 }
 
 // Lower-triangular k-range for products T * X (T zero above the diagonal blocks).

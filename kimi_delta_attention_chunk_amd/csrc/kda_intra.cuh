@@ -76,38 +76,6 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]
     }
 }
 
-// In-chunk inclusive cumulative sum over t of one channel block held in
-// registers (thread = 4 t + part, 8 channels), across the four waves (wave w
-// holds rows 16 w .. 16 w + 15).  wsum: LDS scratch [4][32].  Contains
-// barriers.
-__device__ __forceinline__ void cumsum_rows(float (&G)[8], float* wsum) {
-    const int part = threadIdx.x & 3;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // scan over the 16 rows of this wave (lanes 4 apart hold consecutive rows)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float x = G[i];
-#pragma unroll
-        for (int off = 4; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        G[i] = x;
-    }
-    __syncthreads();  // wsum free
-    if (lane >= 60) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wsum[wave * 32 + 8 * part + i] = G[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float pre = 0.f;
-        for (int w = 0; w < wave; ++w) pre += wsum[w * 32 + 8 * part + i];
-        G[i] += pre;
-    }
-}
-
 // The p-th pair (t, s), s <= t, of the four 16x16 diagonal blocks (136 each).
 __device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
     const int I = p / 136, q = p - 136 * I;
@@ -140,8 +108,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     __shared__ __attribute__((aligned(16))) float S1[S1F];
     __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
     __shared__ float bet[kChunk];
-    __shared__ float wsum[4 * 32];
-    __shared__ float Gref[4 * 32];       // G at rows 16, 32, 48 and at the last row
+    __shared__ float seg[8 * 32];        // column-scan segment totals
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
 
@@ -217,8 +184,6 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[b][i] = -eA * softplus_f(G[b][i] + p.dt_bias[h * DK + b * kCB32 + 8 * part + i]);
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) cumsum_rows(G[b], wsum);
 
     // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,
     // and this thread's 4 diagonal-block entries of each.
@@ -232,20 +197,22 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB32;
-        if (tr == 16 || tr == 32 || tr == 48 || tr == last) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (tr == last) Gref[3 * 32 + 8 * part + i] = G[b][i];
-                if (tr == 16 || tr == 32 || tr == 48) Gref[(tr / 16 - 1) * 32 + 8 * part + i] = G[b][i];
-            }
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             Kb[tr * kLB + 8 * part + i] = kx[b][i];
             Qb[tr * kLB + 8 * part + i] = qx[b][i];
-            Gb[tr * kLB + 8 * part + i] = G[b][i];
+            Gb[tr * kLB + 8 * part + i] = G[b][i];  // per-token log-decay; scanned in place below
         }
         __syncthreads();
+        {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = Gb[(8 * (threadIdx.x >> 5) + i) * kLB + (threadIdx.x & 31)];
+            col_scan_regs<false>(x, Gb, kLB, seg);  // in-chunk cumulative sum G; ends with a barrier
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) G[b][i] = Gb[tr * kLB + 8 * part + i];
+        // G at the reference rows 16 I and at the last row come straight from the scanned tile
         // scaled operands for the off-diagonal Gram blocks, exp(G) q, k exp(G_L - G)
         {
             const int I = tr >> 4;
@@ -255,15 +222,15 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 const int cc = 8 * part + i;
                 const float gt = G[b][i];
                 qgv[i] = __expf(gt) * qx[b][i];
-                khT[(size_t)(cb + cc) * kChunk + tr] = kx[b][i] * __expf(Gref[3 * 32 + cc] - gt);
+                khT[(size_t)(cb + cc) * kChunk + tr] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
                 if (I >= 1) {
-                    const float e = __expf(gt - Gref[(I - 1) * 32 + cc]);
+                    const float e = __expf(gt - Gb[16 * I * kLB + cc]);
                     Kr.put(tr - 16, cc, kx[b][i] * e);
                     Qr.put(tr - 16, cc, qx[b][i] * e);
                 }
 #pragma unroll
                 for (int J = 1; J <= 3; ++J)
-                    if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gref[(J - 1) * 32 + cc] - gt));
+                    if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt));
             }
             float* dst = qg + (size_t)tr * DK + cb + 8 * part;
             *(f32x4*)dst = f32x4{qgv[0], qgv[1], qgv[2], qgv[3]};
@@ -271,7 +238,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         }
         if (tr == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gref[3 * 32 + 8 * part + i]);
+            for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gb[last * kLB + 8 * part + i]);
         }
         __syncthreads();
         // off-diagonal Gram tiles
