@@ -111,6 +111,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     __shared__ float seg[8 * 32];        // column-scan segment totals
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
+    static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
 
     float* Kb = KQG;
     float* Qb = KQG + kChunk * kLB;
@@ -121,7 +122,6 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     const Tile<P> Kc(S1 + 96 * LB8, 96, LB8);
     float* A = S1;                        // fp32 Akk, after pass 1
     const Tile<P> Tt(S1, kChunk, LA);     // T as an MFMA operand, after the solve
-    const Tile<P> BT(KQG, kCB32, LA);     // (beta exp(G) k)^T or (beta v)^T of one block
 
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
@@ -281,23 +281,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         __syncthreads();  // channel-block tiles are rewritten next
     }
 
-    // ---- assemble Akk (LDS, rows times beta, over S1) and Aqk (workspace)
-    float* aq = p.aqk + slot * kChunk * kChunk;
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
-        const int t = e >> 6, s = e & 63;
-        if ((s >> 4) > (t >> 4)) {  // above the diagonal blocks
-            A[t * kLD + s] = 0.f;
-            aq[e] = 0.f;
-        }
-    }
-    // diagonal blocks: zero first, then the packed pairs s <= t
-    for (int e = threadIdx.x; e < 4 * 256; e += kThreads) {
-        const int I = e >> 8, t = 16 * I + ((e >> 4) & 15), s = 16 * I + (e & 15);
-        if (s >= t) {
-            A[t * kLD + s] = 0.f;
-            if (s > t) aq[t * kChunk + s] = 0.f;
-        }
-    }
+    // ---- assemble Akk (fp32, rows times beta, over S1) and Aqk (fp32 staging over KQG).
+    // Only the parts that are read are written: the solve reads the strictly lower part of
+    // Akk; the Aqk copy below writes zeros above the diagonal by index.
+    float* AqL = KQG;  // [t][s], stride LA
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int pidx = threadIdx.x + kThreads * i;
@@ -305,7 +292,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             int t, s;
             diag_pair(pidx, t, s);
             if (s < t) A[t * kLD + s] = bet[t] * dkk[i];
-            aq[t * kChunk + s] = dqk[i];
+            AqL[t * LA + s] = dqk[i];
         }
     }
 #pragma unroll
@@ -318,46 +305,75 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + frag_row(r), s = 16 * J + frag_col();
             if (kind == 0) A[t * kLD + s] = bet[t] * gacc[i][r];
-            else aq[t * kChunk + s] = gacc[i][r];
+            else AqL[t * LA + s] = gacc[i][r];
         }
     }
     __syncthreads();
-    solve_unit_lower(A, Tm, X);  // ends with a barrier
+    {
+        // Aqk to the workspace: coalesced float4 rows, zero above the diagonal
+        f32x4* aq4 = (f32x4*)(p.aqk + slot * kChunk * kChunk);
+#pragma unroll
+        for (int i = 0; i < kChunk * kChunk / 4 / kThreads; ++i) {
+            const int e4 = 4 * (threadIdx.x + kThreads * i);
+            const int t = e4 >> 6, s0 = e4 & 63;
+            f32x4 v;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
+            aq4[e4 >> 2] = v;
+        }
+    }
+    solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
     if (p.tm) {
-        float* to = p.tm + slot * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) to[e] = Tm[(e >> 6) * kLD + (e & 63)];
+        f32x4* to = (f32x4*)(p.tm + slot * kChunk * kChunk);
+#pragma unroll
+        for (int i = 0; i < kChunk * kChunk / 4 / kThreads; ++i) {
+            const int e4 = 4 * (threadIdx.x + kThreads * i);
+            to[e4 >> 2] = *(const f32x4*)&Tm[(e4 >> 6) * kLD + (e4 & 63)];
+        }
     }
 
-    // ---- pass 2: w = T (beta exp(G) k) per channel block, u = T (beta v) per column block
+    // ---- pass 2: w = T (beta exp(G) k) per channel block, u = T (beta v) per column block,
+    // as many blocks per barrier as fit in KQG
     for (int e = threadIdx.x; e < kChunk * kChunk / 4; e += kThreads) {
         const int t = e >> 4, s4 = (e & 15) * 4;
         Tt.put4(t, s4, *(const f32x4*)&Tm[t * kLD + s4]);
     }
+    constexpr int NBLK = NB + NVB;
+    constexpr int GRP = (3 * kChunk * kLB) / (kCB32 * LA);  // blocks per round
+    static_assert(GRP >= 1, "one operand block must fit in KQG");
     const float bt = bet[tr];
     float* wo = p.w + slot * kChunk * DK;
     float* uo = p.u + slot * kChunk * DV;
 #pragma unroll
-    for (int b = 0; b < NB + NVB; ++b) {
-        if (b < NB) {
+    for (int b0 = 0; b0 < NBLK; b0 += GRP) {
+        if (b0 > 0) __syncthreads();  // the previous round's operand tiles are consumed
 #pragma unroll
-            for (int i = 0; i < 8; ++i) BT.put(8 * part + i, tr, bt * __expf(G[b][i]) * kx[b][i]);
-        } else {
+        for (int g = 0; g < GRP; ++g) {
+            const int b = b0 + g;
+            if (b < NBLK) {
+                const Tile<P> BTg(KQG + g * kCB32 * LA, kCB32, LA);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) BT.put(8 * part + i, tr, bt * vx[b - NB][i]);
+                for (int i = 0; i < 8; ++i)
+                    BTg.put(8 * part + i, tr, b < NB ? bt * __expf(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
+                                                     : bt * vx[b < NB ? 0 : b - NB][i]);
+            }
         }
         __syncthreads();
-        float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
-        const int ld = b < NB ? DK : DV;
-        for (int tile = wave; tile < 8; tile += kWaves) {  // 4 x 2 tiles of [64 x 32]
-            const int tm = tile >> 1, tn = tile & 1;
+        constexpr int TPB = 8;  // [64 x 32] tiles per block
+        const int nb = NBLK - b0 < GRP ? NBLK - b0 : GRP;
+        for (int tile = wave; tile < TPB * nb; tile += kWaves) {
+            const int g = tile / TPB, tl = tile % TPB, tm = tl >> 1, tn = tl & 1;
+            const int b = b0 + g;
+            const Tile<P> BTg(KQG + g * kCB32 * LA, kCB32, LA);
             int k0 = 0, k1 = 16 * (tm + 1);
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_tile(Tt.sub(tm * 16), BT.sub(tn * 16), k0, k1, acc);
+            acc = mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
+            float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
+            const int ld = b < NB ? DK : DV;
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * ld + tn * 16 + frag_col()] = acc[r];
         }
-        __syncthreads();
     }
 }
 
