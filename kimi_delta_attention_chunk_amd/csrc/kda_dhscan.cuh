@@ -18,44 +18,60 @@
 
 namespace kda {
 
-template <int DK, typename TIn>
+constexpr int kDhThreads = 512, kDhWaves = 8;  // two waves per SIMD
+
+// One chunk's operands, as loaded: 8-value chunks of the k-block arrays
+// (kda_mma.cuh) -- w, exp(G) q [t][c], (k exp(G_L - G))^T [c][t] and Aqk [t][s] --
+// plus dO and exp(G_L).
+template <int DK, typename TIn, Prec P>
 struct DhRegs {
-    static constexpr int NW = kChunk * DK / 4 / kThreads;      // float4 of w, qg, khT
-    static constexpr int NA = kChunk * kChunk / 4 / kThreads;  // float4 of aqk
-    f32x4 w[NW], q[NW], k[NW], a[NA];
-    float d[8];   // dO[t][jb + 8 part + i] for t = tid >> 2
-    float g[4 * ((DK / 16) * 2 + kWaves - 1) / kWaves];
+    static constexpr int CW = (kChunk * DK / 8 + kDhThreads - 1) / kDhThreads;  // chunks of w, qg, khT
+    static constexpr int CA = kChunk * kChunk / 8 / kDhThreads;                 // chunks of aqk
+    static constexpr int HPW = ((DK / 16) * 2 + kDhWaves - 1) / kDhWaves;       // D tiles per wave
+    KChunk<P> w[CW], q[CW], k[CW], a[CA];
+    float d[4];   // dO[t][jb + 4 part + i] for t = tid >> 3
+    float g[4 * HPW];
 };
 
-template <int DK, int DV, typename TIn>
+template <int DK, int DV, typename TIn, Prec P>
 __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb,
-                                        DhRegs<DK, TIn>& R) {
+                                        DhRegs<DK, TIn, P>& R) {
+    using Rg = DhRegs<DK, TIn, P>;
     const int tid = threadIdx.x, wave = tid >> 6;
-    const f32x4* w = (const f32x4*)(p.w + slot * kChunk * DK);
-    const f32x4* q = (const f32x4*)(p.qg + slot * kChunk * DK);
-    const f32x4* k = (const f32x4*)(p.khT + slot * DK * kChunk);
-    const f32x4* a = (const f32x4*)(p.aqk + slot * kChunk * kChunk);
+    const char* w = (const char*)(p.w + slot * kChunk * DK);
+    const char* q = (const char*)(p.qg + slot * kChunk * DK);
+    const char* k = (const char*)(p.khT + slot * DK * kChunk);
+    const char* a = (const char*)(p.aqk + slot * kChunk * kChunk);
 #pragma unroll
-    for (int i = 0; i < DhRegs<DK, TIn>::NW; ++i) {
-        R.w[i] = w[tid + kThreads * i];
-        R.q[i] = q[tid + kThreads * i];
-        R.k[i] = k[tid + kThreads * i];
+    for (int i = 0; i < Rg::CW; ++i) {
+        const int c8 = tid + kDhThreads * i;
+        if (c8 < kChunk * DK / 8) {
+            const int t = c8 / (DK / 8), k0 = 8 * (c8 % (DK / 8));  // w, qg: row t, index k0
+            load_kchunk(R.w[i], w + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, (k0 >> 3) & 3);
+            load_kchunk(R.q[i], q + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, (k0 >> 3) & 3);
+            const int cc = c8 >> 3, t0 = 8 * (c8 & 7);                // khT: row c, index t0
+            load_kchunk(R.k[i], k + (size_t)(cc * 2 + (t0 >> 5)) * kKBlockBytes, (t0 >> 3) & 3);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < DhRegs<DK, TIn>::NA; ++i) R.a[i] = a[tid + kThreads * i];
-    const int t = tid >> 2, part = tid & 3;
+    for (int i = 0; i < Rg::CA; ++i) {
+        const int c8 = tid + kDhThreads * i;
+        const int t = c8 >> 3, s0 = 8 * (c8 & 7);
+        load_kchunk(R.a[i], a + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, (s0 >> 3) & 3);
+    }
+    const int t = tid >> 3, part = tid & 7;
     if (t < cr.len) {
-        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 8 * part;
+        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 4 * part;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R.d[i] = Elem<TIn>::load(src, i);
+        for (int i = 0; i < 4; ++i) R.d[i] = Elem<TIn>::load(src, i);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) R.d[i] = 0.f;
+        for (int i = 0; i < 4; ++i) R.d[i] = 0.f;
     }
     constexpr int TH = (DK / 16) * 2;
 #pragma unroll
-    for (int i = 0; i < (TH + kWaves - 1) / kWaves; ++i) {
-        const int tile = wave + kWaves * i;
+    for (int i = 0; i < Rg::HPW; ++i) {
+        const int tile = wave + kDhWaves * i;
         if (tile < TH) {
             const int tm = tile >> 1;
 #pragma unroll
@@ -65,10 +81,11 @@ __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRe
 }
 
 template <int DK, int DV, typename TIn, Prec P>
-__global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_wg) {
+__global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int total_wg) {
     constexpr int BV = 32, LK = DK + 8, LA = kChunk + 8, NV = DV / BV;
     constexpr int TH = (DK / 16) * 2;
-    constexpr int HPW = (TH + kWaves - 1) / kWaves;
+    constexpr int HPW = DhRegs<DK, TIn, P>::HPW;
+    constexpr int NTH = kDhThreads, NWV = kDhWaves;
     __shared__ __attribute__((aligned(16))) float sAq[kChunk * LA];   // Aqk^T [t][s]
     __shared__ __attribute__((aligned(16))) float sKh[kChunk * LK];   // Kh [t][c]
     __shared__ __attribute__((aligned(16))) float sQ[DK * LA];        // Qg^T [c][t]
@@ -91,7 +108,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
     f32x4 D[HPW];
 #pragma unroll
     for (int i = 0; i < HPW; ++i) {
-        const int tile = wave + kWaves * i;
+        const int tile = wave + NWV * i;
         D[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile < TH) {
             const int tm = tile >> 1, tn = tile & 1, j = tn * 16 + frag_col();
@@ -103,40 +120,37 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
     }
     int c0, c1;
     p.seq.seq_chunks(n, c0, c1);
-    DhRegs<DK, TIn> R;
-    if (c0 < c1) dh_load<DK, DV, TIn>(p, (size_t)(c1 - 1) * p.H + h, p.seq.chunk(c1 - 1), h, jb, R);
+    DhRegs<DK, TIn, P> R;
+    if (c0 < c1) dh_load<DK, DV, TIn, P>(p, (size_t)(c1 - 1) * p.H + h, p.seq.chunk(c1 - 1), h, jb, R);
     for (int c = c1 - 1; c >= c0; --c) {
         const size_t slot = (size_t)c * p.H + h;
         __syncthreads();  // the previous chunk is done with the operand tiles
 #pragma unroll
-        for (int i = 0; i < DhRegs<DK, TIn>::NW; ++i) {
-            const int e4 = 4 * (tid + kThreads * i);
-            const int t = e4 / DK, cc = e4 - t * DK;       // w, qg: [t][c]
-            const int kc = e4 / kChunk, kt = e4 - kc * kChunk;  // khT: [c][t]
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                WT.put(cc + m, t, R.w[i][m]);
-                QgT.put(cc + m, t, R.q[i][m]);
-                Kh.put(kt + m, kc, R.k[i][m]);
+        for (int i = 0; i < DhRegs<DK, TIn, P>::CW; ++i) {
+            const int c8 = tid + NTH * i;
+            if (c8 < kChunk * DK / 8) {
+                const int t = c8 / (DK / 8), k0 = 8 * (c8 % (DK / 8));
+                put_kchunk_t(WT, k0, t, R.w[i]);   // w^T [c][t]
+                put_kchunk_t(QgT, k0, t, R.q[i]);  // Qg^T [c][t]
+                const int cc = c8 >> 3, t0 = 8 * (c8 & 7);
+                put_kchunk_t(Kh, t0, cc, R.k[i]);  // Kh [t][c]
             }
         }
 #pragma unroll
-        for (int i = 0; i < DhRegs<DK, TIn>::NA; ++i) {
-            const int e4 = 4 * (tid + kThreads * i);
-            const int s = e4 >> 6, t = e4 & 63;  // aqk[s][t]
-#pragma unroll
-            for (int m = 0; m < 4; ++m) AqT.put(t + m, s, R.a[i][m]);
+        for (int i = 0; i < DhRegs<DK, TIn, P>::CA; ++i) {
+            const int c8 = tid + NTH * i;
+            put_kchunk_t(AqT, 8 * (c8 & 7), c8 >> 3, R.a[i]);  // Aqk^T [s][t]
         }
         {
-            const int t = tid >> 2, part = tid & 3;
+            const int t = tid >> 3, part = tid & 7;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dOT.put(8 * part + i, t, R.d[i]);
+            for (int i = 0; i < 4; ++i) dOT.put(4 * part + i, t, R.d[i]);
         }
         float gl[4 * HPW];
 #pragma unroll
         for (int i = 0; i < 4 * HPW; ++i) gl[i] = R.g[i];
         __syncthreads();
-        if (c - 1 >= c0) dh_load<DK, DV, TIn>(p, slot - p.H, p.seq.chunk(c - 1), h, jb, R);
+        if (c - 1 >= c0) dh_load<DK, DV, TIn, P>(p, slot - p.H, p.seq.chunk(c - 1), h, jb, R);
         const bool odd = (c1 - 1 - c) & 1;
         const Tile<P> Db = odd ? DT1 : DT0;
         const Tile<P> Dn = odd ? DT0 : DT1;
@@ -144,7 +158,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
         float* dhs = p.dhs + slot * DK * DV;
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + kWaves * i;
+            const int tile = wave + NWV * i;
             if (tile < TH) {
                 const int tm = tile >> 1, tn = tile & 1;
 #pragma unroll
@@ -154,9 +168,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
         }
         // dv_new = scale Aqk^T dO + Kh D
         float* dvo = p.dvn + slot * kChunk * DV;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + kWaves * i, tm = tile >> 1, tn = tile & 1;
+        {
+            const int tm = wave >> 1, tn = wave & 1;
             int k0 = 16 * tm, k1 = kChunk;
             widen<P>(k0, k1);
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -174,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
         // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + kWaves * i;
+            const int tile = wave + NWV * i;
             if (tile < TH) {
                 const int tm = tile >> 1, tn = tile & 1;
                 f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -189,7 +202,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_scan_kernel(Prm p, int total_
     if (p.dh0) {
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + kWaves * i;
+            const int tile = wave + NWV * i;
             if (tile < TH) {
                 const int tm = tile >> 1, tn = tile & 1;
 #pragma unroll

@@ -221,7 +221,7 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     if constexpr (DK <= 64) {
         const int total = a.N * a.H * (DV / 32);
-        KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, TOut, P>), dim3(total), dim3(kThreads), s, p, total,
+        KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, TOut, P>), dim3(total), dim3(kScanThreads), s, p, total,
                    write_o ? 1 : 0, store ? 1 : 0);
     } else {
         const int total = a.N * a.H * (DV / kBV);

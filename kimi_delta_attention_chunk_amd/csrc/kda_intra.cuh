@@ -123,6 +123,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     float* A = S1;                        // fp32 Akk, after pass 1
     const Tile<P> Tt(S1, kChunk, LA);     // T as an MFMA operand, after the solve
 
+    // w, exp(G) q, (k exp(G_L - G))^T and Aqk go to the workspace in k-block form
+    // (kda_mma.cuh) for the sequential kernels of dk <= 64, which load MFMA
+    // fragments from it directly; plain fp32 (the F32 k-block form) otherwise.
+    constexpr Prec WP = DK <= 64 ? P : Prec::F32;
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
     if (cr.len == 0) return;
@@ -192,8 +196,9 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dkk[3] = {0.f, 0.f, 0.f}, dqk[3] = {0.f, 0.f, 0.f};
 
-    float* qg = p.qg + slot * kChunk * DK;
-    float* khT = p.khT + slot * DK * kChunk;
+    char* qg = (char*)(p.qg + slot * kChunk * DK);    // [t][DK/32] k-blocks
+    char* khT = (char*)(p.khT + slot * DK * kChunk);  // [c][2] k-blocks
+    float* KhS = Tm;                                   // (k exp(G_L - G))^T staging, [c][t], pass 1 only
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB32;
@@ -222,7 +227,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 const int cc = 8 * part + i;
                 const float gt = G[b][i];
                 qgv[i] = __expf(gt) * qx[b][i];
-                khT[(size_t)(cb + cc) * kChunk + tr] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
+                KhS[cc * kLD + tr] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
                 if (I >= 1) {
                     const float e = __expf(gt - Gb[16 * I * kLB + cc]);
                     Kr.put(tr - 16, cc, kx[b][i] * e);
@@ -232,15 +237,21 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 for (int J = 1; J <= 3; ++J)
                     if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt));
             }
-            float* dst = qg + (size_t)tr * DK + cb + 8 * part;
-            *(f32x4*)dst = f32x4{qgv[0], qgv[1], qgv[2], qgv[3]};
-            *(f32x4*)(dst + 4) = f32x4{qgv[4], qgv[5], qgv[6], qgv[7]};
+            store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
         }
         if (tr == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gb[last * kLB + 8 * part + i]);
         }
         __syncthreads();
+        {
+            // (k exp(G_L - G))^T of this channel block to the workspace: row c = cb + tid / 8
+            const int cr8 = threadIdx.x >> 3, w8 = threadIdx.x & 7;
+            float x[8];
+            const f32x4 a0 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8], a1 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8 + 4];
+            x[0] = a0[0]; x[1] = a0[1]; x[2] = a0[2]; x[3] = a0[3]; x[4] = a1[0]; x[5] = a1[1]; x[6] = a1[2]; x[7] = a1[3];
+            store_kblock8<WP>(khT + (size_t)((cb + cr8) * 2 + (w8 >> 2)) * kKBlockBytes, x, w8 & 3);
+        }
         // off-diagonal Gram tiles
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -310,16 +321,16 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     }
     __syncthreads();
     {
-        // Aqk to the workspace: coalesced float4 rows, zero above the diagonal
-        f32x4* aq4 = (f32x4*)(p.aqk + slot * kChunk * kChunk);
+        // Aqk to the workspace in k-block form, zero above the diagonal: 8 entries per thread and pass
+        char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
 #pragma unroll
-        for (int i = 0; i < kChunk * kChunk / 4 / kThreads; ++i) {
-            const int e4 = 4 * (threadIdx.x + kThreads * i);
-            const int t = e4 >> 6, s0 = e4 & 63;
-            f32x4 v;
+        for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
+            const int q8 = threadIdx.x + kThreads * i;
+            const int t = q8 >> 3, s0 = 8 * (q8 & 7);
+            float x[8];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) v[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
-            aq4[e4 >> 2] = v;
+            for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
+            store_kblock8<WP>(aq + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, x, (s0 >> 3) & 3);
         }
     }
     solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
@@ -369,10 +380,30 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
-            float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
-            const int ld = b < NB ? DK : DV;
+            if (DK <= 64 && b < NB) {  // w: staged in Tm [t][c] (stride kLD), written out below
 #pragma unroll
-            for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * ld + tn * 16 + frag_col()] = acc[r];
+                for (int r = 0; r < 4; ++r) Tm[(tm * 16 + frag_row(r)) * kLD + b * kCB32 + tn * 16 + frag_col()] = acc[r];
+            } else {
+                float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
+                const int ld = b < NB ? DK : DV;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * ld + tn * 16 + frag_col()] = acc[r];
+            }
+        }
+    }
+    if constexpr (DK <= 64) {
+        __syncthreads();
+        char* wk = (char*)wo;  // [t][DK/32] k-blocks
+#pragma unroll
+        for (int i = 0; i < (kChunk * DK / 8 + kThreads - 1) / kThreads; ++i) {
+            const int q8 = threadIdx.x + kThreads * i;
+            if (q8 < kChunk * DK / 8) {
+                const int t = q8 / (DK / 8), k0 = 8 * (q8 % (DK / 8));
+                float x[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = Tm[t * kLD + k0 + m];
+                store_kblock8<WP>(wk + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, x, (k0 >> 3) & 3);
+            }
         }
     }
 }

@@ -110,6 +110,130 @@ __device__ __forceinline__ f32x4 mma_tile(const Tile<Prec::BF3>& A, const Tile<P
     return acc;
 }
 
+// ----------------------------------------------------------------- A fragments from memory
+// Operands produced by one kernel and consumed by another are stored in
+// "k-block" form: per row, per block of 32 contraction indices, 128 bytes --
+//   Prec::BF3  the 32 hi parts (bf16) then the 32 lo parts,
+//   Prec::F32  the 32 fp32 values.
+// (For F32 that is plain row-major fp32.)  Lane l of a wave loads the A
+// fragment of row l & 15 straight into registers: 8 consecutive indices
+// 8 g .. 8 g + 7, g = l >> 4, as two 16-byte loads.  mma_frag then contracts
+// them with a B tile in LDS over the same 8 indices per lane: for F32 the 16x16x4
+// instruction at step kk takes index 8 g + kk from lane group g (A and B agree,
+// so the sum is over every index exactly once).
+template <Prec P> struct AFrag;
+template <> struct AFrag<Prec::BF3> { bf16x8 hi, lo; };
+template <> struct AFrag<Prec::F32> { f32x4 a, b; };
+
+// bytes of one (row, k-block) record, and its element type in memory
+constexpr int kKBlockBytes = 128;
+
+__device__ __forceinline__ void load_afrag(AFrag<Prec::BF3>& f, const void* rowblock) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const char* b = (const char*)rowblock;
+    f.hi = *(const bf16x8*)(b + 16 * g);
+    f.lo = *(const bf16x8*)(b + 64 + 16 * g);
+}
+__device__ __forceinline__ void load_afrag(AFrag<Prec::F32>& f, const void* rowblock) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const char* b = (const char*)rowblock;
+    f.a = *(const f32x4*)(b + 32 * g);
+    f.b = *(const f32x4*)(b + 32 * g + 16);
+}
+
+// acc += A(16 x [kb, kb+32)) * B(16 x [kb, kb+32))^T, A from registers, B a tile
+// in LDS at its origin row.
+__device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::BF3>& a, const Tile<Prec::BF3>& B, int kb, f32x4 acc) {
+    const int lane = threadIdx.x & 63;
+    const int bo = (lane & 15) * B.ld + kb + 8 * (lane >> 4);
+    const bf16x8 bh = *(const bf16x8*)(B.hi + bo);
+    const bf16x8 bl = *(const bf16x8*)(B.lo + bo);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, bh, acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const Tile<Prec::F32>& B, int kb, f32x4 acc) {
+    const int lane = threadIdx.x & 63;
+    const float* bp = B.p + (lane & 15) * B.ld + kb + 8 * (lane >> 4);
+    const f32x4 b0 = *(const f32x4*)bp, b1 = *(const f32x4*)(bp + 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[kk], b0[kk], acc, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[kk], b1[kk], acc, 0, 0, 0);
+    return acc;
+}
+
+// Write 8 consecutive values (indices 8 w .. 8 w + 7 of a k-block, w = which)
+// of one row in k-block form.
+template <Prec P>
+__device__ __forceinline__ void store_kblock8(void* rowblock, const float (&x)[8], int which);
+template <>
+__device__ __forceinline__ void store_kblock8<Prec::BF3>(void* rowblock, const float (&x)[8], int which) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[i] = (__bf16)x[i];
+        l[i] = (__bf16)(x[i] - (float)h[i]);
+    }
+    char* b = (char*)rowblock;
+    *(bf16x8*)(b + 16 * which) = h;
+    *(bf16x8*)(b + 64 + 16 * which) = l;
+}
+template <>
+__device__ __forceinline__ void store_kblock8<Prec::F32>(void* rowblock, const float (&x)[8], int which) {
+    float* b = (float*)rowblock + 8 * which;
+    *(f32x4*)b = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)(b + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+// Read 8 consecutive values of one row in k-block form back into fp32 (hi + lo).
+template <Prec P>
+__device__ __forceinline__ void load_kblock8(const void* rowblock, float (&x)[8], int which);
+template <>
+__device__ __forceinline__ void load_kblock8<Prec::BF3>(const void* rowblock, float (&x)[8], int which) {
+    const char* b = (const char*)rowblock;
+    const bf16x8 h = *(const bf16x8*)(b + 16 * which), l = *(const bf16x8*)(b + 64 + 16 * which);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i] + (float)l[i];
+}
+template <>
+__device__ __forceinline__ void load_kblock8<Prec::F32>(const void* rowblock, float (&x)[8], int which) {
+    const float* b = (const float*)rowblock + 8 * which;
+    const f32x4 u = *(const f32x4*)b, v = *(const f32x4*)(b + 4);
+    x[0] = u[0]; x[1] = u[1]; x[2] = u[2]; x[3] = u[3]; x[4] = v[0]; x[5] = v[1]; x[6] = v[2]; x[7] = v[3];
+}
+
+// Eight consecutive values (indices 8 w .. 8 w + 7 of one k-block) of a row in
+// k-block form, as loaded, and their transposed store into an LDS tile:
+// T(k0 + i, row) for i = 0..7 (no conversion: BF3 moves the stored hi/lo).
+template <Prec P> struct KChunk;
+template <> struct KChunk<Prec::BF3> { bf16x8 h, l; };
+template <> struct KChunk<Prec::F32> { f32x4 a, b; };
+__device__ __forceinline__ void load_kchunk(KChunk<Prec::BF3>& c, const void* rowblock, int which) {
+    const char* b = (const char*)rowblock;
+    c.h = *(const bf16x8*)(b + 16 * which);
+    c.l = *(const bf16x8*)(b + 64 + 16 * which);
+}
+__device__ __forceinline__ void load_kchunk(KChunk<Prec::F32>& c, const void* rowblock, int which) {
+    const float* b = (const float*)rowblock + 8 * which;
+    c.a = *(const f32x4*)b;
+    c.b = *(const f32x4*)(b + 4);
+}
+__device__ __forceinline__ void put_kchunk_t(const Tile<Prec::BF3>& T, int k0, int row, const KChunk<Prec::BF3>& c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        T.hi[(k0 + i) * T.ld + row] = c.h[i];
+        T.lo[(k0 + i) * T.ld + row] = c.l[i];
+    }
+}
+__device__ __forceinline__ void put_kchunk_t(const Tile<Prec::F32>& T, int k0, int row, const KChunk<Prec::F32>& c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        T.p[(k0 + i) * T.ld + row] = c.a[i];
+        T.p[(k0 + 4 + i) * T.ld + row] = c.b[i];
+    }
+}
+
 // Round a k range outward to the step of P (for triangular factors whose
 // entries outside the exact range are zero).
 template <Prec P>
