@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_kernel(Prm p, int total_wg) {
         // dv_new = scale Aqk^T dO + Kh D
         float* dvo = p.dvn + slot * kChunk * DV;
         {
-            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            const int wave = wave_id(), lane = threadIdx.x & 63;
             constexpr int TN = kBV / 16, TILES = (kChunk / 16) * TN;
             for (int tile = wave; tile < TILES; tile += kWaves) {
                 const int tm = tile / TN, tn = tile % TN;
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dh_kernel(Prm p, int total_wg) {
         __syncthreads();
         // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
         {
-            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            const int wave = wave_id(), lane = threadIdx.x & 63;
             constexpr int TN = kBV / 16, TILES = (DK / 16) * TN;
             for (int tile = wave; tile < TILES; tile += kWaves) {
                 const int tm = tile / TN, tn = tile % TN;
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
     const TIn* dO = (const TIn*)p.d_o;
     const TIn* vin = (const TIn*)p.v;
     TOut* dvout = (TOut*)p.dv;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
 
     const float* tmi = p.tm + slot * kChunk * kChunk;
     for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     const ChunkRef cr = p.seq.chunk(c);
     if (cr.len == 0) return;
     const size_t slot = (size_t)c * p.H + h;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const bool l2 = p.flags & 1u, gate = p.flags & 2u;
     const TIn* qin = (const TIn*)p.q;
     const TIn* kin = (const TIn*)p.k;

@@ -39,37 +39,6 @@ namespace kda {
 
 constexpr int kBcThreads = 512, kBcWaves = 8;
 
-template <typename TIn>
-__device__ __forceinline__ void load4(const TIn* p, float (&x)[4]);
-template <>
-__device__ __forceinline__ void load4<float>(const float* p, float (&x)[4]) {
-    const f32x4 a = *(const f32x4*)p;
-    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-}
-template <>
-__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float (&x)[4]) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = *(const u32x2*)p;
-    x[0] = __uint_as_float(v[0] << 16);
-    x[1] = __uint_as_float(v[0] & 0xffff0000u);
-    x[2] = __uint_as_float(v[1] << 16);
-    x[3] = __uint_as_float(v[1] & 0xffff0000u);
-}
-template <typename TOut>
-__device__ __forceinline__ void store4(TOut* p, const float (&x)[4]);
-template <>
-__device__ __forceinline__ void store4<float>(float* p, const float (&x)[4]) {
-    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
-}
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4]) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-    v[1] = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
-    *(u32x2*)p = v;
-}
-
 template <int DV, typename TIn, typename TOut, Prec P>
 __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     constexpr int NTH = kBcThreads, NW = kBcWaves;
@@ -97,7 +66,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     const ChunkRef cr = p.seq.chunk(c);
     if (cr.len == 0) return;
     const size_t slot = (size_t)c * p.H + h;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int tr = tid >> 3, part = tid & 7;  // row-wise work: token tr, channels 4 part .. 4 part + 3
     const bool l2 = p.flags & 1u, gate = p.flags & 2u;
     const TIn* qin = (const TIn*)p.q;
@@ -109,26 +78,26 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     const float scale = p.scale;
 
     // ------------------------------------------------ every global load, up front
-    float braw = 0.f;
-    if (tid < kChunk && tid < cr.len) braw = p.beta[(size_t)(cr.t0 + tid) * p.H + h];
+    // (the gate parameters first, so that no later load waits behind the rest)
+    float braw = 0.f, alog = 0.f, dtb[4] = {0.f, 0.f, 0.f, 0.f};
+    if (gate) {
+        alog = p.A_log[h];
+        load4<float>(p.dt_bias + h * DK + 4 * part, dtb);
+    }
+    // rows past the chunk end load row 0 (always valid) and are zeroed after the loads
+    const int trc = in ? tr : 0;
+    if (tid < kChunk) braw = p.beta[(size_t)(cr.t0 + (tid < cr.len ? tid : 0)) * p.H + h];
     float kx[4], qx[4], G[4], graw[4], vx[NVB][4], dox[NVB][4];
-    if (in) {
-        const size_t base = tok_index(cr.t0 + tr, h, p.H, DK) + 4 * part;
+    {
+        const size_t base = tok_index(cr.t0 + trc, h, p.H, DK) + 4 * part;
         load4<TIn>(kin + base, kx);
         load4<TIn>(qin + base, qx);
         load4<float>(p.g + base, graw);
 #pragma unroll
         for (int b = 0; b < NVB; ++b) {
-            const size_t vb = tok_index(cr.t0 + tr, h, p.H, DV) + 32 * b + 4 * part;
+            const size_t vb = tok_index(cr.t0 + trc, h, p.H, DV) + 32 * b + 4 * part;
             load4<TIn>(vin + vb, vx[b]);
             load4<TIn>(doin + vb, dox[b]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kx[i] = qx[i] = graw[i] = 0.f;
-#pragma unroll
-            for (int b = 0; b < NVB; ++b) vx[b][i] = dox[b][i] = 0.f;
         }
     }
     f32x4 Tr[NT4], Hr[NH4], Dr[NH4], Vn[NV4], dVn[NV4];
@@ -144,6 +113,18 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
 #pragma unroll
         for (int i = 0; i < NV4; ++i) { Vn[i] = v4[tid + NTH * i]; dVn[i] = w4[tid + NTH * i]; }
+    }
+    if (tid < kChunk && tid >= cr.len) braw = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kx[i] = in ? kx[i] : 0.f;
+        qx[i] = in ? qx[i] : 0.f;
+        graw[i] = in ? graw[i] : 0.f;
+#pragma unroll
+        for (int b = 0; b < NVB; ++b) {
+            vx[b][i] = in ? vx[b][i] : 0.f;
+            dox[b][i] = in ? dox[b][i] : 0.f;
+        }
     }
 
     // ------------------------------------------------ preparation (registers), resident tiles
@@ -165,10 +146,10 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         if (part == 0) { rnk[tr] = rk; rnq[tr] = rq; }
     }
     const float graw_f[4] = {graw[0], graw[1], graw[2], graw[3]};  // the raw gate input f (gate flag)
+    const float eA = exp_hw(alog);
     if (gate && in) {
-        const float eA = expf(p.A_log[h]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) graw[i] = -eA * softplus_f(graw[i] + p.dt_bias[h * DK + 4 * part + i]);
+        for (int i = 0; i < 4; ++i) graw[i] = -eA * softplus_f(graw[i] + dtb[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -628,10 +609,9 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         float pa = 0.f;
         if (gate) {
-            const float eA = expf(p.A_log[h]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = in ? graw_f[i] + p.dt_bias[h * DK + 4 * part + i] : 0.f;
+                const float x = in ? graw_f[i] + dtb[i] : 0.f;
                 const float df = in ? dgv[i] * (-eA) * dsoftplus_f(x) : 0.f;
                 pa += in ? dgv[i] * (-eA * softplus_f(x)) : 0.f;
                 dgv[i] = df;

@@ -161,7 +161,7 @@ __device__ __forceinline__ void gram_pairwise(const float* KT, const float* QT, 
 // X is scratch of 4*16*kLD16 floats.  Starts and ends with barriers.
 constexpr int kLD16 = 20;
 __device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, float* X) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     // zero the strict upper part and diagonal blocks are filled below
     for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
         const int t = e >> 6, s = e & 63;
@@ -268,7 +268,7 @@ struct TileSet {
     }
     // acc += A(M x K) * B(K x N) with element strides as in mma16_f32
     __device__ __forceinline__ void mma(const float* A, int am, int ak, const float* B, int bk, int bn, int K) {
-        const int wave = threadIdx.x >> 6;
+        const int wave = wave_id();
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int tile = wave + i * kWaves;
@@ -280,7 +280,7 @@ struct TileSet {
     }
     template <class F>
     __device__ __forceinline__ void store(F f) const {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int tile = wave + i * kWaves;

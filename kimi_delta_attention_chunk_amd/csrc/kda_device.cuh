@@ -20,6 +20,11 @@ constexpr float kL2Eps = 1e-6f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar)
+// value: tile and row offsets derived from it stay in SGPRs instead of being
+// recomputed per lane.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ----------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
     return __uint_as_float(((uint32_t)u) << 16);
@@ -41,6 +46,38 @@ template <> struct Elem<uint16_t> {
     __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
     __device__ __forceinline__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 };
+
+// Four consecutive elements of a row (8- or 16-byte aligned) as fp32, and back.
+template <typename TIn>
+__device__ __forceinline__ void load4(const TIn* p, float (&x)[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float (&x)[4]) {
+    const f32x4 a = *(const f32x4*)p;
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float (&x)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = *(const u32x2*)p;
+    x[0] = __uint_as_float(v[0] << 16);
+    x[1] = __uint_as_float(v[0] & 0xffff0000u);
+    x[2] = __uint_as_float(v[1] << 16);
+    x[3] = __uint_as_float(v[1] & 0xffff0000u);
+}
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* p, const float (&x)[4]);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float (&x)[4]) {
+    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v;
+    v[0] = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    v[1] = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    *(u32x2*)p = v;
+}
 
 // ----------------------------------------------------------------- prep math
 // Hardware transcendentals (v_exp_f32, v_log_f32, v_rcp_f32: about 1 ulp),
@@ -113,7 +150,7 @@ __device__ __forceinline__ f32x4 mma16_f32(const float* A, int am, int ak, const
 template <int M, int N, class KRange, class Epi>
 __device__ __forceinline__ void wg_gemm(const float* A, int am, int ak, const float* B, int bk,
                                         int bn, int K, KRange krange, Epi epi) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     constexpr int TN = N / 16, TILES = (M / 16) * (N / 16);
     for (int tile = wave; tile < TILES; tile += kWaves) {
         const int tm = tile / TN, tn = tile % TN;

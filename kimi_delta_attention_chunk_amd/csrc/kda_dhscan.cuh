@@ -37,7 +37,7 @@ template <int DK, int DV, typename TIn, Prec P>
 __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb,
                                         DhRegs<DK, TIn, P>& R) {
     using Rg = DhRegs<DK, TIn, P>;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = wave_id();
     const char* w = (const char*)(p.w + slot * kChunk * DK);
     const char* q = (const char*)(p.qg + slot * kChunk * DK);
     const char* k = (const char*)(p.khT + slot * DK * kChunk);
@@ -60,13 +60,12 @@ __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRe
         load_kchunk(R.a[i], a + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, (s0 >> 3) & 3);
     }
     const int t = tid >> 3, part = tid & 7;
-    if (t < cr.len) {
-        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 4 * part;
+    {
+        // rows past the chunk end read row 0 (always valid) and are zeroed
+        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DV) + jb + 4 * part;
+        load4<TIn>(src, R.d);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.d[i] = Elem<TIn>::load(src, i);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R.d[i] = 0.f;
+        for (int i = 0; i < 4; ++i) R.d[i] = t < cr.len ? R.d[i] : 0.f;
     }
     constexpr int TH = (DK / 16) * 2;
 #pragma unroll
@@ -102,7 +101,7 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
     const int n = nh / p.H, h = nh % p.H;
     if (n >= p.N) return;
     const int jb = vb * BV;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = wave_id();
     const float scale = p.scale;
 
     f32x4 D[HPW];

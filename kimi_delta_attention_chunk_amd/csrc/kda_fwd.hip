@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(kThreads) fwd_output_kernel(Prm p) {
     }
     __syncthreads();
     TOut* o = (TOut*)p.o;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     constexpr int TN = OB / 16, TILES = (kChunk / 16) * TN;
     for (int tile = wave; tile < TILES; tile += kWaves) {
         const int tm = tile / TN, tn = tile % TN;

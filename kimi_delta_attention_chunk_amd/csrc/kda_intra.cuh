@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     const ChunkRef cr = p.seq.chunk(c);
     if (cr.len == 0) return;
     const size_t slot = (size_t)c * p.H + h;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int tr = threadIdx.x >> 2, part = threadIdx.x & 3;  // staging row / channel group
     const bool l2 = p.flags & 1u;
     const TIn* qin = (const TIn*)p.q;
@@ -140,30 +140,41 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     const int last = cr.len - 1;
     const bool in = tr < cr.len;
 
-    // ---- every global load of the chunk, issued up front
-    float kx[NB][8], qx[NB][8], G[NB][8], vx[NVB][8];
-    float braw = 0.f;
+    // ---- every global load of the chunk, issued up front (the gate parameters
+    // too, so that no later load waits behind the bulk of them)
+    const bool gate = p.flags & 2u;
+    float kx[NB][8], qx[NB][8], G[NB][8], vx[NVB][8], dtb[NB][8];
+    float braw = 0.f, alog = 0.f;
     (void)Gb;
-    if (threadIdx.x < kChunk && threadIdx.x < cr.len) braw = p.beta[(size_t)(cr.t0 + threadIdx.x) * p.H + h];
+    if (gate) {
+        alog = p.A_log[h];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) load8<float>(p.dt_bias + h * DK + b * kCB32 + 8 * part, dtb[b]);
+    }
+    // Rows past the chunk end load row 0 (always valid) and are zeroed after the
+    // loads: unconditional loads keep every wait after the whole batch.
+    const int trc = in ? tr : 0;
+    if (threadIdx.x < kChunk) braw = p.beta[(size_t)(cr.t0 + (threadIdx.x < cr.len ? threadIdx.x : 0)) * p.H + h];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        if (in) {
-            const size_t base = tok_index(cr.t0 + tr, h, p.H, DK) + b * kCB32 + 8 * part;
-            load8<TIn>(kin + base, kx[b]);
-            load8<TIn>(qin + base, qx[b]);
-            load8<float>(p.g + base, G[b]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) kx[b][i] = qx[b][i] = G[b][i] = 0.f;
-        }
+        const size_t base = tok_index(cr.t0 + trc, h, p.H, DK) + b * kCB32 + 8 * part;
+        load8<TIn>(kin + base, kx[b]);
+        load8<TIn>(qin + base, qx[b]);
+        load8<float>(p.g + base, G[b]);
     }
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-        if (in) load8<TIn>(vin + tok_index(cr.t0 + tr, h, p.H, DV) + 32 * vb + 8 * part, vx[vb]);
-        else {
+    for (int vb = 0; vb < NVB; ++vb) load8<TIn>(vin + tok_index(cr.t0 + trc, h, p.H, DV) + 32 * vb + 8 * part, vx[vb]);
+    if (threadIdx.x < kChunk && threadIdx.x >= cr.len) braw = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) vx[vb][i] = 0.f;
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            kx[b][i] = in ? kx[b][i] : 0.f;
+            qx[b][i] = in ? qx[b][i] : 0.f;
+            G[b][i] = in ? G[b][i] : 0.f;
         }
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) vx[vb][i] = in ? vx[vb][i] : 0.f;
     }
     // ---- preparation in registers: beta, L2 norms, gate, in-chunk cumulative decay
     if (threadIdx.x < kChunk) bet[threadIdx.x] = (p.flags & 4u) ? (threadIdx.x < cr.len ? sigmoid_f(braw) : 0.f) : braw;
@@ -181,12 +192,12 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) { kx[b][i] *= rk; qx[b][i] *= rq; }
     }
-    if ((p.flags & 2u) && in) {
-        const float eA = expf(p.A_log[h]);
+    if (gate && in) {
+        const float eA = exp_hw(alog);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) G[b][i] = -eA * softplus_f(G[b][i] + p.dt_bias[h * DK + b * kCB32 + 8 * part + i]);
+            for (int i = 0; i < 8; ++i) G[b][i] = -eA * softplus_f(G[b][i] + dtb[b][i]);
     }
 
     // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,

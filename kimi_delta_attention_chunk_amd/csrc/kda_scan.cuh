@@ -39,7 +39,7 @@ struct ScanFrags {
 template <int DK, int DV, Prec P>
 __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, ScanFrags<DK, P>& R) {
     using F = ScanFrags<DK, P>;
-    const int wave = threadIdx.x >> 6, lr = threadIdx.x & 15;
+    const int wave = wave_id(), lr = threadIdx.x & 15;
     const int tm = wave >> 1, tn = wave & 1;
     const char* w = (const char*)(p.w + slot * kChunk * DK);       // [t][DK/32] k-blocks
     const char* q = (const char*)(p.qg + slot * kChunk * DK);      // [t][DK/32]
@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
     const int n = nh / p.H, h = nh % p.H;
     if (n >= p.N) return;
     const int jb = vb * BV;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int tm = wave >> 1, tn = wave & 1;  // this wave's v_new / output tile
 
     // fp32 state: this lane's elements of its state tiles (rows c, column j)
