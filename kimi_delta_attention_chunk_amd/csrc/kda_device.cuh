@@ -212,6 +212,23 @@ struct SeqLayout {
         if (cu == nullptr) { c0 = n * nc_dense; c1 = c0 + nc_dense; }
         else { c0 = coff[n]; c1 = coff[n + 1]; }
     }
+    // Token range [s0, s0 + len) of sequence n.
+    __device__ __forceinline__ void seq_tokens(int n, int64_t& s0, int& len) const {
+        if (cu == nullptr) { s0 = (int64_t)n * T; len = T; }
+        else { s0 = cu[n]; len = cu[n + 1] - cu[n]; }
+    }
+    // Chunk i of sequence n whose tokens are [s0, s0 + len): the chunks of a
+    // sequence are consecutive and each starts 64 tokens after the previous
+    // one, so a sequential pass needs no per-chunk metadata loads.
+    __device__ __forceinline__ static ChunkRef chunk_of(int n, int i, int64_t s0, int len) {
+        ChunkRef r;
+        r.n = n;
+        r.i = i;
+        r.t0 = s0 + (int64_t)i * kChunk;
+        const int rem = len - i * kChunk;
+        r.len = rem < kChunk ? rem : kChunk;
+        return r;
+    }
 };
 
 }  // namespace kda

@@ -119,9 +119,14 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
     }
     int c0, c1;
     p.seq.seq_chunks(n, c0, c1);
+    int64_t s0;
+    int slen;
+    p.seq.seq_tokens(n, s0, slen);
     DhRegs<DK, TIn, P> R;
-    if (c0 < c1) dh_load<DK, DV, TIn, P>(p, (size_t)(c1 - 1) * p.H + h, p.seq.chunk(c1 - 1), h, jb, R);
-    for (int c = c1 - 1; c >= c0; --c) {
+    // The prefetch is unconditional (at the first chunk it reloads it), so the
+    // control flow around it is uniform and the wait covers one chunk only.
+    if (c0 < c1) dh_load<DK, DV, TIn, P>(p, (size_t)(c1 - 1) * p.H + h, SeqLayout::chunk_of(n, c1 - 1 - c0, s0, slen), h, jb, R);
+    for (int c = c1 - 1; c0 < c1 && c >= c0; --c) {
         const size_t slot = (size_t)c * p.H + h;
         __syncthreads();  // the previous chunk is done with the operand tiles
 #pragma unroll
@@ -149,7 +154,10 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
 #pragma unroll
         for (int i = 0; i < 4 * HPW; ++i) gl[i] = R.g[i];
         __syncthreads();
-        if (c - 1 >= c0) dh_load<DK, DV, TIn, P>(p, slot - p.H, p.seq.chunk(c - 1), h, jb, R);
+        {
+            const int cn = c - 1 >= c0 ? c - 1 : c0;
+            dh_load<DK, DV, TIn, P>(p, (size_t)cn * p.H + h, SeqLayout::chunk_of(n, cn - c0, s0, slen), h, jb, R);
+        }
         const bool odd = (c1 - 1 - c) & 1;
         const Tile<P> Db = odd ? DT1 : DT0;
         const Tile<P> Dn = odd ? DT0 : DT1;

@@ -51,16 +51,18 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
         load_afrag(R.w[kb], w + (size_t)(row * F::KB + kb) * kKBlockBytes);
         load_afrag(R.q[kb], q + (size_t)(row * F::KB + kb) * kKBlockBytes);
     }
+    // Every load below is unconditional (a wave without a state tile reads
+    // tile 0's operands, unused; Aqk's second block is read even where it is
+    // zero), so the batch has the same size on every wave and path.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)  // Aqk row t needs s < 16 (tm + 1)
-        if (kb <= (tm >> 1)) load_afrag(R.a[kb], a + (size_t)(row * 2 + kb) * kKBlockBytes);
+    for (int kb = 0; kb < 2; ++kb) if (kb <= (tm >> 1)) load_afrag(R.a[kb], a + (size_t)(row * 2 + kb) * kKBlockBytes);
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
         if (tile < F::TH) {
-            const int crow = 16 * (tile >> 1) + lr;
+        const int crow = 16 * (tile >> 1) + lr;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) load_afrag(R.k[i][kb], k + (size_t)(crow * 2 + kb) * kKBlockBytes);
+        for (int kb = 0; kb < 2; ++kb) load_afrag(R.k[i][kb], k + (size_t)(crow * 2 + kb) * kKBlockBytes);
         }
     }
     const float* u = p.u + slot * kChunk * DV + jb;
@@ -69,8 +71,8 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
-        if (tile < F::TH) {
-            const int tmh = tile >> 1;
+        {
+            const int tmh = (tile < F::TH ? tile : 0) >> 1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + tmh * 16 + frag_row(r)];
         }
@@ -113,14 +115,18 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
     }
     int c0, c1;
     p.seq.seq_chunks(n, c0, c1);
+    int64_t s0;
+    int slen;
+    p.seq.seq_tokens(n, s0, slen);
     TOut* o = (TOut*)p.o;
     F R[2];
-    if (c0 < c1) scan_load<DK, DV, P>(p, (size_t)c0 * p.H + h, jb, R[0]);
-    if (c0 + 1 < c1) scan_load<DK, DV, P>(p, (size_t)(c0 + 1) * p.H + h, jb, R[1]);
+    // Prefetches are unconditional (past the last chunk they reload it), so the
+    // control flow around them is uniform and each wait covers one chunk only.
+    auto slot_of = [&](int cc) { return (size_t)(cc < c1 ? cc : c1 - 1) * p.H + h; };
 
     // One chunk: v_new = u - w h; h' = Diag(exp G_L) h + Kh^T v_new; o = scale (Qg h + Aqk v_new).
     auto step = [&](int c, F& Rc) {
-        const ChunkRef cr = p.seq.chunk(c);
+        const ChunkRef cr = SeqLayout::chunk_of(n, c - c0, s0, slen);
         const size_t slot = (size_t)c * p.H + h;
         const bool odd = (c - c0) & 1;
         const Tile<P> hb = odd ? hT1 : hT0;
@@ -181,12 +187,19 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
             }
         }
     };
-    for (int c = c0; c < c1; c += 2) {
-        step(c, R[0]);
-        if (c + 2 < c1) scan_load<DK, DV, P>(p, (size_t)(c + 2) * p.H + h, jb, R[0]);
-        if (c + 1 < c1) {
-            step(c + 1, R[1]);
-            if (c + 3 < c1) scan_load<DK, DV, P>(p, (size_t)(c + 3) * p.H + h, jb, R[1]);
+    if (c0 < c1) {
+        // (scheduling barriers keep the two batches in issue order: the
+        // waits count completions in order)
+        scan_load<DK, DV, P>(p, slot_of(c0), jb, R[0]);
+        scan_load<DK, DV, P>(p, slot_of(c0 + 1), jb, R[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c = c0; c < c1; c += 2) {
+            step(c, R[0]);
+            scan_load<DK, DV, P>(p, slot_of(c + 2), jb, R[0]);
+            if (c + 1 < c1) {
+                step(c + 1, R[1]);
+                scan_load<DK, DV, P>(p, slot_of(c + 3), jb, R[1]);
+            }
         }
     }
     if (p.hT) {
