@@ -28,6 +28,7 @@
 #include "kda_chunk.cuh"
 #include "kda_bwdchunk.cuh"
 #include "kda_dhscan.cuh"
+#include "kda_pscan.cuh"
 #include "kda_internal.h"
 
 namespace kda {
@@ -640,7 +641,9 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     }
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     const int total = a.N * a.H * (DV / kBV);
-    if constexpr (DK <= 64) {
+    if constexpr (DK == 32 && DV == 64) {
+        KDA_LAUNCH("bwd_dh", (bwd_pdh_kernel<TIn, P>), dim3(total), dim3(kPsThreads), s, p, total);
+    } else if constexpr (DK <= 64) {
         KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     } else {
         KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);

@@ -100,19 +100,15 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             load4<TIn>(doin + vb, dox[b]);
         }
     }
-    f32x4 Tr[NT4], Hr[NH4], Dr[NH4], Vn[NV4], dVn[NV4];
+    f32x4 Tr[NT4], Hr[NH4], Dr[NH4];
     {
         const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
         const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
         const f32x4* d4 = (const f32x4*)(p.dhs + slot * DK * DV);
-        const f32x4* v4 = (const f32x4*)(p.vn + slot * kChunk * DV);
-        const f32x4* w4 = (const f32x4*)(p.dvn + slot * kChunk * DV);
 #pragma unroll
         for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + NTH * i];
 #pragma unroll
         for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
-#pragma unroll
-        for (int i = 0; i < NV4; ++i) { Vn[i] = v4[tid + NTH * i]; dVn[i] = w4[tid + NTH * i]; }
     }
     if (tid < kChunk && tid >= cr.len) braw = 0.f;
 #pragma unroll
@@ -181,6 +177,122 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     if (tr == last) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) GL[4 * part + i] = G[i];
+    }
+
+    // ------------------------------------------------ P0: v_new and dv_new of the chunk
+    //   v_new  = T (beta V - (beta Kg) h)      (= u - w h)
+    //   dv_new = Kh D' + scale Aqk^T dO         (D' = dL/dS at the chunk end)
+    // h^T and D'^T come as row fragments from the state passes' k-block copies
+    // and Aqk^T from the intra-chunk kernel's; beta Kg, Kh, T and dO^T are staged
+    // in LDS.  Wave w forms 64x64 tiles (w >> 1, 2 (w & 1) + e), e = 0, 1; the
+    // results pass through fp32 LDS staging into the row-major registers Vn, dVn
+    // that the dv-side phase stages from.
+    f32x4 Vn[NV4], dVn[NV4];
+    {
+        const int tm = wave >> 1, tn0 = 2 * (wave & 1);
+        const int lr = lane & 15, lg = lane >> 4;
+        AFrag<P> fh[2], fd[2], fa[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            load_afrag(fh[e], (const char*)(p.hsT + slot * DK * DV) + (size_t)(16 * (tn0 + e) + lr) * kKBlockBytes);
+            load_afrag(fd[e], (const char*)(p.dhsT + slot * DK * DV) + (size_t)(16 * (tn0 + e) + lr) * kKBlockBytes);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
+            if (kb >= (tm >> 1))
+                load_afrag(fa[kb], (const char*)(p.aqT + slot * kChunk * kChunk) + (size_t)((16 * tm + lr) * 2 + kb) * kKBlockBytes);
+        float vv[2][4];  // V at this lane's result positions (zero past the chunk end)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tm + 4 * lg + r;
+            const size_t row = tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DV);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float x = Elem<TIn>::load(vin, row + 16 * (tn0 + e) + lr);
+                vv[e][r] = t < cr.len ? x : 0.f;
+            }
+        }
+        // ph: [0, 2560) beta Kg; [2560, 5120) Kh; [5120, 9728) T; [9728, 14336) dO^T;
+        //     [14336, 18688) dv_new and [18688, 23040) v_new, fp32 [t][68]; Z^T over [0, 4608)
+        const Tile<P> BKG(ph, kChunk, L40), KHt(ph + 2560, kChunk, L40), TRW(ph + 5120, kChunk, L72),
+            DOT(ph + 9728, DV, L72);
+        float* DVNs = ph + 14336;
+        float* VNs = ph + 18688;
+        static_assert(18688 + kChunk * 68 <= PH, "P0 staging must fit in ph");
+        {
+            const float b = bet[tr];
+            f32x4 xg, xh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gL = Gs[last * LR + 4 * part + i];  // in-chunk decay at the last token
+                xg[i] = b * __expf(G[i]) * kx[i];
+                xh[i] = kx[i] * __expf(gL - G[i]);
+            }
+            BKG.put4(tr, 4 * part, xg);
+            KHt.put4(tr, 4 * part, xh);
+        }
+#pragma unroll
+        for (int i = 0; i < NT4; ++i) {
+            const int e4 = 4 * (tid + NTH * i);
+            TRW.put4(e4 >> 6, e4 & 63, Tr[i]);
+        }
+#pragma unroll
+        for (int b = 0; b < NVB; ++b)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) DOT.put(32 * b + 4 * part + m, tr, dox[b][m]);
+        __syncthreads();
+        f32x4 z[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int tn = tn0 + e;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            AFrag<P> fx, fy;
+            load_frag(fx, BKG.sub(16 * tm), 0);
+            const f32x4 y = mma_ff(fx, fh[e], zero);
+            load_frag(fx, KHt.sub(16 * tm), 0);
+            const f32x4 x1 = mma_ff(fx, fd[e], zero);
+            f32x4 x2 = zero;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb >= (tm >> 1)) {
+                    load_frag(fy, DOT.sub(16 * tn), 32 * kb);
+                    x2 = mma_ff(fa[kb], fy, x2);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tm + 4 * lg + r;
+                z[e][r] = bet[t] * vv[e][r] - y[r];
+                DVNs[t * 68 + 16 * tn + lr] = x1[r] + scale * x2[r];
+            }
+        }
+        __syncthreads();  // beta Kg and Kh consumed
+        const Tile<P> ZT(ph, DV, L72);  // Z^T [j][s]
+#pragma unroll
+        for (int e = 0; e < 2; ++e) ZT.put4(16 * (tn0 + e) + lr, 16 * tm + 4 * lg, z[e]);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int tn = tn0 + e;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            AFrag<P> fx, fy;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb <= (tm >> 1)) {  // T is lower triangular
+                    load_frag(fx, TRW.sub(16 * tm), 32 * kb);
+                    load_frag(fy, ZT.sub(16 * tn), 32 * kb);
+                    acc = mma_ff(fx, fy, acc);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) VNs[(16 * tm + 4 * lg + r) * 68 + 16 * tn + lr] = acc[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int e4 = 4 * (tid + NTH * i);
+            const int t = e4 / DV, j = e4 - t * DV;
+            Vn[i] = *(const f32x4*)&VNs[t * 68 + j];
+            dVn[i] = *(const f32x4*)&DVNs[t * 68 + j];
+        }
     }
 
     // ------------------------------------------------ P1: contractions over dv

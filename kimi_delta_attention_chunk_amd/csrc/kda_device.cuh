@@ -79,6 +79,25 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4
     *(u32x2*)p = v;
 }
 
+// Load 8 consecutive elements of one token row (16-byte aligned) as fp32.
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(v[i] << 16);
+        x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+
 // ----------------------------------------------------------------- prep math
 // Hardware transcendentals (v_exp_f32, v_log_f32, v_rcp_f32: about 1 ulp),
 // instead of the library's range-reduced versions: the preparation runs

@@ -13,6 +13,7 @@
 #include "kda_chunk.cuh"
 #include "kda_internal.h"
 #include "kda_intra.cuh"
+#include "kda_pscan.cuh"
 #include "kda_scan.cuh"
 
 namespace kda {
@@ -166,6 +167,8 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.dqt = at(L.dqt); p.dkh = at(L.dkh); p.dwv = at(L.dwv); p.daq = at(L.daq); p.dtv = at(L.dtv);
     p.dgl = at(L.dgl); p.dbv = at(L.dbv);
     p.dkt = at(L.dkt); p.dxq = at(L.dxq); p.dxk = at(L.dxk); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
+    p.pm = at(L.pm); p.pmT = at(L.pmT); p.hh = at(L.hh); p.qh = at(L.qh); p.qhT = at(L.qhT); p.ol = at(L.ol);
+    p.aqT = at(L.aqT); p.hsT = at(L.hsT); p.dhsT = at(L.dhsT);
     return p;
 }
 
@@ -184,6 +187,19 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     take(L.qg, slots * C * dk);
     take(L.khT, slots * C * dk);
     take(L.gl, slots * dk);
+    if (dk == 32 && dv == 64) {
+        take(L.pm, slots * dk * dk);
+        take(L.pmT, slots * dk * dk);
+        take(L.hh, slots * dk * dv);
+        take(L.qh, slots * C * dk);
+        take(L.qhT, slots * C * dk);
+        take(L.ol, slots * C * dv);
+        if (backward) {
+            take(L.aqT, slots * C * C);
+            take(L.hsT, slots * dk * dv);
+            take(L.dhsT, slots * dk * dv);
+        }
+    }
     if (backward) {
         take(L.tm, slots * C * C);
         take(L.dhs, slots * dk * dv);
@@ -219,7 +235,11 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     if (a.n_chunks_bound > 0)
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
-    if constexpr (DK <= 64) {
+    if constexpr (DK == 32 && DV == 64) {
+        const int total = a.N * a.H * (DV / 32);
+        KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P>), dim3(total), dim3(kPsThreads), s, p, total,
+                   write_o ? 1 : 0, store ? 1 : 0);
+    } else if constexpr (DK <= 64) {
         const int total = a.N * a.H * (DV / 32);
         KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, TOut, P>), dim3(total), dim3(kScanThreads), s, p, total,
                    write_o ? 1 : 0, store ? 1 : 0);

@@ -57,25 +57,6 @@ __device__ __forceinline__ float wave_scan(float x) {
     return x;
 }
 
-// Load 8 consecutive elements of one token row (16-byte aligned) as fp32.
-template <typename TIn>
-__device__ __forceinline__ void load8(const TIn* p, float (&x)[8]);
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3]; x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
-}
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(v[i] << 16);
-        x[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
-    }
-}
-
 // The p-th pair (t, s), s <= t, of the four 16x16 diagonal blocks (136 each).
 __device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
     const int I = p / 136, q = p - 136 * I;
@@ -109,6 +90,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
     __shared__ float bet[kChunk];
     __shared__ float seg[8 * 32];        // column-scan segment totals
+    __shared__ float glS[DK];            // exp(G_L) (pass 3)
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
     static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
@@ -203,6 +185,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,
     // and this thread's 4 diagonal-block entries of each.
     f32x4 gacc[3];
+    float khs[8];  // this thread's Kh row values (dk = 32, pass 3)
 #pragma unroll
     for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dkk[3] = {0.f, 0.f, 0.f}, dqk[3] = {0.f, 0.f, 0.f};
@@ -232,13 +215,14 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         // scaled operands for the off-diagonal Gram blocks, exp(G) q, k exp(G_L - G)
         {
             const int I = tr >> 4;
-            float qgv[8];
+            float qgv[8], khv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int cc = 8 * part + i;
                 const float gt = G[b][i];
                 qgv[i] = __expf(gt) * qx[b][i];
-                KhS[cc * kLD + tr] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
+                khv[i] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
+                KhS[cc * kLD + tr] = khv[i];
                 if (I >= 1) {
                     const float e = __expf(gt - Gb[16 * I * kLB + cc]);
                     Kr.put(tr - 16, cc, kx[b][i] * e);
@@ -248,14 +232,19 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 for (int J = 1; J <= 3; ++J)
                     if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt));
             }
-            store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
+            if constexpr (DK != 32)  // (dk = 32 keeps the affine form instead)
+                store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
+            if constexpr (DK == 32) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) khs[i] = khv[i];
+            }
         }
-        if (tr == 0) {
+        if (DK != 32 && tr == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gb[last * kLB + 8 * part + i]);
         }
         __syncthreads();
-        {
+        if constexpr (DK != 32) {
             // (k exp(G_L - G))^T of this channel block to the workspace: row c = cb + tid / 8
             const int cr8 = threadIdx.x >> 3, w8 = threadIdx.x & 7;
             float x[8];
@@ -343,7 +332,23 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
             store_kblock8<WP>(aq + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, x, (s0 >> 3) & 3);
         }
+        if (p.aqT) {
+            // Aqk^T (row s, indices t; zero for t < s) for the backward
+            char* aqt = (char*)(p.aqT + slot * kChunk * kChunk);
+#pragma unroll
+            for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
+                const int q8 = threadIdx.x + kThreads * i;
+                const int sr = q8 >> 3, t0 = 8 * (q8 & 7);
+                float x[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
+                store_kblock8<WP>(aqt + (size_t)(sr * 2 + (t0 >> 5)) * kKBlockBytes, x, (t0 >> 3) & 3);
+            }
+        }
     }
+    // Aqk is read back by every wave in pass 3: release it to the workgroup
+    // before the solve's barriers.
+    __threadfence_block();
     solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
     if (p.tm) {
         f32x4* to = (f32x4*)(p.tm + slot * kChunk * kChunk);
@@ -364,6 +369,8 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     constexpr int GRP = (3 * kChunk * kLB) / (kCB32 * LA);  // blocks per round
     static_assert(GRP >= 1, "one operand block must fit in KQG");
     const float bt = bet[tr];
+    static_assert(DK != 32 || NBLK <= GRP, "dk = 32: w and u in one round");
+    f32x4 pacc[DK == 32 ? (8 * GRP + kWaves - 1) / kWaves : 1];  // this wave's w / u tiles (dk = 32)
     float* wo = p.w + slot * kChunk * DK;
     float* uo = p.u + slot * kChunk * DV;
 #pragma unroll
@@ -383,7 +390,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         __syncthreads();
         constexpr int TPB = 8;  // [64 x 32] tiles per block
         const int nb = NBLK - b0 < GRP ? NBLK - b0 : GRP;
-        for (int tile = wave; tile < TPB * nb; tile += kWaves) {
+#pragma unroll
+        for (int kt = 0; kt < (TPB * GRP + kWaves - 1) / kWaves; ++kt) {
+            const int tile = wave + kWaves * kt;
+            if (tile >= TPB * nb) break;
             const int g = tile / TPB, tl = tile % TPB, tm = tl >> 1, tn = tl & 1;
             const int b = b0 + g;
             const Tile<P> BTg(KQG + g * kCB32 * LA, kCB32, LA);
@@ -391,6 +401,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
+            if constexpr (DK == 32) {
+                pacc[kt] = acc;  // w and u go on to pass 3 only
+                continue;
+            }
             if (DK <= 64 && b < NB) {  // w: staged in Tm [t][c] (stride kLD), written out below
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Tm[(tm * 16 + frag_row(r)) * kLD + b * kCB32 + tn * 16 + frag_col()] = acc[r];
@@ -402,7 +416,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             }
         }
     }
-    if constexpr (DK <= 64) {
+    if constexpr (DK == 64) {
         __syncthreads();
         char* wk = (char*)wo;  // [t][DK/32] k-blocks
 #pragma unroll
@@ -415,6 +429,147 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 for (int m = 0; m < 8; ++m) x[m] = Tm[t * kLD + k0 + m];
                 store_kblock8<WP>(wk + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, x, (k0 >> 3) & 3);
             }
+        }
+    }
+    if constexpr (DK == 32) {
+        __syncthreads();  // pass-2 operand tiles (KQG, S1) consumed
+        // ---- pass 3: the chunk as an affine map of the state entering it (dk = 32).
+        //   P   = Diag(exp G_L) - Kh^T w      (32 x 32)   h'     = P h + hh
+        //   hh  = Kh^T u                      (32 x 64)
+        //   qh  = scale (Qg - Aqk w)          (64 x 32)   o      = ol + qh h
+        //   ol  = scale Aqk u                 (64 x 64)
+        // and for the reverse pass D = P^T D' + qh^T dO.  w^T and u^T are staged in
+        // LDS from this wave's pass-2 tiles and Kh^T from the pass-1 registers; Aqk
+        // is read back as register fragments from its k-block array written above.  A D fragment holds four
+        // consecutive rows of one column, so each k-block array is written from the
+        // product of its transpose: P from P^T's tiles and P^T from P's, qh from
+        // qh^T's and qh^T from qh's.  hh and ol are kept in fragment order
+        // ([32-column block][16x16 tile][lane][4]) for the state pass to add to its
+        // accumulators directly.
+        const Tile<P> WT(KQG, DK, LA), UT(KQG + DK * LA, DV, LA);
+        static_assert(DK * LA + DV * LA <= 3 * kChunk * kLB, "w^T and u^T must fit in KQG");
+        float* Qgs = S1;  // exp(G) q, fp32 [t][c], stride kLB
+        const Tile<P> KHT(S1 + kChunk * kLB, DK, LA);  // Kh^T [c][t]
+        static_assert(kChunk * kLB + DK * LA <= S1F, "Qg and Kh^T must fit in S1");
+#pragma unroll
+        for (int i = 0; i < 8; ++i) KHT.put(8 * part + i, tr, khs[i]);
+#pragma unroll
+        for (int kt = 0; kt < (8 * GRP + kWaves - 1) / kWaves; ++kt) {
+            const int tile = wave + kWaves * kt, g = tile / 8, tl = tile % 8, tm = tl >> 1, tn = tl & 1;
+            if (g == 0) WT.put4(tn * 16 + frag_col(), tm * 16 + frag_row(0), pacc[kt]);
+            else UT.put4((g - 1) * 32 + tn * 16 + frag_col(), tm * 16 + frag_row(0), pacc[kt]);
+        }
+        {
+            float qv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = __expf(G[0][i]) * qx[0][i];
+            *(f32x4*)&Qgs[tr * kLB + 8 * part] = f32x4{qv[0], qv[1], qv[2], qv[3]};
+            *(f32x4*)&Qgs[tr * kLB + 8 * part + 4] = f32x4{qv[4], qv[5], qv[6], qv[7]};
+            if (tr == last) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) glS[8 * part + i] = __expf(G[0][i]);
+            }
+        }
+        const char* aqb = (const char*)(p.aqk + slot * kChunk * kChunk);  // [t][2]
+        const int lr = threadIdx.x & 15, lg = (threadIdx.x & 63) >> 4;
+        const float scale = p.scale;
+        // Each wave reads all of Kh^T (two row tiles, two k-blocks; from LDS) and
+        // the Aqk rows of its own 16 output rows (from the k-block array) once, as
+        // register fragments, then forms:
+        //   wave 0: P;  wave 1: P^T;  waves 2, 3: hh rows 16 (w - 2) ..
+        //   all:    qh, qh^T and ol for rows (columns of qh^T) 16 w .. 16 w + 15.
+        AFrag<P> fK[2][2], fQ[2];
+        const int nq = (wave >> 1) + 1;  // Aqk row block w reaches s < 16 (w + 1): k-blocks 0 .. w >> 1
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < nq) load_afrag(fQ[kb], aqb + (size_t)((16 * wave + lr) * 2 + kb) * kKBlockBytes);
+        __syncthreads();
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) load_frag(fK[ta][kb], KHT.sub(16 * ta), 32 * kb);
+        AFrag<P> fb;
+        if (wave < 2) {
+            // P (wave 0) and P^T (wave 1): four 16x16 tiles (ta, tb) of rows c, columns c'
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ta = q >> 1, tb = q & 1;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (wave == 0) {
+                        load_frag(fb, WT.sub(16 * tb), 32 * kb);
+                        acc = mma_ff(fK[ta][kb], fb, acc);
+                    } else {
+                        load_frag(fb, WT.sub(16 * ta), 32 * kb);
+                        acc = mma_ff(fb, fK[tb][kb], acc);
+                    }
+                }
+                f32x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ra = 16 * ta + 4 * lg + i, cb = 16 * tb + lr;
+                    x[i] = (ra == cb ? glS[ra] : 0.f) - acc[i];
+                }
+                float* dst = wave == 0 ? p.pmT : p.pm;
+                store_kblock4<P>((char*)(dst + slot * DK * DK) + (size_t)(16 * tb + lr) * kKBlockBytes, x,
+                                 16 * ta + 4 * lg);
+            }
+        } else {
+            // hh rows 16 ta .., all four column tiles
+            const int ta = wave - 2;
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    load_frag(fb, UT.sub(16 * tj), 32 * kb);
+                    acc = mma_ff(ta == 0 ? fK[0][kb] : fK[1][kb], fb, acc);  // (no dynamic register index)
+                }
+                *(f32x4*)(p.hh + slot * DK * DV + (size_t)(((tj >> 1) * 4 + ta * 2 + (tj & 1)) * 64 + (threadIdx.x & 63)) * 4) =
+                    acc;
+            }
+        }
+        const int tt = wave;
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+            // qh tile (t-tile tt, c-tile tc) -> qh^T (row c, indices t), and qh^T tile (tc, tt) -> qh
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb < nq) {
+                    load_frag(fb, WT.sub(16 * tc), 32 * kb);
+                    a1 = mma_ff(fQ[kb], fb, a1);
+                    a2 = mma_ff(fb, fQ[kb], a2);
+                }
+            }
+            f32x4 x1, x2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int a = 4 * lg + i;
+                x1[i] = scale * (Qgs[(16 * tt + a) * kLB + 16 * tc + lr] - a1[i]);
+                x2[i] = scale * (Qgs[(16 * tt + lr) * kLB + 16 * tc + a] - a2[i]);
+            }
+            store_kblock4<P>((char*)(p.qhT + slot * kChunk * DK) + (size_t)((16 * tc + lr) * 2 + (tt >> 1)) * kKBlockBytes,
+                             x1, (16 * tt + 4 * lg) & 31);
+            store_kblock4<P>((char*)(p.qh + slot * kChunk * DK) + (size_t)(16 * tt + lr) * kKBlockBytes, x2,
+                             16 * tc + 4 * lg);
+        }
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            // ol tile (t-tile tt, column tile tj)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb < nq) {
+                    load_frag(fb, UT.sub(16 * tj), 32 * kb);
+                    acc = mma_ff(fQ[kb], fb, acc);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= scale;
+            *(f32x4*)(p.ol + slot * kChunk * DV + (size_t)(((tj >> 1) * 8 + tt * 2 + (tj & 1)) * 64 + (threadIdx.x & 63)) * 4) =
+                acc;
         }
     }
 }

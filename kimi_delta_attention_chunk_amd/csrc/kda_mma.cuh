@@ -234,6 +234,62 @@ __device__ __forceinline__ void put_kchunk_t(const Tile<Prec::F32>& T, int k0, i
     }
 }
 
+// ----------------------------------------------------------------- fragments in registers
+// Either operand of a product may be held as a register fragment: for C = A B^T
+// the B fragment of output column n has the same lane layout as the A fragment
+// of row n (row = lane & 15, indices 8 g .. 8 g + 7 of the k-block, g = lane >> 4).
+// A fragment of a tile in LDS (`T` at its origin row), k-block starting at kb.
+__device__ __forceinline__ void load_frag(AFrag<Prec::BF3>& f, const Tile<Prec::BF3>& T, int kb) {
+    const int lane = threadIdx.x & 63;
+    const int o = (lane & 15) * T.ld + kb + 8 * (lane >> 4);
+    f.hi = *(const bf16x8*)(T.hi + o);
+    f.lo = *(const bf16x8*)(T.lo + o);
+}
+__device__ __forceinline__ void load_frag(AFrag<Prec::F32>& f, const Tile<Prec::F32>& T, int kb) {
+    const int lane = threadIdx.x & 63;
+    const float* q = T.p + (lane & 15) * T.ld + kb + 8 * (lane >> 4);
+    f.a = *(const f32x4*)q;
+    f.b = *(const f32x4*)(q + 4);
+}
+// acc += A B^T over one k-block, both operands as register fragments.
+__device__ __forceinline__ f32x4 mma_ff(const AFrag<Prec::BF3>& a, const AFrag<Prec::BF3>& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 mma_ff(const AFrag<Prec::F32>& a, const AFrag<Prec::F32>& b, f32x4 acc) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[kk], b.a[kk], acc, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[kk], b.b[kk], acc, 0, 0, 0);
+    return acc;
+}
+
+// Write 4 consecutive values (indices k0 .. k0 + 3 of a k-block, k0 a multiple
+// of 4) of one row in k-block form.  A D fragment holds, per lane, four
+// consecutive rows of one column, i.e. four consecutive k-block indices of a
+// row of the transposed result.
+template <Prec P>
+__device__ __forceinline__ void store_kblock4(void* rowblock, const f32x4& x, int k0);
+template <>
+__device__ __forceinline__ void store_kblock4<Prec::BF3>(void* rowblock, const f32x4& x, int k0) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = (__bf16)x[i];
+        l[i] = (__bf16)(x[i] - (float)h[i]);
+    }
+    char* b = (char*)rowblock;
+    *(bf16x4*)(b + 2 * k0) = h;
+    *(bf16x4*)(b + 64 + 2 * k0) = l;
+}
+template <>
+__device__ __forceinline__ void store_kblock4<Prec::F32>(void* rowblock, const f32x4& x, int k0) {
+    *(f32x4*)((float*)rowblock + k0) = x;
+}
+
 // Round a k range outward to the step of P (for triangular factors whose
 // entries outside the exact range are zero).
 template <Prec P>
