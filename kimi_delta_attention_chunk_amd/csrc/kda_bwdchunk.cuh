@@ -51,9 +51,12 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     __shared__ __attribute__((aligned(16))) float Ks[kChunk * LR];
     __shared__ __attribute__((aligned(16))) float Qs[kChunk * LR];
     __shared__ __attribute__((aligned(16))) float Gs[kChunk * LR];
-    __shared__ __attribute__((aligned(16))) float DQ[kChunk * LR];
-    __shared__ __attribute__((aligned(16))) float DKa[kChunk * LR];
-    __shared__ __attribute__((aligned(16))) float DG[kChunk * LR];
+    // gradient accumulators DQ, DKa, DG, one array (P0 uses it as fp32 staging
+    // before the first accumulator is written)
+    __shared__ __attribute__((aligned(16))) float ACC[3 * kChunk * LR];
+    float* const DQ = ACC;
+    float* const DKa = ACC + kChunk * LR;
+    float* const DG = ACC + 2 * kChunk * LR;
     __shared__ float dAd[4 * 16 * 17], dAqd[4 * 16 * 17];  // diagonal blocks of dA, dAq
     __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
     __shared__ float seg[16 * 32], wsum[NW];
@@ -101,6 +104,12 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
     }
     f32x4 Tr[NT4], Hr[NH4], Dr[NH4];
+    AFrag<P> fa[2];  // Aqk^T rows 16 (w >> 1) .., k-blocks (w >> 2) .. 1 (P0)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
+        if (kb >= (wave >> 2))
+            load_afrag(fa[kb], (const char*)(p.aqT + slot * kChunk * kChunk) +
+                                   (size_t)((16 * (wave >> 1) + (lane & 15)) * 2 + kb) * kKBlockBytes);
     {
         const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
         const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
@@ -182,43 +191,24 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ P0: v_new and dv_new of the chunk
     //   v_new  = T (beta V - (beta Kg) h)      (= u - w h)
     //   dv_new = Kh D' + scale Aqk^T dO         (D' = dL/dS at the chunk end)
-    // h^T and D'^T come as row fragments from the state passes' k-block copies
-    // and Aqk^T from the intra-chunk kernel's; beta Kg, Kh, T and dO^T are staged
-    // in LDS.  Wave w forms 64x64 tiles (w >> 1, 2 (w & 1) + e), e = 0, 1; the
-    // results pass through fp32 LDS staging into the row-major registers Vn, dVn
-    // that the dv-side phase stages from.
+    // Aqk^T comes as row fragments from the intra-chunk kernel's k-block array;
+    // T, beta Kg, Kh, h^T, D'^T and dO^T are staged in LDS from registers.  Wave w
+    // forms 64x64 tiles (w >> 1, 2 (w & 1) + e), e = 0, 1; the results pass
+    // through fp32 LDS staging into the row-major registers Vn, dVn that the
+    // dv-side phase stages from.
     f32x4 Vn[NV4], dVn[NV4];
     {
         const int tm = wave >> 1, tn0 = 2 * (wave & 1);
         const int lr = lane & 15, lg = lane >> 4;
-        AFrag<P> fh[2], fd[2], fa[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            load_afrag(fh[e], (const char*)(p.hsT + slot * DK * DV) + (size_t)(16 * (tn0 + e) + lr) * kKBlockBytes);
-            load_afrag(fd[e], (const char*)(p.dhsT + slot * DK * DV) + (size_t)(16 * (tn0 + e) + lr) * kKBlockBytes);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
-            if (kb >= (tm >> 1))
-                load_afrag(fa[kb], (const char*)(p.aqT + slot * kChunk * kChunk) + (size_t)((16 * tm + lr) * 2 + kb) * kKBlockBytes);
-        float vv[2][4];  // V at this lane's result positions (zero past the chunk end)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * tm + 4 * lg + r;
-            const size_t row = tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DV);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float x = Elem<TIn>::load(vin, row + 16 * (tn0 + e) + lr);
-                vv[e][r] = t < cr.len ? x : 0.f;
-            }
-        }
-        // ph: [0, 2560) beta Kg; [2560, 5120) Kh; [5120, 9728) T; [9728, 14336) dO^T;
-        //     [14336, 18688) dv_new and [18688, 23040) v_new, fp32 [t][68]; Z^T over [0, 4608)
-        const Tile<P> BKG(ph, kChunk, L40), KHt(ph + 2560, kChunk, L40), TRW(ph + 5120, kChunk, L72),
-            DOT(ph + 9728, DV, L72);
-        float* DVNs = ph + 14336;
-        float* VNs = ph + 18688;
-        static_assert(18688 + kChunk * 68 <= PH, "P0 staging must fit in ph");
+        // ph: [0, 4608) T;  [4608, 7168) beta Kg;  [7168, 9728) Kh;  [9728, 12288) h^T;
+        //     [12288, 14848) D'^T;  [14848, 19456) dO^T;  then Z^T over [4608, 9216) and
+        //     v_new (fp32 [t][68]) over [9728, 14080).  ACC: V, then dv_new (fp32 [t][68]).
+        const Tile<P> TRW(ph, kChunk, L72), BKG(ph + 4608, kChunk, L40), KHt(ph + 7168, kChunk, L40),
+            HTt(ph + 9728, DV, L40), DTt(ph + 12288, DV, L40), DOT(ph + 14848, DV, L72);
+        float* const VS = ACC;  // V, overwritten in place by dv_new
+        float* const VNs = ph + 9728;
+        static_assert(14848 + DV * L72 <= PH && 9728 + kChunk * 68 <= 14848 && kChunk * 68 <= 3 * kChunk * LR,
+                      "P0 staging must fit");
         {
             const float b = bet[tr];
             f32x4 xg, xh;
@@ -230,6 +220,12 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             }
             BKG.put4(tr, 4 * part, xg);
             KHt.put4(tr, 4 * part, xh);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                *(f32x4*)&VS[tr * 68 + 32 * vb + 4 * part] = f32x4{vx[vb][0], vx[vb][1], vx[vb][2], vx[vb][3]};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) DOT.put(32 * vb + 4 * part + m, tr, dox[vb][m]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
@@ -237,9 +233,15 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             TRW.put4(e4 >> 6, e4 & 63, Tr[i]);
         }
 #pragma unroll
-        for (int b = 0; b < NVB; ++b)
+        for (int i = 0; i < NH4; ++i) {  // h and D' rows c, columns j .. j + 3 -> h^T, D'^T [j][c]
+            const int e4 = 4 * (tid + NTH * i);
+            const int cc = e4 / DV, j = e4 - cc * DV;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) DOT.put(32 * b + 4 * part + m, tr, dox[b][m]);
+            for (int m = 0; m < 4; ++m) {
+                HTt.put(j + m, cc, Hr[i][m]);
+                DTt.put(j + m, cc, Dr[i][m]);
+            }
+        }
         __syncthreads();
         f32x4 z[2];
 #pragma unroll
@@ -248,9 +250,11 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             AFrag<P> fx, fy;
             load_frag(fx, BKG.sub(16 * tm), 0);
-            const f32x4 y = mma_ff(fx, fh[e], zero);
+            load_frag(fy, HTt.sub(16 * tn), 0);
+            const f32x4 y = mma_ff(fx, fy, zero);
             load_frag(fx, KHt.sub(16 * tm), 0);
-            const f32x4 x1 = mma_ff(fx, fd[e], zero);
+            load_frag(fy, DTt.sub(16 * tn), 0);
+            const f32x4 x1 = mma_ff(fx, fy, zero);
             f32x4 x2 = zero;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -261,12 +265,13 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * tm + 4 * lg + r;
-                z[e][r] = bet[t] * vv[e][r] - y[r];
-                DVNs[t * 68 + 16 * tn + lr] = x1[r] + scale * x2[r];
+                float* vd = &VS[t * 68 + 16 * tn + lr];  // V here, replaced by dv_new
+                z[e][r] = bet[t] * (*vd) - y[r];
+                *vd = x1[r] + scale * x2[r];
             }
         }
-        __syncthreads();  // beta Kg and Kh consumed
-        const Tile<P> ZT(ph, DV, L72);  // Z^T [j][s]
+        __syncthreads();  // beta Kg, Kh, h^T, D'^T consumed
+        const Tile<P> ZT(ph + 4608, DV, L72);  // Z^T [j][s]
 #pragma unroll
         for (int e = 0; e < 2; ++e) ZT.put4(16 * (tn0 + e) + lr, 16 * tm + 4 * lg, z[e]);
         __syncthreads();
@@ -291,7 +296,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             const int e4 = 4 * (tid + NTH * i);
             const int t = e4 / DV, j = e4 - t * DV;
             Vn[i] = *(const f32x4*)&VNs[t * 68 + j];
-            dVn[i] = *(const f32x4*)&DVNs[t * 68 + j];
+            dVn[i] = *(const f32x4*)&VS[t * 68 + j];
         }
     }
 

@@ -64,9 +64,6 @@ struct Prm {
     // the backward D = P^T D' + qh^T dO (k-block or fragment-order arrays, see
     // the intra-chunk kernel); aqT = Aqk^T for the backward chunk kernel
     float *pm, *pmT, *hh, *qh, *qhT, *ol, *aqT;
-    // k-block copies of the states h^T [j][c] and D^T [j][c] for the backward
-    // chunk kernel's v_new / dv_new products (dk = 32)
-    float *hsT, *dhsT;
 };
 
 __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {

@@ -168,7 +168,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.dgl = at(L.dgl); p.dbv = at(L.dbv);
     p.dkt = at(L.dkt); p.dxq = at(L.dxq); p.dxk = at(L.dxk); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
     p.pm = at(L.pm); p.pmT = at(L.pmT); p.hh = at(L.hh); p.qh = at(L.qh); p.qhT = at(L.qhT); p.ol = at(L.ol);
-    p.aqT = at(L.aqT); p.hsT = at(L.hsT); p.dhsT = at(L.dhsT);
+    p.aqT = at(L.aqT);
     return p;
 }
 
@@ -194,11 +194,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
         take(L.qh, slots * C * dk);
         take(L.qhT, slots * C * dk);
         take(L.ol, slots * C * dv);
-        if (backward) {
-            take(L.aqT, slots * C * C);
-            take(L.hsT, slots * dk * dv);
-            take(L.dhsT, slots * dk * dv);
-        }
+        if (backward) take(L.aqT, slots * C * C);
     }
     if (backward) {
         take(L.tm, slots * C * C);

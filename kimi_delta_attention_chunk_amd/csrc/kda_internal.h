@@ -58,7 +58,6 @@ struct WsLayout {
     size_t dqt, dkh, dwv, daq, dtv, dgl, dbv;        // dv-side intermediates
     size_t dkt, dxq, dxk, part_a, part_dt;           // dk-side intermediates
     size_t pm, pmT, hh, qh, qhT, ol, aqT;            // affine chunk form (dk = 32)
-    size_t hsT, dhsT;                                // k-block state copies for the backward (dk = 32)
     size_t total;
 };
 WsLayout ws_layout(const ChunkArgs& a, bool backward);

@@ -81,7 +81,6 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
             float* hs = p.hs + slot * DK * DV;
 #pragma unroll
             for (int r = 0; r < 4; ++r) hs[(size_t)(crow + r) * DV + jb + jcol] = S[r];
-            if (p.hsT) store_kblock4<P>((char*)(p.hsT + slot * DK * DV) + (size_t)(jb + jcol) * kKBlockBytes, S, crow);
         }
         __syncthreads();  // h^T of this chunk complete (the other buffer was read a chunk ago)
         AFrag<P> fb;
@@ -180,7 +179,6 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
         float* dhs = p.dhs + slot * DK * DV;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dhs[(size_t)(crow + r) * DV + jb + jcol] = D[r];
-        if (p.dhsT) store_kblock4<P>((char*)(p.dhsT + slot * DK * DV) + (size_t)(jb + jcol) * kKBlockBytes, D, crow);
         DT[buf].put4(jcol, crow, D);
 #pragma unroll
         for (int i = 0; i < 8; ++i) OT[buf].put(8 * part + i, tt, Rc.d[i]);
