@@ -642,7 +642,8 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     const int total = a.N * a.H * (DV / kBV);
     if constexpr (DK == 32 && DV == 64) {
-        KDA_LAUNCH("bwd_dh", (bwd_pdh_kernel<TIn, P>), dim3(total), dim3(kPsThreads), s, p, total);
+        const int tot16 = a.N * a.H * (DV / kPsBV);
+        KDA_LAUNCH("bwd_dh", (bwd_pdh_kernel<TIn, P, kPsBV>), dim3(tot16), dim3(kPsThreads), s, p, tot16);
     } else if constexpr (DK <= 64) {
         KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     } else {

@@ -232,8 +232,8 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
     if (a.n_chunks_bound > 0)
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     if constexpr (DK == 32 && DV == 64) {
-        const int total = a.N * a.H * (DV / 32);
-        KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P>), dim3(total), dim3(kPsThreads), s, p, total,
+        const int total = a.N * a.H * (DV / kPsBV);
+        KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV>), dim3(total), dim3(kPsThreads), s, p, total,
                    write_o ? 1 : 0, store ? 1 : 0);
     } else if constexpr (DK <= 64) {
         const int total = a.N * a.H * (DV / 32);
