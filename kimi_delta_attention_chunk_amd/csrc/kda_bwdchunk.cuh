@@ -658,40 +658,57 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
     }
-    // diagonal blocks, exact pairwise decays; lane = token t, waves take channels
+    // diagonal blocks, exact pairwise decays; lane = token t (row t >> 4 of the
+    // wave = diagonal block), each wave four channels.  The partner token s of
+    // the same block sits in lane s of the same 16-lane row, so its values come
+    // by DPP row broadcast from this lane's registers; the dA entries of (t, s)
+    // and (s, t) are read once per partner for all four channels.
     {
-        const int t = lane, blk = t >> 4, t0b = blk * 16;
-        float r_dbA = 0.f;  // this lane's share of dbeta from Akk
-#pragma unroll 1
+        const int t = lane, blk = t >> 4, tl = t & 15;
+        const float bt = bet[t];
+        float gtv[DK / NW], ktv[DK / NW], qtv[DK / NW];
+        float rkv[DK / NW], rqv[DK / NW], ck[DK / NW], cq[DK / NW];
+#pragma unroll
         for (int jc = 0; jc < DK / NW; ++jc) {
             const int cc = wave + NW * jc;
-            const float gt = Gs[t * LR + cc], kt = Ks[t * LR + cc], qt = Qs[t * LR + cc];
-            float rkv = 0.f, rqv = 0.f, ck = 0.f, cq = 0.f;
+            gtv[jc] = Gs[t * LR + cc];
+            ktv[jc] = Ks[t * LR + cc];
+            qtv[jc] = Qs[t * LR + cc];
+            rkv[jc] = rqv[jc] = ck[jc] = cq[jc] = 0.f;
+        }
+        const float* dAr_ = dAd + blk * 272;
+        const float* dAqr = dAqd + blk * 272;
+        static_for16([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            const float ad_ts = dAr_[tl * 17 + u], aq_ts = dAqr[tl * 17 + u];  // dA[t][s], dAq[t][s]
+            const float ad_st = dAr_[u * 17 + tl], aq_st = dAqr[u * 17 + tl];  // dA[s][t], dAq[s][t]
+            const float bad = row_bcast<u>(bt) * ad_st;                         // beta_s dA[s][t]
+            const bool lower = u <= tl;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int s = t0b + u;
-                const float gs = Gs[s * LR + cc], ks = Ks[s * LR + cc], qs = Qs[s * LR + cc];
-                const float ad_ts = dAd[blk * 272 + (t & 15) * 17 + u];   // dA[t][s]
-                const float aq_ts = dAqd[blk * 272 + (t & 15) * 17 + u];  // dAq[t][s]
-                const float ad_st = dAd[blk * 272 + u * 17 + (t & 15)];   // dA[s][t]
-                const float aq_st = dAqd[blk * 272 + u * 17 + (t & 15)];  // dAq[s][t]
+            for (int jc = 0; jc < DK / NW; ++jc) {
+                const float gs = row_bcast<u>(gtv[jc]), ks = row_bcast<u>(ktv[jc]), qs = row_bcast<u>(qtv[jc]);
                 // One exp per pair: e^{G_t - G_s} for s <= t, e^{G_s - G_t} for s >= t.  The
                 // stored diagonal blocks are zero outside their triangles (dA strictly lower,
                 // dAq lower), so each product below only counts on its own side.
-                const float x = gt - gs;
-                const float e = exp_hw(u <= (t & 15) ? x : -x);
+                const float x = gtv[jc] - gs;
+                const float e = exp_hw(lower ? x : -x);
                 const float ek = e * ks;
-                rkv = fmaf(ad_ts, ek, rkv);
-                rqv = fmaf(aq_ts, ek, rqv);
-                ck = fmaf(bet[s] * ad_st * ks, e, ck);
-                cq = fmaf(aq_st * qs, e, cq);
+                rkv[jc] = fmaf(ad_ts, ek, rkv[jc]);
+                rqv[jc] = fmaf(aq_ts, ek, rqv[jc]);
+                ck[jc] = fmaf(bad, ek, ck[jc]);
+                cq[jc] = fmaf(aq_st * qs, e, cq[jc]);
             }
-            const float bt = bet[t];
+        });
+        float r_dbA = 0.f;  // this lane's share of dbeta from Akk
+#pragma unroll
+        for (int jc = 0; jc < DK / NW; ++jc) {
+            const int cc = wave + NW * jc;
+            const float kt = ktv[jc], qt = qtv[jc];
             const float dk0 = DKa[t * LR + cc], dq0 = DQ[t * LR + cc], dg0 = DG[t * LR + cc];
-            DKa[t * LR + cc] = dk0 + (bt * rkv + ck + cq);
-            DQ[t * LR + cc] = dq0 + rqv;
-            DG[t * LR + cc] = dg0 + (bt * kt * rkv + qt * rqv - kt * (ck + cq));
-            r_dbA += kt * rkv;
+            DKa[t * LR + cc] = dk0 + (bt * rkv[jc] + ck[jc] + cq[jc]);
+            DQ[t * LR + cc] = dq0 + rqv[jc];
+            DG[t * LR + cc] = dg0 + (bt * kt * rkv[jc] + qt * rqv[jc] - kt * (ck[jc] + cq[jc]));
+            r_dbA += kt * rkv[jc];
         }
         rowp[wave * kChunk + lane] = r_dbA;
     }

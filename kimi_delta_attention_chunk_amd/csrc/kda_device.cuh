@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace kda {
 
 constexpr int kChunk = 64;     // chunk length (tokens)
@@ -146,6 +148,23 @@ __device__ __forceinline__ float sum_rows(float x) {
     return __int_as_float(b[0]) + __int_as_float(b[1]);  // lower half + upper half
 }
 __device__ __forceinline__ float wave_sum(float x) { return sum_rows(sum16(x)); }
+
+// Lane n of this lane's 16-lane row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+
+// f(std::integral_constant<int, u>) for u = 0 .. 15, in order (for DPP
+// controls and other immediates that must be compile-time constants).
+template <class F, int... U>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, U...>) {
+    (f(std::integral_constant<int, U>{}), ...);
+}
+template <class F>
+__device__ __forceinline__ void static_for16(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, 16>{});
+}
 
 // ----------------------------------------------------------------- MFMA fp32 tiles
 // acc(16x16) += A(16 x K) * B(K x 16) over k in [k0, k1), k1 - k0 a multiple of 4.
