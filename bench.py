@@ -42,23 +42,28 @@ def kda_work(B, T, H, dk, dv, C=64):
                                                              fwd_scan writes o and the final state
              backward read q, k, v, f, b, do; write dq, dk, dv, df, db
                                                           -> all of it in bwd_chunk
-      FLOPs  (2 per multiply-add, triangles counted as halves)
-             fwd_intra  Akk, Aqk, w (3 C dk), u (C dv), the unit-triangular inverse (C^2/3)
-             fwd_scan   w h, Kh^T v_new, Qg h (6 dk dv), Aqk v_new (C dv)
-             bwd_dh     Aqk^T dO (C dv), Kh D, Qg^T dO, w^T dv_new (6 dk dv)
-             bwd_chunk  dO h^T, vn D^T, dvn h^T (6 dk dv); dAqk, dT_v, T^T dvn (3 C dv);
-                        dw (bKg)^T, T^T dw (2 C dk); dA = -T^T dT T^T (2 C^2/3);
-                        four decayed pair sums (4 C dk)
-    Intermediates the kernels pass to each other (T, w, u, states, v_new, ...) are
-    not algorithmic bytes; the measured traffic shows them.
+      FLOPs  what each kernel computes (2 per multiply-add, triangles counted as halves),
+             per token-head, i.e. per chunk / C:
+             fwd_intra  Akk, Aqk, w (3 C dk), u (C dv), the unit-triangular inverse (C^2/3),
+                        and the affine chunk form: P, P^T (4 dk^2), hh (2 dk dv),
+                        qh, qh^T (2 C dk), ol (C dv)
+             fwd_scan   h' = P h + hh (2 dk^2 dv / C), o = ol + qh h (2 dk dv)
+             bwd_dh     D = P^T D' + qh^T dO (2 dk^2 dv / C + 2 dk dv)
+             bwd_chunk  v_new = T (beta V - beta Kg h), dv_new = Kh D' + Aqk^T dO
+                        (4 dk dv + 2 C dv); dO h^T, vn D^T, dvn h^T (6 dk dv);
+                        dAqk, dT_v, T^T dvn (3 C dv); dw (bKg)^T, T^T dw (2 C dk);
+                        dA = -T^T dT T^T (2 C^2/3); four decayed pair sums (4 C dk)
+    Intermediates the kernels pass to each other (T, the affine form, states, ...)
+    are not algorithmic bytes; the measured traffic shows them.
     """
     th = B * T * H  # token-heads
     per = {
-        "fwd_intra": (2 * 2 * dk + 2 * dv + 4 * dk + 4, 3 * C * dk + C * dv + C * C / 3),
-        "fwd_scan": (2 * dv + 4 * dk * dv / T, C * dv + 6 * dk * dv),
-        "bwd_dh": (0.0, C * dv + 6 * dk * dv),
+        "fwd_intra": (2 * 2 * dk + 2 * dv + 4 * dk + 4,
+                      3 * C * dk + C * dv + C * C / 3 + 4 * dk * dk + 2 * dk * dv + 2 * C * dk + C * dv),
+        "fwd_scan": (2 * dv + 4 * dk * dv / T, 2 * dk * dk * dv / C + 2 * dk * dv),
+        "bwd_dh": (0.0, 2 * dk * dk * dv / C + 2 * dk * dv),
         "bwd_chunk": (2 * 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv + 2 * 2 * dk + 2 * dv + 4 * dk + 4,
-                      6 * dk * dv + 3 * C * dv + 2 * C * dk + 2 * C * C / 3 + 4 * C * dk),
+                      4 * dk * dv + 2 * C * dv + 6 * dk * dv + 3 * C * dv + 2 * C * dk + 2 * C * C / 3 + 4 * C * dk),
         "bwd_gate_sum": (0.0, 0.0),
     }
     return {k: (th * b, th * f) for k, (b, f) in per.items()}
