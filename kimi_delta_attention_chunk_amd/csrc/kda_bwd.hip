@@ -635,6 +635,11 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     Prm p = make_prm(a, L);
     p.hT = nullptr;
     p.o = nullptr;
+    if constexpr (DK == 32 && DV == 64) {
+        // every array the dk = 32 backward reads or writes must be in the workspace layout
+        if (!p.tm || !p.hs || !p.dhs || !p.aqT || !p.pmT || !p.qhT || !p.part_a || !p.part_dt)
+            return hipErrorInvalidValue;
+    }
     if (!(a.flags & (1u << 4))) {  // no forward saved in ws: recompute it
         hipError_t e = launch_recompute(p, a, s);
         if (e != hipSuccess) return e;

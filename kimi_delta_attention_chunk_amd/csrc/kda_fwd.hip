@@ -160,7 +160,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.dA_log = a.dA_log; p.ddt_bias = a.ddt_bias;
     char* base = (char*)a.ws;
     auto at = [&](size_t off) { return off ? (float*)(base + off) : (float*)nullptr; };
-    p.w = (float*)(base + L.w);  // offset 0
+    p.w = at(L.w);
     p.u = at(L.u); p.aqk = at(L.aqk); p.tm = at(L.tm); p.hs = at(L.hs); p.vn = at(L.vn);
     p.qg = at(L.qg); p.khT = at(L.khT); p.gl = at(L.gl);
     p.dhs = at(L.dhs); p.dvn = at(L.dvn);
@@ -177,8 +177,30 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     const size_t slots = (size_t)a.n_chunks_bound * a.H;
     const size_t C = kChunk, dk = a.dk, dv = a.dv;
     auto bytes = [](size_t n) { return (n * sizeof(float) + 255) & ~(size_t)255; };
-    size_t off = 0;
+    // The first 256 bytes stay unused: offset 0 means "array absent" (null pointer
+    // in the kernel parameters), so no array may start there.
+    size_t off = 256;
     auto take = [&](size_t& field, size_t n) { field = off; off += bytes(n ? n : 1); };
+    if (dk == 32 && dv == 64) {
+        // affine chunk form: only what its kernels read
+        take(L.aqk, slots * C * C);  // Aqk k-blocks, read back within the intra-chunk kernel
+        take(L.hs, slots * dk * dv);
+        take(L.pm, slots * dk * dk);
+        take(L.pmT, slots * dk * dk);
+        take(L.hh, slots * dk * dv);
+        take(L.qh, slots * C * dk);
+        take(L.qhT, slots * C * dk);
+        take(L.ol, slots * C * dv);
+        if (backward) {
+            take(L.aqT, slots * C * C);
+            take(L.tm, slots * C * C);
+            take(L.dhs, slots * dk * dv);
+            take(L.part_a, slots);
+            take(L.part_dt, slots * dk);
+        }
+        L.total = off;
+        return L;
+    }
     take(L.w, slots * C * dk);
     take(L.u, slots * C * dv);
     take(L.aqk, slots * C * C);
@@ -187,15 +209,6 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     take(L.qg, slots * C * dk);
     take(L.khT, slots * C * dk);
     take(L.gl, slots * dk);
-    if (dk == 32 && dv == 64) {
-        take(L.pm, slots * dk * dk);
-        take(L.pmT, slots * dk * dk);
-        take(L.hh, slots * dk * dv);
-        take(L.qh, slots * C * dk);
-        take(L.qhT, slots * C * dk);
-        take(L.ol, slots * C * dv);
-        if (backward) take(L.aqT, slots * C * C);
-    }
     if (backward) {
         take(L.tm, slots * C * C);
         take(L.dhs, slots * dk * dv);
@@ -229,6 +242,11 @@ bool dims_supported(int dk, int dv) {
 template <int DK, int DV, typename TIn, typename TOut>
 hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, bool write_o, bool store) {
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
+    if constexpr (DK == 32 && DV == 64) {
+        // every array these kernels write must be in the workspace layout
+        if (!p.aqk || !p.hs || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
+        if (store && (!p.tm || !p.aqT)) return hipErrorInvalidValue;
+    }
     if (a.n_chunks_bound > 0)
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     if constexpr (DK == 32 && DV == 64) {
