@@ -43,7 +43,9 @@ template <int DV, typename TIn, typename TOut, Prec P>
 __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     constexpr int NTH = kBcThreads, NW = kBcWaves;
     constexpr int DK = 32, NVB = DV / 32, LR = DK + 1;  // odd stride: lanes over tokens hit distinct banks
-    constexpr int L40 = 40, L72 = 72, GV = DV / 16;
+    constexpr int GV = DV / 16;
+    using T32 = STile<P, 32>;  // operand tiles of 32 and 64 values per row
+    using T64 = STile<P, 64>;
     constexpr int NT4 = kChunk * kChunk / 4 / NTH;  // float4 of T per thread
     constexpr int NH4 = DK * DV / 4 / NTH;          // float4 of h (and D)
     constexpr int NV4 = kChunk * DV / 4 / NTH;      // float4 of vn (and dvn)
@@ -203,11 +205,11 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         // ph: [0, 4608) T;  [4608, 7168) beta Kg;  [7168, 9728) Kh;  [9728, 12288) h^T;
         //     [12288, 14848) D'^T;  [14848, 19456) dO^T;  then Z^T over [4608, 9216) and
         //     v_new (fp32 [t][68]) over [9728, 14080).  ACC: V, then dv_new (fp32 [t][68]).
-        const Tile<P> TRW(ph, kChunk, L72), BKG(ph + 4608, kChunk, L40), KHt(ph + 7168, kChunk, L40),
-            HTt(ph + 9728, DV, L40), DTt(ph + 12288, DV, L40), DOT(ph + 14848, DV, L72);
+        const T64 TRW(ph, kChunk), DOT(ph + 14848, DV);
+        const T32 BKG(ph + 4608, kChunk), KHt(ph + 7168, kChunk), HTt(ph + 9728, DV), DTt(ph + 12288, DV);
         float* const VS = ACC;  // V, overwritten in place by dv_new
         float* const VNs = ph + 9728;
-        static_assert(14848 + DV * L72 <= PH && 9728 + kChunk * 68 <= 14848 && kChunk * 68 <= 3 * kChunk * LR,
+        static_assert(14848 + DV * 72 <= PH && 9728 + kChunk * 68 <= 14848 && kChunk * 68 <= 3 * kChunk * LR,
                       "P0 staging must fit");
         {
             const float b = bet[tr];
@@ -271,7 +273,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             }
         }
         __syncthreads();  // beta Kg, Kh, h^T, D'^T consumed
-        const Tile<P> ZT(ph + 4608, DV, L72);  // Z^T [j][s]
+        const T64 ZT(ph + 4608, DV);  // Z^T [j][s]
 #pragma unroll
         for (int e = 0; e < 2; ++e) ZT.put4(16 * (tn0 + e) + lr, 16 * tm + 4 * lg, z[e]);
         __syncthreads();
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     }
 
     // ------------------------------------------------ P1: contractions over dv
-    const Tile<P> TT(ph, kChunk, L72);  // T^T [t][s], phases 1-3
+    const T64 TT(ph, kChunk);  // T^T [t][s], phases 1-3
 #pragma unroll
     for (int i = 0; i < NT4; ++i) {
         const int e4 = 4 * (tid + NTH * i);
@@ -315,9 +317,9 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) aAq[i] = aT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        const Tile<P> dOb(ph + 4608, kChunk, L40), vnb(ph + 7168, kChunk, L40), dvnb(ph + 9728, kChunk, L40),
-            bVb(ph + 12288, kChunk, L40), hb(ph + 14848, DK, L40), Db(ph + 16128, DK, L40),
-            dvnT(ph + 17408, 32, L72);
+        const T32 dOb(ph + 4608, kChunk), vnb(ph + 7168, kChunk), dvnb(ph + 9728, kChunk), bVb(ph + 12288, kChunk),
+            hb(ph + 14848, DK), Db(ph + 16128, DK);
+        const T64 dvnT(ph + 17408, 32);
         float* Vf = ph + 19712;  // fp32 v of the column block [t][j], stride 36
         TOut* dvout = (TOut*)p.dv;
 #pragma unroll
@@ -413,7 +415,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 
     // ------------------------------------------------ P2: through w
     {
-        const Tile<P> dwt(ph + 4608, kChunk, L40), bKg(ph + 7168, kChunk, L40), dwT(ph + 9728, DK, L72);
+        const T32 dwt(ph + 4608, kChunk), bKg(ph + 7168, kChunk);
+        const T64 dwT(ph + 9728, DK);
         __syncthreads();  // P1 tiles consumed
         {
             const float b = bet[tr];
@@ -472,7 +475,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ P3: dA = -T^T dT T^T
     f32x4 dAr[2];
     {
-        const Tile<P> Trow(ph + 4608, kChunk, L72), dTt(ph + 9216, kChunk, L72), YT(ph + 13824, kChunk, L72);
+        const T64 Trow(ph + 4608, kChunk), dTt(ph + 9216, kChunk), YT(ph + 13824, kChunk);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
@@ -527,8 +530,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ P4: decayed pair sums
     {
         // row sums: R'k[t] = sum_{s<t} dA[t][s] k_s e^{G_t-G_s},  Rq[t] = sum_{s<=t} dAq[t][s] k_s e^{..}
-        const Tile<P> dAt(ph, kChunk, L72), dAqt(ph + 4608, kChunk, L72);
-        auto KcT = [&](int i) { return Tile<P>(ph + 9216 + 2304 * i, DK, L72); };
+        const T64 dAt(ph, kChunk), dAqt(ph + 4608, kChunk);
+        auto KcT = [&](int i) { return T64(ph + 9216 + 2304 * i, DK); };
         float gref[3][4];
 #pragma unroll
         for (int I = 1; I <= 3; ++I)
@@ -565,7 +568,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             int k0 = 0, k1 = 16 * I;
             widen<P>(k0, k1);
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            const Tile<P> kc = KcT(I - 1);
+            const T64 kc = KcT(I - 1);
             ak = mma_tile(dAt.sub(16 * I), kc.sub(16 * tn), k0, k1, ak);
             aq = mma_tile(dAqt.sub(16 * I), kc.sub(16 * tn), k0, k1, aq);
             const int cc = 16 * tn + frag_col();
@@ -597,9 +600,9 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     }
     {
         // column sums: Ck[s] = sum_{t>s} beta_t dA[t][s] k_t e^{G_t-G_s}, Cq[s] = sum_{t>=s} dAq[t][s] q_t e^{..}
-        const Tile<P> bdAT(ph, kChunk, L72), dAqT(ph + 4608, kChunk, L72);
-        auto KxT = [&](int j) { return Tile<P>(ph + 9216 + 2304 * j, DK, L72); };
-        auto QxT = [&](int j) { return Tile<P>(ph + 16128 + 2304 * j, DK, L72); };
+        const T64 bdAT(ph, kChunk), dAqT(ph + 4608, kChunk);
+        auto KxT = [&](int j) { return T64(ph + 9216 + 2304 * j, DK); };
+        auto QxT = [&](int j) { return T64(ph + 16128 + 2304 * j, DK); };
         float gref[3][4];
 #pragma unroll
         for (int J = 0; J < 3; ++J)

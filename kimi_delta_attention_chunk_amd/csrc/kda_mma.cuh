@@ -290,6 +290,123 @@ __device__ __forceinline__ void store_kblock4<Prec::F32>(void* rowblock, const f
     *(f32x4*)((float*)rowblock + k0) = x;
 }
 
+// ----------------------------------------------------------------- swizzled tiles
+// STile<P, C>: an R x C operand tile (C = 32 or 64 values per row) laid out for
+// the LDS banks of gfx950.  Measured bank behaviour: ds_read_b128 serves a
+// half-wave per pass in two 8-byte halves over 64 banks of 8 bytes; ds_write_b64
+// serves 16 lanes per pass and ds_write_b16 a half-wave, both over 32 banks of
+// 4 bytes.  A padded row stride (C + 8 bf16) makes every fragment read a 2-way
+// conflict and the transposed scalar stores 4- to 8-way ones.  For BF3 the rows
+// are therefore dense (C bf16 each, hi then lo array as in Tile) and the 16-byte
+// group j of row r is stored at group j ^ f(r), with f chosen so that fragment
+// reads, row-wise stores and transposed stores from row-wise or linear thread
+// layouts are all conflict-free (transposed stores from a linear layout keep a
+// 2-way conflict at C = 32).  The F32 layout is the padded one of Tile.
+// sub(r) moves the origin down r rows (the swizzle follows the absolute row).
+template <int C>
+__device__ __forceinline__ int stile_swz(int row) {
+    static_assert(C == 32 || C == 64, "swizzled tiles hold 32 or 64 values per row");
+    if constexpr (C == 64) return ((row >> 1) & 7) ^ ((row >> 4) & 1);
+    else return ((row >> 1) & 2) ^ (((row >> 3) & 1) * 3);
+}
+template <Prec P, int C> struct STile;
+template <int C> struct STile<Prec::F32, C> {
+    static constexpr int ld = C + 8;
+    float* p;
+    __device__ __forceinline__ STile(float* base, int rows) : p(base) { (void)rows; }
+    __device__ __forceinline__ void put(int r, int k, float x) const { p[r * ld + k] = x; }
+    __device__ __forceinline__ void put4(int r, int k, f32x4 x) const { *(f32x4*)(p + r * ld + k) = x; }
+    __device__ __forceinline__ STile sub(int r) const {
+        STile t = *this;
+        t.p += r * ld;
+        return t;
+    }
+    __device__ __forceinline__ Tile<Prec::F32> plain() const { return Tile<Prec::F32>(p, 0, ld); }
+};
+template <int C> struct STile<Prec::BF3, C> {
+    __bf16* hi;
+    __bf16* lo;
+    int r0;
+    __device__ __forceinline__ STile(float* base, int rows) : hi((__bf16*)base), lo((__bf16*)base + rows * C), r0(0) {}
+    // element offset of (row r of the view, value k) in either array
+    __device__ __forceinline__ int at(int r, int k) const {
+        const int row = r0 + r;
+        return row * C + 8 * ((k >> 3) ^ stile_swz<C>(row)) + (k & 7);
+    }
+    __device__ __forceinline__ void put(int r, int k, float x) const {
+        const __bf16 h = (__bf16)x;
+        const int o = at(r, k);
+        hi[o] = h;
+        lo[o] = (__bf16)(x - (float)h);
+    }
+    __device__ __forceinline__ void put4(int r, int k, f32x4 x) const {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 h, l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = (__bf16)x[i];
+            l[i] = (__bf16)(x[i] - (float)h[i]);
+        }
+        const int o = at(r, k);
+        *(bf16x4*)(hi + o) = h;
+        *(bf16x4*)(lo + o) = l;
+    }
+    __device__ __forceinline__ STile sub(int r) const {
+        STile t = *this;
+        t.r0 += r;
+        return t;
+    }
+};
+
+// acc += A(16 x [k0,k1)) * B(16 x [k0,k1))^T on swizzled tiles (origins at their view rows).
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile(const STile<Prec::F32, CA>& A, const STile<Prec::F32, CB>& B, int k0, int k1,
+                                          f32x4 acc) {
+    return mma_tile(A.plain(), B.plain(), k0, k1, acc);
+}
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile(const STile<Prec::BF3, CA>& A, const STile<Prec::BF3, CB>& B, int k0, int k1,
+                                          f32x4 acc) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int ra = A.r0 + r, rb = B.r0 + r;
+    const int fa = stile_swz<CA>(ra), fb = stile_swz<CB>(rb);
+    for (int k = k0; k < k1; k += 32) {
+        const int j = (k >> 3) + g;
+        const int ao = ra * CA + 8 * (j ^ fa), bo = rb * CB + 8 * (j ^ fb);
+        const bf16x8 ah = *(const bf16x8*)(A.hi + ao);
+        const bf16x8 al = *(const bf16x8*)(A.lo + ao);
+        const bf16x8 bh = *(const bf16x8*)(B.hi + bo);
+        const bf16x8 bl = *(const bf16x8*)(B.lo + bo);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    }
+    return acc;
+}
+// A fragment (rows of the view, k-block starting at kb) of a swizzled tile.
+template <int C>
+__device__ __forceinline__ void load_frag(AFrag<Prec::BF3>& f, const STile<Prec::BF3, C>& T, int kb) {
+    const int lane = threadIdx.x & 63;
+    const int o = T.at(lane & 15, kb + 8 * (lane >> 4));
+    f.hi = *(const bf16x8*)(T.hi + o);
+    f.lo = *(const bf16x8*)(T.lo + o);
+}
+template <int C>
+__device__ __forceinline__ void load_frag(AFrag<Prec::F32>& f, const STile<Prec::F32, C>& T, int kb) {
+    load_frag(f, T.plain(), kb);
+}
+template <int C>
+__device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::BF3>& a, const STile<Prec::BF3, C>& B, int kb, f32x4 acc) {
+    AFrag<Prec::BF3> b;
+    load_frag(b, B, kb);
+    return mma_ff(a, b, acc);
+}
+template <int C>
+__device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const STile<Prec::F32, C>& B, int kb, f32x4 acc) {
+    return mma_frag(a, B.plain(), kb, acc);
+}
+
 // Round a k range outward to the step of P (for triangular factors whose
 // entries outside the exact range are zero).
 template <Prec P>
