@@ -99,11 +99,14 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     float* Qb = KQG + kChunk * kLB;
     float* Gb = KQG + 2 * kChunk * kLB;
     float* X = KQG + kCB32 * LA;         // solve scratch (after pass 1)
-    const Tile<P> Kr(S1, 48, LB8);
-    const Tile<P> Qr(S1 + 48 * LB8, 48, LB8);
-    const Tile<P> Kc(S1 + 96 * LB8, 96, LB8);
-    float* A = S1;                        // fp32 Akk, after pass 1
-    const Tile<P> Tt(S1, kChunk, LA);     // T as an MFMA operand, after the solve
+    using T32 = STile<P, 32>;  // operand tiles of 32 and 64 values per row
+    using T64 = STile<P, 64>;
+    static_assert(STile<Prec::F32, 32>::ld == LB8 && STile<Prec::F32, 64>::ld == LA, "tile footprints");
+    const T32 Kr(S1, 48);
+    const T32 Qr(S1 + 48 * LB8, 48);
+    const T32 Kc(S1 + 96 * LB8, 96);
+    float* A = S1;                  // fp32 Akk, after pass 1
+    const T64 Tt(S1, kChunk);       // T as an MFMA operand, after the solve
 
     // w, exp(G) q, (k exp(G_L - G))^T and Aqk go to the workspace in k-block form
     // (kda_mma.cuh) for the sequential kernels of dk <= 64, which load MFMA
@@ -215,23 +218,27 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         // scaled operands for the off-diagonal Gram blocks, exp(G) q, k exp(G_L - G)
         {
             const int I = tr >> 4;
-            float qgv[8], khv[8];
+            float qgv[8], khv[8], kr[8], qr[8], kc[3][8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int cc = 8 * part + i;
                 const float gt = G[b][i];
                 qgv[i] = __expf(gt) * qx[b][i];
                 khv[i] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
-                KhS[cc * kLD + tr] = khv[i];
-                if (I >= 1) {
-                    const float e = __expf(gt - Gb[16 * I * kLB + cc]);
-                    Kr.put(tr - 16, cc, kx[b][i] * e);
-                    Qr.put(tr - 16, cc, qx[b][i] * e);
-                }
+                if constexpr (DK != 32) KhS[cc * kLD + tr] = khv[i];
+                const float e = __expf(gt - Gb[16 * (I >= 1 ? I : 1) * kLB + cc]);
+                kr[i] = kx[b][i] * e;
+                qr[i] = qx[b][i] * e;
 #pragma unroll
-                for (int J = 1; J <= 3; ++J)
-                    if (tr < 16 * J) Kc.put(kc_off(J) + tr, cc, kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt));
+                for (int J = 1; J <= 3; ++J) kc[J - 1][i] = kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt);
             }
+            if (I >= 1) {
+                Kr.put8(tr - 16, 8 * part, kr);
+                Qr.put8(tr - 16, 8 * part, qr);
+            }
+#pragma unroll
+            for (int J = 1; J <= 3; ++J)
+                if (tr < 16 * J) Kc.put8(kc_off(J) + tr, 8 * part, kc[J - 1]);
             if constexpr (DK != 32)  // (dk = 32 keeps the affine form instead)
                 store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
             if constexpr (DK == 32) {
@@ -259,7 +266,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             const int pr = tau % 6, kind = tau / 6;  // kind 0: Akk, 1: Aqk
             int I, J;
             gram_pair(pr, I, J);
-            const Tile<P> Aop = (kind == 0 ? Kr : Qr).sub((I - 1) * 16);
+            const T32 Aop = (kind == 0 ? Kr : Qr).sub((I - 1) * 16);
             gacc[i] = mma_tile(Aop, Kc.sub(kc_off(I) + 16 * J), 0, kCB32, gacc[i]);
         }
         // diagonal blocks, exact pairwise decays: the 4 x 136 pairs s <= t of the
@@ -380,7 +387,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         for (int g = 0; g < GRP; ++g) {
             const int b = b0 + g;
             if (b < NBLK) {
-                const Tile<P> BTg(KQG + g * kCB32 * LA, kCB32, LA);
+                const T64 BTg(KQG + g * kCB32 * LA, kCB32);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     BTg.put(8 * part + i, tr, b < NB ? bt * __expf(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
@@ -396,7 +403,7 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             if (tile >= TPB * nb) break;
             const int g = tile / TPB, tl = tile % TPB, tm = tl >> 1, tn = tl & 1;
             const int b = b0 + g;
-            const Tile<P> BTg(KQG + g * kCB32 * LA, kCB32, LA);
+            const T64 BTg(KQG + g * kCB32 * LA, kCB32);
             int k0 = 0, k1 = 16 * (tm + 1);
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -446,10 +453,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         // qh^T's and qh^T from qh's.  hh and ol are kept in fragment order
         // ([32-column block][16x16 tile][lane][4]) for the state pass to add to its
         // accumulators directly.
-        const Tile<P> WT(KQG, DK, LA), UT(KQG + DK * LA, DV, LA);
+        const T64 WT(KQG, DK), UT(KQG + DK * LA, DV);
         static_assert(DK * LA + DV * LA <= 3 * kChunk * kLB, "w^T and u^T must fit in KQG");
         float* Qgs = S1;  // exp(G) q, fp32 [t][c], stride kLB
-        const Tile<P> KHT(S1 + kChunk * kLB, DK, LA);  // Kh^T [c][t]
+        const T64 KHT(S1 + kChunk * kLB, DK);  // Kh^T [c][t]
         static_assert(kChunk * kLB + DK * LA <= S1F, "Qg and Kh^T must fit in S1");
 #pragma unroll
         for (int i = 0; i < 8; ++i) KHT.put(8 * part + i, tr, khs[i]);

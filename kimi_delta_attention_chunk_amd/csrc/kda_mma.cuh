@@ -316,6 +316,11 @@ template <int C> struct STile<Prec::F32, C> {
     __device__ __forceinline__ STile(float* base, int rows) : p(base) { (void)rows; }
     __device__ __forceinline__ void put(int r, int k, float x) const { p[r * ld + k] = x; }
     __device__ __forceinline__ void put4(int r, int k, f32x4 x) const { *(f32x4*)(p + r * ld + k) = x; }
+    // eight consecutive values (k a multiple of 8)
+    __device__ __forceinline__ void put8(int r, int k, const float (&x)[8]) const {
+        *(f32x4*)(p + r * ld + k) = f32x4{x[0], x[1], x[2], x[3]};
+        *(f32x4*)(p + r * ld + k + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;
         t.p += r * ld;
@@ -350,6 +355,18 @@ template <int C> struct STile<Prec::BF3, C> {
         const int o = at(r, k);
         *(bf16x4*)(hi + o) = h;
         *(bf16x4*)(lo + o) = l;
+    }
+    // eight consecutive values (k a multiple of 8): one 16-byte group of each array
+    __device__ __forceinline__ void put8(int r, int k, const float (&x)[8]) const {
+        bf16x8 h, l;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            h[i] = (__bf16)x[i];
+            l[i] = (__bf16)(x[i] - (float)h[i]);
+        }
+        const int o = at(r, k);
+        *(bf16x8*)(hi + o) = h;
+        *(bf16x8*)(lo + o) = l;
     }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;

@@ -56,7 +56,8 @@ template <typename TOut, Prec P, int BV>
 __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_wg, int write_o, int store_states) {
     constexpr int DK = kPsDK, DV = kPsDV, LK = DK + 8, NV = DV / BV, NJ = BV / 16, NST = 2 * NJ;
     __shared__ __attribute__((aligned(16))) float sH[2][BV * LK];
-    const Tile<P> HT[2] = {Tile<P>(sH[0], BV, LK), Tile<P>(sH[1], BV, LK)};
+    static_assert(STile<Prec::F32, DK>::ld == LK, "tile footprint");
+    const STile<P, DK> HT[2] = {STile<P, DK>(sH[0], BV), STile<P, DK>(sH[1], BV)};
 
     const int lid = xcd_local_id(blockIdx.x, total_wg);
     const int jbk = lid % NV, nh = lid / NV;
@@ -176,8 +177,9 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
     constexpr int DK = kPsDK, DV = kPsDV, LK = DK + 8, LA = kChunk + 8, NV = DV / BV, NJ = BV / 16, NST = 2 * NJ;
     __shared__ __attribute__((aligned(16))) float sD[2][BV * LK];
     __shared__ __attribute__((aligned(16))) float sO[2][BV * LA];
-    const Tile<P> DT[2] = {Tile<P>(sD[0], BV, LK), Tile<P>(sD[1], BV, LK)};
-    const Tile<P> OT[2] = {Tile<P>(sO[0], BV, LA), Tile<P>(sO[1], BV, LA)};
+    static_assert(STile<Prec::F32, DK>::ld == LK && STile<Prec::F32, kChunk>::ld == LA, "tile footprints");
+    const STile<P, DK> DT[2] = {STile<P, DK>(sD[0], BV), STile<P, DK>(sD[1], BV)};
+    const STile<P, kChunk> OT[2] = {STile<P, kChunk>(sO[0], BV), STile<P, kChunk>(sO[1], BV)};
 
     const int lid = xcd_local_id(blockIdx.x, total_wg);
     const int jbk = lid % NV, nh = lid / NV;
