@@ -64,6 +64,9 @@ struct Prm {
     // the backward D = P^T D' + qh^T dO (k-block or fragment-order arrays, see
     // the intra-chunk kernel); aqT = Aqk^T for the backward chunk kernel
     float *pm, *pmT, *hh, *qh, *qhT, *ol, *aqT;
+    // the workspace's first 256 bytes, never read: lanes whose store is masked
+    // out write here instead, so a store is issued on every path
+    float* sink;
 };
 
 __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {

@@ -169,6 +169,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.dkt = at(L.dkt); p.dxq = at(L.dxq); p.dxk = at(L.dxk); p.part_a = at(L.part_a); p.part_dt = at(L.part_dt);
     p.pm = at(L.pm); p.pmT = at(L.pmT); p.hh = at(L.hh); p.qh = at(L.qh); p.qhT = at(L.qhT); p.ol = at(L.ol);
     p.aqT = at(L.aqT);
+    p.sink = (float*)base;
     return p;
 }
 
@@ -251,8 +252,14 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     if constexpr (DK == 32 && DV == 64) {
         const int total = a.N * a.H * (DV / kPsBV);
-        KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV>), dim3(total), dim3(kPsThreads), s, p, total,
-                   write_o ? 1 : 0, store ? 1 : 0);
+        if (write_o && store)
+            KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV, true, true>), dim3(total), dim3(kPsThreads), s, p, total);
+        else if (write_o)
+            KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV, true, false>), dim3(total), dim3(kPsThreads), s, p, total);
+        else if (store)
+            KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV, false, true>), dim3(total), dim3(kPsThreads), s, p, total);
+        else
+            KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV, false, false>), dim3(total), dim3(kPsThreads), s, p, total);
     } else if constexpr (DK <= 64) {
         const int total = a.N * a.H * (DV / 32);
         KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, TOut, P>), dim3(total), dim3(kScanThreads), s, p, total,

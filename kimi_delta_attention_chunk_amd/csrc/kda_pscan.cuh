@@ -14,7 +14,7 @@
 // registers by waves 0 .. 2 BV / 16 - 1, and wave w forms output rows
 // 16 w .. 16 w + 15.  The state is copied each chunk into a double-buffered LDS
 // tile h^T[j][c], the B operand of every product of the chunk; everything else
-// comes from memory as register fragments, prefetched two chunks ahead.  With
+// comes from memory as register fragments, prefetched four chunks ahead.  With
 // BV = 16 each (sequence, head) runs as four independent chains, which keeps
 // more operand loads in flight per CU than two chains of 32 columns.
 #pragma once
@@ -52,8 +52,12 @@ __device__ __forceinline__ void ps_fwd_load(const Prm& p, size_t slot, int jb, i
     for (int j = 0; j < NJ; ++j) R.ol[j] = *(const f32x4*)(p.ol + slot * kChunk * kPsDV + frag_order(jb + 16 * j, 8, wave));
 }
 
-template <typename TOut, Prec P, int BV>
-__global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_wg, int write_o, int store_states) {
+// WO: write o; SS: store the state entering every chunk (for the backward).
+// Both are compile-time, and every store of the loop body is issued on every
+// path (masked lanes write to p.sink), so the compiler's waits on the memory
+// counter count exactly the operand batches in flight.
+template <typename TOut, Prec P, int BV, bool WO, bool SS>
+__global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_wg) {
     constexpr int DK = kPsDK, DV = kPsDV, LK = DK + 8, NV = DV / BV, NJ = BV / 16, NST = 2 * NJ;
     __shared__ __attribute__((aligned(16))) float sH[2][BV * LK];
     static_assert(STile<Prec::F32, DK>::ld == LK, "tile footprint");
@@ -65,7 +69,7 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
     if (n >= p.N) return;
     const int jb = jbk * BV;
     const int wave = wave_id(), lr = threadIdx.x & 15;
-    const bool owner = wave < NST;  // holds a state tile
+    const bool owner = NST == kPsThreads / 64 || wave < NST;  // holds a state tile
     const int sw = owner ? wave : 0;
     const int tc = sw / NJ, tj = sw % NJ;  // state tile (waves past NST mirror wave 0's loads, unused)
     const int crow = 16 * tc + frag_row(0), jcol = 16 * tj + lr;
@@ -89,13 +93,14 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
     // (read after the next barrier) and its store -- then the chunk's output,
     // which only reads `buf`.  Both buffers were last read before this step's
     // barrier, so one barrier per chunk suffices.
-    auto put_state = [&](int c, int buf) {
+    // (`valid` false: past the sequence end, the store goes to p.sink)
+    auto put_state = [&](int c, int buf, bool valid) {
         if (owner) {
             HT[buf].put4(jcol, crow, S);
-            if (store_states) {
+            if constexpr (SS) {
                 float* hs = p.hs + ((size_t)c * p.H + h) * DK * DV;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) hs[(size_t)(crow + r) * DV + jb + jcol] = S[r];
+                for (int r = 0; r < 4; ++r) *(valid ? hs + (size_t)(crow + r) * DV + jb + jcol : p.sink) = S[r];
             }
         }
     };
@@ -107,8 +112,8 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
             load_frag(fb, HT[buf].sub(16 * tj), 0);
             S = mma_ff(Rc.pm, fb, Rc.hh);
         }
-        if (c + 1 < c1) put_state(c + 1, buf ^ 1);
-        if (write_o) {
+        put_state(c + 1, buf ^ 1, c + 1 < c1);
+        if constexpr (WO) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 AFrag<P> fo;
@@ -117,27 +122,33 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * wave + frag_row(r);
-                    if (t < cr.len) Elem<TOut>::store(o, tok_index(cr.t0 + t, h, p.H, DV) + jb + 16 * j + lr, acc[r]);
+                    TOut* dst = t < cr.len ? o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 16 * j + lr : (TOut*)p.sink;
+                    Elem<TOut>::store(dst, 0, acc[r]);
                 }
             }
         }
     };
     if (c0 < c1) {
-        PsFwdOps<P, NJ> R[2];
-        ps_fwd_load<P, NJ>(p, slot_of(c0), jb, tc, tj, R[0]);
-        ps_fwd_load<P, NJ>(p, slot_of(c0 + 1), jb, tc, tj, R[1]);
-        put_state(c0, 0);
-        // Pairs of chunks with no branch inside the loop body: every path to the
-        // loop latch issues both prefetch batches, so each wait covers one batch
-        // (a skippable second half would make the waits drain the prefetch).
+        // PD chunks' operands in flight.  The loop body has no branch: every path
+        // to the latch issues the same loads and stores, so each wait on the
+        // memory counter covers one chunk's batch (a skippable part would make
+        // the waits drain the prefetch).
+        constexpr int PD = 4;
+        PsFwdOps<P, NJ> R[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) ps_fwd_load<P, NJ>(p, slot_of(c0 + i), jb, tc, tj, R[i]);
+        put_state(c0, 0, true);
         int c = c0;
-        for (; c + 1 < c1; c += 2) {
-            step(c, 0, R[0]);
-            ps_fwd_load<P, NJ>(p, slot_of(c + 2), jb, tc, tj, R[0]);
-            step(c + 1, 1, R[1]);
-            ps_fwd_load<P, NJ>(p, slot_of(c + 3), jb, tc, tj, R[1]);
+        for (; c + PD - 1 < c1; c += PD) {
+#pragma unroll
+            for (int i = 0; i < PD; ++i) {
+                step(c + i, i & 1, R[i]);
+                ps_fwd_load<P, NJ>(p, slot_of(c + PD + i), jb, tc, tj, R[i]);
+            }
         }
-        if (c < c1) step(c, 0, R[0]);
+#pragma unroll
+        for (int i = 0; i < PD - 1; ++i)
+            if (c + i < c1) step(c + i, i & 1, R[i]);
     }
     if (owner && p.hT) {
 #pragma unroll
@@ -146,27 +157,39 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
 }
 
 // ============================================================== reverse pass
-template <Prec P, int BV>
+template <typename TIn, Prec P, int BV>
 struct PsBwdOps {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    static constexpr int NW4 = BV / 4 * (int)sizeof(TIn) / 16;  // 16-byte words of dO per thread
     AFrag<P> pt, qt[2];  // rows of P^T and of qh^T (this wave's state tile rows)
-    float d[BV / 4];     // dO[t][jb + (BV / 4) part ..], t = tid >> 2
+    // dO[t][jb + (BV / 4) part ..], t = tid >> 2, as loaded: converted to fp32
+    // where it is used, so that nothing waits for the load before then
+    u32x4 d[NW4];
+    __device__ __forceinline__ float at(int i) const {
+        if constexpr (sizeof(TIn) == 2) {
+            const uint32_t w = d[i >> 3][(i >> 1) & 3];
+            return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            return __uint_as_float(d[i >> 2][i & 3]);
+        }
+    }
 };
 
 template <typename TIn, Prec P, int BV>
 __device__ __forceinline__ void ps_bwd_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb, int tc,
-                                            PsBwdOps<P, BV>& R) {
+                                            PsBwdOps<TIn, P, BV>& R) {
     const int lr = threadIdx.x & 15;
     load_afrag(R.pt, (const char*)(p.pmT + slot * kPsDK * kPsDK) + (size_t)(16 * tc + lr) * kKBlockBytes);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
         load_afrag(R.qt[kb], (const char*)(p.qhT + slot * kChunk * kPsDK) + (size_t)((16 * tc + lr) * 2 + kb) * kKBlockBytes);
-    // rows past the chunk end read row 0 (always valid) and are zeroed
+    // rows past the chunk end read row 0 (always valid); they are zeroed where used
     const int t = threadIdx.x >> 2, part = threadIdx.x & 3;
     const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, kPsDV) + jb + (BV / 4) * part;
-    if constexpr (BV == 32) load8<TIn>(src, R.d);
-    else load4<TIn>(src, R.d);
+    static_assert(PsBwdOps<TIn, P, BV>::NW4 >= 1, "whole 16-byte words of dO per thread");
 #pragma unroll
-    for (int i = 0; i < BV / 4; ++i) R.d[i] = t < cr.len ? R.d[i] : 0.f;
+    for (int i = 0; i < PsBwdOps<TIn, P, BV>::NW4; ++i)
+        R.d[i] = ((const typename PsBwdOps<TIn, P, BV>::u32x4*)src)[i];
 }
 
 // Chunks in reverse: store D' (dL/dh at the chunk end) for the chunk kernels,
@@ -187,7 +210,7 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
     if (n >= p.N) return;
     const int jb = jbk * BV;
     const int wave = wave_id(), lr = threadIdx.x & 15;
-    const bool owner = wave < NST;
+    const bool owner = NST == kPsThreads / 64 || wave < NST;
     const int sw = owner ? wave : 0;
     const int tc = sw / NJ, tj = sw % NJ;
     const int crow = 16 * tc + frag_row(0), jcol = 16 * tj + lr;
@@ -207,8 +230,9 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
     auto cref = [&](int cc) { return SeqLayout::chunk_of(n, (cc >= c0 ? cc : c0) - c0, s0, slen); };
     auto slot_of = [&](int cc) { return (size_t)(cc >= c0 ? cc : c0) * p.H + h; };
 
-    auto step = [&](int c, int buf, const PsBwdOps<P, BV>& Rc) {
+    auto step = [&](int c, int buf, const PsBwdOps<TIn, P, BV>& Rc) {
         const size_t slot = (size_t)c * p.H + h;
+        const int len = cref(c).len;
         if (owner) {
             float* dhs = p.dhs + slot * DK * DV;
 #pragma unroll
@@ -216,7 +240,7 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
             DT[buf].put4(jcol, crow, D);
         }
 #pragma unroll
-        for (int i = 0; i < BV / 4; ++i) OT[buf].put((BV / 4) * part + i, tt, Rc.d[i]);
+        for (int i = 0; i < BV / 4; ++i) OT[buf].put((BV / 4) * part + i, tt, tt < len ? Rc.at(i) : 0.f);
         __syncthreads();  // D'^T and dO^T of this chunk complete (the other buffers were read a chunk ago)
         if (owner) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -231,17 +255,21 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
         }
     };
     if (c0 < c1) {
-        PsBwdOps<P, BV> R[2];
-        ps_bwd_load<TIn, P, BV>(p, slot_of(c1 - 1), cref(c1 - 1), h, jb, tc, R[0]);
-        ps_bwd_load<TIn, P, BV>(p, slot_of(c1 - 2), cref(c1 - 2), h, jb, tc, R[1]);
+        constexpr int PD = 4;  // chunks of operands in flight (branch-free body, as in the forward pass)
+        PsBwdOps<TIn, P, BV> R[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) ps_bwd_load<TIn, P, BV>(p, slot_of(c1 - 1 - i), cref(c1 - 1 - i), h, jb, tc, R[i]);
         int c = c1 - 1;
-        for (; c - 1 >= c0; c -= 2) {  // (no branch in the body, as in the forward pass)
-            step(c, 0, R[0]);
-            ps_bwd_load<TIn, P, BV>(p, slot_of(c - 2), cref(c - 2), h, jb, tc, R[0]);
-            step(c - 1, 1, R[1]);
-            ps_bwd_load<TIn, P, BV>(p, slot_of(c - 3), cref(c - 3), h, jb, tc, R[1]);
+        for (; c - (PD - 1) >= c0; c -= PD) {
+#pragma unroll
+            for (int i = 0; i < PD; ++i) {
+                step(c - i, i & 1, R[i]);
+                ps_bwd_load<TIn, P, BV>(p, slot_of(c - PD - i), cref(c - PD - i), h, jb, tc, R[i]);
+            }
         }
-        if (c >= c0) step(c, 0, R[0]);
+#pragma unroll
+        for (int i = 0; i < PD - 1; ++i)
+            if (c - i >= c0) step(c - i, i & 1, R[i]);
     }
     if (owner && p.dh0) {
 #pragma unroll
