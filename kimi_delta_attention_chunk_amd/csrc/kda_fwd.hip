@@ -178,13 +178,13 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     const size_t slots = (size_t)a.n_chunks_bound * a.H;
     const size_t C = kChunk, dk = a.dk, dv = a.dv;
     auto bytes = [](size_t n) { return (n * sizeof(float) + 255) & ~(size_t)255; };
-    // The first 256 bytes stay unused: offset 0 means "array absent" (null pointer
-    // in the kernel parameters), so no array may start there.
+    // The first 256 bytes hold no array: offset 0 means "array absent" (null
+    // pointer in the kernel parameters), and masked-out lanes of branch-free
+    // stores write there (Prm::sink).
     size_t off = 256;
     auto take = [&](size_t& field, size_t n) { field = off; off += bytes(n ? n : 1); };
     if (dk == 32 && dv == 64) {
         // affine chunk form: only what its kernels read
-        take(L.aqk, slots * C * C);  // Aqk k-blocks, read back within the intra-chunk kernel
         take(L.hs, slots * dk * dv);
         take(L.pm, slots * dk * dk);
         take(L.pmT, slots * dk * dk);
@@ -245,7 +245,7 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     if constexpr (DK == 32 && DV == 64) {
         // every array these kernels write must be in the workspace layout
-        if (!p.aqk || !p.hs || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
+        if (!p.hs || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
         if (store && (!p.tm || !p.aqT)) return hipErrorInvalidValue;
     }
     if (a.n_chunks_bound > 0)

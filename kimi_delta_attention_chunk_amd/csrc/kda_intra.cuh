@@ -18,7 +18,9 @@
 //     32-column block of v), as MFMA products.
 // Outputs (fp32 workspace, slot = chunk * H + head): w [64][DK], u [64][DV],
 // qg = exp(G) q^ [64][DK], khT = (k^ exp(G_L - G))^T [DK][64], gl = exp(G_L)
-// [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested.
+// [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested;
+// for dk = 32 instead the affine form of the chunk (pass 3), Aqk^T and T for
+// the backward if requested.
 #pragma once
 
 #include "kda_chunk.cuh"
@@ -327,17 +329,38 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         }
     }
     __syncthreads();
+    // dk = 32: the Aqk rows of this wave's 16 output rows of pass 3 (k-blocks
+    // 0 .. w >> 1, zero above the diagonal), kept as register fragments through
+    // the solve and pass 2
+    AFrag<P> fQ[2];
+    const int nq = (wave >> 1) + 1;  // Aqk row block w reaches s < 16 (w + 1): k-blocks 0 .. w >> 1
+    if constexpr (DK == 32) {
+        const int r = 16 * wave + (threadIdx.x & 15), s8 = 8 * ((threadIdx.x & 63) >> 4);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            if (kb < nq) {
+                float x[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int s = 32 * kb + s8 + m;
+                    x[m] = s > r ? 0.f : AqL[r * LA + s];
+                }
+                make_frag(fQ[kb], x);
+            }
+    }
     {
-        // Aqk to the workspace in k-block form, zero above the diagonal: 8 entries per thread and pass
-        char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
+        if constexpr (DK != 32) {
+            // Aqk to the workspace in k-block form, zero above the diagonal: 8 entries per thread and pass
+            char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
 #pragma unroll
-        for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
-            const int q8 = threadIdx.x + kThreads * i;
-            const int t = q8 >> 3, s0 = 8 * (q8 & 7);
-            float x[8];
+            for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
+                const int q8 = threadIdx.x + kThreads * i;
+                const int t = q8 >> 3, s0 = 8 * (q8 & 7);
+                float x[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
-            store_kblock8<WP>(aq + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, x, (s0 >> 3) & 3);
+                for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
+                store_kblock8<WP>(aq + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, x, (s0 >> 3) & 3);
+            }
         }
         if (p.aqT) {
             // Aqk^T (row s, indices t; zero for t < s) for the backward
@@ -353,9 +376,6 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             }
         }
     }
-    // Aqk is read back by every wave in pass 3: release it to the workgroup
-    // before the solve's barriers.
-    __threadfence_block();
     solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
     if (p.tm) {
         f32x4* to = (f32x4*)(p.tm + slot * kChunk * kChunk);
@@ -446,8 +466,8 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
         //   qh  = scale (Qg - Aqk w)          (64 x 32)   o      = ol + qh h
         //   ol  = scale Aqk u                 (64 x 64)
         // and for the reverse pass D = P^T D' + qh^T dO.  w^T and u^T are staged in
-        // LDS from this wave's pass-2 tiles and Kh^T from the pass-1 registers; Aqk
-        // is read back as register fragments from its k-block array written above.  A D fragment holds four
+        // LDS from this wave's pass-2 tiles and Kh^T from the pass-1 registers; the
+        // Aqk fragments were taken from LDS before the solve.  A D fragment holds four
         // consecutive rows of one column, so each k-block array is written from the
         // product of its transpose: P from P^T's tiles and P^T from P's, qh from
         // qh^T's and qh^T from qh's.  hh and ol are kept in fragment order
@@ -477,19 +497,14 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 for (int i = 0; i < 8; ++i) glS[8 * part + i] = __expf(G[0][i]);
             }
         }
-        const char* aqb = (const char*)(p.aqk + slot * kChunk * kChunk);  // [t][2]
         const int lr = threadIdx.x & 15, lg = (threadIdx.x & 63) >> 4;
         const float scale = p.scale;
-        // Each wave reads all of Kh^T (two row tiles, two k-blocks; from LDS) and
-        // the Aqk rows of its own 16 output rows (from the k-block array) once, as
-        // register fragments, then forms:
+        // Each wave reads all of Kh^T (two row tiles, two k-blocks; from LDS) once
+        // as register fragments and, with the Aqk fragments of its own 16 output
+        // rows (fQ, taken before the solve), forms:
         //   wave 0: P;  wave 1: P^T;  waves 2, 3: hh rows 16 (w - 2) ..
         //   all:    qh, qh^T and ol for rows (columns of qh^T) 16 w .. 16 w + 15.
-        AFrag<P> fK[2][2], fQ[2];
-        const int nq = (wave >> 1) + 1;  // Aqk row block w reaches s < 16 (w + 1): k-blocks 0 .. w >> 1
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            if (kb < nq) load_afrag(fQ[kb], aqb + (size_t)((16 * wave + lr) * 2 + kb) * kKBlockBytes);
+        AFrag<P> fK[2][2];
         __syncthreads();
 #pragma unroll
         for (int ta = 0; ta < 2; ++ta)

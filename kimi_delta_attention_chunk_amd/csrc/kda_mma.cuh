@@ -164,6 +164,20 @@ __device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const Tile<
     return acc;
 }
 
+// A fragment from this lane's 8 values (indices 8 g .. 8 g + 7 of the k-block,
+// g = lane >> 4), split as a store to and load from k-block form would.
+__device__ __forceinline__ void make_frag(AFrag<Prec::BF3>& f, const float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f.hi[i] = (__bf16)x[i];
+        f.lo[i] = (__bf16)(x[i] - (float)f.hi[i]);
+    }
+}
+__device__ __forceinline__ void make_frag(AFrag<Prec::F32>& f, const float (&x)[8]) {
+    f.a = f32x4{x[0], x[1], x[2], x[3]};
+    f.b = f32x4{x[4], x[5], x[6], x[7]};
+}
+
 // Write 8 consecutive values (indices 8 w .. 8 w + 7 of a k-block, w = which)
 // of one row in k-block form.
 template <Prec P>
