@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             for (int vb = 0; vb < NVB; ++vb) {
                 *(f32x4*)&VS[tr * 68 + 32 * vb + 4 * part] = f32x4{vx[vb][0], vx[vb][1], vx[vb][2], vx[vb][3]};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) DOT.put(32 * vb + 4 * part + m, tr, dox[vb][m]);
+                for (int m = 0; m < 4; ++m) DOT.put_hi(32 * vb + 4 * part + m, tr, dox[vb][m]);  // dO: bf16 numbers
             }
         }
 #pragma unroll
@@ -261,8 +261,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb >= (tm >> 1)) {
-                    load_frag(fy, DOT.sub(16 * tn), 32 * kb);
-                    x2 = mma_ff(fa[kb], fy, x2);
+                    load_frag_hi(fy, DOT.sub(16 * tn), 32 * kb);
+                    x2 = mma_ff_bh(fa[kb], fy, x2);
                 }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             __syncthreads();  // previous block's tiles consumed
             {
                 const float b = bet[tr];
-                dOb.put4(tr, 4 * part, f32x4{dox[vbk][0], dox[vbk][1], dox[vbk][2], dox[vbk][3]});
+                dOb.put4_hi(tr, 4 * part, f32x4{dox[vbk][0], dox[vbk][1], dox[vbk][2], dox[vbk][3]});  // bf16 numbers
                 bVb.put4(tr, 4 * part, f32x4{b * vx[vbk][0], b * vx[vbk][1], b * vx[vbk][2], b * vx[vbk][3]});
                 *(f32x4*)&Vf[tr * 36 + 4 * part] = f32x4{vx[vbk][0], vx[vbk][1], vx[vbk][2], vx[vbk][3]};
             }
@@ -353,14 +353,31 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 }
             }
             __syncthreads();
-            aQ = mma_tile(dOb.sub(16 * am), hb.sub(16 * an), 0, 32, aQ);
-            aKh = mma_tile(vnb.sub(16 * am), Db.sub(16 * an), 0, 32, aKh);
-            aW = mma_tile(dvnb.sub(16 * am), hb.sub(16 * an), 0, 32, aW);
+            // one k-block each; fragments shared by two products are read once
+            {
+                AFrag<P> fh, fa, fb;
+                load_frag(fh, hb.sub(16 * an), 0);
+                load_frag_hi(fa, dOb.sub(16 * am), 0);
+                aQ = mma_ff_ah(fa, fh, aQ);
+                load_frag(fa, dvnb.sub(16 * am), 0);
+                aW = mma_ff(fa, fh, aW);
+                load_frag(fa, vnb.sub(16 * am), 0);
+                load_frag(fb, Db.sub(16 * an), 0);
+                aKh = mma_ff(fa, fb, aKh);
+            }
+            {
+                const int tn = wave & 3;  // both tiles w, w + 8 of the 64 x 64 results share the column tile
+                AFrag<P> fv, fbv, fa;
+                load_frag(fv, vnb.sub(16 * tn), 0);
+                load_frag(fbv, bVb.sub(16 * tn), 0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
-                aAq[i] = mma_tile(dOb.sub(16 * tm), vnb.sub(16 * tn), 0, 32, aAq[i]);
-                aT[i] = mma_tile(dvnb.sub(16 * tm), bVb.sub(16 * tn), 0, 32, aT[i]);
+                for (int i = 0; i < 2; ++i) {
+                    const int tm = (wave + NW * i) >> 2;
+                    load_frag_hi(fa, dOb.sub(16 * tm), 0);
+                    aAq[i] = mma_ff_ah(fa, fv, aAq[i]);
+                    load_frag(fa, dvnb.sub(16 * tm), 0);
+                    aT[i] = mma_ff(fa, fbv, aT[i]);
+                }
             }
             // X_u = T^T dvn: dV = beta X_u, dbeta_v = rowsum(X_u V)
             {

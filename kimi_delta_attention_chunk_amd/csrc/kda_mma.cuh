@@ -335,6 +335,9 @@ template <int C> struct STile<Prec::F32, C> {
         *(f32x4*)(p + r * ld + k) = f32x4{x[0], x[1], x[2], x[3]};
         *(f32x4*)(p + r * ld + k + 4) = f32x4{x[4], x[5], x[6], x[7]};
     }
+    // (the _hi forms are for values that are bf16 numbers; in fp32 tiles they are the plain ones)
+    __device__ __forceinline__ void put_hi(int r, int k, float x) const { put(r, k, x); }
+    __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const { put4(r, k, x); }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;
         t.p += r * ld;
@@ -369,6 +372,16 @@ template <int C> struct STile<Prec::BF3, C> {
         const int o = at(r, k);
         *(bf16x4*)(hi + o) = h;
         *(bf16x4*)(lo + o) = l;
+    }
+    // Values that are bf16 numbers (bf16 inputs): the lo part is zero and is
+    // neither stored nor read (load_frag_hi, mma_ff_ah / mma_ff_bh).
+    __device__ __forceinline__ void put_hi(int r, int k, float x) const { hi[at(r, k)] = (__bf16)x; }
+    __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (__bf16)x[i];
+        *(bf16x4*)(hi + at(r, k)) = h;
     }
     // eight consecutive values (k a multiple of 8): one 16-byte group of each array
     __device__ __forceinline__ void put8(int r, int k, const float (&x)[8]) const {
@@ -436,6 +449,37 @@ __device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::BF3>& a, const STile
 template <int C>
 __device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const STile<Prec::F32, C>& B, int kb, f32x4 acc) {
     return mma_frag(a, B.plain(), kb, acc);
+}
+
+// Fragments of operands whose values are bf16 numbers (stored with put_hi /
+// put4_hi): only the hi part is read, and the product with the other operand's
+// split skips the term that would multiply a zero lo part.
+template <int C>
+__device__ __forceinline__ void load_frag_hi(AFrag<Prec::BF3>& f, const STile<Prec::BF3, C>& T, int kb) {
+    const int lane = threadIdx.x & 63;
+    f.hi = *(const bf16x8*)(T.hi + T.at(lane & 15, kb + 8 * (lane >> 4)));
+}
+template <int C>
+__device__ __forceinline__ void load_frag_hi(AFrag<Prec::F32>& f, const STile<Prec::F32, C>& T, int kb) {
+    load_frag(f, T, kb);
+}
+// acc += A B^T, A's values bf16 numbers
+__device__ __forceinline__ f32x4 mma_ff_ah(const AFrag<Prec::BF3>& a, const AFrag<Prec::BF3>& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 mma_ff_ah(const AFrag<Prec::F32>& a, const AFrag<Prec::F32>& b, f32x4 acc) {
+    return mma_ff(a, b, acc);
+}
+// acc += A B^T, B's values bf16 numbers
+__device__ __forceinline__ f32x4 mma_ff_bh(const AFrag<Prec::BF3>& a, const AFrag<Prec::BF3>& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 mma_ff_bh(const AFrag<Prec::F32>& a, const AFrag<Prec::F32>& b, f32x4 acc) {
+    return mma_ff(a, b, acc);
 }
 
 // Round a k range outward to the step of P (for triangular factors whose
