@@ -246,17 +246,18 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
         f32x4 z[2];
+        AFrag<P> fbk, fkh;  // this wave's rows of beta Kg and Kh, shared by both column tiles
+        load_frag(fbk, BKG.sub(16 * tm), 0);
+        load_frag(fkh, KHt.sub(16 * tm), 0);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int tn = tn0 + e;
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            AFrag<P> fx, fy;
-            load_frag(fx, BKG.sub(16 * tm), 0);
+            AFrag<P> fy;
             load_frag(fy, HTt.sub(16 * tn), 0);
-            const f32x4 y = mma_ff(fx, fy, zero);
-            load_frag(fx, KHt.sub(16 * tm), 0);
+            const f32x4 y = mma_ff(fbk, fy, zero);
             load_frag(fy, DTt.sub(16 * tn), 0);
-            const f32x4 x1 = mma_ff(fx, fy, zero);
+            const f32x4 x1 = mma_ff(fkh, fy, zero);
             f32x4 x2 = zero;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -277,20 +278,24 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) ZT.put4(16 * (tn0 + e) + lr, 16 * tm + 4 * lg, z[e]);
         __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int tn = tn0 + e;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            AFrag<P> fx, fy;
+        {
+            AFrag<P> ft[2], fy;  // this wave's rows of T (lower triangular: k-blocks 0 .. tm >> 1)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                if (kb <= (tm >> 1)) {  // T is lower triangular
-                    load_frag(fx, TRW.sub(16 * tm), 32 * kb);
-                    load_frag(fy, ZT.sub(16 * tn), 32 * kb);
-                    acc = mma_ff(fx, fy, acc);
-                }
+                if (kb <= (tm >> 1)) load_frag(ft[kb], TRW.sub(16 * tm), 32 * kb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) VNs[(16 * tm + 4 * lg + r) * 68 + 16 * tn + lr] = acc[r];
+            for (int e = 0; e < 2; ++e) {
+                const int tn = tn0 + e;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb <= (tm >> 1)) {
+                        load_frag(fy, ZT.sub(16 * tn), 32 * kb);
+                        acc = mma_ff(ft[kb], fy, acc);
+                    }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) VNs[(16 * tm + 4 * lg + r) * 68 + 16 * tn + lr] = acc[r];
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -454,10 +459,14 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
         // dT = dT_v + dw (beta Kg)^T   (dT_v already carries beta_s: it was formed with beta V)
+        {
+            AFrag<P> fb, fa;  // both tiles w, w + 8 share the column tile w & 3
+            load_frag(fb, bKg.sub(16 * (wave & 3)), 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
-            aT[i] = mma_tile(dwt.sub(16 * tm), bKg.sub(16 * tn), 0, DK, aT[i]);
+            for (int i = 0; i < 2; ++i) {
+                load_frag(fa, dwt.sub(16 * ((wave + NW * i) >> 2)), 0);
+                aT[i] = mma_ff(fa, fb, aT[i]);
+            }
         }
         // X_w = T^T dw: dKg = beta X_w, dbeta_w = rowsum(X_w Kg)
         {
@@ -506,30 +515,52 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             for (int r = 0; r < 4; ++r) dTt.put(16 * tm + frag_row(r), 16 * tn + frag_col(), aT[i][r]);
         }
         __syncthreads();
-        // Y = dT T^T, stored transposed: YT[b][t]
+        // Y = dT T^T, stored transposed: YT[b][t].  This wave's tiles w, w + 8 share
+        // the column tile tn = w & 3, whose T rows are zero past index 16 tn + 15.
+        const int tn = wave & 3, nkb = (16 * tn + 47) / 32;  // k-blocks of T rows tn that can be nonzero
+        {
+            AFrag<P> fb[2], fa;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
-            int k0 = 0, k1 = 16 * (tn + 1);
-            widen<P>(k0, k1);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_tile(dTt.sub(16 * tm), Trow.sub(16 * tn), k0, k1, acc);
-            YT.put4(16 * tn + frag_col(), 16 * tm + frag_row(0), acc);
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb < nkb) load_frag(fb[kb], Trow.sub(16 * tn), 32 * kb);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tm = (wave + NW * i) >> 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb < nkb) {
+                        load_frag(fa, dTt.sub(16 * tm), 32 * kb);
+                        acc = mma_ff(fa, fb[kb], acc);
+                    }
+                YT.put4(16 * tn + frag_col(), 16 * tm + frag_row(0), acc);
+            }
         }
         __syncthreads();
+        {
+            // dA tile (tm, tn) = -(T^T rows tm) Y^T: T^T rows tm are zero before index 16 tm,
+            // so tiles w (tm < 2) take k-blocks 0 and 1, tiles w + 8 (tm >= 2) k-block 1 only
+            AFrag<P> fy1, fa;
+            load_frag(fy1, YT.sub(16 * tn), 32);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (tn <= tm) {
-                int k0 = 16 * tm, k1 = kChunk;
-                widen<P>(k0, k1);
-                acc = mma_tile(TT.sub(16 * tm), YT.sub(16 * tn), k0, k1, acc);
-            }
+            for (int i = 0; i < 2; ++i) {
+                const int tm = (wave + NW * i) >> 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (tn <= tm) {
+                    if (i == 0) {
+                        AFrag<P> fy0;
+                        load_frag(fy0, YT.sub(16 * tn), 0);
+                        load_frag(fa, TT.sub(16 * tm), 0);
+                        acc = mma_ff(fa, fy0, acc);
+                    }
+                    load_frag(fa, TT.sub(16 * tm), 32);
+                    acc = mma_ff(fa, fy1, acc);
+                }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int a = 16 * tm + frag_row(r), bb = 16 * tn + frag_col();
-                dAr[i][r] = bb < a ? -acc[r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int a = 16 * tm + frag_row(r), bb = 16 * tn + frag_col();
+                    dAr[i][r] = bb < a ? -acc[r] : 0.f;
+                }
             }
         }
     }
@@ -582,12 +613,18 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         // 6 tasks: (I, column tile of c), on waves 0..5
         if (wave < 6) {
             const int I = 1 + (wave >> 1), tn = wave & 1;
-            int k0 = 0, k1 = 16 * I;
-            widen<P>(k0, k1);
             f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            const T64 kc = KcT(I - 1);
-            ak = mma_tile(dAt.sub(16 * I), kc.sub(16 * tn), k0, k1, ak);
-            aq = mma_tile(dAqt.sub(16 * I), kc.sub(16 * tn), k0, k1, aq);
+            const T64 kc = KcT(I - 1);  // zero from index 16 I on: k-blocks 0 .. (16 I - 1) / 32
+            AFrag<P> fk, fa;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (32 * kb < 16 * I) {
+                    load_frag(fk, kc.sub(16 * tn), 32 * kb);
+                    load_frag(fa, dAt.sub(16 * I), 32 * kb);
+                    ak = mma_ff(fa, fk, ak);
+                    load_frag(fa, dAqt.sub(16 * I), 32 * kb);
+                    aq = mma_ff(fa, fk, aq);
+                }
             const int cc = 16 * tn + frag_col();
             const float gr = Gs[(16 * I) * LR + cc];
             float gt[4], kt[4], qt[4], bt[4], dk0[4], dq0[4], dg0[4];
