@@ -322,124 +322,152 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) aAq[i] = aT[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-        const T32 dOb(ph + 4608, kChunk), vnb(ph + 7168, kChunk), dvnb(ph + 9728, kChunk), bVb(ph + 12288, kChunk),
-            hb(ph + 14848, DK), Db(ph + 16128, DK);
-        const T64 dvnT(ph + 17408, 32);
-        float* Vf = ph + 19712;  // fp32 v of the column block [t][j], stride 36
-        TOut* dvout = (TOut*)p.dv;
+        // All dv columns at once (two k-blocks per product).  ph: T^T, v_new, dv_new,
+        // dv_new^T, dO; ACC (not yet accumulating): v.  dO and v are bf16 numbers:
+        // hi parts only.  h and D' (rows c, columns j: k-block form for fp32) come
+        // as register fragments from their fp32 arrays.
+        const T64 vnb(ph + 4608, kChunk), dvnb(ph + 9216, kChunk), dvnT(ph + 13824, DV), dOb(ph + 18432, kChunk);
+        const T64 Vh(ACC, kChunk);
+        static_assert(18432 + kChunk * (DV + 8) <= PH && kChunk * (DV + 8) <= 3 * kChunk * LR, "P1 staging must fit");
+        f32x4 hraw[2][2], draw[2][2];  // this lane's 8 values of h / D' rows 16 an + (lane & 15), per k-block
+        {
+            const int row = 16 * an + (lane & 15), c8 = 8 * (lane >> 4);
+            const float* hs = p.hs + slot * DK * DV + (size_t)row * DV + c8;
+            const float* ds = p.dhs + slot * DK * DV + (size_t)row * DV + c8;
 #pragma unroll
-        for (int vbk = 0; vbk < NVB; ++vbk) {
-            const int jb = 32 * vbk;
-            __syncthreads();  // previous block's tiles consumed
-            {
-                const float b = bet[tr];
-                dOb.put4_hi(tr, 4 * part, f32x4{dox[vbk][0], dox[vbk][1], dox[vbk][2], dox[vbk][3]});  // bf16 numbers
-                bVb.put4(tr, 4 * part, f32x4{b * vx[vbk][0], b * vx[vbk][1], b * vx[vbk][2], b * vx[vbk][3]});
-                *(f32x4*)&Vf[tr * 36 + 4 * part] = f32x4{vx[vbk][0], vx[vbk][1], vx[vbk][2], vx[vbk][3]};
-            }
+            for (int kb = 0; kb < NVB; ++kb)
 #pragma unroll
-            for (int i = 0; i < NV4; ++i) {
-                const int e4 = 4 * (tid + NTH * i);
-                const int t = e4 / DV, j = e4 - t * DV;
-                if (j >= jb && j < jb + 32) {
-                    vnb.put4(t, j - jb, Vn[i]);
-                    dvnb.put4(t, j - jb, dVn[i]);
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) dvnT.put(j - jb + m, t, dVn[i][m]);
+                for (int q = 0; q < 2; ++q) {
+                    hraw[kb][q] = *(const f32x4*)(hs + 32 * kb + 4 * q);
+                    draw[kb][q] = *(const f32x4*)(ds + 32 * kb + 4 * q);
                 }
-            }
+        }
+        __syncthreads();  // P0's readers of ph and ACC are done
 #pragma unroll
-            for (int i = 0; i < NH4; ++i) {
-                const int e4 = 4 * (tid + NTH * i);
-                const int cc = e4 / DV, j = e4 - cc * DV;
-                if (j >= jb && j < jb + 32) {
-                    hb.put4(cc, j - jb, Hr[i]);
-                    Db.put4(cc, j - jb, Dr[i]);
-                }
-            }
-            __syncthreads();
-            // one k-block each; fragments shared by two products are read once
+        for (int vb = 0; vb < NVB; ++vb) {
+            dOb.put4_hi(tr, 32 * vb + 4 * part, f32x4{dox[vb][0], dox[vb][1], dox[vb][2], dox[vb][3]});
+            Vh.put4_hi(tr, 32 * vb + 4 * part, f32x4{vx[vb][0], vx[vb][1], vx[vb][2], vx[vb][3]});
+        }
+#pragma unroll
+        for (int i = 0; i < NV4; ++i) {
+            const int e4 = 4 * (tid + NTH * i);
+            const int t = e4 / DV, j = e4 - t * DV;
+            vnb.put4(t, j, Vn[i]);
+            dvnb.put4(t, j, dVn[i]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dvnT.put(j + m, t, dVn[i][m]);
+        }
+        __syncthreads();
+        // dQg = dO h^T, dw = -dvn h^T, dKh = vn D^T: this wave's tile (am, an)
+#pragma unroll
+        for (int kb = 0; kb < NVB; ++kb) {
+            AFrag<P> fh, fa, fb;
             {
-                AFrag<P> fh, fa, fb;
-                load_frag(fh, hb.sub(16 * an), 0);
-                load_frag_hi(fa, dOb.sub(16 * am), 0);
-                aQ = mma_ff_ah(fa, fh, aQ);
-                load_frag(fa, dvnb.sub(16 * am), 0);
-                aW = mma_ff(fa, fh, aW);
-                load_frag(fa, vnb.sub(16 * am), 0);
-                load_frag(fb, Db.sub(16 * an), 0);
-                aKh = mma_ff(fa, fb, aKh);
+                const float xh[8] = {hraw[kb][0][0], hraw[kb][0][1], hraw[kb][0][2], hraw[kb][0][3],
+                                     hraw[kb][1][0], hraw[kb][1][1], hraw[kb][1][2], hraw[kb][1][3]};
+                const float xd[8] = {draw[kb][0][0], draw[kb][0][1], draw[kb][0][2], draw[kb][0][3],
+                                     draw[kb][1][0], draw[kb][1][1], draw[kb][1][2], draw[kb][1][3]};
+                make_frag(fh, xh);
+                make_frag(fb, xd);
             }
-            {
-                const int tn = wave & 3;  // both tiles w, w + 8 of the 64 x 64 results share the column tile
-                AFrag<P> fv, fbv, fa;
-                load_frag(fv, vnb.sub(16 * tn), 0);
-                load_frag(fbv, bVb.sub(16 * tn), 0);
+            load_frag_hi(fa, dOb.sub(16 * am), 32 * kb);
+            aQ = mma_ff_ah(fa, fh, aQ);
+            load_frag(fa, dvnb.sub(16 * am), 32 * kb);
+            aW = mma_ff(fa, fh, aW);
+            load_frag(fa, vnb.sub(16 * am), 32 * kb);
+            aKh = mma_ff(fa, fb, aKh);
+        }
+        // dAqk = dO vn^T and dT_v = dvn (beta V)^T = (dvn V^T) diag(beta): tiles w, w + 8,
+        // which share the column tile w & 3
+        {
+            const int tn = wave & 3;
+#pragma unroll
+            for (int kb = 0; kb < NVB; ++kb) {
+                AFrag<P> fv, fvh, fa;
+                load_frag(fv, vnb.sub(16 * tn), 32 * kb);
+                load_frag_hi(fvh, Vh.sub(16 * tn), 32 * kb);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int tm = (wave + NW * i) >> 2;
-                    load_frag_hi(fa, dOb.sub(16 * tm), 0);
+                    load_frag_hi(fa, dOb.sub(16 * tm), 32 * kb);
                     aAq[i] = mma_ff_ah(fa, fv, aAq[i]);
-                    load_frag(fa, dvnb.sub(16 * tm), 0);
-                    aT[i] = mma_ff(fa, fbv, aT[i]);
+                    load_frag(fa, dvnb.sub(16 * tm), 32 * kb);
+                    aT[i] = mma_ff_bh(fa, fvh, aT[i]);
                 }
             }
-            // X_u = T^T dvn: dV = beta X_u, dbeta_v = rowsum(X_u V)
-            {
-                int k0 = 16 * am, k1 = kChunk;
-                widen<P>(k0, k1);
+            const float bs = bet[16 * tn + frag_col()];  // beta of this lane's column s
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) aT[i][r] *= bs;
+        }
+        // X_u = T^T dvn, tiles (am, an + 2 e): dV = beta X_u, dbeta_v = rowsum(X_u V)
+        {
+            TOut* dvout = (TOut*)p.dv;
+            AFrag<P> ft[2], fy;  // T^T rows am: zero before index 16 am, so k-blocks (am >> 1) .. 1
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (kb >= (am >> 1)) load_frag(ft[kb], TT.sub(16 * am), 32 * kb);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int jt = an + 2 * e;  // 16-column tile of dv
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_tile(TT.sub(16 * am), dvnT.sub(16 * an), k0, k1, acc);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    if (kb >= (am >> 1)) {
+                        load_frag(fy, dvnT.sub(16 * jt), 32 * kb);
+                        acc = mma_ff(ft[kb], fy, acc);
+                    }
                 float bt[4], vv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * am + frag_row(r), j = 16 * an + frag_col();
+                    const int t = 16 * am + frag_row(r);
                     bt[r] = bet[t];
-                    vv[r] = Vf[t * 36 + j];
+                    vv[r] = Vh.get_hi(t, 16 * jt + frag_col());
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * am + frag_row(r), j = 16 * an + frag_col();
+                    const int t = 16 * am + frag_row(r), j = 16 * jt + frag_col();
                     const float part_v = row16_sum(acc[r] * vv[r]);
-                    if (frag_col() == 0) dbv[t * GV + 2 * vbk + an] = part_v;
-                    if (t < cr.len) Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, bt[r] * acc[r]);
+                    if (frag_col() == 0) dbv[t * GV + jt] = part_v;
+                    if (t < cr.len) Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + j, bt[r] * acc[r]);
                 }
             }
         }
-    }
-    // explicit factors of Qg and Kh, as the dQg and dKh tiles come out
-    {
-        const int cc = 16 * an + frag_col();
-        const float glc = GL[cc];
-        float gt[4], kt[4], qt[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * am + frag_row(r);
-            gt[r] = Gs[t * LR + cc];
-            kt[r] = Ks[t * LR + cc];
-            qt[r] = Qs[t * LR + cc];
-        }
-        float colsum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * am + frag_row(r);
-            const float gam = __expf(gt[r]), eL = __expf(glc - gt[r]);
-            const float dqg = scale * aQ[r], dkh = aKh[r];
-            const float kh = kt[r] * eL;
-            DQ[t * LR + cc] = gam * dqg;
-            DKa[t * LR + cc] = eL * dkh;
-            DG[t * LR + cc] = qt[r] * gam * dqg - kh * dkh;
-            colsum += t < cr.len ? kh * dkh : 0.f;
-        }
-        colsum = sum_rows(colsum);
-        if (lane < 16) colp[am * DK + cc] = colsum;
     }
 
     // ------------------------------------------------ P2: through w
     {
         const T32 dwt(ph + 4608, kChunk), bKg(ph + 7168, kChunk);
         const T64 dwT(ph + 9728, DK);
-        __syncthreads();  // P1 tiles consumed
+        __syncthreads();  // P1 tiles consumed (and ACC free for the accumulators)
+        // explicit factors of Qg and Kh, as the dQg and dKh tiles come out
+        {
+            const int cc = 16 * an + frag_col();
+            const float glc = GL[cc];
+            float gt[4], kt[4], qt[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * am + frag_row(r);
+                gt[r] = Gs[t * LR + cc];
+                kt[r] = Ks[t * LR + cc];
+                qt[r] = Qs[t * LR + cc];
+            }
+            float colsum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * am + frag_row(r);
+                const float gam = __expf(gt[r]), eL = __expf(glc - gt[r]);
+                const float dqg = scale * aQ[r], dkh = aKh[r];
+                const float kh = kt[r] * eL;
+                DQ[t * LR + cc] = gam * dqg;
+                DKa[t * LR + cc] = eL * dkh;
+                DG[t * LR + cc] = qt[r] * gam * dqg - kh * dkh;
+                colsum += t < cr.len ? kh * dkh : 0.f;
+            }
+            colsum = sum_rows(colsum);
+            if (lane < 16) colp[am * DK + cc] = colsum;
+        }
         {
             const float b = bet[tr];
             f32x4 v0;

@@ -338,6 +338,7 @@ template <int C> struct STile<Prec::F32, C> {
     // (the _hi forms are for values that are bf16 numbers; in fp32 tiles they are the plain ones)
     __device__ __forceinline__ void put_hi(int r, int k, float x) const { put(r, k, x); }
     __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const { put4(r, k, x); }
+    __device__ __forceinline__ float get_hi(int r, int k) const { return p[r * ld + k]; }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;
         t.p += r * ld;
@@ -376,6 +377,7 @@ template <int C> struct STile<Prec::BF3, C> {
     // Values that are bf16 numbers (bf16 inputs): the lo part is zero and is
     // neither stored nor read (load_frag_hi, mma_ff_ah / mma_ff_bh).
     __device__ __forceinline__ void put_hi(int r, int k, float x) const { hi[at(r, k)] = (__bf16)x; }
+    __device__ __forceinline__ float get_hi(int r, int k) const { return (float)hi[at(r, k)]; }
     __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 h;
