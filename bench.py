@@ -198,6 +198,155 @@ def secondary_run(q, k, v, f, b, do, scale, flags, B, T, H, dk, dv, dev, mult=8,
             "steps": steps, "data": "the headline draw repeated %dx along the batch" % mult}
 
 
+def io_bytes(B, T, H, dk, dv, N, esz, h0, dhT, backward):
+    """Algorithmic HBM bytes of one kda_fwd (+ kda_bwd) call: the inputs read and
+    outputs written once, at their own element sizes (esz for q/k/v/o/do/dq/dk/dv,
+    4 for f, b, df, db and every state)."""
+    th = B * T * H
+    fwd = th * (2 * esz * dk + esz * dv + 4 * dk + 4 + esz * dv)
+    st = N * H * dk * dv * 4
+    fwd += st * ((1 if h0 else 0) + 1)  # h0 read, hT written
+    if not backward:
+        return fwd
+    bwd = th * (2 * esz * dk + esz * dv + 4 * dk + 4 + esz * dv) + th * (2 * esz * dk + esz * dv + 4 * dk + 4)
+    bwd += st * ((1 if h0 else 0) + (1 if dhT else 0) + (1 if h0 else 0))  # h0, dhT read, dh0 written
+    return fwd + bwd
+
+
+def chunked_flops(dk, dv, C=64):
+    """FLOPs per token-head of the chunked forward + backward (2 per multiply-add,
+    triangles as halves): forward 3C dk + 2C dv + C^2/3 + 6 dk dv, backward
+    recompute + gradients (3C dk + C dv + C^2/3 + 4 dk dv) + (6C dk + 4C dv +
+    2C^2/3 + 12 dk dv)."""
+    fwd = 3 * C * dk + 2 * C * dv + C * C / 3 + 6 * dk * dv
+    bwd = (3 * C * dk + C * dv + C * C / 3 + 4 * dk * dv) + (6 * C * dk + 4 * C * dv + 2 * C * C / 3 + 12 * dk * dv)
+    return fwd + bwd
+
+
+def timed_ms(fn, reps, warm=2):
+    """Mean milliseconds of fn() over reps, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def fwd_bwd_workload(name, dev, B, T, H, dk, dv, seed, packed=False, reps=10):
+    """fwd+bwd of another configuration: tokens/s and the fraction of its binding
+    roofline, max(bytes / HBM peak, 3 x FLOPs / bf16 MFMA peak) (products issued as
+    three bf16 MFMAs, hi/lo split)."""
+    import torch
+
+    import kda_inputs
+    import kimi_delta_attention_chunk_amd as kda
+
+    bf = torch.bfloat16
+    cu = plan = None
+    if packed:
+        cu = kda_inputs.geometric_cu_seqlens(seed, total=T).to(dev)
+        N = cu.numel() - 1
+        plan = kda.plan_varlen(cu, T)
+    else:
+        N = B
+    raw = kda_inputs.draw(seed, B, T, H, dk, dv, n_states=N, h0_std=0.1 if packed else None,
+                          upstream=True, dhT=packed)
+    q, k, v, do = (raw[x].to(bf).to(dev) for x in ("q_raw", "k_raw", "v", "do"))
+    f, b, A_log, dtb = (raw[x].to(dev) for x in ("f", "b", "A_log", "dt_bias"))
+    h0 = raw["h0"].to(dev) if raw["h0"] is not None else None
+    dhT = raw["dhT"].to(dev) if raw["dhT"] is not None else None
+    scale = dk ** -0.5
+    flags = dict(A_log=A_log, dt_bias=dtb, l2norm_qk=True, gate_in_kernel=True, beta_logits=True)
+    ws = torch.empty(kda.workspace_bytes((B, T, H, dk), dv, N, True), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.fwd(q, k, v, f, b, scale, h0=h0, cu_seqlens=cu, plan=plan, workspace=ws, save_for_bwd=True,
+                **flags)
+        kda.bwd(q, k, v, f, b, scale, do, h0=h0, dhT=dhT, cu_seqlens=cu, plan=plan, workspace=ws,
+                fwd_saved=True, need_dh0=packed, **flags)
+
+    ms = timed_ms(step, reps)
+    nbytes = io_bytes(B, T, H, dk, dv, N, 2, h0 is not None, dhT is not None, True)
+    flops = chunked_flops(dk, dv) * B * T * H
+    t_hbm, t_mfma = nbytes / (PEAK_HBM_GBS * 1e9), 3 * flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_roof = max(t_hbm, t_mfma)
+    return {"workload": name, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "documents": N,
+            "ms_per_step": ms, "tokens_per_s": B * T / (ms * 1e-3), "reps": reps,
+            "algorithmic_bytes": nbytes, "flops": flops, "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "roofline_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3)}
+
+
+def decode_workload(dev, steps=1000, B=256, H=8, dk=32, dv=64, seed=2):
+    """kda_step for `steps` consecutive tokens of B sequences (bf16 q/k/v, fp32 f/b and
+    state, fused preparation), captured once in a HIP graph and replayed: microseconds
+    per step and effective GB/s of its algorithmic bytes (state read and written, the
+    token's inputs and output).  The 16.8 MB state stays in the 256 MB Infinity Cache
+    between steps, so the warm figure can pass the HBM peak; `cold_step_us` is the
+    median of single steps each after a 512 MB cache flush."""
+    import torch
+
+    import kda_inputs
+    import kimi_delta_attention_chunk_amd as kda
+
+    bf = torch.bfloat16
+    raw = kda_inputs.draw_decode(seed, steps, B, H, dk, dv)
+    q, k, v = (raw[x].to(bf).to(dev) for x in ("q_raw", "k_raw", "v"))
+    f, b, A_log, dtb = (raw[x].to(dev) for x in ("f", "b", "A_log", "dt_bias"))
+    h = raw["h"].to(dev)
+    o = torch.empty((steps, B, H, dv), dtype=bf, device=dev)
+    scale = dk ** -0.5
+    flags = dict(A_log=A_log, dt_bias=dtb, l2norm_qk=True, gate_in_kernel=True, beta_logits=True)
+
+    def one(t):
+        kda.step(q[t], k[t], v[t], f[t], b[t], h, scale, out=o[t], **flags)
+
+    for t in range(8):
+        one(t)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            one(t)
+    ms = timed_ms(graph.replay, 5, warm=1)
+    per = ms * 1e3 / steps
+    nbytes = B * H * (2 * dk * dv * 4 + 2 * 2 * dk + 2 * dv + 4 * dk + 4 + 2 * dv)
+    buf = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    cold = []
+    for t in range(21):
+        buf.fill_(1.0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        one(t)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    cold.sort()
+    return {"workload": "kda_step decode: B=%d H=%d dk=%d dv=%d, %d steps in one HIP graph" % (B, H, dk, dv, steps),
+            "us_per_step": per, "tokens_per_s": B / (per * 1e-6), "algorithmic_bytes_per_step": nbytes,
+            "effective_GBs": nbytes / (per * 1e-6) / 1e9, "frac_of_8TBs": nbytes / (per * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "roofline_us": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6, "cold_step_us": cold[len(cold) // 2]}
+
+
+def other_workloads(dev):
+    """The decode step, the packed 65,536-token row and the dk = dv = 128 heads."""
+    return [
+        decode_workload(dev),
+        fwd_bwd_workload("KDA fwd+bwd, one packed row of 65536 tokens (geometric document lengths, "
+                         "mean 512), per-document h0 and dhT", dev, 1, 65536, 8, 32, 64, 3, packed=True),
+        fwd_bwd_workload("KDA fwd+bwd, larger heads: B=2 T=8192 H=16 dk=dv=128", dev, 2, 8192, 16, 128, 128, 4),
+    ]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +359,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the cache-flushed median and the B=128 run (keeps profiler traces to the timed steps)")
     ap.add_argument("--out-dtype", choices=["bf16", "fp32"], default="bf16")
+    ap.add_argument("--only-extras", action="store_true",
+                    help="run only the other workloads (decode, packed row, dk=128) and print them")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -231,6 +382,10 @@ def main():
     B, T, H, dk, dv = args.batch, args.seq, 8, 32, 64
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_extras:
+        for w in other_workloads(dev):
+            print(json.dumps(w), flush=True)
+        return
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
     raw = kda_inputs.draw(1, B, T, H, dk, dv, upstream=True)
     bf = torch.bfloat16
@@ -323,6 +478,7 @@ def main():
         line["flushed"] = flushed_median(step, dev, reps=21)
         line["flushed"]["tokens_per_s"] = B * T / (line["flushed"]["median_ms"] * 1e-3)
         line["secondary_B128"] = secondary_run(q, k, v, f, b, do, scale, flags, B, T, H, dk, dv, dev)
+        line["other_workloads"] = other_workloads(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(B, T, H, dk, dv, args.cpu_seconds)
     print(json.dumps(line), flush=True)

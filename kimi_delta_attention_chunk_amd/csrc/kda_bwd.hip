@@ -6,8 +6,8 @@
 // change, and the Primus guide's autotune paragraph on
 // chunk_kda_bwd_kernel_intra).  Launch sequence:
 //   1. forward recompute: intra (w, u, Aqk, T) and state pass (h_n, v_new);
-//   2. bwd_dh   one workgroup per (sequence, head, 32 state columns), chunks
-//               in reverse: D = dL/dS at each chunk end, and
+//   2. bwd_dh   one workgroup per (sequence, head, 32 or 16 state columns),
+//               chunks in reverse (kda_dhscan.cuh): D = dL/dS at each chunk end, and
 //               dv_new = scale Aqk^T dO + Kh D,
 //               D     <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new;
 //   3. bwd_dv   one workgroup per (chunk, head): the products that contract
@@ -32,117 +32,6 @@
 #include "kda_internal.h"
 
 namespace kda {
-
-// ============================================================== reverse state pass
-template <int DK, int DV, typename TIn>
-__global__ void __launch_bounds__(kThreads) bwd_dh_kernel(Prm p, int total_wg) {
-    constexpr int LS = kBV + 4;
-    __shared__ float D[DK * LS];
-    __shared__ float QT[DK * kLD];   // scale * q * exp(G), transposed
-    __shared__ float KhT[DK * kLD];  // k * exp(G_L - G), transposed
-    constexpr int GW = DK * kLD > kChunk * (DK + 4) ? DK * kLD : kChunk * (DK + 4);
-    __shared__ float GT[GW];         // cumulative decay, then w (row-major, stride DK+4)
-    __shared__ float AQ[kChunk * kLD];
-    __shared__ float DOs[kChunk * LS];
-    __shared__ float DVN[kChunk * LS];
-    __shared__ float gL[DK];
-    __shared__ float rn[kChunk];
-
-    constexpr int NV = DV / kBV;
-    const int lid = xcd_local_id(blockIdx.x, total_wg);
-    const int vb = lid % NV, nh = lid / NV;
-    const int n = nh / p.H, h = nh % p.H;
-    if (n >= p.N) return;
-    const int jb = vb * kBV;
-    const bool l2 = p.flags & 1u;
-    const float scale = p.scale;
-    const TIn* dO = (const TIn*)p.d_o;
-
-    for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
-        const int cc = e / kBV, j = e - cc * kBV;
-        D[cc * LS + j] = p.dhT ? p.dhT[((size_t)nh * DK + cc) * DV + jb + j] : 0.f;
-    }
-    int c0, c1;
-    p.seq.seq_chunks(n, c0, c1);
-    for (int c = c1 - 1; c >= c0; --c) {
-        const ChunkRef cr = p.seq.chunk(c);
-        const size_t slot = (size_t)c * p.H + h;
-        __syncthreads();
-        float* dhs = p.dhs + slot * DK * DV;
-        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
-            const int cc = e / kBV, j = e - cc * kBV;
-            dhs[cc * DV + jb + j] = D[cc * LS + j];
-        }
-        stage_qk<DK, TIn>((const TIn*)p.k, cr, h, p.H, l2, KhT, rn);
-        stage_qk<DK, TIn>((const TIn*)p.q, cr, h, p.H, l2, QT, rn);
-        stage_g<DK>(p, cr, h, GT, nullptr);
-        const int last = cr.len - 1;
-        for (int e = threadIdx.x; e < DK * kChunk; e += kThreads) {
-            const int cc = e / kChunk, t = e - cc * kChunk;
-            const float gt = GT[cc * kLD + t];
-            KhT[cc * kLD + t] *= __expf(GT[cc * kLD + last] - gt);
-            QT[cc * kLD + t] *= scale * __expf(gt);
-        }
-        if (threadIdx.x < DK) gL[threadIdx.x] = __expf(GT[threadIdx.x * kLD + last]);
-        const float* aq = p.aqk + slot * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) AQ[(e >> 6) * kLD + (e & 63)] = aq[e];
-        for (int e = threadIdx.x; e < kChunk * kBV; e += kThreads) {
-            const int t = e / kBV, j = e - t * kBV;
-            DOs[t * LS + j] = t < cr.len ? Elem<TIn>::load(dO, tok_index(cr.t0 + t, h, p.H, DV) + jb + j) : 0.f;
-        }
-        __syncthreads();  // GT fully consumed: reuse it for w
-        float* WL = GT;
-        const float* wi = p.w + slot * kChunk * DK;
-        for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
-            const int t = e / DK, cc = e - t * DK;
-            WL[t * (DK + 4) + cc] = wi[e];
-        }
-        __syncthreads();
-        // dv_new = scale Aqk^T dO + Kh D
-        float* dvo = p.dvn + slot * kChunk * DV;
-        {
-            const int wave = wave_id(), lane = threadIdx.x & 63;
-            constexpr int TN = kBV / 16, TILES = (kChunk / 16) * TN;
-            for (int tile = wave; tile < TILES; tile += kWaves) {
-                const int tm = tile / TN, tn = tile % TN;
-                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-                a1 = mma16_f32(AQ + tm * 16, 1, kLD, DOs + tn * 16, LS, 1, 16 * tm, kChunk, a1);
-                a2 = mma16_f32(KhT + tm * 16, 1, kLD, D + tn * 16, LS, 1, 0, DK, a2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
-                    const float val = scale * a1[i] + a2[i];
-                    DVN[t * LS + j] = val;
-                    dvo[t * DV + jb + j] = val;
-                }
-            }
-        }
-        __syncthreads();
-        // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
-        {
-            const int wave = wave_id(), lane = threadIdx.x & 63;
-            constexpr int TN = kBV / 16, TILES = (DK / 16) * TN;
-            for (int tile = wave; tile < TILES; tile += kWaves) {
-                const int tm = tile / TN, tn = tile % TN;
-                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-                a1 = mma16_f32(QT + tm * 16 * kLD, kLD, 1, DOs + tn * 16, LS, 1, 0, kChunk, a1);
-                a2 = mma16_f32(WL + tm * 16, 1, DK + 4, DVN + tn * 16, LS, 1, 0, kChunk, a2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int cc = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
-                    D[cc * LS + j] = gL[cc] * D[cc * LS + j] + a1[i] - a2[i];
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (p.dh0) {
-        for (int e = threadIdx.x; e < DK * kBV; e += kThreads) {
-            const int cc = e / kBV, j = e - cc * kBV;
-            p.dh0[((size_t)nh * DK + cc) * DV + jb + j] = D[cc * LS + j];
-        }
-    }
-}
 
 // ============================================================== dv-side contractions
 template <int DK, int DV, typename TIn, typename TOut>
@@ -645,14 +534,13 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
-    const int total = a.N * a.H * (DV / kBV);
     if constexpr (DK == 32 && DV == 64) {
         const int tot16 = a.N * a.H * (DV / kPsBV);
         KDA_LAUNCH("bwd_dh", (bwd_pdh_kernel<TIn, P, kPsBV>), dim3(tot16), dim3(kPsThreads), s, p, tot16);
-    } else if constexpr (DK <= 64) {
-        KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     } else {
-        KDA_LAUNCH("bwd_dh", (bwd_dh_kernel<DK, DV, TIn>), dim3(total), dim3(kThreads), s, p, total);
+        constexpr int BV = DK <= 64 ? 32 : 16;  // dk = 128: the operand tiles fill the LDS
+        const int total = a.N * a.H * (DV / BV);
+        KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, BV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     }
     if (a.n_chunks_bound > 0) {
         if constexpr (DK == 32 && DV == 64) {

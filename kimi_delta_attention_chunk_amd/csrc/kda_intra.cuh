@@ -111,9 +111,9 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     const T64 Tt(S1, kChunk);       // T as an MFMA operand, after the solve
 
     // w, exp(G) q, (k exp(G_L - G))^T and Aqk go to the workspace in k-block form
-    // (kda_mma.cuh) for the sequential kernels of dk <= 64, which load MFMA
-    // fragments from it directly; plain fp32 (the F32 k-block form) otherwise.
-    constexpr Prec WP = DK <= 64 ? P : Prec::F32;
+    // (kda_mma.cuh) for the sequential kernels, which load MFMA fragments from it
+    // directly.
+    constexpr Prec WP = P;
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
     if (cr.len == 0) return;
@@ -435,11 +435,15 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             if (DK <= 64 && b < NB) {  // w: staged in Tm [t][c] (stride kLD), written out below
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Tm[(tm * 16 + frag_row(r)) * kLD + b * kCB32 + tn * 16 + frag_col()] = acc[r];
-            } else {
-                float* out = b < NB ? wo + b * kCB32 : uo + (b - NB) * 32;
-                const int ld = b < NB ? DK : DV;
+            } else if (b < NB) {  // w (dk > 64): k-block b of rows 16 tm .., straight from the fragment
 #pragma unroll
-                for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * ld + tn * 16 + frag_col()] = acc[r];
+                for (int r = 0; r < 4; ++r)
+                    store_kblock1<WP>((char*)wo + (size_t)((tm * 16 + frag_row(r)) * NB + b) * kKBlockBytes, acc[r],
+                                      tn * 16 + frag_col());
+            } else {
+                float* out = uo + (b - NB) * 32;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(size_t)(tm * 16 + frag_row(r)) * DV + tn * 16 + frag_col()] = acc[r];
             }
         }
     }

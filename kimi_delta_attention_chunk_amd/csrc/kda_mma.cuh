@@ -280,6 +280,21 @@ __device__ __forceinline__ f32x4 mma_ff(const AFrag<Prec::F32>& a, const AFrag<P
     return acc;
 }
 
+// Write one value (index k of a k-block) of one row in k-block form.
+template <Prec P>
+__device__ __forceinline__ void store_kblock1(void* rowblock, float x, int k);
+template <>
+__device__ __forceinline__ void store_kblock1<Prec::BF3>(void* rowblock, float x, int k) {
+    const __bf16 h = (__bf16)x;
+    __bf16* b = (__bf16*)rowblock;
+    b[k] = h;
+    b[32 + k] = (__bf16)(x - (float)h);
+}
+template <>
+__device__ __forceinline__ void store_kblock1<Prec::F32>(void* rowblock, float x, int k) {
+    ((float*)rowblock)[k] = x;
+}
+
 // Write 4 consecutive values (indices k0 .. k0 + 3 of a k-block, k0 a multiple
 // of 4) of one row in k-block form.  A D fragment holds, per lane, four
 // consecutive rows of one column, i.e. four consecutive k-block indices of a

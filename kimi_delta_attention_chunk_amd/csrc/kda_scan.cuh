@@ -1,9 +1,9 @@
 // kda_scan.cuh -- the sequential part of the forward: state passing and output.
 //
-// One workgroup per (sequence, head, 32 columns of the state).  For every
+// One workgroup per (sequence, head, BV columns of the state).  For every
 // chunk of the sequence, in order, with h the fp32 state entering it:
-//   v_new = u - w h                         (64 x 32)
-//   o     = scale (exp(G) q h + Aqk v_new)  (64 x 32, written if requested)
+//   v_new = u - w h                         (64 x BV)
+//   o     = scale (exp(G) q h + Aqk v_new)  (64 x BV, written if requested)
 //   h    <- Diag(exp G_L) h + (k exp(G_L - G))^T v_new
 // All operands of a chunk come precomputed from the intra-chunk kernel in
 // k-block form (kda_mma.cuh), so each lane loads its MFMA A fragments straight
@@ -13,6 +13,11 @@
 // that own its 16x16 tiles, and an MFMA copy hT[j][c] is written each chunk,
 // double buffered so that the output product (reading h) and the state update
 // run in the same phase; v_new^T likewise.
+// BV = 32 (dk = 64): each wave forms one v_new tile and the output tile at the
+// same place.  BV = 16 (dk = 128: twice the state rows, so half the columns
+// per workgroup keeps the registers and puts N*H*8 workgroups on the chip):
+// there are only four 64 x 16 tiles, so waves 0-3 form v_new and waves 4-7 the
+// output, each wave holding only the row operand its product needs.
 // Optional stores for the backward: the state entering each chunk and v_new.
 #pragma once
 
@@ -24,32 +29,43 @@ namespace kda {
 constexpr int kScanThreads = 512, kScanWaves = 8;  // two waves per SIMD
 
 // One chunk's operands for this lane, loaded straight from the k-block
-// workspace arrays into MFMA A fragments (wave w owns v_new / output tile
-// (w >> 1, w & 1) and state tile(s) w + 8 i).
-template <int DK, Prec P>
+// workspace arrays into MFMA A fragments.
+template <int DK, int BV, Prec P>
 struct ScanFrags {
     static constexpr int KB = DK / 32;
-    static constexpr int TH = (DK / 16) * 2;                       // state tiles (DK x 32)
-    static constexpr int HPW = (TH + kScanWaves - 1) / kScanWaves;  // state tiles per wave
-    AFrag<P> w[KB], q[KB], a[2], k[HPW][2];
+    static constexpr int TN = BV / 16;                               // 16-column tiles of the block
+    static constexpr int VT = 4 * TN;                                // v_new / output tiles (64 x BV)
+    static constexpr bool SPLIT = VT < kScanWaves;                   // v_new and output on separate waves
+    static_assert(VT == kScanWaves || 2 * VT == kScanWaves, "block width");
+    static constexpr int TH = (DK / 16) * TN;                        // state tiles (DK x BV)
+    static constexpr int HPW = (TH + kScanWaves - 1) / kScanWaves;   // state tiles per wave
+    // x: this wave's row operand over the state rows -- w (v_new tile), or
+    // exp(G) q on the output waves of a split block; q: exp(G) q when the
+    // same wave forms both products.
+    AFrag<P> x[KB], q[SPLIT ? 1 : KB], a[2], k[HPW][2];
     float u[4];        // u at this lane's v_new fragment positions
     float g[4 * HPW];  // exp(G_L) at this lane's state rows
+    // this wave's v_new / output tile (row block tm, column tile tn)
+    __device__ __forceinline__ static int vtile(int wave) { return SPLIT && wave >= VT ? wave - VT : wave; }
+    __device__ __forceinline__ static bool forms_vnew(int wave) { return !SPLIT || wave < VT; }
+    __device__ __forceinline__ static bool forms_out(int wave) { return !SPLIT || wave >= VT; }
 };
 
-template <int DK, int DV, Prec P>
-__device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, ScanFrags<DK, P>& R) {
-    using F = ScanFrags<DK, P>;
+template <int DK, int DV, int BV, Prec P>
+__device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, ScanFrags<DK, BV, P>& R) {
+    using F = ScanFrags<DK, BV, P>;
     const int wave = wave_id(), lr = threadIdx.x & 15;
-    const int tm = wave >> 1, tn = wave & 1;
+    const int vt = F::vtile(wave), tm = vt / F::TN, tn = vt % F::TN;
     const char* w = (const char*)(p.w + slot * kChunk * DK);       // [t][DK/32] k-blocks
     const char* q = (const char*)(p.qg + slot * kChunk * DK);      // [t][DK/32]
     const char* a = (const char*)(p.aqk + slot * kChunk * kChunk); // [t][2]
     const char* k = (const char*)(p.khT + slot * DK * kChunk);     // [c][2]
+    const char* xs = F::forms_vnew(wave) ? w : q;
     const int row = 16 * tm + lr;
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb) {
-        load_afrag(R.w[kb], w + (size_t)(row * F::KB + kb) * kKBlockBytes);
-        load_afrag(R.q[kb], q + (size_t)(row * F::KB + kb) * kKBlockBytes);
+        load_afrag(R.x[kb], xs + (size_t)(row * F::KB + kb) * kKBlockBytes);
+        if constexpr (!F::SPLIT) load_afrag(R.q[kb], q + (size_t)(row * F::KB + kb) * kKBlockBytes);
     }
     // Every load below is unconditional (a wave without a state tile reads
     // tile 0's operands, unused; Aqk's second block is read even where it is
@@ -60,7 +76,7 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
         if (tile < F::TH) {
-        const int crow = 16 * (tile >> 1) + lr;
+        const int crow = 16 * (tile / F::TN) + lr;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) load_afrag(R.k[i][kb], k + (size_t)(crow * 2 + kb) * kKBlockBytes);
         }
@@ -72,17 +88,17 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
         {
-            const int tmh = (tile < F::TH ? tile : 0) >> 1;
+            const int tmh = (tile < F::TH ? tile : 0) / F::TN;
 #pragma unroll
             for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + tmh * 16 + frag_row(r)];
         }
     }
 }
 
-template <int DK, int DV, typename TOut, Prec P>
+template <int DK, int DV, int BV, typename TOut, Prec P>
 __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total_wg, int write_o, int store_states) {
-    using F = ScanFrags<DK, P>;
-    constexpr int BV = 32, LK = DK + 8, LA = kChunk + 8, NV = DV / BV;
+    using F = ScanFrags<DK, BV, P>;
+    constexpr int LK = DK + 8, LA = kChunk + 8, NV = DV / BV, TN = F::TN;
     constexpr int TH = F::TH, HPW = F::HPW, NWV = kScanWaves;
     __shared__ __attribute__((aligned(16))) float sH[2][BV * LK];
     __shared__ __attribute__((aligned(16))) float sV[BV * LA];
@@ -95,7 +111,7 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
     if (n >= p.N) return;
     const int jb = vb * BV;
     const int wave = wave_id();
-    const int tm = wave >> 1, tn = wave & 1;  // this wave's v_new / output tile
+    const int tm = F::vtile(wave) / TN, tn = F::vtile(wave) % TN;  // this wave's v_new / output tile
 
     // fp32 state: this lane's elements of its state tiles (rows c, column j)
     f32x4 S[HPW];
@@ -104,7 +120,7 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
         const int tile = wave + NWV * i;
         S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile < TH) {
-            const int tmh = tile >> 1, tnh = tile & 1, j = tnh * 16 + frag_col();
+            const int tmh = tile / TN, tnh = tile % TN, j = tnh * 16 + frag_col();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int cc = tmh * 16 + frag_row(r);
@@ -138,17 +154,17 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
             for (int i = 0; i < HPW; ++i) {
                 const int tile = wave + NWV * i;
                 if (tile < TH) {
-                    const int tmh = tile >> 1, tnh = tile & 1;
+                    const int tmh = tile / TN, tnh = tile % TN;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         hs[(size_t)(tmh * 16 + frag_row(r)) * DV + jb + tnh * 16 + frag_col()] = S[i][r];
                 }
             }
         }
-        {
+        if (F::forms_vnew(wave)) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < F::KB; ++kb) acc = mma_frag(Rc.w[kb], hb.sub(tn * 16), 32 * kb, acc);
+            for (int kb = 0; kb < F::KB; ++kb) acc = mma_frag(Rc.x[kb], hb.sub(tn * 16), 32 * kb, acc);
             f32x4 val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) val[r] = Rc.u[r] - acc[r];
@@ -165,7 +181,7 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
         for (int i = 0; i < HPW; ++i) {
             const int tile = wave + NWV * i;
             if (tile < TH) {
-                const int tmh = tile >> 1, tnh = tile & 1;
+                const int tmh = tile / TN, tnh = tile % TN;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma_frag(Rc.k[i][0], vnT.sub(tnh * 16), 0, acc);
                 acc = mma_frag(Rc.k[i][1], vnT.sub(tnh * 16), 32, acc);
@@ -174,10 +190,13 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
                 hn.put4(tnh * 16 + frag_col(), tmh * 16 + frag_row(0), S[i]);
             }
         }
-        if (write_o) {
+        if (write_o && F::forms_out(wave)) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < F::KB; ++kb) acc = mma_frag(Rc.q[kb], hb.sub(tn * 16), 32 * kb, acc);
+            for (int kb = 0; kb < F::KB; ++kb) {
+                if constexpr (F::SPLIT) acc = mma_frag(Rc.x[kb], hb.sub(tn * 16), 32 * kb, acc);
+                else acc = mma_frag(Rc.q[kb], hb.sub(tn * 16), 32 * kb, acc);
+            }
             acc = mma_frag(Rc.a[0], vnT.sub(tn * 16), 0, acc);
             if (tm >= 2) acc = mma_frag(Rc.a[1], vnT.sub(tn * 16), 32, acc);
 #pragma unroll
@@ -190,15 +209,15 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
     if (c0 < c1) {
         // (scheduling barriers keep the two batches in issue order: the
         // waits count completions in order)
-        scan_load<DK, DV, P>(p, slot_of(c0), jb, R[0]);
-        scan_load<DK, DV, P>(p, slot_of(c0 + 1), jb, R[1]);
+        scan_load<DK, DV, BV, P>(p, slot_of(c0), jb, R[0]);
+        scan_load<DK, DV, BV, P>(p, slot_of(c0 + 1), jb, R[1]);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = c0; c < c1; c += 2) {
             step(c, R[0]);
-            scan_load<DK, DV, P>(p, slot_of(c + 2), jb, R[0]);
+            scan_load<DK, DV, BV, P>(p, slot_of(c + 2), jb, R[0]);
             if (c + 1 < c1) {
                 step(c + 1, R[1]);
-                scan_load<DK, DV, P>(p, slot_of(c + 3), jb, R[1]);
+                scan_load<DK, DV, BV, P>(p, slot_of(c + 3), jb, R[1]);
             }
         }
     }
@@ -207,7 +226,7 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
         for (int i = 0; i < HPW; ++i) {
             const int tile = wave + NWV * i;
             if (tile < TH) {
-                const int tmh = tile >> 1, tnh = tile & 1;
+                const int tmh = tile / TN, tnh = tile % TN;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     p.hT[((size_t)nh * DK + tmh * 16 + frag_row(r)) * DV + jb + tnh * 16 + frag_col()] = S[i][r];

@@ -91,3 +91,44 @@ def test_step_bf16_output_is_rounded_fp32_output():
     ob = kda.step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], hb, 0.17, out_dtype=torch.bfloat16)
     assert torch.equal(oa.to(torch.bfloat16), ob)
     assert torch.equal(ha, hb)
+
+
+def test_step_graph_replay_equals_eager():
+    """Consecutive decode steps captured in one HIP graph: every replay reproduces the
+    eager steps bit for bit (outputs of every step and the final state), with other
+    eager work and synchronisations between the replays."""
+    B, H, dk, dv, steps = 64, 8, 32, 64, 12
+    raw = kda_inputs.draw_decode(5, steps, B, H, dk, dv)
+    dt = torch.bfloat16
+    q, k, v = (raw[x].to(dt).cuda() for x in ("q_raw", "k_raw", "v"))
+    f, b = raw["f"].cuda(), raw["b"].cuda()
+    A_log, dtb = raw["A_log"].cuda(), raw["dt_bias"].cuda()
+    flags = dict(A_log=A_log, dt_bias=dtb, l2norm_qk=True, gate_in_kernel=True, beta_logits=True)
+    scale = dk ** -0.5
+    h_init = raw["h"].cuda()
+
+    h_eager = h_init.clone()
+    o_eager = torch.empty((steps, B, H, dv), dtype=dt, device="cuda")
+    for t in range(steps):
+        kda.step(q[t], k[t], v[t], f[t], b[t], h_eager, scale, out=o_eager[t], **flags)
+    torch.cuda.synchronize()
+
+    h = h_init.clone()
+    o = torch.empty_like(o_eager)
+    kda.step(q[0], k[0], v[0], f[0], b[0], h.clone(), scale, **flags)  # warm the launch path
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            kda.step(q[t], k[t], v[t], f[t], b[t], h, scale, out=o[t], **flags)
+    other = h_init.clone()
+    for rep in range(3):
+        h.copy_(h_init)
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager), "replay %d: outputs differ from the eager steps" % rep
+        assert torch.equal(h, h_eager), "replay %d: state differs from the eager steps" % rep
+        kda.step(q[rep], k[rep], v[rep], f[rep], b[rep], other, scale, **flags)  # eager work between replays
+        torch.cuda.synchronize()
