@@ -34,8 +34,12 @@
 namespace kda {
 
 // ============================================================== dv-side contractions
+// The per-chunk kernels of dk = 64 and 128 run 8 waves (two per SIMD): their
+// tiles take most of the LDS, so one workgroup fits per CU.
+constexpr int kGThreads = 512, kGWaves = kGThreads / 64;
+
 template <int DK, int DV, typename TIn, typename TOut>
-__global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
+__global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     constexpr int VB = 32, LB = VB + 4, NG = DV / 16;
     __shared__ float Tm[kChunk * kLD];
     __shared__ float Hb[DK * LB];
@@ -58,7 +62,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
 
     const float* tmi = p.tm + slot * kChunk * kChunk;
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
+    for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
     if (threadIdx.x < kChunk) {
         const int t = threadIdx.x;
         float b = 0.f;
@@ -70,8 +74,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
     }
     if (threadIdx.x < DK) dgl[threadIdx.x] = 0.f;
 
-    TileSet<kChunk, DK> aQ, aKh, aW;
-    TileSet<kChunk, kChunk> aAq, aT;
+    TileSet<kChunk, DK, kGWaves> aQ, aKh, aW;
+    TileSet<kChunk, kChunk, kGWaves> aAq, aT;
     aQ.zero(); aKh.zero(); aW.zero(); aAq.zero(); aT.zero();
 
     const float* hs = p.hs + slot * DK * DV;
@@ -80,12 +84,12 @@ __global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
     const float* dvn = p.dvn + slot * kChunk * DV;
     for (int jb = 0; jb < DV; jb += VB) {
         __syncthreads();
-        for (int e = threadIdx.x; e < DK * VB; e += kThreads) {
+        for (int e = threadIdx.x; e < DK * VB; e += kGThreads) {
             const int cc = e / VB, j = e - cc * VB;
             Hb[cc * LB + j] = hs[cc * DV + jb + j];
             Db[cc * LB + j] = dhs[cc * DV + jb + j];
         }
-        for (int e = threadIdx.x; e < kChunk * VB; e += kThreads) {
+        for (int e = threadIdx.x; e < kChunk * VB; e += kGThreads) {
             const int t = e / VB, j = e - t * VB;
             const bool in = t < cr.len;
             const size_t gi = tok_index(cr.t0 + t, h, p.H, DV) + jb + j;
@@ -103,7 +107,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dv_kernel(Prm p) {
         // X_u = T^T dvn  ->  dV = beta . X_u,  dbeta_v = rowsum(X_u . V)
         {
             constexpr int TN = VB / 16, TILES = (kChunk / 16) * TN;
-            for (int tile = wave; tile < TILES; tile += kWaves) {
+            for (int tile = wave; tile < TILES; tile += kGWaves) {
                 const int tm = tile / TN, tn = tile % TN;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma16_f32(Tm + tm * 16, 1, kLD, DVNb + tn * 16, LB, 1, 16 * tm, kChunk, acc);
@@ -150,10 +154,10 @@ constexpr int kCB = 32;  // channels per block in the dk-side kernel
 
 // Stage channels [cb, cb+kCB) of q or k into XT[c][t] (times the row's
 // inverse norm if `rn` is given); zero past the chunk end.
-template <int DK, typename TIn>
+template <int DK, typename TIn, int NTH>
 __device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
                                const float* rn, float* XT) {
-    for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+    for (int e = threadIdx.x; e < kChunk * kCB; e += NTH) {
         const int t = e / kCB, cc = e - t * kCB;
         float x = 0.f;
         if (t < cr.len) {
@@ -167,10 +171,10 @@ __device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, cons
 // Stage channels [cb, cb+kCB) of the log-decay (gate from f if flagged) and
 // form their in-chunk cumulative sums.  Also returns, in graw (nullable), the
 // per-token log-decay itself.  Ends with a barrier.
-template <int DK>
+template <int DK, int NTH>
 __device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw) {
     const bool gate = p.flags & 2u;
-    for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+    for (int e = threadIdx.x; e < kChunk * kCB; e += NTH) {
         const int t = e / kCB, cc = e - t * kCB;
         float x = 0.f;
         if (t < cr.len) {
@@ -192,25 +196,27 @@ __device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, 
     __syncthreads();
 }
 
-// Inverse L2 norms of the raw rows of q or k (4 threads per token).
-template <int DK, typename TIn>
+// Inverse L2 norms of the raw rows of q or k (NTH / 64 threads per token).
+template <int DK, typename TIn, int NTH>
 __device__ __forceinline__ void row_rnorm(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, float* rn) {
-    const int t = threadIdx.x >> 2, part = threadIdx.x & 3;
+    constexpr int PT = NTH / kChunk;
+    static_assert(PT == 4 || PT == 8, "threads per token");
+    const int t = threadIdx.x / PT, part = threadIdx.x % PT;
     float ss = 0.f;
     if (t < cr.len) {
         const size_t base = tok_index(cr.t0 + t, h, H, DK);
-        for (int c = part; c < DK; c += 4) {
+        for (int c = part; c < DK; c += PT) {
             const float x = Elem<TIn>::load(src, base + c);
             ss += x * x;
         }
     }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
+#pragma unroll
+    for (int off = 1; off < PT; off <<= 1) ss += __shfl_xor(ss, off, 64);
     if (part == 0) rn[t] = 1.0f / sqrtf(ss + kL2Eps);
 }
 
 template <int DK, int DV, typename TIn, typename TOut>
-__global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
+__global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     constexpr int LC = kCB + 4, NB = DK / kCB, NG = DK / 16;
     __shared__ float Tm[kChunk * kLD];   // T, later dAqk^T
     __shared__ float dT[kChunk * kLD];
@@ -226,9 +232,9 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     __shared__ float X3[kChunk * LC];
     __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
     __shared__ float dbw_part[kChunk * NG];
-    __shared__ float wpart[kWaves * kChunk];   // per-wave row partials
+    __shared__ float wpart[kGWaves * kChunk];   // per-wave row partials
     __shared__ float dbA[kChunk], dotq[kChunk], dotk[kChunk];
-    __shared__ float pa_part[kWaves * NB];
+    __shared__ float pa_part[kGWaves * NB];
     __shared__ float dgl[DK];
 
     const int c = blockIdx.x, h = blockIdx.y;
@@ -246,7 +252,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
         const float* tmi = p.tm + slot * kChunk * kChunk;
         const float* dti = p.dtv + slot * kChunk * kChunk;
         const float* dai = p.daq + slot * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) {
             const int idx = (e >> 6) * kLD + (e & 63);
             Tm[idx] = tmi[e];
             dT[idx] = dti[e];
@@ -267,18 +273,18 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     if (threadIdx.x < DK) dgl[threadIdx.x] = p.dgl[slot * DK + threadIdx.x];
     __syncthreads();
     if (l2) {
-        row_rnorm<DK, TIn>(qin, cr, h, p.H, rnq);
-        row_rnorm<DK, TIn>(kin, cr, h, p.H, rnk);
+        row_rnorm<DK, TIn, kGThreads>(qin, cr, h, p.H, rnq);
+        row_rnorm<DK, TIn, kGThreads>(kin, cr, h, p.H, rnk);
     }
     __syncthreads();
 
     // ---- phase 3: dT += dw (beta Kg)^T ; dKg = beta . (T^T dw) ; dbeta_w
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        stage_qk_block<DK, TIn>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
-        stage_g_block<DK>(p, cr, h, cb, GTb, nullptr);  // barrier inside covers KTb
+        stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr);  // barrier inside covers KTb
         const float* dwi = p.dwv + slot * kChunk * DK;
-        for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+        for (int e = threadIdx.x; e < kChunk * kCB; e += kGThreads) {
             const int t = e / kCB, cc = e - t * kCB;
             X1[t * LC + cc] = dwi[t * DK + cb + cc];
             const float kg = KTb[cc * kLD + t] * __expf(GTb[cc * kLD + t]);
@@ -288,7 +294,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
         __syncthreads();
         {
             constexpr int TILES = 16;  // 64 x 64 tiles of dT
-            for (int tile = wave; tile < TILES; tile += kWaves) {
+            for (int tile = wave; tile < TILES; tile += kGWaves) {
                 const int tm = tile >> 2, tn = tile & 3;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma16_f32(X1 + tm * 16 * LC, LC, 1, QTb + tn * 16, kLD, 1, 0, kCB, acc);
@@ -300,7 +306,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
             }
             constexpr int TN = kCB / 16, T2 = (kChunk / 16) * TN;
             float* dkt = p.dkt + slot * kChunk * DK;
-            for (int tile = wave; tile < T2; tile += kWaves) {
+            for (int tile = wave; tile < T2; tile += kGWaves) {
                 const int tm = tile / TN, tn = tile % TN;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma16_f32(Tm + tm * 16, 1, kLD, X1 + tn * 16, LC, 1, 16 * tm, kChunk, acc);
@@ -318,7 +324,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
 
     // ---- phase 4: Y = dT T^T ; dA = -T^T Y (strictly lower)
     {
-        for (int tile = wave; tile < 16; tile += kWaves) {
+        for (int tile = wave; tile < 16; tile += kGWaves) {
             const int tm = tile >> 2, tn = tile & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma16_f32(dT + tm * 16 * kLD, kLD, 1, Tm + tn * 16 * kLD, 1, kLD, 0, 16 * (tn + 1), acc);
@@ -326,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
             for (int i = 0; i < 4; ++i) Y[(tm * 16 + 4 * (lane >> 4) + i) * kLD + tn * 16 + (lane & 15)] = acc[i];
         }
         __syncthreads();
-        for (int tile = wave; tile < 16; tile += kWaves) {
+        for (int tile = wave; tile < 16; tile += kGWaves) {
             const int tm = tile >> 2, tn = tile & 3;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (tn <= tm) acc = mma16_f32(Tm + tm * 16, 1, kLD, Y + tn * 16, kLD, 1, 16 * tm, kChunk, acc);
@@ -338,7 +344,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
         }
         __syncthreads();
         // transposed copies for the row-side pair sums (lanes run over t)
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
+        for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) {
             const int t = e >> 6, s = e & 63;
             Y[s * kLD + t] = dA[t * kLD + s];
             Tm[s * kLD + t] = dAq[t * kLD + s];
@@ -353,39 +359,41 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     float r_dbA = 0.f, r_dq = 0.f, r_dk = 0.f;  // per-row partials of this wave
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        stage_qk_block<DK, TIn>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
-        stage_qk_block<DK, TIn>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        stage_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
+        stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
         {
             const float* a1 = p.dqt + slot * kChunk * DK;
             const float* a2 = p.dkh + slot * kChunk * DK;
             const float* a3 = p.dkt + slot * kChunk * DK;
-            for (int e = threadIdx.x; e < kChunk * kCB; e += kThreads) {
+            for (int e = threadIdx.x; e < kChunk * kCB; e += kGThreads) {
                 const int tt = e / kCB, cc = e - tt * kCB;
                 X1[tt * LC + cc] = a1[tt * DK + cb + cc];
                 X2[tt * LC + cc] = a2[tt * DK + cb + cc];
                 X3[tt * LC + cc] = a3[tt * DK + cb + cc];
             }
         }
-        stage_g_block<DK>(p, cr, h, cb, GTb, GRb);  // ends with a barrier
-        for (int cc = wave; cc < kCB; cc += kWaves) {
+        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, GRb);  // ends with a barrier
+        for (int cc = wave; cc < kCB; cc += kGWaves) {
             const float gt = GTb[cc * kLD + t];
             const float kt = KTb[cc * kLD + t];
             const float qt = QTb[cc * kLD + t];
             // pair sums: rows (partner s <= t) and columns (partner s >= t)
+            // One exp per pair, of the non-positive difference: e^{G_t - G_s} for
+            // s <= t, e^{G_s - G_t} for s >= t.  dA, dAq are zero outside their
+            // triangles (dA strictly lower, dAq lower), so every product below
+            // only counts on its own side of the diagonal and no branch is needed.
             float rk = 0.f, rq = 0.f, ck = 0.f, cq = 0.f;
+#pragma unroll 4
             for (int s = 0; s < kChunk; ++s) {
                 const float gs = GTb[cc * kLD + s];
                 const float ks = KTb[cc * kLD + s];
-                if (s <= t) {
-                    const float e = __expf(gt - gs) * ks;
-                    rk += Y[s * kLD + t] * e;   // dA[t][s]
-                    rq += Tm[s * kLD + t] * e;  // scale dAqk[t][s]
-                }
-                if (s >= t) {
-                    const float e = __expf(gs - gt);
-                    ck += bet[s] * dA[s * kLD + t] * ks * e;
-                    cq += dAq[s * kLD + t] * QTb[cc * kLD + s] * e;
-                }
+                const float x = gt - gs;
+                const float e = exp_hw(s <= t ? x : -x);
+                const float ek = e * ks;
+                rk = fmaf(Y[s * kLD + t], ek, rk);    // dA[t][s]
+                rq = fmaf(Tm[s * kLD + t], ek, rq);   // scale dAqk[t][s]
+                ck = fmaf(bet[s] * dA[s * kLD + t], ek, ck);
+                cq = fmaf(dAq[s * kLD + t] * QTb[cc * kLD + s], e, cq);
             }
             const float gam = __expf(gt);
             const float gl_c = GTb[cc * kLD + last];
@@ -444,7 +452,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     __syncthreads();
     if (threadIdx.x < kChunk) {
         float acc = 0.f;
-        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        for (int w = 0; w < kGWaves; ++w) acc += wpart[w * kChunk + t];
         dbA[t] = acc;
     }
     __syncthreads();
@@ -452,7 +460,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     __syncthreads();
     if (threadIdx.x < kChunk) {
         float acc = 0.f;
-        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        for (int w = 0; w < kGWaves; ++w) acc += wpart[w * kChunk + t];
         dotq[t] = acc;
     }
     __syncthreads();
@@ -460,7 +468,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     __syncthreads();
     if (threadIdx.x < kChunk) {
         float acc = 0.f;
-        for (int w = 0; w < kWaves; ++w) acc += wpart[w * kChunk + t];
+        for (int w = 0; w < kGWaves; ++w) acc += wpart[w * kChunk + t];
         dotk[t] = acc;
         if (t < cr.len) {
             float db = p.dbv[slot * kChunk + t] + dbA[t];
@@ -471,13 +479,13 @@ __global__ void __launch_bounds__(kThreads) bwd_dk_kernel(Prm p) {
     }
     if (gate && threadIdx.x == 0) {
         float acc = 0.f;
-        for (int w = 0; w < kWaves; ++w) acc += pa_part[w];
+        for (int w = 0; w < kGWaves; ++w) acc += pa_part[w];
         p.part_a[slot] = acc;
     }
     if (l2) {
         __syncthreads();
         // dx = r (dx^ - (x^ . dx^) x^), x^ the normalised row
-        for (int e = threadIdx.x; e < cr.len * DK; e += kThreads) {
+        for (int e = threadIdx.x; e < cr.len * DK; e += kGThreads) {
             const int tt = e / DK, cc = e - tt * DK;
             const size_t gi = tok_index(cr.t0 + tt, h, p.H, DK) + cc;
             const float qh = Elem<TIn>::load(qin, gi) * rnq[tt];
@@ -547,9 +555,9 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
             KDA_LAUNCH("bwd_chunk", (bwd_chunk_kernel<DV, TIn, TOut, P>), dim3(a.n_chunks_bound, a.H), dim3(kBcThreads),
                        s, p);
         } else {
-            KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+            KDA_LAUNCH("bwd_dv", (bwd_dv_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kGThreads), s,
                        p);
-            KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+            KDA_LAUNCH("bwd_dk", (bwd_dk_kernel<DK, DV, TIn, TOut>), dim3(a.n_chunks_bound, a.H), dim3(kGThreads), s,
                        p);
         }
     }

@@ -262,12 +262,12 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L);
 hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s);
 
 // Register-resident accumulators for the 16x16 tiles of an M x N result that
-// this wave owns (tile = wave + i * kWaves), so several products can be
+// this wave owns (tile = wave + i * NW, NW waves), so several products can be
 // accumulated over blocks of their contraction index without LDS traffic.
-template <int M, int N>
+template <int M, int N, int NW = kWaves>
 struct TileSet {
     static constexpr int TN = N / 16, TILES = (M / 16) * TN;
-    static constexpr int PER = (TILES + kWaves - 1) / kWaves;
+    static constexpr int PER = (TILES + NW - 1) / NW;
     f32x4 acc[PER];
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -278,7 +278,7 @@ struct TileSet {
         const int wave = wave_id();
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int tile = wave + i * kWaves;
+            const int tile = wave + i * NW;
             if (tile < TILES) {
                 const int tm = tile / TN, tn = tile % TN;
                 acc[i] = mma16_f32(A + tm * 16 * am, am, ak, B + tn * 16 * bn, bk, bn, 0, K, acc[i]);
@@ -290,7 +290,7 @@ struct TileSet {
         const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int tile = wave + i * kWaves;
+            const int tile = wave + i * NW;
             if (tile < TILES) {
                 const int tm = tile / TN, tn = tile % TN;
 #pragma unroll
