@@ -169,30 +169,37 @@ __device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, cons
 }
 
 // Stage channels [cb, cb+kCB) of the log-decay (gate from f if flagged) and
-// form their in-chunk cumulative sums.  Also returns, in graw (nullable), the
-// per-token log-decay itself.  Ends with a barrier.
+// form their in-chunk cumulative sums into GT[c][t].  Also returns, in graw
+// (nullable), the per-token log-decay itself.  Thread (sg, c) = (tid >> 5,
+// tid & 31) loads R consecutive tokens of channel c (coalesced rows), scans
+// them in registers and adds the totals of the earlier segments (seg: LDS
+// [64 / R][32]).  Ends with a barrier.
 template <int DK, int NTH>
-__device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw) {
+__device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw,
+                                              float* seg) {
+    constexpr int R = kChunk * kCB / NTH, NS = kChunk / R;
     const bool gate = p.flags & 2u;
-    for (int e = threadIdx.x; e < kChunk * kCB; e += NTH) {
-        const int t = e / kCB, cc = e - t * kCB;
-        float x = 0.f;
-        if (t < cr.len) {
-            x = p.g[tok_index(cr.t0 + t, h, p.H, DK) + cb + cc];
-            if (gate) x = -expf(p.A_log[h]) * softplus_f(x + p.dt_bias[h * DK + cb + cc]);
-        }
-        GT[cc * kLD + t] = x;
-        if (graw) graw[cc * kLD + t] = x;
+    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    const float nA = gate ? -expf(p.A_log[h]) : 0.f;
+    const float db = gate ? p.dt_bias[h * DK + cb + c] : 0.f;
+    float x[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int t = R * sg + i;
+        const int tc = t < cr.len ? t : 0;
+        const float v = p.g[tok_index(cr.t0 + tc, h, p.H, DK) + cb + c];
+        x[i] = t < cr.len ? (gate ? nA * softplus_f(v + db) : v) : 0.f;
+        if (graw) graw[c * kLD + t] = x[i];
     }
+#pragma unroll
+    for (int i = 1; i < R; ++i) x[i] += x[i - 1];
+    seg[sg * 32 + c] = x[R - 1];
     __syncthreads();
-    if (threadIdx.x < kCB) {
-        const int cc = threadIdx.x;
-        float acc = 0.f;
-        for (int t = 0; t < kChunk; ++t) {
-            acc += GT[cc * kLD + t];
-            GT[cc * kLD + t] = acc;
-        }
-    }
+    float off = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) off += j < sg ? seg[j * 32 + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) GT[c * kLD + R * sg + i] = x[i] + off;
     __syncthreads();
 }
 
@@ -236,6 +243,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     __shared__ float dbA[kChunk], dotq[kChunk], dotk[kChunk];
     __shared__ float pa_part[kGWaves * NB];
     __shared__ float dgl[DK];
+    __shared__ float gseg[kChunk * kCB / (kChunk * kCB / kGThreads)];  // column-scan segment totals
 
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
@@ -282,7 +290,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
         stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
-        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr);  // barrier inside covers KTb
+        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // barrier inside covers KTb
         const float* dwi = p.dwv + slot * kChunk * DK;
         for (int e = threadIdx.x; e < kChunk * kCB; e += kGThreads) {
             const int t = e / kCB, cc = e - t * kCB;
@@ -372,29 +380,51 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                 X3[tt * LC + cc] = a3[tt * DK + cb + cc];
             }
         }
-        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, GRb);  // ends with a barrier
-        for (int cc = wave; cc < kCB; cc += kGWaves) {
-            const float gt = GTb[cc * kLD + t];
-            const float kt = KTb[cc * kLD + t];
-            const float qt = QTb[cc * kLD + t];
-            // pair sums: rows (partner s <= t) and columns (partner s >= t)
-            // One exp per pair, of the non-positive difference: e^{G_t - G_s} for
-            // s <= t, e^{G_s - G_t} for s >= t.  dA, dAq are zero outside their
-            // triangles (dA strictly lower, dAq lower), so every product below
-            // only counts on its own side of the diagonal and no branch is needed.
-            float rk = 0.f, rq = 0.f, ck = 0.f, cq = 0.f;
+        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, GRb, gseg);  // ends with a barrier
+        // Pair sums, rows (partner s <= t) and columns (partner s >= t), for this
+        // wave's CPW channels at once: lane = token t; the partner's values come
+        // from lane s by readlane, and the four dA entries of (t, s) and (s, t)
+        // are read once per partner for all channels.  One exp per pair, of the
+        // non-positive difference: e^{G_t - G_s} for s <= t, e^{G_s - G_t} for
+        // s >= t.  dA, dAq are zero outside their triangles (dA strictly lower,
+        // dAq lower), so every product only counts on its own side of the
+        // diagonal and no branch is needed.
+        constexpr int CPW = kCB / kGWaves;
+        float gtv[CPW], ktv[CPW], qtv[CPW], rkv[CPW], rqv[CPW], ckv[CPW], cqv[CPW];
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int cc = wave + kGWaves * j;
+            gtv[j] = GTb[cc * kLD + t];
+            ktv[j] = KTb[cc * kLD + t];
+            qtv[j] = QTb[cc * kLD + t];
+            rkv[j] = rqv[j] = ckv[j] = cqv[j] = 0.f;
+        }
+        {
+            const float btl = bet[t];
 #pragma unroll 4
             for (int s = 0; s < kChunk; ++s) {
-                const float gs = GTb[cc * kLD + s];
-                const float ks = KTb[cc * kLD + s];
-                const float x = gt - gs;
-                const float e = exp_hw(s <= t ? x : -x);
-                const float ek = e * ks;
-                rk = fmaf(Y[s * kLD + t], ek, rk);    // dA[t][s]
-                rq = fmaf(Tm[s * kLD + t], ek, rq);   // scale dAqk[t][s]
-                ck = fmaf(bet[s] * dA[s * kLD + t], ek, ck);
-                cq = fmaf(dAq[s * kLD + t] * QTb[cc * kLD + s], e, cq);
+                const float ad_ts = Y[s * kLD + t], aq_ts = Tm[s * kLD + t];  // dA[t][s], scale dAqk[t][s]
+                const float ad_st = dA[s * kLD + t], aq_st = dAq[s * kLD + t];  // dA[s][t], scale dAqk[s][t]
+                const float bad = lane_value(btl, s) * ad_st;                  // beta_s dA[s][t]
+                const bool lower = s <= t;
+#pragma unroll
+                for (int j = 0; j < CPW; ++j) {
+                    const float gs = lane_value(gtv[j], s), ks = lane_value(ktv[j], s), qs = lane_value(qtv[j], s);
+                    const float x = gtv[j] - gs;
+                    const float e = exp_hw(lower ? x : -x);
+                    const float ek = e * ks;
+                    rkv[j] = fmaf(ad_ts, ek, rkv[j]);
+                    rqv[j] = fmaf(aq_ts, ek, rqv[j]);
+                    ckv[j] = fmaf(bad, ek, ckv[j]);
+                    cqv[j] = fmaf(aq_st * qs, e, cqv[j]);
+                }
             }
+        }
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int cc = wave + kGWaves * j;
+            const float gt = gtv[j], kt = ktv[j], qt = qtv[j];
+            const float rk = rkv[j], rq = rqv[j], ck = ckv[j], cq = cqv[j];
             const float gam = __expf(gt);
             const float gl_c = GTb[cc * kLD + last];
             const float eL = __expf(gl_c - gt);
@@ -535,6 +565,10 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
     if constexpr (DK == 32 && DV == 64) {
         // every array the dk = 32 backward reads or writes must be in the workspace layout
         if (!p.tm || !p.hs || !p.dhs || !p.aqT || !p.pmT || !p.qhT || !p.part_a || !p.part_dt)
+            return hipErrorInvalidValue;
+    } else {
+        // the reverse scan's operands (written by the intra-chunk kernel) and its outputs
+        if (!p.tm || !p.hs || !p.vn || !p.dhs || !p.dvn || !p.aqT || !p.khb || !p.qgT || !p.wT)
             return hipErrorInvalidValue;
     }
     if (!(a.flags & (1u << 4))) {  // no forward saved in ws: recompute it

@@ -26,6 +26,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // value: tile and row offsets derived from it stay in SGPRs instead of being
 // recomputed per lane.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// x of lane s of this wave (s wave-uniform), as a scalar
+__device__ __forceinline__ float lane_value(float x, int s) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
+}
 
 // ----------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {

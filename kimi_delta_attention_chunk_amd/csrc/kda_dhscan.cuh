@@ -1,17 +1,25 @@
-// kda_dhscan.cuh -- the sequential part of the backward: the state gradient.
+// kda_dhscan.cuh -- the sequential part of the backward: the state gradient
+// (dk = 64 and 128; dk = 32 uses the affine form in kda_pscan.cuh).
 //
-// One workgroup per (sequence, head, BV columns of the state: 32 for dk <= 64,
-// 16 for dk = 128 so that the operand tiles fit the 160 KB of LDS), chunks in
+// One workgroup per (sequence, head, BV columns of the state), chunks in
 // reverse.  With D = dL/dS at the end of the chunk (dhT, or 0, at the end of
 // the sequence), per chunk:
-//   dv_new = scale Aqk^T dO + Kh D                       (64 x 32)
+//   dv_new = scale Aqk^T dO + Kh D                       (64 x BV)
 //   D     <- scale (exp(G) q)^T dO + Diag(exp G_L) D - w^T dv_new
 // (the reverse of v_new = u - w h, o = scale (Qg h + Aqk v_new),
 // h' = Diag(exp G_L) h + Kh^T v_new).  D at every chunk end and dv_new are
-// stored for the per-chunk gradient kernel; D after the first chunk is dh0.
-// Operands come from the intra-chunk kernel (aqk, khT, qg, w, gl) and from dO,
-// loaded one chunk ahead into registers, then transposed into MFMA tiles.
-// The fp32 D stays in the registers of the lanes that own its tiles.
+// stored for the per-chunk gradient kernels; D after the first chunk is dh0.
+//
+// Every state-independent operand is an MFMA A fragment loaded straight from
+// the k-block arrays the intra-chunk kernel writes for the reverse pass --
+// Aqk^T and Kh (rows t), (exp(G) q)^T and w^T (rows c) -- two chunks ahead,
+// double buffered, as in the forward scan.  Only dO^T, D^T and dv_new^T pass
+// through LDS: the fp32 D stays in the registers of the lanes that own its
+// 16x16 tiles.  dO^T of the next chunk is staged during the current one (its
+// values arrive with the operand batch of the chunk before), so a chunk costs
+// two barriers.
+// BV = 32 (dk = 64): every wave forms one dv_new tile and one D tile.  BV = 16
+// (dk = 128): four dv_new tiles on waves 0-3, eight D tiles on all waves.
 #pragma once
 
 #include "kda_chunk.cuh"
@@ -21,90 +29,74 @@ namespace kda {
 
 constexpr int kDhThreads = 512, kDhWaves = 8;  // two waves per SIMD
 
-// One chunk's operands, as loaded: 8-value chunks of the k-block arrays
-// (kda_mma.cuh) -- w, exp(G) q [t][c], (k exp(G_L - G))^T [c][t] and Aqk [t][s] --
-// plus dO and exp(G_L).
-template <int DK, int BV, typename TIn, Prec P>
-struct DhRegs {
-    static constexpr int TN = BV / 16;                                          // 16-column tiles of the block
-    static constexpr int CW = (kChunk * DK / 8 + kDhThreads - 1) / kDhThreads;  // chunks of w, qg, khT
-    static constexpr int CA = kChunk * kChunk / 8 / kDhThreads;                 // chunks of aqk
-    static constexpr int HPW = ((DK / 16) * TN + kDhWaves - 1) / kDhWaves;      // D tiles per wave
-    static constexpr int ND = BV / 8;                                           // dO values per thread
-    KChunk<P> w[CW], q[CW], k[CW], a[CA];
-    float d[ND];  // dO[t][jb + ND part + i] for t = tid >> 3
-    float g[4 * HPW];
+template <int DK, int BV, Prec P>
+struct DhFrags {
+    static constexpr int KB = DK / 32;
+    static constexpr int TN = BV / 16;                             // 16-column tiles of the block
+    static constexpr int VT = 4 * TN;                              // dv_new tiles (64 x BV)
+    static constexpr int TH = (DK / 16) * TN;                      // D tiles (DK x BV)
+    static constexpr int HPW = (TH + kDhWaves - 1) / kDhWaves;     // D tiles per wave
+    static constexpr int ND = BV / 8;                              // dO values per thread
+    static_assert(VT <= kDhWaves, "one dv_new tile per wave");
+    AFrag<P> aq[2], kh[KB];          // Aqk^T, Kh rows of this wave's dv_new tile
+    AFrag<P> qt[HPW][2], wt[HPW][2]; // (exp(G) q)^T, w^T rows of its D tiles
+    float g[4 * HPW];                // exp(G_L) at its D rows
+    float d[ND];                     // dO of the chunk processed after this one
 };
 
+// Operands of chunk slot `slot` and dO of the chunk `crd` (the one processed
+// next, or a clamped repeat).  Every load is unconditional.
 template <int DK, int DV, int BV, typename TIn, Prec P>
-__device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb,
-                                        DhRegs<DK, BV, TIn, P>& R) {
-    using Rg = DhRegs<DK, BV, TIn, P>;
-    const int tid = threadIdx.x, wave = wave_id();
-    const char* w = (const char*)(p.w + slot * kChunk * DK);
-    const char* q = (const char*)(p.qg + slot * kChunk * DK);
-    const char* k = (const char*)(p.khT + slot * DK * kChunk);
-    const char* a = (const char*)(p.aqk + slot * kChunk * kChunk);
+__device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& crd, int h, int jb,
+                                        DhFrags<DK, BV, P>& R) {
+    using F = DhFrags<DK, BV, P>;
+    const int wave = wave_id(), lr = threadIdx.x & 15, tid = threadIdx.x;
+    const int vt = wave < F::VT ? wave : 0, tm = vt / F::TN;
+    const char* aq = (const char*)(p.aqT + slot * kChunk * kChunk);  // [t][2]
+    const char* kh = (const char*)(p.khb + slot * kChunk * DK);      // [t][DK/32]
+    const char* qt = (const char*)(p.qgT + slot * DK * kChunk);      // [c][2]
+    const char* wt = (const char*)(p.wT + slot * DK * kChunk);       // [c][2]
+    const int row = 16 * tm + lr;
 #pragma unroll
-    for (int i = 0; i < Rg::CW; ++i) {
-        const int c8 = tid + kDhThreads * i;
-        if (c8 < kChunk * DK / 8) {
-            const int t = c8 / (DK / 8), k0 = 8 * (c8 % (DK / 8));  // w, qg: row t, index k0
-            load_kchunk(R.w[i], w + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, (k0 >> 3) & 3);
-            load_kchunk(R.q[i], q + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, (k0 >> 3) & 3);
-            const int cc = c8 >> 3, t0 = 8 * (c8 & 7);                // khT: row c, index t0
-            load_kchunk(R.k[i], k + (size_t)(cc * 2 + (t0 >> 5)) * kKBlockBytes, (t0 >> 3) & 3);
+    for (int kb = 0; kb < 2; ++kb) load_afrag(R.aq[kb], aq + (size_t)(row * 2 + kb) * kKBlockBytes);
+#pragma unroll
+    for (int kb = 0; kb < F::KB; ++kb) load_afrag(R.kh[kb], kh + (size_t)(row * F::KB + kb) * kKBlockBytes);
+#pragma unroll
+    for (int i = 0; i < F::HPW; ++i) {
+        const int tile = wave + kDhWaves * i;
+        const int c16 = 16 * ((tile < F::TH ? tile : 0) / F::TN);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            load_afrag(R.qt[i][kb], qt + (size_t)((c16 + lr) * 2 + kb) * kKBlockBytes);
+            load_afrag(R.wt[i][kb], wt + (size_t)((c16 + lr) * 2 + kb) * kKBlockBytes);
         }
-    }
 #pragma unroll
-    for (int i = 0; i < Rg::CA; ++i) {
-        const int c8 = tid + kDhThreads * i;
-        const int t = c8 >> 3, s0 = 8 * (c8 & 7);
-        load_kchunk(R.a[i], a + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, (s0 >> 3) & 3);
+        for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + c16 + frag_row(r)];
     }
-    const int t = tid >> 3, part = tid & 7;
     {
-        // rows past the chunk end read row 0 (always valid) and are zeroed
-        const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DV) + jb + Rg::ND * part;
-        if constexpr (Rg::ND == 4) {
+        // dO rows t = tid >> 3, columns jb + ND part ..; rows past the end read row 0 and are zeroed
+        const int t = tid >> 3, part = tid & 7;
+        const TIn* src = (const TIn*)p.d_o + tok_index(crd.t0 + (t < crd.len ? t : 0), h, p.H, DV) + jb + F::ND * part;
+        if constexpr (F::ND == 4) {
             load4<TIn>(src, R.d);
         } else {
 #pragma unroll
-            for (int i = 0; i < Rg::ND; ++i) R.d[i] = Elem<TIn>::load(src, i);
+            for (int i = 0; i < F::ND; ++i) R.d[i] = Elem<TIn>::load(src, i);
         }
 #pragma unroll
-        for (int i = 0; i < Rg::ND; ++i) R.d[i] = t < cr.len ? R.d[i] : 0.f;
-    }
-    constexpr int TH = (DK / 16) * Rg::TN;
-#pragma unroll
-    for (int i = 0; i < Rg::HPW; ++i) {
-        const int tile = wave + kDhWaves * i;
-        if (tile < TH) {
-            const int tm = tile / Rg::TN;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + tm * 16 + frag_row(r)];
-        }
+        for (int i = 0; i < F::ND; ++i) R.d[i] = t < crd.len ? R.d[i] : 0.f;
     }
 }
 
 template <int DK, int DV, int BV, typename TIn, Prec P>
 __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int total_wg) {
-    using Rg = DhRegs<DK, BV, TIn, P>;
-    constexpr int LK = DK + 8, LA = kChunk + 8, NV = DV / BV, TN = Rg::TN;
-    constexpr int TH = (DK / 16) * TN, VT = 4 * TN;  // D tiles; dv_new tiles (64 x BV)
-    static_assert(VT <= kDhWaves, "one dv_new tile per wave");
-    constexpr int HPW = Rg::HPW;
-    constexpr int NTH = kDhThreads, NWV = kDhWaves;
-    __shared__ __attribute__((aligned(16))) float sAq[kChunk * LA];   // Aqk^T [t][s]
-    __shared__ __attribute__((aligned(16))) float sKh[kChunk * LK];   // Kh [t][c]
-    __shared__ __attribute__((aligned(16))) float sQ[DK * LA];        // Qg^T [c][t]
-    __shared__ __attribute__((aligned(16))) float sW[DK * LA];        // w^T [c][t]
-    __shared__ __attribute__((aligned(16))) float sO[BV * LA];        // dO^T [j][t]
-    __shared__ __attribute__((aligned(16))) float sD[2][BV * LK];     // D^T [j][c]
-    __shared__ __attribute__((aligned(16))) float sV[BV * LA];        // dv_new^T [j][t]
-    const Tile<P> AqT(sAq, kChunk, LA), Kh(sKh, kChunk, LK), QgT(sQ, DK, LA), WT(sW, DK, LA), dOT(sO, BV, LA),
+    using F = DhFrags<DK, BV, P>;
+    constexpr int LK = DK + 8, LA = kChunk + 8, NV = DV / BV, TN = F::TN, TH = F::TH, VT = F::VT, HPW = F::HPW;
+    __shared__ __attribute__((aligned(16))) float sO[2][BV * LA];  // dO^T [j][t], double buffered
+    __shared__ __attribute__((aligned(16))) float sD[2][BV * LK];  // D^T [j][c], double buffered
+    __shared__ __attribute__((aligned(16))) float sV[BV * LA];     // dv_new^T [j][t]
+    const Tile<P> dOT0(sO[0], BV, LA), dOT1(sO[1], BV, LA), DT0(sD[0], BV, LK), DT1(sD[1], BV, LK),
         dvnT(sV, BV, LA);
-    const Tile<P> DT0(sD[0], BV, LK), DT1(sD[1], BV, LK);
 
     const int lid = xcd_local_id(blockIdx.x, total_wg);
     const int vb = lid % NV, nh = lid / NV;
@@ -113,11 +105,12 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
     const int jb = vb * BV;
     const int tid = threadIdx.x, wave = wave_id();
     const float scale = p.scale;
+    const int tmv = (wave < VT ? wave : 0) / TN, tnv = (wave < VT ? wave : 0) % TN;  // this wave's dv_new tile
 
     f32x4 D[HPW];
 #pragma unroll
     for (int i = 0; i < HPW; ++i) {
-        const int tile = wave + NWV * i;
+        const int tile = wave + kDhWaves * i;
         D[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile < TH) {
             const int tm = tile / TN, tn = tile % TN, j = tn * 16 + frag_col();
@@ -132,99 +125,108 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
     int64_t s0;
     int slen;
     p.seq.seq_tokens(n, s0, slen);
-    Rg R;
-    // The prefetch is unconditional (at the first chunk it reloads it), so the
-    // control flow around it is uniform and the wait covers one chunk only.
-    if (c0 < c1) dh_load<DK, DV, BV, TIn, P>(p, (size_t)(c1 - 1) * p.H + h, SeqLayout::chunk_of(n, c1 - 1 - c0, s0, slen), h, jb, R);
-    for (int c = c1 - 1; c0 < c1 && c >= c0; --c) {
+    auto clamp = [&](int cc) { return cc >= c0 ? cc : c0; };
+    auto ref = [&](int cc) { return SeqLayout::chunk_of(n, clamp(cc) - c0, s0, slen); };
+    auto slot_of = [&](int cc) { return (size_t)clamp(cc) * p.H + h; };
+    F R[2];
+
+    // Chunk c, the i-th from the end: dO^T of c is in dOb, D^T (at its end) in Db;
+    // stages dO^T of c - 1 (in Rc.d) into dOn and D^T at the chunk start into Dn.
+    auto step = [&](int c, int i, F& Rc) {
         const size_t slot = (size_t)c * p.H + h;
-        __syncthreads();  // the previous chunk is done with the operand tiles
+        const bool odd = i & 1;
+        const Tile<P> dOb = odd ? dOT1 : dOT0, dOn = odd ? dOT0 : dOT1;
+        const Tile<P> Db = odd ? DT1 : DT0, Dn = odd ? DT0 : DT1;
+        __syncthreads();  // dO^T and D^T of this chunk staged; the previous chunk is done with dv_new^T
+        {
+            float* dhs = p.dhs + slot * DK * DV;
 #pragma unroll
-        for (int i = 0; i < Rg::CW; ++i) {
-            const int c8 = tid + NTH * i;
-            if (c8 < kChunk * DK / 8) {
-                const int t = c8 / (DK / 8), k0 = 8 * (c8 % (DK / 8));
-                put_kchunk_t(WT, k0, t, R.w[i]);   // w^T [c][t]
-                put_kchunk_t(QgT, k0, t, R.q[i]);  // Qg^T [c][t]
-                const int cc = c8 >> 3, t0 = 8 * (c8 & 7);
-                put_kchunk_t(Kh, t0, cc, R.k[i]);  // Kh [t][c]
+            for (int k = 0; k < HPW; ++k) {
+                const int tile = wave + kDhWaves * k;
+                if (tile < TH) {
+                    const int tm = tile / TN, tn = tile % TN;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dhs[(size_t)(tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[k][r];
+                }
             }
         }
-#pragma unroll
-        for (int i = 0; i < Rg::CA; ++i) {
-            const int c8 = tid + NTH * i;
-            put_kchunk_t(AqT, 8 * (c8 & 7), c8 >> 3, R.a[i]);  // Aqk^T [s][t]
-        }
-        {
-            const int t = tid >> 3, part = tid & 7;
-#pragma unroll
-            for (int i = 0; i < Rg::ND; ++i) dOT.put(Rg::ND * part + i, t, R.d[i]);
-        }
-        float gl[4 * HPW];
-#pragma unroll
-        for (int i = 0; i < 4 * HPW; ++i) gl[i] = R.g[i];
-        __syncthreads();
-        {
-            const int cn = c - 1 >= c0 ? c - 1 : c0;
-            dh_load<DK, DV, BV, TIn, P>(p, (size_t)cn * p.H + h, SeqLayout::chunk_of(n, cn - c0, s0, slen), h, jb, R);
-        }
-        const bool odd = (c1 - 1 - c) & 1;
-        const Tile<P> Db = odd ? DT1 : DT0;
-        const Tile<P> Dn = odd ? DT0 : DT1;
-        // D at the end of this chunk
-        float* dhs = p.dhs + slot * DK * DV;
-#pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + NWV * i;
-            if (tile < TH) {
-                const int tm = tile / TN, tn = tile % TN;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dhs[(size_t)(tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[i][r];
-            }
-        }
-        // dv_new = scale Aqk^T dO + Kh D
-        float* dvo = p.dvn + slot * kChunk * DV;
         if (wave < VT) {
-            const int tm = wave / TN, tn = wave % TN;
-            int k0 = 16 * tm, k1 = kChunk;
-            widen<P>(k0, k1);
+            // dv_new = scale Aqk^T dO + Kh D (Aqk^T rows 16 tm .. are zero before index 16 tm)
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-            a1 = mma_tile(AqT.sub(tm * 16), dOT.sub(tn * 16), k0, k1, a1);
-            a2 = mma_tile(Kh.sub(tm * 16), Db.sub(tn * 16), 0, DK, a2);
+            if (tmv < 2) a1 = mma_frag(Rc.aq[0], dOb.sub(tnv * 16), 0, a1);
+            a1 = mma_frag(Rc.aq[1], dOb.sub(tnv * 16), 32, a1);
+#pragma unroll
+            for (int kb = 0; kb < F::KB; ++kb) a2 = mma_frag(Rc.kh[kb], Db.sub(tnv * 16), 32 * kb, a2);
             f32x4 val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) val[r] = scale * a1[r] + a2[r];
-            const int j = tn * 16 + frag_col();
-            dvnT.put4(j, tm * 16 + frag_row(0), val);
+            const int j = tnv * 16 + frag_col();
+            dvnT.put4(j, tmv * 16 + frag_row(0), val);
+            float* dvo = p.dvn + slot * kChunk * DV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dvo[(size_t)(tm * 16 + frag_row(r)) * DV + jb + j] = val[r];
+            for (int r = 0; r < 4; ++r) dvo[(size_t)(tmv * 16 + frag_row(r)) * DV + jb + j] = val[r];
+        }
+        {
+            // dO^T of the chunk processed next
+            const int t = tid >> 3, part = tid & 7;
+#pragma unroll
+            for (int k = 0; k < F::ND; ++k) dOn.put(F::ND * part + k, t, Rc.d[k]);
         }
         __syncthreads();
         // D <- scale Qg^T dO + Diag(exp G_L) D - w^T dv_new
 #pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + NWV * i;
+        for (int k = 0; k < HPW; ++k) {
+            const int tile = wave + kDhWaves * k;
             if (tile < TH) {
                 const int tm = tile / TN, tn = tile % TN;
                 f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-                a1 = mma_tile(QgT.sub(tm * 16), dOT.sub(tn * 16), 0, kChunk, a1);
-                a2 = mma_tile(WT.sub(tm * 16), dvnT.sub(tn * 16), 0, kChunk, a2);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) D[i][r] = gl[4 * i + r] * D[i][r] + scale * a1[r] - a2[r];
-                Dn.put4(tn * 16 + frag_col(), tm * 16 + frag_row(0), D[i]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    a1 = mma_frag(Rc.qt[k][kb], dOb.sub(tn * 16), 32 * kb, a1);
+                    a2 = mma_frag(Rc.wt[k][kb], dvnT.sub(tn * 16), 32 * kb, a2);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) D[k][r] = Rc.g[4 * k + r] * D[k][r] + scale * a1[r] - a2[r];
+                Dn.put4(tn * 16 + frag_col(), tm * 16 + frag_row(0), D[k]);
+            }
+        }
+    };
+
+    if (c0 < c1) {
+        {
+            // dO^T of the last chunk, staged before the loop
+            const ChunkRef cr = ref(c1 - 1);
+            const int t = tid >> 3, part = tid & 7;
+            const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DV) + jb + F::ND * part;
+#pragma unroll
+            for (int k = 0; k < F::ND; ++k) {
+                const float x = Elem<TIn>::load(src, k);
+                dOT0.put(F::ND * part + k, t, t < cr.len ? x : 0.f);
+            }
+        }
+        // the operand batch of chunk c carries dO of chunk c - 1
+        dh_load<DK, DV, BV, TIn, P>(p, slot_of(c1 - 1), ref(c1 - 2), h, jb, R[0]);
+        dh_load<DK, DV, BV, TIn, P>(p, slot_of(c1 - 2), ref(c1 - 3), h, jb, R[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c = c1 - 1, i = 0; c >= c0; c -= 2, i += 2) {
+            step(c, i, R[0]);
+            dh_load<DK, DV, BV, TIn, P>(p, slot_of(c - 2), ref(c - 3), h, jb, R[0]);
+            if (c - 1 >= c0) {
+                step(c - 1, i + 1, R[1]);
+                dh_load<DK, DV, BV, TIn, P>(p, slot_of(c - 3), ref(c - 4), h, jb, R[1]);
             }
         }
     }
     if (p.dh0) {
 #pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-            const int tile = wave + NWV * i;
+        for (int k = 0; k < HPW; ++k) {
+            const int tile = wave + kDhWaves * k;
             if (tile < TH) {
                 const int tm = tile / TN, tn = tile % TN;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    p.dh0[((size_t)nh * DK + tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[i][r];
+                    p.dh0[((size_t)nh * DK + tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[k][r];
             }
         }
     }

@@ -37,6 +37,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.w = at(L.w);
     p.u = at(L.u); p.aqk = at(L.aqk); p.tm = at(L.tm); p.hs = at(L.hs); p.vn = at(L.vn);
     p.qg = at(L.qg); p.khT = at(L.khT); p.gl = at(L.gl);
+    p.qgT = at(L.qgT); p.khb = at(L.khb); p.wT = at(L.wT);
     p.dhs = at(L.dhs); p.dvn = at(L.dvn);
     p.dqt = at(L.dqt); p.dkh = at(L.dkh); p.dwv = at(L.dwv); p.daq = at(L.daq); p.dtv = at(L.dtv);
     p.dgl = at(L.dgl); p.dbv = at(L.dbv);
@@ -86,6 +87,10 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     take(L.gl, slots * dk);
     if (backward) {
         take(L.tm, slots * C * C);
+        take(L.aqT, slots * C * C);
+        take(L.qgT, slots * C * dk);
+        take(L.khb, slots * C * dk);
+        take(L.wT, slots * C * dk);
         take(L.dhs, slots * dk * dv);
         take(L.dvn, slots * C * dv);
         take(L.dqt, slots * C * dk);

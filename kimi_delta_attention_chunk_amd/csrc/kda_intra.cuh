@@ -79,7 +79,7 @@ __device__ __forceinline__ void gram_pair(int p, int& I, int& J) {
 __device__ __forceinline__ int kc_off(int I) { return (I - 1) * I * 8; }  // 0, 16, 48
 
 template <int DK, int DV, typename TIn, Prec P>
-__global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
+__global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two workgroups per CU
     constexpr int NB = DK / kCB32, NVB = DV / 32;
     // LDS (about 77 KB, two workgroups per CU):
     //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: BT tile and solve scratch
@@ -198,6 +198,8 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
     char* qg = (char*)(p.qg + slot * kChunk * DK);    // [t][DK/32] k-blocks
     char* khT = (char*)(p.khT + slot * DK * kChunk);  // [c][2] k-blocks
     float* KhS = Tm;                                   // (k exp(G_L - G))^T staging, [c][t], pass 1 only
+    float* QgS = Tm + kCB32 * kLD;                     // (exp(G) q)^T staging, [c][t], pass 1 only (dk >= 64)
+    const bool rev_ops = DK != 32 && p.qgT != nullptr;  // transposed operands for the reverse scan
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB32;
@@ -227,7 +229,10 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
                 const float gt = G[b][i];
                 qgv[i] = __expf(gt) * qx[b][i];
                 khv[i] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
-                if constexpr (DK != 32) KhS[cc * kLD + tr] = khv[i];
+                if constexpr (DK != 32) {
+                    KhS[cc * kLD + tr] = khv[i];
+                    if (rev_ops) QgS[cc * kLD + tr] = qgv[i];
+                }
                 const float e = __expf(gt - Gb[16 * (I >= 1 ? I : 1) * kLB + cc]);
                 kr[i] = kx[b][i] * e;
                 qr[i] = qx[b][i] * e;
@@ -241,8 +246,12 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
 #pragma unroll
             for (int J = 1; J <= 3; ++J)
                 if (tr < 16 * J) Kc.put8(kc_off(J) + tr, 8 * part, kc[J - 1]);
-            if constexpr (DK != 32)  // (dk = 32 keeps the affine form instead)
+            if constexpr (DK != 32) {  // (dk = 32 keeps the affine form instead)
                 store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
+                if (rev_ops)  // Kh rows t, channels of this block
+                    store_kblock8<WP>((char*)(p.khb + slot * kChunk * DK) + (size_t)(tr * (DK / 32) + b) * kKBlockBytes,
+                                      khv, part);
+            }
             if constexpr (DK == 32) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) khs[i] = khv[i];
@@ -260,6 +269,12 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             const f32x4 a0 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8], a1 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8 + 4];
             x[0] = a0[0]; x[1] = a0[1]; x[2] = a0[2]; x[3] = a0[3]; x[4] = a1[0]; x[5] = a1[1]; x[6] = a1[2]; x[7] = a1[3];
             store_kblock8<WP>(khT + (size_t)((cb + cr8) * 2 + (w8 >> 2)) * kKBlockBytes, x, w8 & 3);
+            if (rev_ops) {  // (exp(G) q)^T rows c, tokens as indices
+                const f32x4 b0 = *(const f32x4*)&QgS[cr8 * kLD + 8 * w8], b1 = *(const f32x4*)&QgS[cr8 * kLD + 8 * w8 + 4];
+                x[0] = b0[0]; x[1] = b0[1]; x[2] = b0[2]; x[3] = b0[3]; x[4] = b1[0]; x[5] = b1[1]; x[6] = b1[2]; x[7] = b1[3];
+                store_kblock8<WP>((char*)(p.qgT + slot * DK * kChunk) + (size_t)((cb + cr8) * 2 + (w8 >> 2)) * kKBlockBytes,
+                                  x, w8 & 3);
+            }
         }
         // off-diagonal Gram tiles
 #pragma unroll
@@ -431,6 +446,11 @@ __global__ void __launch_bounds__(kThreads) intra_kernel(Prm p) {
             if constexpr (DK == 32) {
                 pacc[kt] = acc;  // w and u go on to pass 3 only
                 continue;
+            }
+            if (rev_ops && b < NB) {  // w^T rows c, tokens as indices: four consecutive t per lane
+                const int t0 = tm * 16 + frag_row(0), cw = b * kCB32 + tn * 16 + frag_col();
+                store_kblock4<WP>((char*)(p.wT + slot * DK * kChunk) + (size_t)(cw * 2 + (t0 >> 5)) * kKBlockBytes, acc,
+                                  t0 & 31);
             }
             if (DK <= 64 && b < NB) {  // w: staged in Tm [t][c] (stride kLD), written out below
 #pragma unroll
