@@ -62,7 +62,11 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
 
     const float* tmi = p.tm + slot * kChunk * kChunk;
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
+    #pragma unroll
+    for (int e_i = 0; e_i < kChunk * kChunk / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
+        Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
+    }
     if (threadIdx.x < kChunk) {
         const int t = threadIdx.x;
         float b = 0.f;
@@ -84,12 +88,16 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     const float* dvn = p.dvn + slot * kChunk * DV;
     for (int jb = 0; jb < DV; jb += VB) {
         __syncthreads();
-        for (int e = threadIdx.x; e < DK * VB; e += kGThreads) {
+        #pragma unroll
+    for (int e_i = 0; e_i < (DK * VB) / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
             const int cc = e / VB, j = e - cc * VB;
             Hb[cc * LB + j] = hs[cc * DV + jb + j];
             Db[cc * LB + j] = dhs[cc * DV + jb + j];
         }
-        for (int e = threadIdx.x; e < kChunk * VB; e += kGThreads) {
+        #pragma unroll
+    for (int e_i = 0; e_i < (kChunk * VB) / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
             const int t = e / VB, j = e - t * VB;
             const bool in = t < cr.len;
             const size_t gi = tok_index(cr.t0 + t, h, p.H, DV) + jb + j;
@@ -157,7 +165,9 @@ constexpr int kCB = 32;  // channels per block in the dk-side kernel
 template <int DK, typename TIn, int NTH>
 __device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
                                const float* rn, float* XT) {
-    for (int e = threadIdx.x; e < kChunk * kCB; e += NTH) {
+    #pragma unroll
+    for (int e_i = 0; e_i < (kChunk * kCB) / NTH; ++e_i) {
+        const int e = threadIdx.x + e_i * NTH;
         const int t = e / kCB, cc = e - t * kCB;
         float x = 0.f;
         if (t < cr.len) {
@@ -224,7 +234,7 @@ __device__ __forceinline__ void row_rnorm(const TIn* __restrict__ src, const Chu
 
 template <int DK, int DV, typename TIn, typename TOut>
 __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
-    constexpr int LC = kCB + 4, NB = DK / kCB, NG = DK / 16;
+    constexpr int LC = kCB + 4, LS = kCB + 1, NB = DK / kCB, NG = DK / 16;
     __shared__ float Tm[kChunk * kLD];   // T, later dAqk^T
     __shared__ float dT[kChunk * kLD];
     __shared__ float dAq[kChunk * kLD];  // scale * dAqk (lower incl. diagonal)
@@ -233,7 +243,6 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     __shared__ float QTb[kCB * kLD];
     __shared__ float KTb[kCB * kLD];
     __shared__ float GTb[kCB * kLD];
-    __shared__ float GRb[kCB * kLD];     // per-token log-decay (gate chain)
     __shared__ float X1[kChunk * LC];
     __shared__ float X2[kChunk * LC];
     __shared__ float X3[kChunk * LC];
@@ -260,7 +269,9 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         const float* tmi = p.tm + slot * kChunk * kChunk;
         const float* dti = p.dtv + slot * kChunk * kChunk;
         const float* dai = p.daq + slot * kChunk * kChunk;
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) {
+        #pragma unroll
+    for (int e_i = 0; e_i < (kChunk * kChunk) / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
             const int idx = (e >> 6) * kLD + (e & 63);
             Tm[idx] = tmi[e];
             dT[idx] = dti[e];
@@ -292,7 +303,9 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
         stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // barrier inside covers KTb
         const float* dwi = p.dwv + slot * kChunk * DK;
-        for (int e = threadIdx.x; e < kChunk * kCB; e += kGThreads) {
+        #pragma unroll
+    for (int e_i = 0; e_i < (kChunk * kCB) / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
             const int t = e / kCB, cc = e - t * kCB;
             X1[t * LC + cc] = dwi[t * DK + cb + cc];
             const float kg = KTb[cc * kLD + t] * __expf(GTb[cc * kLD + t]);
@@ -352,7 +365,9 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         }
         __syncthreads();
         // transposed copies for the row-side pair sums (lanes run over t)
-        for (int e = threadIdx.x; e < kChunk * kChunk; e += kGThreads) {
+        #pragma unroll
+    for (int e_i = 0; e_i < (kChunk * kChunk) / kGThreads; ++e_i) {
+        const int e = threadIdx.x + e_i * kGThreads;
             const int t = e >> 6, s = e & 63;
             Y[s * kLD + t] = dA[t * kLD + s];
             Tm[s * kLD + t] = dAq[t * kLD + s];
@@ -365,31 +380,110 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     const int t = lane;
     float pa_acc = 0.f;               // sum of dg * g over this wave's (t, c)
     float r_dbA = 0.f, r_dq = 0.f, r_dk = 0.f;  // per-row partials of this wave
+    // Pair sums of Akk = beta_t sum_c k_t k_s e^{G_t - G_s} and Aqk = sum_c q_t k_s e^{G_t - G_s}
+    // per channel block, split by 16-token blocks:
+    //   off-diagonal blocks (I > J) as MFMA products, the decay factored through a
+    //   reference row r between the pair, e^{G_t - G_r} e^{G_r - G_s} (both at most 1):
+    //     row sums    (t in I, partners s in J)  r = 16 J + 15, the last row of J:
+    //                 P[t][c] = sum_{s in J} dA[t][s] Kt[s][c],  Kt[s][c] = k_s e^{G_r - G_s}
+    //     column sums (s in J, partners t in I)  r = 16 I, the first row of I:
+    //                 C[s][c] = sum_{t in I} dA[t][s] Kb[t][c],  Kb[t][c] = beta_t k_t e^{G_t - G_r}
+    //                 (and q_t e^{G_t - G_r} with dAq)
+    //   so one scaled operand per side serves every block pair; the results are
+    //   scaled by the other factor and gathered in LDS ([t][c]: ODk, ODq, ODc);
+    //   diagonal blocks: the exact exp of each difference, partners by DPP row
+    //   broadcast within the 16-lane row of the block.
+    float* const STa = dT;                 // Kt, then Kb      [64][LS] (dT is free after phase 4)
+    float* const STb = dT + kChunk * LS;   // Qb               [64][LS]
+    float* const ODk = X1;                 // off-diagonal row sums with dA  [t][c]
+    float* const ODq = X2;                 // off-diagonal row sums with dAq
+    float* const ODc = X3;                 // off-diagonal column sums (dA and dAq)
+    static_assert(2 * kChunk * LS <= kChunk * kLD && kChunk * LS <= kChunk * LC, "pair-sum staging must fit");
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
         stage_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
         stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        // this lane's epilogue operands (token t = lane, channels cb + wave + kGWaves j), issued
+        // now so that they arrive during the pair sums
+        constexpr int CPW = kCB / kGWaves;
+        float dq_r[CPW], dkh_r[CPW], dkt_r[CPW], f_r[CPW], db_r[CPW];
         {
-            const float* a1 = p.dqt + slot * kChunk * DK;
-            const float* a2 = p.dkh + slot * kChunk * DK;
-            const float* a3 = p.dkt + slot * kChunk * DK;
-            for (int e = threadIdx.x; e < kChunk * kCB; e += kGThreads) {
-                const int tt = e / kCB, cc = e - tt * kCB;
-                X1[tt * LC + cc] = a1[tt * DK + cb + cc];
-                X2[tt * LC + cc] = a2[tt * DK + cb + cc];
-                X3[tt * LC + cc] = a3[tt * DK + cb + cc];
+            const size_t wrow = slot * kChunk * DK + (size_t)t * DK + cb;
+            const size_t grow = tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DK) + cb;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) {
+                const int cc = wave + kGWaves * j;
+                dq_r[j] = p.dqt[wrow + cc];
+                dkh_r[j] = p.dkh[wrow + cc];
+                dkt_r[j] = p.dkt[wrow + cc];
+                f_r[j] = gate ? p.g[grow + cc] : 0.f;
+                db_r[j] = gate ? p.dt_bias[h * DK + cb + cc] : 0.f;
             }
         }
-        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, GRb, gseg);  // ends with a barrier
-        // Pair sums, rows (partner s <= t) and columns (partner s >= t), for this
-        // wave's CPW channels at once: lane = token t; the partner's values come
-        // from lane s by readlane, and the four dA entries of (t, s) and (s, t)
-        // are read once per partner for all channels.  One exp per pair, of the
-        // non-positive difference: e^{G_t - G_s} for s <= t, e^{G_s - G_t} for
-        // s >= t.  dA, dAq are zero outside their triangles (dA strictly lower,
-        // dAq lower), so every product only counts on its own side of the
-        // diagonal and no branch is needed.
-        constexpr int CPW = kCB / kGWaves;
+        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // ends with a barrier
+        // -- off-diagonal row sums
+#pragma unroll
+        for (int e_i = 0; e_i < kChunk * kCB / kGThreads; ++e_i) {
+            const int e = threadIdx.x + e_i * kGThreads;
+            const int sr = e >> 5, cc = e & 31, r = (sr | 15);
+            const float x = KTb[cc * kLD + sr] * exp_hw(GTb[cc * kLD + r] - GTb[cc * kLD + sr]);
+            STa[sr * LS + cc] = sr < 48 ? x : 0.f;
+            ODc[sr * LS + cc] = 0.f;
+            if (sr < 16) { ODk[sr * LS + cc] = 0.f; ODq[sr * LS + cc] = 0.f; }
+        }
+        __syncthreads();
+        if (wave < 6) {  // tile (I, tn), I = 1 .. 3
+            const int I = 1 + (wave >> 1), tn = wave & 1, c = 16 * tn + frag_col();
+            f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = rk;
+            for (int J = 0; J < I; ++J) {
+                f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+                pk = mma16_f32(dA + 16 * I * kLD + 16 * J, kLD, 1, STa + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pk);
+                pq = mma16_f32(dAq + 16 * I * kLD + 16 * J, kLD, 1, STa + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pq);
+                const float gr = GTb[c * kLD + 16 * J + 15];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = exp_hw(GTb[c * kLD + 16 * I + frag_row(i)] - gr);
+                    rk[i] = fmaf(e, pk[i], rk[i]);
+                    rq[i] = fmaf(e, pq[i], rq[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ODk[(16 * I + frag_row(i)) * LS + c] = rk[i];
+                ODq[(16 * I + frag_row(i)) * LS + c] = rq[i];
+            }
+        }
+        __syncthreads();
+        // -- off-diagonal column sums
+#pragma unroll
+        for (int e_i = 0; e_i < kChunk * kCB / kGThreads; ++e_i) {
+            const int e = threadIdx.x + e_i * kGThreads;
+            const int tr = e >> 5, cc = e & 31, r = tr & ~15;
+            const float x = exp_hw(GTb[cc * kLD + tr] - GTb[cc * kLD + r]);
+            STa[tr * LS + cc] = tr >= 16 ? bet[tr] * KTb[cc * kLD + tr] * x : 0.f;
+            STb[tr * LS + cc] = tr >= 16 ? QTb[cc * kLD + tr] * x : 0.f;
+        }
+        __syncthreads();
+        if (wave < 6) {  // tile (J, tn), J = 0 .. 2
+            const int J = wave >> 1, tn = wave & 1, c = 16 * tn + frag_col();
+            f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+            for (int I = J + 1; I < 4; ++I) {
+                f32x4 pk = {0.f, 0.f, 0.f, 0.f};
+                pk = mma16_f32(Y + 16 * J * kLD + 16 * I, kLD, 1, STa + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
+                pk = mma16_f32(Tm + 16 * J * kLD + 16 * I, kLD, 1, STb + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
+                const float gr = GTb[c * kLD + 16 * I];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cs[i] = fmaf(exp_hw(gr - GTb[c * kLD + 16 * J + frag_row(i)]), pk[i], cs[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ODc[(16 * J + frag_row(i)) * LS + c] = cs[i];
+        }
+        __syncthreads();
+        // -- diagonal blocks and the per-token epilogue: lane = token t, CPW channels per wave.
+        // The partner s = 16 (t >> 4) + u sits in lane u of this lane's 16-lane row.  One exp
+        // per pair, of the non-positive difference: e^{G_t - G_s} for s <= t, e^{G_s - G_t}
+        // for s >= t; dA, dAq are zero outside their triangles (dA strictly lower, dAq lower),
+        // so every product only counts on its own side of the diagonal.
         float gtv[CPW], ktv[CPW], qtv[CPW], rkv[CPW], rqv[CPW], ckv[CPW], cqv[CPW];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
@@ -401,15 +495,17 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         }
         {
             const float btl = bet[t];
-#pragma unroll 4
-            for (int s = 0; s < kChunk; ++s) {
-                const float ad_ts = Y[s * kLD + t], aq_ts = Tm[s * kLD + t];  // dA[t][s], scale dAqk[t][s]
-                const float ad_st = dA[s * kLD + t], aq_st = dAq[s * kLD + t];  // dA[s][t], scale dAqk[s][t]
-                const float bad = lane_value(btl, s) * ad_st;                  // beta_s dA[s][t]
-                const bool lower = s <= t;
+            const int sb = t & ~15, tl = t & 15;
+            static_for16([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                const int sa = sb + u;
+                const float ad_ts = Y[sa * kLD + t], aq_ts = Tm[sa * kLD + t];  // dA[t][s], scale dAqk[t][s]
+                const float ad_st = dA[sa * kLD + t], aq_st = dAq[sa * kLD + t];  // dA[s][t], scale dAqk[s][t]
+                const float bad = row_bcast<u>(btl) * ad_st;                     // beta_s dA[s][t]
+                const bool lower = u <= tl;
 #pragma unroll
                 for (int j = 0; j < CPW; ++j) {
-                    const float gs = lane_value(gtv[j], s), ks = lane_value(ktv[j], s), qs = lane_value(qtv[j], s);
+                    const float gs = row_bcast<u>(gtv[j]), ks = row_bcast<u>(ktv[j]), qs = row_bcast<u>(qtv[j]);
                     const float x = gtv[j] - gs;
                     const float e = exp_hw(lower ? x : -x);
                     const float ek = e * ks;
@@ -418,17 +514,25 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                     ckv[j] = fmaf(bad, ek, ckv[j]);
                     cqv[j] = fmaf(aq_st * qs, e, cqv[j]);
                 }
-            }
+            });
+        }
+        // this lane owns (t, its CPW channels) of the gathered sums
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int cc = wave + kGWaves * j;
+            ODk[t * LS + cc] += rkv[j];
+            ODq[t * LS + cc] += rqv[j];
+            ODc[t * LS + cc] += ckv[j] + cqv[j];
         }
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
             const int cc = wave + kGWaves * j;
-            const float gt = gtv[j], kt = ktv[j], qt = qtv[j];
-            const float rk = rkv[j], rq = rqv[j], ck = ckv[j], cq = cqv[j];
+            const float gt = GTb[cc * kLD + t], kt = KTb[cc * kLD + t], qt = QTb[cc * kLD + t];
+            const float rk = ODk[t * LS + cc], rq = ODq[t * LS + cc], ck = ODc[t * LS + cc], cq = 0.f;
             const float gam = __expf(gt);
             const float gl_c = GTb[cc * kLD + last];
             const float eL = __expf(gl_c - gt);
-            const float dqt = X1[t * LC + cc], dkh = X2[t * LC + cc], dkg = X3[t * LC + cc];
+            const float dqt = dq_r[j], dkh = dkh_r[j], dkg = dkt_r[j];
             const float bt = bet[t];
             const float kh = kt * eL;
             float dQ = rq + gam * dqt;
@@ -453,9 +557,9 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             if (gate) {
                 float dfv = 0.f;
                 if (t < cr.len) {
-                    const float x = p.g[gi] + p.dt_bias[h * DK + cb + cc];
+                    const float x = f_r[j] + db_r[j];
                     dfv = sfx * (-eA) * dsoftplus_f(x);
-                    pa_acc += sfx * GRb[cc * kLD + t];
+                    pa_acc += sfx * ((-eA) * softplus_f(x));
                 }
                 dgo = dfv;
                 const float colsum = wave_sum(dfv);
@@ -515,8 +619,11 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     if (l2) {
         __syncthreads();
         // dx = r (dx^ - (x^ . dx^) x^), x^ the normalised row
-        for (int e = threadIdx.x; e < cr.len * DK; e += kGThreads) {
+#pragma unroll 4
+        for (int e_i = 0; e_i < kChunk * DK / kGThreads; ++e_i) {
+            const int e = threadIdx.x + e_i * kGThreads;
             const int tt = e / DK, cc = e - tt * DK;
+            if (tt >= cr.len) continue;
             const size_t gi = tok_index(cr.t0 + tt, h, p.H, DK) + cc;
             const float qh = Elem<TIn>::load(qin, gi) * rnq[tt];
             const float kh = Elem<TIn>::load(kin, gi) * rnk[tt];
