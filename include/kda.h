@@ -184,6 +184,49 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
              const float* g, const float* beta, const float* A_log, const float* dt_bias,
              float* h, void* o, kda_stream_t stream);
 
+/* ----------------------------------------------------------------------------
+ * Short causal depthwise convolution, the step before KDA in its layer
+ * ("Pure KDA 300M on Primus" guide, Overview: kernel size 4, depthwise, on
+ * the concatenated q/k/v channels; Troubleshooting: [B, T, D] is the native
+ * layout; torchtitan PR #4347, description: with document offsets the window
+ * resets at every document start).  Readings: an optional bias and an
+ * optional SiLU, which the pages do not fix.
+ *   z[b,t,c] = sum_{i<W} w[c,i] x[b, t-(W-1)+i, c]  over positions of the same
+ *              document (earlier positions count as zero) + bias[c]
+ *   y        = z, or SiLU(z) with KDA_CONV_SILU
+ *   x, y       [B,T,D] dtype / out_dtype, D a multiple of 8
+ *   w          [D,W] fp32, W in 1..4; bias [D] fp32, nullable (= 0)
+ *   cu_seqlens [N+1] int32 document offsets, nullable (dense rows); needs B == 1
+ * Backward: dx [B,T,D] out_dtype; dw [D,W] and dbias [D] (nullable) fp32, sums
+ * over all tokens in a fixed order (deterministic); ws of at least
+ * kda_conv_bwd_workspace(B,T,D,W) bytes (0 = invalid sizes). */
+enum { KDA_CONV_SILU = 1u << 0 };
+int kda_conv_fwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kda_dtype out_dtype,
+                 uint32_t flags, const void* x, const float* w, const float* bias,
+                 const int32_t* cu_seqlens, int32_t N, void* y, kda_stream_t stream);
+size_t kda_conv_bwd_workspace(int32_t B, int32_t T, int32_t D, int32_t W);
+int kda_conv_bwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kda_dtype out_dtype,
+                 uint32_t flags, const void* x, const float* w, const float* bias,
+                 const int32_t* cu_seqlens, int32_t N, const void* dy, void* dx, float* dw,
+                 float* dbias, void* ws, size_t ws_bytes, kda_stream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * Gated RMS norm of the KDA output, the step after KDA in its layer (openkimi
+ * README, Profiling and H100 acceptance: the KDA output goes through a fused
+ * RMSNorm and a sigmoid gate; Primus guide, Overview: per-head output gate,
+ * RMSNorm eps 1e-6).  Per row of dv values (one token and head):
+ *   y = o (mean(o^2) + eps)^{-1/2} * weight * sigmoid(gate)
+ *   o, gate, y   [rows, dv] dtype / out_dtype (rows = B*T*H), dv in {32, 64, 128}
+ *   weight       [dv] fp32, shared by the heads (reading: one g_norm of head_v_dim)
+ * Backward: d_o, dgate [rows, dv] out_dtype; dweight [dv] fp32, a sum over all
+ * rows in a fixed order; ws of at least kda_gnorm_bwd_workspace(rows, dv) bytes. */
+int kda_gnorm_fwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype, float eps,
+                  const void* o, const void* gate, const float* weight, void* y, kda_stream_t stream);
+size_t kda_gnorm_bwd_workspace(int64_t rows, int32_t dv);
+int kda_gnorm_bwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype, float eps,
+                  const void* o, const void* gate, const float* weight, const void* dy, void* d_o,
+                  void* dgate, float* dweight, void* ws, size_t ws_bytes, kda_stream_t stream);
+
 /* Opt-in per-kernel timing for benchmarks.  kda_timing_enable(1) clears the
  * record and brackets every later kernel launch of this library with a pair
  * of hipEvents on the launch stream (enable(0) stops; pending events are
@@ -191,7 +234,8 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
  * SYNCHRONISES on them) and adds their durations to per-kernel totals, read
  * with kda_timing_count() / kda_timing_get(i, &name, &launches, &total_ms);
  * `name` stays valid until the next enable call.  Kernel names: plan, step,
- * fwd_intra, fwd_state, fwd_output, bwd_dh, bwd_dv, bwd_dk, bwd_gate_sum. */
+ * fwd_intra, fwd_scan, bwd_dh, bwd_chunk, bwd_dv, bwd_dk, bwd_gate_sum,
+ * conv_fwd, conv_bwd, conv_wsum, gnorm_fwd, gnorm_bwd, gnorm_wsum. */
 int kda_timing_enable(int on);
 int kda_timing_collect(void);
 int kda_timing_count(void);

@@ -25,7 +25,10 @@ CHUNK = 64
 EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd_workspace",
            "kda_bwd_workspace", "kda_fwd", "kda_bwd", "kda_step", "kda_status_str",
            "kda_last_error", "kda_timing_enable", "kda_timing_collect", "kda_timing_count",
-           "kda_timing_get"]
+           "kda_timing_get", "kda_conv_fwd", "kda_conv_bwd_workspace", "kda_conv_bwd", "kda_gnorm_fwd",
+           "kda_gnorm_bwd_workspace", "kda_gnorm_bwd"]
+CONV_SILU = 1
+RMS_EPS = 1e-6
 
 
 class KdaDesc(ctypes.Structure):
@@ -85,6 +88,20 @@ def load_library():
     lib.kda_timing_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
     lib.kda_timing_get.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.kda_conv_fwd.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, u32, vp, vp, vp, vp, i32, vp, vp]
+    lib.kda_conv_fwd.restype = ctypes.c_int
+    lib.kda_conv_bwd_workspace.argtypes = [i32, i32, i32, i32]
+    lib.kda_conv_bwd_workspace.restype = sz
+    lib.kda_conv_bwd.argtypes = ([i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, u32, vp, vp, vp, vp, i32]
+                                 + [vp] * 5 + [sz, vp])
+    lib.kda_conv_bwd.restype = ctypes.c_int
+    lib.kda_gnorm_fwd.argtypes = [i64, i32, ctypes.c_int, ctypes.c_int, f32, vp, vp, vp, vp, vp]
+    lib.kda_gnorm_fwd.restype = ctypes.c_int
+    lib.kda_gnorm_bwd_workspace.argtypes = [i64, i32]
+    lib.kda_gnorm_bwd_workspace.restype = sz
+    lib.kda_gnorm_bwd.argtypes = [i64, i32, ctypes.c_int, ctypes.c_int, f32] + [vp] * 8 + [sz, vp]
+    lib.kda_gnorm_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -316,4 +333,94 @@ def timing_collect() -> dict:
         ms = ctypes.c_double()
         _check(lib.kda_timing_get(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)))
         out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out
+
+
+# ---------------------------------------------------------------- short convolution
+def _conv_inputs(x, w, bias, cu_seqlens):
+    _req(x, "x", (torch.bfloat16, torch.float32))
+    if x.dim() != 3:
+        raise ValueError("x must be [B,T,D]")
+    dev = x.device
+    B, T, D = x.shape
+    _req(w, "w", torch.float32, None, dev)
+    if w.dim() != 2 or w.shape[0] != D:
+        raise ValueError("w must be [D,W]")
+    _req(bias, "bias", torch.float32, (D,), dev, optional=True)
+    N = 0
+    if cu_seqlens is not None:
+        _req(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        N = cu_seqlens.numel() - 1
+    return B, T, D, w.shape[1], N
+
+
+def conv_fwd(x, w, bias=None, cu_seqlens=None, *, silu=False, out_dtype=None):
+    """kda_conv_fwd: short causal depthwise convolution of x [B,T,D]; returns y [B,T,D]."""
+    lib = load_library()
+    B, T, D, W, N = _conv_inputs(x, w, bias, cu_seqlens)
+    out_dtype = out_dtype or x.dtype
+    y = torch.empty((B, T, D), dtype=out_dtype, device=x.device)
+    _check(lib.kda_conv_fwd(B, T, D, W, _dt(x.dtype), _dt(out_dtype), CONV_SILU if silu else 0, _ptr(x), _ptr(w),
+                            _ptr(bias), _ptr(cu_seqlens), N, _ptr(y), _stream(x.device)))
+    return y
+
+
+def conv_bwd(x, w, dy, bias=None, cu_seqlens=None, *, silu=False, out_dtype=None, need_dbias=True, workspace=None):
+    """kda_conv_bwd: returns dict dx [B,T,D], dw [D,W] fp32, dbias [D] fp32 (or None)."""
+    lib = load_library()
+    B, T, D, W, N = _conv_inputs(x, w, bias, cu_seqlens)
+    dev = x.device
+    _req(dy, "dy", x.dtype, (B, T, D), dev)
+    out_dtype = out_dtype or x.dtype
+    out = dict(dx=torch.empty((B, T, D), dtype=out_dtype, device=dev),
+               dw=torch.empty((D, W), dtype=torch.float32, device=dev),
+               dbias=torch.empty((D,), dtype=torch.float32, device=dev) if need_dbias else None)
+    need = lib.kda_conv_bwd_workspace(B, T, D, W)
+    if need == 0:
+        _check(KDA_ERR_INVALID)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.kda_conv_bwd(B, T, D, W, _dt(x.dtype), _dt(out_dtype), CONV_SILU if silu else 0, _ptr(x), _ptr(w),
+                            _ptr(bias), _ptr(cu_seqlens), N, _ptr(dy), _ptr(out["dx"]), _ptr(out["dw"]),
+                            _ptr(out["dbias"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+# ---------------------------------------------------------------- gated norm
+def _gnorm_inputs(o, gate, weight):
+    _req(o, "o", (torch.bfloat16, torch.float32))
+    dev = o.device
+    dv = o.shape[-1]
+    _req(gate, "gate", o.dtype, tuple(o.shape), dev)
+    _req(weight, "weight", torch.float32, (dv,), dev)
+    return o.numel() // dv if dv else 0, dv
+
+
+def gnorm_fwd(o, gate, weight, eps=RMS_EPS, *, out_dtype=None):
+    """kda_gnorm_fwd: y = rmsnorm(o) * weight * sigmoid(gate) over the last axis (dv)."""
+    lib = load_library()
+    rows, dv = _gnorm_inputs(o, gate, weight)
+    out_dtype = out_dtype or o.dtype
+    y = torch.empty(o.shape, dtype=out_dtype, device=o.device)
+    _check(lib.kda_gnorm_fwd(rows, dv, _dt(o.dtype), _dt(out_dtype), float(eps), _ptr(o), _ptr(gate), _ptr(weight),
+                             _ptr(y), _stream(o.device)))
+    return y
+
+
+def gnorm_bwd(o, gate, weight, dy, eps=RMS_EPS, *, out_dtype=None, workspace=None):
+    """kda_gnorm_bwd: returns dict do, dgate (shape of o) and dweight [dv] fp32."""
+    lib = load_library()
+    rows, dv = _gnorm_inputs(o, gate, weight)
+    dev = o.device
+    _req(dy, "dy", o.dtype, tuple(o.shape), dev)
+    out_dtype = out_dtype or o.dtype
+    out = dict(do=torch.empty(o.shape, dtype=out_dtype, device=dev),
+               dgate=torch.empty(o.shape, dtype=out_dtype, device=dev),
+               dweight=torch.empty((dv,), dtype=torch.float32, device=dev))
+    need = lib.kda_gnorm_bwd_workspace(rows, dv)
+    if need == 0:
+        _check(KDA_ERR_INVALID)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.kda_gnorm_bwd(rows, dv, _dt(o.dtype), _dt(out_dtype), float(eps), _ptr(o), _ptr(gate), _ptr(weight),
+                             _ptr(dy), _ptr(out["do"]), _ptr(out["dgate"]), _ptr(out["dweight"]), _ptr(ws),
+                             ws.numel(), _stream(dev)))
     return out

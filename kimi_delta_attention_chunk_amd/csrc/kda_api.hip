@@ -262,4 +262,129 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
     return KDA_OK;
 }
 
+// ---------------------------------------------------------------- short convolution
+static int conv_check(int32_t B, int32_t T, int32_t D, int32_t W, int dtype, int out_dtype, uint32_t flags,
+                      const int32_t* cu, int32_t N) {
+    if (B < 1 || T < 0 || D < 8 || D % 8 != 0)
+        return fail(KDA_ERR_INVALID, "bad sizes B=%d T=%d D=%d (D a positive multiple of 8)", B, T, D);
+    if (W < 1 || W > 4) return fail(KDA_ERR_UNSUPPORTED, "kernel width W=%d not supported (1..4)", W);
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return fail(KDA_ERR_INVALID, "bad dtype");
+    if (flags & ~(uint32_t)KDA_CONV_SILU) return fail(KDA_ERR_INVALID, "unknown flag bits 0x%x", flags);
+    if ((int64_t)B * T * D > ((int64_t)1 << 40)) return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
+    if (cu) {
+        if (B != 1) return fail(KDA_ERR_INVALID, "document offsets require B == 1 (got B=%d)", B);
+        if (N < 1) return fail(KDA_ERR_INVALID, "document offsets need N >= 1 (got N=%d)", N);
+        int rc = check_ptr(cu, "cu_seqlens", true);
+        if (rc) return rc;
+    }
+    return KDA_OK;
+}
+
+static kda::ConvArgs conv_args(int32_t B, int32_t T, int32_t D, int32_t W, int dtype, int out_dtype, uint32_t flags,
+                               const void* x, const float* w, const float* bias, const int32_t* cu, int32_t N) {
+    kda::ConvArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = B; a.T = T; a.D = D; a.W = W; a.N = cu ? N : 1;
+    a.in_bf16 = dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16; a.silu = flags & KDA_CONV_SILU;
+    a.cu = cu; a.x = x; a.w = w; a.bias = bias;
+    return a;
+}
+
+int kda_conv_fwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kda_dtype out_dtype, uint32_t flags,
+                 const void* x, const float* w, const float* bias, const int32_t* cu_seqlens, int32_t N, void* y,
+                 kda_stream_t stream) {
+    g_err[0] = 0;
+    int rc = conv_check(B, T, D, W, dtype, out_dtype, flags, cu_seqlens, N);
+    if (rc) return rc;
+    if ((rc = check_ptr(x, "x", true)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
+        (rc = check_ptr(y, "y", true)))
+        return rc;
+    kda::ConvArgs a = conv_args(B, T, D, W, dtype, out_dtype, flags, x, w, bias, cu_seqlens, N);
+    a.y = y;
+    hipError_t e = kda::launch_conv(a, false, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv_fwd launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+size_t kda_conv_bwd_workspace(int32_t B, int32_t T, int32_t D, int32_t W) {
+    if (B < 1 || T < 0 || D < 8 || D % 8 != 0 || W < 1 || W > 4) return 0;
+    const size_t n = kda::conv_bwd_workspace(B, T, D);
+    return n ? n : 256;
+}
+
+int kda_conv_bwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kda_dtype out_dtype, uint32_t flags,
+                 const void* x, const float* w, const float* bias, const int32_t* cu_seqlens, int32_t N,
+                 const void* dy, void* dx, float* dw, float* dbias, void* ws, size_t ws_bytes, kda_stream_t stream) {
+    g_err[0] = 0;
+    int rc = conv_check(B, T, D, W, dtype, out_dtype, flags, cu_seqlens, N);
+    if (rc) return rc;
+    if ((rc = check_ptr(x, "x", true)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
+        (rc = check_ptr(dy, "dy", true)) || (rc = check_ptr(dx, "dx", true)) || (rc = check_ptr(dw, "dw", true)) ||
+        (rc = check_ptr(dbias, "dbias", false)) || (rc = check_ptr(ws, "ws", true)))
+        return rc;
+    const size_t need = kda_conv_bwd_workspace(B, T, D, W);
+    if (ws_bytes < need) return fail(KDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    kda::ConvArgs a = conv_args(B, T, D, W, dtype, out_dtype, flags, x, w, bias, cu_seqlens, N);
+    a.dy = dy; a.dx = dx; a.dw = dw; a.dbias = dbias; a.part = (float*)ws;
+    hipError_t e = kda::launch_conv(a, true, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv_bwd launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+// ---------------------------------------------------------------- gated norm
+static int gnorm_check(int64_t rows, int32_t dv, int dtype, int out_dtype, float eps) {
+    if (rows < 0) return fail(KDA_ERR_INVALID, "rows=%lld must be >= 0", (long long)rows);
+    if (dv != 32 && dv != 64 && dv != 128) return fail(KDA_ERR_UNSUPPORTED, "dv=%d not supported (32, 64, 128)", dv);
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return fail(KDA_ERR_INVALID, "bad dtype");
+    if (!(eps > 0.f)) return fail(KDA_ERR_INVALID, "eps must be positive");
+    if (rows > ((int64_t)1 << 34)) return fail(KDA_ERR_UNSUPPORTED, "too many rows");
+    return KDA_OK;
+}
+
+int kda_gnorm_fwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype, float eps, const void* o,
+                  const void* gate, const float* weight, void* y, kda_stream_t stream) {
+    g_err[0] = 0;
+    int rc = gnorm_check(rows, dv, dtype, out_dtype, eps);
+    if (rc) return rc;
+    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(gate, "gate", true)) ||
+        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(y, "y", true)))
+        return rc;
+    kda::GnormArgs a;
+    memset(&a, 0, sizeof a);
+    a.rows = rows; a.dv = dv; a.in_bf16 = dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16; a.eps = eps;
+    a.o = o; a.gate = gate; a.weight = weight; a.y = y;
+    hipError_t e = kda::launch_gnorm(a, false, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "gnorm_fwd launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+size_t kda_gnorm_bwd_workspace(int64_t rows, int32_t dv) {
+    if (rows < 0 || (dv != 32 && dv != 64 && dv != 128)) return 0;
+    const size_t n = kda::gnorm_bwd_workspace(rows, dv);
+    return n ? n : 256;
+}
+
+int kda_gnorm_bwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype, float eps, const void* o,
+                  const void* gate, const float* weight, const void* dy, void* d_o, void* dgate, float* dweight,
+                  void* ws, size_t ws_bytes, kda_stream_t stream) {
+    g_err[0] = 0;
+    int rc = gnorm_check(rows, dv, dtype, out_dtype, eps);
+    if (rc) return rc;
+    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(gate, "gate", true)) ||
+        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(dy, "dy", true)) ||
+        (rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dgate, "dgate", true)) ||
+        (rc = check_ptr(dweight, "dweight", true)) || (rc = check_ptr(ws, "ws", true)))
+        return rc;
+    const size_t need = kda_gnorm_bwd_workspace(rows, dv);
+    if (ws_bytes < need) return fail(KDA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    kda::GnormArgs a;
+    memset(&a, 0, sizeof a);
+    a.rows = rows; a.dv = dv; a.in_bf16 = dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16; a.eps = eps;
+    a.o = o; a.gate = gate; a.weight = weight; a.dy = dy; a.d_o = d_o; a.dgate = dgate; a.dweight = dweight;
+    a.part = (float*)ws;
+    hipError_t e = kda::launch_gnorm(a, true, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "gnorm_bwd launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
 }  // extern "C"

@@ -86,6 +86,23 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4
 }
 
 // Load 8 consecutive elements of one token row (16-byte aligned) as fp32.
+// Store 8 consecutive fp32 values to one token row (16-byte aligned) as TOut.
+template <typename TOut>
+__device__ __forceinline__ void store8(TOut* p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
+    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&x)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+    *(u32x4*)p = v;
+}
+
 template <typename TIn>
 __device__ __forceinline__ void load8(const TIn* p, float (&x)[8]);
 template <>
@@ -142,6 +159,24 @@ __device__ __forceinline__ float sum4(float x) {
 __device__ __forceinline__ float sum8(float x) { x = sum4(x); return x + dpp_f<0x141>(x); }   // row_half_mirror
 // the 16 lanes 16m .. 16m+15 (one DPP row)
 __device__ __forceinline__ float sum16(float x) { x = sum8(x); return x + dpp_f<0x140>(x); }  // row_mirror
+// Sum over the N consecutive lanes (N = 4, 8 or 16) of this lane's group.
+template <int N>
+__device__ __forceinline__ float row_group_sum(float x) {
+    if constexpr (N == 4) return sum4(x);
+    else if constexpr (N == 8) return sum8(x);
+    else {
+        static_assert(N == 16, "groups of 4, 8 or 16 lanes");
+        return sum16(x);
+    }
+}
+// Sum over the lanes of this wave congruent to this lane modulo N (a butterfly
+// in a fixed order).
+template <int N>
+__device__ __forceinline__ float rows_of_wave_sum(float x) {
+#pragma unroll
+    for (int off = N; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
 // lanes l and l^8
 __device__ __forceinline__ float sum_x8(float x) { return x + dpp_f<0x128>(x); }  // row_ror:8
 // lanes l, l^16, l^32, l^48

@@ -20,6 +20,39 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, hipStream_t s);
 
+// Short causal depthwise convolution over [B, T, D] rows (kda_ops.hip).
+struct ConvArgs {
+    int B, T, D, W, N;
+    bool in_bf16, out_bf16, silu;
+    const int32_t* cu;  // document offsets [N + 1] (B == 1), or null
+    const void* x;
+    const float *w, *bias;
+    void* y;
+    const void* dy;
+    void* dx;
+    float *dw, *dbias;
+    float* part;  // workspace: per row-block partial sums of dw and dbias
+};
+hipError_t launch_conv(const ConvArgs& a, bool backward, hipStream_t s);
+size_t conv_bwd_workspace(int B, int T, int D);
+
+// Gated RMS norm over rows of dv values (kda_ops.hip).
+struct GnormArgs {
+    int64_t rows;
+    int dv;
+    bool in_bf16, out_bf16;
+    float eps;
+    const void *o, *gate;
+    const float* weight;
+    void* y;
+    const void* dy;
+    void *d_o, *dgate;
+    float* dweight;
+    float* part;  // workspace: per workgroup partial sums of dweight
+};
+hipError_t launch_gnorm(const GnormArgs& a, bool backward, hipStream_t s);
+size_t gnorm_bwd_workspace(int64_t rows, int dv);
+
 hipError_t launch_plan(const int32_t* cu, int N, int T, int chunk, int max_chunks,
                        int32_t* chunk_indices, int32_t* chunk_offsets, hipStream_t s);
 

@@ -31,23 +31,6 @@ namespace kda {
 constexpr int kCB32 = 32;        // channels per block
 constexpr int kLB = kCB32 + 4;   // row stride of [token][channel-block] tiles
 
-// Store 8 consecutive fp32 values to one token row (16-byte aligned) as TOut.
-template <typename TOut>
-__device__ __forceinline__ void store8(TOut* p, const float (&x)[8]);
-template <>
-__device__ __forceinline__ void store8<float>(float* p, const float (&x)[8]) {
-    *(f32x4*)p = f32x4{x[0], x[1], x[2], x[3]};
-    *(f32x4*)(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
-}
-template <>
-__device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&x)[8]) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-    *(u32x4*)p = v;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order.
 __device__ __forceinline__ float wave_scan(float x) {
     const int lane = threadIdx.x & 63;

@@ -126,3 +126,49 @@ def test_python_wrapper_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         kda.fwd(x, x, torch.zeros(1, 4, 1, 64), x, torch.zeros(1, 4, 1), 1.0)
+
+
+# ---------------------------------------------------------------- short convolution, gated norm
+def _fake(i=1):
+    return ctypes.c_void_p(0x100000 * i)  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=12), B.KDA_ERR_INVALID),
+    (dict(D=0), B.KDA_ERR_INVALID),
+    (dict(W=5), B.KDA_ERR_UNSUPPORTED),
+    (dict(W=0), B.KDA_ERR_UNSUPPORTED),
+    (dict(flags=2), B.KDA_ERR_INVALID),
+    (dict(cu=True, Bn=2), B.KDA_ERR_INVALID),
+    (dict(x=None), B.KDA_ERR_INVALID),
+    (dict(x=ctypes.c_void_p(0x100008)), B.KDA_ERR_INVALID),
+])
+def test_conv_fwd_rejects(kw, code):
+    lib = kda.load_library()
+    a = dict(Bn=1, T=64, D=64, W=4, flags=0, x=_fake(1), cu=False)
+    a.update(kw)
+    rc = lib.kda_conv_fwd(a["Bn"], a["T"], a["D"], a["W"], B.KDA_BF16, B.KDA_BF16, a["flags"], a["x"], _fake(2),
+                          None, _fake(3) if a["cu"] else None, 3, _fake(4), None)
+    assert rc == code, lib.kda_last_error()
+
+
+def test_conv_bwd_workspace_checked():
+    lib = kda.load_library()
+    need = lib.kda_conv_bwd_workspace(1, 64, 64, 4)
+    assert need > 0 and lib.kda_conv_bwd_workspace(1, 64, 12, 4) == 0
+    rc = lib.kda_conv_bwd(1, 64, 64, 4, B.KDA_BF16, B.KDA_BF16, 0, _fake(1), _fake(2), None, None, 0, _fake(3),
+                          _fake(4), _fake(5), None, _fake(6), need - 1, None)
+    assert rc == B.KDA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("rows,dv,eps,code", [(10, 48, 1e-6, B.KDA_ERR_UNSUPPORTED), (-1, 64, 1e-6, B.KDA_ERR_INVALID),
+                                              (10, 64, 0.0, B.KDA_ERR_INVALID)])
+def test_gnorm_rejects(rows, dv, eps, code):
+    lib = kda.load_library()
+    rc = lib.kda_gnorm_fwd(rows, dv, B.KDA_BF16, B.KDA_BF16, eps, _fake(1), _fake(2), _fake(3), _fake(4), None)
+    assert rc == code, lib.kda_last_error()
+    need = lib.kda_gnorm_bwd_workspace(1000, 64)
+    assert need > 0
+    rc = lib.kda_gnorm_bwd(1000, 64, B.KDA_BF16, B.KDA_BF16, 1e-6, _fake(1), _fake(2), _fake(3), _fake(4), _fake(5),
+                           _fake(6), _fake(7), _fake(8), need - 1, None)
+    assert rc == B.KDA_ERR_WORKSPACE
