@@ -337,9 +337,47 @@ def decode_workload(dev, steps=1000, B=256, H=8, dk=32, dv=64, seed=2):
             "roofline_us": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6, "cold_step_us": cold[len(cold) // 2]}
 
 
+def layer_ops_workload(dev, B=16, T=2048, H=8, dk=32, dv=64, W=4, reps=20):
+    """The two operations next to KDA in the layer, fwd+bwd at the 300M layer shape, bf16:
+    the short convolution over the concatenated q/k/v channels (D = H (2 dk + dv), kernel
+    W, SiLU) and the gated output norm over H heads of dv values.  Both are HBM-bound:
+    algorithmic bytes = every input read once and every output written once."""
+    import torch
+
+    import kimi_delta_attention_chunk_amd as kda
+
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(9)
+    D = H * (2 * dk + dv)
+    x = torch.randn(B, T, D, generator=g).to(bf).to(dev)
+    w = (torch.randn(D, W, generator=g) * 0.5).to(dev)
+    dy = torch.randn(B, T, D, generator=g).to(bf).to(dev)
+    o, gate, dyo = (torch.randn(B, T, H, dv, generator=g).to(bf).to(dev) for _ in range(3))
+    wt = torch.ones(dv, device=dev)
+    ws_c = torch.empty(kda.load_library().kda_conv_bwd_workspace(B, T, D, W), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(kda.load_library().kda_gnorm_bwd_workspace(B * T * H, dv), dtype=torch.uint8, device=dev)
+    out = []
+    conv_ms = timed_ms(lambda: (kda.conv_fwd(x, w, silu=True),
+                                kda.conv_bwd(x, w, dy, silu=True, need_dbias=False, workspace=ws_c)), reps)
+    nbytes = 2 * B * T * D * 2 + 3 * B * T * D * 2  # fwd: x, y; bwd: x, dy, dx
+    out.append({"workload": "short conv fwd+bwd: [%d, %d, %d] bf16, kernel %d, SiLU" % (B, T, D, W),
+                "ms_per_step": conv_ms, "tokens_per_s": B * T / (conv_ms * 1e-3), "algorithmic_bytes": nbytes,
+                "achieved_GBs": nbytes / (conv_ms * 1e-3) / 1e9, "bound": "hbm",
+                "frac": nbytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+    gn_ms = timed_ms(lambda: (kda.gnorm_fwd(o, gate, wt), kda.gnorm_bwd(o, gate, wt, dyo, workspace=ws_g)), reps)
+    n = B * T * H * dv
+    nbytes = 3 * n * 2 + 5 * n * 2  # fwd: o, gate, y; bwd: o, gate, dy, do, dgate
+    out.append({"workload": "gated output norm fwd+bwd: [%d, %d, %d, %d] bf16" % (B, T, H, dv),
+                "ms_per_step": gn_ms, "tokens_per_s": B * T / (gn_ms * 1e-3), "algorithmic_bytes": nbytes,
+                "achieved_GBs": nbytes / (gn_ms * 1e-3) / 1e9, "bound": "hbm",
+                "frac": nbytes / (gn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS})
+    return out
+
+
 def other_workloads(dev):
-    """The decode step, the packed 65,536-token row and the dk = dv = 128 heads."""
-    return [
+    """The decode step, the packed 65,536-token row, the dk = dv = 128 heads, and the
+    short convolution and gated output norm of the layer."""
+    return layer_ops_workload(dev) + [
         decode_workload(dev),
         fwd_bwd_workload("KDA fwd+bwd, one packed row of 65536 tokens (geometric document lengths, "
                          "mean 512), per-document h0 and dhT", dev, 1, 65536, 8, 32, 64, 3, packed=True),

@@ -14,7 +14,7 @@
 // Loads are 16 bytes per lane along the channel axis (coalesced token rows).
 // The backward forms dz = dy * act'(z) on the fly; dx is the anti-causal
 // correlation of dz with w; dw and dbias are summed per run, then over the
-// runs of a workgroup in LDS, then over the workgroups in a fixed order
+// runs of a workgroup in LDS, then over the workgroups by a fixed tree
 // (deterministic, no atomics).
 //
 // Gated norm (openkimi README, Profiling and H100 acceptance: the KDA output
@@ -256,16 +256,33 @@ __global__ void __launch_bounds__(kOpsThreads) conv_bwd_kernel(ConvArgs a) {
     }
 }
 
-// dw[c][i] and dbias[c]: the per-workgroup partials summed over the row blocks in order.
+// sum over k < nblk of part[k * M + e], by a whole workgroup: thread t adds
+// k = t, t + 256, ... in order, then a fixed tree over the threads, so the
+// result does not depend on scheduling.  Every thread gets the sum.
+__device__ __forceinline__ float block_col_sum(const float* __restrict__ part, int nblk, int M, int e) {
+    __shared__ float red[kOpsThreads];
+    float s = 0.f;
+    for (int k = threadIdx.x; k < nblk; k += kOpsThreads) s += part[(size_t)k * M + e];
+    red[threadIdx.x] = s;
+    __syncthreads();
+#pragma unroll
+    for (int off = kOpsThreads / 2; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    return red[0];
+}
+
+// dw[c][i] and dbias[c] (i == W): one workgroup per value, over the row blocks' partials.
 template <int W>
 __global__ void __launch_bounds__(kOpsThreads) conv_wsum_kernel(ConvArgs a, int nblk) {
-    const int e = blockIdx.x * kOpsThreads + threadIdx.x;
-    if (e >= a.D * (W + 1)) return;
-    float s = 0.f;
-    for (int k = 0; k < nblk; ++k) s += a.part[(size_t)k * a.D * (W + 1) + e];
-    const int c = e / (W + 1), i = e % (W + 1);
-    if (i < W) a.dw[c * W + i] = s;
-    else if (a.dbias) a.dbias[c] = s;
+    const int e = blockIdx.x;  // < D * (W + 1)
+    const float s = block_col_sum(a.part, nblk, a.D * (W + 1), e);
+    if (threadIdx.x == 0) {
+        const int c = e / (W + 1), i = e % (W + 1);
+        if (i < W) a.dw[c * W + i] = s;
+        else if (a.dbias) a.dbias[c] = s;
+    }
 }
 
 size_t conv_bwd_workspace(int B, int T, int D) {
@@ -284,9 +301,7 @@ static hipError_t conv_launch(const ConvArgs& a, bool backward, hipStream_t s) {
         return hipSuccess;
     }
     KDA_LAUNCH("conv_bwd", (conv_bwd_kernel<W, TIn, TOut, SILU>), grid, dim3(kOpsThreads), s, a);
-    const int n = a.D * (W + 1);
-    KDA_LAUNCH("conv_wsum", (conv_wsum_kernel<W>), dim3((n + kOpsThreads - 1) / kOpsThreads), dim3(kOpsThreads), s,
-               a, (int)grid.y);
+    KDA_LAUNCH("conv_wsum", (conv_wsum_kernel<W>), dim3(a.D * (W + 1)), dim3(kOpsThreads), s, a, (int)grid.y);
     return hipSuccess;
 }
 
@@ -406,12 +421,11 @@ __global__ void __launch_bounds__(kOpsThreads) gnorm_bwd_kernel(GnormArgs a) {
     }
 }
 
+// dweight[c]: one workgroup per channel, over the workgroups' partials.
 __global__ void __launch_bounds__(kOpsThreads) gnorm_wsum_kernel(GnormArgs a, int nblk) {
-    const int c = blockIdx.x * kOpsThreads + threadIdx.x;
-    if (c >= a.dv) return;
-    float s = 0.f;
-    for (int k = 0; k < nblk; ++k) s += a.part[(size_t)k * a.dv + c];
-    a.dweight[c] = s;
+    const int c = blockIdx.x;  // < dv
+    const float s = block_col_sum(a.part, nblk, a.dv, c);
+    if (threadIdx.x == 0) a.dweight[c] = s;
 }
 
 static int gnorm_blocks(int64_t rows, int dv) {
@@ -430,8 +444,7 @@ static hipError_t gnorm_launch(const GnormArgs& a, bool backward, hipStream_t s)
         return hipSuccess;
     }
     KDA_LAUNCH("gnorm_bwd", (gnorm_bwd_kernel<DV, TIn, TOut>), dim3(nblk), dim3(kOpsThreads), s, a);
-    KDA_LAUNCH("gnorm_wsum", gnorm_wsum_kernel, dim3((DV + kOpsThreads - 1) / kOpsThreads), dim3(kOpsThreads), s, a,
-               nblk);
+    KDA_LAUNCH("gnorm_wsum", gnorm_wsum_kernel, dim3(DV), dim3(kOpsThreads), s, a, nblk);
     return hipSuccess;
 }
 
