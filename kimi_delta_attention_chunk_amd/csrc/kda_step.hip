@@ -8,7 +8,9 @@
 // One workgroup per (sequence, head).  Thread (rg, j) owns column j of the
 // state and the rows rg*RPT .. rg*RPT+RPT-1, so for a fixed row the 64-wide
 // wave reads consecutive columns (coalesced 256-byte rows of the fp32 state).
-// The two column sums (S'^T k and S^T q) are reduced across row groups in LDS.
+// The state loads are issued first, so they overlap the staging of q, k and
+// the decay; the two column sums (S'^T k and S^T q) are reduced across row
+// groups in LDS (three barriers per step).
 #include "kda_device.cuh"
 #include "kda_internal.h"
 
@@ -24,6 +26,7 @@ __global__ void __launch_bounds__(kThreads) step_kernel(
     constexpr int RG = kThreads / DV;  // row groups
     static_assert(DK % RG == 0, "DK must split over the row groups");
     constexpr int RPT = DK / RG;       // rows per thread
+    static_assert(DK <= kThreads, "one thread per key channel");
 
     const int bh = blockIdx.x;
     if (bh >= BH) return;
@@ -32,66 +35,75 @@ __global__ void __launch_bounds__(kThreads) step_kernel(
     const int j = tid % DV, rg = tid / DV;
 
     __shared__ float s_q[DK], s_k[DK], s_a[DK];
-    __shared__ float s_red[RG][DV];
-    __shared__ float s_norm[2];
+    __shared__ float s_p[RG][DV], s_o[RG][DV];
+    __shared__ float s_norm[2][kThreads / 64];
 
-    // Stage q, k and the decay for this (sequence, head).
-    if (tid < DK) {
-        const size_t base = (size_t)bh * DK + tid;
-        s_q[tid] = Elem<TIn>::load(q, base);
-        s_k[tid] = Elem<TIn>::load(k, base);
-        float gg = g[base];
-        if (flags & 2u) gg = -expf(A_log[head]) * softplus_f(gg + dt_bias[head * DK + tid]);
-        s_a[tid] = expf(gg);
-    }
-    __syncthreads();
-    if (flags & 1u) {
-        // L2 norm of q (wave 0) and k (wave 1), DK <= 128 values each.
-        const int w = tid >> 6, l = tid & 63;
-        if (w < 2) {
-            const float* x = w == 0 ? s_q : s_k;
-            float ss = 0.f;
-            for (int c = l; c < DK; c += 64) ss += x[c] * x[c];
-            ss = wave_sum(ss);
-            if (l == 0) s_norm[w] = 1.0f / sqrtf(ss + kL2Eps);
-        }
-        __syncthreads();
-        if (tid < DK) { s_q[tid] *= s_norm[0]; s_k[tid] *= s_norm[1]; }
-        __syncthreads();
-    }
+    // this thread's state entries, first
+    float* hs = h + (size_t)bh * DK * DV;
+    float S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) S[i] = hs[(rg * RPT + i) * DV + j];
+    const float vj = Elem<TIn>::load(v, (size_t)bh * DV + j);
     float b = beta[bh];
     if (flags & 4u) b = sigmoid_f(b);
 
-    float* hs = h + (size_t)bh * DK * DV;
-    float S[RPT];
+    // q, k and the decay of this (sequence, head): thread c < DK holds channel c
+    float qc = 0.f, kc = 0.f, ac = 0.f;
+    if (tid < DK) {
+        const size_t base = (size_t)bh * DK + tid;
+        qc = Elem<TIn>::load(q, base);
+        kc = Elem<TIn>::load(k, base);
+        float gg = g[base];
+        if (flags & 2u) gg = -expf(A_log[head]) * softplus_f(gg + dt_bias[head * DK + tid]);
+        ac = expf(gg);
+    }
+    if (flags & 1u) {
+        // L2 norms of q and k over the DK channels (whole waves; lanes past DK hold 0)
+        const float sq = wave_sum(qc * qc), sk = wave_sum(kc * kc);
+        float tq = sq, tk = sk;
+        if constexpr (DK > 64) {
+            if ((tid & 63) == 0) { s_norm[0][tid >> 6] = sq; s_norm[1][tid >> 6] = sk; }
+            __syncthreads();
+            tq = 0.f;
+            tk = 0.f;
+#pragma unroll
+            for (int w = 0; w < DK / 64; ++w) { tq += s_norm[0][w]; tk += s_norm[1][w]; }
+        }
+        qc *= 1.0f / sqrtf(tq + kL2Eps);
+        kc *= 1.0f / sqrtf(tk + kL2Eps);
+    }
+    if (tid < DK) { s_q[tid] = qc; s_k[tid] = kc; s_a[tid] = ac; }
+    __syncthreads();
+
+    // decay, prediction p_j = (S'^T k)_j
     float p = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int c = rg * RPT + i;
-        S[i] = hs[c * DV + j] * s_a[c];
-        p += S[i] * s_k[c];
+        S[i] *= s_a[c];
+        p = fmaf(S[i], s_k[c], p);
     }
-    s_red[rg][j] = p;
+    s_p[rg][j] = p;
     __syncthreads();
     float pj = 0.f;
 #pragma unroll
-    for (int r = 0; r < RG; ++r) pj += s_red[r][j];
-    const float rj = Elem<TIn>::load(v, (size_t)bh * DV + j) - pj;
+    for (int r = 0; r < RG; ++r) pj += s_p[r][j];
+    const float rj = b * (vj - pj);
+    // delta-rule write, then the output read o_j = scale (S^T q)_j
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int c = rg * RPT + i;
-        S[i] += b * s_k[c] * rj;
+        S[i] = fmaf(s_k[c], rj, S[i]);
         hs[c * DV + j] = S[i];
-        acc += S[i] * s_q[c];
+        acc = fmaf(S[i], s_q[c], acc);
     }
-    __syncthreads();  // everyone has read s_red
-    s_red[rg][j] = acc;
+    s_o[rg][j] = acc;
     __syncthreads();
     if (rg == 0) {
         float oj = 0.f;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) oj += s_red[r][j];
+        for (int r = 0; r < RG; ++r) oj += s_o[r][j];
         Elem<TOut>::store(o, (size_t)bh * DV + j, scale * oj);
     }
 }
