@@ -374,6 +374,53 @@ def layer_ops_workload(dev, B=16, T=2048, H=8, dk=32, dv=64, W=4, reps=20):
     return out
 
 
+def long_document_workload(dev, T=65536, H=8, dk=32, dv=64, seg=1024, reps=5, seed=5):
+    """One document of T tokens, fwd+bwd: directly (its state pass is H * dv / 32 chains of
+    T / 64 chunks each) and segment-parallel on the same GPU (T / seg segments run from a zero
+    state, chained by their transition matrices, then rerun from their true states; the
+    context-parallel scheme, with the ranks' segments on one device)."""
+    import torch
+
+    import kda_inputs
+    import kimi_delta_attention_chunk_amd as kda
+
+    bf = torch.bfloat16
+    raw = kda_inputs.draw(seed, 1, T, H, dk, dv, h0_std=0.1, upstream=True, dhT=True)
+    q, k, v, do = (raw[x].to(bf).to(dev) for x in ("q_raw", "k_raw", "v", "do"))
+    f, b, A_log, dtb = (raw[x].to(dev) for x in ("f", "b", "A_log", "dt_bias"))
+    h0, dhT = raw["h0"].to(dev), raw["dhT"].to(dev)
+    scale = dk ** -0.5
+    flags = dict(A_log=A_log, dt_bias=dtb, l2norm_qk=True, gate_in_kernel=True, beta_logits=True)
+    args = (q, k, v, f, b)
+    ws = torch.empty(kda.workspace_bytes((1, T, H, dk), dv, 1, True), dtype=torch.uint8, device=dev)
+
+    def direct():
+        kda.fwd(*args, scale, h0=h0, workspace=ws, save_for_bwd=True, **flags)
+        kda.bwd(*args, scale, do, h0=h0, dhT=dhT, workspace=ws, fwd_saved=True, **flags)
+
+    R = T // seg
+    cu = torch.arange(0, T + 1, seg, dtype=torch.int32, device=dev)
+    plan = kda.plan_varlen(cu, T)
+    wsc = torch.empty(kda.workspace_bytes((1, T, H, dk), dv, R, True), dtype=torch.uint8, device=dev)
+    pk = dict(cu_seqlens=cu, plan=plan, **flags)
+
+    def segmented():
+        _, c = kda.fwd(*args, scale, workspace=wsc, **pk)
+        M = kda.segment_maps(*args, workspace=wsc, **pk)
+        h_in, _ = kda.state_scan(M, c, h0[0])
+        kda.fwd(*args, scale, h0=h_in, workspace=wsc, save_for_bwd=True, **pk)
+        e = kda.bwd(*args, scale, do, h0=h_in, workspace=wsc, fwd_saved=True, **pk)["dh0"]
+        D, _ = kda.state_scan(M, e, dhT[0], transpose=True)
+        kda.bwd(*args, scale, do, h0=h_in, dhT=D, workspace=wsc, fwd_saved=True, **pk)
+
+    ms_d = timed_ms(direct, reps, warm=1)
+    ms_s = timed_ms(segmented, reps, warm=1)
+    return {"workload": "KDA fwd+bwd, one document of %d tokens, H=%d dk=%d dv=%d, bf16" % (T, H, dk, dv),
+            "direct_ms": ms_d, "direct_tokens_per_s": T / (ms_d * 1e-3),
+            "segment_parallel_ms": ms_s, "segment_parallel_tokens_per_s": T / (ms_s * 1e-3),
+            "segments": R, "segment_tokens": seg}
+
+
 def other_workloads(dev):
     """The decode step, the packed 65,536-token row, the dk = dv = 128 heads, and the
     short convolution and gated output norm of the layer."""
@@ -382,6 +429,7 @@ def other_workloads(dev):
         fwd_bwd_workload("KDA fwd+bwd, one packed row of 65536 tokens (geometric document lengths, "
                          "mean 512), per-document h0 and dhT", dev, 1, 65536, 8, 32, 64, 3, packed=True),
         fwd_bwd_workload("KDA fwd+bwd, larger heads: B=2 T=8192 H=16 dk=dv=128", dev, 2, 8192, 16, 128, 128, 4),
+        long_document_workload(dev),
     ]
 
 

@@ -185,6 +185,31 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
              float* h, void* o, kda_stream_t stream);
 
 /* ----------------------------------------------------------------------------
+ * Context parallelism, dk = 32, dv = 64 (the one-GPU part of splitting a long
+ * row over devices; the pages pack documents instead -- Packing PR -- and show
+ * no context parallelism for KDA).  A chunk maps the state entering it
+ * affinely to the state leaving it, so a segment of chunks does too:
+ * h_out = M h_in + c, with c = kda_fwd's hT for h0 = 0.
+ * kda_segment_maps: M [N,H,dk,dk] fp32 of every sequence (or packed document)
+ *   of the call: the product of its chunks' transition matrices, first chunk
+ *   rightmost (the identity for an empty one).  Inputs and flags as kda_fwd
+ *   (no h0); ws of at least kda_fwd_workspace(desc) bytes.
+ * kda_state_scan: chains R segments, H heads (dk = 32, dv = 64 only):
+ *   transpose = 0:  x = x0 (nullable = 0); for r = 0 .. R-1: x_in[r] = x; x = M_r x + c_r
+ *   transpose = 1:  x = x0; for r = R-1 .. 0: x_in[r] = x; x = M_r^T x + c_r
+ *   x_out (nullable) receives the final x.  M [R,H,dk,dk], c, x_in [R,H,dk,dv],
+ *   x0, x_out [H,dk,dv], all fp32.  Forward: c_r = the segments' hT from h0 = 0,
+ *   x0 = the row's h0; x_in[r] is then segment r's true h0 and x_out the row's hT.
+ *   Backward: c_r = the segments' dh0 from kda_bwd with dhT = 0, x0 = the row's
+ *   dhT; x_in[r] is then segment r's true dhT and x_out the row's dh0. */
+int kda_segment_maps(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                     const int32_t* chunk_indices, const int32_t* chunk_offsets, float* M, void* ws,
+                     size_t ws_bytes, kda_stream_t stream);
+int kda_state_scan(int32_t R, int32_t H, int32_t dk, int32_t dv, int32_t transpose, const float* M,
+                   const float* c, const float* x0, float* x_in, float* x_out, kda_stream_t stream);
+
+/* ----------------------------------------------------------------------------
  * Short causal depthwise convolution, the step before KDA in its layer
  * ("Pure KDA 300M on Primus" guide, Overview: kernel size 4, depthwise, on
  * the concatenated q/k/v channels; Troubleshooting: [B, T, D] is the native
@@ -235,7 +260,7 @@ int kda_gnorm_bwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype
  * with kda_timing_count() / kda_timing_get(i, &name, &launches, &total_ms);
  * `name` stays valid until the next enable call.  Kernel names: plan, step,
  * fwd_intra, fwd_scan, bwd_dh, bwd_chunk, bwd_dv, bwd_dk, bwd_gate_sum,
- * conv_fwd, conv_bwd, conv_wsum, gnorm_fwd, gnorm_bwd, gnorm_wsum. */
+ * conv_fwd, conv_bwd, conv_wsum, gnorm_fwd, gnorm_bwd, gnorm_wsum, seg_map, state_scan. */
 int kda_timing_enable(int on);
 int kda_timing_collect(void);
 int kda_timing_count(void);

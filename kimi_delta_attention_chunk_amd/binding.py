@@ -26,7 +26,7 @@ EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd
            "kda_bwd_workspace", "kda_fwd", "kda_bwd", "kda_step", "kda_status_str",
            "kda_last_error", "kda_timing_enable", "kda_timing_collect", "kda_timing_count",
            "kda_timing_get", "kda_conv_fwd", "kda_conv_bwd_workspace", "kda_conv_bwd", "kda_gnorm_fwd",
-           "kda_gnorm_bwd_workspace", "kda_gnorm_bwd"]
+           "kda_gnorm_bwd_workspace", "kda_gnorm_bwd", "kda_segment_maps", "kda_state_scan"]
 CONV_SILU = 1
 RMS_EPS = 1e-6
 
@@ -102,6 +102,10 @@ def load_library():
     lib.kda_gnorm_bwd_workspace.restype = sz
     lib.kda_gnorm_bwd.argtypes = [i64, i32, ctypes.c_int, ctypes.c_int, f32] + [vp] * 8 + [sz, vp]
     lib.kda_gnorm_bwd.restype = ctypes.c_int
+    lib.kda_segment_maps.argtypes = [dp] + [vp] * 12 + [sz, vp]
+    lib.kda_segment_maps.restype = ctypes.c_int
+    lib.kda_state_scan.argtypes = [i32, i32, i32, i32, i32] + [vp] * 6
+    lib.kda_state_scan.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -424,3 +428,43 @@ def gnorm_bwd(o, gate, weight, dy, eps=RMS_EPS, *, out_dtype=None, workspace=Non
                              _ptr(dy), _ptr(out["do"]), _ptr(out["dgate"]), _ptr(out["dweight"]), _ptr(ws),
                              ws.numel(), _stream(dev)))
     return out
+
+
+# ---------------------------------------------------------------- context parallelism (dk = 32)
+def segment_maps(q, k, v, g, beta, cu_seqlens=None, plan=None, *, A_log=None, dt_bias=None, l2norm_qk=False,
+                 gate_in_kernel=False, beta_logits=False, workspace=None):
+    """kda_segment_maps: the state-transition matrix M [N,H,dk,dk] of every sequence or packed
+    document: h_out = M h_in + (its hT from h0 = 0)."""
+    lib = load_library()
+    B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, None, cu_seqlens, plan, A_log, dt_bias, gate_in_kernel)
+    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits)
+    desc = _desc(q, v, N, 1.0, flags, q.dtype)
+    dev = q.device
+    M = torch.empty((N, H, dk, dk), dtype=torch.float32, device=dev)
+    need = lib.kda_fwd_workspace(ctypes.byref(desc))
+    if need == 0:
+        _check(KDA_ERR_INVALID)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    idx, off = plan if plan is not None else (None, None)
+    _check(lib.kda_segment_maps(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                                _ptr(dt_bias), _ptr(cu_seqlens), _ptr(idx), _ptr(off), _ptr(M), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return M
+
+
+def state_scan(M, c, x0=None, *, transpose=False):
+    """kda_state_scan: chains R segments; returns (x_in [R,H,dk,dv], x_out [H,dk,dv])."""
+    lib = load_library()
+    _req(M, "M", torch.float32)
+    R, H, dk, _ = M.shape
+    dev = M.device
+    _req(c, "c", torch.float32, None, dev)
+    if c.dim() != 4 or tuple(c.shape[:3]) != (R, H, dk):
+        raise ValueError("c must be [R,H,dk,dv]")
+    dv = c.shape[-1]
+    _req(x0, "x0", torch.float32, (H, dk, dv), dev, optional=True)
+    x_in = torch.empty((R, H, dk, dv), dtype=torch.float32, device=dev)
+    x_out = torch.empty((H, dk, dv), dtype=torch.float32, device=dev)
+    _check(lib.kda_state_scan(R, H, dk, dv, 1 if transpose else 0, _ptr(M), _ptr(c), _ptr(x0), _ptr(x_in),
+                              _ptr(x_out), _stream(dev)))
+    return x_in, x_out

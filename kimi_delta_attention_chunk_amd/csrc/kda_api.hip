@@ -262,6 +262,46 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
     return KDA_OK;
 }
 
+// ---------------------------------------------------------------- context parallelism (dk = 32)
+int kda_segment_maps(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                     const float* beta, const float* A_log, const float* dt_bias, const int32_t* cu_seqlens,
+                     const int32_t* chunk_indices, const int32_t* chunk_offsets, float* M, void* ws, size_t ws_bytes,
+                     kda_stream_t stream) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
+    if (rc) return rc;
+    if (desc->dk != 32 || desc->dv != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "segment maps need dk = 32, dv = 64 (got %d, %d)", desc->dk, desc->dv);
+    if (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED)) return fail(KDA_ERR_INVALID, "save/saved flags do not apply");
+    if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, nullptr))) return rc;
+    if ((rc = check_ptr(M, "M", true))) return rc;
+    const size_t need = kda::ws_layout(a, false).total;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.ws = ws; a.ws_bytes = ws_bytes;
+    hipError_t e = kda::launch_segment_maps(a, M, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "segment maps launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+int kda_state_scan(int32_t R, int32_t H, int32_t dk, int32_t dv, int32_t transpose, const float* M, const float* c,
+                   const float* x0, float* x_in, float* x_out, kda_stream_t stream) {
+    g_err[0] = 0;
+    if (R < 1 || H < 1) return fail(KDA_ERR_INVALID, "bad sizes R=%d H=%d", R, H);
+    if (dk != 32 || dv != 64) return fail(KDA_ERR_UNSUPPORTED, "state scan needs dk = 32, dv = 64 (got %d, %d)", dk, dv);
+    if (transpose != 0 && transpose != 1) return fail(KDA_ERR_INVALID, "transpose must be 0 or 1");
+    int rc;
+    if ((rc = check_ptr(M, "M", true)) || (rc = check_ptr(c, "c", true)) || (rc = check_ptr(x0, "x0", false)) ||
+        (rc = check_ptr(x_in, "x_in", true)) || (rc = check_ptr(x_out, "x_out", false)))
+        return rc;
+    hipError_t e = kda::launch_state_scan(R, H, dk, dv, transpose != 0, M, c, x0, x_in, x_out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "state scan launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
 // ---------------------------------------------------------------- short convolution
 static int conv_check(int32_t B, int32_t T, int32_t D, int32_t W, int dtype, int out_dtype, uint32_t flags,
                       const int32_t* cu, int32_t N) {

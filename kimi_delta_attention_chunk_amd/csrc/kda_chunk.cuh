@@ -261,6 +261,7 @@ struct TriKUpper {
 // state pass (states entering each chunk, v_new; hT if p.hT is set).
 Prm make_prm(const ChunkArgs& a, const WsLayout& L);
 hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s);
+hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t s);
 
 // Register-resident accumulators for the 16x16 tiles of an M x N result that
 // this wave owns (tile = wave + i * NW, NW waves), so several products can be

@@ -1,0 +1,162 @@
+// kda_cp.hip -- the building blocks of context parallelism for dk = 32: the
+// affine map of a segment of chunks, and the short scan that chains segments.
+//
+// A chunk maps the state entering it to the state leaving it affinely,
+// h' = P h + hh (kda_pscan.cuh), so a segment of chunks -- a rank's share of a
+// long row, or any run of chunks -- does too: h_out = M h_in + c with
+// M = P_last ... P_first (dk x dk) and c = the segment's final state from a
+// zero entering state (kda_fwd's hT with h0 = 0).  Segments can therefore be
+// computed independently and chained afterwards:
+//   forward   h_in[0] = h0;  h_in[r+1] = M_r h_in[r] + c_r      (hT = h_out of the last)
+//   backward  D[R-1] = dhT;  D[r-1] = M_r^T D[r] + e_r          (dh0 = M_0^T D[0] + e_0)
+// where e_r is the gradient with respect to the segment's entering state from
+// its own outputs (kda_bwd's dh0 with dhT = 0) and D[r] = dL/dh_out[r].  A
+// second pass of each segment with its h_in (and D) then gives the same outputs
+// and gradients as one pass over the whole row.
+//
+// seg_map_kernel: one workgroup of four waves per (segment, head); the 32 x 32
+// product X = P X runs chunk after chunk from X = I with the same fragment
+// scheme as the state pass (P's rows as register fragments from the intra
+// kernel's k-block array, prefetched four chunks ahead; X^T in a
+// double-buffered LDS tile, one barrier per chunk).
+// state_scan_kernel: one workgroup per (head, 32 state columns); fp32 FMA over
+// the segments in order, M_r staged in LDS (transposed for the backward).
+#include "../../include/kda.h"
+#include "kda_chunk.cuh"
+#include "kda_internal.h"
+#include "kda_mma.cuh"
+#include "kda_pscan.cuh"
+
+namespace kda {
+
+template <Prec P>
+__global__ void __launch_bounds__(kPsThreads) seg_map_kernel(Prm p, float* __restrict__ M) {
+    constexpr int DK = kPsDK, LK = DK + 8, PD = 4;
+    __shared__ __attribute__((aligned(16))) float sX[2][DK * LK];
+    static_assert(STile<Prec::F32, DK>::ld == LK, "tile footprint");
+    const STile<P, DK> XT[2] = {STile<P, DK>(sX[0], DK), STile<P, DK>(sX[1], DK)};
+    const int nh = blockIdx.x;
+    const int n = nh / p.H, h = nh % p.H;
+    if (n >= p.N) return;
+    const int wave = wave_id(), lr = threadIdx.x & 15;
+    const int tc = wave >> 1, tj = wave & 1;  // this wave's 16x16 tile of X
+    const int crow = 16 * tc + frag_row(0), jcol = 16 * tj + lr;
+    f32x4 S;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[r] = crow + r == jcol ? 1.f : 0.f;
+    int c0, c1;
+    p.seq.seq_chunks(n, c0, c1);
+    auto slot_of = [&](int cc) { return (size_t)(cc < c1 ? cc : c1 - 1) * p.H + h; };
+    auto load = [&](int cc, AFrag<P>& f) {
+        load_afrag(f, (const char*)(p.pm + slot_of(cc) * DK * DK) + (size_t)(16 * tc + lr) * kKBlockBytes);
+    };
+    XT[0].put4(jcol, crow, S);
+    if (c0 < c1) {
+        AFrag<P> R[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) load(c0 + i, R[i]);
+        auto step = [&](int buf, const AFrag<P>& pm) {
+            __syncthreads();  // X^T of this chunk complete; the other buffer's readers are done
+            AFrag<P> fb;
+            load_frag(fb, XT[buf].sub(16 * tj), 0);
+            S = mma_ff(pm, fb, f32x4{0.f, 0.f, 0.f, 0.f});
+            XT[buf ^ 1].put4(jcol, crow, S);
+        };
+        int c = c0;
+        for (; c + PD - 1 < c1; c += PD) {
+#pragma unroll
+            for (int i = 0; i < PD; ++i) {
+                step(i & 1, R[i]);
+                load(c + PD + i, R[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PD - 1; ++i)
+            if (c + i < c1) step(i & 1, R[i]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) M[((size_t)nh * DK + crow + r) * DK + jcol] = S[r];
+}
+
+// X <- A_r X + c_r over the segments (A_r = M_r, or M_r^T in reverse order for
+// the backward); out[r] receives X before segment r's step.
+template <int DK>
+__global__ void __launch_bounds__(kThreads) state_scan_kernel(int R, int H, int DV, int transpose,
+                                                              const float* __restrict__ M,
+                                                              const float* __restrict__ c,
+                                                              const float* __restrict__ x0, float* __restrict__ out,
+                                                              float* __restrict__ xfinal) {
+    constexpr int BV = 32, LX = BV + 4, LM = DK + 1;
+    constexpr int RPT = DK * BV / 4 / kThreads;  // float4 of the state block per thread
+    static_assert(RPT >= 1, "state block");
+    __shared__ __attribute__((aligned(16))) float sX[DK * LX];
+    __shared__ float sA[DK * LM];
+    const int h = blockIdx.x, jb = blockIdx.y * BV;
+    const int tid = threadIdx.x;
+    // this thread's float4s of the state block: rows i, columns j4 .. j4 + 3
+    int ii[RPT], jj[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int e = tid + kThreads * q;
+        ii[q] = e / (BV / 4);
+        jj[q] = 4 * (e % (BV / 4));
+    }
+    f32x4 X[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q)
+        X[q] = x0 ? *(const f32x4*)(x0 + ((size_t)h * DK + ii[q]) * DV + jb + jj[q]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < R; ++s) {
+        const int r = transpose ? R - 1 - s : s;
+        const size_t seg = (size_t)r * H + h;
+        // stage A_r and X
+        for (int e = tid; e < DK * DK; e += kThreads) {
+            const int a = e / DK, b = e - a * DK;
+            const float m = M[seg * DK * DK + e];
+            if (transpose) sA[b * LM + a] = m;
+            else sA[a * LM + b] = m;
+        }
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            *(f32x4*)&sX[ii[q] * LX + jj[q]] = X[q];
+            *(f32x4*)(out + (seg * DK + ii[q]) * DV + jb + jj[q]) = X[q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            f32x4 acc = *(const f32x4*)(c + (seg * DK + ii[q]) * DV + jb + jj[q]);
+            for (int k = 0; k < DK; ++k) {
+                const float a = sA[ii[q] * LM + k];
+                const f32x4 x = *(const f32x4*)&sX[k * LX + jj[q]];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m] = fmaf(a, x[m], acc[m]);
+            }
+            X[q] = acc;
+        }
+        __syncthreads();  // sA, sX are restaged next
+    }
+    if (xfinal) {
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) *(f32x4*)(xfinal + ((size_t)h * DK + ii[q]) * DV + jb + jj[q]) = X[q];
+    }
+}
+
+hipError_t launch_segment_maps(const ChunkArgs& a, float* M, hipStream_t s) {
+    const Prm p = make_prm(a, ws_layout(a, false));
+    const hipError_t e = launch_recompute_intra(p, a, s);
+    if (e != hipSuccess) return e;
+    if (a.in_bf16)
+        KDA_LAUNCH("seg_map", seg_map_kernel<Prec::BF3>, dim3(a.N * a.H), dim3(kPsThreads), s, p, M);
+    else
+        KDA_LAUNCH("seg_map", seg_map_kernel<Prec::F32>, dim3(a.N * a.H), dim3(kPsThreads), s, p, M);
+    return hipSuccess;
+}
+
+hipError_t launch_state_scan(int R, int H, int dk, int dv, bool transpose, const float* M, const float* c,
+                             const float* x0, float* out, float* xfinal, hipStream_t s) {
+    if (dk != 32 || dv % 32 != 0) return hipErrorInvalidValue;
+    KDA_LAUNCH("state_scan", state_scan_kernel<32>, dim3(H, dv / 32), dim3(kThreads), s, R, H, dv, transpose ? 1 : 0,
+               M, c, x0, out, xfinal);
+    return hipSuccess;
+}
+
+}  // namespace kda

@@ -160,6 +160,20 @@ hipError_t launch_recompute(const Prm& p, const ChunkArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// The intra-chunk kernel alone (dk = 32: the affine form of every chunk), into
+// the forward workspace layout.
+hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t s) {
+    if (a.dk != 32 || a.dv != 64 || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
+    if (a.n_chunks_bound == 0) return hipSuccess;
+    if (a.in_bf16)
+        KDA_LAUNCH("fwd_intra", (intra_kernel<32, 64, uint16_t, Prec::BF3>), dim3(a.n_chunks_bound, a.H), dim3(kThreads),
+                   s, p);
+    else
+        KDA_LAUNCH("fwd_intra", (intra_kernel<32, 64, float, Prec::F32>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+                   p);
+    return hipSuccess;
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
     const bool save = a.flags & (1u << 3);

@@ -36,6 +36,11 @@ struct ConvArgs {
 hipError_t launch_conv(const ConvArgs& a, bool backward, hipStream_t s);
 size_t conv_bwd_workspace(int B, int T, int D);
 
+// Context parallelism (kda_cp.hip): the chain of segment maps, x <- M_r x + c_r
+// over the segments (M_r^T, segments in reverse, with `transpose`).
+hipError_t launch_state_scan(int R, int H, int dk, int dv, bool transpose, const float* M, const float* c,
+                             const float* x0, float* out, float* xfinal, hipStream_t s);
+
 // Gated RMS norm over rows of dv values (kda_ops.hip).
 struct GnormArgs {
     int64_t rows;
@@ -114,5 +119,8 @@ void prof_end(hipStream_t s, const char* name);
         if (kda_launch_err_ != hipSuccess) return kda_launch_err_;             \
     } while (0)
 hipError_t launch_bwd(const ChunkArgs& a, hipStream_t s);
+// The transition matrix of every sequence of a call, dk = 32 (kda_cp.hip; runs
+// the intra-chunk kernel into the forward workspace first).
+hipError_t launch_segment_maps(const ChunkArgs& a, float* M, hipStream_t s);
 
 }  // namespace kda

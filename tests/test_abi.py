@@ -172,3 +172,20 @@ def test_gnorm_rejects(rows, dv, eps, code):
     rc = lib.kda_gnorm_bwd(1000, 64, B.KDA_BF16, B.KDA_BF16, 1e-6, _fake(1), _fake(2), _fake(3), _fake(4), _fake(5),
                            _fake(6), _fake(7), _fake(8), need - 1, None)
     assert rc == B.KDA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- context parallelism
+def test_segment_maps_and_state_scan_reject():
+    lib = kda.load_library()
+    d = _desc(dk=64, dv=64)
+    rc = lib.kda_segment_maps(ctypes.byref(d), *([_fake(1)] * 5), None, None, None, None, None, _fake(2), _fake(3),
+                              1 << 30, None)
+    assert rc == B.KDA_ERR_UNSUPPORTED, lib.kda_last_error()
+    d = _desc()
+    rc = lib.kda_segment_maps(ctypes.byref(d), *([_fake(1)] * 5), None, None, None, None, None, _fake(2), _fake(3),
+                              16, None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+    assert lib.kda_state_scan(4, 2, 64, 64, 0, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_UNSUPPORTED
+    assert lib.kda_state_scan(0, 2, 32, 64, 0, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
+    assert lib.kda_state_scan(4, 2, 32, 64, 2, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
+    assert lib.kda_state_scan(4, 2, 32, 64, 0, None, _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID

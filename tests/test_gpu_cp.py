@@ -1,0 +1,75 @@
+"""Context parallelism on one GPU (dk = 32): one long document split into segments
+that run independently, chained by their transition matrices (kda_segment_maps,
+kda_state_scan), and rerun with their true entering states / end gradients,
+reproduces the single pass over the whole document (the oracle's), forward and
+backward.  Weak decay, nonzero h0 and dhT, so the state carries across every
+segment boundary."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_chunk_amd as kda
+from cases import check_close, oracle_bwd, oracle_fwd, prepared, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _cp_run(d, scale, cu, backward):
+    T = d["q"].shape[1]
+    cuc = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    plan = kda.plan_varlen(cuc, T)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    # 1. every segment from a zero state: its final state c_r, and its transition matrix M_r
+    _, c = kda.fwd(*args, scale, cu_seqlens=cuc, plan=plan, out_dtype=torch.float32)
+    M = kda.segment_maps(*args, cu_seqlens=cuc, plan=plan)
+    # 2. the chain: each segment's true entering state, and the row's final state
+    h_in, hT = kda.state_scan(M, c, d["h0"][0])
+    # 3. every segment again from its true entering state
+    o, _ = kda.fwd(*args, scale, h0=h_in, cu_seqlens=cuc, plan=plan, out_dtype=torch.float32)
+    if not backward:
+        return o, hT, None
+    # 4. each segment's own gradient with respect to its entering state, the reverse chain
+    #    (each segment's true end gradient, and the row's dh0), then the gradients
+    e = kda.bwd(*args, scale, d["do"], h0=h_in, cu_seqlens=cuc, plan=plan, out_dtype=torch.float32)["dh0"]
+    D, dh0 = kda.state_scan(M, e, d["dhT"][0], transpose=True)
+    gr = kda.bwd(*args, scale, d["do"], h0=h_in, dhT=D, cu_seqlens=cuc, plan=plan, out_dtype=torch.float32)
+    gr["dh0"] = dh0
+    return o, hT, gr
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("cu", [[0, 512, 1024, 1536, 2048], [0, 300, 1100, 1101, 2048]], ids=["aligned", "ragged"])
+def test_context_parallel_equals_single_pass(dtype, cu):
+    T, H, dk, dv = 2048, 4, 32, 64
+    inp, _ = prepared(11, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, upstream=True, dhT=True)
+    d = to_dev(inp, "cuda:0")
+    scale = dk ** -0.5
+    o, hT, gr = _cp_run(d, scale, cu, backward=True)
+    torch.cuda.synchronize()
+    oref, href = oracle_fwd(inp, scale)
+    gref = oracle_bwd(inp, scale)
+    check_close("o", o, oref, dtype)
+    check_close("hT", hT[None], href, dtype)
+    for nm in ("dq", "dk", "dv", "dg", "dbeta"):
+        check_close(nm, gr[nm], gref[nm], dtype)
+    check_close("dh0", gr["dh0"][None], gref["dh0"], dtype)
+
+
+def test_segment_map_of_one_document_is_its_state_map():
+    """M h0 + hT(h0 = 0) = hT(h0) for every document of a packed row, and an empty
+    document's map is the identity."""
+    lens = [700, 0, 1, 64, 1283]
+    cu = np.cumsum([0] + lens).tolist()
+    T, H, dk, dv = cu[-1], 2, 32, 64
+    inp, _ = prepared(12, 1, T, H, dk, dv, torch.float32, weak=True, h0_std=0.1, n_states=len(lens))
+    d = to_dev(inp, "cuda:0")
+    cuc = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    plan = kda.plan_varlen(cuc, T)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    M = kda.segment_maps(*args, cu_seqlens=cuc, plan=plan)
+    _, c = kda.fwd(*args, 0.1, cu_seqlens=cuc, plan=plan)
+    _, hT = kda.fwd(*args, 0.1, h0=d["h0"], cu_seqlens=cuc, plan=plan)
+    torch.cuda.synchronize()
+    pred = torch.matmul(M, d["h0"]) + c
+    check_close("M h0 + c", pred, hT.double().cpu().numpy(), torch.float32)
+    assert torch.equal(M[1], torch.eye(dk, device="cuda").expand(H, dk, dk))
