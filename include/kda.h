@@ -69,7 +69,8 @@ enum {
     KDA_F_GATE_IN_KERNEL = 1u << 1,
     KDA_F_BETA_LOGITS = 1u << 2,
     KDA_F_SAVE_FOR_BWD = 1u << 3,
-    KDA_F_FWD_SAVED = 1u << 4
+    KDA_F_FWD_SAVED = 1u << 4,
+    KDA_F_DH0_ONLY = 1u << 5
 };
 /* Saving the forward for the backward (the usual training pattern):
  *   KDA_F_SAVE_FOR_BWD  (kda_fwd) also keep, in the workspace, the per-chunk
@@ -81,7 +82,17 @@ enum {
  *                       call with KDA_F_SAVE_FOR_BWD on the same descriptor
  *                       (other flags equal), inputs and varlen tables, with
  *                       nothing written to it in between.  The results are
- *                       identical to a backward that recomputes. */
+ *                       identical to a backward that recomputes.
+ *                       (kda_fwd) the intra-chunk quantities of these inputs
+ *                       are in `ws` already (from a kda_fwd with
+ *                       KDA_F_SAVE_FOR_BWD): only the state pass runs, from
+ *                       this call's h0 (with KDA_F_SAVE_FOR_BWD too it keeps
+ *                       the new states for the backward).
+ *                       (kda_segment_maps) read the chunks' transitions from
+ *                       such a `ws` instead of forming them.
+ *   KDA_F_DH0_ONLY      (kda_bwd) run the reverse state pass alone: only dh0
+ *                       (required) is written; dq, dk, dv, dg, dbeta, dA_log
+ *                       and ddt_bias may be null and are left untouched. */
 
 /* Problem descriptor.
  *   B      rows (B == 1 when packed)

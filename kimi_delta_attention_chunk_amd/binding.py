@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_BF16, KDA_FP32 = 0, 1
-F_QK_L2NORM, F_GATE_IN_KERNEL, F_BETA_LOGITS, F_SAVE_FOR_BWD, F_FWD_SAVED = 1, 2, 4, 8, 16
+F_QK_L2NORM, F_GATE_IN_KERNEL, F_BETA_LOGITS, F_SAVE_FOR_BWD, F_FWD_SAVED, F_DH0_ONLY = 1, 2, 4, 8, 16, 32
 CHUNK = 64
 
 EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd_workspace",
@@ -215,22 +215,27 @@ def _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias, gate_i
 
 def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=None,
         dt_bias=None, l2norm_qk=False, gate_in_kernel=False, beta_logits=False, out_dtype=None,
-        output_final_state=True, workspace=None, save_for_bwd=False):
+        output_final_state=True, workspace=None, save_for_bwd=False, fwd_saved=False):
     """kda_fwd.  Returns (o [B,T,H,dv], hT [N,H,dk,dv] or None).
 
     With save_for_bwd the workspace (which must then be sized for the backward)
-    keeps what kda_bwd(..., fwd_saved=True, workspace=same) needs.
+    keeps what kda_bwd(..., fwd_saved=True, workspace=same) needs.  With fwd_saved
+    the workspace already holds such a forward of the same inputs: only the state
+    pass runs again, from this call's h0.
     """
     lib = load_library()
     B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias,
                                        gate_in_kernel)
     out_dtype = out_dtype or q.dtype
-    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_SAVE_FOR_BWD if save_for_bwd else 0)
+    flags = (_flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_SAVE_FOR_BWD if save_for_bwd else 0)
+             | (F_FWD_SAVED if fwd_saved else 0))
+    if fwd_saved and workspace is None:
+        raise ValueError("fwd_saved needs the saved forward's workspace")
     desc = _desc(q, v, N, scale, flags, out_dtype)
     dev = q.device
     o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if output_final_state else None
-    need = (lib.kda_bwd_workspace if save_for_bwd else lib.kda_fwd_workspace)(ctypes.byref(desc))
+    need = (lib.kda_bwd_workspace if (save_for_bwd or fwd_saved) else lib.kda_fwd_workspace)(ctypes.byref(desc))
     if need == 0:
         _check(KDA_ERR_INVALID)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
@@ -243,9 +248,10 @@ def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=N
 
 def bwd(q, k, v, g, beta, scale, d_o, h0=None, dhT=None, cu_seqlens=None, plan=None, *,
         A_log=None, dt_bias=None, l2norm_qk=False, gate_in_kernel=False, beta_logits=False,
-        out_dtype=None, need_dh0=True, workspace=None, fwd_saved=False):
+        out_dtype=None, need_dh0=True, workspace=None, fwd_saved=False, dh0_only=False):
     """kda_bwd.  Returns dict dq, dk, dv, dg, dbeta, dh0 (and dA_log, ddt_bias with the gate).
 
+    dh0_only: only the reverse state pass runs; the result holds dh0 alone.
     fwd_saved: `workspace` holds a kda_fwd(..., save_for_bwd=True) of the same
     inputs, so the forward is not recomputed.
     """
@@ -256,19 +262,24 @@ def bwd(q, k, v, g, beta, scale, d_o, h0=None, dhT=None, cu_seqlens=None, plan=N
     _req(d_o, "d_o", q.dtype, (B, T, H, dv), dev)
     _req(dhT, "dhT", torch.float32, (N, H, dk, dv), dev, optional=True)
     out_dtype = out_dtype or q.dtype
-    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_FWD_SAVED if fwd_saved else 0)
+    flags = (_flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_FWD_SAVED if fwd_saved else 0)
+             | (F_DH0_ONLY if dh0_only else 0))
     if fwd_saved and workspace is None:
         raise ValueError("fwd_saved needs the forward's workspace")
     desc = _desc(q, v, N, scale, flags, out_dtype)
-    out = dict(
-        dq=torch.empty((B, T, H, dk), dtype=out_dtype, device=dev),
-        dk=torch.empty((B, T, H, dk), dtype=out_dtype, device=dev),
-        dv=torch.empty((B, T, H, dv), dtype=out_dtype, device=dev),
-        dg=torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
-        dbeta=torch.empty((B, T, H), dtype=torch.float32, device=dev),
-        dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if need_dh0 else None,
-    )
-    if gate_in_kernel:
+    if dh0_only:
+        out = dict(dq=None, dk=None, dv=None, dg=None, dbeta=None,
+                   dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev))
+    else:
+        out = dict(
+            dq=torch.empty((B, T, H, dk), dtype=out_dtype, device=dev),
+            dk=torch.empty((B, T, H, dk), dtype=out_dtype, device=dev),
+            dv=torch.empty((B, T, H, dv), dtype=out_dtype, device=dev),
+            dg=torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+            dbeta=torch.empty((B, T, H), dtype=torch.float32, device=dev),
+            dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if need_dh0 else None,
+        )
+    if gate_in_kernel and not dh0_only:
         out["dA_log"] = torch.empty((H,), dtype=torch.float32, device=dev)
         out["ddt_bias"] = torch.empty((H, dk), dtype=torch.float32, device=dev)
     need = lib.kda_bwd_workspace(ctypes.byref(desc))
@@ -432,12 +443,15 @@ def gnorm_bwd(o, gate, weight, dy, eps=RMS_EPS, *, out_dtype=None, workspace=Non
 
 # ---------------------------------------------------------------- context parallelism (dk = 32)
 def segment_maps(q, k, v, g, beta, cu_seqlens=None, plan=None, *, A_log=None, dt_bias=None, l2norm_qk=False,
-                 gate_in_kernel=False, beta_logits=False, workspace=None):
+                 gate_in_kernel=False, beta_logits=False, workspace=None, fwd_saved=False):
     """kda_segment_maps: the state-transition matrix M [N,H,dk,dk] of every sequence or packed
-    document: h_out = M h_in + (its hT from h0 = 0)."""
+    document: h_out = M h_in + (its hT from h0 = 0).  fwd_saved: `workspace` holds a
+    kda_fwd(..., save_for_bwd=True) of the same inputs, whose chunk transitions are reused."""
     lib = load_library()
     B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, None, cu_seqlens, plan, A_log, dt_bias, gate_in_kernel)
-    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits)
+    flags = _flags(l2norm_qk, gate_in_kernel, beta_logits) | (F_FWD_SAVED if fwd_saved else 0)
+    if fwd_saved and workspace is None:
+        raise ValueError("fwd_saved needs the saved forward's workspace")
     desc = _desc(q, v, N, 1.0, flags, q.dtype)
     dev = q.device
     M = torch.empty((N, H, dk, dk), dtype=torch.float32, device=dev)

@@ -33,8 +33,8 @@ int check_ptr(const void* p, const char* name, bool required) {
 
 bool dtype_ok(int d) { return d == KDA_BF16 || d == KDA_FP32; }
 
-const uint32_t kKnownFlags =
-    KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS | KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED;
+const uint32_t kKnownFlags = KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS | KDA_F_SAVE_FOR_BWD |
+                             KDA_F_FWD_SAVED | KDA_F_DH0_ONLY;
 const uint32_t kStepFlags = KDA_F_QK_L2NORM | KDA_F_GATE_IN_KERNEL | KDA_F_BETA_LOGITS;
 
 int validate_desc(const kda_desc* d) {
@@ -193,8 +193,8 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     if (rc) return rc;
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
     if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(hT, "hT", false))) return rc;
-    if (desc->flags & KDA_F_FWD_SAVED) return fail(KDA_ERR_INVALID, "KDA_F_FWD_SAVED is a backward flag");
-    const size_t need = kda::ws_layout(a, (desc->flags & KDA_F_SAVE_FOR_BWD) != 0).total;
+    if (desc->flags & KDA_F_DH0_ONLY) return fail(KDA_ERR_INVALID, "KDA_F_DH0_ONLY is a backward flag");
+    const size_t need = kda::ws_layout(a, (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED)) != 0).total;
     if (ws == nullptr || ws_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
     if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
@@ -216,11 +216,13 @@ int kda_bwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     if (rc) return rc;
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
     if (desc->flags & KDA_F_SAVE_FOR_BWD) return fail(KDA_ERR_INVALID, "KDA_F_SAVE_FOR_BWD is a forward flag");
-    const bool gate = desc->flags & KDA_F_GATE_IN_KERNEL;
+    // with KDA_F_DH0_ONLY only dh0 is produced: the per-token gradients may be null
+    const bool only = desc->flags & KDA_F_DH0_ONLY;
+    const bool gate = (desc->flags & KDA_F_GATE_IN_KERNEL) && !only;
     if ((rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dhT, "dhT", false)) ||
-        (rc = check_ptr(dq, "dq", true)) || (rc = check_ptr(dk, "dk", true)) || (rc = check_ptr(dv, "dv", true)) ||
-        (rc = check_ptr(dg, "dg", true)) || (rc = check_ptr(dbeta, "dbeta", true)) ||
-        (rc = check_ptr(dh0, "dh0", false)) || (rc = check_ptr(dA_log, "dA_log", gate)) ||
+        (rc = check_ptr(dq, "dq", !only)) || (rc = check_ptr(dk, "dk", !only)) || (rc = check_ptr(dv, "dv", !only)) ||
+        (rc = check_ptr(dg, "dg", !only)) || (rc = check_ptr(dbeta, "dbeta", !only)) ||
+        (rc = check_ptr(dh0, "dh0", only)) || (rc = check_ptr(dA_log, "dA_log", gate)) ||
         (rc = check_ptr(ddt_bias, "ddt_bias", gate)))
         return rc;
     const size_t need = kda::ws_layout(a, true).total;
@@ -273,7 +275,7 @@ int kda_segment_maps(const kda_desc* desc, const void* q, const void* k, const v
     if (rc) return rc;
     if (desc->dk != 32 || desc->dv != 64)
         return fail(KDA_ERR_UNSUPPORTED, "segment maps need dk = 32, dv = 64 (got %d, %d)", desc->dk, desc->dv);
-    if (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED)) return fail(KDA_ERR_INVALID, "save/saved flags do not apply");
+    if (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_DH0_ONLY)) return fail(KDA_ERR_INVALID, "flag does not apply");
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, nullptr))) return rc;
     if ((rc = check_ptr(M, "M", true))) return rc;
     const size_t need = kda::ws_layout(a, false).total;

@@ -691,6 +691,7 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
         const int total = a.N * a.H * (DV / BV);
         KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, BV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     }
+    if (a.flags & (1u << 5)) return hipSuccess;  // KDA_F_DH0_ONLY: the state pass alone
     if (a.n_chunks_bound > 0) {
         if constexpr (DK == 32 && DV == 64) {
             KDA_LAUNCH("bwd_chunk", (bwd_chunk_kernel<DV, TIn, TOut, P>), dim3(a.n_chunks_bound, a.H), dim3(kBcThreads),

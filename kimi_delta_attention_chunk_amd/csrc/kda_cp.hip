@@ -141,9 +141,12 @@ __global__ void __launch_bounds__(kThreads) state_scan_kernel(int R, int H, int 
 }
 
 hipError_t launch_segment_maps(const ChunkArgs& a, float* M, hipStream_t s) {
+    // (the forward arrays lead both layouts, so a saved forward's P is read at the same offset)
     const Prm p = make_prm(a, ws_layout(a, false));
-    const hipError_t e = launch_recompute_intra(p, a, s);
-    if (e != hipSuccess) return e;
+    if (!(a.flags & (1u << 4))) {  // not KDA_F_FWD_SAVED: form the chunks' P first
+        const hipError_t e = launch_recompute_intra(p, a, s);
+        if (e != hipSuccess) return e;
+    }
     if (a.in_bf16)
         KDA_LAUNCH("seg_map", seg_map_kernel<Prec::BF3>, dim3(a.N * a.H), dim3(kPsThreads), s, p, M);
     else

@@ -118,14 +118,15 @@ bool dims_supported(int dk, int dv) {
 // forward); `store` : keep the state entering each chunk and v_new (the
 // backward's recompute).
 template <int DK, int DV, typename TIn, typename TOut>
-hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, bool write_o, bool store) {
+hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, bool write_o, bool store,
+                               bool run_intra = true) {
     constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
     if constexpr (DK == 32 && DV == 64) {
         // every array these kernels write must be in the workspace layout
         if (!p.hs || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
         if (store && (!p.tm || !p.aqT)) return hipErrorInvalidValue;
     }
-    if (a.n_chunks_bound > 0)
+    if (run_intra && a.n_chunks_bound > 0)
         KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
     if constexpr (DK == 32 && DV == 64) {
         const int total = a.N * a.H * (DV / kPsBV);
@@ -176,10 +177,11 @@ hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t 
 
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
-    const bool save = a.flags & (1u << 3);
-    const WsLayout L = ws_layout(a, save);
+    const bool save = a.flags & (1u << 3), saved = a.flags & (1u << 4);
+    // (with KDA_F_FWD_SAVED the intra-chunk quantities are already in the save layout)
+    const WsLayout L = ws_layout(a, save || saved);
     const Prm p = make_prm(a, L);
-    return launch_fwd_pipeline<DK, DV, TIn, TOut>(p, a, s, true, save);
+    return launch_fwd_pipeline<DK, DV, TIn, TOut>(p, a, s, true, save, !saved);
 }
 
 template <int DK, int DV>

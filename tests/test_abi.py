@@ -189,3 +189,35 @@ def test_segment_maps_and_state_scan_reject():
     assert lib.kda_state_scan(0, 2, 32, 64, 0, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
     assert lib.kda_state_scan(4, 2, 32, 64, 2, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
     assert lib.kda_state_scan(4, 2, 32, 64, 0, None, _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
+
+
+def test_state_pass_only_and_saved_forward_flags():
+    lib = kda.load_library()
+    fake = _fake(1)
+    # kda_fwd: the state-pass-only flag belongs to the backward
+    d = _desc(flags=B.F_DH0_ONLY)
+    rc = lib.kda_fwd(ctypes.byref(d), *([fake] * 5), None, None, None, None, None, None, fake, None, fake, 1 << 40,
+                     None)
+    assert rc == B.KDA_ERR_INVALID and b"backward flag" in lib.kda_last_error()
+    # kda_fwd with a saved forward sizes its workspace like the saving forward
+    d = _desc(flags=B.F_FWD_SAVED)
+    need = _ws(d, backward=True)
+    assert need > _ws(_desc())
+    rc = lib.kda_fwd(ctypes.byref(d), *([fake] * 5), None, None, None, None, None, None, fake, None, fake, need - 1,
+                     None)
+    assert rc == B.KDA_ERR_WORKSPACE
+    # kda_bwd with the state pass only: dh0 is required, the per-token gradients may be null
+    d = _desc(flags=B.F_DH0_ONLY | B.F_FWD_SAVED)
+    head = [fake] * 5 + [None, None, None, None, None, None]
+    rc = lib.kda_bwd(ctypes.byref(d), *head, fake, None, None, None, None, None, None, None, None, None, fake, 16,
+                     None)
+    assert rc == B.KDA_ERR_INVALID and b"dh0" in lib.kda_last_error()
+    rc = lib.kda_bwd(ctypes.byref(d), *head, fake, None, None, None, None, None, None, _fake(2), None, None, fake, 16,
+                     None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+    # gate parameters are not needed when no gate gradient is formed
+    d = _desc(flags=B.F_DH0_ONLY | B.F_GATE_IN_KERNEL)
+    head_g = [fake] * 5 + [fake, fake, None, None, None, None]
+    rc = lib.kda_bwd(ctypes.byref(d), *head_g, fake, None, None, None, None, None, None, _fake(2), None, None, fake,
+                     16, None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()

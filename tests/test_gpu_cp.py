@@ -14,6 +14,29 @@ from cases import check_close, oracle_bwd, oracle_fwd, prepared, to_dev
 pytestmark = pytest.mark.gpu
 
 
+def _cp_run_saved(d, scale, cu):
+    """The same scheme without repeated work: the chunk quantities are formed once (the
+    first forward keeps them), the maps and the second state pass reuse them, and the
+    first backward pass runs the reverse state pass alone."""
+    T, H = d["q"].shape[1], d["q"].shape[2]
+    cuc = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    plan = kda.plan_varlen(cuc, T)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    R = len(cu) - 1
+    ws = torch.empty(kda.workspace_bytes(tuple(d["q"].shape), d["v"].shape[-1], R, True, d["q"].dtype),
+                     dtype=torch.uint8, device="cuda")
+    pk = dict(cu_seqlens=cuc, plan=plan, workspace=ws)
+    _, c = kda.fwd(*args, scale, save_for_bwd=True, out_dtype=torch.float32, **pk)
+    M = kda.segment_maps(*args, fwd_saved=True, **pk)
+    h_in, hT = kda.state_scan(M, c, d["h0"][0])
+    o, _ = kda.fwd(*args, scale, h0=h_in, fwd_saved=True, save_for_bwd=True, out_dtype=torch.float32, **pk)
+    e = kda.bwd(*args, scale, d["do"], h0=h_in, fwd_saved=True, dh0_only=True, **pk)["dh0"]
+    D, dh0 = kda.state_scan(M, e, d["dhT"][0], transpose=True)
+    gr = kda.bwd(*args, scale, d["do"], h0=h_in, dhT=D, fwd_saved=True, out_dtype=torch.float32, **pk)
+    gr["dh0"] = dh0
+    return o, hT, gr
+
+
 def _cp_run(d, scale, cu, backward):
     T = d["q"].shape[1]
     cuc = torch.tensor(cu, dtype=torch.int32, device="cuda")
@@ -53,6 +76,28 @@ def test_context_parallel_equals_single_pass(dtype, cu):
     for nm in ("dq", "dk", "dv", "dg", "dbeta"):
         check_close(nm, gr[nm], gref[nm], dtype)
     check_close("dh0", gr["dh0"][None], gref["dh0"], dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_context_parallel_from_saved_forward(dtype):
+    """The scheme with the chunk quantities formed once: same results as the plain one,
+    bit for bit, and as the oracle's single pass."""
+    T, H, dk, dv = 2048, 4, 32, 64
+    cu = [0, 300, 1100, 1101, 2048]
+    inp, _ = prepared(13, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, upstream=True, dhT=True)
+    d = to_dev(inp, "cuda:0")
+    scale = dk ** -0.5
+    o1, h1, g1 = _cp_run(d, scale, cu, backward=True)
+    o2, h2, g2 = _cp_run_saved(d, scale, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    for nm in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(g1[nm], g2[nm]), nm
+    oref, href = oracle_fwd(inp, scale)
+    gref = oracle_bwd(inp, scale)
+    check_close("o", o2, oref, dtype)
+    check_close("dk", g2["dk"], gref["dk"], dtype)
+    check_close("dh0", g2["dh0"][None], gref["dh0"], dtype)
 
 
 def test_segment_map_of_one_document_is_its_state_map():
