@@ -132,3 +132,77 @@ def test_step_graph_replay_equals_eager():
         assert torch.equal(h, h_eager), "replay %d: state differs from the eager steps" % rep
         kda.step(q[rep], k[rep], v[rep], f[rep], b[rep], other, scale, **flags)  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_multi_layer_decode_graph(dtype):
+    """Decode through a stack of layers, the output of each layer's step being the v input
+    of the next (written straight into it), every (token, layer) step captured in one HIP
+    graph: the eager chain matches the oracle's chain, and every replay reproduces the
+    eager chain bit for bit."""
+    L, B, H, dk, dv, steps = 3, 32, 4, 32, 64, 5
+    scale = dk ** -0.5
+    layers = [kda_inputs.draw_decode(40 + l, steps, B, H, dk, dv, a_log_range=kda_inputs.A_LOG_RANGE_WEAK)
+              for l in range(L)]
+    dev = []
+    for raw in layers:
+        dev.append(dict(q=raw["q_raw"].to(dtype).cuda(), k=raw["k_raw"].to(dtype).cuda(), f=raw["f"].cuda(),
+                        b=raw["b"].cuda(), h=raw["h"].cuda(),
+                        flags=dict(A_log=raw["A_log"].cuda(), dt_bias=raw["dt_bias"].cuda(), l2norm_qk=True,
+                                   gate_in_kernel=True, beta_logits=True)))
+    v0 = layers[0]["v"].to(dtype).cuda()
+
+    def run(hs, outs, check_rne=False):
+        for t in range(steps):
+            for l, d in enumerate(dev):
+                vin = v0[t] if l == 0 else outs[l - 1][t]
+                if check_rne:  # the same call with an fp32 output, on a copy of the state
+                    o32 = kda.step(d["q"][t], d["k"][t], vin, d["f"][t], d["b"][t], hs[l].clone(), scale,
+                                   out_dtype=torch.float32, **d["flags"])
+                kda.step(d["q"][t], d["k"][t], vin, d["f"][t], d["b"][t], hs[l], scale, out=outs[l][t],
+                         **d["flags"])
+                if check_rne:
+                    assert torch.equal(outs[l][t], o32.to(dtype)), "t=%d layer=%d: not RNE(fp32)" % (t, l)
+
+    h_e = [d["h"].clone() for d in dev]
+    o_e = [torch.empty((steps, B, H, dv), dtype=dtype, device="cuda") for _ in range(L)]
+    run(h_e, o_e, check_rne=dtype == torch.bfloat16)
+    torch.cuda.synchronize()
+
+    # the oracle's chain, in fp64 throughout (the GPU's outputs are never fed to it)
+    href = [to_np(raw["h"]) for raw in layers]
+    prev = None
+    for t in range(steps):
+        for l, raw in enumerate(layers):
+            qh, kh, g, beta = oracle.prep_forward(to_np(dev[l]["q"][t]), to_np(dev[l]["k"][t]), to_np(raw["f"][t]),
+                                                  to_np(raw["A_log"]), to_np(raw["dt_bias"]), to_np(raw["b"][t]))
+            vin = to_np(v0[t]) if l == 0 else prev
+            prev, href[l] = oracle.step(qh, kh, vin, g, beta, scale, href[l])
+            if dtype == torch.float32:
+                check_close("o[t=%d, layer=%d]" % (t, l), o_e[l][t], prev, dtype)
+            else:
+                # a bf16 output is the rounding of the fp32 one (checked above): the bound of an
+                # fp32 output plus its own final rounding, at most 2^-9 of each value
+                got = to_np(o_e[l][t])
+                excess = np.max(np.abs(got - prev) - 2.0 ** -9 * np.abs(prev))
+                assert excess <= 2e-2 * np.sqrt(np.mean(prev ** 2)), "o[t=%d, layer=%d]" % (t, l)
+    for l in range(L):
+        check_close("h[layer=%d]" % l, h_e[l], href[l], dtype)
+
+    hs = [d["h"].clone() for d in dev]
+    outs = [torch.empty_like(o) for o in o_e]
+    run([h.clone() for h in hs], [torch.empty_like(o) for o in o_e])  # warm the launch path
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(hs, outs)
+    for rep in range(3):
+        for l in range(L):
+            hs[l].copy_(dev[l]["h"])
+            outs[l].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(outs[l], o_e[l]), "replay %d: layer %d outputs differ" % (rep, l)
+            assert torch.equal(hs[l], h_e[l]), "replay %d: layer %d state differs" % (rep, l)
