@@ -216,15 +216,17 @@ __device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, 
 // Inverse L2 norms of the raw rows of q or k (NTH / 64 threads per token).
 template <int DK, typename TIn, int NTH>
 __device__ __forceinline__ void row_rnorm(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, float* rn) {
-    constexpr int PT = NTH / kChunk;
-    static_assert(PT == 4 || PT == 8, "threads per token");
+    constexpr int PT = NTH / kChunk, CPT = DK / PT;  // threads per token, channels per thread
+    static_assert((PT == 4 || PT == 8) && CPT % 4 == 0, "threads per token");
     const int t = threadIdx.x / PT, part = threadIdx.x % PT;
     float ss = 0.f;
     if (t < cr.len) {
-        const size_t base = tok_index(cr.t0 + t, h, H, DK);
-        for (int c = part; c < DK; c += PT) {
-            const float x = Elem<TIn>::load(src, base + c);
-            ss += x * x;
+        const TIn* row = src + tok_index(cr.t0 + t, h, H, DK) + CPT * part;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4) {
+            float x[4];
+            load4<TIn>(row + c, x);
+            ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
         }
     }
 #pragma unroll
@@ -403,22 +405,20 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         const int cb = b * kCB;
         stage_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
         stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
-        // this lane's epilogue operands (token t = lane, channels cb + wave + kGWaves j), issued
-        // now so that they arrive during the pair sums
+        // this lane's epilogue operands (token t = lane, channels cb + CPW wave .. + CPW - 1, one
+        // 16-byte access per array), issued now so that they arrive during the pair sums
         constexpr int CPW = kCB / kGWaves;
-        float dq_r[CPW], dkh_r[CPW], dkt_r[CPW], f_r[CPW], db_r[CPW];
-        {
-            const size_t wrow = slot * kChunk * DK + (size_t)t * DK + cb;
-            const size_t grow = tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DK) + cb;
-#pragma unroll
-            for (int j = 0; j < CPW; ++j) {
-                const int cc = wave + kGWaves * j;
-                dq_r[j] = p.dqt[wrow + cc];
-                dkh_r[j] = p.dkh[wrow + cc];
-                dkt_r[j] = p.dkt[wrow + cc];
-                f_r[j] = gate ? p.g[grow + cc] : 0.f;
-                db_r[j] = gate ? p.dt_bias[h * DK + cb + cc] : 0.f;
-            }
+        static_assert(CPW == 4, "one float4 of channels per lane");
+        const int c4 = CPW * wave;  // this wave's first channel in the block
+        float dq_r[CPW], dkh_r[CPW], dkt_r[CPW], f_r[CPW] = {0.f, 0.f, 0.f, 0.f}, db_r[CPW] = {0.f, 0.f, 0.f, 0.f};
+        const size_t wrow = slot * kChunk * DK + (size_t)t * DK + cb + c4;
+        const size_t grow = tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DK) + cb + c4;
+        load4<float>(p.dqt + wrow, dq_r);
+        load4<float>(p.dkh + wrow, dkh_r);
+        load4<float>(p.dkt + wrow, dkt_r);
+        if (gate) {
+            load4<float>(p.g + grow, f_r);
+            load4<float>(p.dt_bias + h * DK + cb + c4, db_r);
         }
         stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // ends with a barrier
         // -- off-diagonal row sums
@@ -487,7 +487,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         float gtv[CPW], ktv[CPW], qtv[CPW], rkv[CPW], rqv[CPW], ckv[CPW], cqv[CPW];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int cc = wave + kGWaves * j;
+            const int cc = c4 + j;
             gtv[j] = GTb[cc * kLD + t];
             ktv[j] = KTb[cc * kLD + t];
             qtv[j] = QTb[cc * kLD + t];
@@ -519,14 +519,15 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         // this lane owns (t, its CPW channels) of the gathered sums
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int cc = wave + kGWaves * j;
+            const int cc = c4 + j;
             ODk[t * LS + cc] += rkv[j];
             ODq[t * LS + cc] += rqv[j];
             ODc[t * LS + cc] += ckv[j] + cqv[j];
         }
+        float dg_o[CPW], dq_o[CPW], dk_o[CPW];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int cc = wave + kGWaves * j;
+            const int cc = c4 + j;
             const float gt = GTb[cc * kLD + t], kt = KTb[cc * kLD + t], qt = QTb[cc * kLD + t];
             const float rk = ODk[t * LS + cc], rq = ODq[t * LS + cc], ck = ODc[t * LS + cc], cq = 0.f;
             const float gam = __expf(gt);
@@ -546,14 +547,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             r_dq += qt * dQ;
             r_dk += kt * dK;
             // reverse in-chunk cumulative sum: dg_t = sum_{u >= t} dG_u
-            float sfx = dG;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_down(sfx, off, 64);
-                if (t + off < 64) sfx += o;
-            }
+            const float sfx = wave_suffix_sum(dG);
             float dgo = sfx;
-            const size_t gi = tok_index(cr.t0 + t, h, p.H, DK) + cb + cc;
             if (gate) {
                 float dfv = 0.f;
                 if (t < cr.len) {
@@ -565,15 +560,18 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                 const float colsum = wave_sum(dfv);
                 if (lane == 0) p.part_dt[slot * DK + cb + cc] = colsum;
             }
-            if (t < cr.len) {
-                p.dg[gi] = dgo;
-                if (l2) {
-                    p.dxq[slot * kChunk * DK + t * DK + cb + cc] = dQ;
-                    p.dxk[slot * kChunk * DK + t * DK + cb + cc] = dK;
-                } else {
-                    Elem<TOut>::store((TOut*)p.dq, gi, dQ);
-                    Elem<TOut>::store((TOut*)p.dk, gi, dK);
-                }
+            dg_o[j] = dgo;
+            dq_o[j] = dQ;
+            dk_o[j] = dK;
+        }
+        if (t < cr.len) {
+            store4<float>(p.dg + grow, dg_o);
+            if (l2) {
+                store4<float>(p.dxq + wrow, dq_o);
+                store4<float>(p.dxk + wrow, dk_o);
+            } else {
+                store4<TOut>((TOut*)p.dq + grow, dq_o);
+                store4<TOut>((TOut*)p.dk + grow, dk_o);
             }
         }
         __syncthreads();  // tiles of this block are reused by the next
@@ -619,18 +617,27 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     if (l2) {
         __syncthreads();
         // dx = r (dx^ - (x^ . dx^) x^), x^ the normalised row
-#pragma unroll 4
-        for (int e_i = 0; e_i < kChunk * DK / kGThreads; ++e_i) {
+        // four consecutive channels per thread and access
+#pragma unroll
+        for (int e_i = 0; e_i < kChunk * DK / 4 / kGThreads; ++e_i) {
             const int e = threadIdx.x + e_i * kGThreads;
-            const int tt = e / DK, cc = e - tt * DK;
+            const int tt = e / (DK / 4), cc = 4 * (e - tt * (DK / 4));
             if (tt >= cr.len) continue;
             const size_t gi = tok_index(cr.t0 + tt, h, p.H, DK) + cc;
-            const float qh = Elem<TIn>::load(qin, gi) * rnq[tt];
-            const float kh = Elem<TIn>::load(kin, gi) * rnk[tt];
-            const float dxq = p.dxq[slot * kChunk * DK + tt * DK + cc];
-            const float dxk = p.dxk[slot * kChunk * DK + tt * DK + cc];
-            Elem<TOut>::store((TOut*)p.dq, gi, rnq[tt] * (dxq - dotq[tt] * qh));
-            Elem<TOut>::store((TOut*)p.dk, gi, rnk[tt] * (dxk - dotk[tt] * kh));
+            const size_t wi = slot * kChunk * DK + (size_t)tt * DK + cc;
+            float xq[4], xk[4], dxq[4], dxk[4], oq[4], ok[4];
+            load4<TIn>(qin + gi, xq);
+            load4<TIn>(kin + gi, xk);
+            load4<float>(p.dxq + wi, dxq);
+            load4<float>(p.dxk + wi, dxk);
+            const float rq = rnq[tt], rk = rnk[tt], sq = dotq[tt], sk = dotk[tt];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                oq[i] = rq * (dxq[i] - sq * (xq[i] * rq));
+                ok[i] = rk * (dxk[i] - sk * (xk[i] * rk));
+            }
+            store4<TOut>((TOut*)p.dq + gi, oq);
+            store4<TOut>((TOut*)p.dk + gi, ok);
         }
     }
 }

@@ -194,6 +194,26 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
 }
 
+// Inclusive suffix sum over the 64 lanes: lane t receives x_t + x_{t+1} + ... + x_63.
+// Within each 16-lane row a shift-left scan (row_shl 1, 2, 4, 8; lanes past the
+// row end read 0), then the totals of the later rows are added: a row's total is
+// its first lane after the scan, and the permlane swaps bring the other rows'.
+__device__ __forceinline__ float wave_suffix_sum(float x) {
+    x += dpp_f<0x101>(x);  // row_shl:1
+    x += dpp_f<0x102>(x);  // row_shl:2
+    x += dpp_f<0x104>(x);  // row_shl:4
+    x += dpp_f<0x108>(x);  // row_shl:8
+    const float tot = row_bcast<0>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(tot), __float_as_int(tot), false, false);
+    const float odd = __int_as_float(a[1]);  // total of the odd row of this lane's pair (row 1 or 3)
+    const float pair = __int_as_float(a[0]) + odd;
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(pair), __float_as_int(pair), false, false);
+    const float upper = __int_as_float(b[1]);  // rows 2 + 3
+    const int r = (threadIdx.x & 63) >> 4;
+    const float later = r == 0 ? odd + upper : r == 1 ? upper : r == 2 ? odd : 0.f;
+    return x + later;
+}
+
 // f(std::integral_constant<int, u>) for u = 0 .. 15, in order (for DPP
 // controls and other immediates that must be compile-time constants).
 template <class F, int... U>

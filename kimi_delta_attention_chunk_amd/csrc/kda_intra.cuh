@@ -31,17 +31,6 @@ namespace kda {
 constexpr int kCB32 = 32;        // channels per block
 constexpr int kLB = kCB32 + 4;   // row stride of [token][channel-block] tiles
 
-// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
-__device__ __forceinline__ float wave_scan(float x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
 // The p-th pair (t, s), s <= t, of the four 16x16 diagonal blocks (136 each).
 __device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
     const int I = p / 136, q = p - 136 * I;
