@@ -160,46 +160,71 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
 // ============================================================== dk-side
 constexpr int kCB = 32;  // channels per block in the dk-side kernel
 
-// Stage channels [cb, cb+kCB) of q or k into XT[c][t] (times the row's
-// inverse norm if `rn` is given); zero past the chunk end.
+// Channel blocks [cb, cb + kCB) are staged in two steps, so that a block's
+// global loads can be issued one block ahead: load_* brings this thread's
+// values into registers (zero past the chunk end), put_* writes them to LDS.
+// q or k: thread element e = tid + NTH i is (token e / kCB, channel e % kCB).
+template <int NTH>
+struct QkBlock {
+    float x[kChunk * kCB / NTH];
+};
 template <int DK, typename TIn, int NTH>
-__device__ __forceinline__ void stage_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
-                               const float* rn, float* XT) {
-    #pragma unroll
-    for (int e_i = 0; e_i < (kChunk * kCB) / NTH; ++e_i) {
-        const int e = threadIdx.x + e_i * NTH;
+__device__ __forceinline__ void load_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
+                                              QkBlock<NTH>& r) {
+#pragma unroll
+    for (int i = 0; i < kChunk * kCB / NTH; ++i) {
+        const int e = threadIdx.x + i * NTH;
         const int t = e / kCB, cc = e - t * kCB;
-        float x = 0.f;
-        if (t < cr.len) {
-            x = Elem<TIn>::load(src, tok_index(cr.t0 + t, h, H, DK) + cb + cc);
-            if (rn) x *= rn[t];
-        }
-        XT[cc * kLD + t] = x;
+        const float x = Elem<TIn>::load(src, tok_index(cr.t0 + (t < cr.len ? t : 0), h, H, DK) + cb + cc);
+        r.x[i] = t < cr.len ? x : 0.f;
+    }
+}
+// XT[c][t] = x (times the row's inverse norm if `rn` is given)
+template <int NTH>
+__device__ __forceinline__ void put_qk_block(const QkBlock<NTH>& r, const float* rn, float* XT) {
+#pragma unroll
+    for (int i = 0; i < kChunk * kCB / NTH; ++i) {
+        const int e = threadIdx.x + i * NTH;
+        const int t = e / kCB, cc = e - t * kCB;
+        XT[cc * kLD + t] = rn ? r.x[i] * rn[t] : r.x[i];
     }
 }
 
-// Stage channels [cb, cb+kCB) of the log-decay (gate from f if flagged) and
-// form their in-chunk cumulative sums into GT[c][t].  Also returns, in graw
-// (nullable), the per-token log-decay itself.  Thread (sg, c) = (tid >> 5,
-// tid & 31) loads R consecutive tokens of channel c (coalesced rows), scans
-// them in registers and adds the totals of the earlier segments (seg: LDS
-// [64 / R][32]).  Ends with a barrier.
+// The log-decay (or the raw gate input f) of channels [cb, cb + kCB): thread
+// (sg, c) = (tid >> 5, tid & 31) holds R consecutive tokens of channel c.
+template <int NTH>
+struct GBlock {
+    static constexpr int R = kChunk * kCB / NTH;
+    float x[R];
+    float db;  // dt_bias of the channel (gate flag)
+};
 template <int DK, int NTH>
-__device__ __forceinline__ void stage_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, float* GT, float* graw,
-                                              float* seg) {
-    constexpr int R = kChunk * kCB / NTH, NS = kChunk / R;
+__device__ __forceinline__ void load_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, GBlock<NTH>& r) {
+    constexpr int R = GBlock<NTH>::R;
+    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int t = R * sg + i;
+        r.x[i] = p.g[tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DK) + cb + c];
+    }
+    r.db = (p.flags & 2u) ? p.dt_bias[h * DK + cb + c] : 0.f;
+}
+// GT[c][t] = in-chunk cumulative log-decay (the gate from f if flagged; zero
+// past the chunk end).  Thread (sg, c) scans its R tokens in registers and adds
+// the totals of the earlier segments (seg: LDS [64 / R][32]).  Two barriers;
+// ends with one.
+template <int NTH>
+__device__ __forceinline__ void put_g_block(const Prm& p, const ChunkRef& cr, int h, const GBlock<NTH>& r, float* GT,
+                                            float* seg) {
+    constexpr int R = GBlock<NTH>::R, NS = kChunk / R;
     const bool gate = p.flags & 2u;
     const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
     const float nA = gate ? -expf(p.A_log[h]) : 0.f;
-    const float db = gate ? p.dt_bias[h * DK + cb + c] : 0.f;
     float x[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int t = R * sg + i;
-        const int tc = t < cr.len ? t : 0;
-        const float v = p.g[tok_index(cr.t0 + tc, h, p.H, DK) + cb + c];
-        x[i] = t < cr.len ? (gate ? nA * softplus_f(v + db) : v) : 0.f;
-        if (graw) graw[c * kLD + t] = x[i];
+        x[i] = t < cr.len ? (gate ? nA * softplus_f(r.x[i] + r.db) : r.x[i]) : 0.f;
     }
 #pragma unroll
     for (int i = 1; i < R; ++i) x[i] += x[i - 1];
@@ -293,6 +318,23 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     }
     if (threadIdx.x < DK) dgl[threadIdx.x] = p.dgl[slot * DK + threadIdx.x];
     __syncthreads();
+    // channel block 0 of k, the log-decay and dw, for phase 3
+    QkBlock<kGThreads> qr, kr;
+    GBlock<kGThreads> gr;
+    constexpr int NE = kChunk * kCB / kGThreads;
+    float dwr[NE];
+    const float* dwi = p.dwv + slot * kChunk * DK;
+    auto load_dw = [&](int cb) {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = threadIdx.x + i * kGThreads;
+            const int t = e / kCB, cc = e - t * kCB;
+            dwr[i] = dwi[t * DK + cb + cc];
+        }
+    };
+    load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, 0, kr);
+    load_g_block<DK, kGThreads>(p, cr, h, 0, gr);
+    load_dw(0);
     if (l2) {
         row_rnorm<DK, TIn, kGThreads>(qin, cr, h, p.H, rnq);
         row_rnorm<DK, TIn, kGThreads>(kin, cr, h, p.H, rnk);
@@ -300,20 +342,29 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     __syncthreads();
 
     // ---- phase 3: dT += dw (beta Kg)^T ; dKg = beta . (T^T dw) ; dbeta_w
+    // (each block's global loads are issued during the block before)
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
-        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // barrier inside covers KTb
-        const float* dwi = p.dwv + slot * kChunk * DK;
-        #pragma unroll
-    for (int e_i = 0; e_i < (kChunk * kCB) / kGThreads; ++e_i) {
-        const int e = threadIdx.x + e_i * kGThreads;
+        put_qk_block<kGThreads>(kr, l2 ? rnk : nullptr, KTb);
+        put_g_block<kGThreads>(p, cr, h, gr, GTb, gseg);  // its barriers cover KTb
+        if (b + 1 < NB) {
+            load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
+            load_g_block<DK, kGThreads>(p, cr, h, cb + kCB, gr);
+        } else {  // the first block of the pair-sum phase
+            load_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, 0, qr);
+            load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, 0, kr);
+            load_g_block<DK, kGThreads>(p, cr, h, 0, gr);
+        }
+#pragma unroll
+        for (int e_i = 0; e_i < NE; ++e_i) {
+            const int e = threadIdx.x + e_i * kGThreads;
             const int t = e / kCB, cc = e - t * kCB;
-            X1[t * LC + cc] = dwi[t * DK + cb + cc];
+            X1[t * LC + cc] = dwr[e_i];
             const float kg = KTb[cc * kLD + t] * __expf(GTb[cc * kLD + t]);
             X2[t * LC + cc] = kg;                 // Kg[t][c]
             QTb[cc * kLD + t] = bet[t] * kg;      // (beta Kg)^T, reusing the q tile
         }
+        if (b + 1 < NB) load_dw(cb + kCB);
         __syncthreads();
         {
             constexpr int TILES = 16;  // 64 x 64 tiles of dT
@@ -403,8 +454,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     static_assert(2 * kChunk * LS <= kChunk * kLD && kChunk * LS <= kChunk * LC, "pair-sum staging must fit");
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        stage_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb, l2 ? rnq : nullptr, QTb);
-        stage_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb, l2 ? rnk : nullptr, KTb);
+        put_qk_block<kGThreads>(qr, l2 ? rnq : nullptr, QTb);
+        put_qk_block<kGThreads>(kr, l2 ? rnk : nullptr, KTb);
         // this lane's epilogue operands (token t = lane, channels cb + CPW wave .. + CPW - 1, one
         // 16-byte access per array), issued now so that they arrive during the pair sums
         constexpr int CPW = kCB / kGWaves;
@@ -420,7 +471,12 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             load4<float>(p.g + grow, f_r);
             load4<float>(p.dt_bias + h * DK + cb + c4, db_r);
         }
-        stage_g_block<DK, kGThreads>(p, cr, h, cb, GTb, nullptr, gseg);  // ends with a barrier
+        put_g_block<kGThreads>(p, cr, h, gr, GTb, gseg);  // ends with a barrier
+        if (b + 1 < NB) {
+            load_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb + kCB, qr);
+            load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
+            load_g_block<DK, kGThreads>(p, cr, h, cb + kCB, gr);
+        }
         // -- off-diagonal row sums
 #pragma unroll
         for (int e_i = 0; e_i < kChunk * kCB / kGThreads; ++e_i) {
