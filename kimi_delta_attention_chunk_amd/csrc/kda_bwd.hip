@@ -38,19 +38,61 @@ namespace kda {
 // tiles take most of the LDS, so one workgroup fits per CU.
 constexpr int kGThreads = 512, kGWaves = kGThreads / 64;
 
+// acc += A B^T over [k0, k1) on swizzled tiles (origins at their view rows).
+// AH / BH: that operand holds bf16 numbers, stored with put_hi (no lo part).
+template <bool AH, bool BH, Prec P, int CA, int CB>
+__device__ __forceinline__ f32x4 mma_st(const STile<P, CA>& A, const STile<P, CB>& B, int k0, int k1, f32x4 acc) {
+    static_assert(!(AH && BH), "at most one operand without a lo part");
+    if constexpr (P == Prec::F32) {
+        return mma_tile(A, B, k0, k1, acc);
+    } else {
+        for (int kb = k0; kb < k1; kb += 32) {
+            AFrag<P> a, b;
+            if constexpr (AH) load_frag_hi(a, A, kb); else load_frag(a, A, kb);
+            if constexpr (BH) load_frag_hi(b, B, kb); else load_frag(b, B, kb);
+            if constexpr (AH) acc = mma_ff_ah(a, b, acc);
+            else if constexpr (BH) acc = mma_ff_bh(a, b, acc);
+            else acc = mma_ff(a, b, acc);
+        }
+        return acc;
+    }
+}
+// The same product into every tile of a TileSet that this wave owns.
+template <bool AH, bool BH, class TS, Prec P, int CA, int CB>
+__device__ __forceinline__ void tiles_mma(TS& ts, const STile<P, CA>& A, const STile<P, CB>& B, int k0, int k1) {
+    const int wave = wave_id();
+#pragma unroll
+    for (int i = 0; i < TS::PER; ++i) {
+        const int tile = wave + i * TS::NWAVES;
+        if (tile < TS::TILES) {
+            const int tm = tile / TS::TN, tn = tile % TS::TN;
+            ts.acc[i] = mma_st<AH, BH>(A.sub(16 * tm), B.sub(16 * tn), k0, k1, ts.acc[i]);
+        }
+    }
+}
+
+// Per 32-column block jb of v: the products over the block's columns, accumulated
+// in registers across the blocks (P: bf16x3 MFMA for bf16 inputs, fp32 MFMA for
+// fp32 inputs; dO and v are input values, so for bf16 inputs their lo parts are
+// zero and those products take two MFMAs):
+//   dQg += dO h^T, dKh += vn D^T, dw += dvn h^T, dAqk += dO vn^T, dT_v += dvn V^T
+// and X_u = T^T dvn (dV = beta X_u, dbeta_v = rowsum(X_u V)); dGamma_L = rowsum(h D).
 template <int DK, int DV, typename TIn, typename TOut>
 __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
-    constexpr int VB = 32, LB = VB + 4, NG = DV / 16;
-    __shared__ float Tm[kChunk * kLD];
-    __shared__ float Hb[DK * LB];
-    __shared__ float Db[DK * LB];
-    __shared__ float DOb[kChunk * LB];
-    __shared__ float VNb[kChunk * LB];
-    __shared__ float DVNb[kChunk * LB];
-    __shared__ float Vb[kChunk * LB];
+    constexpr int VB = 32, NG = DV / 16;
+    constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
+    using T32 = STile<P, 32>;
+    using T64 = STile<P, 64>;
+    constexpr int F32R = P == Prec::F32 ? 40 : 32, F64R = P == Prec::F32 ? 72 : 64;  // floats per tile row
+    __shared__ __attribute__((aligned(16))) float sT[kChunk * F64R];     // T^T [t][s]
+    __shared__ __attribute__((aligned(16))) float sDVT[VB * F64R];       // dvn^T [j][s]
+    __shared__ __attribute__((aligned(16))) float sH[DK * F32R], sD[DK * F32R];
+    __shared__ __attribute__((aligned(16))) float sDO[kChunk * F32R], sV[kChunk * F32R];
+    __shared__ __attribute__((aligned(16))) float sVN[kChunk * F32R], sDVN[kChunk * F32R];
     __shared__ float bet[kChunk];
     __shared__ float dbv_part[kChunk * NG];
-    __shared__ float dgl[DK];
+    const T64 TT(sT, kChunk), DVT(sDVT, VB);
+    const T32 Hs(sH, DK), Ds(sD, DK), DOs(sDO, kChunk), Vs(sV, kChunk), VNs(sVN, kChunk), DVNs(sDVN, kChunk);
 
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
@@ -59,16 +101,22 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     const TIn* dO = (const TIn*)p.d_o;
     const TIn* vin = (const TIn*)p.v;
     TOut* dvout = (TOut*)p.dv;
-    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
 
-    const float* tmi = p.tm + slot * kChunk * kChunk;
-    #pragma unroll
-    for (int e_i = 0; e_i < kChunk * kChunk / kGThreads; ++e_i) {
-        const int e = threadIdx.x + e_i * kGThreads;
-        Tm[(e >> 6) * kLD + (e & 63)] = tmi[e];
+    {
+        // T^T: row t of the tile holds T[s][t] over s (T is unit lower triangular)
+        const float* tmi = p.tm + slot * kChunk * kChunk;
+#pragma unroll
+        for (int i = 0; i < kChunk * kChunk / 4 / kGThreads; ++i) {
+            const int e4 = tid + i * kGThreads;
+            const int s_ = e4 / (kChunk / 4), t4 = 4 * (e4 % (kChunk / 4));
+            const f32x4 x = *(const f32x4*)(tmi + s_ * kChunk + t4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) TT.put(t4 + r, s_, x[r]);
+        }
     }
-    if (threadIdx.x < kChunk) {
-        const int t = threadIdx.x;
+    if (tid < kChunk) {
+        const int t = tid;
         float b = 0.f;
         if (t < cr.len) {
             b = p.beta[(size_t)(cr.t0 + t) * p.H + h];
@@ -76,7 +124,6 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
         }
         bet[t] = b;
     }
-    if (threadIdx.x < DK) dgl[threadIdx.x] = 0.f;
 
     TileSet<kChunk, DK, kGWaves> aQ, aKh, aW;
     TileSet<kChunk, kChunk, kGWaves> aAq, aT;
@@ -86,54 +133,69 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     const float* dhs = p.dhs + slot * DK * DV;
     const float* vn = p.vn + slot * kChunk * DV;
     const float* dvn = p.dvn + slot * kChunk * DV;
+    // thread's float4 of the h / D block (fixed rows over the blocks) and its row-sum partials
+    constexpr int HQ = DK * VB / 4 / kGThreads;
+    static_assert(HQ >= 1 && kChunk * VB / 4 == kGThreads, "one float4 of each token block per thread");
+    float hd[HQ];
+#pragma unroll
+    for (int i = 0; i < HQ; ++i) hd[i] = 0.f;
+    const int tt = tid / (VB / 4), j4 = 4 * (tid % (VB / 4));  // token block: (token, 4 columns)
+    const bool tin = tt < cr.len;
+    const size_t tok = tok_index(cr.t0 + (tin ? tt : 0), h, p.H, DV);
     for (int jb = 0; jb < DV; jb += VB) {
-        __syncthreads();
-        #pragma unroll
-    for (int e_i = 0; e_i < (DK * VB) / kGThreads; ++e_i) {
-        const int e = threadIdx.x + e_i * kGThreads;
-            const int cc = e / VB, j = e - cc * VB;
-            Hb[cc * LB + j] = hs[cc * DV + jb + j];
-            Db[cc * LB + j] = dhs[cc * DV + jb + j];
+        __syncthreads();  // the previous block's readers are done
+#pragma unroll
+        for (int i = 0; i < HQ; ++i) {
+            const int e4 = tid + i * kGThreads;
+            const int cc = e4 / (VB / 4), q4 = 4 * (e4 % (VB / 4));
+            const f32x4 xh = *(const f32x4*)(hs + cc * DV + jb + q4);
+            const f32x4 xd = *(const f32x4*)(dhs + cc * DV + jb + q4);
+            Hs.put4(cc, q4, xh);
+            Ds.put4(cc, q4, xd);
+            hd[i] += xh[0] * xd[0] + xh[1] * xd[1] + xh[2] * xd[2] + xh[3] * xd[3];
         }
-        #pragma unroll
-    for (int e_i = 0; e_i < (kChunk * VB) / kGThreads; ++e_i) {
-        const int e = threadIdx.x + e_i * kGThreads;
-            const int t = e / VB, j = e - t * VB;
-            const bool in = t < cr.len;
-            const size_t gi = tok_index(cr.t0 + t, h, p.H, DV) + jb + j;
-            DOb[t * LB + j] = in ? Elem<TIn>::load(dO, gi) : 0.f;
-            Vb[t * LB + j] = in ? Elem<TIn>::load(vin, gi) : 0.f;
-            VNb[t * LB + j] = vn[t * DV + jb + j];
-            DVNb[t * LB + j] = dvn[t * DV + jb + j];
+        {
+            float xo[4], xv[4];
+            load4<TIn>(dO + tok + jb + j4, xo);
+            load4<TIn>(vin + tok + jb + j4, xv);
+            const f32x4 xn = *(const f32x4*)(vn + tt * DV + jb + j4);
+            const f32x4 xdn = *(const f32x4*)(dvn + tt * DV + jb + j4);
+            f32x4 o4, v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                o4[r] = tin ? xo[r] : 0.f;
+                v4[r] = tin ? xv[r] : 0.f;
+                DVT.put(j4 + r, tt, xdn[r]);
+            }
+            DOs.put4_hi(tt, j4, o4);
+            Vs.put4_hi(tt, j4, v4);
+            VNs.put4(tt, j4, xn);
+            DVNs.put4(tt, j4, xdn);
         }
         __syncthreads();
-        aQ.mma(DOb, LB, 1, Hb, 1, LB, VB);
-        aKh.mma(VNb, LB, 1, Db, 1, LB, VB);
-        aW.mma(DVNb, LB, 1, Hb, 1, LB, VB);
-        aAq.mma(DOb, LB, 1, VNb, 1, LB, VB);
-        aT.mma(DVNb, LB, 1, Vb, 1, LB, VB);
+        tiles_mma<true, false>(aQ, DOs, Hs, 0, VB);
+        tiles_mma<false, false>(aKh, VNs, Ds, 0, VB);
+        tiles_mma<false, false>(aW, DVNs, Hs, 0, VB);
+        tiles_mma<true, false>(aAq, DOs, VNs, 0, VB);
+        tiles_mma<false, true>(aT, DVNs, Vs, 0, VB);
         // X_u = T^T dvn  ->  dV = beta . X_u,  dbeta_v = rowsum(X_u . V)
         {
             constexpr int TN = VB / 16, TILES = (kChunk / 16) * TN;
             for (int tile = wave; tile < TILES; tile += kGWaves) {
                 const int tm = tile / TN, tn = tile % TN;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma16_f32(Tm + tm * 16, 1, kLD, DVNb + tn * 16, LB, 1, 16 * tm, kChunk, acc);
+                int k0 = 16 * tm, k1 = kChunk;
+                widen<P>(k0, k1);
+                const f32x4 acc = mma_st<false, false>(TT.sub(16 * tm), DVT.sub(16 * tn), k0, k1,
+                                                       f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = tm * 16 + 4 * (lane >> 4) + i, j = tn * 16 + (lane & 15);
                     if (t < cr.len)
                         Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + jb + j, bet[t] * acc[i]);
-                    const float part = row16_sum(acc[i] * Vb[t * LB + j]);
+                    const float part = row16_sum(acc[i] * Vs.get_hi(t, j));
                     if ((lane & 15) == 0) dbv_part[t * NG + (jb >> 4) + tn] = part;
                 }
             }
-        }
-        if (threadIdx.x < DK) {
-            const int cc = threadIdx.x;
-            float acc = 0.f;
-            for (int j = 0; j < VB; ++j) acc += Hb[cc * LB + j] * Db[cc * LB + j];
-            dgl[cc] += acc;
         }
     }
     const float scale = p.scale;
@@ -147,14 +209,20 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     aW.store([&](int t, int cc, float x) { o_w[t * DK + cc] = -x; });
     aAq.store([&](int t, int s, float x) { o_aq[t * kChunk + s] = s <= t ? scale * x : 0.f; });
     aT.store([&](int t, int s, float x) { o_t[t * kChunk + s] = bet[s] * x; });
+    // dGamma_L: the VB / 4 = 8 consecutive lanes sharing a row of h hold its partial sums
+#pragma unroll
+    for (int i = 0; i < HQ; ++i) {
+        const float sum = sum8(hd[i]);
+        const int e4 = tid + i * kGThreads;
+        if ((e4 % (VB / 4)) == 0) p.dgl[slot * DK + e4 / (VB / 4)] = sum;
+    }
     __syncthreads();
-    if (threadIdx.x < kChunk) {
-        const int t = threadIdx.x;
+    if (tid < kChunk) {
+        const int t = tid;
         float acc = 0.f;
         for (int gidx = 0; gidx < NG; ++gidx) acc += dbv_part[t * NG + gidx];
         p.dbv[slot * kChunk + t] = acc;
     }
-    if (threadIdx.x < DK) p.dgl[slot * DK + threadIdx.x] = dgl[threadIdx.x];
 }
 
 // ============================================================== dk-side

@@ -268,7 +268,7 @@ hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t 
 // accumulated over blocks of their contraction index without LDS traffic.
 template <int M, int N, int NW = kWaves>
 struct TileSet {
-    static constexpr int TN = N / 16, TILES = (M / 16) * TN;
+    static constexpr int TN = N / 16, TILES = (M / 16) * TN, NWAVES = NW;
     static constexpr int PER = (TILES + NW - 1) / NW;
     f32x4 acc[PER];
     __device__ __forceinline__ void zero() {
