@@ -1,6 +1,7 @@
-"""Parity of the exact launch configuration bench.py times (the 300M layer shape,
-B=16, T=2048, H=8, dk=32, dv=64, bf16 q/k/v, fused preparation, one workspace with
-save-for-backward, bf16 outputs), element by element against the oracle.
+"""Parity of the exact launch configurations bench.py times, element by element
+against the oracle: the 300M layer shape (B=16, T=2048, H=8, dk=32, dv=64) and the
+larger-head workload (B=2, T=8192, H=16, dk=dv=128), both with bf16 q/k/v, fused
+preparation, one workspace with save-for-backward and bf16 outputs.
 
 bf16 outputs: the same calls with fp32 outputs are checked against the oracle at
 the bf16-input bound, and the bf16 outputs must be their round-to-nearest-even,
@@ -28,8 +29,11 @@ def _run(d, out_dtype):
     return o, hT, g
 
 
-def test_bench_configuration():
-    raw = kda_inputs.draw(1, 16, 2048, 8, 32, 64, upstream=True)   # the bench's own draw
+@pytest.mark.parametrize("shape,seed", [((16, 2048, 8, 32, 64), 1), ((2, 8192, 16, 128, 128), 4)],
+                         ids=["layer300M_B16", "dk128_B2_T8192_H16"])
+def test_bench_configuration(shape, seed):
+    B, T, H, dk, dv = shape
+    raw = kda_inputs.draw(seed, B, T, H, dk, dv, upstream=True)   # the bench's own draw
     rin = raw_inputs(raw, torch.bfloat16)
     d = to_dev(rin)
     o32, h32, g32 = _run(d, torch.float32)
@@ -41,7 +45,7 @@ def test_bench_configuration():
         assert torch.equal(g32[nm].to(torch.bfloat16), g16[nm]), nm
     for nm in ("dg", "dbeta", "dA_log", "ddt_bias"):
         assert torch.equal(g32[nm], g16[nm]), nm
-    scale = 32 ** -0.5
+    scale = dk ** -0.5
     oref, href = oracle_fwd_raw(rin, scale)
     check_close("o", o32, oref, torch.bfloat16)
     check_close("hT", h32, href, torch.bfloat16)
