@@ -29,7 +29,6 @@
 namespace kda {
 
 constexpr int kLD = kChunk + 4;  // padded stride of [channel][token] tiles
-constexpr int kBV = 32;          // state columns per workgroup of the sequential passes
 
 // Logical workgroup id such that consecutive logical ids run on the same XCD
 // (hardware deals workgroups round-robin over the 8 XCDs, each with its own
@@ -72,94 +71,6 @@ struct Prm {
 
 __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
     return ((size_t)t * H + h) * d;
-}
-
-// Stage q or k of one chunk into XT[c][t] (zero past the chunk end), and
-// L2-normalise every token if `l2`.  Ends with a barrier.
-template <int DK, typename TIn>
-__device__ __forceinline__ void stage_qk(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, bool l2,
-                         float* XT, float* rnorm /* [64] scratch, nullable if !l2 */) {
-    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
-        const int t = e / DK, c = e - t * DK;
-        float x = 0.f;
-        if (t < cr.len) x = Elem<TIn>::load(src, tok_index(cr.t0 + t, h, H, DK) + c);
-        XT[c * kLD + t] = x;
-    }
-    __syncthreads();
-    if (l2) {
-        if (threadIdx.x < kChunk) {
-            const int t = threadIdx.x;
-            float ss = 0.f;
-            for (int c = 0; c < DK; ++c) ss += XT[c * kLD + t] * XT[c * kLD + t];
-            rnorm[t] = 1.0f / sqrtf(ss + kL2Eps);
-        }
-        __syncthreads();
-        for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
-            const int c = e / kChunk, t = e - c * kChunk;
-            XT[c * kLD + t] *= rnorm[t];
-        }
-        __syncthreads();
-    }
-}
-
-// Stage the log-decay of one chunk (computing the gate from f if the gate
-// flag is set) and turn it into the in-chunk cumulative sum GT[c][t].  Past
-// the chunk end g = 0, so G stays at G_{L-1}.  Optionally also stages beta
-// (sigmoid of logits if flagged; 0 past the end).  Ends with a barrier.
-template <int DK>
-__device__ __forceinline__ void stage_g(const Prm& p, const ChunkRef& cr, int h, float* GT, float* bet) {
-    const bool gate = p.flags & 2u;
-    for (int e = threadIdx.x; e < kChunk * DK; e += kThreads) {
-        const int t = e / DK, c = e - t * DK;
-        float x = 0.f;
-        if (t < cr.len) {
-            x = p.g[tok_index(cr.t0 + t, h, p.H, DK) + c];
-            if (gate) x = -expf(p.A_log[h]) * softplus_f(x + p.dt_bias[h * DK + c]);
-        }
-        GT[c * kLD + t] = x;
-    }
-    if (bet != nullptr && threadIdx.x < kChunk) {
-        const int t = threadIdx.x;
-        float b = 0.f;
-        if (t < cr.len) {
-            b = p.beta[(size_t)(cr.t0 + t) * p.H + h];
-            if (p.flags & 4u) b = sigmoid_f(b);
-        }
-        bet[t] = b;
-    }
-    __syncthreads();
-    if (threadIdx.x < DK) {
-        const int c = threadIdx.x;
-        float acc = 0.f;
-        for (int t = 0; t < kChunk; ++t) {
-            acc += GT[c * kLD + t];
-            GT[c * kLD + t] = acc;
-        }
-    }
-    __syncthreads();
-}
-
-// Pairwise decayed Gram matrices of one chunk (exact exp of each difference):
-//   A[t][s]  = beta_t sum_c K_tc K_sc e^{G_tc-G_sc}   (s < t, else 0)
-//   Aq(t,s)  =        sum_c Q_tc K_sc e^{G_tc-G_sc}   (s <= t, else 0), passed to `aq_out`
-// Each wave owns one row t at a time; its lanes run over s.
-template <int DK, class AqOut>
-__device__ __forceinline__ void gram_pairwise(const float* KT, const float* QT, const float* GT, const float* bet,
-                              float* A, AqOut aq_out) {
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
-        const int t = e >> 6, s = e & 63;
-        float akk = 0.f, aqk = 0.f;
-        if (s <= t) {
-            for (int c = 0; c < DK; ++c) {
-                const float ex = __expf(GT[c * kLD + t] - GT[c * kLD + s]);
-                const float ks = KT[c * kLD + s] * ex;
-                akk += KT[c * kLD + t] * ks;
-                if (QT) aqk += QT[c * kLD + t] * ks;
-            }
-        }
-        A[t * kLD + s] = (s < t) ? bet[t] * akk : 0.f;
-        aq_out(t, s, (s <= t) ? aqk : 0.f);
-    }
 }
 
 // T = (I + A)^{-1} for strictly lower-triangular A (64x64, stride kLD), by
@@ -246,15 +157,6 @@ __device__ __forceinline__ void col_scan_regs(float (&x)[R], float* A, int ld, f
     __syncthreads();
 }
 
-// Lower-triangular k-range for products T * X (T zero above the diagonal blocks).
-struct TriK {
-    __device__ __forceinline__ void operator()(int tm, int, int& k0, int& k1) const { k0 = 0; k1 = 16 * (tm + 1); }
-};
-// Upper-triangular k-range for products T^T * X (rows of T^T are zero left of the block).
-struct TriKUpper {
-    __device__ __forceinline__ void operator()(int tm, int, int& k0, int& k1) const { k0 = 16 * tm; k1 = kChunk; }
-};
-
 // ----------------------------------------------------------------- host helpers
 // (kda_fwd.hip) Kernel parameters of a call, and the forward recompute used
 // by the backward: intra-chunk (w, u, Aqk and, if p.tm is set, T) then the
@@ -274,18 +176,6 @@ struct TileSet {
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int i = 0; i < PER; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // acc += A(M x K) * B(K x N) with element strides as in mma16_f32
-    __device__ __forceinline__ void mma(const float* A, int am, int ak, const float* B, int bk, int bn, int K) {
-        const int wave = wave_id();
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int tile = wave + i * NW;
-            if (tile < TILES) {
-                const int tm = tile / TN, tn = tile % TN;
-                acc[i] = mma16_f32(A + tm * 16 * am, am, ak, B + tn * 16 * bn, bk, bn, 0, K, acc[i]);
-            }
-        }
     }
     template <class F>
     __device__ __forceinline__ void store(F f) const {

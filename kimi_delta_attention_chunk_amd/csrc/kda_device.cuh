@@ -26,10 +26,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // value: tile and row offsets derived from it stay in SGPRs instead of being
 // recomputed per lane.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-// x of lane s of this wave (s wave-uniform), as a scalar
-__device__ __forceinline__ float lane_value(float x, int s) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), s));
-}
 
 // ----------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
@@ -239,30 +235,6 @@ __device__ __forceinline__ f32x4 mma16_f32(const float* A, int am, int ak, const
     }
     return acc;
 }
-
-// Workgroup GEMM over 16x16 output tiles, tiles dealt round-robin to waves.
-//   out(m,n) = sum_k A(m,k) B(k,n), M x N x K, all multiples of 16 (K of 4).
-// `krange(tm, tn, &k0, &k1)` may narrow the k range of a tile (triangular
-// operands); `epi(m, n, value)` consumes each result element.
-template <int M, int N, class KRange, class Epi>
-__device__ __forceinline__ void wg_gemm(const float* A, int am, int ak, const float* B, int bk,
-                                        int bn, int K, KRange krange, Epi epi) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    constexpr int TN = N / 16, TILES = (M / 16) * (N / 16);
-    for (int tile = wave; tile < TILES; tile += kWaves) {
-        const int tm = tile / TN, tn = tile % TN;
-        int k0 = 0, k1 = K;
-        krange(tm, tn, k0, k1);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (k1 > k0) acc = mma16_f32(A + tm * 16 * am, am, ak, B + tn * 16 * bn, bk, bn, k0, k1, acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) epi(tm * 16 + 4 * (lane >> 4) + i, tn * 16 + (lane & 15), acc[i]);
-    }
-}
-
-struct FullK {
-    __device__ __forceinline__ void operator()(int, int, int&, int&) const {}
-};
 
 // ----------------------------------------------------------------- chunk addressing
 // A chunk is a run of at most kChunk tokens of one sequence.  Dense rows:
