@@ -65,6 +65,38 @@ def draw(seed: int, B: int, T: int, H: int, dk: int, dv: int, *, n_states: int |
     return out
 
 
+def draw_device(seed: int, B: int, T: int, H: int, dk: int, dv: int, device, dtype=torch.bfloat16, *,
+                n_states: int | None = None, h0_std: float | None = None, upstream: bool = False,
+                dhT: bool = False) -> dict:
+    """The draws of ``draw`` made on the device (a device ``torch.Generator``), for
+    rows too large to draw on the host: q_raw, k_raw, v (and do) come out in
+    ``dtype``, the rest in float32.  Same distributions as ``draw``; the values
+    differ from it (another generator)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    N = B if n_states is None else n_states
+
+    def normal(shape, std=1.0, out_dtype=torch.float32):
+        x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+        if std != 1.0:
+            x.mul_(std)
+        return x if out_dtype == torch.float32 else x.to(out_dtype)
+
+    out = {}
+    out["q_raw"] = normal((B, T, H, dk), out_dtype=dtype)
+    out["k_raw"] = normal((B, T, H, dk), out_dtype=dtype)
+    out["v"] = normal((B, T, H, dv), out_dtype=dtype)
+    out["f"] = normal((B, T, H, dk))
+    lo, hi = A_LOG_RANGE
+    out["A_log"] = torch.log(torch.rand(H, generator=gen, dtype=torch.float32, device=device) * (hi - lo) + lo)
+    out["dt_bias"] = normal((H, dk), 0.1)
+    out["b"] = normal((B, T, H))
+    out["h0"] = normal((N, H, dk, dv), h0_std) if h0_std is not None else None
+    out["do"] = normal((B, T, H, dv), out_dtype=dtype) if upstream else None
+    out["dhT"] = normal((N, H, dk, dv)) if (upstream and dhT) else None
+    return out
+
+
 def draw_decode(seed: int, steps: int, B: int, H: int, dk: int, dv: int, h_std: float = 0.1,
                 a_log_range=A_LOG_RANGE) -> dict:
     """Raw draws for ``steps`` consecutive one-token decode steps.
