@@ -29,6 +29,9 @@
  *     outputs untouched; kda_last_error() then describes it (thread-local).
  *   - Results are deterministic run to run (no floating-point atomics).
  *   - No output may alias an input, except the in-place state of kda_step.
+ *   - Empty inputs (T = 0, or rows = 0 for the gated norm) are valid: the
+ *     per-token (per-row) arrays may then be null; states pass through
+ *     (hT = h0, dh0 = dhT) and parameter gradients are written as zeros.
  */
 #ifndef KDA_H
 #define KDA_H

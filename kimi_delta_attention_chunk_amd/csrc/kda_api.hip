@@ -104,8 +104,9 @@ int ws_args(const kda_desc* d, kda::ChunkArgs& a) {
 int check_common_inputs(const kda_desc* d, const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* A_log, const float* dt_bias, const float* h0) {
     int rc;
-    if ((rc = check_ptr(q, "q", true)) || (rc = check_ptr(k, "k", true)) || (rc = check_ptr(v, "v", true)) ||
-        (rc = check_ptr(g, "g", true)) || (rc = check_ptr(beta, "beta", true)) || (rc = check_ptr(h0, "h0", false)))
+    const bool tok = d->T > 0;  // with no tokens the per-token arrays may be null
+    if ((rc = check_ptr(q, "q", tok)) || (rc = check_ptr(k, "k", tok)) || (rc = check_ptr(v, "v", tok)) ||
+        (rc = check_ptr(g, "g", tok)) || (rc = check_ptr(beta, "beta", tok)) || (rc = check_ptr(h0, "h0", false)))
         return rc;
     const bool gate = d->flags & KDA_F_GATE_IN_KERNEL;
     if ((rc = check_ptr(A_log, "A_log", gate)) || (rc = check_ptr(dt_bias, "dt_bias", gate))) return rc;
@@ -192,7 +193,7 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
     if (rc) return rc;
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
-    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(hT, "hT", false))) return rc;
+    if ((rc = check_ptr(o, "o", desc->T > 0)) || (rc = check_ptr(hT, "hT", false))) return rc;
     if (desc->flags & KDA_F_DH0_ONLY) return fail(KDA_ERR_INVALID, "KDA_F_DH0_ONLY is a backward flag");
     const size_t need = kda::ws_layout(a, (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED)) != 0).total;
     if (ws == nullptr || ws_bytes < need)
@@ -219,9 +220,10 @@ int kda_bwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     // with KDA_F_DH0_ONLY only dh0 is produced: the per-token gradients may be null
     const bool only = desc->flags & KDA_F_DH0_ONLY;
     const bool gate = (desc->flags & KDA_F_GATE_IN_KERNEL) && !only;
-    if ((rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dhT, "dhT", false)) ||
-        (rc = check_ptr(dq, "dq", !only)) || (rc = check_ptr(dk, "dk", !only)) || (rc = check_ptr(dv, "dv", !only)) ||
-        (rc = check_ptr(dg, "dg", !only)) || (rc = check_ptr(dbeta, "dbeta", !only)) ||
+    const bool tok = desc->T > 0, grads = tok && !only;  // with no tokens the per-token arrays may be null
+    if ((rc = check_ptr(d_o, "d_o", tok)) || (rc = check_ptr(dhT, "dhT", false)) ||
+        (rc = check_ptr(dq, "dq", grads)) || (rc = check_ptr(dk, "dk", grads)) || (rc = check_ptr(dv, "dv", grads)) ||
+        (rc = check_ptr(dg, "dg", grads)) || (rc = check_ptr(dbeta, "dbeta", grads)) ||
         (rc = check_ptr(dh0, "dh0", only)) || (rc = check_ptr(dA_log, "dA_log", gate)) ||
         (rc = check_ptr(ddt_bias, "ddt_bias", gate)))
         return rc;
@@ -338,8 +340,9 @@ int kda_conv_fwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kd
     g_err[0] = 0;
     int rc = conv_check(B, T, D, W, dtype, out_dtype, flags, cu_seqlens, N);
     if (rc) return rc;
-    if ((rc = check_ptr(x, "x", true)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
-        (rc = check_ptr(y, "y", true)))
+    const bool tok = T > 0;  // with no tokens x and y may be null
+    if ((rc = check_ptr(x, "x", tok)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
+        (rc = check_ptr(y, "y", tok)))
         return rc;
     kda::ConvArgs a = conv_args(B, T, D, W, dtype, out_dtype, flags, x, w, bias, cu_seqlens, N);
     a.y = y;
@@ -360,8 +363,9 @@ int kda_conv_bwd(int32_t B, int32_t T, int32_t D, int32_t W, kda_dtype dtype, kd
     g_err[0] = 0;
     int rc = conv_check(B, T, D, W, dtype, out_dtype, flags, cu_seqlens, N);
     if (rc) return rc;
-    if ((rc = check_ptr(x, "x", true)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
-        (rc = check_ptr(dy, "dy", true)) || (rc = check_ptr(dx, "dx", true)) || (rc = check_ptr(dw, "dw", true)) ||
+    const bool tok = T > 0;  // with no tokens x, dy and dx may be null
+    if ((rc = check_ptr(x, "x", tok)) || (rc = check_ptr(w, "w", true)) || (rc = check_ptr(bias, "bias", false)) ||
+        (rc = check_ptr(dy, "dy", tok)) || (rc = check_ptr(dx, "dx", tok)) || (rc = check_ptr(dw, "dw", true)) ||
         (rc = check_ptr(dbias, "dbias", false)) || (rc = check_ptr(ws, "ws", true)))
         return rc;
     const size_t need = kda_conv_bwd_workspace(B, T, D, W);
@@ -388,8 +392,9 @@ int kda_gnorm_fwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype
     g_err[0] = 0;
     int rc = gnorm_check(rows, dv, dtype, out_dtype, eps);
     if (rc) return rc;
-    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(gate, "gate", true)) ||
-        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(y, "y", true)))
+    const bool any = rows > 0;  // with no rows the row arrays may be null
+    if ((rc = check_ptr(o, "o", any)) || (rc = check_ptr(gate, "gate", any)) ||
+        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(y, "y", any)))
         return rc;
     kda::GnormArgs a;
     memset(&a, 0, sizeof a);
@@ -412,9 +417,10 @@ int kda_gnorm_bwd(int64_t rows, int32_t dv, kda_dtype dtype, kda_dtype out_dtype
     g_err[0] = 0;
     int rc = gnorm_check(rows, dv, dtype, out_dtype, eps);
     if (rc) return rc;
-    if ((rc = check_ptr(o, "o", true)) || (rc = check_ptr(gate, "gate", true)) ||
-        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(dy, "dy", true)) ||
-        (rc = check_ptr(d_o, "d_o", true)) || (rc = check_ptr(dgate, "dgate", true)) ||
+    const bool any = rows > 0;  // with no rows the row arrays may be null
+    if ((rc = check_ptr(o, "o", any)) || (rc = check_ptr(gate, "gate", any)) ||
+        (rc = check_ptr(weight, "weight", true)) || (rc = check_ptr(dy, "dy", any)) ||
+        (rc = check_ptr(d_o, "d_o", any)) || (rc = check_ptr(dgate, "dgate", any)) ||
         (rc = check_ptr(dweight, "dweight", true)) || (rc = check_ptr(ws, "ws", true)))
         return rc;
     const size_t need = kda_gnorm_bwd_workspace(rows, dv);

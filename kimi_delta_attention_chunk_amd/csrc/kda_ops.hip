@@ -295,7 +295,11 @@ template <int W, typename TIn, typename TOut, bool SILU>
 static hipError_t conv_launch(const ConvArgs& a, bool backward, hipStream_t s) {
     const int rpr = (a.T + kConvRun - 1) / kConvRun;
     const dim3 grid((a.D / 8 + kConvCG - 1) / kConvCG, (a.B * rpr + kConvRuns - 1) / kConvRuns);
-    if (grid.y == 0) return hipSuccess;
+    if (grid.y == 0) {  // no tokens: nothing to convolve; the weight gradients are zero
+        if (backward)
+            KDA_LAUNCH("conv_wsum", (conv_wsum_kernel<W>), dim3(a.D * (W + 1)), dim3(kOpsThreads), s, a, 0);
+        return hipSuccess;
+    }
     if (!backward) {
         KDA_LAUNCH("conv_fwd", (conv_fwd_kernel<W, TIn, TOut, SILU>), grid, dim3(kOpsThreads), s, a);
         return hipSuccess;
@@ -438,7 +442,10 @@ size_t gnorm_bwd_workspace(int64_t rows, int dv) { return (size_t)gnorm_blocks(r
 template <int DV, typename TIn, typename TOut>
 static hipError_t gnorm_launch(const GnormArgs& a, bool backward, hipStream_t s) {
     const int nblk = gnorm_blocks(a.rows, DV);
-    if (nblk == 0) return hipSuccess;
+    if (nblk == 0) {  // no rows: the weight gradient is zero
+        if (backward) KDA_LAUNCH("gnorm_wsum", gnorm_wsum_kernel, dim3(DV), dim3(kOpsThreads), s, a, 0);
+        return hipSuccess;
+    }
     if (!backward) {
         KDA_LAUNCH("gnorm_fwd", (gnorm_fwd_kernel<DV, TIn, TOut>), dim3(nblk), dim3(kOpsThreads), s, a);
         return hipSuccess;

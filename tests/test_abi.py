@@ -221,3 +221,25 @@ def test_state_pass_only_and_saved_forward_flags():
     rc = lib.kda_bwd(ctypes.byref(d), *head_g, fake, None, None, None, None, None, None, _fake(2), None, None, fake,
                      16, None)
     assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+
+
+def test_empty_inputs_need_no_token_pointers():
+    lib = kda.load_library()
+    fake = _fake(1)
+    d = _desc(T=0)
+    # no tokens: null q, k, v, g, beta and o pass the checks (the tiny workspace is what fails)
+    rc = lib.kda_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, None, None, fake,
+                     fake, 16, None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+    rc = lib.kda_bwd(ctypes.byref(d), *([None] * 11), None, None, None, None, None, None, None, _fake(2), None, None,
+                     fake, 16, None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+    # with tokens the same call is rejected for the missing q
+    d = _desc(T=64)
+    rc = lib.kda_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, None, None, fake,
+                     fake, 16, None)
+    assert rc == B.KDA_ERR_INVALID and b"q must not be null" in lib.kda_last_error()
+    # gated norm without rows: the row arrays may be null, the workspace is still checked
+    rc = lib.kda_gnorm_bwd(0, 64, B.KDA_BF16, B.KDA_BF16, 1e-6, None, None, _fake(3), None, None, None, _fake(4),
+                           _fake(5), 0, None)
+    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
