@@ -341,6 +341,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     __shared__ float X1[kChunk * LC];
     __shared__ float X2[kChunk * LC];
     __shared__ float X3[kChunk * LC];
+    __shared__ float STk[kChunk * LS];  // Kt of the off-diagonal row sums
     __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
     __shared__ float dbw_part[kChunk * NG];
     __shared__ float wpart[kGWaves * kChunk];   // per-wave row partials
@@ -514,8 +515,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     //   scaled by the other factor and gathered in LDS ([t][c]: ODk, ODq, ODc);
     //   diagonal blocks: the exact exp of each difference, partners by DPP row
     //   broadcast within the 16-lane row of the block.
-    float* const STa = dT;                 // Kt, then Kb      [64][LS] (dT is free after phase 4)
-    float* const STb = dT + kChunk * LS;   // Qb               [64][LS]
+    float* const STa = dT;                 // Kb  [64][LS] (dT is free after phase 4)
+    float* const STb = dT + kChunk * LS;   // Qb  [64][LS]
     float* const ODk = X1;                 // off-diagonal row sums with dA  [t][c]
     float* const ODq = X2;                 // off-diagonal row sums with dAq
     float* const ODc = X3;                 // off-diagonal column sums (dA and dAq)
@@ -545,62 +546,60 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
             load_g_block<DK, kGThreads>(p, cr, h, cb + kCB, gr);
         }
-        // -- off-diagonal row sums
+        // -- off-diagonal row and column sums: the scaled operands of both, then both products
 #pragma unroll
         for (int e_i = 0; e_i < kChunk * kCB / kGThreads; ++e_i) {
             const int e = threadIdx.x + e_i * kGThreads;
-            const int sr = e >> 5, cc = e & 31, r = (sr | 15);
-            const float x = KTb[cc * kLD + sr] * exp_hw(GTb[cc * kLD + r] - GTb[cc * kLD + sr]);
-            STa[sr * LS + cc] = sr < 48 ? x : 0.f;
-            ODc[sr * LS + cc] = 0.f;
+            const int sr = e >> 5, cc = e & 31, r = (sr | 15), r0 = sr & ~15;
+            const float gs = GTb[cc * kLD + sr], ks = KTb[cc * kLD + sr];
+            const float x = ks * exp_hw(GTb[cc * kLD + r] - gs);  // row sums: partner s = sr, r its block's last row
+            const float y = exp_hw(gs - GTb[cc * kLD + r0]);       // column sums: t = sr, r0 its block's first row
+            STk[sr * LS + cc] = sr < 48 ? x : 0.f;
+            STa[sr * LS + cc] = sr >= 16 ? bet[sr] * ks * y : 0.f;
+            STb[sr * LS + cc] = sr >= 16 ? QTb[cc * kLD + sr] * y : 0.f;
+            if (sr >= 48) ODc[sr * LS + cc] = 0.f;
             if (sr < 16) { ODk[sr * LS + cc] = 0.f; ODq[sr * LS + cc] = 0.f; }
         }
         __syncthreads();
-        if (wave < 6) {  // tile (I, tn), I = 1 .. 3
-            const int I = 1 + (wave >> 1), tn = wave & 1, c = 16 * tn + frag_col();
-            f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = rk;
-            for (int J = 0; J < I; ++J) {
-                f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
-                pk = mma16_f32(dA + 16 * I * kLD + 16 * J, kLD, 1, STa + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pk);
-                pq = mma16_f32(dAq + 16 * I * kLD + 16 * J, kLD, 1, STa + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pq);
-                const float gr = GTb[c * kLD + 16 * J + 15];
+        if (wave < 6) {
+            // row tile (I, tn), I = 1 .. 3, over J < I; column tile (J, tn), J = 0 .. 2, over I > J:
+            // I + (3 - J) = 4 block products per wave
+            const int tn = wave & 1, c = 16 * tn + frag_col();
+            {
+                const int I = 1 + (wave >> 1);
+                f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = rk;
+                for (int J = 0; J < I; ++J) {
+                    f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = pk;
+                    pk = mma16_f32(dA + 16 * I * kLD + 16 * J, kLD, 1, STk + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pk);
+                    pq = mma16_f32(dAq + 16 * I * kLD + 16 * J, kLD, 1, STk + 16 * J * LS + 16 * tn, LS, 1, 0, 16, pq);
+                    const float gr = GTb[c * kLD + 16 * J + 15];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = exp_hw(GTb[c * kLD + 16 * I + frag_row(i)] - gr);
+                        rk[i] = fmaf(e, pk[i], rk[i]);
+                        rq[i] = fmaf(e, pq[i], rq[i]);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = exp_hw(GTb[c * kLD + 16 * I + frag_row(i)] - gr);
-                    rk[i] = fmaf(e, pk[i], rk[i]);
-                    rq[i] = fmaf(e, pq[i], rq[i]);
+                    ODk[(16 * I + frag_row(i)) * LS + c] = rk[i];
+                    ODq[(16 * I + frag_row(i)) * LS + c] = rq[i];
                 }
             }
+            {
+                const int J = wave >> 1;
+                f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+                for (int I = J + 1; I < 4; ++I) {
+                    f32x4 pk = {0.f, 0.f, 0.f, 0.f};
+                    pk = mma16_f32(Y + 16 * J * kLD + 16 * I, kLD, 1, STa + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
+                    pk = mma16_f32(Tm + 16 * J * kLD + 16 * I, kLD, 1, STb + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
+                    const float gr = GTb[c * kLD + 16 * I];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ODk[(16 * I + frag_row(i)) * LS + c] = rk[i];
-                ODq[(16 * I + frag_row(i)) * LS + c] = rq[i];
+                    for (int i = 0; i < 4; ++i) cs[i] = fmaf(exp_hw(gr - GTb[c * kLD + 16 * J + frag_row(i)]), pk[i], cs[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ODc[(16 * J + frag_row(i)) * LS + c] = cs[i];
             }
-        }
-        __syncthreads();
-        // -- off-diagonal column sums
-#pragma unroll
-        for (int e_i = 0; e_i < kChunk * kCB / kGThreads; ++e_i) {
-            const int e = threadIdx.x + e_i * kGThreads;
-            const int tr = e >> 5, cc = e & 31, r = tr & ~15;
-            const float x = exp_hw(GTb[cc * kLD + tr] - GTb[cc * kLD + r]);
-            STa[tr * LS + cc] = tr >= 16 ? bet[tr] * KTb[cc * kLD + tr] * x : 0.f;
-            STb[tr * LS + cc] = tr >= 16 ? QTb[cc * kLD + tr] * x : 0.f;
-        }
-        __syncthreads();
-        if (wave < 6) {  // tile (J, tn), J = 0 .. 2
-            const int J = wave >> 1, tn = wave & 1, c = 16 * tn + frag_col();
-            f32x4 cs = {0.f, 0.f, 0.f, 0.f};
-            for (int I = J + 1; I < 4; ++I) {
-                f32x4 pk = {0.f, 0.f, 0.f, 0.f};
-                pk = mma16_f32(Y + 16 * J * kLD + 16 * I, kLD, 1, STa + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
-                pk = mma16_f32(Tm + 16 * J * kLD + 16 * I, kLD, 1, STb + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
-                const float gr = GTb[c * kLD + 16 * I];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cs[i] = fmaf(exp_hw(gr - GTb[c * kLD + 16 * J + frag_row(i)]), pk[i], cs[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ODc[(16 * J + frag_row(i)) * LS + c] = cs[i];
         }
         __syncthreads();
         // -- diagonal blocks and the per-token epilogue: lane = token t, CPW channels per wave.
