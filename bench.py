@@ -475,7 +475,7 @@ def main():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the operator shards by sequence and head with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
