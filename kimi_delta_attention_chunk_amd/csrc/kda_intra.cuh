@@ -31,15 +31,16 @@ namespace kda {
 constexpr int kCB32 = 32;        // channels per block
 constexpr int kLB = kCB32 + 4;   // row stride of [token][channel-block] tiles
 
-// The p-th pair (t, s), s <= t, of the four 16x16 diagonal blocks (136 each).
+// The p-th pair (t, s), s < t, of the four 16x16 diagonal blocks (120 each).
 __device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
-    const int I = p / 136, q = p - 136 * I;
-    int tl = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
-    if ((tl + 1) * (tl + 2) / 2 <= q) ++tl;
-    if (tl * (tl + 1) / 2 > q) --tl;
+    const int I = p / 120, q = p - 120 * I;
+    int tl = (int)((sqrtf(8.f * q + 1.f) + 1.f) * 0.5f);  // tl (tl - 1) / 2 <= q < tl (tl + 1) / 2
+    if (tl * (tl - 1) / 2 > q) --tl;
+    if ((tl + 1) * tl / 2 <= q) ++tl;
     t = 16 * I + tl;
-    s = 16 * I + q - tl * (tl + 1) / 2;
+    s = 16 * I + q - tl * (tl - 1) / 2;
 }
+constexpr int kDiagPairs = 4 * 120;
 
 // Gram tile list: pairs (I, J), J < I, of 16x16 blocks below the diagonal.
 __device__ __forceinline__ void gram_pair(int p, int& I, int& J) {
@@ -165,7 +166,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     float khs[8];  // this thread's Kh row values (dk = 32, pass 3)
 #pragma unroll
     for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dkk[3] = {0.f, 0.f, 0.f}, dqk[3] = {0.f, 0.f, 0.f};
+    float dkk[2] = {0.f, 0.f}, dqk[2] = {0.f, 0.f}, dqd = 0.f;
 
     char* qg = (char*)(p.qg + slot * kChunk * DK);    // [t][DK/32] k-blocks
     char* khT = (char*)(p.khT + slot * DK * kChunk);  // [c][2] k-blocks
@@ -258,12 +259,13 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             const T32 Aop = (kind == 0 ? Kr : Qr).sub((I - 1) * 16);
             gacc[i] = mma_tile(Aop, Kc.sub(kc_off(I) + 16 * J), 0, kCB32, gacc[i]);
         }
-        // diagonal blocks, exact pairwise decays: the 4 x 136 pairs s <= t of the
-        // 16x16 diagonal blocks, packed over the threads
+        // diagonal blocks, exact pairwise decays: the 4 x 120 pairs s < t of the 16x16
+        // diagonal blocks, two per thread (the last 32 threads have one); then the
+        // diagonal itself, Aqk[t][t] = q_t . k_t (no decay), four threads per token
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int pidx = threadIdx.x + kThreads * i;
-            if (pidx < 4 * 136) {
+            if (pidx < kDiagPairs) {
                 int t, s;
                 diag_pair(pidx, t, s);
                 f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aqv = {0.f, 0.f, 0.f, 0.f};
@@ -285,6 +287,15 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 dqk[i] += (aqv[0] + aqv[1]) + (aqv[2] + aqv[3]);
             }
         }
+        {
+            static_assert(kThreads == 4 * kChunk && kCB32 == 32, "four threads of 8 channels per token");
+            const int t = threadIdx.x >> 2, c8 = 8 * (threadIdx.x & 3);
+            const f32x4 q0 = *(const f32x4*)&Qb[t * kLB + c8], q1 = *(const f32x4*)&Qb[t * kLB + c8 + 4];
+            const f32x4 k0 = *(const f32x4*)&Kb[t * kLB + c8], k1 = *(const f32x4*)&Kb[t * kLB + c8 + 4];
+            const float a = ((q0[0] * k0[0] + q0[1] * k0[1]) + (q0[2] * k0[2] + q0[3] * k0[3])) +
+                            ((q1[0] * k1[0] + q1[1] * k1[1]) + (q1[2] * k1[2] + q1[3] * k1[3]));
+            dqd += sum4(a);
+        }
         __syncthreads();  // channel-block tiles are rewritten next
     }
 
@@ -293,15 +304,16 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     // Akk; the Aqk copy below writes zeros above the diagonal by index.
     float* AqL = KQG;  // [t][s], stride LA
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 2; ++i) {
         const int pidx = threadIdx.x + kThreads * i;
-        if (pidx < 4 * 136) {
+        if (pidx < kDiagPairs) {
             int t, s;
             diag_pair(pidx, t, s);
-            if (s < t) A[t * kLD + s] = bet[t] * dkk[i];
+            A[t * kLD + s] = bet[t] * dkk[i];
             AqL[t * LA + s] = dqk[i];
         }
     }
+    if ((threadIdx.x & 3) == 0) AqL[(threadIdx.x >> 2) * (LA + 1)] = dqd;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int tau = wave + 4 * i;
