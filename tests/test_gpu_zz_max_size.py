@@ -20,6 +20,9 @@ pytestmark = pytest.mark.gpu
 
 
 def test_packed_row_past_2e31_elements():
+    free, _ = torch.cuda.mem_get_info()
+    if free < (200 << 30):
+        pytest.skip("needs about 200 GB of free device memory (%.0f GB free)" % (free / 2 ** 30))
     H, dk, dv = 32, 32, 64
     lens = [4096] + [65536] * 33 + [57343, 4096, 37, 1]
     T = int(sum(lens))
