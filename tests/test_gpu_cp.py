@@ -118,3 +118,46 @@ def test_segment_map_of_one_document_is_its_state_map():
     pred = torch.matmul(M, d["h0"]) + c
     check_close("M h0 + c", pred, hT.double().cpu().numpy(), torch.float32)
     assert torch.equal(M[1], torch.eye(dk, device="cuda").expand(H, dk, dk))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_context_parallel_packed_row_of_two_documents(dtype):
+    """A packed row of two documents, each cut into segments (three, and two with a
+    one-token segment); the segments run as one packed row, each document's chain is
+    scanned on its own from its own h0 / dhT, and the result equals the oracle's pass
+    over the two-document row."""
+    T, H, dk, dv = 2200, 4, 32, 64
+    docs = [0, 1500, 2200]
+    seg = [0, 512, 1100, 1500, 1501, 2200]
+    chains = [(0, 3), (3, 5)]  # the segments of each document
+    inp, _ = prepared(14, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, n_states=2, upstream=True, dhT=True)
+    d = to_dev(inp, "cuda:0")
+    scale = dk ** -0.5
+    cuc = torch.tensor(seg, dtype=torch.int32, device="cuda")
+    plan = kda.plan_varlen(cuc, T)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    R = len(seg) - 1
+    ws = torch.empty(kda.workspace_bytes((1, T, H, dk), dv, R, True, dtype), dtype=torch.uint8, device="cuda")
+    pk = dict(cu_seqlens=cuc, plan=plan, workspace=ws)
+    _, c = kda.fwd(*args, scale, save_for_bwd=True, out_dtype=torch.float32, **pk)
+    M = kda.segment_maps(*args, fwd_saved=True, **pk)
+    h_in = torch.empty_like(c)
+    hT = torch.empty((2, H, dk, dv), dtype=torch.float32, device="cuda")
+    for n, (a, b) in enumerate(chains):
+        h_in[a:b], hT[n] = kda.state_scan(M[a:b], c[a:b], d["h0"][n])
+    o, _ = kda.fwd(*args, scale, h0=h_in, fwd_saved=True, save_for_bwd=True, out_dtype=torch.float32, **pk)
+    e = kda.bwd(*args, scale, d["do"], h0=h_in, fwd_saved=True, dh0_only=True, **pk)["dh0"]
+    D = torch.empty_like(e)
+    dh0 = torch.empty((2, H, dk, dv), dtype=torch.float32, device="cuda")
+    for n, (a, b) in enumerate(chains):
+        D[a:b], dh0[n] = kda.state_scan(M[a:b], e[a:b], d["dhT"][n], transpose=True)
+    gr = kda.bwd(*args, scale, d["do"], h0=h_in, dhT=D, fwd_saved=True, out_dtype=torch.float32, **pk)
+    torch.cuda.synchronize()
+    cu_docs = torch.tensor(docs, dtype=torch.int32)
+    oref, href = oracle_fwd(inp, scale, cu=cu_docs)
+    gref = oracle_bwd(inp, scale, cu=cu_docs)
+    check_close("o", o, oref, dtype)
+    check_close("hT", hT, href, dtype)
+    for nm in ("dq", "dk", "dv", "dg", "dbeta"):
+        check_close(nm, gr[nm], gref[nm], dtype)
+    check_close("dh0", dh0, gref["dh0"], dtype)
