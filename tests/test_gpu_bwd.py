@@ -35,6 +35,8 @@ CASES = [
     ("bf16_weak", 2, 300, 4, 32, 64, torch.bfloat16, dict(weak=True, h0_std=0.1, dhT=True)),
     ("bf16_default", 2, 256, 8, 32, 64, torch.bfloat16, {}),
     ("dk64_fp32", 1, 150, 2, 64, 64, torch.float32, dict(weak=True, h0_std=0.1, dhT=True)),
+    ("dk64_bf16_weak_h0", 2, 150, 2, 64, 64, torch.bfloat16, dict(weak=True, h0_std=0.1, dhT=True)),
+    ("dk64_bf16_default", 2, 256, 4, 64, 64, torch.bfloat16, {}),
     ("dk128_fp32", 1, 200, 2, 128, 128, torch.float32, dict(weak=True, h0_std=0.1, dhT=True)),
     ("dk128_bf16", 2, 190, 2, 128, 128, torch.bfloat16, dict(weak=True, dhT=True)),
 ]
@@ -49,6 +51,49 @@ def test_bwd_matches_oracle(case):
     got = run_bwd(d, scale)
     ref = oracle_bwd(inp, scale)
     compare(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("variant", ["g0", "beta1_unit"])
+def test_bwd_layer_shape_adversarial(variant, dtype):
+    """The layer shape (T=2048, H=8, dk=32, dv=64; B=2) with no decay or with beta = 1 on
+    unit keys, h0 ~ N(0, 0.1), upstream do and dhT ~ N(0, 1): with g = 0 every chunk's
+    state gradient reaches the first chunk."""
+    inp, _ = prepared(70 + len(variant), 2, 2048, 8, 32, 64, dtype, variant=variant, h0_std=0.1,
+                      upstream=True, dhT=True)
+    d = to_dev(inp)
+    got = run_bwd(d, 32 ** -0.5)
+    ref = oracle_bwd(inp, 32 ** -0.5)
+    compare(got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)], ids=["dk64", "dk128"])
+def test_bwd_packed_larger_heads(dims, dtype):
+    """Packed rows at dk = 64 and 128 with empty, one-token and partial-chunk documents,
+    per-document h0 and dhT, against the oracle; the 96 + 160 pair equals its separate
+    runs bit for bit."""
+    dk, dv = dims
+    lens = [1, 0, 64, 65, 1, 1, 130, 3, 0, 200]
+    inp = _packed(28, lens, H=2, dk=dk, dv=dv, dtype=dtype)
+    d = to_dev(inp)
+    got = run_bwd(d, dk ** -0.5)
+    ref = oracle_bwd(inp, dk ** -0.5, cu=inp["cu"])
+    compare(got, ref, dtype)
+    assert torch.equal(got["dh0"][1], d["dhT"][1]) and torch.equal(got["dh0"][8], d["dhT"][8])
+    inp = _packed(29, [96, 160], dk=dk, dv=dv, dtype=dtype)
+    d = to_dev(inp)
+    got = run_bwd(d, 0.2)
+    cu = [0, 96, 256]
+    for n in range(2):
+        sl = slice(cu[n], cu[n + 1])
+        part = {k: d[k][:, sl].contiguous() for k in ("q", "k", "v", "g", "beta", "do")}
+        part["h0"] = d["h0"][n:n + 1].contiguous()
+        part["dhT"] = d["dhT"][n:n + 1].contiguous()
+        gn = run_bwd(part, 0.2)
+        for nm in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(gn[nm], got[nm][:, sl]), (n, nm)
+        assert torch.equal(gn["dh0"][0], got["dh0"][n]), n
 
 
 def test_bwd_bf16_outputs_are_rounded_fp32_outputs():

@@ -27,6 +27,8 @@ CASES = [
     ("bf16_weak", 2, 300, 4, 32, 64, torch.bfloat16, dict(weak=True, h0_std=0.1)),
     ("bf16_default", 2, 256, 8, 32, 64, torch.bfloat16, {}),
     ("dk64_fp32", 1, 150, 2, 64, 64, torch.float32, dict(weak=True, h0_std=0.1)),
+    ("dk64_bf16_weak_h0", 2, 150, 2, 64, 64, torch.bfloat16, dict(weak=True, h0_std=0.1)),
+    ("dk64_bf16_default", 2, 256, 4, 64, 64, torch.bfloat16, {}),
     ("dk128_fp32", 1, 200, 2, 128, 128, torch.float32, dict(weak=True, h0_std=0.1)),
     ("dk128_bf16", 2, 190, 2, 128, 128, torch.bfloat16, dict(weak=True)),
 ]
@@ -40,6 +42,32 @@ def test_fwd_matches_oracle(case):
     scale = dk ** -0.5
     o, hT = run_fwd(d, scale)
     oref, href = oracle_fwd(inp, scale)
+    check_close("o", o, oref, dtype)
+    check_close("hT", hT, href, dtype)
+
+
+def test_fwd_config0_seed0():
+    """The small forward configuration exactly as specified: fp32, B=1, H=1, T=128, dk=32,
+    dv=64, scale = dk^-0.5, the default distributions, h0 = 0, drawn with seed 0."""
+    inp, _ = prepared(0, 1, 128, 1, 32, 64, torch.float32)
+    assert inp["h0"] is None
+    d = to_dev(inp)
+    o, hT = run_fwd(d, 32 ** -0.5)
+    oref, href = oracle_fwd(inp, 32 ** -0.5)
+    check_close("o", o, oref, torch.float32)
+    check_close("hT", hT, href, torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("variant", ["g0", "beta1_unit"])
+def test_fwd_layer_shape_adversarial(variant, dtype):
+    """The layer shape (T=2048, H=8, dk=32, dv=64; B=2) with no decay (g = 0: the pure
+    delta rule, the state carries across all 32 chunks) or with beta = 1 on unit keys
+    (every write replaces the key's old value), h0 ~ N(0, 0.1)."""
+    inp, _ = prepared(60 + len(variant), 2, 2048, 8, 32, 64, dtype, variant=variant, h0_std=0.1)
+    d = to_dev(inp)
+    o, hT = run_fwd(d, 32 ** -0.5)
+    oref, href = oracle_fwd(inp, 32 ** -0.5)
     check_close("o", o, oref, dtype)
     check_close("hT", hT, href, dtype)
 
@@ -140,3 +168,31 @@ def test_packed_config_row_forward():
     oref, href = oracle_fwd(inp, 32 ** -0.5, cu=cu)
     check_close("o", o, oref, torch.bfloat16)
     check_close("hT", hT, href, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128)], ids=["dk64", "dk128"])
+def test_packed_larger_heads_with_short_and_empty_documents(dims, dtype):
+    """Packed rows at dk = 64 and 128: empty, one-token and partial-chunk documents,
+    per-document h0, against the oracle; and the 96 + 160 pair equals its separate runs
+    bit for bit."""
+    dk, dv = dims
+    lens = [1, 0, 64, 65, 1, 1, 130, 3, 0, 200]
+    inp = _packed(18, lens, H=2, dk=dk, dv=dv, dtype=dtype)
+    d = to_dev(inp)
+    o, hT = run_fwd(d, dk ** -0.5, cu=d["cu"])
+    oref, href = oracle_fwd(inp, dk ** -0.5, cu=inp["cu"])
+    check_close("o", o, oref, dtype)
+    check_close("hT", hT, href, dtype)
+    assert torch.equal(hT[1], d["h0"][1]) and torch.equal(hT[8], d["h0"][8])
+    inp = _packed(19, [96, 160], dk=dk, dv=dv, dtype=dtype)
+    d = to_dev(inp)
+    o, hT = run_fwd(d, 0.2, cu=d["cu"])
+    cu = [0, 96, 256]
+    for n in range(2):
+        sl = slice(cu[n], cu[n + 1])
+        part = {k: d[k][:, sl].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        part["h0"] = d["h0"][n:n + 1].contiguous()
+        on, hn = run_fwd(part, 0.2)
+        assert torch.equal(on, o[:, sl]), n
+        assert torch.equal(hn[0], hT[n]), n

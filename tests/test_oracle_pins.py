@@ -292,6 +292,20 @@ def test_l2norm_unit_length_and_direction():
     assert np.all(np.linalg.norm(y2, axis=-1) < 1.0)
 
 
+def test_l2norm_epsilon_inside_the_root_closed_form():
+    """x = (3, 4): |x|^2 = 25, so x^ = x / sqrt(25 + eps) with eps inside the root.
+    An eps outside it, x / (|x| + eps) = x / 5.000001, differs by about 1.8e-7
+    relative (sqrt(25 + 1e-6) = 5.0000001), far above the rtol used here; so does a
+    missing eps (x / 5, 2e-8 relative)."""
+    x = np.array([[3.0, 4.0]])
+    for eps in (1e-6, 0.5):
+        y = oracle.l2norm(x, eps=eps)
+        np.testing.assert_allclose(y, x / math.sqrt(25.0 + eps), rtol=1e-15, atol=0)
+        assert abs(y[0, 0] - 3.0 / (5.0 + eps)) > 1e-9
+    # the default is eps = 1e-6 (reading 5 of the pages' silence)
+    np.testing.assert_allclose(oracle.l2norm(x), x / math.sqrt(25.0 + 1e-6), rtol=1e-15, atol=0)
+
+
 def test_prep_backward_finite_differences():
     rng = np.random.default_rng(5)
     T, H, dk = 4, 2, 3
