@@ -10,10 +10,13 @@ runs: gate preparation, intra-chunk, state passing, output, the mirrored
 backward and the preparation chain.  Inputs are synthetic (kda_inputs), drawn
 on the CPU and copied to HBM before the timed region.
 
-Prints one JSON line.  `roofline` reports the kernel that takes the most
+Prints one JSON line.  `value` and `ms_per_step` come from K steps timed with
+nothing else on the stream.  `roofline` reports the kernel that takes the most
 time, with its algorithmic work per launch (see kda_work below) divided by
-its average duration measured with HIP events on the launch stream.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+its average duration, measured with a HIP-event pair around every launch on
+the launch stream during a second pass of the same K steps.  `cpu_baseline`
+times the fp64 oracle on the same draw: forward, forward + backward, and a
+single-thread leg.
 """
 from __future__ import annotations
 
@@ -109,39 +112,70 @@ def copy_calibration(mb):
     print(json.dumps({"copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
-def cpu_baseline(B, T, H, dk, dv, seconds):
-    """The fp64 oracle (as it stands) on a bounded sample: whole sequences of the
-    same workload, all heads, repeated until about `seconds` of CPU work."""
+def cpu_threads():
+    """Host threads for the oracle: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when the environment sets it (the host's share per GPU)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return (min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n), n
+
+
+def cpu_baseline(raw, T, H, dk, dv, single_seqs=1):
+    """The fp64 oracle (as it stands, never tuned) on the same draw the GPU times:
+    forward (prep + recurrence) and forward + backward (prep, recurrence, its
+    backward, prep backward) over the whole batch on all host threads, and
+    forward + backward on `single_seqs` sequences on one thread; each leg one
+    warm-up and three timed repetitions, median wall clock."""
+    import statistics
+
     import numpy as np
 
-    import kda_inputs
     import oracle
 
     import torch
 
-    threads = oracle.num_threads()
-    nseq = max(1, min(B, threads // H))  # enough (sequence, head) pairs for every thread
-    raw = kda_inputs.draw(1, nseq, T, H, dk, dv, upstream=True)
-    as_bf16 = lambda x: raw[x].to(torch.bfloat16).double().numpy()  # same values the GPU receives
+    threads, affinity = cpu_threads()
+    as_bf16 = lambda x: raw[x].to(torch.bfloat16).double().numpy()  # the values the GPU receives
     q, k, v, do = (as_bf16(x) for x in ("q_raw", "k_raw", "v", "do"))
     f, b = (raw[x].double().numpy() for x in ("f", "b"))
     A_log = raw["A_log"].numpy().astype(np.float64)
     dtb = raw["dt_bias"].numpy().astype(np.float64)
     scale = dk ** -0.5
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        qh, kh, g, beta = oracle.prep_forward(q, k, f, A_log, dtb, b)
-        o, hT = oracle.forward(qh, kh, v, g, beta, scale)
-        gr = oracle.backward(qh, kh, v, g, beta, scale, do)
-        oracle.prep_backward(q, k, f, A_log, dtb, b, gr["dq"], gr["dk"], gr["dg"], gr["dbeta"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": nseq * T * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d x (%d sequences x %d tokens x %d heads), prep+fwd+bwd+prep-bwd in fp64, %.1f s"
-                      % (reps, nseq, T, H, el)}
+    B = q.shape[0]
+
+    def fwd(sl, nt):
+        qh, kh, g, beta = oracle.prep_forward(q[sl], k[sl], f[sl], A_log, dtb, b[sl])
+        oracle.forward(qh, kh, v[sl], g, beta, scale, nthreads=nt)
+
+    def fwd_bwd(sl, nt):
+        qh, kh, g, beta = oracle.prep_forward(q[sl], k[sl], f[sl], A_log, dtb, b[sl])
+        oracle.forward(qh, kh, v[sl], g, beta, scale, nthreads=nt)
+        gr = oracle.backward(qh, kh, v[sl], g, beta, scale, do[sl], nthreads=nt)
+        oracle.prep_backward(q[sl], k[sl], f[sl], A_log, dtb, b[sl], gr["dq"], gr["dk"], gr["dg"], gr["dbeta"])
+
+    def median_s(fn, *a):
+        fn(*a)
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn(*a)
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    everything = slice(0, B)
+    one = slice(0, min(single_seqs, B))
+    t_f = median_s(fwd, everything, threads)
+    t_fb = median_s(fwd_bwd, everything, threads)
+    t_1 = median_s(fwd_bwd, one, 1)
+    n1 = one.stop - one.start
+    return {"value": B * T / t_fb, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole timed batch (%d x %d tokens x %d heads, the GPU's own draw) on %d threads; "
+                      "the single-thread leg on %d sequence(s); fp64, 1 warm-up + 3 timed, median"
+                      % (B, T, H, threads, n1),
+            "fwd_tokens_per_s": B * T / t_f, "fwd_bwd_tokens_per_s": B * T / t_fb,
+            "fwd_s": t_f, "fwd_bwd_s": t_fb,
+            "single_thread_fwd_bwd_tokens_per_s": n1 * T / t_1, "single_thread_fwd_bwd_s": t_1,
+            "affinity_cpus": affinity}
 
 
 def flushed_median(step, dev, reps):
@@ -464,7 +498,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--seq", type=int, default=2048)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the cache-flushed median and the B=128 run (keeps profiler traces to the timed steps)")
@@ -522,8 +555,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; per-kernel HIP events on the launch stream
-    kda.timing_enable(True)
+    # timed region: K steps with nothing else on the stream
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -533,6 +565,16 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel durations: the same K steps again, each launch between a pair of HIP
+    # events on its own stream (the events are kept out of the headline loop above)
+    kda.timing_enable(True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_instrumented = ev0.elapsed_time(ev1) / args.steps
     per_kernel = kda.timing_collect()
     kda.timing_enable(False)
 
@@ -540,7 +582,7 @@ def main():
     value = tokens / (ms * 1e-3)
     work = kda_work(B, T, H, dk, dv)
     kernels = {name: {"launches_per_step": n / args.steps, "avg_us": 1e3 * tot / n,
-                      "share": tot / (ms * args.steps)} for name, (n, tot) in per_kernel.items()}
+                      "share": tot / (ms_instrumented * args.steps)} for name, (n, tot) in per_kernel.items()}
     dom = max(per_kernel, key=lambda nm: per_kernel[nm][1])
     n_dom, tot_dom = per_kernel[dom]
     avg_s = tot_dom / n_dom * 1e-3
@@ -583,6 +625,7 @@ def main():
                               "achieved_GBs": step_bytes / (ms * 1e-3) / 1e9,
                               "frac_of_8TBs": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "kernels": kernels,
+        "instrumented_ms_per_step": ms_instrumented,
     }
     if not args.no_extras:
         line["flushed"] = flushed_median(step, dev, reps=21)
@@ -590,7 +633,7 @@ def main():
         line["secondary_B128"] = secondary_run(q, k, v, f, b, do, scale, flags, B, T, H, dk, dv, dev)
         line["other_workloads"] = other_workloads(dev)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(B, T, H, dk, dv, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(raw, T, H, dk, dv)
     print(json.dumps(line), flush=True)
 
 

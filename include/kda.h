@@ -24,6 +24,8 @@
  *     *_workspace queries.  The library never allocates, frees or
  *     synchronizes, and never reads device memory on the host.
  *   - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream).
+ *   - Every call declared `int` returns a kda_status value (the enum below;
+ *     `int` keeps the ABI's return type fixed-width across compilers).
  *   - Arguments are checked from the descriptor and the pointer values only.
  *     On any error the call returns before launching anything and leaves all
  *     outputs untouched; kda_last_error() then describes it (thread-local).
@@ -119,7 +121,10 @@ typedef struct kda_desc {
 
 /* Host-only upper bound on the number of chunks that N documents totalling T
  * tokens can have: floor((T + N*(chunk-1)) / chunk).  Returns -1 on bad
- * arguments.  Size chunk_indices for kda_plan_varlen with it. */
+ * arguments.  Size chunk_indices for kda_plan_varlen with it.
+ * (torchtitan PR #4347, Performance: the per-batch offset tables are built
+ * without a device-to-host copy; this bound sizes them, and the grid of every
+ * packed call, from host integers alone -- surplus workgroups exit.) */
 int32_t kda_max_chunks(int32_t T, int32_t N, int32_t chunk);
 
 /* Per-document chunk metadata for a packed row (torchtitan PR #4347: the
@@ -140,15 +145,31 @@ int kda_plan_varlen(const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t chu
 
 /* Debug check of device cu_seqlens (cu[0] == 0, non-decreasing, cu[N] == T).
  * SYNCHRONISES the stream and copies N+1 ints to the host.  Returns KDA_OK or
- * KDA_ERR_INVALID. */
+ * KDA_ERR_INVALID (KDA_ERR_HIP if the copy fails).
+ * (torchtitan PR #4347, Performance and the Qwen3.5 paragraph: a device-to-host
+ * read of the offsets in every layer was the cost that PR removed, so the
+ * compute calls never read cu_seqlens on the host; their well-formedness is a
+ * documented precondition, and this separate call checks it in tests.) */
 int kda_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, kda_stream_t stream);
 
 /* Workspace bytes needed by kda_fwd / kda_bwd for this descriptor (0 if the
- * descriptor is invalid; kda_last_error says why). */
+ * descriptor is invalid; kda_last_error says why).  The caller allocates the
+ * workspace once and passes it to every call; the library allocates nothing.
+ * ("Pure KDA 300M on Primus" guide, Troubleshooting, "Out-of-memory at iter 1":
+ * a kernel that allocates its own copies of q/k/v doubles their activation
+ * memory; here every buffer, scratch included, is the caller's.)  For packed
+ * rows pass B = 1 and N = the number of documents: the size then covers
+ * kda_max_chunks(T, N, 64) chunks. */
 size_t kda_fwd_workspace(const kda_desc* desc);
 size_t kda_bwd_workspace(const kda_desc* desc);
 
-/* Forward.
+/* Forward: o and the final states hT of the recurrence at the top of this
+ * file, in chunked form (openkimi README, What is implemented: the chunk_kda
+ * row, with fused Q/K norm, decay gate and beta; torchtitan PR #4347,
+ * description: the recurrence takes cu_seqlens so that the state resets at
+ * every document start).  Errors: KDA_ERR_INVALID / _UNSUPPORTED /
+ * _WORKSPACE before any launch, outputs untouched; KDA_ERR_HIP if a launch
+ * fails.
  *   q, k        [B,T,H,dk] dtype  (raw if KDA_F_QK_L2NORM)
  *   v           [B,T,H,dv] dtype
  *   g           [B,T,H,dk] fp32 log-decay (f if KDA_F_GATE_IN_KERNEL)
@@ -166,7 +187,11 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
             const int32_t* chunk_offsets, void* o, float* hT, void* ws, size_t ws_bytes,
             kda_stream_t stream);
 
-/* Backward of kda_fwd with respect to every input it was given.
+/* Backward of kda_fwd with respect to every input it was given (openkimi
+ * README, What is implemented: the chunk_kda row is forward and backward, with
+ * the exact fp32-state recurrence as its reference; Profiling and H100
+ * acceptance: gradients are compared with that reference, and decay-gradient
+ * accuracy is the acceptance criterion).  Errors as kda_fwd.
  *   inputs as kda_fwd, plus
  *   d_o         [B,T,H,dv] dtype upstream gradient of o
  *   dhT         [N,H,dk,dv] fp32 upstream gradient of hT, nullable (= 0)
