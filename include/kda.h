@@ -187,6 +187,33 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
             const int32_t* chunk_offsets, void* o, float* hT, void* ws, size_t ws_bytes,
             kda_stream_t stream);
 
+/* Forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics and kernels as kda_fwd,
+ * minus ws / ws_bytes: the workspace is a fixed scratch array of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, allocated
+ * when the library's code is loaded on that GPU and held until the process
+ * ends.  The call allocates and frees nothing.
+ *   - kda_fwd_workspace(desc) must not exceed KDA_NOALLOC_SCRATCH_BYTES, else
+ *     KDA_ERR_UNSUPPORTED (before any launch).  At dk = 32, dv = 64 that is
+ *     about 1,200 chunk-heads, e.g. 8,192 tokens x 8 heads.
+ *   - KDA_F_SAVE_FOR_BWD, KDA_F_FWD_SAVED and KDA_F_DH0_ONLY are refused
+ *     (KDA_ERR_INVALID): the scratch does not outlive the call.
+ *   - The stream's device must be the current device.  The first call on a
+ *     device looks up that device's scratch address (hipGetSymbolAddress);
+ *     make one call outside any graph capture first.
+ *   - Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *     on one GPU (other streams, other threads) race and must be serialised
+ *     by the caller.  No part of the scratch needs to start at zero: each call
+ *     writes every scratch value before reading it.
+ *   - With kda_timing_enable(1) the timing hooks create events; leave timing
+ *     off where nothing may be allocated. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_fwd_noalloc(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+                    const int32_t* cu_seqlens, const int32_t* chunk_indices,
+                    const int32_t* chunk_offsets, void* o, float* hT, kda_stream_t stream);
+
 /* Backward of kda_fwd with respect to every input it was given (openkimi
  * README, What is implemented: the chunk_kda row is forward and backward, with
  * the exact fp32-state recurrence as its reference; Profiling and H100

@@ -26,7 +26,8 @@ EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd
            "kda_bwd_workspace", "kda_fwd", "kda_bwd", "kda_step", "kda_status_str",
            "kda_last_error", "kda_timing_enable", "kda_timing_collect", "kda_timing_count",
            "kda_timing_get", "kda_conv_fwd", "kda_conv_bwd_workspace", "kda_conv_bwd", "kda_gnorm_fwd",
-           "kda_gnorm_bwd_workspace", "kda_gnorm_bwd", "kda_segment_maps", "kda_state_scan"]
+           "kda_gnorm_bwd_workspace", "kda_gnorm_bwd", "kda_segment_maps", "kda_state_scan",
+           "kda_fwd_noalloc"]
 CONV_SILU = 1
 RMS_EPS = 1e-6
 
@@ -71,6 +72,8 @@ def load_library():
     lib.kda_bwd_workspace.restype = sz
     lib.kda_fwd.argtypes = [dp] + [vp] * 14 + [sz, vp]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [dp] + [vp] * 14
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [dp] + [vp] * 22 + [sz, vp]
     lib.kda_bwd.restype = ctypes.c_int
     lib.kda_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, f32, u32] + [vp] * 10
@@ -243,6 +246,29 @@ def fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=N
     _check(lib.kda_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                        _ptr(A_log), _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), _ptr(idx), _ptr(off),
                        _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(dev)))
+    return o, hT
+
+
+def fwd_noalloc(q, k, v, g, beta, scale, h0=None, cu_seqlens=None, plan=None, *, A_log=None,
+                dt_bias=None, l2norm_qk=False, gate_in_kernel=False, beta_logits=False, out_dtype=None,
+                o=None, hT=None):
+    """kda_fwd_noalloc: the forward on the library's own fixed scratch (no workspace).
+    Writes into `o` / `hT` when given (nothing is allocated then), else into new tensors.
+    Returns (o, hT)."""
+    lib = load_library()
+    B, T, H, dk, dv, N = _check_inputs(q, k, v, g, beta, h0, cu_seqlens, plan, A_log, dt_bias,
+                                       gate_in_kernel)
+    out_dtype = out_dtype or q.dtype
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    _req(o, "o", out_dtype, (B, T, H, dv), dev)
+    _req(hT, "hT", torch.float32, (N, H, dk, dv), dev, optional=True)
+    desc = _desc(q, v, N, scale, _flags(l2norm_qk, gate_in_kernel, beta_logits), out_dtype)
+    idx, off = plan if plan is not None else (None, None)
+    _check(lib.kda_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), _ptr(idx),
+                               _ptr(off), _ptr(o), _ptr(hT), _stream(dev)))
     return o, hT
 
 

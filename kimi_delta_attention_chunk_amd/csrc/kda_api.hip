@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
@@ -113,6 +115,44 @@ int check_common_inputs(const kda_desc* d, const void* q, const void* k, const v
     return KDA_OK;
 }
 
+// Scratch of kda_fwd_noalloc: a file-scope device array, one copy per GPU, held
+// until the process ends.  In host code its name is only a stand-in for the
+// device symbol, never a device address: the address of each GPU's copy is
+// looked up once per device (hipGetSymbolAddress, that device current) and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The scratch address on the device that `stream` runs on, which must be the
+// current device (so that the lookup resolves that device's copy).
+int scratch_on_stream_device(hipStream_t stream, void** out) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (stream != nullptr) {
+        hipDevice_t sd = -1;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sd != cur)
+            return fail(KDA_ERR_INVALID, "the stream belongs to device %d but device %d is current; make the "
+                                         "stream's device current", (int)sd, cur);
+    }
+    if (cur < 0 || cur >= kMaxDevices) return fail(KDA_ERR_UNSUPPORTED, "device index %d out of range", cur);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[cur] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", cur, hipGetErrorString(e));
+        g_scratch_ptr[cur] = p;
+    }
+    *out = g_scratch_ptr[cur];
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +241,34 @@ int kda_fwd(const kda_desc* desc, const void* q, const void* k, const void* v, c
     if (!aligned16(ws)) return fail(KDA_ERR_INVALID, "ws is not 16-byte aligned");
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0;
     a.o = o; a.hT = hT; a.ws = ws; a.ws_bytes = ws_bytes;
+    hipError_t e = kda::launch_fwd(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free forward
+int kda_fwd_noalloc(const kda_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                    const float* beta, const float* A_log, const float* dt_bias, const float* h0,
+                    const int32_t* cu_seqlens, const int32_t* chunk_indices, const int32_t* chunk_offsets,
+                    void* o, float* hT, kda_stream_t stream) {
+    g_err[0] = 0;
+    if (desc != nullptr && (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_FWD_SAVED | KDA_F_DH0_ONLY)))
+        return fail(KDA_ERR_INVALID, "kda_fwd_noalloc takes no save/saved/dh0 flag: its scratch does not "
+                                     "outlive the call");
+    kda::ChunkArgs a;
+    int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
+    if (rc) return rc;
+    if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, h0))) return rc;
+    if ((rc = check_ptr(o, "o", desc->T > 0)) || (rc = check_ptr(hT, "hT", false))) return rc;
+    const size_t need = kda::ws_layout(a, false).total;
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "kda_fwd_noalloc: this problem needs %zu bytes of scratch, more than its fixed %zu "
+                    "(use kda_fwd with a workspace)", need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((rc = scratch_on_stream_device((hipStream_t)stream, &ws))) return rc;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0;
+    a.o = o; a.hT = hT; a.ws = ws; a.ws_bytes = (size_t)KDA_NOALLOC_SCRATCH_BYTES;
     hipError_t e = kda::launch_fwd(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
     return KDA_OK;

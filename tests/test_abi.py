@@ -243,3 +243,24 @@ def test_empty_inputs_need_no_token_pointers():
     rc = lib.kda_gnorm_bwd(0, 64, B.KDA_BF16, B.KDA_BF16, 1e-6, None, None, _fake(3), None, None, None, _fake(4),
                            _fake(5), 0, None)
     assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+
+
+def test_noalloc_forward_validation():
+    """kda_fwd_noalloc refuses the save/saved/dh0 flags and problems whose workspace would
+    not fit its fixed scratch, before any device call."""
+    lib = kda.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 5 + [None, None, None, None, None, None, fake, None, None]
+    for fl in (B.F_SAVE_FOR_BWD, B.F_FWD_SAVED, B.F_DH0_ONLY):
+        d = _desc(flags=fl)
+        assert lib.kda_fwd_noalloc(ctypes.byref(d), *args) == B.KDA_ERR_INVALID
+        assert b"noalloc" in lib.kda_last_error()
+    big = _desc(B=16, T=2048, H=8, N=16)
+    assert _ws(big) > 64 << 20
+    assert lib.kda_fwd_noalloc(ctypes.byref(big), *args) == B.KDA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.kda_last_error()
+    fits = _desc(B=4, T=2048, H=8, N=4)
+    assert _ws(fits) <= 64 << 20
+    bad_null = list(args)
+    bad_null[0] = None
+    assert lib.kda_fwd_noalloc(ctypes.byref(fits), *bad_null) == B.KDA_ERR_INVALID
