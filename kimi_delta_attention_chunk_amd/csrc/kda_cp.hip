@@ -19,8 +19,9 @@
 // scheme as the state pass (P's rows as register fragments from the intra
 // kernel's k-block array, prefetched four chunks ahead; X^T in a
 // double-buffered LDS tile, one barrier per chunk).
-// state_scan_kernel: one workgroup per (head, 32 state columns); fp32 FMA over
-// the segments in order, M_r staged in LDS (transposed for the backward).
+// state_scan_kernel: one workgroup per (head, 32 state columns); fp32 MFMA over
+// the segments in order, M_r staged in LDS (transposed for the backward), the
+// next segments' operands in flight while the current one is applied.
 #include "../../include/kda.h"
 #include "kda_chunk.cuh"
 #include "kda_internal.h"
@@ -79,7 +80,12 @@ __global__ void __launch_bounds__(kPsThreads) seg_map_kernel(Prm p, float* __res
 }
 
 // X <- A_r X + c_r over the segments (A_r = M_r, or M_r^T in reverse order for
-// the backward); out[r] receives X before segment r's step.
+// the backward); out[r] receives X before segment r's step.  The chain is
+// latency-bound (R dependent steps of a small product): the 32 x 32 block of X
+// is four 16x16 tiles held as fp32 MFMA accumulators, one per wave, and each
+// step is eight v_mfma_f32_16x16x4_f32 on operands read from double-buffered
+// LDS tiles (one barrier per segment), while the next four segments' A and c
+// are in flight in registers.
 template <int DK>
 __global__ void __launch_bounds__(kThreads) state_scan_kernel(int R, int H, int DV, int transpose,
                                                               const float* __restrict__ M,
@@ -87,56 +93,75 @@ __global__ void __launch_bounds__(kThreads) state_scan_kernel(int R, int H, int 
                                                               const float* __restrict__ x0, float* __restrict__ out,
                                                               float* __restrict__ xfinal) {
     constexpr int BV = 32, LX = BV + 4, LM = DK + 1;
-    constexpr int RPT = DK * BV / 4 / kThreads;  // float4 of the state block per thread
-    static_assert(RPT >= 1, "state block");
-    __shared__ __attribute__((aligned(16))) float sX[DK * LX];
-    __shared__ float sA[DK * LM];
+    constexpr int MPT = DK * DK / kThreads;  // entries of A staged per thread
+    static_assert(DK == 32 && kThreads == 256 && DK * DK % kThreads == 0, "four 16x16 tiles, one per wave");
+    __shared__ __attribute__((aligned(16))) float sX[2][DK * LX];
+    __shared__ float sA[2][DK * LM];
     const int h = blockIdx.x, jb = blockIdx.y * BV;
-    const int tid = threadIdx.x;
-    // this thread's float4s of the state block: rows i, columns j4 .. j4 + 3
-    int ii[RPT], jj[RPT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int tm = wave >> 1, tn = wave & 1;  // this wave's tile: rows 16 tm .., columns 16 tn ..
+    const int lr = lane & 15, lg = lane >> 4;
+    const int col = jb + 16 * tn + lr;         // this lane's column of X (D fragment)
+    const int row0 = 16 * tm + 4 * lg;         // and its four rows row0 .. row0 + 3
+    f32x4 X;
 #pragma unroll
-    for (int q = 0; q < RPT; ++q) {
-        const int e = tid + kThreads * q;
-        ii[q] = e / (BV / 4);
-        jj[q] = 4 * (e % (BV / 4));
-    }
-    f32x4 X[RPT];
+    for (int i = 0; i < 4; ++i) X[i] = x0 ? x0[((size_t)h * DK + row0 + i) * DV + col] : 0.f;
+    // PD segments' A and c in flight (a register ring; slot = segment index mod PD)
+    constexpr int PD = 4;
+    float mreg[PD][MPT];
+    f32x4 creg[PD];
+    auto seg_of = [&](int s) { return (size_t)(transpose ? R - 1 - s : s) * H + h; };
+    auto fetch = [&](int s, int slot) {  // A and c of the s-th segment in scan order
+        const size_t seg = seg_of(s < R ? s : R - 1);
 #pragma unroll
-    for (int q = 0; q < RPT; ++q)
-        X[q] = x0 ? *(const f32x4*)(x0 + ((size_t)h * DK + ii[q]) * DV + jb + jj[q]) : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < R; ++s) {
-        const int r = transpose ? R - 1 - s : s;
-        const size_t seg = (size_t)r * H + h;
-        // stage A_r and X
-        for (int e = tid; e < DK * DK; e += kThreads) {
-            const int a = e / DK, b = e - a * DK;
-            const float m = M[seg * DK * DK + e];
-            if (transpose) sA[b * LM + a] = m;
-            else sA[a * LM + b] = m;
+        for (int i = 0; i < MPT; ++i) mreg[slot][i] = M[seg * DK * DK + tid + kThreads * i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) creg[slot][i] = c[(seg * DK + row0 + i) * DV + col];
+    };
+    auto step = [&](int s, int slot) {
+        const int b = s & 1;
+        const size_t seg = seg_of(s);
+#pragma unroll
+        for (int i = 0; i < MPT; ++i) {
+            const int e = tid + kThreads * i, a = e / DK, bb = e - a * DK;
+            if (transpose) sA[b][bb * LM + a] = mreg[slot][i];
+            else sA[b][a * LM + bb] = mreg[slot][i];
         }
 #pragma unroll
-        for (int q = 0; q < RPT; ++q) {
-            *(f32x4*)&sX[ii[q] * LX + jj[q]] = X[q];
-            *(f32x4*)(out + (seg * DK + ii[q]) * DV + jb + jj[q]) = X[q];
+        for (int i = 0; i < 4; ++i) {
+            sX[b][(row0 + i) * LX + 16 * tn + lr] = X[i];
+            out[(seg * DK + row0 + i) * DV + col] = X[i];
         }
+        // One barrier per segment: buffer b was last read in step s - 2, and every
+        // thread passed step s - 1's barrier after finishing that step.
         __syncthreads();
+        f32x4 acc = creg[slot];
 #pragma unroll
-        for (int q = 0; q < RPT; ++q) {
-            f32x4 acc = *(const f32x4*)(c + (seg * DK + ii[q]) * DV + jb + jj[q]);
-            for (int k = 0; k < DK; ++k) {
-                const float a = sA[ii[q] * LM + k];
-                const f32x4 x = *(const f32x4*)&sX[k * LX + jj[q]];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = fmaf(a, x[m], acc[m]);
-            }
-            X[q] = acc;
+        for (int k = 0; k < DK; k += 4) {
+            const float a = sA[b][(16 * tm + lr) * LM + k + lg];   // A(row 16 tm + lr, k + lg)
+            const float x = sX[b][(k + lg) * LX + 16 * tn + lr];   // X(k + lg, column 16 tn + lr)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x, acc, 0, 0, 0);
         }
-        __syncthreads();  // sA, sX are restaged next
+        X = acc;
+    };
+#pragma unroll
+    for (int i = 0; i < PD; ++i) fetch(i, i);
+    // The loop body issues the same loads on every path (past the end it reloads
+    // the last segment), so each wait on the memory counter covers one batch.
+    int s = 0;
+    for (; s + PD <= R; s += PD) {
+#pragma unroll
+        for (int i = 0; i < PD; ++i) {
+            step(s + i, i);
+            fetch(s + i + PD, i);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < PD - 1; ++i)
+        if (s + i < R) step(s + i, i);
     if (xfinal) {
 #pragma unroll
-        for (int q = 0; q < RPT; ++q) *(f32x4*)(xfinal + ((size_t)h * DK + ii[q]) * DV + jb + jj[q]) = X[q];
+        for (int i = 0; i < 4; ++i) xfinal[((size_t)h * DK + row0 + i) * DV + col] = X[i];
     }
 }
 
