@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         for (int i = 0; i < 4; ++i) { sk += kx[i] * kx[i]; sq += qx[i] * qx[i]; }
         sk = sum8(sk);
         sq = sum8(sq);
-        const float rk = 1.0f / sqrtf(sk + kL2Eps), rq = 1.0f / sqrtf(sq + kL2Eps);
+        const float rk = rsqrt_hw(sk + kL2Eps), rq = rsqrt_hw(sq + kL2Eps);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { kx[i] *= rk; qx[i] *= rq; }
         if (part == 0) { rnk[tr] = rk; rnq[tr] = rq; }
@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         const int cc = 4 * part + i;
         Ks[tr * LR + cc] = kx[i];
         Qs[tr * LR + cc] = qx[i];
-        Gs[tr * LR + cc] = graw[i];
+        Gs[tr * LR + cc] = graw[i] * kLog2e;  // base-2 log-decay (cumulated in place below)
     }
     // dGamma_L = rowsum(h . D): 16 consecutive lanes share one row c per float4 slot
 #pragma unroll
@@ -217,8 +217,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float gL = Gs[last * LR + 4 * part + i];  // in-chunk decay at the last token
-                xg[i] = b * __expf(G[i]) * kx[i];
-                xh[i] = kx[i] * __expf(gL - G[i]);
+                xg[i] = b * exp2_hw(G[i]) * kx[i];
+                xh[i] = kx[i] * exp2_hw(gL - G[i]);
             }
             BKG.put4(tr, 4 * part, xg);
             KHt.put4(tr, 4 * part, xh);
@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * am + frag_row(r);
-                const float gam = __expf(gt[r]), eL = __expf(glc - gt[r]);
+                const float gam = exp2_hw(gt[r]), eL = exp2_hw(glc - gt[r]);
                 const float dqg = scale * aQ[r], dkh = aKh[r];
                 const float kh = kt[r] * eL;
                 DQ[t * LR + cc] = gam * dqg;
@@ -472,7 +472,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             const float b = bet[tr];
             f32x4 v0;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) v0[m] = b * __expf(G[m]) * kx[m];
+            for (int m = 0; m < 4; ++m) v0[m] = b * exp2_hw(G[m]) * kx[m];
             bKg.put4(tr, 4 * part, v0);
         }
         {
@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * am + frag_row(r);
-                const float gam = __expf(gt[r]);
+                const float gam = exp2_hw(gt[r]);
                 const float kg = gam * kt[r], dkg = bt[r] * acc[r];
                 DKa[t * LR + cc] = dk0[r] + gam * dkg;
                 DG[t * LR + cc] = dg0[r] + kt[r] * gam * dkg;
@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         for (int I = 1; I <= 3; ++I) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e = __expf(gref[I - 1][i] - G[i]);
+                const float e = exp2_hw(gref[I - 1][i] - G[i]);
                 KcT(I - 1).put(4 * part + i, tr, tr < 16 * I ? kx[i] * e : 0.f);
             }
         }
@@ -670,7 +670,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * I + frag_row(r);
-                const float e = __expf(gt[r] - gr);
+                const float e = exp2_hw(gt[r] - gr);
                 const float rkv = e * ak[r], rqv = e * aq[r];
                 DKa[t * LR + cc] = dk0[r] + bt[r] * rkv;
                 DQ[t * LR + cc] = dq0[r] + rqv;
@@ -708,7 +708,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             for (int i = 0; i < 4; ++i) {
                 const int cc = 4 * part + i;
                 const bool after = tr > 16 * J + 15;
-                const float e = after ? __expf(G[i] - gref[J][i]) : 0.f;
+                const float e = after ? exp2_hw(G[i] - gref[J][i]) : 0.f;
                 KxT(J).put(cc, tr, kx[i] * e);
                 QxT(J).put(cc, tr, qx[i] * e);
             }
@@ -735,7 +735,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = 16 * J + frag_row(r);
-                const float e = __expf(gr - gs[r]);
+                const float e = exp2_hw(gr - gs[r]);
                 const float cs = e * (ak[r] + aq[r]);
                 DKa[s * LR + cc] = dk0[r] + cs;
                 DG[s * LR + cc] = dg0[r] - ks[r] * cs;
@@ -776,7 +776,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 // stored diagonal blocks are zero outside their triangles (dA strictly lower,
                 // dAq lower), so each product below only counts on its own side.
                 const float x = gtv[jc] - gs;
-                const float e = exp_hw(lower ? x : -x);
+                const float e = exp2_hw(lower ? x : -x);
                 const float ek = e * ks;
                 rkv[jc] = fmaf(ad_ts, ek, rkv[jc]);
                 rqv[jc] = fmaf(aq_ts, ek, rqv[jc]);
@@ -804,7 +804,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     {
         const int cs = tid & 31, sg = tid >> 5;
         const float extra = ((colp[cs] + colp[DK + cs]) + (colp[2 * DK + cs] + colp[3 * DK + cs])) +
-                            __expf(GL[cs]) * dgl[cs];
+                            exp2_hw(GL[cs]) * dgl[cs];
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -122,14 +122,22 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]
 // instead of the library's range-reduced versions: the preparation runs
 // them per element in every chunk kernel.
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// The chunk kernels keep the in-chunk cumulative log-decay in base 2 (G log2 e),
+// so each decay factor exp(G_t - G_s) is one v_exp_f32 of a difference.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 // log(1 + y) for y >= 0 to full relative precision: log(z) * y / (z - 1) with
 // z = 1 + y rounded, which cancels the rounding of z (y when z rounds to 1).
+// The correction factor y / (z - 1) is within an ulp or two of 1, so the
+// hardware reciprocal (about 1 ulp) is as good as a division here.
 __device__ __forceinline__ float log1p_hw(float y) {
     const float z = 1.f + y;
     const float l = __builtin_amdgcn_logf(z) * 0.6931471805599453f;
-    return z == 1.f ? y : l * (y / (z - 1.f));
+    return z == 1.f ? y : l * (y * __builtin_amdgcn_rcpf(z - 1.f));
 }
+// (x)^-1/2 by the hardware reciprocal square root (about 1 ulp), for the L2 norms.
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
 // softplus with the usual threshold: x for x > 20; else max(x, 0) + log1p(e^-|x|).
 __device__ __forceinline__ float softplus_f(float x) {
     return x > 20.f ? x : fmaxf(x, 0.f) + log1p_hw(exp_hw(-fabsf(x)));

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             for (int i = 0; i < 8; ++i) { sk += kx[b][i] * kx[b][i]; sq += qx[b][i] * qx[b][i]; }
         sk += __shfl_xor(sk, 1, 64); sk += __shfl_xor(sk, 2, 64);
         sq += __shfl_xor(sq, 1, 64); sq += __shfl_xor(sq, 2, 64);
-        const float rk = 1.0f / sqrtf(sk + kL2Eps), rq = 1.0f / sqrtf(sq + kL2Eps);
+        const float rk = rsqrt_hw(sk + kL2Eps), rq = rsqrt_hw(sq + kL2Eps);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         for (int i = 0; i < 8; ++i) {
             Kb[tr * kLB + 8 * part + i] = kx[b][i];
             Qb[tr * kLB + 8 * part + i] = qx[b][i];
-            Gb[tr * kLB + 8 * part + i] = G[b][i];  // per-token log-decay; scanned in place below
+            Gb[tr * kLB + 8 * part + i] = G[b][i] * kLog2e;  // base-2 log-decay; scanned in place below
         }
         __syncthreads();
         {
@@ -200,17 +200,17 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             for (int i = 0; i < 8; ++i) {
                 const int cc = 8 * part + i;
                 const float gt = G[b][i];
-                qgv[i] = __expf(gt) * qx[b][i];
-                khv[i] = kx[b][i] * __expf(Gb[last * kLB + cc] - gt);
+                qgv[i] = exp2_hw(gt) * qx[b][i];
+                khv[i] = kx[b][i] * exp2_hw(Gb[last * kLB + cc] - gt);
                 if constexpr (DK != 32) {
                     KhS[cc * kLD + tr] = khv[i];
                     if (rev_ops) QgS[cc * kLD + tr] = qgv[i];
                 }
-                const float e = __expf(gt - Gb[16 * (I >= 1 ? I : 1) * kLB + cc]);
+                const float e = exp2_hw(gt - Gb[16 * (I >= 1 ? I : 1) * kLB + cc]);
                 kr[i] = kx[b][i] * e;
                 qr[i] = qx[b][i] * e;
 #pragma unroll
-                for (int J = 1; J <= 3; ++J) kc[J - 1][i] = kx[b][i] * __expf(Gb[16 * J * kLB + cc] - gt);
+                for (int J = 1; J <= 3; ++J) kc[J - 1][i] = kx[b][i] * exp2_hw(Gb[16 * J * kLB + cc] - gt);
             }
             if (I >= 1) {
                 Kr.put8(tr - 16, 8 * part, kr);
@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         }
         if (DK != 32 && tr == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = __expf(Gb[last * kLB + 8 * part + i]);
+            for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = exp2_hw(Gb[last * kLB + 8 * part + i]);
         }
         __syncthreads();
         if constexpr (DK != 32) {
@@ -278,7 +278,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                     const f32x4 qt = *(const f32x4*)&Qb[t * kLB + c4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const float e = ks[m] * __expf(gt[m] - gs[m]);
+                        const float e = ks[m] * exp2_hw(gt[m] - gs[m]);
                         ak[m] += kt[m] * e;
                         aqv[m] += qt[m] * e;
                     }
@@ -409,7 +409,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 const T64 BTg(KQG + g * kCB32 * LA, kCB32);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    BTg.put(8 * part + i, tr, b < NB ? bt * __expf(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
+                    BTg.put(8 * part + i, tr, b < NB ? bt * exp2_hw(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
                                                      : bt * vx[b < NB ? 0 : b - NB][i]);
             }
         }
@@ -497,12 +497,12 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         {
             float qv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qv[i] = __expf(G[0][i]) * qx[0][i];
+            for (int i = 0; i < 8; ++i) qv[i] = exp2_hw(G[0][i]) * qx[0][i];
             *(f32x4*)&Qgs[tr * kLB + 8 * part] = f32x4{qv[0], qv[1], qv[2], qv[3]};
             *(f32x4*)&Qgs[tr * kLB + 8 * part + 4] = f32x4{qv[4], qv[5], qv[6], qv[7]};
             if (tr == last) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) glS[8 * part + i] = __expf(G[0][i]);
+                for (int i = 0; i < 8; ++i) glS[8 * part + i] = exp2_hw(G[0][i]);
             }
         }
         const int lr = threadIdx.x & 15, lg = (threadIdx.x & 63) >> 4;
