@@ -14,11 +14,11 @@
 //   P3  dA = -T^T dT T^T, strictly lower (T = (I + A)^{-1})
 //   P4  the decayed pair sums of Akk = beta_t sum k_t k_s e^{G_t-G_s} and
 //       Aqk = sum q_t k_s e^{G_t-G_s}: for rows t (partner s <= t) and columns s
-//       (partner t >= s).  Off-diagonal 16x16 blocks are MFMA products with
-//       the decay factored through a reference row r between the pair
-//       (exp(G_t - G_r) exp(G_r - G_s), both at most 1): r = the first row of
-//       the row block for the row sums, the last row of the column block for
-//       the column sums.  Diagonal blocks use the exact exp of each difference.
+//       (partner t >= s).  Off-diagonal 16x16 blocks (t in block I, s in J < I)
+//       are MFMA products with the decay split at the first row of I and the
+//       last row of J (three factors, each at most 1): the outer two scale the
+//       operands, one staged copy each, the middle one each block pair's
+//       product.  Diagonal blocks use the exact exp of each difference.
 //   P5  the explicit factors (Qg, Kg, Kh, exp(G_L)) are folded in as they are
 //       produced; dg is the reverse in-chunk cumulative sum of dG; then the
 //       gate, sigmoid and L2-norm chains.
@@ -165,15 +165,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         Qs[tr * LR + cc] = qx[i];
         Gs[tr * LR + cc] = graw[i] * kLog2e;  // base-2 log-decay (cumulated in place below)
     }
-    // dGamma_L = rowsum(h . D): 16 consecutive lanes share one row c per float4 slot
-#pragma unroll
-    for (int i = 0; i < NH4; ++i) {
-        const int e4 = 4 * (tid + NTH * i);
-        const int cc = e4 / DV;
-        const float s = sum16(Hr[i][0] * Dr[i][0] + Hr[i][1] * Dr[i][1] + Hr[i][2] * Dr[i][2] + Hr[i][3] * Dr[i][3]);
-        static_assert(DV == 64, "one row of h per 16 lanes");
-        if ((lane & 15) == 0) dgl[cc] = s;
-    }
     __syncthreads();
     {
         // in-chunk cumulative log-decay G, in place in Gs
@@ -188,6 +179,32 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     if (tr == last) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) GL[4 * part + i] = G[i];
+    }
+    // (h and D', loaded last, are first needed here: the barrier above and the
+    // scan did not wait for them)
+    // dGamma_L (read in P5) = rowsum(h . D): 16 consecutive lanes share one row c per float4 slot
+#pragma unroll
+    for (int i = 0; i < NH4; ++i) {
+        const int e4 = 4 * (tid + NTH * i);
+        const int cc = e4 / DV;
+        const float s = sum16(Hr[i][0] * Dr[i][0] + Hr[i][1] * Dr[i][1] + Hr[i][2] * Dr[i][2] + Hr[i][3] * Dr[i][3]);
+        static_assert(DV == 64, "one row of h per 16 lanes");
+        if ((lane & 15) == 0) dgl[cc] = s;
+    }
+    // h and D' again, rows 16 (w & 1) + (lane & 15), as the register fragments of P1's
+    // products: issued now, so that they arrive during P0
+    f32x4 hraw[2][2], draw[2][2];  // this lane's 8 values of h / D' rows 16 an + (lane & 15), per k-block
+    {
+        const int row = 16 * (wave & 1) + (lane & 15), c8 = 8 * (lane >> 4);
+        const float* hs = p.hs + slot * DK * DV + (size_t)row * DV + c8;
+        const float* ds = p.dhs + slot * DK * DV + (size_t)row * DV + c8;
+#pragma unroll
+        for (int kb = 0; kb < NVB; ++kb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                hraw[kb][q] = *(const f32x4*)(hs + 32 * kb + 4 * q);
+                draw[kb][q] = *(const f32x4*)(ds + 32 * kb + 4 * q);
+            }
     }
 
     // ------------------------------------------------ P0: v_new and dv_new of the chunk
@@ -329,19 +346,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         const T64 vnb(ph + 4608, kChunk), dvnb(ph + 9216, kChunk), dvnT(ph + 13824, DV), dOb(ph + 18432, kChunk);
         const T64 Vh(ACC, kChunk);
         static_assert(18432 + kChunk * (DV + 8) <= PH && kChunk * (DV + 8) <= 3 * kChunk * LR, "P1 staging must fit");
-        f32x4 hraw[2][2], draw[2][2];  // this lane's 8 values of h / D' rows 16 an + (lane & 15), per k-block
-        {
-            const int row = 16 * an + (lane & 15), c8 = 8 * (lane >> 4);
-            const float* hs = p.hs + slot * DK * DV + (size_t)row * DV + c8;
-            const float* ds = p.dhs + slot * DK * DV + (size_t)row * DV + c8;
-#pragma unroll
-            for (int kb = 0; kb < NVB; ++kb)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    hraw[kb][q] = *(const f32x4*)(hs + 32 * kb + 4 * q);
-                    draw[kb][q] = *(const f32x4*)(ds + 32 * kb + 4 * q);
-                }
-        }
         __syncthreads();  // P0's readers of ph and ACC are done
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
@@ -604,15 +608,20 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     }
 
     // ------------------------------------------------ P4: decayed pair sums
+    // Off-diagonal 16x16 blocks (t in block I, s in block J < I) split the decay
+    // at the first row a_I = 16 I of I and the last row b_J = 16 J + 15 of J:
+    //   exp(G_t - G_s) = exp(G_t - G_{a_I}) exp(G_{a_I} - G_{b_J}) exp(G_{b_J} - G_s),
+    // each factor at most 1 (s <= b_J < a_I <= t).  The outer factors scale one
+    // staged copy of each operand (every token by its own block's reference);
+    // the middle factor, one number per channel and block pair, scales that
+    // pair's 16-deep product.
     {
         // row sums: R'k[t] = sum_{s<t} dA[t][s] k_s e^{G_t-G_s},  Rq[t] = sum_{s<=t} dAq[t][s] k_s e^{..}
         const T64 dAt(ph, kChunk), dAqt(ph + 4608, kChunk);
-        auto KcT = [&](int i) { return T64(ph + 9216 + 2304 * i, DK); };
-        float gref[3][4];
+        const T64 KcT(ph + 9216, DK);  // [c][s] = k_s e^{G_{b(s)} - G_s}, b(s) the last row of s's block
+        float gend[4];
 #pragma unroll
-        for (int I = 1; I <= 3; ++I)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gref[I - 1][i] = Gs[(16 * I) * LR + 4 * part + i];
+        for (int i = 0; i < 4; ++i) gend[i] = Gs[(16 * (tr >> 4) + 15) * LR + 4 * part + i];
         __syncthreads();  // P3 tiles consumed
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -628,33 +637,28 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 }
             }
         }
-        // KcT_I[c][s] = k_s e^{G_{16 I} - G_s} for s < 16 I, else 0
 #pragma unroll
-        for (int I = 1; I <= 3; ++I) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = exp2_hw(gref[I - 1][i] - G[i]);
-                KcT(I - 1).put(4 * part + i, tr, tr < 16 * I ? kx[i] * e : 0.f);
-            }
-        }
+        for (int i = 0; i < 4; ++i) KcT.put(4 * part + i, tr, kx[i] * exp2_hw(gend[i] - G[i]));
         __syncthreads();
         // 6 tasks: (I, column tile of c), on waves 0..5
         if (wave < 6) {
             const int I = 1 + (wave >> 1), tn = wave & 1;
-            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            const T64 kc = KcT(I - 1);  // zero from index 16 I on: k-blocks 0 .. (16 I - 1) / 32
-            AFrag<P> fk, fa;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                if (32 * kb < 16 * I) {
-                    load_frag(fk, kc.sub(16 * tn), 32 * kb);
-                    load_frag(fa, dAt.sub(16 * I), 32 * kb);
-                    ak = mma_ff(fa, fk, ak);
-                    load_frag(fa, dAqt.sub(16 * I), 32 * kb);
-                    aq = mma_ff(fa, fk, aq);
-                }
             const int cc = 16 * tn + frag_col();
-            const float gr = Gs[(16 * I) * LR + cc];
+            const float gr = Gs[(16 * I) * LR + cc];  // G at a_I
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int J = 0; J < 3; ++J)
+                if (J < I) {
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 pk = mma_tile_k16(dAt.sub(16 * I), KcT.sub(16 * tn), 16 * J, zero);
+                    const f32x4 pq = mma_tile_k16(dAqt.sub(16 * I), KcT.sub(16 * tn), 16 * J, zero);
+                    const float m = exp2_hw(gr - Gs[(16 * J + 15) * LR + cc]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ak[r] = fmaf(m, pk[r], ak[r]);
+                        aq[r] = fmaf(m, pq[r], aq[r]);
+                    }
+                }
             float gt[4], kt[4], qt[4], bt[4], dk0[4], dq0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -683,13 +687,11 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     {
         // column sums: Ck[s] = sum_{t>s} beta_t dA[t][s] k_t e^{G_t-G_s}, Cq[s] = sum_{t>=s} dAq[t][s] q_t e^{..}
         const T64 bdAT(ph, kChunk), dAqT(ph + 4608, kChunk);
-        auto KxT = [&](int j) { return T64(ph + 9216 + 2304 * j, DK); };
-        auto QxT = [&](int j) { return T64(ph + 16128 + 2304 * j, DK); };
-        float gref[3][4];
+        // [c][t] = k_t e^{G_t - G_{a(t)}} and q_t e^{..}, a(t) the first row of t's block
+        const T64 KxT(ph + 9216, DK), QxT(ph + 9216 + 2304, DK);
+        float gst[4];
 #pragma unroll
-        for (int J = 0; J < 3; ++J)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gref[J][i] = Gs[(16 * J + 15) * LR + 4 * part + i];
+        for (int i = 0; i < 4; ++i) gst[i] = Gs[(16 * (tr >> 4)) * LR + 4 * part + i];
         __syncthreads();  // row-sum tiles consumed
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -701,28 +703,32 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             bdAT.put4(s, 16 * tm + frag_row(0), bd);
             dAqT.put4(s, 16 * tm + frag_row(0), aAq[i]);
         }
-        // KxT_J[c][t] = k_t e^{G_t - G_{16 J + 15}} for t > 16 J + 15, else 0 (QxT_J likewise)
 #pragma unroll
-        for (int J = 0; J < 3; ++J) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int cc = 4 * part + i;
-                const bool after = tr > 16 * J + 15;
-                const float e = after ? exp2_hw(G[i] - gref[J][i]) : 0.f;
-                KxT(J).put(cc, tr, kx[i] * e);
-                QxT(J).put(cc, tr, qx[i] * e);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 4 * part + i;
+            const float e = exp2_hw(G[i] - gst[i]);
+            KxT.put(cc, tr, kx[i] * e);
+            QxT.put(cc, tr, qx[i] * e);
         }
         __syncthreads();
         if (wave < 6) {
             const int J = wave >> 1, tn = wave & 1;
-            int k0 = 16 * J + 16, k1 = kChunk;
-            widen<P>(k0, k1);
-            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-            ak = mma_tile(bdAT.sub(16 * J), KxT(J).sub(16 * tn), k0, k1, ak);
-            aq = mma_tile(dAqT.sub(16 * J), QxT(J).sub(16 * tn), k0, k1, aq);
             const int cc = 16 * tn + frag_col();
-            const float gr = Gs[(16 * J + 15) * LR + cc];
+            const float gr = Gs[(16 * J + 15) * LR + cc];  // G at b_J
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I = 1; I < 4; ++I)
+                if (I > J) {
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 pk = mma_tile_k16(bdAT.sub(16 * J), KxT.sub(16 * tn), 16 * I, zero);
+                    const f32x4 pq = mma_tile_k16(dAqT.sub(16 * J), QxT.sub(16 * tn), 16 * I, zero);
+                    const float m = exp2_hw(Gs[(16 * I) * LR + cc] - gr);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ak[r] = fmaf(m, pk[r], ak[r]);
+                        aq[r] = fmaf(m, pq[r], aq[r]);
+                    }
+                }
             float gs[4], ks[4], dk0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

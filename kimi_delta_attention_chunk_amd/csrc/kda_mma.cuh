@@ -445,6 +445,28 @@ __device__ __forceinline__ f32x4 mma_tile(const STile<Prec::BF3, CA>& A, const S
     }
     return acc;
 }
+// acc += A(16 x [k0, k0+16)) * B(16 x [k0, k0+16))^T on swizzled tiles, k0 a
+// multiple of 16: a 16-deep product (v_mfma_f32_16x16x16_bf16, three times on the
+// hi/lo split; lane l holds indices k0 + 4 (l >> 4) .. + 3 of row l & 15).
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile_k16(const STile<Prec::F32, CA>& A, const STile<Prec::F32, CB>& B, int k0,
+                                              f32x4 acc) {
+    return mma_tile(A.plain(), B.plain(), k0, k0 + 16, acc);
+}
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile_k16(const STile<Prec::BF3, CA>& A, const STile<Prec::BF3, CB>& B, int k0,
+                                              f32x4 acc) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, k = k0 + 4 * (lane >> 4);
+    const int ao = A.at(r, k), bo = B.at(r, k);
+    const s16x4 ah = *(const s16x4*)(A.hi + ao), al = *(const s16x4*)(A.lo + ao);
+    const s16x4 bh = *(const s16x4*)(B.hi + bo), bl = *(const s16x4*)(B.lo + bo);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+    return acc;
+}
 // A fragment (rows of the view, k-block starting at kb) of a swizzled tile.
 template <int C>
 __device__ __forceinline__ void load_frag(AFrag<Prec::BF3>& f, const STile<Prec::BF3, C>& T, int kb) {
