@@ -74,33 +74,38 @@ __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
 }
 
 // T = (I + A)^{-1} for strictly lower-triangular A (64x64, stride kLD), by
-// 16x16 blocks: diagonal blocks by forward substitution (one wave per block,
-// one lane per column), then the off-diagonal blocks level by level,
+// 16x16 blocks: diagonal blocks by forward substitution, then the off-diagonal
+// blocks level by level,
 //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
-// X is scratch of 4*16*kLD16 floats.  Starts and ends with barriers.
+// Only the blocks on and below the diagonal of Tm are written (those above are
+// zero by definition; readers of Tm mask them).  A is read only strictly below
+// the diagonal.  X is scratch of 4*16*kLD16 floats.  Ends with a barrier.
 constexpr int kLD16 = 20;
 __device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, float* X) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    // zero the strict upper part and diagonal blocks are filled below
-    for (int e = threadIdx.x; e < kChunk * kChunk; e += kThreads) {
-        const int t = e >> 6, s = e & 63;
-        if ((s >> 4) > (t >> 4)) Tm[t * kLD + s] = 0.f;
-    }
     {
-        const int I = wave;  // 4 waves <-> 4 diagonal blocks
-        if (lane < 16) {
-            const int j = lane;
-            float x[16];
+        // diagonal block I = wave, right-looking: lane (column j = lane >> 2, quad
+        // position q = lane & 3) holds rows 4 q .. 4 q + 3 of column j.  Once row k
+        // is final it is x_k: its owner (quad position k >> 2) broadcasts it to its
+        // quad by DPP, and every row t > k takes -A[t][k] x_k.
+        const int I = wave, j = lane >> 2, q = lane & 3;
+        const float* Ab = A + (16 * I + 4 * q) * kLD + 16 * I;  // this lane's first row of the block
+        float r[4];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == j) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) r[i] = (4 * q + i == j) ? 1.f : 0.f;
+        static_for16([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            constexpr int qk = k >> 2;
+            constexpr int ctl = qk | (qk << 2) | (qk << 4) | (qk << 6);  // quad_perm [qk, qk, qk, qk]
+            const float xk = dpp_f<ctl>(r[k & 3]);
 #pragma unroll
-                for (int m = 0; m < t; ++m) acc -= A[(16 * I + t) * kLD + 16 * I + m] * x[m];
-                x[t] = acc;
+            for (int i = 0; i < 4; ++i) {
+                const float a = (4 * q + i > k) ? Ab[i * kLD + k] : 0.f;  // strictly below the diagonal only
+                r[i] = fmaf(-a, xk, r[i]);
             }
+        });
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Tm[(16 * I + t) * kLD + 16 * I + j] = x[t];
-        }
+        for (int i = 0; i < 4; ++i) Tm[(16 * I + 4 * q + i) * kLD + 16 * I + j] = r[i];
     }
     __syncthreads();
     for (int lvl = 1; lvl < 4; ++lvl) {

@@ -381,7 +381,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
 #pragma unroll
         for (int i = 0; i < kChunk * kChunk / 4 / kThreads; ++i) {
             const int e4 = 4 * (threadIdx.x + kThreads * i);
-            to[e4 >> 2] = *(const f32x4*)&Tm[(e4 >> 6) * kLD + (e4 & 63)];
+            const int t = e4 >> 6, s = e4 & 63;  // (blocks above the diagonal are zero, not stored in Tm)
+            to[e4 >> 2] = (s >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&Tm[t * kLD + s];
         }
     }
 
@@ -389,7 +390,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     // as many blocks per barrier as fit in KQG
     for (int e = threadIdx.x; e < kChunk * kChunk / 4; e += kThreads) {
         const int t = e >> 4, s4 = (e & 15) * 4;
-        Tt.put4(t, s4, *(const f32x4*)&Tm[t * kLD + s4]);
+        Tt.put4(t, s4, (s4 >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&Tm[t * kLD + s4]);
     }
     constexpr int NBLK = NB + NVB;
     constexpr int GRP = (3 * kChunk * kLB) / (kCB32 * LA);  // blocks per round
