@@ -277,8 +277,8 @@ __device__ __forceinline__ void load_g_block(const Prm& p, const ChunkRef& cr, i
     }
     r.db = (p.flags & 2u) ? p.dt_bias[h * DK + cb + c] : 0.f;
 }
-// GT[c][t] = in-chunk cumulative log-decay (the gate from f if flagged; zero
-// past the chunk end).  Thread (sg, c) scans its R tokens in registers and adds
+// GT[c][t] = in-chunk cumulative log-decay in base 2 (G log2 e; the gate from f
+// if flagged; zero past the chunk end), so a decay factor is one exp2.  Thread (sg, c) scans its R tokens in registers and adds
 // the totals of the earlier segments (seg: LDS [64 / R][32]).  Two barriers;
 // ends with one.
 template <int NTH>
@@ -292,7 +292,7 @@ __device__ __forceinline__ void put_g_block(const Prm& p, const ChunkRef& cr, in
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int t = R * sg + i;
-        x[i] = t < cr.len ? (gate ? nA * softplus_f(r.x[i] + r.db) : r.x[i]) : 0.f;
+        x[i] = t < cr.len ? (gate ? nA * softplus_f(r.x[i] + r.db) : r.x[i]) * kLog2e : 0.f;  // base 2
     }
 #pragma unroll
     for (int i = 1; i < R; ++i) x[i] += x[i - 1];
@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             const int e = threadIdx.x + e_i * kGThreads;
             const int t = e / kCB, cc = e - t * kCB;
             X1[t * LC + cc] = dwr[e_i];
-            const float kg = KTb[cc * kLD + t] * __expf(GTb[cc * kLD + t]);
+            const float kg = KTb[cc * kLD + t] * exp2_hw(GTb[cc * kLD + t]);
             X2[t * LC + cc] = kg;                 // Kg[t][c]
             QTb[cc * kLD + t] = bet[t] * kg;      // (beta Kg)^T, reusing the q tile
         }
@@ -552,8 +552,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             const int e = threadIdx.x + e_i * kGThreads;
             const int sr = e >> 5, cc = e & 31, r = (sr | 15), r0 = sr & ~15;
             const float gs = GTb[cc * kLD + sr], ks = KTb[cc * kLD + sr];
-            const float x = ks * exp_hw(GTb[cc * kLD + r] - gs);  // row sums: partner s = sr, r its block's last row
-            const float y = exp_hw(gs - GTb[cc * kLD + r0]);       // column sums: t = sr, r0 its block's first row
+            const float x = ks * exp2_hw(GTb[cc * kLD + r] - gs);  // row sums: partner s = sr, r its block's last row
+            const float y = exp2_hw(gs - GTb[cc * kLD + r0]);       // column sums: t = sr, r0 its block's first row
             STk[sr * LS + cc] = sr < 48 ? x : 0.f;
             STa[sr * LS + cc] = sr >= 16 ? bet[sr] * ks * y : 0.f;
             STb[sr * LS + cc] = sr >= 16 ? QTb[cc * kLD + sr] * y : 0.f;
@@ -575,7 +575,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                     const float gr = GTb[c * kLD + 16 * J + 15];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = exp_hw(GTb[c * kLD + 16 * I + frag_row(i)] - gr);
+                        const float e = exp2_hw(GTb[c * kLD + 16 * I + frag_row(i)] - gr);
                         rk[i] = fmaf(e, pk[i], rk[i]);
                         rq[i] = fmaf(e, pq[i], rq[i]);
                     }
@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                     pk = mma16_f32(Tm + 16 * J * kLD + 16 * I, kLD, 1, STb + 16 * I * LS + 16 * tn, LS, 1, 0, 16, pk);
                     const float gr = GTb[c * kLD + 16 * I];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) cs[i] = fmaf(exp_hw(gr - GTb[c * kLD + 16 * J + frag_row(i)]), pk[i], cs[i]);
+                    for (int i = 0; i < 4; ++i) cs[i] = fmaf(exp2_hw(gr - GTb[c * kLD + 16 * J + frag_row(i)]), pk[i], cs[i]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ODc[(16 * J + frag_row(i)) * LS + c] = cs[i];
@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
                 for (int j = 0; j < CPW; ++j) {
                     const float gs = row_bcast<u>(gtv[j]), ks = row_bcast<u>(ktv[j]), qs = row_bcast<u>(qtv[j]);
                     const float x = gtv[j] - gs;
-                    const float e = exp_hw(lower ? x : -x);
+                    const float e = exp2_hw(lower ? x : -x);
                     const float ek = e * ks;
                     rkv[j] = fmaf(ad_ts, ek, rkv[j]);
                     rqv[j] = fmaf(aq_ts, ek, rqv[j]);
@@ -653,9 +653,9 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             const int cc = c4 + j;
             const float gt = GTb[cc * kLD + t], kt = KTb[cc * kLD + t], qt = QTb[cc * kLD + t];
             const float rk = ODk[t * LS + cc], rq = ODq[t * LS + cc], ck = ODc[t * LS + cc], cq = 0.f;
-            const float gam = __expf(gt);
+            const float gam = exp2_hw(gt);
             const float gl_c = GTb[cc * kLD + last];
-            const float eL = __expf(gl_c - gt);
+            const float eL = exp2_hw(gl_c - gt);
             const float dqt = dq_r[j], dkh = dkh_r[j], dkg = dkt_r[j];
             const float bt = bet[t];
             const float kh = kt * eL;
@@ -664,7 +664,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             float dG = bt * kt * rk + qt * rq - kt * (ck + cq) + qt * gam * dqt + kt * gam * dkg - kh * dkh;
             // dG_L collects sum_t Kh . dKh and exp(G_L) dGamma_L
             const float sl = wave_sum(t < cr.len ? kh * dkh : 0.f);
-            if (t == last) dG += sl + __expf(gl_c) * dgl[cb + cc];
+            if (t == last) dG += sl + exp2_hw(gl_c) * dgl[cb + cc];
             if (t >= cr.len) { dQ = 0.f; dK = 0.f; dG = 0.f; }
             r_dbA += kt * rk;
             r_dq += qt * dQ;
