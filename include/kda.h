@@ -163,6 +163,17 @@ int kda_check_cu_seqlens(const int32_t* cu_seqlens, int32_t N, int32_t T, kda_st
 size_t kda_fwd_workspace(const kda_desc* desc);
 size_t kda_bwd_workspace(const kda_desc* desc);
 
+/* Introspection of the workspace layout (host only; no device access): the
+ * arrays that kda_fwd (backward = 0) or kda_bwd and a saving kda_fwd
+ * (backward = 1) keep in the workspace for this descriptor, in workspace
+ * order -- the name, byte offset and byte size of each.  Fills at most `cap`
+ * entries of the arrays given (any of them may be null) and returns the number
+ * of arrays, or -1 if the descriptor is invalid (kda_last_error says why).
+ * The first 256 bytes of a workspace hold no array (offset 0 marks an absent
+ * one inside the library).  For tests and tools that check the layout. */
+int kda_debug_ws_layout(const kda_desc* desc, int backward, const char** names, size_t* offsets,
+                        size_t* bytes, int cap);
+
 /* Forward: o and the final states hT of the recurrence at the top of this
  * file, in chunked form (openkimi README, What is implemented: the chunk_kda
  * row, with fused Q/K norm, decay gate and beta; torchtitan PR #4347,

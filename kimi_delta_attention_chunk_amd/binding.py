@@ -27,7 +27,7 @@ EXPORTS = ["kda_max_chunks", "kda_plan_varlen", "kda_check_cu_seqlens", "kda_fwd
            "kda_last_error", "kda_timing_enable", "kda_timing_collect", "kda_timing_count",
            "kda_timing_get", "kda_conv_fwd", "kda_conv_bwd_workspace", "kda_conv_bwd", "kda_gnorm_fwd",
            "kda_gnorm_bwd_workspace", "kda_gnorm_bwd", "kda_segment_maps", "kda_state_scan",
-           "kda_fwd_noalloc"]
+           "kda_fwd_noalloc", "kda_debug_ws_layout"]
 CONV_SILU = 1
 RMS_EPS = 1e-6
 
@@ -72,6 +72,9 @@ def load_library():
     lib.kda_bwd_workspace.restype = sz
     lib.kda_fwd.argtypes = [dp] + [vp] * 14 + [sz, vp]
     lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_debug_ws_layout.argtypes = [dp, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.c_int]
+    lib.kda_debug_ws_layout.restype = ctypes.c_int
     lib.kda_fwd_noalloc.argtypes = [dp] + [vp] * 14
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_bwd.argtypes = [dp] + [vp] * 22 + [sz, vp]
@@ -320,6 +323,21 @@ def bwd(q, k, v, g, beta, scale, d_o, h0=None, dhT=None, cu_seqlens=None, plan=N
                        _ptr(out.get("dA_log")), _ptr(out.get("ddt_bias")), _ptr(ws), ws.numel(),
                        _stream(dev)))
     return out
+
+
+def workspace_arrays(q_shape, dv, N, backward, dtype=torch.bfloat16):
+    """kda_debug_ws_layout: [(name, byte offset, byte size)] of the workspace arrays, in order."""
+    lib = load_library()
+    B, T, H, dk = q_shape
+    desc = KdaDesc(B, T, H, dk, dv, N, CHUNK, _dt(dtype), _dt(dtype), 1.0, 0)
+    n = lib.kda_debug_ws_layout(ctypes.byref(desc), int(backward), None, None, None, 0)
+    if n < 0:
+        _check(KDA_ERR_INVALID)
+    names = (ctypes.c_char_p * n)()
+    offs = (ctypes.c_size_t * n)()
+    nbs = (ctypes.c_size_t * n)()
+    lib.kda_debug_ws_layout(ctypes.byref(desc), int(backward), names, offs, nbs, n)
+    return [(names[i].decode(), int(offs[i]), int(nbs[i])) for i in range(n)]
 
 
 def workspace_bytes(q_shape, dv, N, backward, dtype=torch.bfloat16, flags=0):

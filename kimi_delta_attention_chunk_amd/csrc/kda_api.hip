@@ -217,6 +217,28 @@ size_t kda_fwd_workspace(const kda_desc* desc) {
     return kda::ws_layout(a, false).total;
 }
 
+int kda_debug_ws_layout(const kda_desc* desc, int backward, const char** names, size_t* offsets, size_t* bytes,
+                        int cap) {
+    g_err[0] = 0;
+    kda::ChunkArgs a;
+    if (ws_args(desc, a)) return -1;
+    struct Out {
+        const char** names;
+        size_t *offsets, *bytes;
+        int cap, n;
+    } out{names, offsets, bytes, cap, 0};
+    kda::ws_layout(a, backward != 0, [](void* ctx, const char* name, size_t off, size_t nb) {
+        Out& o = *(Out*)ctx;
+        if (o.n < o.cap) {
+            if (o.names) o.names[o.n] = name;
+            if (o.offsets) o.offsets[o.n] = off;
+            if (o.bytes) o.bytes[o.n] = nb;
+        }
+        ++o.n;
+    }, &out);
+    return out.n;
+}
+
 size_t kda_bwd_workspace(const kda_desc* desc) {
     g_err[0] = 0;
     kda::ChunkArgs a;

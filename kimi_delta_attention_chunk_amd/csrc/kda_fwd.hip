@@ -48,7 +48,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     return p;
 }
 
-WsLayout ws_layout(const ChunkArgs& a, bool backward) {
+WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec, void* ctx) {
     WsLayout L{};
     const size_t slots = (size_t)a.n_chunks_bound * a.H;
     const size_t C = kChunk, dk = a.dk, dv = a.dv;
@@ -57,7 +57,12 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     // pointer in the kernel parameters), and masked-out lanes of branch-free
     // stores write there (Prm::sink).
     size_t off = 256;
-    auto take = [&](size_t& field, size_t n) { field = off; off += bytes(n ? n : 1); };
+    auto take_named = [&](size_t& field, size_t n, const char* name) {
+        field = off;
+        if (rec) rec(ctx, name, off, bytes(n ? n : 1));
+        off += bytes(n ? n : 1);
+    };
+#define take(field, n) take_named(field, n, #field + 2)  // the array's name without "L."
     if (dk == 32 && dv == 64) {
         // affine chunk form: only what its kernels read
         take(L.hs, slots * dk * dv);
@@ -108,6 +113,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward) {
     }
     L.total = off;
     return L;
+#undef take
 }
 
 bool dims_supported(int dk, int dv) {

@@ -99,7 +99,10 @@ struct WsLayout {
     size_t pm, pmT, hh, qh, qhT, ol, aqT;            // affine chunk form (dk = 32)
     size_t total;
 };
-WsLayout ws_layout(const ChunkArgs& a, bool backward);
+// `rec`, if set, is told the name, byte offset and byte size of every array the
+// layout holds, in order (the introspection call kda_debug_ws_layout uses it).
+typedef void (*WsRecord)(void* ctx, const char* name, size_t offset, size_t bytes);
+WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec = nullptr, void* ctx = nullptr);
 
 bool dims_supported(int dk, int dv);
 hipError_t launch_fwd(const ChunkArgs& a, hipStream_t s);

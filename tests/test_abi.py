@@ -264,3 +264,38 @@ def test_noalloc_forward_validation():
     bad_null = list(args)
     bad_null[0] = None
     assert lib.kda_fwd_noalloc(ctypes.byref(fits), *bad_null) == B.KDA_ERR_INVALID
+
+
+# The arrays each kernel family writes (a missing one would send its stores to the
+# absent marker, offset 0).
+_WRITTEN = {
+    (32, False): {"hs", "pm", "pmT", "hh", "qh", "qhT", "ol"},
+    (32, True): {"hs", "pm", "pmT", "hh", "qh", "qhT", "ol", "aqT", "tm", "dhs", "part_a", "part_dt"},
+    (64, False): {"w", "u", "aqk", "hs", "vn", "qg", "khT", "gl"},
+}
+_WRITTEN[(64, True)] = _WRITTEN[(64, False)] | {"tm", "aqT", "qgT", "khb", "wT", "dhs", "dvn", "dqt", "dkh", "dwv",
+                                                  "daq", "dtv", "dgl", "dbv", "dkt", "dxq", "dxk", "part_a", "part_dt"}
+
+
+@pytest.mark.parametrize("dims", [(32, 64), (64, 64), (128, 128)])
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+@pytest.mark.parametrize("shape", [(1, 130, 3, 1), (2, 2048, 8, 2), (1, 1000, 2, 7), (1, 1, 1, 1)],
+                         ids=["dense1", "dense2", "packed7", "one_token"])
+def test_workspace_layout_has_no_array_at_offset_zero(dims, backward, shape):
+    """Every array of every layout lies past the 256-byte sink, 256-byte aligned, inside the
+    size the workspace query reports, with no overlap; and every array the kernels write is
+    present (this pins the layout fix after an array once sat at offset 0, the absent
+    marker, and a kernel's stores went to a null pointer)."""
+    dk, dv = dims
+    B, T, H, N = shape
+    arrays = kda.binding.workspace_arrays((B, T, H, dk), dv, N, backward)
+    total = kda.workspace_bytes((B, T, H, dk), dv, N, backward)
+    end = 256
+    for name, off, nb in arrays:
+        assert off >= 256 and off % 256 == 0 and nb > 0, (name, off, nb)
+        assert off >= end, (name, off, end)  # in order, disjoint
+        end = off + nb
+    assert end <= total
+    names = {n for n, _, _ in arrays}
+    need = _WRITTEN[(min(dk, 64), backward)]
+    assert need <= names, need - names
