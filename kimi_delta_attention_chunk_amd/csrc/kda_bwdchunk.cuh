@@ -615,6 +615,111 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // staged copy of each operand (every token by its own block's reference);
     // the middle factor, one number per channel and block pair, scales that
     // pair's 16-deep product.
+    if constexpr (P == Prec::BF3) {
+        // All seven operand tiles fit in LDS at once, so one staging phase serves both
+        // sums, and wave (block b, channels 16 tn ..) forms the row sums of b (over the
+        // blocks J < b) and its column sums (over the blocks I > b): b + (3 - b) = three
+        // 16-deep block products on every wave, and each wave alone owns the
+        // accumulator rows it updates.
+        const T64 dAt(ph, kChunk), dAqt(ph + 4096, kChunk), bdAT(ph + 8192, kChunk), dAqT(ph + 12288, kChunk);
+        const T64 KcT(ph + 16384, DK);  // [c][s] = k_s e^{G_{b(s)} - G_s}, b(s) the last row of s's block
+        // [c][t] = k_t e^{G_t - G_{a(t)}} and q_t e^{..}, a(t) the first row of t's block
+        const T64 KxT(ph + 18432, DK), QxT(ph + 20480, DK);
+        static_assert(20480 + 2048 <= PH, "P4 tiles must fit (bf16 hi/lo tiles)");
+        float gend[4], gst[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gend[i] = Gs[(16 * (tr >> 4) + 15) * LR + 4 * part + i];
+            gst[i] = Gs[(16 * (tr >> 4)) * LR + 4 * part + i];
+        }
+        __syncthreads();  // P3 tiles consumed
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tm + frag_row(r), s = 16 * tn + frag_col();
+                dAt.put(t, s, dAr[i][r]);
+                dAqt.put(t, s, aAq[i][r]);
+                if (tm == tn) {
+                    dAd[tm * 272 + (t & 15) * 17 + (s & 15)] = dAr[i][r];
+                    dAqd[tm * 272 + (t & 15) * 17 + (s & 15)] = aAq[i][r];
+                }
+            }
+            const int s = 16 * tn + frag_col();
+            f32x4 bd;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bd[r] = bet[16 * tm + frag_row(r)] * dAr[i][r];
+            bdAT.put4(s, 16 * tm + frag_row(0), bd);
+            dAqT.put4(s, 16 * tm + frag_row(0), aAq[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = 4 * part + i;
+            KcT.put(cc, tr, kx[i] * exp2_hw(gend[i] - G[i]));
+            const float e = exp2_hw(G[i] - gst[i]);
+            KxT.put(cc, tr, kx[i] * e);
+            QxT.put(cc, tr, qx[i] * e);
+        }
+        __syncthreads();
+        {
+            const int bk = wave >> 1, tn = wave & 1;
+            const int cc = 16 * tn + frag_col();
+            const float ga = Gs[(16 * bk) * LR + cc];       // G at the block's first row
+            const float gb = Gs[(16 * bk + 15) * LR + cc];  // and at its last row
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 ak = zero, aq = zero, ck = zero, cq = zero;
+#pragma unroll
+            for (int J = 0; J < 3; ++J)
+                if (J < bk) {  // row sums: partners in the earlier block J
+                    const f32x4 pk = mma_tile_k16(dAt.sub(16 * bk), KcT.sub(16 * tn), 16 * J, zero);
+                    const f32x4 pq = mma_tile_k16(dAqt.sub(16 * bk), KcT.sub(16 * tn), 16 * J, zero);
+                    const float m = exp2_hw(ga - Gs[(16 * J + 15) * LR + cc]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ak[r] = fmaf(m, pk[r], ak[r]);
+                        aq[r] = fmaf(m, pq[r], aq[r]);
+                    }
+                }
+#pragma unroll
+            for (int I = 1; I < 4; ++I)
+                if (I > bk) {  // column sums: partners in the later block I
+                    const f32x4 pk = mma_tile_k16(bdAT.sub(16 * bk), KxT.sub(16 * tn), 16 * I, zero);
+                    const f32x4 pq = mma_tile_k16(dAqT.sub(16 * bk), QxT.sub(16 * tn), 16 * I, zero);
+                    const float m = exp2_hw(Gs[(16 * I) * LR + cc] - gb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ck[r] = fmaf(m, pk[r], ck[r]);
+                        cq[r] = fmaf(m, pq[r], cq[r]);
+                    }
+                }
+            float gt[4], kt[4], qt[4], bt[4], dk0[4], dq0[4], dg0[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * bk + frag_row(r);
+                gt[r] = Gs[t * LR + cc];
+                kt[r] = Ks[t * LR + cc];
+                qt[r] = Qs[t * LR + cc];
+                bt[r] = bet[t];
+                dk0[r] = DKa[t * LR + cc];
+                dq0[r] = DQ[t * LR + cc];
+                dg0[r] = DG[t * LR + cc];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * bk + frag_row(r);
+                const float e = exp2_hw(gt[r] - ga), e2 = exp2_hw(gb - gt[r]);
+                const float rkv = e * ak[r], rqv = e * aq[r];  // zero in block 0 (no earlier block)
+                const float cs = e2 * (ck[r] + cq[r]);         // zero in block 3 (no later block)
+                DKa[t * LR + cc] = dk0[r] + bt[r] * rkv + cs;
+                DQ[t * LR + cc] = dq0[r] + rqv;
+                DG[t * LR + cc] = dg0[r] + bt[r] * kt[r] * rkv + qt[r] * rqv - kt[r] * cs;
+                const float pb = row16_sum(kt[r] * rkv);
+                if (frag_col() == 0) dba[t * 2 + tn] = pb;
+            }
+        }
+        __syncthreads();
+    } else {
     {
         // row sums: R'k[t] = sum_{s<t} dA[t][s] k_s e^{G_t-G_s},  Rq[t] = sum_{s<=t} dAq[t][s] k_s e^{..}
         const T64 dAt(ph, kChunk), dAqt(ph + 4608, kChunk);
@@ -748,6 +853,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             }
         }
         __syncthreads();
+    }
     }
     // diagonal blocks, exact pairwise decays; lane = token t (row t >> 4 of the
     // wave = diagonal block), each wave four channels.  The partner token s of
