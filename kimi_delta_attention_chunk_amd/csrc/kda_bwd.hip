@@ -817,7 +817,7 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
         const int tot16 = a.N * a.H * (DV / kPsBV);
         KDA_LAUNCH("bwd_dh", (bwd_pdh_kernel<TIn, P, kPsBV>), dim3(tot16), dim3(kPsThreads), s, p, tot16);
     } else {
-        constexpr int BV = DK <= 64 ? 32 : 16;  // dk = 128: the operand tiles fill the LDS
+        constexpr int BV = DK <= 32 ? 32 : 16;  // dk >= 64: more workgroups; dk = 128: the operand tiles fill the LDS
         const int total = a.N * a.H * (DV / BV);
         KDA_LAUNCH("bwd_dh", (bwd_dh_scan_kernel<DK, DV, BV, TIn, P>), dim3(total), dim3(kDhThreads), s, p, total);
     }

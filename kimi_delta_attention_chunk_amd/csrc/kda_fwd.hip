@@ -145,7 +145,7 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
         else
             KDA_LAUNCH("fwd_scan", (fwd_pscan_kernel<TOut, P, kPsBV, false, false>), dim3(total), dim3(kPsThreads), s, p, total);
     } else {
-        constexpr int BV = DK <= 64 ? 32 : 16;  // dk = 128: 16 columns per workgroup (kda_scan.cuh)
+        constexpr int BV = DK <= 32 ? 32 : 16;  // dk >= 64: 16 columns per workgroup (kda_scan.cuh)
         const int total = a.N * a.H * (DV / BV);
         KDA_LAUNCH("fwd_scan", (fwd_scan_kernel<DK, DV, BV, TOut, P>), dim3(total), dim3(kScanThreads), s, p, total,
                    write_o ? 1 : 0, store ? 1 : 0);
