@@ -18,7 +18,10 @@
 //       are MFMA products with the decay split at the first row of I and the
 //       last row of J (three factors, each at most 1): the outer two scale the
 //       operands, one staged copy each, the middle one each block pair's
-//       product.  Diagonal blocks use the exact exp of each difference.
+//       product.  In the bf16 path the diagonal blocks are split the same way
+//       into 4-token sub-blocks (4-deep fp32 products between sub-blocks, exact
+//       decays for the pairs inside one); the fp32 path takes the exact exp of
+//       every difference in the diagonal blocks.
 //   P5  the explicit factors (Qg, Kg, Kh, exp(G_L)) are folded in as they are
 //       produced; dg is the reverse in-chunk cumulative sum of dG; then the
 //       gate, sigmoid and L2-norm chains.
@@ -620,7 +623,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         // sums, and wave (block b, channels 16 tn ..) forms the row sums of b (over the
         // blocks J < b) and its column sums (over the blocks I > b): b + (3 - b) = three
         // 16-deep block products on every wave, and each wave alone owns the
-        // accumulator rows it updates.
+        // accumulator rows it updates.  The same wave then takes the pairs of its
+        // diagonal block b, so these sums are complete when they are added in.
         const T64 dAt(ph, kChunk), dAqt(ph + 4096, kChunk), bdAT(ph + 8192, kChunk), dAqT(ph + 12288, kChunk);
         const T64 KcT(ph + 16384, DK);  // [c][s] = k_s e^{G_{b(s)} - G_s}, b(s) the last row of s's block
         // [c][t] = k_t e^{G_t - G_{a(t)}} and q_t e^{..}, a(t) the first row of t's block
@@ -663,18 +667,25 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
         {
+            // Wave (block bk, channels 16 tn ..).  Lane l holds rows 16 bk + 4 g + r
+            // (r = 0..3) of column cc: the whole 4-token sub-block g = l >> 4.  The
+            // decays are split at this sub-block's first row a (row sums) and last
+            // row b (column sums), so the outer factors below are per row and
+            // every middle factor is per lane.
             const int bk = wave >> 1, tn = wave & 1;
-            const int cc = 16 * tn + frag_col();
-            const float ga = Gs[(16 * bk) * LR + cc];       // G at the block's first row
-            const float gb = Gs[(16 * bk + 15) * LR + cc];  // and at its last row
+            const int g4 = lane >> 4, n = lane & 15;
+            const int cc = 16 * tn + n;
+            const int ra = 16 * bk + 4 * g4;
+            const float gA = Gs[ra * LR + cc];        // G at the sub-block's first row
+            const float gB = Gs[(ra + 3) * LR + cc];  // and at its last row
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
             f32x4 ak = zero, aq = zero, ck = zero, cq = zero;
 #pragma unroll
             for (int J = 0; J < 3; ++J)
-                if (J < bk) {  // row sums: partners in the earlier block J
+                if (J < bk) {  // row sums: partners in the earlier block J (16-deep products)
                     const f32x4 pk = mma_tile_k16(dAt.sub(16 * bk), KcT.sub(16 * tn), 16 * J, zero);
                     const f32x4 pq = mma_tile_k16(dAqt.sub(16 * bk), KcT.sub(16 * tn), 16 * J, zero);
-                    const float m = exp2_hw(ga - Gs[(16 * J + 15) * LR + cc]);
+                    const float m = exp2_hw(gA - Gs[(16 * J + 15) * LR + cc]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         ak[r] = fmaf(m, pk[r], ak[r]);
@@ -686,17 +697,54 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 if (I > bk) {  // column sums: partners in the later block I
                     const f32x4 pk = mma_tile_k16(bdAT.sub(16 * bk), KxT.sub(16 * tn), 16 * I, zero);
                     const f32x4 pq = mma_tile_k16(dAqT.sub(16 * bk), QxT.sub(16 * tn), 16 * I, zero);
-                    const float m = exp2_hw(Gs[(16 * I) * LR + cc] - gb);
+                    const float m = exp2_hw(Gs[(16 * I) * LR + cc] - gB);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         ck[r] = fmaf(m, pk[r], ck[r]);
                         cq[r] = fmaf(m, pq[r], cq[r]);
                     }
                 }
+            // The diagonal block bk, by its 4-token sub-blocks: pairs in different
+            // sub-blocks as 4-deep fp32 products (v_mfma_f32_16x16x4_f32: lane l
+            // gives A[l & 15][l >> 4] and B[l >> 4][l & 15]) with the decay split
+            // at the sub-blocks' boundary rows, each factor at most 1; the middle
+            // factor is zero where the partner sub-block is not on the summed side.
+            const float* dAb = dAd + bk * 272;   // dA[16 bk + i][16 bk + j] at i * 17 + j
+            const float* dAqb = dAqd + bk * 272;
+#pragma unroll
+            for (int J = 0; J < 3; ++J) {  // row sums: partner sub-block J < g
+                const int s = 16 * bk + 4 * J + g4;  // this lane's B row (k index l >> 4)
+                const float gbJ = Gs[(16 * bk + 4 * J + 3) * LR + cc];
+                const float b = Ks[s * LR + cc] * exp2_hw(gbJ - Gs[s * LR + cc]);
+                const f32x4 pk = __builtin_amdgcn_mfma_f32_16x16x4f32(dAb[n * 17 + 4 * J + g4], b, zero, 0, 0, 0);
+                const f32x4 pq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAqb[n * 17 + 4 * J + g4], b, zero, 0, 0, 0);
+                const float m = J < g4 ? exp2_hw(gA - gbJ) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ak[r] = fmaf(m, pk[r], ak[r]);
+                    aq[r] = fmaf(m, pq[r], aq[r]);
+                }
+            }
+#pragma unroll
+            for (int I = 1; I < 4; ++I) {  // column sums: partner sub-block I > g
+                const int ti = 4 * I + g4;  // this lane's B row within the block
+                const float gaI = Gs[(16 * bk + 4 * I) * LR + cc];
+                const float e = exp2_hw(Gs[(16 * bk + ti) * LR + cc] - gaI);
+                const float bk_ = Ks[(16 * bk + ti) * LR + cc] * e, bq = Qs[(16 * bk + ti) * LR + cc] * e;
+                const float a1 = bet[16 * bk + ti] * dAb[ti * 17 + n];  // beta_t dA[t][s], s = 16 bk + n
+                const f32x4 pk = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bk_, zero, 0, 0, 0);
+                const f32x4 pq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAqb[ti * 17 + n], bq, zero, 0, 0, 0);
+                const float m = I > g4 ? exp2_hw(gaI - gB) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ck[r] = fmaf(m, pk[r], ck[r]);
+                    cq[r] = fmaf(m, pq[r], cq[r]);
+                }
+            }
             float gt[4], kt[4], qt[4], bt[4], dk0[4], dq0[4], dg0[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * bk + frag_row(r);
+                const int t = ra + r;
                 gt[r] = Gs[t * LR + cc];
                 kt[r] = Ks[t * LR + cc];
                 qt[r] = Qs[t * LR + cc];
@@ -705,17 +753,39 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                 dq0[r] = DQ[t * LR + cc];
                 dg0[r] = DG[t * LR + cc];
             }
+            // pairs inside the sub-block (all in this lane): exact decays
+            float rkx[4], rqx[4], ckx[4], cqx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float aqd = dAqb[(4 * g4 + i) * 17 + 4 * g4 + i];  // dAq[t][t], decay 1
+                rkx[i] = 0.f;
+                rqx[i] = aqd * kt[i];
+                ckx[i] = 0.f;
+                cqx[i] = aqd * qt[i];
+            }
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < i; ++j) {  // t = row i, s = row j < i
+                    const float da = dAb[(4 * g4 + i) * 17 + 4 * g4 + j], daq = dAqb[(4 * g4 + i) * 17 + 4 * g4 + j];
+                    const float e = exp2_hw(gt[i] - gt[j]);
+                    const float kse = kt[j] * e, kte = kt[i] * e;
+                    rkx[i] = fmaf(da, kse, rkx[i]);
+                    rqx[i] = fmaf(daq, kse, rqx[i]);
+                    ckx[j] = fmaf(bt[i] * da, kte, ckx[j]);
+                    cqx[j] = fmaf(daq, qt[i] * e, cqx[j]);
+                }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * bk + frag_row(r);
-                const float e = exp2_hw(gt[r] - ga), e2 = exp2_hw(gb - gt[r]);
-                const float rkv = e * ak[r], rqv = e * aq[r];  // zero in block 0 (no earlier block)
-                const float cs = e2 * (ck[r] + cq[r]);         // zero in block 3 (no later block)
+                const int t = ra + r;
+                const float e = exp2_hw(gt[r] - gA), e2 = exp2_hw(gB - gt[r]);
+                const float rkv = fmaf(e, ak[r], rkx[r]), rqv = fmaf(e, aq[r], rqx[r]);
+                const float cs = fmaf(e2, ck[r] + cq[r], ckx[r] + cqx[r]);
                 DKa[t * LR + cc] = dk0[r] + bt[r] * rkv + cs;
                 DQ[t * LR + cc] = dq0[r] + rqv;
                 DG[t * LR + cc] = dg0[r] + bt[r] * kt[r] * rkv + qt[r] * rqv - kt[r] * cs;
                 const float pb = row16_sum(kt[r] * rkv);
-                if (frag_col() == 0) dba[t * 2 + tn] = pb;
+                if (n == 0) dba[t * 2 + tn] = pb;
             }
         }
         __syncthreads();
@@ -854,8 +924,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         }
         __syncthreads();
     }
-    }
-    // diagonal blocks, exact pairwise decays; lane = token t (row t >> 4 of the
+    // diagonal blocks (fp32 path), exact pairwise decays; lane = token t (row t >> 4 of the
     // wave = diagonal block), each wave four channels.  The partner token s of
     // the same block sits in lane s of the same 16-lane row, so its values come
     // by DPP row broadcast from this lane's registers; the dA entries of (t, s)
@@ -910,6 +979,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         rowp[wave * kChunk + lane] = r_dbA;
     }
     __syncthreads();
+    }  // (diagonal blocks: fp32 path)
 
     // ------------------------------------------------ P5: dg, gate chain, outputs
     // (a) dG_L into the last row, rows past the end zeroed, reverse cumulative sum -> DG holds dg
@@ -981,8 +1051,10 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     if (tid < kChunk) {
         const int t = tid;
         float db = 0.f;
+        if constexpr (P != Prec::BF3) {  // the fp32 path's diagonal blocks
 #pragma unroll
-        for (int w = 0; w < NW; ++w) db += rowp[w * kChunk + t];
+            for (int w = 0; w < NW; ++w) db += rowp[w * kChunk + t];
+        }
         db += dba[t * 2] + dba[t * 2 + 1] + dbw[t * 2] + dbw[t * 2 + 1];
 #pragma unroll
         for (int g = 0; g < GV; ++g) db += dbv[t * GV + g];

@@ -62,7 +62,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec, void* ctx) {
         if (rec) rec(ctx, name, off, bytes(n ? n : 1));
         off += bytes(n ? n : 1);
     };
-#define take(field, n) take_named(field, n, #field + 2)  // the array's name without "L."
+#define take(field, n) take_named(field, n, &(#field)[2])  // the array's name without "L."
     if (dk == 32 && dv == 64) {
         // affine chunk form: only what its kernels read
         take(L.hs, slots * dk * dv);
