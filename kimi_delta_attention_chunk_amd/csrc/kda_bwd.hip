@@ -486,7 +486,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             }
         }
         __syncthreads();
-        // transposed copies for the row-side pair sums (lanes run over t)
+        // transposed copies for the column sums (A operands with rows s)
         #pragma unroll
     for (int e_i = 0; e_i < (kChunk * kChunk) / kGThreads; ++e_i) {
         const int e = threadIdx.x + e_i * kGThreads;
@@ -513,8 +513,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     //                 (and q_t e^{G_t - G_r} with dAq)
     //   so one scaled operand per side serves every block pair; the results are
     //   scaled by the other factor and gathered in LDS ([t][c]: ODk, ODq, ODc);
-    //   diagonal blocks: the exact exp of each difference, partners by DPP row
-    //   broadcast within the 16-lane row of the block.
+    //   diagonal blocks: split the same way into 4-token sub-blocks (4-deep
+    //   products between sub-blocks), exact exps for the pairs inside one.
     float* const STa = dT;                 // Kb  [64][LS] (dT is free after phase 4)
     float* const STb = dT + kChunk * LS;   // Qb  [64][LS]
     float* const ODk = X1;                 // off-diagonal row sums with dA  [t][c]
@@ -602,51 +602,91 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             }
         }
         __syncthreads();
-        // -- diagonal blocks and the per-token epilogue: lane = token t, CPW channels per wave.
-        // The partner s = 16 (t >> 4) + u sits in lane u of this lane's 16-lane row.  One exp
-        // per pair, of the non-positive difference: e^{G_t - G_s} for s <= t, e^{G_s - G_t}
-        // for s >= t; dA, dAq are zero outside their triangles (dA strictly lower, dAq lower),
-        // so every product only counts on its own side of the diagonal.
-        float gtv[CPW], ktv[CPW], qtv[CPW], rkv[CPW], rqv[CPW], ckv[CPW], cqv[CPW];
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-            const int cc = c4 + j;
-            gtv[j] = GTb[cc * kLD + t];
-            ktv[j] = KTb[cc * kLD + t];
-            qtv[j] = QTb[cc * kLD + t];
-            rkv[j] = rqv[j] = ckv[j] = cqv[j] = 0.f;
-        }
+        // -- diagonal blocks, by 4-token sub-blocks.  Wave (block bk, channels 16 tn ..):
+        // lane l holds rows 16 bk + 4 g + r (r = 0..3) of column cc, the whole sub-block
+        // g = l >> 4.  Pairs in different sub-blocks are 4-deep fp32 products
+        // (v_mfma_f32_16x16x4_f32: lane l gives A[l & 15][l >> 4] and B[l >> 4][l & 15])
+        // with the decay split at the sub-blocks' boundary rows (three factors, each at
+        // most 1; the middle one zero where the partner sub-block is not on the summed
+        // side); the pairs inside a sub-block take the exact exp of their difference.
         {
-            const float btl = bet[t];
-            const int sb = t & ~15, tl = t & 15;
-            static_for16([&](auto uc) {
-                constexpr int u = decltype(uc)::value;
-                const int sa = sb + u;
-                const float ad_ts = Y[sa * kLD + t], aq_ts = Tm[sa * kLD + t];  // dA[t][s], scale dAqk[t][s]
-                const float ad_st = dA[sa * kLD + t], aq_st = dAq[sa * kLD + t];  // dA[s][t], scale dAqk[s][t]
-                const float bad = row_bcast<u>(btl) * ad_st;                     // beta_s dA[s][t]
-                const bool lower = u <= tl;
+            const int bk = wave >> 1, tn = wave & 1;
+            const int g4 = lane >> 4, n = lane & 15;
+            const int cc = 16 * tn + n;
+            const int ra = 16 * bk + 4 * g4, r0 = 16 * bk;
+            const float* Gc = GTb + cc * kLD;  // G[.][cc], k[.][cc], q[.][cc]
+            const float* Kc = KTb + cc * kLD;
+            const float* Qc = QTb + cc * kLD;
+            const float gA = Gc[ra], gB = Gc[ra + 3];  // G at the sub-block's first and last rows
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            f32x4 ak = zero, aq = zero, ac = zero;
 #pragma unroll
-                for (int j = 0; j < CPW; ++j) {
-                    const float gs = row_bcast<u>(gtv[j]), ks = row_bcast<u>(ktv[j]), qs = row_bcast<u>(qtv[j]);
-                    const float x = gtv[j] - gs;
-                    const float e = exp2_hw(lower ? x : -x);
-                    const float ek = e * ks;
-                    rkv[j] = fmaf(ad_ts, ek, rkv[j]);
-                    rqv[j] = fmaf(aq_ts, ek, rqv[j]);
-                    ckv[j] = fmaf(bad, ek, ckv[j]);
-                    cqv[j] = fmaf(aq_st * qs, e, cqv[j]);
+            for (int J = 0; J < 3; ++J) {  // row sums: partner sub-block J < g
+                const int s = r0 + 4 * J + g4;  // this lane's B row (k index l >> 4)
+                const float gbJ = Gc[r0 + 4 * J + 3];
+                const float b = Kc[s] * exp2_hw(gbJ - Gc[s]);
+                const int ai = (r0 + n) * kLD + r0 + 4 * J + g4;  // dA[16 bk + n][s]
+                const f32x4 pk = __builtin_amdgcn_mfma_f32_16x16x4f32(dA[ai], b, zero, 0, 0, 0);
+                const f32x4 pq = __builtin_amdgcn_mfma_f32_16x16x4f32(dAq[ai], b, zero, 0, 0, 0);
+                const float m = J < g4 ? exp2_hw(gA - gbJ) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ak[r] = fmaf(m, pk[r], ak[r]);
+                    aq[r] = fmaf(m, pq[r], aq[r]);
                 }
-            });
-        }
-        // this lane owns (t, its CPW channels) of the gathered sums
+            }
 #pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-            const int cc = c4 + j;
-            ODk[t * LS + cc] += rkv[j];
-            ODq[t * LS + cc] += rqv[j];
-            ODc[t * LS + cc] += ckv[j] + cqv[j];
+            for (int I = 1; I < 4; ++I) {  // column sums: partner sub-block I > g
+                const int tI = r0 + 4 * I + g4;  // this lane's B row
+                const float gaI = Gc[r0 + 4 * I];
+                const float e = exp2_hw(Gc[tI] - gaI);
+                const int ai = tI * kLD + r0 + n;  // dA[t][16 bk + n]
+                f32x4 pc = __builtin_amdgcn_mfma_f32_16x16x4f32(dA[ai], bet[tI] * Kc[tI] * e, zero, 0, 0, 0);
+                pc = __builtin_amdgcn_mfma_f32_16x16x4f32(dAq[ai], Qc[tI] * e, pc, 0, 0, 0);
+                const float m = I > g4 ? exp2_hw(gaI - gB) : 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ac[r] = fmaf(m, pc[r], ac[r]);
+            }
+            float gt[4], kt[4], qt[4], bt[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                gt[r] = Gc[ra + r];
+                kt[r] = Kc[ra + r];
+                qt[r] = Qc[ra + r];
+                bt[r] = bet[ra + r];
+            }
+            // pairs inside the sub-block (all in this lane)
+            float rkx[4], rqx[4], cx[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float aqd = dAq[(ra + i) * kLD + ra + i];  // scale dAqk[t][t], decay 1
+                rkx[i] = 0.f;
+                rqx[i] = aqd * kt[i];
+                cx[i] = aqd * qt[i];
+            }
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < i; ++j) {  // t = row i, s = row j < i
+                    const float da = dA[(ra + i) * kLD + ra + j], daq = dAq[(ra + i) * kLD + ra + j];
+                    const float e = exp2_hw(gt[i] - gt[j]);
+                    const float kse = kt[j] * e;
+                    rkx[i] = fmaf(da, kse, rkx[i]);
+                    rqx[i] = fmaf(daq, kse, rqx[i]);
+                    cx[j] = fmaf(bt[i] * da, kt[i] * e, cx[j]);
+                    cx[j] = fmaf(daq, qt[i] * e, cx[j]);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int o = (ra + r) * LS + cc;
+                const float e = exp2_hw(gt[r] - gA), e2 = exp2_hw(gB - gt[r]);
+                ODk[o] += fmaf(e, ak[r], rkx[r]);
+                ODq[o] += fmaf(e, aq[r], rqx[r]);
+                ODc[o] += fmaf(e2, ac[r], cx[r]);
+            }
         }
+        __syncthreads();
+        // -- the per-token epilogue: lane = token t, CPW channels per wave
         float dg_o[CPW], dq_o[CPW], dk_o[CPW];
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
