@@ -63,7 +63,8 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     float* const DKa = ACC + kChunk * LR;
     float* const DG = ACC + 2 * kChunk * LR;
     __shared__ float dAd[4 * 16 * 17], dAqd[4 * 16 * 17];  // diagonal blocks of dA, dAq
-    __shared__ float bet[kChunk], rnq[kChunk], rnk[kChunk];
+    __shared__ __attribute__((aligned(16))) float bet[kChunk];
+    __shared__ float rnq[kChunk], rnk[kChunk];
     __shared__ float seg[16 * 32], wsum[NW];
     __shared__ float GL[DK], dgl[DK], colp[NW * DK];
     __shared__ float dbv[kChunk * GV], dbw[kChunk * 2], dba[kChunk * 2], rowp[NW * kChunk];
@@ -384,8 +385,10 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             load_frag(fa, vnb.sub(16 * am), 32 * kb);
             aKh = mma_ff(fa, fb, aKh);
         }
-        // dAqk = dO vn^T and dT_v = dvn (beta V)^T = (dvn V^T) diag(beta): tiles w, w + 8,
-        // which share the column tile w & 3
+        // dAqk = dO vn^T: tiles w, w + 8, which share the column tile w & 3; and
+        // dT_v = dvn (beta V)^T = (dvn V^T) diag(beta), held transposed (aT: tiles (w & 3,
+        // w >> 2 + 2 i) of dT^T), so that a lane's four values are consecutive s of a row
+        // t of dT when it is staged
         {
             const int tn = wave & 3;
 #pragma unroll
@@ -399,46 +402,42 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
                     load_frag_hi(fa, dOb.sub(16 * tm), 32 * kb);
                     aAq[i] = mma_ff_ah(fa, fv, aAq[i]);
                     load_frag(fa, dvnb.sub(16 * tm), 32 * kb);
-                    aT[i] = mma_ff_bh(fa, fvh, aT[i]);
+                    aT[i] = mma_ff_ah(fvh, fa, aT[i]);
                 }
             }
-            const float bs = bet[16 * tn + frag_col()];  // beta of this lane's column s
+            const f32x4 bs = *(const f32x4*)&bet[16 * tn + frag_row(0)];  // beta of this lane's rows s
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) aT[i][r] *= bs;
+                for (int r = 0; r < 4; ++r) aT[i][r] *= bs[r];
         }
-        // X_u = T^T dvn, tiles (am, an + 2 e): dV = beta X_u, dbeta_v = rowsum(X_u V)
+        // X_u = T^T dvn, formed transposed: tiles (an + 2 e, am) of X_u^T = dvn^T T, so
+        // that a lane holds four consecutive columns j of one row t of dV = beta X_u
+        // (one 8-byte store); dbeta_v = rowsum(X_u V)
         {
             TOut* dvout = (TOut*)p.dv;
             AFrag<P> ft[2], fy;  // T^T rows am: zero before index 16 am, so k-blocks (am >> 1) .. 1
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 if (kb >= (am >> 1)) load_frag(ft[kb], TT.sub(16 * am), 32 * kb);
+            const int t = 16 * am + frag_col();
+            const float bt = bet[t];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int jt = an + 2 * e;  // 16-column tile of dv
+                const int j0 = 16 * jt + frag_row(0);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     if (kb >= (am >> 1)) {
                         load_frag(fy, dvnT.sub(16 * jt), 32 * kb);
-                        acc = mma_ff(ft[kb], fy, acc);
+                        acc = mma_ff(fy, ft[kb], acc);
                     }
-                float bt[4], vv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * am + frag_row(r);
-                    bt[r] = bet[t];
-                    vv[r] = Vh.get_hi(t, 16 * jt + frag_col());
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * am + frag_row(r), j = 16 * jt + frag_col();
-                    const float part_v = row16_sum(acc[r] * vv[r]);
-                    if (frag_col() == 0) dbv[t * GV + jt] = part_v;
-                    if (t < cr.len) Elem<TOut>::store(dvout, tok_index(cr.t0 + t, h, p.H, DV) + j, bt[r] * acc[r]);
-                }
+                const f32x4 vv = Vh.get4_hi(t, j0);
+                const float part_v = sum_rows((acc[0] * vv[0] + acc[1] * vv[1]) + (acc[2] * vv[2] + acc[3] * vv[3]));
+                if (lane < 16) dbv[t * GV + jt] = part_v;
+                const float o[4] = {bt * acc[0], bt * acc[1], bt * acc[2], bt * acc[3]};
+                if (t < cr.len) store4<TOut>(dvout + tok_index(cr.t0 + t, h, p.H, DV) + j0, o);
             }
         }
     }
@@ -493,14 +492,15 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             dwT.put4(cc, 16 * am + frag_row(0), dw);
         }
         __syncthreads();
-        // dT = dT_v + dw (beta Kg)^T   (dT_v already carries beta_s: it was formed with beta V)
+        // dT = dT_v + dw (beta Kg)^T, transposed as aT   (dT_v already carries beta_s: it was
+        // formed with beta V)
         {
             AFrag<P> fb, fa;  // both tiles w, w + 8 share the column tile w & 3
             load_frag(fb, bKg.sub(16 * (wave & 3)), 0);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 load_frag(fa, dwt.sub(16 * ((wave + NW * i) >> 2)), 0);
-                aT[i] = mma_ff(fa, fb, aT[i]);
+                aT[i] = mma_ff(fb, fa, aT[i]);
             }
         }
         // X_w = T^T dw: dKg = beta X_w, dbeta_w = rowsum(X_w Kg)
@@ -546,8 +546,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int tile = wave + NW * i, tm = tile >> 2, tn = tile & 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dTt.put(16 * tm + frag_row(r), 16 * tn + frag_col(), aT[i][r]);
+            dTt.put4(16 * tm + frag_col(), 16 * tn + frag_row(0), aT[i]);  // row t, s .. s + 3
         }
         __syncthreads();
         // Y = dT T^T, stored transposed: YT[b][t].  This wave's tiles w, w + 8 share
@@ -1014,7 +1013,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             for (int i = 0; i < 4; ++i) {
                 const float x = in ? graw_f[i] + dtb[i] : 0.f;
                 const float df = in ? dgv[i] * (-eA) * dsoftplus_f(x) : 0.f;
-                pa += in ? dgv[i] * (-eA * softplus_f(x)) : 0.f;
+                pa += dgv[i] * graw[i];  // graw: the log-decay -e^A softplus(x) (zero past the end)
                 dgv[i] = df;
             }
             // column sums of df over this wave's 8 rows (lanes 8 apart), per wave

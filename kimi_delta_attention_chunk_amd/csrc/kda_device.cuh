@@ -31,12 +31,14 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
     return __uint_as_float(((uint32_t)u) << 16);
 }
-// Round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Round to nearest even; NaN stays NaN (the hardware conversion,
+// v_cvt_pk_bf16_f32, in the default round-to-nearest-even mode).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values packed as a 32-bit word, a in the low half (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -76,8 +78,8 @@ template <>
 __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float (&x)[4]) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-    v[1] = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    v[0] = pack_bf16x2(x[0], x[1]);
+    v[1] = pack_bf16x2(x[2], x[3]);
     *(u32x2*)p = v;
 }
 
@@ -95,7 +97,7 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&x)[8
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     *(u32x4*)p = v;
 }
 

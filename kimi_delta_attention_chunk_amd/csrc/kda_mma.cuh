@@ -354,6 +354,7 @@ template <int C> struct STile<Prec::F32, C> {
     __device__ __forceinline__ void put_hi(int r, int k, float x) const { put(r, k, x); }
     __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const { put4(r, k, x); }
     __device__ __forceinline__ float get_hi(int r, int k) const { return p[r * ld + k]; }
+    __device__ __forceinline__ f32x4 get4_hi(int r, int k) const { return *(const f32x4*)(p + r * ld + k); }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;
         t.p += r * ld;
@@ -393,6 +394,12 @@ template <int C> struct STile<Prec::BF3, C> {
     // neither stored nor read (load_frag_hi, mma_ff_ah / mma_ff_bh).
     __device__ __forceinline__ void put_hi(int r, int k, float x) const { hi[at(r, k)] = (__bf16)x; }
     __device__ __forceinline__ float get_hi(int r, int k) const { return (float)hi[at(r, k)]; }
+    // four consecutive values (k a multiple of 4), one 8-byte read
+    __device__ __forceinline__ f32x4 get4_hi(int r, int k) const {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 h = *(const bf16x4*)(hi + at(r, k));
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
     __device__ __forceinline__ void put4_hi(int r, int k, f32x4 x) const {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 h;
