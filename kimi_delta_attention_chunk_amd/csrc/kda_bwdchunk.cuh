@@ -114,8 +114,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
         if (kb >= (wave >> 2))
-            load_afrag(fa[kb], (const char*)(p.aqT + slot * kChunk * kChunk) +
-                                   (size_t)((16 * (wave >> 1) + (lane & 15)) * 2 + kb) * kKBlockBytes);
+            load_afrag(fa[kb], frag_rec(p.aqT + slot * kChunk * kChunk, 16 * (wave >> 1) + (lane & 15), kb, 2));
     {
         const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
         const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
@@ -214,7 +213,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ P0: v_new and dv_new of the chunk
     //   v_new  = T (beta V - (beta Kg) h)      (= u - w h)
     //   dv_new = Kh D' + scale Aqk^T dO         (D' = dL/dS at the chunk end)
-    // Aqk^T comes as row fragments from the intra-chunk kernel's k-block array;
+    // Aqk^T comes as row fragments from the intra-chunk kernel's fragment-form array;
     // T, beta Kg, Kh, h^T, D'^T and dO^T are staged in LDS from registers.  Wave w
     // forms 64x64 tiles (w >> 1, 2 (w & 1) + e), e = 0, 1; the results pass
     // through fp32 LDS staging into the row-major registers Vn, dVn that the
@@ -345,7 +344,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     {
         // All dv columns at once (two k-blocks per product).  ph: T^T, v_new, dv_new,
         // dv_new^T, dO; ACC (not yet accumulating): v.  dO and v are bf16 numbers:
-        // hi parts only.  h and D' (rows c, columns j: k-block form for fp32) come
+        // hi parts only.  h and D' (rows c, columns j, row-major fp32) come
         // as register fragments from their fp32 arrays.
         const T64 vnb(ph + 4608, kChunk), dvnb(ph + 9216, kChunk), dvnT(ph + 13824, DV), dOb(ph + 18432, kChunk);
         const T64 Vh(ACC, kChunk);

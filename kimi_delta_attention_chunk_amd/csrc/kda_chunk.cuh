@@ -61,7 +61,7 @@ struct Prm {
     float *dqt, *dkh, *dwv, *daq, *dtv, *dgl, *dbv;
     float *dkt, *dxq, *dxk, *part_a, *part_dt;
     // affine form of a chunk (dk = 32): h' = P h + hh, o = ol + qh h, and for
-    // the backward D = P^T D' + qh^T dO (k-block or fragment-order arrays, see
+    // the backward D = P^T D' + qh^T dO (fragment-form or fragment-order arrays, see
     // the intra-chunk kernel); aqT = Aqk^T for the backward chunk kernel
     float *pm, *pmT, *hh, *qh, *qhT, *ol, *aqT;
     // the workspace's first 256 bytes, never read: lanes whose store is masked

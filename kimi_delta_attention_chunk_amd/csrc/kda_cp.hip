@@ -17,7 +17,7 @@
 // seg_map_kernel: one workgroup of four waves per (segment, head); the 32 x 32
 // product X = P X runs chunk after chunk from X = I with the same fragment
 // scheme as the state pass (P's rows as register fragments from the intra
-// kernel's k-block array, prefetched four chunks ahead; X^T in a
+// kernel's fragment-form array, prefetched four chunks ahead; X^T in a
 // double-buffered LDS tile, one barrier per chunk).
 // state_scan_kernel: one workgroup per (head, 32 state columns); fp32 MFMA over
 // the segments in order, M_r staged in LDS (transposed for the backward), the
@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(kPsThreads) seg_map_kernel(Prm p, float* __res
     p.seq.seq_chunks(n, c0, c1);
     auto slot_of = [&](int cc) { return (size_t)(cc < c1 ? cc : c1 - 1) * p.H + h; };
     auto load = [&](int cc, AFrag<P>& f) {
-        load_afrag(f, (const char*)(p.pm + slot_of(cc) * DK * DK) + (size_t)(16 * tc + lr) * kKBlockBytes);
+        load_afrag(f, frag_rec(p.pm + slot_of(cc) * DK * DK, 16 * tc + lr, 0, 1));
     };
     XT[0].put4(jcol, crow, S);
     if (c0 < c1) {

@@ -11,7 +11,7 @@
 // stored for the per-chunk gradient kernels; D after the first chunk is dh0.
 //
 // Every state-independent operand is an MFMA A fragment loaded straight from
-// the k-block arrays the intra-chunk kernel writes for the reverse pass --
+// the fragment-form arrays the intra-chunk kernel writes for the reverse pass --
 // Aqk^T and Kh (rows t), (exp(G) q)^T and w^T (rows c) -- two chunks ahead,
 // double buffered, as in the forward scan.  Only dO^T, D^T and dv_new^T pass
 // through LDS: the fp32 D stays in the registers of the lanes that own its
@@ -58,17 +58,17 @@ __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRe
     const char* wt = (const char*)(p.wT + slot * DK * kChunk);       // [c][2]
     const int row = 16 * tm + lr;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) load_afrag(R.aq[kb], aq + (size_t)(row * 2 + kb) * kKBlockBytes);
+    for (int kb = 0; kb < 2; ++kb) load_afrag(R.aq[kb], frag_rec(aq, row, kb, 2));
 #pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb) load_afrag(R.kh[kb], kh + (size_t)(row * F::KB + kb) * kKBlockBytes);
+    for (int kb = 0; kb < F::KB; ++kb) load_afrag(R.kh[kb], frag_rec(kh, row, kb, F::KB));
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kDhWaves * i;
         const int c16 = 16 * ((tile < F::TH ? tile : 0) / F::TN);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            load_afrag(R.qt[i][kb], qt + (size_t)((c16 + lr) * 2 + kb) * kKBlockBytes);
-            load_afrag(R.wt[i][kb], wt + (size_t)((c16 + lr) * 2 + kb) * kKBlockBytes);
+            load_afrag(R.qt[i][kb], frag_rec(qt, c16 + lr, kb, 2));
+            load_afrag(R.wt[i][kb], frag_rec(wt, c16 + lr, kb, 2));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + c16 + frag_row(r)];

@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     float* A = S1;                  // fp32 Akk, after pass 1
     const T64 Tt(S1, kChunk);       // T as an MFMA operand, after the solve
 
-    // w, exp(G) q, (k exp(G_L - G))^T and Aqk go to the workspace in k-block form
+    // w, exp(G) q, (k exp(G_L - G))^T and Aqk go to the workspace in fragment form
     // (kda_mma.cuh) for the sequential kernels, which load MFMA fragments from it
     // directly.
     constexpr Prec WP = P;
@@ -168,8 +168,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dkk[2] = {0.f, 0.f}, dqk[2] = {0.f, 0.f}, dqd = 0.f;
 
-    char* qg = (char*)(p.qg + slot * kChunk * DK);    // [t][DK/32] k-blocks
-    char* khT = (char*)(p.khT + slot * DK * kChunk);  // [c][2] k-blocks
+    char* qg = (char*)(p.qg + slot * kChunk * DK);    // rows t, DK/32 k-blocks
+    char* khT = (char*)(p.khT + slot * DK * kChunk);  // rows c, 2 k-blocks
     float* KhS = Tm;                                   // (k exp(G_L - G))^T staging, [c][t], pass 1 only
     float* QgS = Tm + kCB32 * kLD;                     // (exp(G) q)^T staging, [c][t], pass 1 only (dk >= 64)
     const bool rev_ops = DK != 32 && p.qgT != nullptr;  // transposed operands for the reverse scan
@@ -220,10 +220,9 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             for (int J = 1; J <= 3; ++J)
                 if (tr < 16 * J) Kc.put8(kc_off(J) + tr, 8 * part, kc[J - 1]);
             if constexpr (DK != 32) {  // (dk = 32 keeps the affine form instead)
-                store_kblock8<WP>(qg + (size_t)(tr * (DK / 32) + b) * kKBlockBytes, qgv, part);
+                store_frag8<WP>(frag_rec(qg, tr, b, DK / 32), tr, qgv, part);
                 if (rev_ops)  // Kh rows t, channels of this block
-                    store_kblock8<WP>((char*)(p.khb + slot * kChunk * DK) + (size_t)(tr * (DK / 32) + b) * kKBlockBytes,
-                                      khv, part);
+                    store_frag8<WP>(frag_rec(p.khb + slot * kChunk * DK, tr, b, DK / 32), tr, khv, part);
             }
             if constexpr (DK == 32) {
 #pragma unroll
@@ -241,12 +240,11 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             float x[8];
             const f32x4 a0 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8], a1 = *(const f32x4*)&KhS[cr8 * kLD + 8 * w8 + 4];
             x[0] = a0[0]; x[1] = a0[1]; x[2] = a0[2]; x[3] = a0[3]; x[4] = a1[0]; x[5] = a1[1]; x[6] = a1[2]; x[7] = a1[3];
-            store_kblock8<WP>(khT + (size_t)((cb + cr8) * 2 + (w8 >> 2)) * kKBlockBytes, x, w8 & 3);
+            store_frag8<WP>(frag_rec(khT, cb + cr8, w8 >> 2, 2), cb + cr8, x, w8 & 3);
             if (rev_ops) {  // (exp(G) q)^T rows c, tokens as indices
                 const f32x4 b0 = *(const f32x4*)&QgS[cr8 * kLD + 8 * w8], b1 = *(const f32x4*)&QgS[cr8 * kLD + 8 * w8 + 4];
                 x[0] = b0[0]; x[1] = b0[1]; x[2] = b0[2]; x[3] = b0[3]; x[4] = b1[0]; x[5] = b1[1]; x[6] = b1[2]; x[7] = b1[3];
-                store_kblock8<WP>((char*)(p.qgT + slot * DK * kChunk) + (size_t)((cb + cr8) * 2 + (w8 >> 2)) * kKBlockBytes,
-                                  x, w8 & 3);
+                store_frag8<WP>(frag_rec(p.qgT + slot * DK * kChunk, cb + cr8, w8 >> 2, 2), cb + cr8, x, w8 & 3);
             }
         }
         // off-diagonal Gram tiles
@@ -349,7 +347,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     }
     {
         if constexpr (DK != 32) {
-            // Aqk to the workspace in k-block form, zero above the diagonal: 8 entries per thread and pass
+            // Aqk to the workspace in fragment form, zero above the diagonal: 8 entries per thread and pass
             char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
 #pragma unroll
             for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
@@ -358,7 +356,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 float x[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
-                store_kblock8<WP>(aq + (size_t)(t * 2 + (s0 >> 5)) * kKBlockBytes, x, (s0 >> 3) & 3);
+                store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
             }
         }
         if (p.aqT) {
@@ -371,7 +369,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 float x[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
-                store_kblock8<WP>(aqt + (size_t)(sr * 2 + (t0 >> 5)) * kKBlockBytes, x, (t0 >> 3) & 3);
+                store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
             }
         }
     }
@@ -434,8 +432,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             }
             if (rev_ops && b < NB) {  // w^T rows c, tokens as indices: four consecutive t per lane
                 const int t0 = tm * 16 + frag_row(0), cw = b * kCB32 + tn * 16 + frag_col();
-                store_kblock4<WP>((char*)(p.wT + slot * DK * kChunk) + (size_t)(cw * 2 + (t0 >> 5)) * kKBlockBytes, acc,
-                                  t0 & 31);
+                store_frag4<WP>(frag_rec(p.wT + slot * DK * kChunk, cw, t0 >> 5, 2), cw, acc, t0 & 31);
             }
             if (DK <= 64 && b < NB) {  // w: staged in Tm [t][c] (stride kLD), written out below
 #pragma unroll
@@ -443,8 +440,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             } else if (b < NB) {  // w (dk > 64): k-block b of rows 16 tm .., straight from the fragment
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    store_kblock1<WP>((char*)wo + (size_t)((tm * 16 + frag_row(r)) * NB + b) * kKBlockBytes, acc[r],
-                                      tn * 16 + frag_col());
+                    store_frag1<WP>(frag_rec(wo, tm * 16 + frag_row(r), b, NB), tm * 16 + frag_row(r), acc[r],
+                                    tn * 16 + frag_col());
             } else {
                 float* out = uo + (b - NB) * 32;
 #pragma unroll
@@ -454,7 +451,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     }
     if constexpr (DK == 64) {
         __syncthreads();
-        char* wk = (char*)wo;  // [t][DK/32] k-blocks
+        char* wk = (char*)wo;  // rows t, DK/32 k-blocks
 #pragma unroll
         for (int i = 0; i < (kChunk * DK / 8 + kThreads - 1) / kThreads; ++i) {
             const int q8 = threadIdx.x + kThreads * i;
@@ -463,7 +460,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 float x[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) x[m] = Tm[t * kLD + k0 + m];
-                store_kblock8<WP>(wk + (size_t)(t * (DK / 32) + (k0 >> 5)) * kKBlockBytes, x, (k0 >> 3) & 3);
+                store_frag8<WP>(frag_rec(wk, t, k0 >> 5, DK / 32), t, x, (k0 >> 3) & 3);
             }
         }
     }
@@ -477,7 +474,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         // and for the reverse pass D = P^T D' + qh^T dO.  w^T and u^T are staged in
         // LDS from this wave's pass-2 tiles and Kh^T from the pass-1 registers; the
         // Aqk fragments were taken from LDS before the solve.  A D fragment holds four
-        // consecutive rows of one column, so each k-block array is written from the
+        // consecutive rows of one column, so each fragment-form array is written from the
         // product of its transpose: P from P^T's tiles and P^T from P's, qh from
         // qh^T's and qh^T from qh's.  hh and ol are kept in fragment order
         // ([32-column block][16x16 tile][lane][4]) for the state pass to add to its
@@ -543,8 +540,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                     x[i] = (ra == cb ? glS[ra] : 0.f) - acc[i];
                 }
                 float* dst = wave == 0 ? p.pmT : p.pm;
-                store_kblock4<P>((char*)(dst + slot * DK * DK) + (size_t)(16 * tb + lr) * kKBlockBytes, x,
-                                 16 * ta + 4 * lg);
+                store_frag4<P>(frag_rec(dst + slot * DK * DK, 16 * tb + lr, 0, 1), 16 * tb + lr, x, 16 * ta + 4 * lg);
             }
         } else {
             // hh rows 16 ta .., all four column tiles
@@ -581,10 +577,9 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 x1[i] = scale * (Qgs[(16 * tt + a) * kLB + 16 * tc + lr] - a1[i]);
                 x2[i] = scale * (Qgs[(16 * tt + lr) * kLB + 16 * tc + a] - a2[i]);
             }
-            store_kblock4<P>((char*)(p.qhT + slot * kChunk * DK) + (size_t)((16 * tc + lr) * 2 + (tt >> 1)) * kKBlockBytes,
-                             x1, (16 * tt + 4 * lg) & 31);
-            store_kblock4<P>((char*)(p.qh + slot * kChunk * DK) + (size_t)(16 * tt + lr) * kKBlockBytes, x2,
-                             16 * tc + 4 * lg);
+            store_frag4<P>(frag_rec(p.qhT + slot * kChunk * DK, 16 * tc + lr, tt >> 1, 2), 16 * tc + lr, x1,
+                           (16 * tt + 4 * lg) & 31);
+            store_frag4<P>(frag_rec(p.qh + slot * kChunk * DK, 16 * tt + lr, 0, 1), 16 * tt + lr, x2, 16 * tc + 4 * lg);
         }
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {

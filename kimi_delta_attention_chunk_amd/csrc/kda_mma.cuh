@@ -112,33 +112,39 @@ __device__ __forceinline__ f32x4 mma_tile(const Tile<Prec::BF3>& A, const Tile<P
 
 // ----------------------------------------------------------------- A fragments from memory
 // Operands produced by one kernel and consumed by another are stored in
-// "k-block" form: per row, per block of 32 contraction indices, 128 bytes --
-//   Prec::BF3  the 32 hi parts (bf16) then the 32 lo parts,
-//   Prec::F32  the 32 fp32 values.
-// (For F32 that is plain row-major fp32.)  Lane l of a wave loads the A
-// fragment of row l & 15 straight into registers: 8 consecutive indices
-// 8 g .. 8 g + 7, g = l >> 4, as two 16-byte loads.  mma_frag then contracts
-// them with a B tile in LDS over the same 8 indices per lane: for F32 the 16x16x4
-// instruction at step kk takes index 8 g + kk from lane group g (A and B agree,
-// so the sum is over every index exactly once).
+// "fragment" form: per 16-row tile and block of 32 contraction indices, one
+// 2 KB record in the lane order of the MFMA operand -- lane l = 16 g + (r & 15)
+// holds indices 8 g .. 8 g + 7 of row r -- first 64 x 16 bytes (BF3: the 8 hi
+// parts; F32: values 0 .. 3), then 64 x 16 bytes (BF3: the 8 lo parts; F32:
+// values 4 .. 7).  A wave loads a fragment straight into registers with two
+// fully contiguous 1 KB reads (whole cache lines, in order).  mma_frag then
+// contracts it with a B tile in LDS over the same 8 indices per lane: for F32
+// the 16x16x4 instruction at step kk takes index 8 g + kk from lane group g
+// (A and B agree, so the sum is over every index exactly once).
 template <Prec P> struct AFrag;
 template <> struct AFrag<Prec::BF3> { bf16x8 hi, lo; };
 template <> struct AFrag<Prec::F32> { f32x4 a, b; };
 
-// bytes of one (row, k-block) record, and its element type in memory
-constexpr int kKBlockBytes = 128;
-
-__device__ __forceinline__ void load_afrag(AFrag<Prec::BF3>& f, const void* rowblock) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const char* b = (const char*)rowblock;
-    f.hi = *(const bf16x8*)(b + 16 * g);
-    f.lo = *(const bf16x8*)(b + 64 + 16 * g);
+constexpr int kFragRecBytes = 2048;
+// The record of (the 16-row tile of) row `row` and k-block kb of an array of
+// KB k-blocks per row.
+__device__ __forceinline__ char* frag_rec(void* base, int row, int kb, int KB) {
+    return (char*)base + ((size_t)(row >> 4) * KB + kb) * kFragRecBytes;
 }
-__device__ __forceinline__ void load_afrag(AFrag<Prec::F32>& f, const void* rowblock) {
-    const int g = (threadIdx.x & 63) >> 4;
-    const char* b = (const char*)rowblock;
-    f.a = *(const f32x4*)(b + 32 * g);
-    f.b = *(const f32x4*)(b + 32 * g + 16);
+__device__ __forceinline__ const char* frag_rec(const void* base, int row, int kb, int KB) {
+    return (const char*)base + ((size_t)(row >> 4) * KB + kb) * kFragRecBytes;
+}
+
+// This lane's share of a fragment (rows of the record's tile, lane & 15 the row).
+__device__ __forceinline__ void load_afrag(AFrag<Prec::BF3>& f, const char* rec) {
+    const int lane = threadIdx.x & 63;
+    f.hi = *(const bf16x8*)(rec + 16 * lane);
+    f.lo = *(const bf16x8*)(rec + 1024 + 16 * lane);
+}
+__device__ __forceinline__ void load_afrag(AFrag<Prec::F32>& f, const char* rec) {
+    const int lane = threadIdx.x & 63;
+    f.a = *(const f32x4*)(rec + 16 * lane);
+    f.b = *(const f32x4*)(rec + 1024 + 16 * lane);
 }
 
 // acc += A(16 x [kb, kb+32)) * B(16 x [kb, kb+32))^T, A from registers, B a tile
@@ -165,7 +171,7 @@ __device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const Tile<
 }
 
 // A fragment from this lane's 8 values (indices 8 g .. 8 g + 7 of the k-block,
-// g = lane >> 4), split as a store to and load from k-block form would.
+// g = lane >> 4), split as a store to and load from fragment form would.
 __device__ __forceinline__ void make_frag(AFrag<Prec::BF3>& f, const float (&x)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -179,73 +185,26 @@ __device__ __forceinline__ void make_frag(AFrag<Prec::F32>& f, const float (&x)[
 }
 
 // Write 8 consecutive values (indices 8 w .. 8 w + 7 of a k-block, w = which)
-// of one row in k-block form.
+// of row `row` into its fragment record `rec`.
 template <Prec P>
-__device__ __forceinline__ void store_kblock8(void* rowblock, const float (&x)[8], int which);
+__device__ __forceinline__ void store_frag8(char* rec, int row, const float (&x)[8], int which);
 template <>
-__device__ __forceinline__ void store_kblock8<Prec::BF3>(void* rowblock, const float (&x)[8], int which) {
+__device__ __forceinline__ void store_frag8<Prec::BF3>(char* rec, int row, const float (&x)[8], int which) {
     bf16x8 h, l;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         h[i] = (__bf16)x[i];
         l[i] = (__bf16)(x[i] - (float)h[i]);
     }
-    char* b = (char*)rowblock;
-    *(bf16x8*)(b + 16 * which) = h;
-    *(bf16x8*)(b + 64 + 16 * which) = l;
+    char* b = rec + 16 * (16 * which + (row & 15));
+    *(bf16x8*)b = h;
+    *(bf16x8*)(b + 1024) = l;
 }
 template <>
-__device__ __forceinline__ void store_kblock8<Prec::F32>(void* rowblock, const float (&x)[8], int which) {
-    float* b = (float*)rowblock + 8 * which;
+__device__ __forceinline__ void store_frag8<Prec::F32>(char* rec, int row, const float (&x)[8], int which) {
+    char* b = rec + 16 * (16 * which + (row & 15));
     *(f32x4*)b = f32x4{x[0], x[1], x[2], x[3]};
-    *(f32x4*)(b + 4) = f32x4{x[4], x[5], x[6], x[7]};
-}
-// Read 8 consecutive values of one row in k-block form back into fp32 (hi + lo).
-template <Prec P>
-__device__ __forceinline__ void load_kblock8(const void* rowblock, float (&x)[8], int which);
-template <>
-__device__ __forceinline__ void load_kblock8<Prec::BF3>(const void* rowblock, float (&x)[8], int which) {
-    const char* b = (const char*)rowblock;
-    const bf16x8 h = *(const bf16x8*)(b + 16 * which), l = *(const bf16x8*)(b + 64 + 16 * which);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)h[i] + (float)l[i];
-}
-template <>
-__device__ __forceinline__ void load_kblock8<Prec::F32>(const void* rowblock, float (&x)[8], int which) {
-    const float* b = (const float*)rowblock + 8 * which;
-    const f32x4 u = *(const f32x4*)b, v = *(const f32x4*)(b + 4);
-    x[0] = u[0]; x[1] = u[1]; x[2] = u[2]; x[3] = u[3]; x[4] = v[0]; x[5] = v[1]; x[6] = v[2]; x[7] = v[3];
-}
-
-// Eight consecutive values (indices 8 w .. 8 w + 7 of one k-block) of a row in
-// k-block form, as loaded, and their transposed store into an LDS tile:
-// T(k0 + i, row) for i = 0..7 (no conversion: BF3 moves the stored hi/lo).
-template <Prec P> struct KChunk;
-template <> struct KChunk<Prec::BF3> { bf16x8 h, l; };
-template <> struct KChunk<Prec::F32> { f32x4 a, b; };
-__device__ __forceinline__ void load_kchunk(KChunk<Prec::BF3>& c, const void* rowblock, int which) {
-    const char* b = (const char*)rowblock;
-    c.h = *(const bf16x8*)(b + 16 * which);
-    c.l = *(const bf16x8*)(b + 64 + 16 * which);
-}
-__device__ __forceinline__ void load_kchunk(KChunk<Prec::F32>& c, const void* rowblock, int which) {
-    const float* b = (const float*)rowblock + 8 * which;
-    c.a = *(const f32x4*)b;
-    c.b = *(const f32x4*)(b + 4);
-}
-__device__ __forceinline__ void put_kchunk_t(const Tile<Prec::BF3>& T, int k0, int row, const KChunk<Prec::BF3>& c) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        T.hi[(k0 + i) * T.ld + row] = c.h[i];
-        T.lo[(k0 + i) * T.ld + row] = c.l[i];
-    }
-}
-__device__ __forceinline__ void put_kchunk_t(const Tile<Prec::F32>& T, int k0, int row, const KChunk<Prec::F32>& c) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        T.p[(k0 + i) * T.ld + row] = c.a[i];
-        T.p[(k0 + 4 + i) * T.ld + row] = c.b[i];
-    }
+    *(f32x4*)(b + 1024) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
 // ----------------------------------------------------------------- fragments in registers
@@ -280,29 +239,29 @@ __device__ __forceinline__ f32x4 mma_ff(const AFrag<Prec::F32>& a, const AFrag<P
     return acc;
 }
 
-// Write one value (index k of a k-block) of one row in k-block form.
+// Write one value (index k of a k-block) of row `row` into its fragment record.
 template <Prec P>
-__device__ __forceinline__ void store_kblock1(void* rowblock, float x, int k);
+__device__ __forceinline__ void store_frag1(char* rec, int row, float x, int k);
 template <>
-__device__ __forceinline__ void store_kblock1<Prec::BF3>(void* rowblock, float x, int k) {
+__device__ __forceinline__ void store_frag1<Prec::BF3>(char* rec, int row, float x, int k) {
     const __bf16 h = (__bf16)x;
-    __bf16* b = (__bf16*)rowblock;
-    b[k] = h;
-    b[32 + k] = (__bf16)(x - (float)h);
+    __bf16* b = (__bf16*)(rec + 16 * (16 * (k >> 3) + (row & 15))) + (k & 7);
+    b[0] = h;
+    b[512] = (__bf16)(x - (float)h);  // 1024 bytes on: the lo part
 }
 template <>
-__device__ __forceinline__ void store_kblock1<Prec::F32>(void* rowblock, float x, int k) {
-    ((float*)rowblock)[k] = x;
+__device__ __forceinline__ void store_frag1<Prec::F32>(char* rec, int row, float x, int k) {
+    *(float*)(rec + 16 * (16 * (k >> 3) + (row & 15)) + ((k & 4) ? 1024 : 0) + 4 * (k & 3)) = x;
 }
 
 // Write 4 consecutive values (indices k0 .. k0 + 3 of a k-block, k0 a multiple
-// of 4) of one row in k-block form.  A D fragment holds, per lane, four
-// consecutive rows of one column, i.e. four consecutive k-block indices of a
-// row of the transposed result.
+// of 4) of row `row` into its fragment record.  A D fragment holds, per lane,
+// four consecutive rows of one column, i.e. four consecutive k-block indices of
+// a row of the transposed result.
 template <Prec P>
-__device__ __forceinline__ void store_kblock4(void* rowblock, const f32x4& x, int k0);
+__device__ __forceinline__ void store_frag4(char* rec, int row, const f32x4& x, int k0);
 template <>
-__device__ __forceinline__ void store_kblock4<Prec::BF3>(void* rowblock, const f32x4& x, int k0) {
+__device__ __forceinline__ void store_frag4<Prec::BF3>(char* rec, int row, const f32x4& x, int k0) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 h, l;
 #pragma unroll
@@ -310,13 +269,13 @@ __device__ __forceinline__ void store_kblock4<Prec::BF3>(void* rowblock, const f
         h[i] = (__bf16)x[i];
         l[i] = (__bf16)(x[i] - (float)h[i]);
     }
-    char* b = (char*)rowblock;
-    *(bf16x4*)(b + 2 * k0) = h;
-    *(bf16x4*)(b + 64 + 2 * k0) = l;
+    char* b = rec + 16 * (16 * (k0 >> 3) + (row & 15)) + 2 * (k0 & 4);
+    *(bf16x4*)b = h;
+    *(bf16x4*)(b + 1024) = l;
 }
 template <>
-__device__ __forceinline__ void store_kblock4<Prec::F32>(void* rowblock, const f32x4& x, int k0) {
-    *(f32x4*)((float*)rowblock + k0) = x;
+__device__ __forceinline__ void store_frag4<Prec::F32>(char* rec, int row, const f32x4& x, int k0) {
+    *(f32x4*)(rec + 16 * (16 * (k0 >> 3) + (row & 15)) + ((k0 & 4) ? 1024 : 0)) = x;
 }
 
 // ----------------------------------------------------------------- swizzled tiles

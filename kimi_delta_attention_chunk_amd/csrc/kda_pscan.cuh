@@ -45,8 +45,8 @@ struct PsFwdOps {
 template <Prec P, int NJ>
 __device__ __forceinline__ void ps_fwd_load(const Prm& p, size_t slot, int jb, int tc, int tj, PsFwdOps<P, NJ>& R) {
     const int wave = wave_id(), lr = threadIdx.x & 15;
-    load_afrag(R.pm, (const char*)(p.pm + slot * kPsDK * kPsDK) + (size_t)(16 * tc + lr) * kKBlockBytes);
-    load_afrag(R.qh, (const char*)(p.qh + slot * kChunk * kPsDK) + (size_t)(16 * wave + lr) * kKBlockBytes);
+    load_afrag(R.pm, frag_rec(p.pm + slot * kPsDK * kPsDK, 16 * tc + lr, 0, 1));
+    load_afrag(R.qh, frag_rec(p.qh + slot * kChunk * kPsDK, 16 * wave + lr, 0, 1));
     R.hh = *(const f32x4*)(p.hh + slot * kPsDK * kPsDV + frag_order(jb + 16 * tj, 4, tc));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) R.ol[j] = *(const f32x4*)(p.ol + slot * kChunk * kPsDV + frag_order(jb + 16 * j, 8, wave));
@@ -179,10 +179,10 @@ template <typename TIn, Prec P, int BV>
 __device__ __forceinline__ void ps_bwd_load(const Prm& p, size_t slot, const ChunkRef& cr, int h, int jb, int tc,
                                             PsBwdOps<TIn, P, BV>& R) {
     const int lr = threadIdx.x & 15;
-    load_afrag(R.pt, (const char*)(p.pmT + slot * kPsDK * kPsDK) + (size_t)(16 * tc + lr) * kKBlockBytes);
+    load_afrag(R.pt, frag_rec(p.pmT + slot * kPsDK * kPsDK, 16 * tc + lr, 0, 1));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        load_afrag(R.qt[kb], (const char*)(p.qhT + slot * kChunk * kPsDK) + (size_t)((16 * tc + lr) * 2 + kb) * kKBlockBytes);
+        load_afrag(R.qt[kb], frag_rec(p.qhT + slot * kChunk * kPsDK, 16 * tc + lr, kb, 2));
     // rows past the chunk end read row 0 (always valid); they are zeroed where used
     const int t = threadIdx.x >> 2, part = threadIdx.x & 3;
     const TIn* src = (const TIn*)p.d_o + tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, kPsDV) + jb + (BV / 4) * part;

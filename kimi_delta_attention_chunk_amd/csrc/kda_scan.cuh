@@ -6,7 +6,7 @@
 //   o     = scale (exp(G) q h + Aqk v_new)  (64 x BV, written if requested)
 //   h    <- Diag(exp G_L) h + (k exp(G_L - G))^T v_new
 // All operands of a chunk come precomputed from the intra-chunk kernel in
-// k-block form (kda_mma.cuh), so each lane loads its MFMA A fragments straight
+// fragment form (kda_mma.cuh), so each lane loads its MFMA A fragments straight
 // into registers, two chunks ahead (double buffered), and the loop body is
 // three products with two barriers.  Only the operands that depend on the
 // state pass through LDS: the fp32 state stays in the registers of the lanes
@@ -28,7 +28,7 @@ namespace kda {
 
 constexpr int kScanThreads = 512, kScanWaves = 8;  // two waves per SIMD
 
-// One chunk's operands for this lane, loaded straight from the k-block
+// One chunk's operands for this lane, loaded straight from the fragment-form
 // workspace arrays into MFMA A fragments.
 template <int DK, int BV, Prec P>
 struct ScanFrags {
@@ -56,7 +56,7 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     using F = ScanFrags<DK, BV, P>;
     const int wave = wave_id(), lr = threadIdx.x & 15;
     const int vt = F::vtile(wave), tm = vt / F::TN, tn = vt % F::TN;
-    const char* w = (const char*)(p.w + slot * kChunk * DK);       // [t][DK/32] k-blocks
+    const char* w = (const char*)(p.w + slot * kChunk * DK);       // rows t, DK/32 k-blocks
     const char* q = (const char*)(p.qg + slot * kChunk * DK);      // [t][DK/32]
     const char* a = (const char*)(p.aqk + slot * kChunk * kChunk); // [t][2]
     const char* k = (const char*)(p.khT + slot * DK * kChunk);     // [c][2]
@@ -64,21 +64,21 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     const int row = 16 * tm + lr;
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb) {
-        load_afrag(R.x[kb], xs + (size_t)(row * F::KB + kb) * kKBlockBytes);
-        if constexpr (!F::SPLIT) load_afrag(R.q[kb], q + (size_t)(row * F::KB + kb) * kKBlockBytes);
+        load_afrag(R.x[kb], frag_rec(xs, row, kb, F::KB));
+        if constexpr (!F::SPLIT) load_afrag(R.q[kb], frag_rec(q, row, kb, F::KB));
     }
     // Every load below is unconditional (a wave without a state tile reads
     // tile 0's operands, unused; Aqk's second block is read even where it is
     // zero), so the batch has the same size on every wave and path.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) if (kb <= (tm >> 1)) load_afrag(R.a[kb], a + (size_t)(row * 2 + kb) * kKBlockBytes);
+    for (int kb = 0; kb < 2; ++kb) if (kb <= (tm >> 1)) load_afrag(R.a[kb], frag_rec(a, row, kb, 2));
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
         if (tile < F::TH) {
         const int crow = 16 * (tile / F::TN) + lr;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) load_afrag(R.k[i][kb], k + (size_t)(crow * 2 + kb) * kKBlockBytes);
+        for (int kb = 0; kb < 2; ++kb) load_afrag(R.k[i][kb], frag_rec(k, crow, kb, 2));
         }
     }
     const float* u = p.u + slot * kChunk * DV + jb;
