@@ -70,8 +70,9 @@ __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRe
             load_afrag(R.qt[i][kb], frag_rec(qt, c16 + lr, kb, 2));
             load_afrag(R.wt[i][kb], frag_rec(wt, c16 + lr, kb, 2));
         }
+        const f32x4 g4 = *(const f32x4*)&p.gl[slot * DK + c16 + frag_row(0)];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R.g[4 * i + r] = p.gl[slot * DK + c16 + frag_row(r)];
+        for (int r = 0; r < 4; ++r) R.g[4 * i + r] = g4[r];
     }
     {
         // dO rows t = tid >> 3, columns jb + ND part ..; rows past the end read row 0 and are zeroed
@@ -128,13 +129,14 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
     auto clamp = [&](int cc) { return cc >= c0 ? cc : c0; };
     auto ref = [&](int cc) { return SeqLayout::chunk_of(n, clamp(cc) - c0, s0, slen); };
     auto slot_of = [&](int cc) { return (size_t)clamp(cc) * p.H + h; };
-    F R[2];
-
-    // Chunk c, the i-th from the end: dO^T of c is in dOb, D^T (at its end) in Db;
-    // stages dO^T of c - 1 (in Rc.d) into dOn and D^T at the chunk start into Dn.
-    auto step = [&](int c, int i, F& Rc) {
+    // Chunk c, the i-th from the end (i = c1 - 1 - c): dO^T of c is in dOb, D^T (at
+    // its end) in Db; stages dO^T of c - 1 (in Rc.d) into dOn and D^T at the chunk
+    // start into Dn.  Every global store is issued on every wave and path (stores
+    // a wave does not make go to p.sink), so the waits on the memory counter count
+    // exactly the operand batches in flight.
+    auto step = [&](int c, const F& Rc) {
         const size_t slot = (size_t)c * p.H + h;
-        const bool odd = i & 1;
+        const bool odd = (c1 - 1 - c) & 1;
         const Tile<P> dOb = odd ? dOT1 : dOT0, dOn = odd ? dOT0 : dOT1;
         const Tile<P> Db = odd ? DT1 : DT0, Dn = odd ? DT0 : DT1;
         __syncthreads();  // dO^T and D^T of this chunk staged; the previous chunk is done with dv_new^T
@@ -143,14 +145,14 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
 #pragma unroll
             for (int k = 0; k < HPW; ++k) {
                 const int tile = wave + kDhWaves * k;
-                if (tile < TH) {
-                    const int tm = tile / TN, tn = tile % TN;
+                const bool has = tile < TH;
+                const int tm = (has ? tile : 0) / TN, tn = (has ? tile : 0) % TN;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        dhs[(size_t)(tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col()] = D[k][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    *(has ? dhs + (size_t)(tm * 16 + frag_row(r)) * DV + jb + tn * 16 + frag_col() : p.sink) = D[k][r];
             }
         }
+        f32x4 val = {0.f, 0.f, 0.f, 0.f};
         if (wave < VT) {
             // dv_new = scale Aqk^T dO + Kh D (Aqk^T rows 16 tm .. are zero before index 16 tm)
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -158,14 +160,15 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
             a1 = mma_frag(Rc.aq[1], dOb.sub(tnv * 16), 32, a1);
 #pragma unroll
             for (int kb = 0; kb < F::KB; ++kb) a2 = mma_frag(Rc.kh[kb], Db.sub(tnv * 16), 32 * kb, a2);
-            f32x4 val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) val[r] = scale * a1[r] + a2[r];
-            const int j = tnv * 16 + frag_col();
-            dvnT.put4(j, tmv * 16 + frag_row(0), val);
+            dvnT.put4(tnv * 16 + frag_col(), tmv * 16 + frag_row(0), val);
+        }
+        {
             float* dvo = p.dvn + slot * kChunk * DV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dvo[(size_t)(tmv * 16 + frag_row(r)) * DV + jb + j] = val[r];
+            for (int r = 0; r < 4; ++r)
+                *(wave < VT ? dvo + (size_t)(tmv * 16 + frag_row(r)) * DV + jb + tnv * 16 + frag_col() : p.sink) = val[r];
         }
         {
             // dO^T of the chunk processed next
@@ -205,18 +208,22 @@ __global__ void __launch_bounds__(kDhThreads) bwd_dh_scan_kernel(Prm p, int tota
                 dOT0.put(F::ND * part + k, t, t < cr.len ? x : 0.f);
             }
         }
-        // the operand batch of chunk c carries dO of chunk c - 1
-        dh_load<DK, DV, BV, TIn, P>(p, slot_of(c1 - 1), ref(c1 - 2), h, jb, R[0]);
-        dh_load<DK, DV, BV, TIn, P>(p, slot_of(c1 - 2), ref(c1 - 3), h, jb, R[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        for (int c = c1 - 1, i = 0; c >= c0; c -= 2, i += 2) {
-            step(c, i, R[0]);
-            dh_load<DK, DV, BV, TIn, P>(p, slot_of(c - 2), ref(c - 3), h, jb, R[0]);
-            if (c - 1 >= c0) {
-                step(c - 1, i + 1, R[1]);
-                dh_load<DK, DV, BV, TIn, P>(p, slot_of(c - 3), ref(c - 4), h, jb, R[1]);
+        // the operand batch of chunk c carries dO of chunk c - 1; PD batches in flight
+        constexpr int PD = 2;
+        F R[PD];
+#pragma unroll
+        for (int k = 0; k < PD; ++k) dh_load<DK, DV, BV, TIn, P>(p, slot_of(c1 - 1 - k), ref(c1 - 2 - k), h, jb, R[k]);
+        int c = c1 - 1;
+        for (; c - (PD - 1) >= c0; c -= PD) {
+#pragma unroll
+            for (int k = 0; k < PD; ++k) {
+                step(c - k, R[k]);
+                dh_load<DK, DV, BV, TIn, P>(p, slot_of(c - k - PD), ref(c - k - PD - 1), h, jb, R[k]);
             }
         }
+#pragma unroll
+        for (int k = 0; k < PD - 1; ++k)
+            if (c - k >= c0) step(c - k, R[k]);
     }
     if (p.dh0) {
 #pragma unroll
