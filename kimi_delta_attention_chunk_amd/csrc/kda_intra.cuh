@@ -31,14 +31,16 @@ namespace kda {
 constexpr int kCB32 = 32;        // channels per block
 constexpr int kLB = kCB32 + 4;   // row stride of [token][channel-block] tiles
 
-// The p-th pair (t, s), s < t, of the four 16x16 diagonal blocks (120 each).
+// The p-th pair (t, s), s < t, of the four 16x16 diagonal blocks (120 each),
+// enumerated in integer arithmetic: within a block, rows a = g + 1 and 15 - g
+// (g = 0..6) have 16 partners together, so group g = q >> 4 takes row a's
+// partners and then row 15 - g's; group 7 is row 8's eight partners.
 __device__ __forceinline__ void diag_pair(int p, int& t, int& s) {
     const int I = p / 120, q = p - 120 * I;
-    int tl = (int)((sqrtf(8.f * q + 1.f) + 1.f) * 0.5f);  // tl (tl - 1) / 2 <= q < tl (tl + 1) / 2
-    if (tl * (tl - 1) / 2 > q) --tl;
-    if ((tl + 1) * tl / 2 <= q) ++tl;
-    t = 16 * I + tl;
-    s = 16 * I + q - tl * (tl - 1) / 2;
+    const int g = q >> 4, u = q & 15, a = g + 1;
+    const bool first = u < a;  // (always in group 7: a = 8, u < 8)
+    t = 16 * I + (first ? a : 15 - g);
+    s = 16 * I + (first ? u : u - a);
 }
 constexpr int kDiagPairs = 4 * 120;
 
