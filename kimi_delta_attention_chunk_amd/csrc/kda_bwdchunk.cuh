@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     const bool in = tr < cr.len;
     const float scale = p.scale;
 
-    // ------------------------------------------------ every global load, up front
+    // ------------------------------------------------ the inputs' global loads, up front
     // (the gate parameters first, so that no later load waits behind the rest)
     float braw = 0.f, alog = 0.f, dtb[4] = {0.f, 0.f, 0.f, 0.f};
     if (gate) {
@@ -111,19 +111,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     }
     f32x4 Tr[NT4], Hr[NH4], Dr[NH4];
     AFrag<P> fa[2];  // Aqk^T rows 16 (w >> 1) .., k-blocks (w >> 2) .. 1 (P0)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
-        if (kb >= (wave >> 2))
-            load_afrag(fa[kb], frag_rec(p.aqT + slot * kChunk * kChunk, 16 * (wave >> 1) + (lane & 15), kb, 2));
-    {
-        const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
-        const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
-        const f32x4* d4 = (const f32x4*)(p.dhs + slot * DK * DV);
-#pragma unroll
-        for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + NTH * i];
-#pragma unroll
-        for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
-    }
     if (tid < kChunk && tid >= cr.len) braw = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -169,6 +156,22 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         Gs[tr * LR + cc] = graw[i] * kLog2e;  // base-2 log-decay (cumulated in place below)
     }
     __syncthreads();
+    // The chunk's intermediates (Aqk^T, T, h, D'), issued once the preparation's
+    // inputs have arrived: issued with them, they shared the bandwidth of the
+    // start of every round (every CU loads at once) and delayed the preparation.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
+        if (kb >= (wave >> 2))
+            load_afrag(fa[kb], frag_rec(p.aqT + slot * kChunk * kChunk, 16 * (wave >> 1) + (lane & 15), kb, 2));
+    {
+        const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
+        const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
+        const f32x4* d4 = (const f32x4*)(p.dhs + slot * DK * DV);
+#pragma unroll
+        for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + NTH * i];
+#pragma unroll
+        for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
+    }
     {
         // in-chunk cumulative log-decay G, in place in Gs
         float x[4];
