@@ -102,12 +102,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         load4<TIn>(kin + base, kx);
         load4<TIn>(qin + base, qx);
         load4<float>(p.g + base, graw);
-#pragma unroll
-        for (int b = 0; b < NVB; ++b) {
-            const size_t vb = tok_index(cr.t0 + trc, h, p.H, DV) + 32 * b + 4 * part;
-            load4<TIn>(vin + vb, vx[b]);
-            load4<TIn>(doin + vb, dox[b]);
-        }
     }
     f32x4 Tr[NT4], Hr[NH4], Dr[NH4];
     AFrag<P> fa[2];  // Aqk^T rows 16 (w >> 1) .., k-blocks (w >> 2) .. 1 (P0)
@@ -117,11 +111,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         kx[i] = in ? kx[i] : 0.f;
         qx[i] = in ? qx[i] : 0.f;
         graw[i] = in ? graw[i] : 0.f;
-#pragma unroll
-        for (int b = 0; b < NVB; ++b) {
-            vx[b][i] = in ? vx[b][i] : 0.f;
-            dox[b][i] = in ? dox[b][i] : 0.f;
-        }
     }
 
     // ------------------------------------------------ preparation (registers), resident tiles
@@ -156,9 +145,16 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         Gs[tr * LR + cc] = graw[i] * kLog2e;  // base-2 log-decay (cumulated in place below)
     }
     __syncthreads();
-    // The chunk's intermediates (Aqk^T, T, h, D'), issued once the preparation's
-    // inputs have arrived: issued with them, they shared the bandwidth of the
-    // start of every round (every CU loads at once) and delayed the preparation.
+    // v, dO and the chunk's intermediates (Aqk^T, T, h, D'), issued once the
+    // preparation's inputs have arrived: issued with them, they shared the
+    // bandwidth of the start of every round (every CU loads at once) and
+    // delayed the preparation.
+#pragma unroll
+    for (int b = 0; b < NVB; ++b) {  // v and dO (rows past the end: zeroed in P0)
+        const size_t vb = tok_index(cr.t0 + trc, h, p.H, DV) + 32 * b + 4 * part;
+        load4<TIn>(vin + vb, vx[b]);
+        load4<TIn>(doin + vb, dox[b]);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)  // Aqk^T row block tm reaches t >= 16 tm: k-blocks tm >> 1 .. 1
         if (kb >= (wave >> 2))
@@ -247,6 +243,11 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             KHt.put4(tr, 4 * part, xh);
 #pragma unroll
             for (int vb = 0; vb < NVB; ++vb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vx[vb][i] = in ? vx[vb][i] : 0.f;
+                    dox[vb][i] = in ? dox[vb][i] : 0.f;
+                }
                 *(f32x4*)&VS[tr * 68 + 32 * vb + 4 * part] = f32x4{vx[vb][0], vx[vb][1], vx[vb][2], vx[vb][3]};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) DOT.put_hi(32 * vb + 4 * part + m, tr, dox[vb][m]);  // dO: bf16 numbers

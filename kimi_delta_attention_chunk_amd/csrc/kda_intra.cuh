@@ -124,8 +124,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         load8<TIn>(qin + base, qx[b]);
         load8<float>(p.g + base, G[b]);
     }
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) load8<TIn>(vin + tok_index(cr.t0 + trc, h, p.H, DV) + 32 * vb + 8 * part, vx[vb]);
     if (threadIdx.x < kChunk && threadIdx.x >= cr.len) braw = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -135,8 +133,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             qx[b][i] = in ? qx[b][i] : 0.f;
             G[b][i] = in ? G[b][i] : 0.f;
         }
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) vx[vb][i] = in ? vx[vb][i] : 0.f;
     }
     // ---- preparation in registers: beta, L2 norms, gate, in-chunk cumulative decay
     if (threadIdx.x < kChunk) bet[threadIdx.x] = (p.flags & 4u) ? (threadIdx.x < cr.len ? sigmoid_f(braw) : 0.f) : braw;
@@ -161,6 +157,11 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
 #pragma unroll
             for (int i = 0; i < 8; ++i) G[b][i] = -eA * softplus_f(G[b][i] + dtb[b][i]);
     }
+
+    // v, first needed in pass 2: issued once the preparation's inputs have arrived
+    // (rows past the chunk end are zeroed where v is used)
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) load8<TIn>(vin + tok_index(cr.t0 + trc, h, p.H, DV) + 32 * vb + 8 * part, vx[vb]);
 
     // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,
     // and this thread's 4 diagonal-block entries of each.
@@ -411,7 +412,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     BTg.put(8 * part + i, tr, b < NB ? bt * exp2_hw(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
-                                                     : bt * vx[b < NB ? 0 : b - NB][i]);
+                                                     : bt * (in ? vx[b < NB ? 0 : b - NB][i] : 0.f));
             }
         }
         __syncthreads();
