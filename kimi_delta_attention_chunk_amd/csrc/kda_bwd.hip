@@ -105,12 +105,12 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
 
     {
         // T^T: row t of the tile holds T[s][t] over s (T is unit lower triangular)
-        const float* tmi = p.tm + slot * kChunk * kChunk;
+        const float* tmi = p.tm + slot * kTPacked;
 #pragma unroll
         for (int i = 0; i < kChunk * kChunk / 4 / kGThreads; ++i) {
             const int e4 = tid + i * kGThreads;
             const int s_ = e4 / (kChunk / 4), t4 = 4 * (e4 % (kChunk / 4));
-            const f32x4 x = *(const f32x4*)(tmi + s_ * kChunk + t4);
+            const f32x4 x = tpk_load4(tmi, s_, t4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) TT.put(t4 + r, s_, x[r]);
         }
@@ -362,14 +362,18 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
 
     // ---- load the chunk matrices and row scalars
     {
-        const float* tmi = p.tm + slot * kChunk * kChunk;
+        const float* tmi = p.tm + slot * kTPacked;
         const float* dti = p.dtv + slot * kChunk * kChunk;
         const float* dai = p.daq + slot * kChunk * kChunk;
         #pragma unroll
     for (int e_i = 0; e_i < (kChunk * kChunk) / kGThreads; ++e_i) {
         const int e = threadIdx.x + e_i * kGThreads;
             const int idx = (e >> 6) * kLD + (e & 63);
-            Tm[idx] = tmi[e];
+            {
+                const int t = e >> 6, s = e & 63;  // T packed: zero above the block diagonal
+                const float x = tmi[tpk_index(t, (s >> 4) > (t >> 4) ? t : s)];
+                Tm[idx] = (s >> 4) > (t >> 4) ? 0.f : x;
+            }
             dT[idx] = dti[e];
             dAq[idx] = dai[e];
         }

@@ -160,11 +160,14 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         if (kb >= (wave >> 2))
             load_afrag(fa[kb], frag_rec(p.aqT + slot * kChunk * kChunk, 16 * (wave >> 1) + (lane & 15), kb, 2));
     {
-        const f32x4* t4 = (const f32x4*)(p.tm + slot * kChunk * kChunk);
+        const float* tpk = p.tm + slot * kTPacked;
         const f32x4* h4 = (const f32x4*)(p.hs + slot * DK * DV);
         const f32x4* d4 = (const f32x4*)(p.dhs + slot * DK * DV);
 #pragma unroll
-        for (int i = 0; i < NT4; ++i) Tr[i] = t4[tid + NTH * i];
+        for (int i = 0; i < NT4; ++i) {
+            const int e4 = 4 * (tid + NTH * i);
+            Tr[i] = tpk_load4(tpk, e4 >> 6, e4 & 63);
+        }
 #pragma unroll
         for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
     }

@@ -73,6 +73,21 @@ __device__ __forceinline__ size_t tok_index(int64_t t, int h, int H, int d) {
     return ((size_t)t * H + h) * d;
 }
 
+// T = (I + A)^{-1} is unit lower triangular: in the workspace only its 10 blocks
+// (I, J), J <= I, of 16x16 are kept, each row-major, in the order (0,0) (1,0)
+// (1,1) (2,0) ... (3,3): 10 KB per chunk instead of 16.
+constexpr int kTPacked = 10 * 256;  // floats per chunk
+__host__ __device__ constexpr int tpk_index(int t, int s) {
+    return ((((t >> 4) * ((t >> 4) + 1)) / 2 + (s >> 4)) << 8) + ((t & 15) << 4) + (s & 15);
+}
+// T[t][s .. s + 3] (s a multiple of 4) from the packed form: zero above the block
+// diagonal (the load is issued on every lane, from the diagonal block there).
+__device__ __forceinline__ f32x4 tpk_load4(const float* T, int t, int s) {
+    const bool upper = (s >> 4) > (t >> 4);
+    const f32x4 x = *(const f32x4*)(T + tpk_index(t, upper ? t : s));
+    return upper ? f32x4{0.f, 0.f, 0.f, 0.f} : x;
+}
+
 // T = (I + A)^{-1} for strictly lower-triangular A (64x64, stride kLD), by
 // 16x16 blocks: diagonal blocks by forward substitution, then the off-diagonal
 // blocks level by level,

@@ -74,7 +74,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec, void* ctx) {
         take(L.ol, slots * C * dv);
         if (backward) {
             take(L.aqT, slots * C * C);
-            take(L.tm, slots * C * C);
+            take(L.tm, slots * kTPacked);
             take(L.dhs, slots * dk * dv);
             take(L.part_a, slots);
             take(L.part_dt, slots * dk);
@@ -91,7 +91,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec, void* ctx) {
     take(L.khT, slots * C * dk);
     take(L.gl, slots * dk);
     if (backward) {
-        take(L.tm, slots * C * C);
+        take(L.tm, slots * kTPacked);
         take(L.aqT, slots * C * C);
         take(L.qgT, slots * C * dk);
         take(L.khb, slots * C * dk);

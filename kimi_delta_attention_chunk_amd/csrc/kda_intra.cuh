@@ -378,12 +378,12 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     }
     solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
     if (p.tm) {
-        f32x4* to = (f32x4*)(p.tm + slot * kChunk * kChunk);
-#pragma unroll
-        for (int i = 0; i < kChunk * kChunk / 4 / kThreads; ++i) {
-            const int e4 = 4 * (threadIdx.x + kThreads * i);
-            const int t = e4 >> 6, s = e4 & 63;  // (blocks above the diagonal are zero, not stored in Tm)
-            to[e4 >> 2] = (s >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&Tm[t * kLD + s];
+        // the 10 blocks on and below the diagonal, packed (tpk_index)
+        f32x4* to = (f32x4*)(p.tm + slot * kTPacked);
+        for (int e = threadIdx.x; e < kTPacked / 4; e += kThreads) {
+            const int b = e >> 6, I = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3)), J = b - I * (I + 1) / 2;
+            const int t = 16 * I + ((e & 63) >> 2), s = 16 * J + 4 * (e & 3);
+            to[e] = *(const f32x4*)&Tm[t * kLD + s];
         }
     }
 
