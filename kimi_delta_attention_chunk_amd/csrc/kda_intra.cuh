@@ -359,7 +359,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 float x[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
-                store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
+                // (the block of rows t < 32, s >= 32 is zero and never read: not written)
+                if (t >= 32 || s0 < 32) store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
             }
         }
         if (p.aqT) {
@@ -372,7 +373,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 float x[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
-                store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
+                // (the block of rows s >= 32, t < 32 is zero and never read: not written)
+                if (sr < 32 || t0 >= 32) store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
             }
         }
     }
