@@ -7,7 +7,7 @@
 //   h    <- Diag(exp G_L) h + (k exp(G_L - G))^T v_new
 // All operands of a chunk come precomputed from the intra-chunk kernel in
 // fragment form (kda_mma.cuh), so each lane loads its MFMA A fragments straight
-// into registers, two chunks ahead (double buffered), and the loop body is
+// into registers, two or three chunks ahead, and the loop body is
 // three products with two barriers.  Only the operands that depend on the
 // state pass through LDS: the fp32 state stays in the registers of the lanes
 // that own its 16x16 tiles, and an MFMA copy hT[j][c] is written each chunk,
@@ -135,7 +135,10 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
     int slen;
     p.seq.seq_tokens(n, s0, slen);
     TOut* o = (TOut*)p.o;
-    F R[2];
+    // operand batches in flight: three at dk = 64; at dk = 128 the registers of two
+    // waves per SIMD hold two
+    constexpr int PD = DK <= 64 ? 3 : 2;
+    F R[PD];
     // Prefetches are unconditional (past the last chunk they reload it), so the
     // control flow around them is uniform and each wait covers one chunk only.
     auto slot_of = [&](int cc) { return (size_t)(cc < c1 ? cc : c1 - 1) * p.H + h; };
@@ -207,18 +210,18 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
         }
     };
     if (c0 < c1) {
-        // (scheduling barriers keep the two batches in issue order: the
-        // waits count completions in order)
-        scan_load<DK, DV, BV, P>(p, slot_of(c0), jb, R[0]);
-        scan_load<DK, DV, BV, P>(p, slot_of(c0 + 1), jb, R[1]);
+        // (scheduling barriers keep the batches in issue order: the waits count
+        // completions in order)
+#pragma unroll
+        for (int i = 0; i < PD; ++i) scan_load<DK, DV, BV, P>(p, slot_of(c0 + i), jb, R[i]);
         __builtin_amdgcn_sched_barrier(0);
-        for (int c = c0; c < c1; c += 2) {
-            step(c, R[0]);
-            scan_load<DK, DV, BV, P>(p, slot_of(c + 2), jb, R[0]);
-            if (c + 1 < c1) {
-                step(c + 1, R[1]);
-                scan_load<DK, DV, BV, P>(p, slot_of(c + 3), jb, R[1]);
-            }
+        for (int c = c0; c < c1; c += PD) {
+#pragma unroll
+            for (int i = 0; i < PD; ++i)
+                if (i == 0 || c + i < c1) {
+                    step(c + i, R[i]);
+                    scan_load<DK, DV, BV, P>(p, slot_of(c + i + PD), jb, R[i]);
+                }
         }
     }
     if (p.hT) {
