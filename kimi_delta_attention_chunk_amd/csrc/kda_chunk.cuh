@@ -94,11 +94,13 @@ __device__ __forceinline__ f32x4 tpk_load4(const float* T, int t, int s) {
 //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
 // Only the blocks on and below the diagonal of Tm are written (those above are
 // zero by definition; readers of Tm mask them).  A is read only strictly below
-// the diagonal.  X is scratch of 4*16*kLD16 floats.  Ends with a barrier.
+// the diagonal.  X is scratch of 4*16*kLD16 floats.  Waves 0-3 compute; a
+// workgroup of more waves passes the others through the barriers.  Ends with a
+// barrier.
 constexpr int kLD16 = 20;
 __device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, float* X) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    {
+    if (wave < 4) {
         // diagonal block I = wave, right-looking: lane (column j = lane >> 2, quad
         // position q = lane & 3) holds rows 4 q .. 4 q + 3 of column j.  Once row k
         // is final it is x_k: its owner (quad position k >> 2) broadcasts it to its

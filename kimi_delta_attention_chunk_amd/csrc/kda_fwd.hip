@@ -3,7 +3,8 @@
 // Two launches per call (the in-chunk algebra is in kda_chunk.cuh):
 //   fwd_intra   one workgroup per (chunk, head): gate preparation, in-chunk
 //               cumulative decay, Gram matrices, UT inverse, w and u, Aqk
-//               (dk = 32: the chunk's affine form instead), kda_intra.cuh;
+//               (kda_intra.cuh); dk = 32: the chunk's affine form instead, by
+//               a workgroup of eight waves (kda_intra32.cuh);
 //   fwd_scan    one workgroup per (sequence, head, block of state columns):
 //               chunk after chunk with the fp32 state in registers, the state
 //               update and the output o (kda_pscan.cuh for dk = 32,
@@ -15,6 +16,7 @@
 #include "kda_chunk.cuh"
 #include "kda_internal.h"
 #include "kda_intra.cuh"
+#include "kda_intra32.cuh"
 #include "kda_pscan.cuh"
 #include "kda_scan.cuh"
 
@@ -132,8 +134,12 @@ hipError_t launch_fwd_pipeline(const Prm& p, const ChunkArgs& a, hipStream_t s, 
         if (!p.hs || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
         if (store && (!p.tm || !p.aqT)) return hipErrorInvalidValue;
     }
-    if (run_intra && a.n_chunks_bound > 0)
-        KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+    if (run_intra && a.n_chunks_bound > 0) {
+        if constexpr (DK == 32 && DV == 64)
+            KDA_LAUNCH("fwd_intra", (intra32_kernel<TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kI32Threads), s, p);
+        else
+            KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DV, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+    }
     if constexpr (DK == 32 && DV == 64) {
         const int total = a.N * a.H * (DV / kPsBV);
         if (write_o && store)
@@ -173,10 +179,10 @@ hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t 
     if (a.dk != 32 || a.dv != 64 || !p.pm || !p.pmT || !p.hh || !p.qh || !p.qhT || !p.ol) return hipErrorInvalidValue;
     if (a.n_chunks_bound == 0) return hipSuccess;
     if (a.in_bf16)
-        KDA_LAUNCH("fwd_intra", (intra_kernel<32, 64, uint16_t, Prec::BF3>), dim3(a.n_chunks_bound, a.H), dim3(kThreads),
+        KDA_LAUNCH("fwd_intra", (intra32_kernel<uint16_t, Prec::BF3>), dim3(a.n_chunks_bound, a.H), dim3(kI32Threads),
                    s, p);
     else
-        KDA_LAUNCH("fwd_intra", (intra_kernel<32, 64, float, Prec::F32>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s,
+        KDA_LAUNCH("fwd_intra", (intra32_kernel<float, Prec::F32>), dim3(a.n_chunks_bound, a.H), dim3(kI32Threads), s,
                    p);
     return hipSuccess;
 }

@@ -18,9 +18,9 @@
 //     32-column block of v), as MFMA products.
 // Outputs (fp32 workspace, slot = chunk * H + head): w [64][DK], u [64][DV],
 // qg = exp(G) q^ [64][DK], khT = (k^ exp(G_L - G))^T [DK][64], gl = exp(G_L)
-// [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested;
-// for dk = 32 instead the affine form of the chunk (pass 3), Aqk^T and T for
-// the backward if requested.
+// [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested.
+// dk = 32 (dv = 64) keeps the chunk's affine form instead and has a kernel of
+// its own with eight waves (kda_intra32.cuh), which shares the helpers below.
 #pragma once
 
 #include "kda_chunk.cuh"
@@ -55,6 +55,7 @@ __device__ __forceinline__ int kc_off(int I) { return (I - 1) * I * 8; }  // 0, 
 
 template <int DK, int DV, typename TIn, Prec P>
 __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two workgroups per CU
+    static_assert(DK >= 64, "dk = 32: intra32_kernel");
     constexpr int NB = DK / kCB32, NVB = DV / 32;
     // LDS (about 77 KB, two workgroups per CU):
     //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: BT tile and solve scratch
@@ -67,7 +68,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
     __shared__ float bet[kChunk];
     __shared__ float seg[8 * 32];        // column-scan segment totals
-    __shared__ float glS[DK];            // exp(G_L) (pass 3)
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
     static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
@@ -166,7 +166,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     // Gram accumulators: 12 off-diagonal tiles (6 of Akk, 6 of Aqk), 3 per wave,
     // and this thread's 4 diagonal-block entries of each.
     f32x4 gacc[3];
-    float khs[8];  // this thread's Kh row values (dk = 32, pass 3)
 #pragma unroll
     for (int i = 0; i < 3; ++i) gacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dkk[2] = {0.f, 0.f}, dqk[2] = {0.f, 0.f}, dqd = 0.f;
@@ -175,7 +174,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     char* khT = (char*)(p.khT + slot * DK * kChunk);  // rows c, 2 k-blocks
     float* KhS = Tm;                                   // (k exp(G_L - G))^T staging, [c][t], pass 1 only
     float* QgS = Tm + kCB32 * kLD;                     // (exp(G) q)^T staging, [c][t], pass 1 only (dk >= 64)
-    const bool rev_ops = DK != 32 && p.qgT != nullptr;  // transposed operands for the reverse scan
+    const bool rev_ops = p.qgT != nullptr;  // transposed operands for the reverse scan
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB32;
@@ -205,10 +204,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 const float gt = G[b][i];
                 qgv[i] = exp2_hw(gt) * qx[b][i];
                 khv[i] = kx[b][i] * exp2_hw(Gb[last * kLB + cc] - gt);
-                if constexpr (DK != 32) {
-                    KhS[cc * kLD + tr] = khv[i];
-                    if (rev_ops) QgS[cc * kLD + tr] = qgv[i];
-                }
+                KhS[cc * kLD + tr] = khv[i];
+                if (rev_ops) QgS[cc * kLD + tr] = qgv[i];
                 const float e = exp2_hw(gt - Gb[16 * (I >= 1 ? I : 1) * kLB + cc]);
                 kr[i] = kx[b][i] * e;
                 qr[i] = qx[b][i] * e;
@@ -222,22 +219,16 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
 #pragma unroll
             for (int J = 1; J <= 3; ++J)
                 if (tr < 16 * J) Kc.put8(kc_off(J) + tr, 8 * part, kc[J - 1]);
-            if constexpr (DK != 32) {  // (dk = 32 keeps the affine form instead)
-                store_frag8<WP>(frag_rec(qg, tr, b, DK / 32), tr, qgv, part);
-                if (rev_ops)  // Kh rows t, channels of this block
-                    store_frag8<WP>(frag_rec(p.khb + slot * kChunk * DK, tr, b, DK / 32), tr, khv, part);
-            }
-            if constexpr (DK == 32) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) khs[i] = khv[i];
-            }
+            store_frag8<WP>(frag_rec(qg, tr, b, DK / 32), tr, qgv, part);
+            if (rev_ops)  // Kh rows t, channels of this block
+                store_frag8<WP>(frag_rec(p.khb + slot * kChunk * DK, tr, b, DK / 32), tr, khv, part);
         }
-        if (DK != 32 && tr == 0) {
+        if (tr == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) p.gl[slot * DK + cb + 8 * part + i] = exp2_hw(Gb[last * kLB + 8 * part + i]);
         }
         __syncthreads();
-        if constexpr (DK != 32) {
+        {
             // (k exp(G_L - G))^T of this channel block to the workspace: row c = cb + tid / 8
             const int cr8 = threadIdx.x >> 3, w8 = threadIdx.x & 7;
             float x[8];
@@ -329,53 +320,32 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         }
     }
     __syncthreads();
-    // dk = 32: the Aqk rows of this wave's 16 output rows of pass 3 (k-blocks
-    // 0 .. w >> 1, zero above the diagonal), kept as register fragments through
-    // the solve and pass 2
-    AFrag<P> fQ[2];
-    const int nq = (wave >> 1) + 1;  // Aqk row block w reaches s < 16 (w + 1): k-blocks 0 .. w >> 1
-    if constexpr (DK == 32) {
-        const int r = 16 * wave + (threadIdx.x & 15), s8 = 8 * ((threadIdx.x & 63) >> 4);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            if (kb < nq) {
-                float x[8];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int s = 32 * kb + s8 + m;
-                    x[m] = s > r ? 0.f : AqL[r * LA + s];
-                }
-                make_frag(fQ[kb], x);
-            }
-    }
     {
-        if constexpr (DK != 32) {
-            // Aqk to the workspace in fragment form, zero above the diagonal: 8 entries per thread and pass
-            char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
+        // Aqk to the workspace in fragment form, zero above the diagonal: 8 entries per thread and pass
+        char* aq = (char*)(p.aqk + slot * kChunk * kChunk);
 #pragma unroll
-            for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
-                const int q8 = threadIdx.x + kThreads * i;
-                const int t = q8 >> 3, s0 = 8 * (q8 & 7);
-                float x[8];
+        for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
+            const int q8 = threadIdx.x + kThreads * i;
+            const int t = q8 >> 3, s0 = 8 * (q8 & 7);
+            float x[8];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
-                // (the block of rows t < 32, s >= 32 is zero and never read: not written)
-                if (t >= 32 || s0 < 32) store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
-            }
+            for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
+            // (the block of rows t < 32, s >= 32 is zero and never read: not written)
+            if (t >= 32 || s0 < 32) store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
         }
-        if (p.aqT) {
-            // Aqk^T (row s, indices t; zero for t < s) for the backward
-            char* aqt = (char*)(p.aqT + slot * kChunk * kChunk);
+    }
+    if (p.aqT) {
+        // Aqk^T (row s, indices t; zero for t < s) for the backward
+        char* aqt = (char*)(p.aqT + slot * kChunk * kChunk);
 #pragma unroll
-            for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
-                const int q8 = threadIdx.x + kThreads * i;
-                const int sr = q8 >> 3, t0 = 8 * (q8 & 7);
-                float x[8];
+        for (int i = 0; i < kChunk * kChunk / 8 / kThreads; ++i) {
+            const int q8 = threadIdx.x + kThreads * i;
+            const int sr = q8 >> 3, t0 = 8 * (q8 & 7);
+            float x[8];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
-                // (the block of rows s >= 32, t < 32 is zero and never read: not written)
-                if (sr < 32 || t0 >= 32) store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
-            }
+            for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
+            // (the block of rows s >= 32, t < 32 is zero and never read: not written)
+            if (sr < 32 || t0 >= 32) store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
         }
     }
     solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
@@ -399,8 +369,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     constexpr int GRP = (3 * kChunk * kLB) / (kCB32 * LA);  // blocks per round
     static_assert(GRP >= 1, "one operand block must fit in KQG");
     const float bt = bet[tr];
-    static_assert(DK != 32 || NBLK <= GRP, "dk = 32: w and u in one round");
-    f32x4 pacc[DK == 32 ? (8 * GRP + kWaves - 1) / kWaves : 1];  // this wave's w / u tiles (dk = 32)
     float* wo = p.w + slot * kChunk * DK;
     float* uo = p.u + slot * kChunk * DV;
 #pragma unroll
@@ -431,10 +399,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
-            if constexpr (DK == 32) {
-                pacc[kt] = acc;  // w and u go on to pass 3 only
-                continue;
-            }
             if (rev_ops && b < NB) {  // w^T rows c, tokens as indices: four consecutive t per lane
                 const int t0 = tm * 16 + frag_row(0), cw = b * kCB32 + tn * 16 + frag_col();
                 store_frag4<WP>(frag_rec(p.wT + slot * DK * kChunk, cw, t0 >> 5, 2), cw, acc, t0 & 31);
@@ -467,140 +431,6 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
                 for (int m = 0; m < 8; ++m) x[m] = Tm[t * kLD + k0 + m];
                 store_frag8<WP>(frag_rec(wk, t, k0 >> 5, DK / 32), t, x, (k0 >> 3) & 3);
             }
-        }
-    }
-    if constexpr (DK == 32) {
-        __syncthreads();  // pass-2 operand tiles (KQG, S1) consumed
-        // ---- pass 3: the chunk as an affine map of the state entering it (dk = 32).
-        //   P   = Diag(exp G_L) - Kh^T w      (32 x 32)   h'     = P h + hh
-        //   hh  = Kh^T u                      (32 x 64)
-        //   qh  = scale (Qg - Aqk w)          (64 x 32)   o      = ol + qh h
-        //   ol  = scale Aqk u                 (64 x 64)
-        // and for the reverse pass D = P^T D' + qh^T dO.  w^T and u^T are staged in
-        // LDS from this wave's pass-2 tiles and Kh^T from the pass-1 registers; the
-        // Aqk fragments were taken from LDS before the solve.  A D fragment holds four
-        // consecutive rows of one column, so each fragment-form array is written from the
-        // product of its transpose: P from P^T's tiles and P^T from P's, qh from
-        // qh^T's and qh^T from qh's.  hh and ol are kept in fragment order
-        // ([32-column block][16x16 tile][lane][4]) for the state pass to add to its
-        // accumulators directly.
-        const T64 WT(KQG, DK), UT(KQG + DK * LA, DV);
-        static_assert(DK * LA + DV * LA <= 3 * kChunk * kLB, "w^T and u^T must fit in KQG");
-        float* Qgs = S1;  // exp(G) q, fp32 [t][c], stride kLB
-        const T64 KHT(S1 + kChunk * kLB, DK);  // Kh^T [c][t]
-        static_assert(kChunk * kLB + DK * LA <= S1F, "Qg and Kh^T must fit in S1");
-#pragma unroll
-        for (int i = 0; i < 8; ++i) KHT.put(8 * part + i, tr, khs[i]);
-#pragma unroll
-        for (int kt = 0; kt < (8 * GRP + kWaves - 1) / kWaves; ++kt) {
-            const int tile = wave + kWaves * kt, g = tile / 8, tl = tile % 8, tm = tl >> 1, tn = tl & 1;
-            if (g == 0) WT.put4(tn * 16 + frag_col(), tm * 16 + frag_row(0), pacc[kt]);
-            else UT.put4((g - 1) * 32 + tn * 16 + frag_col(), tm * 16 + frag_row(0), pacc[kt]);
-        }
-        {
-            float qv[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qv[i] = exp2_hw(G[0][i]) * qx[0][i];
-            *(f32x4*)&Qgs[tr * kLB + 8 * part] = f32x4{qv[0], qv[1], qv[2], qv[3]};
-            *(f32x4*)&Qgs[tr * kLB + 8 * part + 4] = f32x4{qv[4], qv[5], qv[6], qv[7]};
-            if (tr == last) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) glS[8 * part + i] = exp2_hw(G[0][i]);
-            }
-        }
-        const int lr = threadIdx.x & 15, lg = (threadIdx.x & 63) >> 4;
-        const float scale = p.scale;
-        // Each wave reads all of Kh^T (two row tiles, two k-blocks; from LDS) once
-        // as register fragments and, with the Aqk fragments of its own 16 output
-        // rows (fQ, taken before the solve), forms:
-        //   wave 0: P;  wave 1: P^T;  waves 2, 3: hh rows 16 (w - 2) ..
-        //   all:    qh, qh^T and ol for rows (columns of qh^T) 16 w .. 16 w + 15.
-        AFrag<P> fK[2][2];
-        __syncthreads();
-#pragma unroll
-        for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) load_frag(fK[ta][kb], KHT.sub(16 * ta), 32 * kb);
-        AFrag<P> fb;
-        if (wave < 2) {
-            // P (wave 0) and P^T (wave 1): four 16x16 tiles (ta, tb) of rows c, columns c'
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int ta = q >> 1, tb = q & 1;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    if (wave == 0) {
-                        load_frag(fb, WT.sub(16 * tb), 32 * kb);
-                        acc = mma_ff(fK[ta][kb], fb, acc);
-                    } else {
-                        load_frag(fb, WT.sub(16 * ta), 32 * kb);
-                        acc = mma_ff(fb, fK[tb][kb], acc);
-                    }
-                }
-                f32x4 x;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ra = 16 * ta + 4 * lg + i, cb = 16 * tb + lr;
-                    x[i] = (ra == cb ? glS[ra] : 0.f) - acc[i];
-                }
-                float* dst = wave == 0 ? p.pmT : p.pm;
-                store_frag4<P>(frag_rec(dst + slot * DK * DK, 16 * tb + lr, 0, 1), 16 * tb + lr, x, 16 * ta + 4 * lg);
-            }
-        } else {
-            // hh rows 16 ta .., all four column tiles
-            const int ta = wave - 2;
-#pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    load_frag(fb, UT.sub(16 * tj), 32 * kb);
-                    acc = mma_ff(ta == 0 ? fK[0][kb] : fK[1][kb], fb, acc);  // (no dynamic register index)
-                }
-                *(f32x4*)(p.hh + slot * DK * DV + (size_t)(((tj >> 1) * 4 + ta * 2 + (tj & 1)) * 64 + (threadIdx.x & 63)) * 4) =
-                    acc;
-            }
-        }
-        const int tt = wave;
-#pragma unroll
-        for (int tc = 0; tc < 2; ++tc) {
-            // qh tile (t-tile tt, c-tile tc) -> qh^T (row c, indices t), and qh^T tile (tc, tt) -> qh
-            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < nq) {
-                    load_frag(fb, WT.sub(16 * tc), 32 * kb);
-                    a1 = mma_ff(fQ[kb], fb, a1);
-                    a2 = mma_ff(fb, fQ[kb], a2);
-                }
-            }
-            f32x4 x1, x2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int a = 4 * lg + i;
-                x1[i] = scale * (Qgs[(16 * tt + a) * kLB + 16 * tc + lr] - a1[i]);
-                x2[i] = scale * (Qgs[(16 * tt + lr) * kLB + 16 * tc + a] - a2[i]);
-            }
-            store_frag4<P>(frag_rec(p.qhT + slot * kChunk * DK, 16 * tc + lr, tt >> 1, 2), 16 * tc + lr, x1,
-                           (16 * tt + 4 * lg) & 31);
-            store_frag4<P>(frag_rec(p.qh + slot * kChunk * DK, 16 * tt + lr, 0, 1), 16 * tt + lr, x2, 16 * tc + 4 * lg);
-        }
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-            // ol tile (t-tile tt, column tile tj)
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < nq) {
-                    load_frag(fb, UT.sub(16 * tj), 32 * kb);
-                    acc = mma_ff(fQ[kb], fb, acc);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= scale;
-            *(f32x4*)(p.ol + slot * kChunk * DV + (size_t)(((tj >> 1) * 8 + tt * 2 + (tj & 1)) * 64 + (threadIdx.x & 63)) * 4) =
-                acc;
         }
     }
 }
