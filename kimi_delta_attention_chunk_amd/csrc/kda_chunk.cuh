@@ -93,20 +93,53 @@ __device__ __forceinline__ f32x4 tpk_load4(const float* T, int t, int s) {
 // blocks level by level,
 //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
 // Only the blocks on and below the diagonal of Tm are written (those above are
-// zero by definition; readers of Tm mask them).  A is read only strictly below
-// the diagonal.  X is scratch of 4*16*kLD16 floats.  Waves 0-3 compute; a
-// workgroup of more waves passes the others through the barriers.  Ends with a
-// barrier.
-constexpr int kLD16 = 20;
-__device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, float* X) {
+// zero by definition; readers of Tm mask them).  Only A's entries strictly below
+// the diagonal enter the result (the others are read and discarded by
+// selection).  Waves 0-3 compute; a workgroup of more waves passes the others
+// through the barriers.  Ends with a barrier.
+//
+// Level LVL: wave w forms block (I, J) = (LVL + w, w).  Both products are MFMA
+// chains whose operands are all read from LDS before the first product.  The
+// sum X = sum_K A_IK T_KJ stays in its accumulator registers: in the product
+// T_II X the contraction index is visited in a permuted order, lane group g
+// taking index 4 g + s at step s, which is exactly the row that the lane's
+// accumulator register s of X holds, so X is the B operand as it stands.
+template <int LVL>
+__device__ __forceinline__ void solve_level(const float* A, float* Tm, int wave, int lane) {
+    const int I = LVL + wave, J = wave;
+    if (I >= 4) return;
+    const int r = lane & 15, kq = lane >> 4;
+    constexpr int NS = 4 * LVL;  // steps of 4 over the contraction range [16 J, 16 I)
+    float a[NS], b[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        a[s] = A[(16 * I + r) * kLD + 16 * J + 4 * s + kq];
+        b[s] = Tm[(16 * J + 4 * s + kq) * kLD + 16 * J + r];
+    }
+    const f32x4 t = *(const f32x4*)&Tm[(16 * I + r) * kLD + 16 * I + 4 * kq];  // T_II, row r, columns 4 kq ..
+    f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], x, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) y = __builtin_amdgcn_mfma_f32_16x16x4f32(t[s], x[s], y, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tm[(16 * I + 4 * kq + i) * kLD + 16 * J + r] = -y[i];
+}
+__device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     if (wave < 4) {
         // diagonal block I = wave, right-looking: lane (column j = lane >> 2, quad
         // position q = lane & 3) holds rows 4 q .. 4 q + 3 of column j.  Once row k
         // is final it is x_k: its owner (quad position k >> 2) broadcasts it to its
-        // quad by DPP, and every row t > k takes -A[t][k] x_k.
+        // quad by DPP, and every row t > k takes -A[t][k] x_k.  The lane's four rows
+        // of A's block are read whole before the chain starts.
         const int I = wave, j = lane >> 2, q = lane & 3;
         const float* Ab = A + (16 * I + 4 * q) * kLD + 16 * I;  // this lane's first row of the block
+        f32x4 ar[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ar[i][c] = *(const f32x4*)(Ab + i * kLD + 4 * c);
         float r[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] = (4 * q + i == j) ? 1.f : 0.f;
@@ -117,7 +150,7 @@ __device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, floa
             const float xk = dpp_f<ctl>(r[k & 3]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float a = (4 * q + i > k) ? Ab[i * kLD + k] : 0.f;  // strictly below the diagonal only
+                const float a = (4 * q + i > k) ? ar[i][k >> 2][k & 3] : 0.f;  // strictly below the diagonal only
                 r[i] = fmaf(-a, xk, r[i]);
             }
         });
@@ -125,26 +158,12 @@ __device__ __forceinline__ void solve_unit_lower(const float* A, float* Tm, floa
         for (int i = 0; i < 4; ++i) Tm[(16 * I + 4 * q + i) * kLD + 16 * I + j] = r[i];
     }
     __syncthreads();
-    for (int lvl = 1; lvl < 4; ++lvl) {
-        // blocks (I, J = I - lvl), I = lvl..3; one wave each
-        const int I = lvl + wave, J = wave;
-        const bool active = I < 4;
-        // X_w = sum_{K=J}^{I-1} A_IK T_KJ
-        if (active) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma16_f32(A + (16 * I) * kLD, kLD, 1, Tm + 16 * J, kLD, 1, 16 * J, 16 * I, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[wave * 16 * kLD16 + (4 * (lane >> 4) + i) * kLD16 + (lane & 15)] = acc[i];
-        }
-        __syncthreads();
-        if (active) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma16_f32(Tm + (16 * I) * kLD + 16 * I, kLD, 1, X + wave * 16 * kLD16, kLD16, 1, 0, 16, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Tm[(16 * I + 4 * (lane >> 4) + i) * kLD + 16 * J + (lane & 15)] = -acc[i];
-        }
-        __syncthreads();
-    }
+    solve_level<1>(A, Tm, wave, lane);
+    __syncthreads();
+    solve_level<2>(A, Tm, wave, lane);
+    __syncthreads();
+    solve_level<3>(A, Tm, wave, lane);
+    __syncthreads();
 }
 
 // Inclusive cumulative sum over the 64 rows of a 64 x 32 LDS array A (row

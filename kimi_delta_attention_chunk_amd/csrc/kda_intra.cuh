@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     static_assert(DK >= 64, "dk = 32: intra32_kernel");
     constexpr int NB = DK / kCB32, NVB = DV / 32;
     // LDS (about 77 KB, two workgroups per CU):
-    //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: BT tile and solve scratch
+    //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: Aqk staging, BT tiles
     //   S1   Kr | Qr | Kc   MFMA tiles of the off-diagonal Gram blocks; then Akk (fp32); then T (tile)
     //   Tm   T, fp32 (the solve)
     constexpr int LB8 = kCB32 + 8, LA = kChunk + 8;
@@ -69,13 +69,12 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     __shared__ float bet[kChunk];
     __shared__ float seg[8 * 32];        // column-scan segment totals
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
-    static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
+    static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
     static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
 
     float* Kb = KQG;
     float* Qb = KQG + kChunk * kLB;
     float* Gb = KQG + 2 * kChunk * kLB;
-    float* X = KQG + kCB32 * LA;         // solve scratch (after pass 1)
     using T32 = STile<P, 32>;  // operand tiles of 32 and 64 values per row
     using T64 = STile<P, 64>;
     static_assert(STile<Prec::F32, 32>::ld == LB8 && STile<Prec::F32, 64>::ld == LA, "tile footprints");
@@ -348,7 +347,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             if (sr < 32 || t0 >= 32) store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
         }
     }
-    solve_unit_lower(A, Tm, X);  // ends with a barrier (X is written only after its first barrier)
+    solve_unit_lower(A, Tm);  // ends with a barrier
     if (p.tm) {
         // the 10 blocks on and below the diagonal, packed (tpk_index)
         f32x4* to = (f32x4*)(p.tm + slot * kTPacked);

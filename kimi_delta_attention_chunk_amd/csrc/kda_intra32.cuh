@@ -30,7 +30,7 @@ template <typename TIn, Prec P>
 __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // two workgroups per CU
     constexpr int DK = 32, DV = 64, NVB = DV / 32;
     // LDS, as in intra_kernel:
-    //   KQG  Kb | Qb | Gb   fp32 [t][c]; after pass 1: Aqk staging, solve scratch, BT tiles, w^T / u^T
+    //   KQG  Kb | Qb | Gb   fp32 [t][c]; after pass 1: Aqk staging, BT tiles, w^T / u^T
     //   S1   Kr | Qr | Kc   MFMA tiles of the off-diagonal Gram blocks; then Akk; then T (tile); then Qg, Kh^T
     //   Tm   T, fp32 (the solve)
     constexpr int LB8 = kCB32 + 8, LA = kChunk + 8;
@@ -42,14 +42,13 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
     __shared__ float seg[16 * 32];  // column-scan segment totals (4 rows per thread)
     __shared__ float glS[DK];       // exp(G_L)
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
-    static_assert(kCB32 * LA + 4 * 16 * kLD16 <= 3 * kChunk * kLB, "BT and X must fit in KQG");
+    static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
     static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
     static_assert(kI32Threads == 8 * kChunk, "eight threads per token row");
 
     float* Kb = KQG;
     float* Qb = KQG + kChunk * kLB;
     float* Gb = KQG + 2 * kChunk * kLB;
-    float* X = KQG + kCB32 * LA;  // solve scratch (after pass 1)
     using T32 = STile<P, 32>;
     using T64 = STile<P, 64>;
     static_assert(STile<Prec::F32, 32>::ld == LB8 && STile<Prec::F32, 64>::ld == LA, "tile footprints");
@@ -256,7 +255,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
         if (sr < 32 || t0 >= 32)
             store_frag8<P>(frag_rec((char*)(p.aqT + slot * kChunk * kChunk), sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
     }
-    solve_unit_lower(A, Tm, X);  // (waves 0-3; ends with a barrier, X is written only after its first barrier)
+    solve_unit_lower(A, Tm);  // (waves 0-3; ends with a barrier)
     if (p.tm) {
         // the 10 blocks on and below the diagonal, packed (tpk_index)
         f32x4* to = (f32x4*)(p.tm + slot * kTPacked);
