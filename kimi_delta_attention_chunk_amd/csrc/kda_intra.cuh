@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     //   KQG  Kb | Qb | Gb   one channel block, fp32 [t][c]; after pass 1: Aqk staging, BT tiles
     //   S1   Kr | Qr | Kc   MFMA tiles of the off-diagonal Gram blocks; then Akk (fp32); then T (tile)
     //   Tm   T, fp32 (the solve)
-    constexpr int LB8 = kCB32 + 8, LA = kChunk + 8;
+    constexpr int LB8 = kCB32 + 8, LA = kChunk + 8, LQ = kChunk + 1;
     constexpr int S1F = (48 + 48 + 96) * LB8;
     __shared__ __attribute__((aligned(16))) float KQG[3 * kChunk * kLB];
     __shared__ __attribute__((aligned(16))) float S1[S1F];
@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     __shared__ float seg[8 * 32];        // column-scan segment totals
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
-    static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
+    static_assert(kChunk * LQ <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
 
     float* Kb = KQG;
     float* Qb = KQG + kChunk * kLB;
@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     // ---- assemble Akk (fp32, rows times beta, over S1) and Aqk (fp32 staging over KQG).
     // Only the parts that are read are written: the solve reads the strictly lower part of
     // Akk; the Aqk copy below writes zeros above the diagonal by index.
-    float* AqL = KQG;  // [t][s], stride LA
+    float* AqL = KQG;  // [t][s], stride LQ (odd: its row-wise and column-wise reads are free of bank conflicts)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int pidx = threadIdx.x + kThreads * i;
@@ -301,10 +301,10 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             int t, s;
             diag_pair(pidx, t, s);
             A[t * kLD + s] = bet[t] * dkk[i];
-            AqL[t * LA + s] = dqk[i];
+            AqL[t * LQ + s] = dqk[i];
         }
     }
-    if ((threadIdx.x & 3) == 0) AqL[(threadIdx.x >> 2) * (LA + 1)] = dqd;
+    if ((threadIdx.x & 3) == 0) AqL[(threadIdx.x >> 2) * (LQ + 1)] = dqd;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int tau = wave + 4 * i;
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * I + frag_row(r), s = 16 * J + frag_col();
             if (kind == 0) A[t * kLD + s] = bet[t] * gacc[i][r];
-            else AqL[t * LA + s] = gacc[i][r];
+            else AqL[t * LQ + s] = gacc[i][r];
         }
     }
     __syncthreads();
@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             const int t = q8 >> 3, s0 = 8 * (q8 & 7);
             float x[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LA + s0 + m];
+            for (int m = 0; m < 8; ++m) x[m] = s0 + m > t ? 0.f : AqL[t * LQ + s0 + m];
             // (the block of rows t < 32, s >= 32 is zero and never read: not written)
             if (t >= 32 || s0 < 32) store_frag8<WP>(frag_rec(aq, t, s0 >> 5, 2), t, x, (s0 >> 3) & 3);
         }
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             const int sr = q8 >> 3, t0 = 8 * (q8 & 7);
             float x[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
+            for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LQ + sr];
             // (the block of rows s >= 32, t < 32 is zero and never read: not written)
             if (sr < 32 || t0 >= 32) store_frag8<WP>(frag_rec(aqt, sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
         }

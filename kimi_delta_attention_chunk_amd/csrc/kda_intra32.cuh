@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
     //   KQG  Kb | Qb | Gb   fp32 [t][c]; after pass 1: Aqk staging, BT tiles, w^T / u^T
     //   S1   Kr | Qr | Kc   MFMA tiles of the off-diagonal Gram blocks; then Akk; then T (tile); then Qg, Kh^T
     //   Tm   T, fp32 (the solve)
-    constexpr int LB8 = kCB32 + 8, LA = kChunk + 8;
+    constexpr int LB8 = kCB32 + 8, LA = kChunk + 8, LQ = kChunk + 1;
     constexpr int S1F = (48 + 48 + 96) * LB8;
     __shared__ __attribute__((aligned(16))) float KQG[3 * kChunk * kLB];
     __shared__ __attribute__((aligned(16))) float S1[S1F];
@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
     __shared__ float glS[DK];       // exp(G_L)
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
-    static_assert(kChunk * LA <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
+    static_assert(kChunk * LQ <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
     static_assert(kI32Threads == 8 * kChunk, "eight threads per token row");
 
     float* Kb = KQG;
@@ -203,12 +203,12 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
 
     // ---- assemble Akk (fp32, rows times beta, over S1; strictly lower part only, as
     // the solve reads it) and Aqk (fp32 staging over KQG; zero above the diagonal by index below)
-    float* AqL = KQG;  // [t][s], stride LA
+    float* AqL = KQG;  // [t][s], stride LQ (odd: its row-wise and column-wise reads are free of bank conflicts)
     if (pidx < kDiagPairs) {
         A[pt * kLD + ps] = bet[pt] * dkk;
-        AqL[pt * LA + ps] = dqk;
+        AqL[pt * LQ + ps] = dqk;
     }
-    if ((threadIdx.x & 7) == 0) AqL[tr * (LA + 1)] = dqd;
+    if ((threadIdx.x & 7) == 0) AqL[tr * (LQ + 1)] = dqd;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tau = wave + kI32Waves * i;
@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * I + frag_row(r), s = 16 * J + frag_col();
                 if (kind == 0) A[t * kLD + s] = bet[t] * gacc[i][r];
-                else AqL[t * LA + s] = gacc[i][r];
+                else AqL[t * LQ + s] = gacc[i][r];
             }
         }
     }
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const int s = 32 * kb + s8 + m;
-                    x[m] = s > r ? 0.f : AqL[r * LA + s];
+                    x[m] = s > r ? 0.f : AqL[r * LQ + s];
                 }
                 make_frag(fQ[kb], x);
             }
@@ -250,7 +250,7 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
         const int sr = threadIdx.x >> 3, t0 = 8 * (threadIdx.x & 7);
         float x[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LA + sr];
+        for (int m = 0; m < 8; ++m) x[m] = t0 + m < sr ? 0.f : AqL[(t0 + m) * LQ + sr];
         // (the block of rows s >= 32, t < 32 is zero and never read: not written)
         if (sr < 32 || t0 >= 32)
             store_frag8<P>(frag_rec((char*)(p.aqT + slot * kChunk * kChunk), sr, t0 >> 5, 2), sr, x, (t0 >> 3) & 3);
