@@ -31,6 +31,36 @@ enum class Prec { F32, BF3 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// The hi/lo split of two values as packed bf16 pairs: hi = x rounded to bf16,
+// lo = the remainder x - hi (exact in fp32) rounded to bf16.  The remainder is
+// taken from the packed hi word, so a pair costs one conversion for hi, two bit
+// operations, two subtractions and one conversion for lo (element-wise code
+// converts every value twice).
+// (The low half is moved up with a byte permute: written as a shift, the
+// compiler rebuilds it from a second conversion of x0.)
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hp, uint32_t& lp) {
+    hp = pack_bf16x2(x0, x1);
+    const float h0 = __uint_as_float(__builtin_amdgcn_perm(hp, 0u, 0x05040c0cu));  // bytes 1:0 of hp -> 3:2
+    lp = pack_bf16x2(x0 - h0, x1 - __uint_as_float(hp & 0xffff0000u));
+}
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+// four values (hi and lo each as two words) and eight values (four words)
+__device__ __forceinline__ void split4(const float* x, u32x2v& h, u32x2v& l) {
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    h = u32x2v{h0, h1};
+    l = u32x2v{l0, l1};
+}
+__device__ __forceinline__ void split8(const float* x, u32x4v& h, u32x4v& l) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], hw[i], lw[i]);
+    h = u32x4v{hw[0], hw[1], hw[2], hw[3]};
+    l = u32x4v{lw[0], lw[1], lw[2], lw[3]};
+}
+
 template <Prec P> struct KStep;
 template <> struct KStep<Prec::F32> { static constexpr int value = 4; };
 template <> struct KStep<Prec::BF3> { static constexpr int value = 32; };
@@ -66,15 +96,11 @@ template <> struct Tile<Prec::BF3> {
     }
     // four consecutive values (k a multiple of 4)
     __device__ __forceinline__ void put4(int r, int k, f32x4 x) const {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 h, l;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h[i] = (__bf16)x[i];
-            l[i] = (__bf16)(x[i] - (float)h[i]);
-        }
-        *(bf16x4*)(hi + r * ld + k) = h;
-        *(bf16x4*)(lo + r * ld + k) = l;
+        const float v[4] = {x[0], x[1], x[2], x[3]};
+        u32x2v h, l;
+        split4(v, h, l);
+        *(u32x2v*)(hi + r * ld + k) = h;
+        *(u32x2v*)(lo + r * ld + k) = l;
     }
     __device__ __forceinline__ float get(int r, int k) const { return (float)hi[r * ld + k] + (float)lo[r * ld + k]; }
     __device__ __forceinline__ Tile sub(int r) const { return Tile(hi + r * ld, lo + r * ld, ld); }
@@ -173,11 +199,10 @@ __device__ __forceinline__ f32x4 mma_frag(const AFrag<Prec::F32>& a, const Tile<
 // A fragment from this lane's 8 values (indices 8 g .. 8 g + 7 of the k-block,
 // g = lane >> 4), split as a store to and load from fragment form would.
 __device__ __forceinline__ void make_frag(AFrag<Prec::BF3>& f, const float (&x)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        f.hi[i] = (__bf16)x[i];
-        f.lo[i] = (__bf16)(x[i] - (float)f.hi[i]);
-    }
+    u32x4v h, l;
+    split8(x, h, l);
+    f.hi = __builtin_bit_cast(bf16x8, h);
+    f.lo = __builtin_bit_cast(bf16x8, l);
 }
 __device__ __forceinline__ void make_frag(AFrag<Prec::F32>& f, const float (&x)[8]) {
     f.a = f32x4{x[0], x[1], x[2], x[3]};
@@ -190,15 +215,11 @@ template <Prec P>
 __device__ __forceinline__ void store_frag8(char* rec, int row, const float (&x)[8], int which);
 template <>
 __device__ __forceinline__ void store_frag8<Prec::BF3>(char* rec, int row, const float (&x)[8], int which) {
-    bf16x8 h, l;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h[i] = (__bf16)x[i];
-        l[i] = (__bf16)(x[i] - (float)h[i]);
-    }
+    u32x4v h, l;
+    split8(x, h, l);
     char* b = rec + 16 * (16 * which + (row & 15));
-    *(bf16x8*)b = h;
-    *(bf16x8*)(b + 1024) = l;
+    *(u32x4v*)b = h;
+    *(u32x4v*)(b + 1024) = l;
 }
 template <>
 __device__ __forceinline__ void store_frag8<Prec::F32>(char* rec, int row, const float (&x)[8], int which) {
@@ -262,16 +283,12 @@ template <Prec P>
 __device__ __forceinline__ void store_frag4(char* rec, int row, const f32x4& x, int k0);
 template <>
 __device__ __forceinline__ void store_frag4<Prec::BF3>(char* rec, int row, const f32x4& x, int k0) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = (__bf16)x[i];
-        l[i] = (__bf16)(x[i] - (float)h[i]);
-    }
+    const float v[4] = {x[0], x[1], x[2], x[3]};
+    u32x2v h, l;
+    split4(v, h, l);
     char* b = rec + 16 * (16 * (k0 >> 3) + (row & 15)) + 2 * (k0 & 4);
-    *(bf16x4*)b = h;
-    *(bf16x4*)(b + 1024) = l;
+    *(u32x2v*)b = h;
+    *(u32x2v*)(b + 1024) = l;
 }
 template <>
 __device__ __forceinline__ void store_frag4<Prec::F32>(char* rec, int row, const f32x4& x, int k0) {
@@ -338,16 +355,12 @@ template <int C> struct STile<Prec::BF3, C> {
         lo[o] = (__bf16)(x - (float)h);
     }
     __device__ __forceinline__ void put4(int r, int k, f32x4 x) const {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 h, l;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h[i] = (__bf16)x[i];
-            l[i] = (__bf16)(x[i] - (float)h[i]);
-        }
+        const float v[4] = {x[0], x[1], x[2], x[3]};
+        u32x2v h, l;
+        split4(v, h, l);
         const int o = at(r, k);
-        *(bf16x4*)(hi + o) = h;
-        *(bf16x4*)(lo + o) = l;
+        *(u32x2v*)(hi + o) = h;
+        *(u32x2v*)(lo + o) = l;
     }
     // Values that are bf16 numbers (bf16 inputs): the lo part is zero and is
     // neither stored nor read (load_frag_hi, mma_ff_ah / mma_ff_bh).
@@ -368,15 +381,11 @@ template <int C> struct STile<Prec::BF3, C> {
     }
     // eight consecutive values (k a multiple of 8): one 16-byte group of each array
     __device__ __forceinline__ void put8(int r, int k, const float (&x)[8]) const {
-        bf16x8 h, l;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            h[i] = (__bf16)x[i];
-            l[i] = (__bf16)(x[i] - (float)h[i]);
-        }
+        u32x4v h, l;
+        split8(x, h, l);
         const int o = at(r, k);
-        *(bf16x8*)(hi + o) = h;
-        *(bf16x8*)(lo + o) = l;
+        *(u32x4v*)(hi + o) = h;
+        *(u32x4v*)(lo + o) = l;
     }
     __device__ __forceinline__ STile sub(int r) const {
         STile t = *this;
