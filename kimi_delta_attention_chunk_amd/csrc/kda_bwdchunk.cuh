@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     __shared__ float dAd[4 * 16 * 17], dAqd[4 * 16 * 17];  // diagonal blocks of dA, dAq
     __shared__ __attribute__((aligned(16))) float bet[kChunk];
     __shared__ float rnq[kChunk], rnk[kChunk];
-    __shared__ float seg[16 * 32], wsum[NW];
+    __shared__ float wsum[NW];
     __shared__ float GL[DK], dgl[DK], colp[NW * DK];
     __shared__ float dbv[kChunk * GV], dbw[kChunk * 2], dba[kChunk * 2], rowp[NW * kChunk];
     constexpr int PH = 23040;
@@ -172,12 +172,13 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
     }
     {
-        // in-chunk cumulative log-decay G, in place in Gs
+        // in-chunk cumulative log-decay G, in place in Gs: wave w scans columns 4 w .. 4 w + 3
+        static_assert(NW * 4 == DK, "four columns per wave");
         float x[4];
-        const int cs = tid & 31, sg = tid >> 5;
+        const int col = 4 * wave + (lane >> 4), s = lane & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = Gs[(4 * sg + i) * LR + cs];
-        col_scan_regs<false>(x, Gs, LR, seg);
+        for (int i = 0; i < 4; ++i) x[i] = Gs[(4 * s + i) * LR + col];
+        col_scan16<false>(x, Gs, LR, col, s);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[i] = Gs[tr * LR + 4 * part + i];
@@ -989,18 +990,19 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     // ------------------------------------------------ P5: dg, gate chain, outputs
     // (a) dG_L into the last row, rows past the end zeroed, reverse cumulative sum -> DG holds dg
     {
-        const int cs = tid & 31, sg = tid >> 5;
+        // (wave w scans columns 4 w .. 4 w + 3; the scan's closing barrier also orders
+        // these reads of colp before its reuse below)
+        const int cs = 4 * wave + (lane >> 4), s = lane & 15;
         const float extra = ((colp[cs] + colp[DK + cs]) + (colp[2 * DK + cs] + colp[3 * DK + cs])) +
                             exp2_hw(GL[cs]) * dgl[cs];
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = 4 * sg + i;
+            const int t = 4 * s + i;
             const float v = DG[t * LR + cs];
             x[i] = t < cr.len ? v + (t == last ? extra : 0.f) : 0.f;
         }
-        __syncthreads();  // colp is reused below
-        col_scan_regs<true>(x, DG, LR, seg);
+        col_scan16<true>(x, DG, LR, cs, s);
     }
     // (b) row-wise pass, thread = (token tr, 4 channels): gate, sigmoid and L2 chains, stores
     {

@@ -198,6 +198,46 @@ __device__ __forceinline__ void col_scan_regs(float (&x)[R], float* A, int ld, f
     __syncthreads();
 }
 
+// Inclusive cumulative sum over the 64 rows of a 64 x 32 LDS array A (row
+// stride ld), forward or in reverse, by a workgroup of 8 waves without a
+// segment exchange: wave w scans columns 4 w .. 4 w + 3, lane (row-of-16 r =
+// lane >> 4, position s = lane & 15) holds in x rows 4 s .. 4 s + 3 of column
+// col = 4 w + r.  Each lane scans its four rows; the totals of the 16 lanes
+// of a DPP row are combined by a Hillis-Steele scan over the row (lane shifts
+// of 1, 2, 4, 8), and every lane adds the total of the lanes before (after)
+// it.  The results go back to A, each element by the lane that read it.  Ends
+// with a barrier.
+template <bool REV>
+__device__ __forceinline__ void col_scan16(float (&x)[4], float* A, int ld, int col, int s) {
+    if (!REV) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i) x[i] += x[i - 1];
+    } else {
+#pragma unroll
+        for (int i = 2; i >= 0; --i) x[i] += x[i + 1];
+    }
+    // exclusive scan of the lane totals: shift by one lane, then an inclusive scan
+    // (lanes shifted in from outside the row read zero)
+    const float tot = REV ? x[0] : x[3];
+    float v;
+    if (!REV) {
+        v = dpp_f<0x111>(tot);  // row_shr:1
+        v += dpp_f<0x111>(v);
+        v += dpp_f<0x112>(v);   // row_shr:2
+        v += dpp_f<0x114>(v);   // row_shr:4
+        v += dpp_f<0x118>(v);   // row_shr:8
+    } else {
+        v = dpp_f<0x101>(tot);  // row_shl:1
+        v += dpp_f<0x101>(v);
+        v += dpp_f<0x102>(v);
+        v += dpp_f<0x104>(v);
+        v += dpp_f<0x108>(v);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[(4 * s + i) * ld + col] = x[i] + v;
+    __syncthreads();
+}
+
 // ----------------------------------------------------------------- host helpers
 // (kda_fwd.hip) Kernel parameters of a call, and the forward recompute used
 // by the backward: intra-chunk (w, u, Aqk and, if p.tm is set, T) then the
