@@ -38,13 +38,14 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
     __shared__ __attribute__((aligned(16))) float KQG[3 * kChunk * kLB];
     __shared__ __attribute__((aligned(16))) float S1[S1F];
     __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
-    __shared__ float bet[kChunk];
+    __shared__ __attribute__((aligned(16))) float bet[kChunk];
     __shared__ float seg[16 * 32];  // column-scan segment totals (4 rows per thread)
     __shared__ float glS[DK];       // exp(G_L)
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
     static_assert(kChunk * LQ <= 3 * kChunk * kLB, "the Aqk staging must fit in KQG");
     static_assert(kI32Threads == 8 * kChunk, "eight threads per token row");
+    static_assert(P != Prec::BF3 || sizeof(TIn) == 2, "the bf16 path has bf16 inputs (v is a bf16 number)");
 
     float* Kb = KQG;
     float* Qb = KQG + kChunk * kLB;
@@ -266,21 +267,23 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
         }
     }
 
-    // ---- pass 2: w = T (beta exp(G) k) and u = T (beta v), one round of three
-    // [32 x 64] operand blocks in KQG
+    // ---- pass 2: w = (T Diag(beta)) (exp(G) k) and u = (T Diag(beta)) v, one round of
+    // three [32 x 64] operand blocks in KQG.  beta is folded into T's columns, so that v
+    // (a bf16 number for bf16 inputs) is an operand as it stands: hi part only, two
+    // MFMAs per k-block for u.
     for (int e = threadIdx.x; e < kChunk * kChunk / 4; e += kI32Threads) {
         const int t = e >> 4, s4 = (e & 15) * 4;
-        Tt.put4(t, s4, (s4 >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&Tm[t * kLD + s4]);
+        const f32x4 tb = *(const f32x4*)&Tm[t * kLD + s4] * *(const f32x4*)&bet[s4];
+        Tt.put4(t, s4, (s4 >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : tb);
     }
     static_assert(3 * kCB32 * LA <= 3 * kChunk * kLB, "three operand blocks must fit in KQG");
     {
-        const float bt = bet[tr];
         const T64 B0(KQG, kCB32), B1(KQG + kCB32 * LA, kCB32), B2(KQG + 2 * kCB32 * LA, kCB32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            B0.put(ch + i, tr, bt * exp2_hw(G[i]) * kx[i]);
-            B1.put(ch + i, tr, bt * (in ? vx[0][i] : 0.f));
-            B2.put(ch + i, tr, bt * (in ? vx[1][i] : 0.f));
+            B0.put(ch + i, tr, exp2_hw(G[i]) * kx[i]);
+            B1.put_hi(ch + i, tr, in ? vx[0][i] : 0.f);
+            B2.put_hi(ch + i, tr, in ? vx[1][i] : 0.f);
         }
     }
     __syncthreads();
@@ -295,7 +298,8 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
         const T64 BTg(KQG + g * kCB32 * LA, kCB32);
         int k0 = 0, k1 = 16 * (tm + 1);
         widen<P>(k0, k1);
-        pacc[g] = mma_tile(Tt.sub(tm * 16), BTg.sub(hf * 16), k0, k1, f32x4{0.f, 0.f, 0.f, 0.f});
+        pacc[g] = g == 0 ? mma_tile(Tt.sub(tm * 16), BTg.sub(hf * 16), k0, k1, f32x4{0.f, 0.f, 0.f, 0.f})
+                         : mma_tile_bh(Tt.sub(tm * 16), BTg.sub(hf * 16), k0, k1, f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();  // pass-2 operand tiles (KQG, S1) consumed
 

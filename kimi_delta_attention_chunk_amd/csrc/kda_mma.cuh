@@ -420,6 +420,31 @@ __device__ __forceinline__ f32x4 mma_tile(const STile<Prec::BF3, CA>& A, const S
     }
     return acc;
 }
+// As mma_tile, for a B tile whose values are bf16 numbers (stored with put_hi):
+// B's lo part is zero and is not read, two MFMAs per k-block.
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile_bh(const STile<Prec::BF3, CA>& A, const STile<Prec::BF3, CB>& B, int k0,
+                                             int k1, f32x4 acc) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int ra = A.r0 + r, rb = B.r0 + r;
+    const int fa = stile_swz<CA>(ra), fb = stile_swz<CB>(rb);
+    for (int k = k0; k < k1; k += 32) {
+        const int j = (k >> 3) + g;
+        const int ao = ra * CA + 8 * (j ^ fa), bo = rb * CB + 8 * (j ^ fb);
+        const bf16x8 ah = *(const bf16x8*)(A.hi + ao);
+        const bf16x8 al = *(const bf16x8*)(A.lo + ao);
+        const bf16x8 bh = *(const bf16x8*)(B.hi + bo);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    }
+    return acc;
+}
+template <int CA, int CB>
+__device__ __forceinline__ f32x4 mma_tile_bh(const STile<Prec::F32, CA>& A, const STile<Prec::F32, CB>& B, int k0,
+                                             int k1, f32x4 acc) {
+    return mma_tile(A.plain(), B.plain(), k0, k1, acc);
+}
 // acc += A(16 x [k0, k0+16)) * B(16 x [k0, k0+16))^T on swizzled tiles, k0 a
 // multiple of 16: a 16-deep product (v_mfma_f32_16x16x16_bf16, three times on the
 // hi/lo split; lane l holds indices k0 + 4 (l >> 4) .. + 3 of row l & 15).

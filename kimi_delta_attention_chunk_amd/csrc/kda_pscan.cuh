@@ -239,16 +239,17 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
             for (int r = 0; r < 4; ++r) dhs[(size_t)(crow + r) * DV + jb + jcol] = D[r];
             DT[buf].put4(jcol, crow, D);
         }
+        // dO is a bf16 number: its hi part alone (the lo part is zero and neither stored nor read)
 #pragma unroll
-        for (int i = 0; i < BV / 4; ++i) OT[buf].put((BV / 4) * part + i, tt, tt < len ? Rc.at(i) : 0.f);
+        for (int i = 0; i < BV / 4; ++i) OT[buf].put_hi((BV / 4) * part + i, tt, tt < len ? Rc.at(i) : 0.f);
         __syncthreads();  // D'^T and dO^T of this chunk complete (the other buffers were read a chunk ago)
         if (owner) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             AFrag<P> fb;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                load_frag(fb, OT[buf].sub(16 * tj), 32 * kb);
-                acc = mma_ff(Rc.qt[kb], fb, acc);
+                load_frag_hi(fb, OT[buf].sub(16 * tj), 32 * kb);
+                acc = mma_ff_bh(Rc.qt[kb], fb, acc);
             }
             load_frag(fb, DT[buf].sub(16 * tj), 0);
             D = mma_ff(Rc.pt, fb, acc);
