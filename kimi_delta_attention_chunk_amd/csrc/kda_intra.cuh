@@ -15,7 +15,8 @@
 //     operands.  Diagonal blocks take the exact exp of each (t, s) difference.
 //   solve: T = (I + Akk)^{-1} (kda_chunk.cuh, fp32).
 //   pass 2: w = T beta exp(G) k  (per channel block) and u = T beta v (per
-//     32-column block of v), as MFMA products.
+//     32-column block of v), as MFMA products; beta is folded into T's columns,
+//     so that v (a bf16 number for bf16 inputs) is an operand as it stands.
 // Outputs (fp32 workspace, slot = chunk * H + head): w [64][DK], u [64][DV],
 // qg = exp(G) q^ [64][DK], khT = (k^ exp(G_L - G))^T [DK][64], gl = exp(G_L)
 // [DK], aqk [64][64] (zero above the diagonal), and T [64][64] if requested.
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
     __shared__ __attribute__((aligned(16))) float KQG[3 * kChunk * kLB];
     __shared__ __attribute__((aligned(16))) float S1[S1F];
     __shared__ __attribute__((aligned(16))) float Tm[kChunk * kLD];
-    __shared__ float bet[kChunk];
+    __shared__ __attribute__((aligned(16))) float bet[kChunk];
     __shared__ float seg[8 * 32];        // column-scan segment totals
     static_assert(kChunk * kLD <= S1F && kChunk * LA <= S1F, "Akk and the T tile must fit in S1");
     static_assert(kCB32 * LA <= 3 * kChunk * kLB, "a BT tile must fit in KQG");
@@ -358,16 +359,18 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         }
     }
 
-    // ---- pass 2: w = T (beta exp(G) k) per channel block, u = T (beta v) per column block,
-    // as many blocks per barrier as fit in KQG
+    // ---- pass 2: w = (T Diag(beta)) (exp(G) k) per channel block, u = (T Diag(beta)) v per
+    // column block (v: hi parts only, two MFMAs per k-block), as many blocks per barrier as
+    // fit in KQG
+    static_assert(P != Prec::BF3 || sizeof(TIn) == 2, "the bf16 path has bf16 inputs (v is a bf16 number)");
     for (int e = threadIdx.x; e < kChunk * kChunk / 4; e += kThreads) {
         const int t = e >> 4, s4 = (e & 15) * 4;
-        Tt.put4(t, s4, (s4 >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&Tm[t * kLD + s4]);
+        const f32x4 tb = *(const f32x4*)&Tm[t * kLD + s4] * *(const f32x4*)&bet[s4];
+        Tt.put4(t, s4, (s4 >> 4) > (t >> 4) ? f32x4{0.f, 0.f, 0.f, 0.f} : tb);
     }
     constexpr int NBLK = NB + NVB;
     constexpr int GRP = (3 * kChunk * kLB) / (kCB32 * LA);  // blocks per round
     static_assert(GRP >= 1, "one operand block must fit in KQG");
-    const float bt = bet[tr];
     float* wo = p.w + slot * kChunk * DK;
     float* uo = p.u + slot * kChunk * DV;
 #pragma unroll
@@ -379,9 +382,10 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             if (b < NBLK) {
                 const T64 BTg(KQG + g * kCB32 * LA, kCB32);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    BTg.put(8 * part + i, tr, b < NB ? bt * exp2_hw(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]
-                                                     : bt * (in ? vx[b < NB ? 0 : b - NB][i] : 0.f));
+                for (int i = 0; i < 8; ++i) {
+                    if (b < NB) BTg.put(8 * part + i, tr, exp2_hw(G[b < NB ? b : 0][i]) * kx[b < NB ? b : 0][i]);
+                    else BTg.put_hi(8 * part + i, tr, in ? vx[b < NB ? 0 : b - NB][i] : 0.f);
+                }
             }
         }
         __syncthreads();
@@ -397,7 +401,8 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
             int k0 = 0, k1 = 16 * (tm + 1);
             widen<P>(k0, k1);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
+            acc = b < NB ? mma_tile(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc)
+                         : mma_tile_bh(Tt.sub(tm * 16), BTg.sub(tn * 16), k0, k1, acc);
             if (rev_ops && b < NB) {  // w^T rows c, tokens as indices: four consecutive t per lane
                 const int t0 = tm * 16 + frag_row(0), cw = b * kCB32 + tn * 16 + frag_col();
                 store_frag4<WP>(frag_rec(p.wT + slot * DK * kChunk, cw, t0 >> 5, 2), cw, acc, t0 & 31);
