@@ -42,6 +42,25 @@ namespace kda {
 
 constexpr int kBcThreads = 512, kBcWaves = 8;
 
+// Staging of T's values as loaded (fp32, or with bf16 inputs the hi/lo split
+// words of tpk_load4_split carried as raw bits): four consecutive values of a
+// row, or value m of such a group.
+template <int C>
+__device__ __forceinline__ void put_t4(const STile<Prec::F32, C>& T, int r, int k, f32x4 x) { T.put4(r, k, x); }
+template <int C>
+__device__ __forceinline__ void put_t4(const STile<Prec::BF3, C>& T, int r, int k, f32x4 x) {
+    const tpk_words w = __builtin_bit_cast(tpk_words, x);
+    T.put4_split(r, k, u32x2v{w[0], w[1]}, u32x2v{w[2], w[3]});
+}
+template <int C>
+__device__ __forceinline__ void put_t1(const STile<Prec::F32, C>& T, int r, int k, f32x4 x, int m) { T.put(r, k, x[m]); }
+template <int C>
+__device__ __forceinline__ void put_t1(const STile<Prec::BF3, C>& T, int r, int k, f32x4 x, int m) {
+    const tpk_words w = __builtin_bit_cast(tpk_words, x);
+    const int sh = 16 * (m & 1);
+    T.put_split(r, k, (uint16_t)(w[m >> 1] >> sh), (uint16_t)(w[2 + (m >> 1)] >> sh));
+}
+
 template <int DV, typename TIn, typename TOut, Prec P>
 __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
     constexpr int NTH = kBcThreads, NW = kBcWaves;
@@ -166,7 +185,10 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
             const int e4 = 4 * (tid + NTH * i);
-            Tr[i] = tpk_load4(tpk, e4 >> 6, e4 & 63);
+            if constexpr (P == Prec::BF3)  // (the hi/lo split words, kept as raw bits)
+                Tr[i] = __builtin_bit_cast(f32x4, tpk_load4_split(tpk, e4 >> 6, e4 & 63));
+            else
+                Tr[i] = tpk_load4(tpk, e4 >> 6, e4 & 63);
         }
 #pragma unroll
         for (int i = 0; i < NH4; ++i) { Hr[i] = h4[tid + NTH * i]; Dr[i] = d4[tid + NTH * i]; }
@@ -260,7 +282,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
             const int e4 = 4 * (tid + NTH * i);
-            TRW.put4(e4 >> 6, e4 & 63, Tr[i]);
+            put_t4(TRW, e4 >> 6, e4 & 63, Tr[i]);
         }
 #pragma unroll
         for (int i = 0; i < NH4; ++i) {  // h and D' rows c, columns j .. j + 3 -> h^T, D'^T [j][c]
@@ -342,7 +364,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         const int e4 = 4 * (tid + NTH * i);
         const int s = e4 >> 6, t = e4 & 63;  // T[s][t .. t+3]
 #pragma unroll
-        for (int m = 0; m < 4; ++m) TT.put(t + m, s, Tr[i][m]);
+        for (int m = 0; m < 4; ++m) put_t1(TT, t + m, s, Tr[i], m);
     }
     // [64 x 32] results: wave w owns tile (w >> 1, w & 1); [64 x 64]: tiles w, w + 8 -> (tile >> 2, tile & 3)
     const int am = wave >> 1, an = wave & 1;
@@ -548,7 +570,7 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
 #pragma unroll
         for (int i = 0; i < NT4; ++i) {
             const int e4 = 4 * (tid + NTH * i);
-            Trow.put4(e4 >> 6, e4 & 63, Tr[i]);
+            put_t4(Trow, e4 >> 6, e4 & 63, Tr[i]);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

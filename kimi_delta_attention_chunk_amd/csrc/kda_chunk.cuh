@@ -87,6 +87,15 @@ __device__ __forceinline__ f32x4 tpk_load4(const float* T, int t, int s) {
     const f32x4 x = *(const f32x4*)(T + tpk_index(t, upper ? t : s));
     return upper ? f32x4{0.f, 0.f, 0.f, 0.f} : x;
 }
+// With bf16 inputs the dk = 32 kernels keep each group of four values in the
+// packed form as its bf16 hi/lo split (the operand form of every product T
+// enters): words (hi 0-1, hi 2-3, lo 0-1, lo 2-3), 16 bytes as in fp32.
+typedef uint32_t tpk_words __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ tpk_words tpk_load4_split(const float* T, int t, int s) {
+    const bool upper = (s >> 4) > (t >> 4);
+    const tpk_words x = *(const tpk_words*)(T + tpk_index(t, upper ? t : s));
+    return upper ? tpk_words{0u, 0u, 0u, 0u} : x;  // (the split of zeros is zero)
+}
 
 // T = (I + A)^{-1} for strictly lower-triangular A (64x64, stride kLD), by
 // 16x16 blocks: diagonal blocks by forward substitution, then the off-diagonal

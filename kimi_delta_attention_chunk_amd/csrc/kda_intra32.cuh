@@ -263,7 +263,15 @@ __global__ void __launch_bounds__(kI32Threads, 2) intra32_kernel(Prm p) {  // tw
         for (int e = threadIdx.x; e < kTPacked / 4; e += kI32Threads) {
             const int b = e >> 6, I = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3)), J = b - I * (I + 1) / 2;
             const int t = 16 * I + ((e & 63) >> 2), s = 16 * J + 4 * (e & 3);
-            to[e] = *(const f32x4*)&Tm[t * kLD + s];
+            const f32x4 x = *(const f32x4*)&Tm[t * kLD + s];
+            if constexpr (P == Prec::BF3) {  // stored as its hi/lo split (tpk_load4_split)
+                const float v[4] = {x[0], x[1], x[2], x[3]};
+                u32x2v hw, lw;
+                split4(v, hw, lw);
+                *(tpk_words*)&to[e] = tpk_words{hw[0], hw[1], lw[0], lw[1]};
+            } else {
+                to[e] = x;
+            }
         }
     }
 

@@ -362,6 +362,18 @@ template <int C> struct STile<Prec::BF3, C> {
         *(u32x2v*)(hi + o) = h;
         *(u32x2v*)(lo + o) = l;
     }
+    // Values already split: four (k a multiple of 4) as two words each of hi and lo
+    // parts, or one as its two halves.
+    __device__ __forceinline__ void put4_split(int r, int k, u32x2v h, u32x2v l) const {
+        const int o = at(r, k);
+        *(u32x2v*)(hi + o) = h;
+        *(u32x2v*)(lo + o) = l;
+    }
+    __device__ __forceinline__ void put_split(int r, int k, uint16_t h, uint16_t l) const {
+        const int o = at(r, k);
+        *(uint16_t*)(hi + o) = h;
+        *(uint16_t*)(lo + o) = l;
+    }
     // Values that are bf16 numbers (bf16 inputs): the lo part is zero and is
     // neither stored nor read (load_frag_hi, mma_ff_ah / mma_ff_bh).
     __device__ __forceinline__ void put_hi(int r, int k, float x) const { hi[at(r, k)] = (__bf16)x; }
