@@ -658,12 +658,6 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
         // [c][t] = k_t e^{G_t - G_{a(t)}} and q_t e^{..}, a(t) the first row of t's block
         const T64 KxT(ph + 18432, DK), QxT(ph + 20480, DK);
         static_assert(20480 + 2048 <= PH, "P4 tiles must fit (bf16 hi/lo tiles)");
-        float gend[4], gst[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            gend[i] = Gs[(16 * (tr >> 4) + 15) * LR + 4 * part + i];
-            gst[i] = Gs[(16 * (tr >> 4)) * LR + 4 * part + i];
-        }
         __syncthreads();  // P3 tiles consumed
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -685,13 +679,26 @@ __global__ void __launch_bounds__(kBcThreads) bwd_chunk_kernel(Prm p) {
             bdAT.put4(s, 16 * tm + frag_row(0), bd);
             dAqT.put4(s, 16 * tm + frag_row(0), aAq[i]);
         }
+        {
+            // channel c, tokens t0 .. t0 + 3 of one 16-token block, read down the columns of
+            // the fp32 rows (odd stride: no bank conflicts), so that each tile row takes four
+            // consecutive tokens in one store
+            static_assert(NTH == DK * kChunk / 4, "one four-token group per thread");
+            const int c = tid & 31, t0 = 4 * (tid >> 5), b0 = t0 & ~15;
+            const float gend = Gs[(b0 + 15) * LR + c], gst = Gs[b0 * LR + c];
+            f32x4 kc4, kx4, qx4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int cc = 4 * part + i;
-            KcT.put(cc, tr, kx[i] * exp2_hw(gend[i] - G[i]));
-            const float e = exp2_hw(G[i] - gst[i]);
-            KxT.put(cc, tr, kx[i] * e);
-            QxT.put(cc, tr, qx[i] * e);
+            for (int m = 0; m < 4; ++m) {
+                const int t = t0 + m;
+                const float g = Gs[t * LR + c], kv = Ks[t * LR + c], qv = Qs[t * LR + c];
+                kc4[m] = kv * exp2_hw(gend - g);
+                const float e = exp2_hw(g - gst);
+                kx4[m] = kv * e;
+                qx4[m] = qv * e;
+            }
+            KcT.put4(c, t0, kc4);
+            KxT.put4(c, t0, kx4);
+            QxT.put4(c, t0, qx4);
         }
         __syncthreads();
         {
