@@ -45,7 +45,7 @@ struct DhFrags {
 };
 
 // Operands of chunk slot `slot` and dO of the chunk `crd` (the one processed
-// next, or a clamped repeat).  Every load is unconditional.
+// next, or a clamped repeat).
 template <int DK, int DV, int BV, typename TIn, Prec P>
 __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRef& crd, int h, int jb,
                                         DhFrags<DK, BV, P>& R) {
@@ -57,16 +57,20 @@ __device__ __forceinline__ void dh_load(const Prm& p, size_t slot, const ChunkRe
     const char* qt = (const char*)(p.qgT + slot * DK * kChunk);      // [c][2]
     const char* wt = (const char*)(p.wT + slot * DK * kChunk);       // [c][2]
     const int row = 16 * tm + lr;
+    // A wave loads only the fragments its own products use (the conditions are
+    // wave-uniform): the operand bytes each CU fetches per chunk bound this pass.
+    if (wave < F::VT) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) load_afrag(R.aq[kb], frag_rec(aq, row, kb, 2));
+        for (int kb = 0; kb < 2; ++kb) load_afrag(R.aq[kb], frag_rec(aq, row, kb, 2));
 #pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb) load_afrag(R.kh[kb], frag_rec(kh, row, kb, F::KB));
+        for (int kb = 0; kb < F::KB; ++kb) load_afrag(R.kh[kb], frag_rec(kh, row, kb, F::KB));
+    }
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kDhWaves * i;
         const int c16 = 16 * ((tile < F::TH ? tile : 0) / F::TN);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {  // (a wave without a D tile reads tile 0's: a branch here costs more)
             load_afrag(R.qt[i][kb], frag_rec(qt, c16 + lr, kb, 2));
             load_afrag(R.wt[i][kb], frag_rec(wt, c16 + lr, kb, 2));
         }

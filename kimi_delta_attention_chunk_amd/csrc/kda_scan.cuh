@@ -67,11 +67,11 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
         load_afrag(R.x[kb], frag_rec(xs, row, kb, F::KB));
         if constexpr (!F::SPLIT) load_afrag(R.q[kb], frag_rec(q, row, kb, F::KB));
     }
-    // Every load below is unconditional (a wave without a state tile reads
-    // tile 0's operands, unused; Aqk's second block is read even where it is
-    // zero), so the batch has the same size on every wave and path.
+    // A wave loads only the fragments its own products use (the conditions are
+    // wave-uniform): the operand bytes each CU fetches per chunk bound this pass.
+    // Aqk: the output waves, only its blocks below the diagonal.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) if (kb <= (tm >> 1)) load_afrag(R.a[kb], frag_rec(a, row, kb, 2));
+    for (int kb = 0; kb < 2; ++kb) if (F::forms_out(wave) && kb <= (tm >> 1)) load_afrag(R.a[kb], frag_rec(a, row, kb, 2));
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
@@ -83,7 +83,7 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     }
     const float* u = p.u + slot * kChunk * DV + jb;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) R.u[r] = u[(size_t)(tm * 16 + frag_row(r)) * DV + tn * 16 + frag_col()];
+    for (int r = 0; r < 4; ++r) if (F::forms_vnew(wave)) R.u[r] = u[(size_t)(tm * 16 + frag_row(r)) * DV + tn * 16 + frag_col()];
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
