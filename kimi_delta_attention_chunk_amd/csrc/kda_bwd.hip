@@ -258,51 +258,30 @@ __device__ __forceinline__ void put_qk_block(const QkBlock<NTH>& r, const float*
     }
 }
 
-// The log-decay (or the raw gate input f) of channels [cb, cb + kCB): thread
+// The in-chunk cumulative log-decay G of channels [cb, cb + kCB), in base 2 as
+// the intra-chunk kernel formed and saved it (flat past the chunk end, so every
+// decay factor between a row and a later reference row stays at most 1): thread
 // (sg, c) = (tid >> 5, tid & 31) holds R consecutive tokens of channel c.
 template <int NTH>
 struct GBlock {
     static constexpr int R = kChunk * kCB / NTH;
     float x[R];
-    float db;  // dt_bias of the channel (gate flag)
 };
 template <int DK, int NTH>
-__device__ __forceinline__ void load_g_block(const Prm& p, const ChunkRef& cr, int h, int cb, GBlock<NTH>& r) {
+__device__ __forceinline__ void load_g_block(const Prm& p, size_t slot, int cb, GBlock<NTH>& r) {
+    constexpr int R = GBlock<NTH>::R;
+    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    const float* gs = p.gcs + slot * kChunk * DK + cb + c;
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.x[i] = gs[(size_t)(R * sg + i) * DK];
+}
+// GT[c][t] = G; ends with a barrier.
+template <int NTH>
+__device__ __forceinline__ void put_g_block(const GBlock<NTH>& r, float* GT) {
     constexpr int R = GBlock<NTH>::R;
     const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int t = R * sg + i;
-        r.x[i] = p.g[tok_index(cr.t0 + (t < cr.len ? t : 0), h, p.H, DK) + cb + c];
-    }
-    r.db = (p.flags & 2u) ? p.dt_bias[h * DK + cb + c] : 0.f;
-}
-// GT[c][t] = in-chunk cumulative log-decay in base 2 (G log2 e; the gate from f
-// if flagged; zero past the chunk end), so a decay factor is one exp2.  Thread (sg, c) scans its R tokens in registers and adds
-// the totals of the earlier segments (seg: LDS [64 / R][32]).  Two barriers;
-// ends with one.
-template <int NTH>
-__device__ __forceinline__ void put_g_block(const Prm& p, const ChunkRef& cr, int h, const GBlock<NTH>& r, float* GT,
-                                            float* seg) {
-    constexpr int R = GBlock<NTH>::R, NS = kChunk / R;
-    const bool gate = p.flags & 2u;
-    const int c = threadIdx.x & 31, sg = threadIdx.x >> 5;
-    const float nA = gate ? -expf(p.A_log[h]) : 0.f;
-    float x[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int t = R * sg + i;
-        x[i] = t < cr.len ? (gate ? nA * softplus_f(r.x[i] + r.db) : r.x[i]) * kLog2e : 0.f;  // base 2
-    }
-#pragma unroll
-    for (int i = 1; i < R; ++i) x[i] += x[i - 1];
-    seg[sg * 32 + c] = x[R - 1];
-    __syncthreads();
-    float off = 0.f;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) off += j < sg ? seg[j * 32 + c] : 0.f;
-#pragma unroll
-    for (int i = 0; i < R; ++i) GT[c * kLD + R * sg + i] = x[i] + off;
+    for (int i = 0; i < R; ++i) GT[c * kLD + R * sg + i] = r.x[i];
     __syncthreads();
 }
 
@@ -348,7 +327,6 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     __shared__ float dbA[kChunk], dotq[kChunk], dotk[kChunk];
     __shared__ float pa_part[kGWaves * NB];
     __shared__ float dgl[DK];
-    __shared__ float gseg[kChunk * kCB / (kChunk * kCB / kGThreads)];  // column-scan segment totals
 
     const int c = blockIdx.x, h = blockIdx.y;
     const ChunkRef cr = p.seq.chunk(c);
@@ -406,7 +384,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
         }
     };
     load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, 0, kr);
-    load_g_block<DK, kGThreads>(p, cr, h, 0, gr);
+    load_g_block<DK, kGThreads>(p, slot, 0, gr);
     load_dw(0);
     if (l2) {
         row_rnorm<DK, TIn, kGThreads>(qin, cr, h, p.H, rnq);
@@ -419,14 +397,14 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
         put_qk_block<kGThreads>(kr, l2 ? rnk : nullptr, KTb);
-        put_g_block<kGThreads>(p, cr, h, gr, GTb, gseg);  // its barriers cover KTb
+        put_g_block<kGThreads>(gr, GTb);  // its barrier covers KTb
         if (b + 1 < NB) {
             load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
-            load_g_block<DK, kGThreads>(p, cr, h, cb + kCB, gr);
+            load_g_block<DK, kGThreads>(p, slot, cb + kCB, gr);
         } else {  // the first block of the pair-sum phase
             load_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, 0, qr);
             load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, 0, kr);
-            load_g_block<DK, kGThreads>(p, cr, h, 0, gr);
+            load_g_block<DK, kGThreads>(p, slot, 0, gr);
         }
 #pragma unroll
         for (int e_i = 0; e_i < NE; ++e_i) {
@@ -544,11 +522,11 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
             load4<float>(p.g + grow, f_r);
             load4<float>(p.dt_bias + h * DK + cb + c4, db_r);
         }
-        put_g_block<kGThreads>(p, cr, h, gr, GTb, gseg);  // ends with a barrier
+        put_g_block<kGThreads>(gr, GTb);  // ends with a barrier
         if (b + 1 < NB) {
             load_qk_block<DK, TIn, kGThreads>(qin, cr, h, p.H, cb + kCB, qr);
             load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
-            load_g_block<DK, kGThreads>(p, cr, h, cb + kCB, gr);
+            load_g_block<DK, kGThreads>(p, slot, cb + kCB, gr);
         }
         // -- off-diagonal row and column sums: the scaled operands of both, then both products
 #pragma unroll
@@ -849,7 +827,7 @@ static hipError_t launch_bwd_t(const ChunkArgs& a, hipStream_t s) {
             return hipErrorInvalidValue;
     } else {
         // the reverse scan's operands (written by the intra-chunk kernel) and its outputs
-        if (!p.tm || !p.hs || !p.vn || !p.dhs || !p.dvn || !p.aqT || !p.khb || !p.qgT || !p.wT)
+        if (!p.tm || !p.hs || !p.vn || !p.dhs || !p.dvn || !p.aqT || !p.khb || !p.qgT || !p.wT || !p.gcs)
             return hipErrorInvalidValue;
     }
     if (!(a.flags & (1u << 4))) {  // no forward saved in ws: recompute it

@@ -57,6 +57,7 @@ struct Prm {
     float *w, *u, *aqk, *tm, *hs, *vn;   // forward recompute (tm only for the backward)
     float *qg, *khT, *gl;                // exp(G) q, (k exp(G_L - G))^T, exp(G_L)
     float *qgT, *khb, *wT;               // (exp(G) q)^T, k exp(G_L - G), w^T: the reverse scan (dk >= 64)
+    float* gcs;                          // in-chunk cumulative log-decay G (base 2, [t][c]) for the dk-side kernel (dk >= 64)
     float *dhs, *dvn;                    // backward state pass
     float *dqt, *dkh, *dwv, *daq, *dtv, *dgl, *dbv;
     float *dkt, *dxq, *dxk, *part_a, *part_dt;

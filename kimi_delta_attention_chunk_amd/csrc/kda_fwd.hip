@@ -39,7 +39,7 @@ Prm make_prm(const ChunkArgs& a, const WsLayout& L) {
     p.w = at(L.w);
     p.u = at(L.u); p.aqk = at(L.aqk); p.tm = at(L.tm); p.hs = at(L.hs); p.vn = at(L.vn);
     p.qg = at(L.qg); p.khT = at(L.khT); p.gl = at(L.gl);
-    p.qgT = at(L.qgT); p.khb = at(L.khb); p.wT = at(L.wT);
+    p.qgT = at(L.qgT); p.khb = at(L.khb); p.wT = at(L.wT); p.gcs = at(L.gcs);
     p.dhs = at(L.dhs); p.dvn = at(L.dvn);
     p.dqt = at(L.dqt); p.dkh = at(L.dkh); p.dwv = at(L.dwv); p.daq = at(L.daq); p.dtv = at(L.dtv);
     p.dgl = at(L.dgl); p.dbv = at(L.dbv);
@@ -98,6 +98,7 @@ WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec, void* ctx) {
         take(L.qgT, slots * C * dk);
         take(L.khb, slots * C * dk);
         take(L.wT, slots * C * dk);
+        take(L.gcs, slots * C * dk);
         take(L.dhs, slots * dk * dv);
         take(L.dvn, slots * C * dv);
         take(L.dqt, slots * C * dk);

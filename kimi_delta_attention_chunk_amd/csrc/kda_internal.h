@@ -93,6 +93,7 @@ struct WsLayout {
     size_t w, u, aqk, tm, hs, vn;                    // forward recompute
     size_t qg, khT, gl;                              // per-chunk operands of the scan
     size_t qgT, khb, wT;                             // transposed operands of the reverse scan (dk >= 64)
+    size_t gcs;                                      // in-chunk cumulative log-decay (dk >= 64 backward)
     size_t dhs, dvn;                                 // backward state pass
     size_t dqt, dkh, dwv, daq, dtv, dgl, dbv;        // dv-side intermediates
     size_t dkt, dxq, dxk, part_a, part_dt;           // dk-side intermediates

@@ -193,6 +193,11 @@ __global__ void __launch_bounds__(kThreads, 2) intra_kernel(Prm p) {  // two wor
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) G[b][i] = Gb[tr * kLB + 8 * part + i];
+        if (p.gcs) {  // the backward's dk-side kernel reads G instead of forming it again
+            f32x4* gd = (f32x4*)(p.gcs + (slot * kChunk + tr) * DK + cb + 8 * part);
+            gd[0] = f32x4{G[b][0], G[b][1], G[b][2], G[b][3]};
+            gd[1] = f32x4{G[b][4], G[b][5], G[b][6], G[b][7]};
+        }
         // G at the reference rows 16 I and at the last row come straight from the scanned tile
         // scaled operands for the off-diagonal Gram blocks, exp(G) q, k exp(G_L - G)
         {
