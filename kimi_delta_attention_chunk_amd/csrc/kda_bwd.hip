@@ -230,31 +230,33 @@ constexpr int kCB = 32;  // channels per block in the dk-side kernel
 
 // Channel blocks [cb, cb + kCB) are staged in two steps, so that a block's
 // global loads can be issued one block ahead: load_* brings this thread's
-// values into registers (zero past the chunk end), put_* writes them to LDS.
+// values into registers as they are stored in memory, put_* converts them and
+// writes them to LDS.  (A conversion or mask right after a load would make the
+// compiler wait for that load there, a block early.)
 // q or k: thread element e = tid + NTH i is (token e / kCB, channel e % kCB).
-template <int NTH>
+template <int NTH, typename TIn>
 struct QkBlock {
-    float x[kChunk * kCB / NTH];
+    TIn x[kChunk * kCB / NTH];
 };
 template <int DK, typename TIn, int NTH>
 __device__ __forceinline__ void load_qk_block(const TIn* __restrict__ src, const ChunkRef& cr, int h, int H, int cb,
-                                              QkBlock<NTH>& r) {
+                                              QkBlock<NTH, TIn>& r) {
 #pragma unroll
     for (int i = 0; i < kChunk * kCB / NTH; ++i) {
         const int e = threadIdx.x + i * NTH;
-        const int t = e / kCB, cc = e - t * kCB;
-        const float x = Elem<TIn>::load(src, tok_index(cr.t0 + (t < cr.len ? t : 0), h, H, DK) + cb + cc);
-        r.x[i] = t < cr.len ? x : 0.f;
+        const int t = e / kCB, cc = e - t * kCB;  // rows past the chunk end read row 0, zeroed in put_qk_block
+        r.x[i] = src[tok_index(cr.t0 + (t < cr.len ? t : 0), h, H, DK) + cb + cc];
     }
 }
-// XT[c][t] = x (times the row's inverse norm if `rn` is given)
-template <int NTH>
-__device__ __forceinline__ void put_qk_block(const QkBlock<NTH>& r, const float* rn, float* XT) {
+// XT[c][t] = x (times the row's inverse norm if `rn` is given; zero past the chunk end)
+template <int NTH, typename TIn>
+__device__ __forceinline__ void put_qk_block(const QkBlock<NTH, TIn>& r, int len, const float* rn, float* XT) {
 #pragma unroll
     for (int i = 0; i < kChunk * kCB / NTH; ++i) {
         const int e = threadIdx.x + i * NTH;
         const int t = e / kCB, cc = e - t * kCB;
-        XT[cc * kLD + t] = rn ? r.x[i] * rn[t] : r.x[i];
+        const float x = t < len ? Elem<TIn>::cvt(r.x[i]) : 0.f;
+        XT[cc * kLD + t] = rn ? x * rn[t] : x;
     }
 }
 
@@ -370,7 +372,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     if (threadIdx.x < DK) dgl[threadIdx.x] = p.dgl[slot * DK + threadIdx.x];
     __syncthreads();
     // channel block 0 of k, the log-decay and dw, for phase 3
-    QkBlock<kGThreads> qr, kr;
+    QkBlock<kGThreads, TIn> qr, kr;
     GBlock<kGThreads> gr;
     constexpr int NE = kChunk * kCB / kGThreads;
     float dwr[NE];
@@ -396,7 +398,7 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     // (each block's global loads are issued during the block before)
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        put_qk_block<kGThreads>(kr, l2 ? rnk : nullptr, KTb);
+        put_qk_block(kr, cr.len, l2 ? rnk : nullptr, KTb);
         put_g_block<kGThreads>(gr, GTb);  // its barrier covers KTb
         if (b + 1 < NB) {
             load_qk_block<DK, TIn, kGThreads>(kin, cr, h, p.H, cb + kCB, kr);
@@ -505,8 +507,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dk_kernel(Prm p) {
     static_assert(2 * kChunk * LS <= kChunk * kLD && kChunk * LS <= kChunk * LC, "pair-sum staging must fit");
     for (int b = 0; b < NB; ++b) {
         const int cb = b * kCB;
-        put_qk_block<kGThreads>(qr, l2 ? rnq : nullptr, QTb);
-        put_qk_block<kGThreads>(kr, l2 ? rnk : nullptr, KTb);
+        put_qk_block(qr, cr.len, l2 ? rnq : nullptr, QTb);
+        put_qk_block(kr, cr.len, l2 ? rnk : nullptr, KTb);
         // this lane's epilogue operands (token t = lane, channels cb + CPW wave .. + CPW - 1, one
         // 16-byte access per array), issued now so that they arrive during the pair sums
         constexpr int CPW = kCB / kGWaves;

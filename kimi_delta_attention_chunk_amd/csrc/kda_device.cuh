@@ -44,10 +44,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+    __device__ __forceinline__ static float cvt(float x) { return x; }  // a value as loaded, to fp32
     __device__ __forceinline__ static void store(float* p, size_t i, float x) { p[i] = x; }
 };
 template <> struct Elem<uint16_t> {
     __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+    __device__ __forceinline__ static float cvt(uint16_t x) { return bf16_to_f32(x); }
     __device__ __forceinline__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
