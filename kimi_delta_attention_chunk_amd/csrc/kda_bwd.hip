@@ -142,29 +142,55 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
     const int tt = tid / (VB / 4), j4 = 4 * (tid % (VB / 4));  // token block: (token, 4 columns)
     const bool tin = tt < cr.len;
     const size_t tok = tok_index(cr.t0 + (tin ? tt : 0), h, p.H, DV);
+    // One block's global values for this thread, as loaded: the next block's loads
+    // are issued once this block is staged, so that they arrive during its products
+    // (converted or masked right after the load, a value would be waited for there).
+    using Raw4 = typename std::conditional<std::is_same<TIn, uint16_t>::value, u32x2v, f32x4>::type;
+    struct Blk {
+        f32x4 xh[HQ], xd[HQ], xn, xdn;
+        Raw4 xo, xv;
+    };
+    auto load_blk = [&](int jb, Blk& B) {
+#pragma unroll
+        for (int i = 0; i < HQ; ++i) {
+            const int e4 = tid + i * kGThreads;
+            const int cc = e4 / (VB / 4), q4 = 4 * (e4 % (VB / 4));
+            B.xh[i] = *(const f32x4*)(hs + cc * DV + jb + q4);
+            B.xd[i] = *(const f32x4*)(dhs + cc * DV + jb + q4);
+        }
+        B.xo = *(const Raw4*)(dO + tok + jb + j4);
+        B.xv = *(const Raw4*)(vin + tok + jb + j4);
+        B.xn = *(const f32x4*)(vn + tt * DV + jb + j4);
+        B.xdn = *(const f32x4*)(dvn + tt * DV + jb + j4);
+    };
+    auto raw_at = [](const Raw4& x, int r) -> float {
+        if constexpr (std::is_same<TIn, uint16_t>::value) {
+            const uint32_t w = x[r >> 1];
+            return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            return x[r];
+        }
+    };
+    Blk B;
+    load_blk(0, B);
     for (int jb = 0; jb < DV; jb += VB) {
         __syncthreads();  // the previous block's readers are done
 #pragma unroll
         for (int i = 0; i < HQ; ++i) {
             const int e4 = tid + i * kGThreads;
             const int cc = e4 / (VB / 4), q4 = 4 * (e4 % (VB / 4));
-            const f32x4 xh = *(const f32x4*)(hs + cc * DV + jb + q4);
-            const f32x4 xd = *(const f32x4*)(dhs + cc * DV + jb + q4);
+            const f32x4 xh = B.xh[i], xd = B.xd[i];
             Hs.put4(cc, q4, xh);
             Ds.put4(cc, q4, xd);
             hd[i] += xh[0] * xd[0] + xh[1] * xd[1] + xh[2] * xd[2] + xh[3] * xd[3];
         }
         {
-            float xo[4], xv[4];
-            load4<TIn>(dO + tok + jb + j4, xo);
-            load4<TIn>(vin + tok + jb + j4, xv);
-            const f32x4 xn = *(const f32x4*)(vn + tt * DV + jb + j4);
-            const f32x4 xdn = *(const f32x4*)(dvn + tt * DV + jb + j4);
+            const f32x4 xn = B.xn, xdn = B.xdn;
             f32x4 o4, v4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                o4[r] = tin ? xo[r] : 0.f;
-                v4[r] = tin ? xv[r] : 0.f;
+                o4[r] = tin ? raw_at(B.xo, r) : 0.f;
+                v4[r] = tin ? raw_at(B.xv, r) : 0.f;
                 DVT.put(j4 + r, tt, xdn[r]);
             }
             DOs.put4_hi(tt, j4, o4);
@@ -172,6 +198,8 @@ __global__ void __launch_bounds__(kGThreads) bwd_dv_kernel(Prm p) {
             VNs.put4(tt, j4, xn);
             DVNs.put4(tt, j4, xdn);
         }
+        // the next block (past the last one: the last again, unused), with no branch around the loads
+        load_blk(jb + VB < DV ? jb + VB : jb, B);
         __syncthreads();
         tiles_mma<true, false>(aQ, DOs, Hs, 0, VB);
         tiles_mma<false, false>(aKh, VNs, Ds, 0, VB);
