@@ -8,10 +8,10 @@
 // offsets the window resets at every document start):
 //   z[t, c] = sum_{i < W} w[c, i] x[t - (W-1) + i, c]   (same document only)
 //             + bias[c];        y = z, or SiLU(z) with KDA_CONV_SILU.
-// Thread (channel group of 8, run of kConvRun tokens): the window of the last
+// Thread (channel group of 8, 4 in the backward; run of kConvRun tokens): the window of the last
 // W inputs (and, in the backward, of the last W dz values) slides through the
 // run in registers, so each input row is read once plus a W - 1 row halo.
-// Loads are 16 bytes per lane along the channel axis (coalesced token rows).
+// Loads are 16 bytes per lane (8 in the backward) along the channel axis (coalesced token rows).
 // The backward forms dz = dy * act'(z) on the fly; dx is the anti-causal
 // correlation of dz with w; dw and dbias are summed per run, then over the
 // runs of a workgroup in LDS, then over the workgroups by a fixed tree
@@ -34,6 +34,8 @@ constexpr int kOpsThreads = 256;
 constexpr int kConvRun = 16;          // tokens per thread
 constexpr int kConvCG = 32;           // channel groups (of 8) per workgroup
 constexpr int kConvRuns = kOpsThreads / kConvCG;  // runs per workgroup
+constexpr int kBwdCPT = 4;            // channels per thread in the backward (8 in the forward): its
+                                      // windows of x and dz and its dw partials then fit four waves per SIMD
 
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 __device__ __forceinline__ float dsilu_f(float z) {
@@ -136,15 +138,15 @@ __global__ void __launch_bounds__(kOpsThreads) conv_fwd_kernel(ConvArgs a) {
 
 template <int W, typename TIn, typename TOut, bool SILU>
 __global__ void __launch_bounds__(kOpsThreads) conv_bwd_kernel(ConvArgs a) {
-    __shared__ float red[kConvRuns][kConvCG][(W + 1) * 8 + 1];
+    __shared__ float red[kConvRuns][kConvCG][(W + 1) * kBwdCPT + 1];
     const int cl = threadIdx.x % kConvCG, rl = threadIdx.x / kConvCG;
     const int cg = blockIdx.x * kConvCG + cl;
     const int run = blockIdx.y * kConvRuns + rl;
     const int rpr = (a.T + kConvRun - 1) / kConvRun;
-    const bool active = cg * 8 < a.D && run < a.B * rpr;
-    float dwp[W][8], dbp[8];
+    const bool active = cg * kBwdCPT < a.D && run < a.B * rpr;
+    float dwp[W][kBwdCPT], dbp[kBwdCPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kBwdCPT; ++j) {
         dbp[j] = 0.f;
 #pragma unroll
         for (int i = 0; i < W; ++i) dwp[i][j] = 0.f;
@@ -152,26 +154,26 @@ __global__ void __launch_bounds__(kOpsThreads) conv_bwd_kernel(ConvArgs a) {
     if (active) {
         const int b = run / rpr, t0 = (run % rpr) * kConvRun;
         const int t1 = t0 + kConvRun < a.T ? t0 + kConvRun : a.T;
-        const int c0 = cg * 8;
+        const int c0 = cg * kBwdCPT;
         const size_t rowoff = (size_t)b * a.T * a.D + c0;
         const TIn* x = (const TIn*)a.x + rowoff;
         const TIn* dy = (const TIn*)a.dy + rowoff;
         TOut* dx = (TOut*)a.dx + rowoff;
-        float w[W][8], bias[8];
+        float w[W][kBwdCPT], bias[kBwdCPT];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kBwdCPT; ++j) {
 #pragma unroll
             for (int i = 0; i < W; ++i) w[i][j] = a.w[(size_t)(c0 + j) * W + i];
             bias[j] = a.bias ? a.bias[c0 + j] : 0.f;
         }
         // windows over positions p - (W-1) .. p: inputs (with their documents) and dz
-        float xw[W][8], zw[W][8];
+        float xw[W][kBwdCPT], zw[W][kBwdCPT];
         int xd[W];
 #pragma unroll
         for (int i = 0; i < W; ++i) {
             xd[i] = -1;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xw[i][j] = zw[i][j] = 0.f;
+            for (int j = 0; j < kBwdCPT; ++j) xw[i][j] = zw[i][j] = 0.f;
         }
         DocCursor dc;
         dc.start(a.cu, a.N, a.T, t0 - (W - 1));
@@ -183,74 +185,74 @@ __global__ void __launch_bounds__(kOpsThreads) conv_bwd_kernel(ConvArgs a) {
             for (int i = 0; i < W - 1; ++i) {
                 xd[i] = xd[i + 1];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < kBwdCPT; ++j) {
                     xw[i][j] = xw[i + 1][j];
                     zw[i][j] = zw[i + 1][j];
                 }
             }
             xd[W - 1] = dp;
-            if (dp >= 0) load8<TIn>(x + (size_t)p * a.D, xw[W - 1]);
+            if (dp >= 0) load4<TIn>(x + (size_t)p * a.D, xw[W - 1]);
             // dz at p, for p in [t0, t1 + W - 1): the window then holds x[p - (W-1) .. p]
-            float dz[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float dz[kBwdCPT] = {};
             if (k >= W - 1 && dp >= 0 && p < t1 + W - 1) {
-                load8<TIn>(dy + (size_t)p * a.D, dz);
+                load4<TIn>(dy + (size_t)p * a.D, dz);
                 if (SILU) {
-                    float z[8];
+                    float z[kBwdCPT];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) z[j] = bias[j];
+                    for (int j = 0; j < kBwdCPT; ++j) z[j] = bias[j];
 #pragma unroll
                     for (int i = 0; i < W; ++i) {
                         const bool same = xd[i] == dp;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) z[j] = fmaf(w[i][j], same ? xw[i][j] : 0.f, z[j]);
+                        for (int j = 0; j < kBwdCPT; ++j) z[j] = fmaf(w[i][j], same ? xw[i][j] : 0.f, z[j]);
                     }
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) dz[j] *= dsilu_f(z[j]);
+                    for (int j = 0; j < kBwdCPT; ++j) dz[j] *= dsilu_f(z[j]);
                 }
                 if (p < t1) {  // this run's own positions: dw and dbias
 #pragma unroll
                     for (int i = 0; i < W; ++i) {
                         const bool same = xd[i] == dp;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) dwp[i][j] = fmaf(dz[j], same ? xw[i][j] : 0.f, dwp[i][j]);
+                        for (int j = 0; j < kBwdCPT; ++j) dwp[i][j] = fmaf(dz[j], same ? xw[i][j] : 0.f, dwp[i][j]);
                     }
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) dbp[j] += dz[j];
+                    for (int j = 0; j < kBwdCPT; ++j) dbp[j] += dz[j];
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) zw[W - 1][j] = dz[j];
+            for (int j = 0; j < kBwdCPT; ++j) zw[W - 1][j] = dz[j];
             // dx at s = p - (W-1): sum_i w[i] dz[s + lag_i], lag_i = W-1-i, same document as s
             const int s = p - (W - 1);
             if (s >= t0 && s < t1 && xd[0] >= 0) {
-                float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                float g[kBwdCPT] = {};
 #pragma unroll
                 for (int i = 0; i < W; ++i) {
                     const bool same = xd[W - 1 - i] == xd[0];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) g[j] = fmaf(w[i][j], same ? zw[W - 1 - i][j] : 0.f, g[j]);
+                    for (int j = 0; j < kBwdCPT; ++j) g[j] = fmaf(w[i][j], same ? zw[W - 1 - i][j] : 0.f, g[j]);
                 }
-                store8<TOut>(dx + (size_t)s * a.D, g);
+                store4<TOut>(dx + (size_t)s * a.D, g);
             }
         }
     }
     // dw, dbias: this workgroup's runs in LDS, summed in a fixed order
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kBwdCPT; ++j) {
 #pragma unroll
-        for (int i = 0; i < W; ++i) red[rl][cl][i * 8 + j] = dwp[i][j];
-        red[rl][cl][W * 8 + j] = dbp[j];
+        for (int i = 0; i < W; ++i) red[rl][cl][i * kBwdCPT + j] = dwp[i][j];
+        red[rl][cl][W * kBwdCPT + j] = dbp[j];
     }
     __syncthreads();
-    constexpr int NV = kConvCG * (W + 1) * 8;  // partial values of this workgroup
+    constexpr int NV = kConvCG * (W + 1) * kBwdCPT;  // partial values of this workgroup
     for (int e = threadIdx.x; e < NV; e += kOpsThreads) {
-        const int c = e / ((W + 1) * 8), v = e % ((W + 1) * 8);
+        const int c = e / ((W + 1) * kBwdCPT), v = e % ((W + 1) * kBwdCPT);
         float s = 0.f;
 #pragma unroll
         for (int r = 0; r < kConvRuns; ++r) s += red[r][c][v];
-        const int ch = (blockIdx.x * kConvCG + c) * 8 + (v & 7);
+        const int ch = (blockIdx.x * kConvCG + c) * kBwdCPT + v % kBwdCPT;
         if (ch < a.D) {
-            const int i = v >> 3;  // tap, or W for the bias
+            const int i = v / kBwdCPT;  // tap, or W for the bias
             a.part[((size_t)blockIdx.y * a.D + ch) * (W + 1) + i] = s;
         }
     }
@@ -304,7 +306,8 @@ static hipError_t conv_launch(const ConvArgs& a, bool backward, hipStream_t s) {
         KDA_LAUNCH("conv_fwd", (conv_fwd_kernel<W, TIn, TOut, SILU>), grid, dim3(kOpsThreads), s, a);
         return hipSuccess;
     }
-    KDA_LAUNCH("conv_bwd", (conv_bwd_kernel<W, TIn, TOut, SILU>), grid, dim3(kOpsThreads), s, a);
+    const dim3 gridb((a.D / kBwdCPT + kConvCG - 1) / kConvCG, grid.y);
+    KDA_LAUNCH("conv_bwd", (conv_bwd_kernel<W, TIn, TOut, SILU>), gridb, dim3(kOpsThreads), s, a);
     KDA_LAUNCH("conv_wsum", (conv_wsum_kernel<W>), dim3(a.D * (W + 1)), dim3(kOpsThreads), s, a, (int)grid.y);
     return hipSuccess;
 }
