@@ -202,7 +202,7 @@ def test_bwd_packed_config_row():
 
 
 @pytest.mark.parametrize("dtype,dims", [(torch.bfloat16, (32, 64)), (torch.float32, (32, 64)),
-                                        (torch.bfloat16, (128, 128))])
+                                        (torch.bfloat16, (128, 128)), (torch.float32, (64, 64))])
 def test_bwd_from_saved_forward_equals_recompute(dtype, dims):
     """kda_fwd(save_for_bwd) + kda_bwd(fwd_saved) gives bitwise the same gradients as a
     backward that recomputes the forward, and the same forward outputs."""
