@@ -262,7 +262,7 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
              float* h, void* o, kda_stream_t stream);
 
 /* ----------------------------------------------------------------------------
- * Context parallelism, dk = 32, dv = 64 (the one-GPU part of splitting a long
+ * Context parallelism, every supported (dk, dv) (the one-GPU part of splitting a long
  * row over devices; the pages pack documents instead -- Packing PR -- and show
  * no context parallelism for KDA).  A chunk maps the state entering it
  * affinely to the state leaving it, so a segment of chunks does too:
@@ -271,7 +271,7 @@ int kda_step(int32_t B, int32_t H, int32_t dk, int32_t dv, kda_dtype dtype, kda_
  *   of the call: the product of its chunks' transition matrices, first chunk
  *   rightmost (the identity for an empty one).  Inputs and flags as kda_fwd
  *   (no h0); ws of at least kda_fwd_workspace(desc) bytes.
- * kda_state_scan: chains R segments, H heads (dk = 32, dv = 64 only):
+ * kda_state_scan: chains R segments, H heads ((dk, dv) as kda_fwd supports):
  *   transpose = 0:  x = x0 (nullable = 0); for r = 0 .. R-1: x_in[r] = x; x = M_r x + c_r
  *   transpose = 1:  x = x0; for r = R-1 .. 0: x_in[r] = x; x = M_r^T x + c_r
  *   x_out (nullable) receives the final x.  M [R,H,dk,dk], c, x_in [R,H,dk,dv],

@@ -485,7 +485,7 @@ def gnorm_bwd(o, gate, weight, dy, eps=RMS_EPS, *, out_dtype=None, workspace=Non
     return out
 
 
-# ---------------------------------------------------------------- context parallelism (dk = 32)
+# ---------------------------------------------------------------- context parallelism
 def segment_maps(q, k, v, g, beta, cu_seqlens=None, plan=None, *, A_log=None, dt_bias=None, l2norm_qk=False,
                  gate_in_kernel=False, beta_logits=False, workspace=None, fwd_saved=False):
     """kda_segment_maps: the state-transition matrix M [N,H,dk,dk] of every sequence or packed

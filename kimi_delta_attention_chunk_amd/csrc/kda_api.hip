@@ -365,8 +365,6 @@ int kda_segment_maps(const kda_desc* desc, const void* q, const void* k, const v
     kda::ChunkArgs a;
     int rc = make_args(desc, cu_seqlens, chunk_indices, chunk_offsets, a);
     if (rc) return rc;
-    if (desc->dk != 32 || desc->dv != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "segment maps need dk = 32, dv = 64 (got %d, %d)", desc->dk, desc->dv);
     if (desc->flags & (KDA_F_SAVE_FOR_BWD | KDA_F_DH0_ONLY)) return fail(KDA_ERR_INVALID, "flag does not apply");
     if ((rc = check_common_inputs(desc, q, k, v, g, beta, A_log, dt_bias, nullptr))) return rc;
     if ((rc = check_ptr(M, "M", true))) return rc;
@@ -385,7 +383,8 @@ int kda_state_scan(int32_t R, int32_t H, int32_t dk, int32_t dv, int32_t transpo
                    const float* x0, float* x_in, float* x_out, kda_stream_t stream) {
     g_err[0] = 0;
     if (R < 1 || H < 1) return fail(KDA_ERR_INVALID, "bad sizes R=%d H=%d", R, H);
-    if (dk != 32 || dv != 64) return fail(KDA_ERR_UNSUPPORTED, "state scan needs dk = 32, dv = 64 (got %d, %d)", dk, dv);
+    if (!((dk == 32 && dv == 64) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128)))
+        return fail(KDA_ERR_UNSUPPORTED, "state scan needs (dk, dv) in (32, 64), (64, 64), (128, 128) (got %d, %d)", dk, dv);
     if (transpose != 0 && transpose != 1) return fail(KDA_ERR_INVALID, "transpose must be 0 or 1");
     int rc;
     if ((rc = check_ptr(M, "M", true)) || (rc = check_ptr(c, "c", true)) || (rc = check_ptr(x0, "x0", false)) ||

@@ -1,4 +1,5 @@
-// kda_cp.hip -- the building blocks of context parallelism for dk = 32: the
+// kda_cp.hip -- the building blocks of context parallelism (the maps for dk = 32
+// here; for dk = dv >= 64 the forward state pass forms them, kda_scan.cuh): the
 // affine map of a segment of chunks, and the short scan that chains segments.
 //
 // A chunk maps the state entering it to the state leaving it affinely,
@@ -165,7 +166,107 @@ __global__ void __launch_bounds__(kThreads) state_scan_kernel(int R, int H, int 
     }
 }
 
+// The same chain for dk = dv in {64, 128}: one workgroup of eight waves per
+// (head, 32 columns of X); wave w holds the D fragments of X's tiles in row block
+// 16 tm (tm = w at dk = 128, with both column tiles; w >> 1 at dk = 64, column
+// tile w & 1).  A (dk x dk) is too large to stage per segment, so each lane
+// reads its rows of A straight from memory as fp32 MFMA A operands, four
+// consecutive k at once: step e of k-block kb takes k = 16 kb + 4 g + e from lane
+// group g, for A and for X alike (any assignment of k to steps gives the same
+// sum).  X^T sits in double-buffered LDS ([column][k], one barrier per segment);
+// the next segment's A and c are in flight while the current one is applied.
+constexpr int kWideThreads = 512;
+template <int DK, bool TR>
+__global__ void __launch_bounds__(kWideThreads) state_scan_wide_kernel(int R, int H, const float* __restrict__ M,
+                                                                      const float* __restrict__ c,
+                                                                      const float* __restrict__ x0,
+                                                                      float* __restrict__ out,
+                                                                      float* __restrict__ xfinal) {
+    constexpr int DV = DK, BV = 32, TPW = DK / 64, KB = DK / 16, LX = DK + 4, PD = 2;
+    static_assert((DK == 64 || DK == 128) && kWideThreads == 512, "two or one tiles per wave, eight waves");
+    __shared__ __attribute__((aligned(16))) float sX[2][BV * LX];  // X^T [column][k]
+    const int h = blockIdx.x, jb = blockIdx.y * BV;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int tm = TPW == 2 ? wave : wave >> 1;  // this wave's row block
+    const int tn0 = TPW == 2 ? 0 : (wave & 1);   // its first column tile
+    const int row0 = 16 * tm + 4 * lg;           // this lane's four rows of X (D fragment)
+    const int arow = 16 * tm + lr;               // and its row of A (A fragment)
+    f32x4 X[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int col = jb + 16 * (tn0 + t) + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[t][i] = x0 ? x0[((size_t)h * DK + row0 + i) * DV + col] : 0.f;
+    }
+    f32x4 areg[PD][KB], creg[PD][TPW];
+    auto seg_of = [&](int s) { return (size_t)(TR ? R - 1 - s : s) * H + h; };
+    auto fetch = [&](int s, int slot) {  // A and c of the s-th segment in scan order (past the end: the last)
+        const size_t seg = seg_of(s < R ? s : R - 1);
+        const float* Ms = M + seg * DK * DK;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if constexpr (TR) {  // A = M^T: A[arow][k] = M[k][arow]
+#pragma unroll
+                for (int e = 0; e < 4; ++e) areg[slot][kb][e] = Ms[(size_t)(16 * kb + 4 * lg + e) * DK + arow];
+            } else {
+                areg[slot][kb] = *(const f32x4*)(Ms + (size_t)arow * DK + 16 * kb + 4 * lg);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) creg[slot][t][i] = c[(seg * DK + row0 + i) * DV + jb + 16 * (tn0 + t) + lr];
+    };
+    auto step = [&](int s, int slot) {
+        const int b = s & 1;
+        const size_t seg = seg_of(s);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int cl = 16 * (tn0 + t) + lr;
+            *(f32x4*)&sX[b][cl * LX + row0] = X[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(seg * DK + row0 + i) * DV + jb + cl] = X[t][i];
+        }
+        // One barrier per segment: buffer b was last read in step s - 2, and every
+        // thread passed step s - 1's barrier after finishing that step.
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int cl = 16 * (tn0 + t) + lr;
+            f32x4 acc = creg[slot][t];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const f32x4 xv = *(const f32x4*)&sX[b][cl * LX + 16 * kb + 4 * lg];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(areg[slot][kb][e], xv[e], acc, 0, 0, 0);
+            }
+            X[t] = acc;
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < PD; ++i) fetch(i, i);
+    int s = 0;
+    for (; s + PD <= R; s += PD) {
+#pragma unroll
+        for (int i = 0; i < PD; ++i) {
+            step(s + i, i);
+            fetch(s + i + PD, i);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PD - 1; ++i)
+        if (s + i < R) step(s + i, i);
+    if (xfinal) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xfinal[((size_t)h * DK + row0 + i) * DV + jb + 16 * (tn0 + t) + lr] = X[t][i];
+    }
+}
+
 hipError_t launch_segment_maps(const ChunkArgs& a, float* M, hipStream_t s) {
+    if (a.dk != 32) return launch_segmaps_wide(a, M, s);  // dk = dv >= 64: the direct form's state pass
     // (the forward arrays lead both layouts, so a saved forward's P is read at the same offset)
     const Prm p = make_prm(a, ws_layout(a, false));
     if (!(a.flags & (1u << 4))) {  // not KDA_F_FWD_SAVED: form the chunks' P first
@@ -181,6 +282,21 @@ hipError_t launch_segment_maps(const ChunkArgs& a, float* M, hipStream_t s) {
 
 hipError_t launch_state_scan(int R, int H, int dk, int dv, bool transpose, const float* M, const float* c,
                              const float* x0, float* out, float* xfinal, hipStream_t s) {
+    if ((dk == 64 || dk == 128) && dv == dk) {
+        const dim3 grid(H, dv / 32);
+        if (dk == 64) {
+            if (transpose)
+                KDA_LAUNCH("state_scan", (state_scan_wide_kernel<64, true>), grid, dim3(kWideThreads), s, R, H, M, c, x0, out, xfinal);
+            else
+                KDA_LAUNCH("state_scan", (state_scan_wide_kernel<64, false>), grid, dim3(kWideThreads), s, R, H, M, c, x0, out, xfinal);
+        } else {
+            if (transpose)
+                KDA_LAUNCH("state_scan", (state_scan_wide_kernel<128, true>), grid, dim3(kWideThreads), s, R, H, M, c, x0, out, xfinal);
+            else
+                KDA_LAUNCH("state_scan", (state_scan_wide_kernel<128, false>), grid, dim3(kWideThreads), s, R, H, M, c, x0, out, xfinal);
+        }
+        return hipSuccess;
+    }
     if (dk != 32 || dv % 32 != 0) return hipErrorInvalidValue;
     KDA_LAUNCH("state_scan", state_scan_kernel<32>, dim3(H, dv / 32), dim3(kThreads), s, R, H, dv, transpose ? 1 : 0,
                M, c, x0, out, xfinal);

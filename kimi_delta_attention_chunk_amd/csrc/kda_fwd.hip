@@ -188,6 +188,39 @@ hipError_t launch_recompute_intra(const Prm& p, const ChunkArgs& a, hipStream_t 
     return hipSuccess;
 }
 
+// The transition map M of every sequence at dk = dv >= 64 (context parallelism):
+// the intra-chunk kernel (unless the workspace holds a saved forward), then the
+// forward state pass in its SEGMAP mode, which runs the chunks' transitions from
+// the identity and writes M where the final state would go.
+template <int DK, typename TIn>
+static hipError_t launch_segmaps_t(Prm p, const ChunkArgs& a, float* M, bool saved, hipStream_t s) {
+    constexpr Prec P = std::is_same<TIn, uint16_t>::value ? Prec::BF3 : Prec::F32;
+    if (!p.w || !p.khT || !p.gl) return hipErrorInvalidValue;
+    if (!saved && a.n_chunks_bound > 0)
+        KDA_LAUNCH("fwd_intra", (intra_kernel<DK, DK, TIn, P>), dim3(a.n_chunks_bound, a.H), dim3(kThreads), s, p);
+    p.hT = M;
+    p.h0 = nullptr;
+    p.o = nullptr;
+    p.hs = nullptr;
+    p.vn = nullptr;
+    constexpr int BV = 16;  // as the forward pass at dk >= 64
+    const int total = a.N * a.H * (DK / BV);
+    KDA_LAUNCH("seg_map", (fwd_scan_kernel<DK, DK, BV, float, P, true>), dim3(total), dim3(kScanThreads), s, p, total,
+               0, 0);
+    return hipSuccess;
+}
+
+hipError_t launch_segmaps_wide(const ChunkArgs& a, float* M, hipStream_t s) {
+    const Prm p = make_prm(a, ws_layout(a, false));
+    const bool saved = a.flags & (1u << 4);  // KDA_F_FWD_SAVED: the forward arrays lead both layouts
+    if (a.dk == 64 && a.dv == 64)
+        return a.in_bf16 ? launch_segmaps_t<64, uint16_t>(p, a, M, saved, s) : launch_segmaps_t<64, float>(p, a, M, saved, s);
+    if (a.dk == 128 && a.dv == 128)
+        return a.in_bf16 ? launch_segmaps_t<128, uint16_t>(p, a, M, saved, s)
+                         : launch_segmaps_t<128, float>(p, a, M, saved, s);
+    return hipErrorInvalidValue;
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_fwd_t(const ChunkArgs& a, hipStream_t s) {
     const bool save = a.flags & (1u << 3), saved = a.flags & (1u << 4);

@@ -106,6 +106,7 @@ typedef void (*WsRecord)(void* ctx, const char* name, size_t offset, size_t byte
 WsLayout ws_layout(const ChunkArgs& a, bool backward, WsRecord rec = nullptr, void* ctx = nullptr);
 
 bool dims_supported(int dk, int dv);
+hipError_t launch_segmaps_wide(const ChunkArgs& a, float* M, hipStream_t s);  // dk = dv >= 64
 hipError_t launch_fwd(const ChunkArgs& a, hipStream_t s);
 
 // Opt-in per-kernel timing (kda_timing.hip): a pair of hipEvents around a launch.

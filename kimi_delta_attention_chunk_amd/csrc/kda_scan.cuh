@@ -51,7 +51,7 @@ struct ScanFrags {
     __device__ __forceinline__ static bool forms_out(int wave) { return !SPLIT || wave >= VT; }
 };
 
-template <int DK, int DV, int BV, Prec P>
+template <int DK, int DV, int BV, Prec P, bool SEGMAP>
 __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, ScanFrags<DK, BV, P>& R) {
     using F = ScanFrags<DK, BV, P>;
     const int wave = wave_id(), lr = threadIdx.x & 15;
@@ -83,7 +83,10 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     }
     const float* u = p.u + slot * kChunk * DV + jb;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) if (F::forms_vnew(wave)) R.u[r] = u[(size_t)(tm * 16 + frag_row(r)) * DV + tn * 16 + frag_col()];
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (SEGMAP) R.u[r] = 0.f;  // (u = 0: the recurrence applies the transitions alone)
+        else if (F::forms_vnew(wave)) R.u[r] = u[(size_t)(tm * 16 + frag_row(r)) * DV + tn * 16 + frag_col()];
+    }
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
@@ -95,8 +98,12 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     }
 }
 
-template <int DK, int DV, int BV, typename TOut, Prec P>
+// SEGMAP: the transition map of every sequence instead (dv = dk): from h = I with
+// u = 0 the recurrence gives M = P_last ... P_first, P = Diag(exp G_L) - Kh^T w,
+// written to p.hT; nothing else is written.
+template <int DK, int DV, int BV, typename TOut, Prec P, bool SEGMAP = false>
 __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total_wg, int write_o, int store_states) {
+    static_assert(!SEGMAP || DK == DV, "a transition map is dk x dk");
     using F = ScanFrags<DK, BV, P>;
     constexpr int LK = DK + 8, LA = kChunk + 8, NV = DV / BV, TN = F::TN;
     constexpr int TH = F::TH, HPW = F::HPW, NWV = kScanWaves;
@@ -124,7 +131,8 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int cc = tmh * 16 + frag_row(r);
-                S[i][r] = p.h0 ? p.h0[((size_t)nh * DK + cc) * DV + jb + j] : 0.f;
+                if constexpr (SEGMAP) S[i][r] = cc == jb + j ? 1.f : 0.f;
+                else S[i][r] = p.h0 ? p.h0[((size_t)nh * DK + cc) * DV + jb + j] : 0.f;
             }
             hT0.put4(j, tmh * 16 + frag_row(0), S[i]);
         }
@@ -213,14 +221,14 @@ __global__ void __launch_bounds__(kScanThreads) fwd_scan_kernel(Prm p, int total
         // (scheduling barriers keep the batches in issue order: the waits count
         // completions in order)
 #pragma unroll
-        for (int i = 0; i < PD; ++i) scan_load<DK, DV, BV, P>(p, slot_of(c0 + i), jb, R[i]);
+        for (int i = 0; i < PD; ++i) scan_load<DK, DV, BV, P, SEGMAP>(p, slot_of(c0 + i), jb, R[i]);
         __builtin_amdgcn_sched_barrier(0);
         for (int c = c0; c < c1; c += PD) {
 #pragma unroll
             for (int i = 0; i < PD; ++i)
                 if (i == 0 || c + i < c1) {
                     step(c + i, R[i]);
-                    scan_load<DK, DV, BV, P>(p, slot_of(c + i + PD), jb, R[i]);
+                    scan_load<DK, DV, BV, P, SEGMAP>(p, slot_of(c + i + PD), jb, R[i]);
                 }
         }
     }

@@ -177,15 +177,18 @@ def test_gnorm_rejects(rows, dv, eps, code):
 # ---------------------------------------------------------------- context parallelism
 def test_segment_maps_and_state_scan_reject():
     lib = kda.load_library()
-    d = _desc(dk=64, dv=64)
+    d = _desc(dk=64, dv=128)  # not a supported pair
     rc = lib.kda_segment_maps(ctypes.byref(d), *([_fake(1)] * 5), None, None, None, None, None, _fake(2), _fake(3),
                               1 << 30, None)
     assert rc == B.KDA_ERR_UNSUPPORTED, lib.kda_last_error()
-    d = _desc()
-    rc = lib.kda_segment_maps(ctypes.byref(d), *([_fake(1)] * 5), None, None, None, None, None, _fake(2), _fake(3),
-                              16, None)
-    assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
-    assert lib.kda_state_scan(4, 2, 64, 64, 0, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_UNSUPPORTED
+    for dk, dv in ((32, 64), (64, 64), (128, 128)):  # every supported pair: the workspace is checked
+        d = _desc(dk=dk, dv=dv)
+        rc = lib.kda_segment_maps(ctypes.byref(d), *([_fake(1)] * 5), None, None, None, None, None, _fake(2),
+                                  _fake(3), 16, None)
+        assert rc == B.KDA_ERR_WORKSPACE, lib.kda_last_error()
+    for dk, dv in ((64, 128), (128, 64), (32, 32)):
+        assert lib.kda_state_scan(4, 2, dk, dv, 0, _fake(1), _fake(2), None, _fake(3), None, None) == \
+            B.KDA_ERR_UNSUPPORTED
     assert lib.kda_state_scan(0, 2, 32, 64, 0, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
     assert lib.kda_state_scan(4, 2, 32, 64, 2, _fake(1), _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID
     assert lib.kda_state_scan(4, 2, 32, 64, 0, None, _fake(2), None, _fake(3), None, None) == B.KDA_ERR_INVALID

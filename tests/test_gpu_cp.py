@@ -1,4 +1,4 @@
-"""Context parallelism on one GPU (dk = 32): one long document split into segments
+"""Context parallelism on one GPU (every supported dk, dv): one long document split into segments
 that run independently, chained by their transition matrices (kda_segment_maps,
 kda_state_scan), and rerun with their true entering states / end gradients,
 reproduces the single pass over the whole document (the oracle's), forward and
@@ -60,10 +60,25 @@ def _cp_run(d, scale, cu, backward):
     return o, hT, gr
 
 
+DIMS = [(32, 64), (64, 64), (128, 128)]
+
+
+def _row(dk):
+    """Row length and its aligned / ragged segment offsets (shorter rows at the larger
+    heads keep the oracle's fp64 pass to seconds)."""
+    T = 2048 if dk == 32 else 1024
+    q = T // 4
+    return T, {"aligned": [0, q, 2 * q, 3 * q, T], "ragged": [0, 300, q + 300, q + 301, T]}
+
+
+@pytest.mark.parametrize("dims", DIMS, ids=["dk32", "dk64", "dk128"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
-@pytest.mark.parametrize("cu", [[0, 512, 1024, 1536, 2048], [0, 300, 1100, 1101, 2048]], ids=["aligned", "ragged"])
-def test_context_parallel_equals_single_pass(dtype, cu):
-    T, H, dk, dv = 2048, 4, 32, 64
+@pytest.mark.parametrize("split", ["aligned", "ragged"])
+def test_context_parallel_equals_single_pass(dtype, split, dims):
+    dk, dv = dims
+    T, cus = _row(dk)
+    cu = cus[split]
+    H = 4
     inp, _ = prepared(11, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, upstream=True, dhT=True)
     d = to_dev(inp, "cuda:0")
     scale = dk ** -0.5
@@ -78,12 +93,15 @@ def test_context_parallel_equals_single_pass(dtype, cu):
     check_close("dh0", gr["dh0"][None], gref["dh0"], dtype)
 
 
+@pytest.mark.parametrize("dims", DIMS, ids=["dk32", "dk64", "dk128"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
-def test_context_parallel_from_saved_forward(dtype):
+def test_context_parallel_from_saved_forward(dtype, dims):
     """The scheme with the chunk quantities formed once: same results as the plain one,
     bit for bit, and as the oracle's single pass."""
-    T, H, dk, dv = 2048, 4, 32, 64
-    cu = [0, 300, 1100, 1101, 2048]
+    dk, dv = dims
+    T, cus = _row(dk)
+    cu = cus["ragged"]
+    H = 4
     inp, _ = prepared(13, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, upstream=True, dhT=True)
     d = to_dev(inp, "cuda:0")
     scale = dk ** -0.5
@@ -100,12 +118,14 @@ def test_context_parallel_from_saved_forward(dtype):
     check_close("dh0", g2["dh0"][None], gref["dh0"], dtype)
 
 
-def test_segment_map_of_one_document_is_its_state_map():
+@pytest.mark.parametrize("dims", DIMS, ids=["dk32", "dk64", "dk128"])
+def test_segment_map_of_one_document_is_its_state_map(dims):
     """M h0 + hT(h0 = 0) = hT(h0) for every document of a packed row, and an empty
     document's map is the identity."""
     lens = [700, 0, 1, 64, 1283]
     cu = np.cumsum([0] + lens).tolist()
-    T, H, dk, dv = cu[-1], 2, 32, 64
+    dk, dv = dims
+    T, H = cu[-1], 2
     inp, _ = prepared(12, 1, T, H, dk, dv, torch.float32, weak=True, h0_std=0.1, n_states=len(lens))
     d = to_dev(inp, "cuda:0")
     cuc = torch.tensor(cu, dtype=torch.int32, device="cuda")
