@@ -480,14 +480,16 @@ def long_document_workload(dev, T=65536, H=8, dk=32, dv=64, seg=1024, reps=5, se
 
 
 def other_workloads(dev):
-    """The decode step, the packed 65,536-token row, the dk = dv = 128 heads, and the
-    short convolution and gated output norm of the layer."""
+    """The decode step, the packed 65,536-token row, the dk = dv = 128 heads, one long
+    document (dk = 32 and dk = dv = 128) in one pass and segment-parallel, and the short
+    convolution and gated output norm of the layer."""
     return layer_ops_workload(dev) + [
         decode_workload(dev),
         fwd_bwd_workload("KDA fwd+bwd, one packed row of 65536 tokens (geometric document lengths, "
                          "mean 512), per-document h0 and dhT", dev, 1, 65536, 8, 32, 64, 3, packed=True),
         fwd_bwd_workload("KDA fwd+bwd, larger heads: B=2 T=8192 H=16 dk=dv=128", dev, 2, 8192, 16, 128, 128, 4),
         long_document_workload(dev),
+        long_document_workload(dev, T=16384, H=16, dk=128, dv=128, seg=1024),
     ]
 
 
