@@ -64,14 +64,16 @@ __device__ __forceinline__ void scan_load(const Prm& p, size_t slot, int jb, Sca
     const int row = 16 * tm + lr;
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb) {
-        load_afrag(R.x[kb], frag_rec(xs, row, kb, F::KB));
-        if constexpr (!F::SPLIT) load_afrag(R.q[kb], frag_rec(q, row, kb, F::KB));
+        // (SEGMAP: no output, so the output waves' exp(G) q is not loaded)
+        if (!SEGMAP || F::forms_vnew(wave)) load_afrag(R.x[kb], frag_rec(xs, row, kb, F::KB));
+        if constexpr (!F::SPLIT && !SEGMAP) load_afrag(R.q[kb], frag_rec(q, row, kb, F::KB));
     }
     // A wave loads only the fragments its own products use (the conditions are
     // wave-uniform): the operand bytes each CU fetches per chunk bound this pass.
     // Aqk: the output waves, only its blocks below the diagonal.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) if (F::forms_out(wave) && kb <= (tm >> 1)) load_afrag(R.a[kb], frag_rec(a, row, kb, 2));
+    for (int kb = 0; kb < 2; ++kb)
+        if (!SEGMAP && F::forms_out(wave) && kb <= (tm >> 1)) load_afrag(R.a[kb], frag_rec(a, row, kb, 2));
 #pragma unroll
     for (int i = 0; i < F::HPW; ++i) {
         const int tile = wave + kScanWaves * i;
