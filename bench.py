@@ -369,29 +369,41 @@ def decode_workload(dev, steps=1000, B=256, H=8, dk=32, dv=64, seed=2):
     # a stack of layers: each layer's output is the next layer's v (written straight into
     # it), every (token, layer) step in one graph; each layer has its own state, so the
     # stack's states (L x 16.8 MB) no longer stay in the Infinity Cache between steps
-    L, lsteps = 12, 32
-    hs = [h.clone() for _ in range(L)]
-    outs = [torch.empty((lsteps, B, H, dv), dtype=bf, device=dev) for _ in range(L)]
+    # (12 layers, 201 MB, partly; 24 layers, 403 MB, not at all: each step streams its
+    # state from HBM)
+    def stack_us(L, lsteps):
+        hs = [h.clone() for _ in range(L)]
+        outs = [torch.empty((lsteps, B, H, dv), dtype=bf, device=dev) for _ in range(L)]
 
-    def stack():
-        for t in range(lsteps):
-            for l in range(L):
-                vin = v[t] if l == 0 else outs[l - 1][t]
-                kda.step(q[t], k[t], vin, f[t], b[t], hs[l], scale, out=outs[l][t], **flags)
+        def stack():
+            for t in range(lsteps):
+                for l in range(L):
+                    vin = v[t] if l == 0 else outs[l - 1][t]
+                    kda.step(q[t], k[t], vin, f[t], b[t], hs[l], scale, out=outs[l][t], **flags)
 
-    stack()
-    torch.cuda.synchronize()
-    lgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(lgraph):
         stack()
-    lper = timed_ms(lgraph.replay, 5, warm=1) * 1e3 / (L * lsteps)
+        torch.cuda.synchronize()
+        lgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(lgraph):
+            stack()
+        us = timed_ms(lgraph.replay, 5, warm=1) * 1e3 / (L * lsteps)
+        del lgraph, hs, outs
+        return us
+
+    L, lsteps = 12, 32
+    lper = stack_us(L, lsteps)
+    L2, lsteps2 = 24, 16
+    lper2 = stack_us(L2, lsteps2)
     return {"workload": "kda_step decode: B=%d H=%d dk=%d dv=%d, %d steps in one HIP graph" % (B, H, dk, dv, steps),
             "us_per_step": per, "tokens_per_s": B / (per * 1e-6), "algorithmic_bytes_per_step": nbytes,
             "effective_GBs": nbytes / (per * 1e-6) / 1e9, "frac_of_8TBs": nbytes / (per * 1e-6) / 1e9 / PEAK_HBM_GBS,
             "roofline_us": nbytes / (PEAK_HBM_GBS * 1e9) * 1e6, "cold_step_us": cold[len(cold) // 2],
             "layer_stack": {"layers": L, "tokens": lsteps, "us_per_layer_step": lper,
                             "effective_GBs": nbytes / (lper * 1e-6) / 1e9,
-                            "frac_of_8TBs": nbytes / (lper * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+                            "frac_of_8TBs": nbytes / (lper * 1e-6) / 1e9 / PEAK_HBM_GBS},
+            "layer_stack_from_hbm": {"layers": L2, "tokens": lsteps2, "us_per_layer_step": lper2,
+                                     "effective_GBs": nbytes / (lper2 * 1e-6) / 1e9,
+                                     "frac_of_8TBs": nbytes / (lper2 * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
 
 def layer_ops_workload(dev, B=16, T=2048, H=8, dk=32, dv=64, W=4, reps=20):
