@@ -140,15 +140,19 @@ def test_segment_map_of_one_document_is_its_state_map(dims):
     assert torch.equal(M[1], torch.eye(dk, device="cuda").expand(H, dk, dk))
 
 
+@pytest.mark.parametrize("dims", DIMS, ids=["dk32", "dk64", "dk128"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
-def test_context_parallel_packed_row_of_two_documents(dtype):
+def test_context_parallel_packed_row_of_two_documents(dtype, dims):
     """A packed row of two documents, each cut into segments (three, and two with a
     one-token segment); the segments run as one packed row, each document's chain is
     scanned on its own from its own h0 / dhT, and the result equals the oracle's pass
     over the two-document row."""
-    T, H, dk, dv = 2200, 4, 32, 64
-    docs = [0, 1500, 2200]
-    seg = [0, 512, 1100, 1500, 1501, 2200]
+    dk, dv = dims
+    H = 4
+    if dk == 32:
+        T, docs, seg = 2200, [0, 1500, 2200], [0, 512, 1100, 1500, 1501, 2200]
+    else:
+        T, docs, seg = 1100, [0, 750, 1100], [0, 256, 550, 750, 751, 1100]
     chains = [(0, 3), (3, 5)]  # the segments of each document
     inp, _ = prepared(14, 1, T, H, dk, dv, dtype, weak=True, h0_std=0.1, n_states=2, upstream=True, dhT=True)
     d = to_dev(inp, "cuda:0")
