@@ -62,6 +62,12 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
     __shared__ __attribute__((aligned(16))) float sH[2][BV * LK];
     static_assert(STile<Prec::F32, DK>::ld == LK, "tile footprint");
     const STile<P, DK> HT[2] = {STile<P, DK>(sH[0], BV), STile<P, DK>(sH[1], BV)};
+    // the chunk's output rows, staged so that they leave as 16-byte words (double buffered
+    // like h^T: chunk c's rows are written after the barrier of chunk c and stored after
+    // the barrier of chunk c + 1); rows padded by 16 bytes
+    constexpr int OE = 16 / (int)sizeof(TOut), OLD = BV + OE, OWR = BV / OE;
+    static_assert(kChunk * OWR % kPsThreads == 0, "whole 16-byte words per thread");
+    __shared__ __attribute__((aligned(16))) TOut sO[WO ? 2 : 1][WO ? kChunk * OLD : OE];
 
     const int lid = xcd_local_id(blockIdx.x, total_wg);
     const int jbk = lid % NV, nh = lid / NV;
@@ -104,9 +110,23 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
             }
         }
     };
+    // the staged rows of chunk c (buffer `buf`) to o; rows past the chunk end, and every row
+    // when `valid` is false, go to p.sink
+    auto flush_o = [&](int c, int buf, bool valid) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const int len = valid ? SeqLayout::chunk_of(n, c - c0, s0, slen).len : 0;
+        const int64_t t0 = valid ? SeqLayout::chunk_of(n, c - c0, s0, slen).t0 : 0;
+#pragma unroll
+        for (int i = 0; i < kChunk * OWR / kPsThreads; ++i) {
+            const int w = threadIdx.x + i * kPsThreads, t = w / OWR, cw = w % OWR;
+            const u32x4 x = *(const u32x4*)&sO[buf][t * OLD + cw * OE];
+            TOut* dst = t < len ? o + tok_index(t0 + t, h, p.H, DV) + jb + cw * OE : (TOut*)p.sink;
+            *(u32x4*)dst = x;
+        }
+    };
     auto step = [&](int c, int buf, const PsFwdOps<P, NJ>& Rc) {
-        const ChunkRef cr = SeqLayout::chunk_of(n, c - c0, s0, slen);
         __syncthreads();  // h^T of this chunk complete; the other buffer's readers are done
+        if constexpr (WO) flush_o(c - 1, buf ^ 1, c > c0);
         if (owner) {
             AFrag<P> fb;
             load_frag(fb, HT[buf].sub(16 * tj), 0);
@@ -120,11 +140,7 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
                 load_frag(fo, HT[buf].sub(16 * j), 0);
                 const f32x4 acc = mma_ff(Rc.qh, fo, Rc.ol[j]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * wave + frag_row(r);
-                    TOut* dst = t < cr.len ? o + tok_index(cr.t0 + t, h, p.H, DV) + jb + 16 * j + lr : (TOut*)p.sink;
-                    Elem<TOut>::store(dst, 0, acc[r]);
-                }
+                for (int r = 0; r < 4; ++r) Elem<TOut>::store(sO[buf], (16 * wave + frag_row(r)) * OLD + 16 * j + lr, acc[r]);
             }
         }
     };
@@ -149,6 +165,10 @@ __global__ void __launch_bounds__(kPsThreads) fwd_pscan_kernel(Prm p, int total_
 #pragma unroll
         for (int i = 0; i < PD - 1; ++i)
             if (c + i < c1) step(c + i, i & 1, R[i]);
+        if constexpr (WO) {
+            __syncthreads();
+            flush_o(c1 - 1, (c1 - 1 - c0) & 1, true);
+        }
     }
     if (owner && p.hT) {
 #pragma unroll
