@@ -14,9 +14,10 @@
 // registers by waves 0 .. 2 BV / 16 - 1, and wave w forms output rows
 // 16 w .. 16 w + 15.  The state is copied each chunk into a double-buffered LDS
 // tile h^T[j][c], the B operand of every product of the chunk; everything else
-// comes from memory as register fragments, prefetched four chunks ahead.  With
-// BV = 16 each (sequence, head) runs as four independent chains, which keeps
-// more operand loads in flight per CU than two chains of 32 columns.
+// comes from memory as register fragments, prefetched four chunks ahead (two
+// in the reverse pass).  BV = 32 is the one launched: with BV = 16 each
+// (sequence, head) runs as four independent chains instead of two, and at the
+// layer shape that measured slower (every chain re-reads P and qh).
 #pragma once
 
 #include "kda_chunk.cuh"
@@ -276,7 +277,10 @@ __global__ void __launch_bounds__(kPsThreads) bwd_pdh_kernel(Prm p, int total_wg
         }
     };
     if (c0 < c1) {
-        constexpr int PD = 4;  // chunks of operands in flight (branch-free body, as in the forward pass)
+        // chunks of operands in flight (branch-free body, as in the forward pass).  Two are
+        // as fast as four (memory latency is not what sets the time per chunk) and keep the
+        // kernel at 112 VGPRs; four took 256 + 8 AGPRs, six spilled to AGPRs and ran slower.
+        constexpr int PD = 2;
         PsBwdOps<TIn, P, BV> R[PD];
 #pragma unroll
         for (int i = 0; i < PD; ++i) ps_bwd_load<TIn, P, BV>(p, slot_of(c1 - 1 - i), cref(c1 - 1 - i), h, jb, tc, R[i]);
